@@ -1,0 +1,208 @@
+"""Throughput of the Graph Machine sparse-layer pass on one MI355X.
+
+One step = one pass of the whole hot path over one batch of synthetic input:
+  gm_ser_forward   A' = Sparsify_4(A A)             (16 two-hop candidates)
+  gm_sea_forward   o = SEA(q, k, v, A')
+  gm_sea_backward  dq, dk, dv, dw' from dout
+  gm_ser_backward  dw (both legs are A, so both contributions land in dw)
+on B=8 sequences of n=4096 tokens, 16 query / 8 KV heads, d=128, bf16
+activations, fp32 edges and gradients, edges half local (previous 64
+tokens) and half far (uniform on [0, i]).  Inputs are resident in HBM
+before timing starts; outputs and workspace are preallocated.
+
+Prints one JSON line: units (tokens x KV heads) per second, the pass's
+algorithmic HBM bandwidth, per-call times from HIP events on the launch
+stream, the roofline entry of the dominant call, and the CPU oracle's rate
+on a bounded sample of the same workload (rank 0, N=1).
+
+    python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu-baseline]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import sparse_dynamic_routing_amd as gm  # noqa: E402
+import synth  # noqa: E402
+
+METRIC = ("SER+SEA fwd+bwd tokens·KV-heads/s at n=4096,s1=4; "
+          "achieved HBM GB/s vs peak")
+PEAK_HBM_GBS = 8000.0
+
+# Algorithmic (compulsory) bytes per unit: every input byte read once, every
+# output byte written once; K/V counted once per unit (unique rows).
+# G = 2 query heads per KV head, d = 128, bf16 activations, fp32 gradients.
+BYTES_PER_UNIT = {
+    "gm_ser_forward": 32 + 32,                          # A row + A' row
+    "gm_sea_forward": 512 + 32 + 512 + 512,             # q, A', K+V, o
+    "gm_sea_backward": 512 + 512 + 32 + 512 + 1024 + 16 + 1024,  # q dO A' KV dq dw' dK dV
+    "gm_ser_backward": 32 + 32 + 16 + 16,               # A, A', dw', dw
+}
+CALLS = list(BYTES_PER_UNIT)
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    return ap.parse_args()
+
+
+class Pass:
+    """Device inputs, preallocated outputs and the four calls of one step."""
+
+    def __init__(self, p: synth.Preset):
+        self.p = p
+        idx, w = synth.edges(p.seed, p.B, p.n, p.hkv, p.s2, mode=p.mode)
+        self.host_edges = (idx, w)
+        dt = p.dtype
+        qs, ks = (p.B, p.n, p.hq, p.d), (p.B, p.n, p.hkv, p.d)
+        self.host_act = {name: synth.normal(p.seed, name, shape, dt)
+                         for name, shape in (("q", qs), ("k", ks), ("v", ks), ("dout", qs))}
+        cu = lambda t: t.contiguous().cuda()  # noqa: E731
+        self.idx, self.w = cu(torch.from_numpy(idx)), cu(torch.from_numpy(w))
+        self.q, self.k, self.v, self.dout = (cu(self.host_act[n]) for n in ("q", "k", "v", "dout"))
+        f32 = dict(dtype=torch.float32, device="cuda")
+        es = (p.B, p.n, p.hkv, p.s1)
+        self.ia = torch.empty(es, dtype=torch.int32, device="cuda")
+        self.wa = torch.empty(es, **f32)
+        self.o = torch.empty_like(self.q)
+        self.dq = torch.empty(qs, **f32)
+        self.dk = torch.empty(ks, **f32)
+        self.dv = torch.empty(ks, **f32)
+        self.dwa = torch.empty(es, **f32)
+        self.dA = torch.empty(self.idx.shape, **f32)
+        self.ws = gm.ser_workspace(self.idx, self.idx, aliased=True)
+
+    def calls(self):
+        return [
+            lambda: gm.gm_ser_forward(self.idx, self.w, self.idx, self.w, self.ia, self.wa),
+            lambda: gm.gm_sea_forward(self.q, self.k, self.v, self.ia, self.wa, self.o),
+            lambda: gm.gm_sea_backward(self.q, self.k, self.v, self.ia, self.wa, self.dout,
+                                       self.dq, self.dk, self.dv, self.dwa),
+            lambda: gm.gm_ser_backward(self.idx, self.w, self.idx, self.w, self.ia, self.wa,
+                                       self.dwa, self.dA, self.dA, self.ws),
+        ]
+
+
+def time_gpu(ps: Pass, steps: int, warmup: int):
+    calls = ps.calls()
+    for _ in range(warmup):
+        for c in calls:
+            c()
+    torch.cuda.synchronize()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(calls) + 1)]
+          for _ in range(steps)]
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    start.record()
+    for s in range(steps):
+        ev[s][0].record()
+        for i, c in enumerate(calls):
+            c()
+            ev[s][i + 1].record()
+    end.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    total_ms = start.elapsed_time(end)
+    per_call = {name: float(np.mean([ev[s][i].elapsed_time(ev[s][i + 1]) for s in range(steps)]))
+                for i, name in enumerate(CALLS)}
+    return total_ms / steps, per_call, wall
+
+
+def cpu_baseline(ps: Pass, budget_s: float):
+    """The oracle, single-threaded, on whole (batch, KV head) pairs of the same
+    workload, in pair order, until the time budget is spent (whole pairs)."""
+    import oracle
+    orc = oracle.get()
+    p = ps.p
+    G = p.hq // p.hkv
+    idx, w = ps.host_edges
+    act = {k: v.float().numpy() for k, v in ps.host_act.items()}
+    done, spent = 0, 0.0
+    pairs = [(b, h) for b in range(p.B) for h in range(p.hkv)]
+    while spent < budget_s and done < 4 * len(pairs):
+        b, h = pairs[done % len(pairs)]
+        sl = lambda x, g=0: np.ascontiguousarray(  # noqa: E731
+            x[b:b + 1, :, h * g:(h + 1) * g] if g else x[b:b + 1, :, h:h + 1], dtype=None)
+        e_i, e_w = sl(idx), sl(w).astype(np.float64)
+        q, k, v, do = (np.ascontiguousarray(sl(act[n], G if n in ("q", "dout") else 0),
+                                            dtype=np.float64) for n in ("q", "k", "v", "dout"))
+        t0 = time.perf_counter()
+        ia, wa = orc.ser_forward(e_i, e_w, e_i, e_w, p.s1)
+        orc.sea_forward(q, k, v, ia, wa)
+        dq, dk, dv, dwa = orc.sea_backward(q, k, v, ia, wa, do)
+        orc.ser_backward(e_i, e_w, e_i, e_w, ia, wa, dwa, aliased=True)
+        spent += time.perf_counter() - t0
+        done += 1
+    units = done * p.n
+    return {"value": units / spent, "unit": "tokens·KV-heads/s", "cores": 1,
+            "kind": "oracle",
+            "sample": f"{done} whole (batch, KV head) pairs of the measured workload "
+                      f"({units} units, {spent:.1f} s), single-threaded C oracle in fp64"}
+
+
+def main():
+    a = parse()
+    if a.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: this path has no cross-GPU step (units are "
+              "independent per (batch, KV head)); run it with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    gm.load()
+    p = synth.PRESETS["metric"]
+    ps = Pass(p)
+    torch.cuda.synchronize()
+    ms, per_call, wall = time_gpu(ps, a.steps, a.warmup)
+    U = p.units
+    pass_bytes = sum(BYTES_PER_UNIT.values()) * U
+    dom = max(per_call, key=per_call.get)
+    dom_gbs = BYTES_PER_UNIT[dom] * U / (per_call[dom] * 1e-3) / 1e9
+    line = {
+        "metric": METRIC,
+        "value": U / (ms * 1e-3),
+        "unit": "tokens·KV-heads/s",
+        "n_gpus": 1,
+        "steps": a.steps,
+        "warmup": a.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "SER+SEA layer pass fwd+bwd: B=8, n=4096, 16 q / 8 KV heads, "
+                               "d=128, s1=s2=s3=4, local/far edge mix",
+                   "B": p.B, "n": p.n, "hq": p.hq, "hkv": p.hkv, "d": p.d,
+                   "s1": p.s1, "s2": p.s2, "s3": p.s3, "units_per_step": U,
+                   "parallelism": "single GPU"},
+        "pass_algorithmic_GBps": pass_bytes / (ms * 1e-3) / 1e9,
+        "pass_frac_of_peak": pass_bytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS,
+        "per_call_ms": per_call,
+        "roofline": {"kernel": dom, "bound": "hbm", "achieved": dom_gbs, "peak": PEAK_HBM_GBS,
+                     "unit": "GB/s", "frac": dom_gbs / PEAK_HBM_GBS, "traffic": None,
+                     "bytes_per_unit": BYTES_PER_UNIT[dom], "units_per_launch": U},
+        "wall_s_timed": wall,
+    }
+    if not a.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(ps, a.cpu_seconds)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,173 @@
+/*
+ * gm.h -- C ABI of the Graph Machine sparse-layer path for AMD MI355X (gfx950).
+ *
+ * Two stages of a Graph Machine sparse layer, forward and backward, as
+ * described on the pages about the Graph Machine (arXiv 2609.02881):
+ *   SER  sparse edge referral: A' = Sparsify_s1(A1 A2) over two-hop paths
+ *        ("Graph Machine: Towards Better Pretraining via Edges", ai.info,
+ *        Key Contributions 3 and Methodology in Plain English);
+ *   SEA  sparse edge attention: softmax over the edge slots of
+ *        scale * q.k + ln w (product of experts), weighted sum of values
+ *        (same page, Key Contributions 3 and Methodology);
+ *   backward passes through the soft edge weights only; indices get no
+ *   gradient ("Graph Machine" news article on rit.work, section on what was
+ *   done; ai.info Methodology).
+ *
+ * Conventions shared by every call
+ *   - Tensors are dense, row-major, contiguous, and live in device memory
+ *     owned by the caller.  The library never allocates or frees memory;
+ *     scratch space is passed in as a workspace where a call needs one.
+ *   - A "unit" is one (batch b, token i, KV head h).  Edge tensors hold one
+ *     row of s slots per unit: idx[B][n][hkv][s] int32, w[B][n][hkv][s] fp32.
+ *     Indices are local to the sequence and causal: 0 <= idx <= i.  A slot
+ *     with w == 0 is padding (index 0 is the padding token that absorbs
+ *     missing edges); w must be >= 0 and finite.  Indices are NOT range
+ *     checked on the device: an index outside [0, i] reads or writes outside
+ *     the row and is undefined behaviour; gm_check_edges is the validator.
+ *   - q, o, dout, dq are [B][n][hq][d]; k, v, dk, dv are [B][n][hkv][d].
+ *     Query head hq uses KV head hq / (hq_count / hkv) (grouped heads).
+ *   - Every call is asynchronous on `stream` (NULL = the null stream), and
+ *     every output is fully overwritten.  Shapes, pointers and alignment are
+ *     checked on the host first; on any error the call returns a non-zero
+ *     status and launches nothing.  Kernel launch failures return
+ *     GM_ERR_HIP.
+ *   - Limits: B, n, hkv >= 0 (zero sizes are a no-op), B*n*hkv < 2^31,
+ *     1 <= s <= 64, s2*s3 <= 64, d in {16, 32, 64, 128, 256}, hq % hkv == 0,
+ *     hq / hkv in {1, 2, 4, 8, 16}; activation pointers 16-byte aligned,
+ *     edge pointers 4-byte aligned.
+ *   - Determinism: gm_ser_forward and gm_sea_forward are bitwise
+ *     deterministic.  gm_ser_backward accumulates in fp64 and rounds once.
+ *     gm_sea_backward scatters dk/dv with fp32 atomic adds, so their last
+ *     bits may vary between runs.
+ */
+#ifndef GM_H
+#define GM_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    GM_OK = 0,
+    GM_ERR_NULL = 1,         /* a required pointer is NULL                  */
+    GM_ERR_SHAPE = 2,        /* a size is negative, zero where not allowed,
+                                or the product overflows                     */
+    GM_ERR_UNSUPPORTED = 3,  /* s, d, dtype or head ratio outside the limits */
+    GM_ERR_WORKSPACE = 4,    /* workspace missing or too small               */
+    GM_ERR_HIP = 5,          /* a HIP launch or runtime call failed          */
+    GM_ERR_ALIGN = 6,        /* a pointer is not aligned as required         */
+    GM_ERR_ALIAS = 7         /* an output overlaps an input it must not      */
+} gm_status;
+
+typedef enum { GM_F32 = 0, GM_BF16 = 1 } gm_dtype;
+
+/*
+ * Sparse edge referral, forward: A' = Sparsify_s1(A1 A2)
+ * (ai.info Key Contributions 3; Methodology: the first leg's indices fetch
+ * the second leg's indices and weights; hard top-s selection).
+ *   in   idx1, w1  [B][n][hkv][s2]  leg 1 (row i of A1)
+ *        idx2, w2  [B][n][hkv][s3]  leg 2 (row j of A2); may equal leg 1
+ *   out  idx_out, w_out [B][n][hkv][s1]  must not overlap the legs
+ * For unit (b,i,h): every path i -> j = idx1[i,a] -> m = idx2[j,c] has weight
+ * w1[i,a] * w2[j,c]; paths to the same m are merged by summing (in double,
+ * in (a, c) order), the sum is rounded to fp32, and the s1 targets of largest
+ * positive weight are kept, equal weights ordered by lower index.  Slots are
+ * written in that order; unused slots get (0, 0.0f).  Requires s2*s3 <= 64.
+ */
+gm_status gm_ser_forward(int B, int n, int hkv,
+                         const int32_t* idx1, const float* w1, int s2,
+                         const int32_t* idx2, const float* w2, int s3,
+                         int32_t* idx_out, float* w_out, int s1,
+                         hipStream_t stream);
+
+/*
+ * Sparse edge attention, forward (ai.info Key Contributions 3: edge indices
+ * pick the positions that supply keys and values, node factor = scaled
+ * query-key score, edge factor = log edge weight, product of experts;
+ * Methodology: RoPE omitted).
+ *   in   q [B][n][hq][d], k, v [B][n][hkv][d]  dtype dt (fp32 or bf16)
+ *        idx, w [B][n][hkv][s1]
+ *        scale: multiplies q.k (normally 1/sqrt(d))
+ *   out  o [B][n][hq][d] dtype dt
+ * o[hq] = sum_t p_t v[idx_t], p = softmax over live slots (w_t > 0) of
+ * scale*q.k[idx_t] + ln w_t; a unit with no live slot gets o = 0.
+ * Arithmetic is fp32 for bf16 inputs and fp64 for fp32 inputs.
+ */
+gm_status gm_sea_forward(int B, int n, int hq, int hkv, int d, gm_dtype dt,
+                         float scale, const void* q, const void* k, const void* v,
+                         const int32_t* idx, const float* w, int s1, void* o,
+                         hipStream_t stream);
+
+/*
+ * Sparse edge attention, backward: chain rule of gm_sea_forward with the
+ * indices held fixed (rit.work: indices get no gradient, learning goes
+ * through the soft edge weights).
+ *   in   q, k, v, idx, w, s1, scale as for the forward; dout [B][n][hq][d] dt
+ *   out  dq [B][n][hq][d] fp32, dk, dv [B][n][hkv][d] fp32,
+ *        dw [B][n][hkv][s1] fp32; no output may overlap an input.
+ * With g_t = dout.v[idx_t], gbar = sum p_t g_t, dl_t = p_t (g_t - gbar):
+ * dq = scale sum_t dl_t k[idx_t]; dk[idx_t] += scale dl_t q;
+ * dv[idx_t] += p_t dout; dw_t = sum over the group's query heads of
+ * dl_t / w_t.  Padding slots (w = 0) get and pass no gradient.
+ */
+gm_status gm_sea_backward(int B, int n, int hq, int hkv, int d, gm_dtype dt,
+                          float scale, const void* q, const void* k, const void* v,
+                          const int32_t* idx, const float* w, int s1,
+                          const void* dout, float* dq, float* dk, float* dv,
+                          float* dw, hipStream_t stream);
+
+/*
+ * Bytes of device workspace gm_ser_backward needs for these sizes
+ * (fp64 accumulators for dw1 and dw2, one array when they alias).
+ */
+size_t gm_ser_backward_workspace_bytes(int B, int n, int hkv, int s2, int s3,
+                                       int aliased);
+
+/*
+ * Sparse edge referral, backward: chain rule of gm_ser_forward with the
+ * selection held fixed (ai.info Methodology: only retained weights get
+ * gradients).
+ *   in   legs as for the forward; idx_out, w_out [B][n][hkv][s1] the A' the
+ *        forward produced; dw_out [B][n][hkv][s1] the gradient of w_out
+ *   out  dw1 [B][n][hkv][s2], dw2 [B][n][hkv][s3] fp32.  dw1 == dw2 is
+ *        allowed (A' = Sparsify(A A), s2 == s3): the sum of both is written.
+ *   ws   device workspace of gm_ser_backward_workspace_bytes(...) bytes,
+ *        8-byte aligned.
+ * For each path (a, c) with w1 > 0 and w2 > 0 whose target equals a
+ * retained slot t (w_out_t > 0): dw1[i,a] += dw_out_t w2[j,c] and
+ * dw2[j,c] += dw_out_t w1[i,a].  Slots with zero weight get 0.
+ */
+gm_status gm_ser_backward(int B, int n, int hkv,
+                          const int32_t* idx1, const float* w1, int s2,
+                          const int32_t* idx2, const float* w2, int s3,
+                          const int32_t* idx_out, const float* w_out, int s1,
+                          const float* dw_out, float* dw1, float* dw2,
+                          void* workspace, size_t workspace_bytes,
+                          hipStream_t stream);
+
+/*
+ * Debug validator of an edge tensor.  Adds to counts[0] the number of slots
+ * whose index lies outside [0, i] or whose weight is negative or not finite,
+ * and to counts[1] the number of live slots (w > 0), i.e. the key/value rows
+ * SEA reads (ai.info Main Findings, KV access).  counts is device memory of
+ * two uint64 the caller zeroes; the call is asynchronous on `stream`.
+ */
+gm_status gm_check_edges(int B, int n, int hkv, const int32_t* idx,
+                         const float* w, int s, unsigned long long* counts,
+                         hipStream_t stream);
+
+/* Static text for a status code. */
+const char* gm_status_string(gm_status status);
+
+/* ABI version: bumped on any change of the calls above. */
+int gm_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GM_H */

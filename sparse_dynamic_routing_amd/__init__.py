@@ -1,0 +1,13 @@
+"""Graph Machine sparse-layer hot path for AMD MI355X (gfx950).
+
+Sparse edge referral (SER) and sparse edge attention (SEA), forward and
+backward, as hand-written HIP kernels behind the C ABI of include/gm.h
+(libgm.so).  This package is the thin Python binding of that library; see
+``binding`` for the calls.  Importing the package does not load the library;
+the first call does, and raises if it is not built.
+"""
+from .binding import (  # noqa: F401
+    EXPORTS, GMError, check_edges, gm_check_edges, gm_sea_backward, gm_sea_forward,
+    gm_ser_backward, gm_ser_backward_workspace_bytes, gm_ser_forward, load, sea_backward,
+    sea_forward, ser_backward, ser_forward, ser_workspace,
+)

@@ -1,0 +1,224 @@
+"""ctypes binding of libgm.so, the C ABI declared in include/gm.h.
+
+Argument marshalling only: every function here checks that the torch
+tensors it is given match the C call (device, dtype, contiguity, shapes),
+then passes their device pointers, sizes and the current HIP stream to the
+library.  All arithmetic runs in the HIP kernels.  There is no fallback: if
+libgm.so is missing or cannot be loaded, every call raises.
+
+The functions named like the C calls (``gm_ser_forward`` ...) write into
+output tensors the caller provides; ``ser_forward`` and friends allocate the
+outputs with torch and return them.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+import torch
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libgm.so")
+
+GM_F32, GM_BF16 = 0, 1
+STATUS = {0: "GM_OK", 1: "GM_ERR_NULL", 2: "GM_ERR_SHAPE", 3: "GM_ERR_UNSUPPORTED",
+          4: "GM_ERR_WORKSPACE", 5: "GM_ERR_HIP", 6: "GM_ERR_ALIGN", 7: "GM_ERR_ALIAS"}
+EXPORTS = ("gm_ser_forward", "gm_sea_forward", "gm_sea_backward",
+           "gm_ser_backward_workspace_bytes", "gm_ser_backward", "gm_check_edges",
+           "gm_status_string", "gm_abi_version")
+
+
+class GMError(RuntimeError):
+    def __init__(self, call: str, code: int, text: str):
+        super().__init__(f"{call} failed: {STATUS.get(code, code)} ({text})")
+        self.code = code
+
+
+_lib = None
+_I, _P, _F, _Z = ctypes.c_int, ctypes.c_void_p, ctypes.c_float, ctypes.c_size_t
+
+
+def load(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Load libgm.so (torch first, so the library binds to torch's HIP runtime)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise ImportError(f"{path} is not built; run `python -m sparse_dynamic_routing_amd.build`")
+    lib = ctypes.CDLL(path)
+    sig = {
+        "gm_ser_forward": [_I, _I, _I, _P, _P, _I, _P, _P, _I, _P, _P, _I, _P],
+        "gm_sea_forward": [_I, _I, _I, _I, _I, _I, _F, _P, _P, _P, _P, _P, _I, _P, _P],
+        "gm_sea_backward": [_I, _I, _I, _I, _I, _I, _F, _P, _P, _P, _P, _P, _I, _P,
+                            _P, _P, _P, _P, _P],
+        "gm_ser_backward_workspace_bytes": [_I, _I, _I, _I, _I, _I],
+        "gm_ser_backward": [_I, _I, _I, _P, _P, _I, _P, _P, _I, _P, _P, _I, _P, _P, _P,
+                            _P, _Z, _P],
+        "gm_check_edges": [_I, _I, _I, _P, _P, _I, _P, _P],
+        "gm_status_string": [_I],
+        "gm_abi_version": [],
+    }
+    for name, args in sig.items():
+        f = getattr(lib, name)
+        f.argtypes = args
+        f.restype = _I
+    lib.gm_ser_backward_workspace_bytes.restype = _Z
+    lib.gm_status_string.restype = ctypes.c_char_p
+    _lib = lib
+    return lib
+
+
+def _call(name: str, *args) -> None:
+    lib = load()
+    rc = getattr(lib, name)(*args)
+    if rc != 0:
+        raise GMError(name, rc, lib.gm_status_string(rc).decode())
+
+
+def _stream(stream) -> int:
+    s = torch.cuda.current_stream() if stream is None else stream
+    return s.cuda_stream
+
+
+def _ptr(t: torch.Tensor | None):
+    return None if t is None else t.data_ptr()
+
+
+def _need(t: torch.Tensor, name: str, dtypes, shape=None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be on the GPU, got {t.device}")
+    if t.dtype not in dtypes:
+        raise TypeError(f"{name} has dtype {t.dtype}, expected one of {dtypes}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+
+
+def _act_dtype(t: torch.Tensor) -> int:
+    return GM_BF16 if t.dtype == torch.bfloat16 else GM_F32
+
+
+_ACT = (torch.float32, torch.bfloat16)
+
+
+# --------------------------------------------------------------- C-named calls
+def gm_ser_forward(idx1, w1, idx2, w2, idx_out, w_out, stream=None) -> None:
+    B, n, hkv, s2 = idx1.shape
+    s3, s1 = idx2.shape[-1], idx_out.shape[-1]
+    _need(idx1, "idx1", (torch.int32,)); _need(w1, "w1", (torch.float32,), idx1.shape)
+    _need(idx2, "idx2", (torch.int32,), (B, n, hkv, s3))
+    _need(w2, "w2", (torch.float32,), idx2.shape)
+    _need(idx_out, "idx_out", (torch.int32,), (B, n, hkv, s1))
+    _need(w_out, "w_out", (torch.float32,), idx_out.shape)
+    _call("gm_ser_forward", B, n, hkv, _ptr(idx1), _ptr(w1), s2, _ptr(idx2), _ptr(w2), s3,
+          _ptr(idx_out), _ptr(w_out), s1, _stream(stream))
+
+
+def gm_sea_forward(q, k, v, idx, w, o, scale=None, stream=None) -> None:
+    B, n, hq, d = q.shape
+    hkv, s1 = idx.shape[2], idx.shape[3]
+    _need(q, "q", _ACT)
+    _need(k, "k", (q.dtype,), (B, n, hkv, d)); _need(v, "v", (q.dtype,), (B, n, hkv, d))
+    _need(idx, "idx", (torch.int32,), (B, n, hkv, s1)); _need(w, "w", (torch.float32,), idx.shape)
+    _need(o, "o", (q.dtype,), q.shape)
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    _call("gm_sea_forward", B, n, hq, hkv, d, _act_dtype(q), scale, _ptr(q), _ptr(k), _ptr(v),
+          _ptr(idx), _ptr(w), s1, _ptr(o), _stream(stream))
+
+
+def gm_sea_backward(q, k, v, idx, w, dout, dq, dk, dv, dw, scale=None, stream=None) -> None:
+    B, n, hq, d = q.shape
+    hkv, s1 = idx.shape[2], idx.shape[3]
+    _need(q, "q", _ACT)
+    _need(k, "k", (q.dtype,), (B, n, hkv, d)); _need(v, "v", (q.dtype,), (B, n, hkv, d))
+    _need(idx, "idx", (torch.int32,), (B, n, hkv, s1)); _need(w, "w", (torch.float32,), idx.shape)
+    _need(dout, "dout", (q.dtype,), q.shape)
+    _need(dq, "dq", (torch.float32,), q.shape)
+    _need(dk, "dk", (torch.float32,), k.shape); _need(dv, "dv", (torch.float32,), v.shape)
+    _need(dw, "dw", (torch.float32,), idx.shape)
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    _call("gm_sea_backward", B, n, hq, hkv, d, _act_dtype(q), scale, _ptr(q), _ptr(k), _ptr(v),
+          _ptr(idx), _ptr(w), s1, _ptr(dout), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dw),
+          _stream(stream))
+
+
+def gm_ser_backward_workspace_bytes(B, n, hkv, s2, s3, aliased) -> int:
+    return int(load().gm_ser_backward_workspace_bytes(B, n, hkv, s2, s3, int(bool(aliased))))
+
+
+def gm_ser_backward(idx1, w1, idx2, w2, idx_out, w_out, dw_out, dw1, dw2, workspace,
+                    stream=None) -> None:
+    B, n, hkv, s2 = idx1.shape
+    s3, s1 = idx2.shape[-1], idx_out.shape[-1]
+    _need(idx1, "idx1", (torch.int32,)); _need(w1, "w1", (torch.float32,), idx1.shape)
+    _need(idx2, "idx2", (torch.int32,), (B, n, hkv, s3))
+    _need(w2, "w2", (torch.float32,), idx2.shape)
+    _need(idx_out, "idx_out", (torch.int32,), (B, n, hkv, s1))
+    _need(w_out, "w_out", (torch.float32,), idx_out.shape)
+    _need(dw_out, "dw_out", (torch.float32,), idx_out.shape)
+    _need(dw1, "dw1", (torch.float32,), idx1.shape); _need(dw2, "dw2", (torch.float32,), idx2.shape)
+    _need(workspace, "workspace", (torch.uint8, torch.float64))
+    _call("gm_ser_backward", B, n, hkv, _ptr(idx1), _ptr(w1), s2, _ptr(idx2), _ptr(w2), s3,
+          _ptr(idx_out), _ptr(w_out), s1, _ptr(dw_out), _ptr(dw1), _ptr(dw2), _ptr(workspace),
+          workspace.numel() * workspace.element_size(), _stream(stream))
+
+
+def gm_check_edges(idx, w, counts, stream=None) -> None:
+    B, n, hkv, s = idx.shape
+    _need(idx, "idx", (torch.int32,)); _need(w, "w", (torch.float32,), idx.shape)
+    _need(counts, "counts", (torch.int64,), (2,))
+    _call("gm_check_edges", B, n, hkv, _ptr(idx), _ptr(w), s, _ptr(counts), _stream(stream))
+
+
+# ------------------------------------------------------- allocating wrappers
+def ser_forward(idx1, w1, idx2, w2, s1, stream=None):
+    shape = tuple(idx1.shape[:3]) + (s1,)
+    idx_out = torch.empty(shape, dtype=torch.int32, device=idx1.device)
+    w_out = torch.empty(shape, dtype=torch.float32, device=idx1.device)
+    gm_ser_forward(idx1, w1, idx2, w2, idx_out, w_out, stream)
+    return idx_out, w_out
+
+
+def sea_forward(q, k, v, idx, w, scale=None, stream=None):
+    o = torch.empty_like(q)
+    gm_sea_forward(q, k, v, idx, w, o, scale, stream)
+    return o
+
+
+def sea_backward(q, k, v, idx, w, dout, scale=None, stream=None):
+    f32 = dict(dtype=torch.float32, device=q.device)
+    dq = torch.empty(q.shape, **f32)
+    dk = torch.empty(k.shape, **f32)
+    dv = torch.empty(v.shape, **f32)
+    dw = torch.empty(idx.shape, **f32)
+    gm_sea_backward(q, k, v, idx, w, dout, dq, dk, dv, dw, scale, stream)
+    return dq, dk, dv, dw
+
+
+def ser_workspace(idx1, idx2, aliased, device=None) -> torch.Tensor:
+    B, n, hkv, s2 = idx1.shape
+    nbytes = gm_ser_backward_workspace_bytes(B, n, hkv, s2, idx2.shape[-1], aliased)
+    return torch.empty(max(nbytes, 8) // 8, dtype=torch.float64,
+                       device=device or idx1.device)
+
+
+def ser_backward(idx1, w1, idx2, w2, idx_out, w_out, dw_out, aliased=False, workspace=None,
+                 stream=None):
+    """(dw1, dw2); with ``aliased`` the legs are one tensor and one gradient
+    (the same tensor, returned twice) receives both contributions."""
+    dw1 = torch.empty(idx1.shape, dtype=torch.float32, device=idx1.device)
+    dw2 = dw1 if aliased else torch.empty(idx2.shape, dtype=torch.float32, device=idx1.device)
+    ws = ser_workspace(idx1, idx2, aliased) if workspace is None else workspace
+    gm_ser_backward(idx1, w1, idx2, w2, idx_out, w_out, dw_out, dw1, dw2, ws, stream)
+    return dw1, dw2
+
+
+def check_edges(idx, w, stream=None):
+    """(bad slots, live slots) of an edge tensor; synchronises the stream."""
+    counts = torch.zeros(2, dtype=torch.int64, device=idx.device)
+    gm_check_edges(idx, w, counts, stream)
+    c = counts.cpu()
+    return int(c[0]), int(c[1])

@@ -1,0 +1,208 @@
+// C ABI of the Graph Machine sparse-layer path (declared in include/gm.h):
+// host-side argument checks, then the kernel launches on the caller's stream.
+// Nothing here allocates; every check happens before the first launch.
+#include "gm.h"
+#include "gm_internal.h"
+
+#include <limits.h>
+#include <stdint.h>
+
+namespace {
+
+using gm::TeamShape;
+
+bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
+
+bool pow2_in(int x, int lo, int hi) { return x >= lo && x <= hi && (x & (x - 1)) == 0; }
+
+// Units and element counts must fit the kernels' index types.
+gm_status check_units(int B, int n, int hkv) {
+    if (B < 0 || n < 0 || hkv < 0) return GM_ERR_SHAPE;
+    if ((long long)B * n * hkv >= (long long)INT_MAX) return GM_ERR_SHAPE;
+    return GM_OK;
+}
+
+bool empty(int B, int n, int hkv) { return (long long)B * n * hkv == 0; }
+
+gm_status check_edge_ptrs(const int32_t* idx, const float* w) {
+    if (!idx || !w) return GM_ERR_NULL;
+    if (!aligned(idx, 4) || !aligned(w, 4)) return GM_ERR_ALIGN;
+    return GM_OK;
+}
+
+gm_status check_sea(int B, int n, int hq, int hkv, int d, gm_dtype dt, int s1) {
+    gm_status st = check_units(B, n, hkv);
+    if (st != GM_OK) return st;
+    if (hq < 0) return GM_ERR_SHAPE;
+    if (hkv == 0) return empty(B, n, hkv) ? GM_OK : GM_ERR_SHAPE;
+    if (hq % hkv != 0 || hq == 0) return GM_ERR_UNSUPPORTED;
+    if (!pow2_in(hq / hkv, 1, 16)) return GM_ERR_UNSUPPORTED;
+    if (!pow2_in(d, 16, 256)) return GM_ERR_UNSUPPORTED;
+    if (dt != GM_F32 && dt != GM_BF16) return GM_ERR_UNSUPPORTED;
+    if (s1 < 1 || s1 > 64) return GM_ERR_UNSUPPORTED;
+    if ((long long)B * n * hq * d >= (1ll << 46)) return GM_ERR_SHAPE;
+    return GM_OK;
+}
+
+gm_status check_ser(int B, int n, int hkv, int s1, int s2, int s3) {
+    gm_status st = check_units(B, n, hkv);
+    if (st != GM_OK) return st;
+    if (s1 < 1 || s1 > 64 || s2 < 1 || s3 < 1 || s2 * s3 > 64) return GM_ERR_UNSUPPORTED;
+    return GM_OK;
+}
+
+gm_status hip_status(hipError_t e) { return e == hipSuccess ? GM_OK : GM_ERR_HIP; }
+
+bool overlaps(const void* a, size_t an, const void* b, size_t bn) {
+    const uintptr_t x = (uintptr_t)a, y = (uintptr_t)b;
+    return a && b && x < y + bn && y < x + an;
+}
+
+}  // namespace
+
+extern "C" {
+
+int gm_abi_version(void) { return 1; }
+
+const char* gm_status_string(gm_status s) {
+    switch (s) {
+        case GM_OK: return "ok";
+        case GM_ERR_NULL: return "a required pointer is NULL";
+        case GM_ERR_SHAPE: return "invalid or overflowing size";
+        case GM_ERR_UNSUPPORTED: return "s, d, dtype or head ratio outside the supported set";
+        case GM_ERR_WORKSPACE: return "workspace missing or too small";
+        case GM_ERR_HIP: return "HIP launch or runtime error";
+        case GM_ERR_ALIGN: return "pointer not aligned as required";
+        case GM_ERR_ALIAS: return "an output overlaps an input";
+    }
+    return "unknown status";
+}
+
+gm_status gm_ser_forward(int B, int n, int hkv, const int32_t* idx1, const float* w1, int s2,
+                         const int32_t* idx2, const float* w2, int s3, int32_t* idx_out,
+                         float* w_out, int s1, hipStream_t stream) {
+    gm_status st = check_ser(B, n, hkv, s1, s2, s3);
+    if (st != GM_OK) return st;
+    if (empty(B, n, hkv)) return GM_OK;
+    if ((st = check_edge_ptrs(idx1, w1)) != GM_OK) return st;
+    if ((st = check_edge_ptrs(idx2, w2)) != GM_OK) return st;
+    if ((st = check_edge_ptrs(idx_out, w_out)) != GM_OK) return st;
+    const size_t rows = (size_t)B * n * hkv;
+    const size_t o4 = rows * s1 * 4;
+    if (overlaps(idx_out, o4, idx1, rows * s2 * 4) || overlaps(idx_out, o4, w1, rows * s2 * 4) ||
+        overlaps(idx_out, o4, idx2, rows * s3 * 4) || overlaps(idx_out, o4, w2, rows * s3 * 4) ||
+        overlaps(w_out, o4, idx1, rows * s2 * 4) || overlaps(w_out, o4, w1, rows * s2 * 4) ||
+        overlaps(w_out, o4, idx2, rows * s3 * 4) || overlaps(w_out, o4, w2, rows * s3 * 4) ||
+        overlaps(idx_out, o4, w_out, o4))
+        return GM_ERR_ALIAS;
+    return hip_status(gm::launch_ser_forward(B, n, hkv, idx1, w1, s2, idx2, w2, s3, idx_out,
+                                             w_out, s1, stream));
+}
+
+gm_status gm_sea_forward(int B, int n, int hq, int hkv, int d, gm_dtype dt, float scale,
+                         const void* q, const void* k, const void* v, const int32_t* idx,
+                         const float* w, int s1, void* o, hipStream_t stream) {
+    gm_status st = check_sea(B, n, hq, hkv, d, dt, s1);
+    if (st != GM_OK) return st;
+    if (empty(B, n, hkv)) return GM_OK;
+    if (!q || !k || !v || !o) return GM_ERR_NULL;
+    if ((st = check_edge_ptrs(idx, w)) != GM_OK) return st;
+    if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16))
+        return GM_ERR_ALIGN;
+    const size_t es = dt == GM_BF16 ? 2 : 4;
+    const size_t qb = (size_t)B * n * hq * d * es, kb = (size_t)B * n * hkv * d * es;
+    if (overlaps(o, qb, q, qb) || overlaps(o, qb, k, kb) || overlaps(o, qb, v, kb) ||
+        overlaps(o, qb, idx, (size_t)B * n * hkv * s1 * 4) ||
+        overlaps(o, qb, w, (size_t)B * n * hkv * s1 * 4))
+        return GM_ERR_ALIAS;
+    return hip_status(gm::launch_sea_forward(B, n, hq, hkv, d, dt == GM_BF16, scale, q, k, v,
+                                             idx, w, s1, o, stream));
+}
+
+gm_status gm_sea_backward(int B, int n, int hq, int hkv, int d, gm_dtype dt, float scale,
+                          const void* q, const void* k, const void* v, const int32_t* idx,
+                          const float* w, int s1, const void* dout, float* dq, float* dk,
+                          float* dv, float* dw, hipStream_t stream) {
+    gm_status st = check_sea(B, n, hq, hkv, d, dt, s1);
+    if (st != GM_OK) return st;
+    if (empty(B, n, hkv)) return GM_OK;
+    if (!q || !k || !v || !dout || !dq || !dk || !dv || !dw) return GM_ERR_NULL;
+    if ((st = check_edge_ptrs(idx, w)) != GM_OK) return st;
+    if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(dout, 16) ||
+        !aligned(dq, 16) || !aligned(dk, 16) || !aligned(dv, 16) || !aligned(dw, 4))
+        return GM_ERR_ALIGN;
+    const size_t es = dt == GM_BF16 ? 2 : 4;
+    const size_t nq = (size_t)B * n * hq * d, nk = (size_t)B * n * hkv * d;
+    const size_t ne = (size_t)B * n * hkv * s1;
+    const void* ins[6] = {q, k, v, dout, idx, w};
+    const size_t inb[6] = {nq * es, nk * es, nk * es, nq * es, ne * 4, ne * 4};
+    const void* outs[4] = {dq, dk, dv, dw};
+    const size_t outb[4] = {nq * 4, nk * 4, nk * 4, ne * 4};
+    for (int a = 0; a < 4; ++a) {
+        for (int b = 0; b < 6; ++b)
+            if (overlaps(outs[a], outb[a], ins[b], inb[b])) return GM_ERR_ALIAS;
+        for (int b = a + 1; b < 4; ++b)
+            if (overlaps(outs[a], outb[a], outs[b], outb[b])) return GM_ERR_ALIAS;
+    }
+    return hip_status(gm::launch_sea_backward(B, n, hq, hkv, d, dt == GM_BF16, scale, q, k, v,
+                                              idx, w, s1, dout, dq, dk, dv, dw, stream));
+}
+
+size_t gm_ser_backward_workspace_bytes(int B, int n, int hkv, int s2, int s3, int aliased) {
+    if (check_units(B, n, hkv) != GM_OK || s2 < 1 || s3 < 1) return 0;
+    const size_t rows = (size_t)B * n * hkv;
+    const size_t a = rows * s2 * sizeof(double);
+    return aliased ? a : a + rows * s3 * sizeof(double);
+}
+
+gm_status gm_ser_backward(int B, int n, int hkv, const int32_t* idx1, const float* w1, int s2,
+                          const int32_t* idx2, const float* w2, int s3,
+                          const int32_t* idx_out, const float* w_out, int s1,
+                          const float* dw_out, float* dw1, float* dw2, void* workspace,
+                          size_t workspace_bytes, hipStream_t stream) {
+    gm_status st = check_ser(B, n, hkv, s1, s2, s3);
+    if (st != GM_OK) return st;
+    if (empty(B, n, hkv)) return GM_OK;
+    if ((st = check_edge_ptrs(idx1, w1)) != GM_OK) return st;
+    if ((st = check_edge_ptrs(idx2, w2)) != GM_OK) return st;
+    if ((st = check_edge_ptrs(idx_out, w_out)) != GM_OK) return st;
+    if (!dw_out || !dw1 || !dw2) return GM_ERR_NULL;
+    if (!aligned(dw_out, 4) || !aligned(dw1, 4) || !aligned(dw2, 4)) return GM_ERR_ALIGN;
+    const bool aliased = dw1 == dw2;
+    if (aliased && s2 != s3) return GM_ERR_ALIAS;
+    const size_t need = gm_ser_backward_workspace_bytes(B, n, hkv, s2, s3, aliased);
+    if (!workspace || workspace_bytes < need) return GM_ERR_WORKSPACE;
+    if (!aligned(workspace, 8)) return GM_ERR_ALIGN;
+    const size_t rows = (size_t)B * n * hkv;
+    const void* ins[7] = {idx1, w1, idx2, w2, idx_out, w_out, dw_out};
+    const size_t inb[7] = {rows * s2 * 4, rows * s2 * 4, rows * s3 * 4, rows * s3 * 4,
+                           rows * s1 * 4, rows * s1 * 4, rows * s1 * 4};
+    const void* outs[3] = {dw1, dw2, workspace};
+    const size_t outb[3] = {rows * s2 * 4, rows * s3 * 4, need};
+    for (int a = 0; a < 3; ++a) {
+        for (int b = 0; b < 7; ++b)
+            if (overlaps(outs[a], outb[a], ins[b], inb[b])) return GM_ERR_ALIAS;
+        for (int b = a + 1; b < 3; ++b) {
+            if (a == 0 && b == 1 && aliased) continue;
+            if (overlaps(outs[a], outb[a], outs[b], outb[b])) return GM_ERR_ALIAS;
+        }
+    }
+    double* ws1 = static_cast<double*>(workspace);
+    double* ws2 = aliased ? ws1 : ws1 + rows * s2;
+    return hip_status(gm::launch_ser_backward(B, n, hkv, idx1, w1, s2, idx2, w2, s3, idx_out,
+                                              w_out, s1, dw_out, dw1, dw2, ws1, ws2, stream));
+}
+
+gm_status gm_check_edges(int B, int n, int hkv, const int32_t* idx, const float* w, int s,
+                         unsigned long long* counts, hipStream_t stream) {
+    gm_status st = check_units(B, n, hkv);
+    if (st != GM_OK) return st;
+    if (s < 1) return GM_ERR_SHAPE;
+    if (empty(B, n, hkv)) return GM_OK;
+    if ((st = check_edge_ptrs(idx, w)) != GM_OK) return st;
+    if (!counts) return GM_ERR_NULL;
+    if (!aligned(counts, 8)) return GM_ERR_ALIGN;
+    return hip_status(gm::launch_check_edges(B, n, hkv, idx, w, s, counts, stream));
+}
+
+}  // extern "C"

@@ -1,0 +1,46 @@
+// Internal launch interface between the C ABI (gm_api.hip) and the kernels.
+// Host code only; argument checking has already happened when these run.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace gm {
+
+// Lane team of one unit in the SEA kernels: R lanes hold one d-row (16 bytes
+// each), P slots are handled side by side, team = R * P lanes (<= 64), and
+// the s slots are walked in nchunk chunks of P.
+struct TeamShape {
+    int R, P, team, nchunk, log2R;
+};
+TeamShape sea_team(int d, int elem_bytes, int s);
+
+hipError_t launch_ser_forward(int B, int n, int hkv, const int32_t* idx1, const float* w1,
+                              int s2, const int32_t* idx2, const float* w2, int s3,
+                              int32_t* idx_out, float* w_out, int s1, hipStream_t st);
+
+hipError_t launch_sea_forward(int B, int n, int hq, int hkv, int d, bool bf16, float scale,
+                              const void* q, const void* k, const void* v,
+                              const int32_t* idx, const float* w, int s, void* o,
+                              hipStream_t st);
+
+hipError_t launch_sea_backward(int B, int n, int hq, int hkv, int d, bool bf16, float scale,
+                               const void* q, const void* k, const void* v,
+                               const int32_t* idx, const float* w, int s, const void* dout,
+                               float* dq, float* dk, float* dv, float* dw, hipStream_t st);
+
+hipError_t launch_ser_backward(int B, int n, int hkv, const int32_t* idx1, const float* w1,
+                               int s2, const int32_t* idx2, const float* w2, int s3,
+                               const int32_t* idx_out, const float* w_out, int s1,
+                               const float* dw_out, float* dw1, float* dw2, double* ws1,
+                               double* ws2, hipStream_t st);
+
+hipError_t launch_check_edges(int B, int n, int hkv, const int32_t* idx, const float* w, int s,
+                              unsigned long long* counts, hipStream_t st);
+
+// Zero `count` floats (or doubles) with a fill kernel (graph-capture safe).
+hipError_t launch_zero_f32(float* p, size_t count, hipStream_t st);
+hipError_t launch_zero_f64(double* p, size_t count, hipStream_t st);
+
+}  // namespace gm

@@ -1,0 +1,294 @@
+// Sparse edge referral (SER), forward and backward, for gfx950.
+//
+// Forward (ai.info "Graph Machine: Towards Better Pretraining via Edges",
+// Key Contributions 3: A' = Sparsify_s1(A1 A2) over the up-to s2*s3 two-hop
+// candidates; Methodology: the first leg's indices fetch the second leg's
+// indices and weights, hard top-s selection; rit.work article: paths to the
+// same address are merged and the heaviest kept).
+//
+// One lane per path: a team of L = pow2(s2*s3) lanes per unit (b, i, h);
+// lane a*s3 + c follows leg-1 slot a to token j and reads leg-2 slot c of
+// row j.  The whole row fits one wavefront, so the merge and the top-s1 run
+// in registers with cross-lane shuffles:
+//   merge  each lane scans the team's lanes in path order (a, c) and sums,
+//          in double starting from 0, the path weights (exact fp32*fp32
+//          products) whose target equals its own; the lowest such lane owns
+//          the target.  This is the order and precision of the definition,
+//          so the fp32-rounded weight is bit-exact.
+//   rank   an owner's rank is the number of owners with a larger positive
+//          weight, or the same weight and a lower index; ranks < s1 write
+//          their slot.  A ballot counts the owners; the remaining slots get
+//          the padding edge (0, 0.0f).
+//
+// Backward (ai.info Methodology: only retained weights get gradients): for
+// each path whose target is a retained slot t (w_out_t > 0) and whose two
+// leg weights are positive, dw1[i,a] += dw_out_t w2[j,c] and
+// dw2[j,c] += dw_out_t w1[i,a].  Contributions are added in fp64 with
+// atomics into a workspace (dw2 lands in other tokens' rows), then rounded
+// once to fp32.  When dw1 and dw2 alias, one workspace receives both.
+#include "gm_common.h"
+#include "gm_internal.h"
+
+namespace gm {
+namespace {
+
+struct SerArgs {
+    const int32_t* idx1;
+    const float* w1;
+    const int32_t* idx2;
+    const float* w2;
+    int32_t* idx_out;
+    float* w_out;
+    int n, hkv, s1, s2, s3, U;
+};
+
+template <int L>
+__global__ __launch_bounds__(kBlock) void ser_fwd_kernel(SerArgs a) {
+    const int lane = threadIdx.x & (kWave - 1);
+    const int sub = lane & (L - 1);
+    const int base = lane & ~(L - 1);
+    const long long gunit = ((long long)blockIdx.x * kBlock + threadIdx.x) / L;
+    if (gunit >= a.U) return;  // whole team leaves together
+    const int unit = (int)gunit;
+    const int ncand = a.s2 * a.s3;
+    const bool valid = sub < ncand;
+    int m = -1;
+    double cw = 0.0;
+    if (valid) {
+        const int h = unit % a.hkv;
+        const int b = unit / a.hkv / a.n;
+        const int la = sub / a.s3;
+        const int lc = sub - la * a.s3;
+        const int j = a.idx1[(size_t)unit * a.s2 + la];
+        const float x = a.w1[(size_t)unit * a.s2 + la];
+        const size_t r2 = ((size_t)b * a.n + j) * a.hkv + h;
+        m = a.idx2[r2 * a.s3 + lc];
+        const float y = a.w2[r2 * a.s3 + lc];
+        cw = (double)x * (double)y;  // exact: 24-bit x 24-bit mantissas
+    }
+    // merge duplicate targets, summing in path order
+    double acc = 0.0;
+    bool owner = valid;
+#pragma unroll
+    for (int k = 0; k < L; ++k) {
+        const int mk = __shfl(m, base + k, kWave);
+        const double ck = __shfl(cw, base + k, kWave);
+        if (valid && mk == m) {
+            acc += ck;
+            if (k < sub) owner = false;
+        }
+    }
+    const float key = (float)acc;
+    const bool cand = owner && key > 0.0f;
+    // rank among candidates: larger weight first, then lower index
+    int rank = 0;
+#pragma unroll
+    for (int k = 0; k < L; ++k) {
+        const float kk = __shfl(key, base + k, kWave);
+        const int mk = __shfl(m, base + k, kWave);
+        const int ck = __shfl((int)cand, base + k, kWave);
+        if (ck && (kk > key || (kk == key && mk < m))) ++rank;
+    }
+    const size_t ob = (size_t)unit * a.s1;
+    if (cand && rank < a.s1) {
+        a.idx_out[ob + rank] = m;
+        a.w_out[ob + rank] = key;
+    }
+    const unsigned long long bal = __ballot(cand);
+    const unsigned long long mask = (L == 64) ? ~0ull : (((1ull << L) - 1ull) << base);
+    const int nd = __popcll(bal & mask);
+    for (int p = nd + sub; p < a.s1; p += L) {
+        a.idx_out[ob + p] = 0;
+        a.w_out[ob + p] = 0.0f;
+    }
+}
+
+struct SerBwdArgs {
+    const int32_t* idx1;
+    const float* w1;
+    const int32_t* idx2;
+    const float* w2;
+    const int32_t* idx_out;
+    const float* w_out;
+    const float* dw_out;
+    double* ws1;
+    double* ws2;
+    int n, hkv, s1, s2, s3, U;
+};
+
+template <int L>
+__global__ __launch_bounds__(kBlock) void ser_bwd_kernel(SerBwdArgs a) {
+    const int lane = threadIdx.x & (kWave - 1);
+    const int sub = lane & (L - 1);
+    const long long gunit = ((long long)blockIdx.x * kBlock + threadIdx.x) / L;
+    if (gunit >= a.U) return;
+    const int unit = (int)gunit;
+    if (sub >= a.s2 * a.s3) return;   // no cross-lane traffic below
+    const int h = unit % a.hkv;
+    const int b = unit / a.hkv / a.n;
+    const int la = sub / a.s3;
+    const int lc = sub - la * a.s3;
+    const float x = a.w1[(size_t)unit * a.s2 + la];
+    if (!(x > 0.0f)) return;
+    const int j = a.idx1[(size_t)unit * a.s2 + la];
+    const size_t r2 = ((size_t)b * a.n + j) * a.hkv + h;
+    const int m = a.idx2[r2 * a.s3 + lc];
+    const float y = a.w2[r2 * a.s3 + lc];
+    if (!(y > 0.0f)) return;
+    double g = 0.0;
+    bool hit = false;
+    const size_t ob = (size_t)unit * a.s1;
+    for (int t = 0; t < a.s1; ++t) {
+        if (a.w_out[ob + t] > 0.0f && a.idx_out[ob + t] == m) {
+            g += (double)a.dw_out[ob + t];
+            hit = true;
+        }
+    }
+    if (!hit) return;
+    unsafeAtomicAdd(a.ws1 + (size_t)unit * a.s2 + la, g * (double)y);
+    unsafeAtomicAdd(a.ws2 + r2 * a.s3 + lc, g * (double)x);
+}
+
+__global__ __launch_bounds__(kBlock) void round_f64_kernel(const double* src, float* dst,
+                                                           size_t count) {
+    for (size_t e = (size_t)blockIdx.x * kBlock + threadIdx.x; e < count;
+         e += (size_t)gridDim.x * kBlock)
+        dst[e] = (float)src[e];
+}
+
+__global__ __launch_bounds__(kBlock) void zero_f32_kernel(float* p, size_t count) {
+    // float4 stores when 16-byte aligned, plain stores otherwise
+    const size_t n4 = ((uintptr_t)p & 15u) ? 0 : count / 4;
+    float4* p4 = reinterpret_cast<float4*>(p);
+    const size_t stride = (size_t)gridDim.x * kBlock;
+    for (size_t e = (size_t)blockIdx.x * kBlock + threadIdx.x; e < n4; e += stride)
+        p4[e] = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (size_t e = n4 * 4 + (size_t)blockIdx.x * kBlock + threadIdx.x; e < count; e += stride)
+        p[e] = 0.f;
+}
+
+__global__ __launch_bounds__(kBlock) void zero_f64_kernel(double* p, size_t count) {
+    const size_t stride = (size_t)gridDim.x * kBlock;
+    for (size_t e = (size_t)blockIdx.x * kBlock + threadIdx.x; e < count; e += stride)
+        p[e] = 0.0;
+}
+
+__global__ __launch_bounds__(kBlock) void check_edges_kernel(int n, int hkv, const int32_t* idx,
+                                                             const float* w, int s,
+                                                             size_t count,
+                                                             unsigned long long* counts) {
+    unsigned long long bad = 0, live = 0;
+    for (size_t e = (size_t)blockIdx.x * kBlock + threadIdx.x; e < count;
+         e += (size_t)gridDim.x * kBlock) {
+        const size_t unit = e / s;
+        const int i = (int)((unit / hkv) % n);
+        const int j = idx[e];
+        const float wt = w[e];
+        if (j < 0 || j > i || !(wt >= 0.0f) || wt == INFINITY) ++bad;
+        if (wt > 0.0f) ++live;
+    }
+    for (int m = 32; m > 0; m >>= 1) {
+        bad += __shfl_xor(bad, m, kWave);
+        live += __shfl_xor(live, m, kWave);
+    }
+    if ((threadIdx.x & (kWave - 1)) == 0) {
+        if (bad) atomicAdd(counts, bad);
+        if (live) atomicAdd(counts + 1, live);
+    }
+}
+
+unsigned grid_for(size_t work, unsigned cap) {
+    size_t blocks = (work + kBlock - 1) / kBlock;
+    if (blocks < 1) blocks = 1;
+    return (unsigned)(blocks < cap ? blocks : cap);
+}
+
+template <int L>
+hipError_t run_fwd(const SerArgs& a, hipStream_t st) {
+    const long long threads = (long long)a.U * L;
+    hipLaunchKernelGGL((ser_fwd_kernel<L>), dim3((unsigned)((threads + kBlock - 1) / kBlock)),
+                       dim3(kBlock), 0, st, a);
+    return hipGetLastError();
+}
+
+template <int L>
+hipError_t run_bwd(const SerBwdArgs& a, hipStream_t st) {
+    const long long threads = (long long)a.U * L;
+    hipLaunchKernelGGL((ser_bwd_kernel<L>), dim3((unsigned)((threads + kBlock - 1) / kBlock)),
+                       dim3(kBlock), 0, st, a);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_zero_f32(float* p, size_t count, hipStream_t st) {
+    if (!count) return hipSuccess;
+    hipLaunchKernelGGL(zero_f32_kernel, dim3(grid_for(count / 4 + 1, 8192)), dim3(kBlock), 0, st,
+                       p, count);
+    return hipGetLastError();
+}
+
+hipError_t launch_zero_f64(double* p, size_t count, hipStream_t st) {
+    if (!count) return hipSuccess;
+    hipLaunchKernelGGL(zero_f64_kernel, dim3(grid_for(count, 8192)), dim3(kBlock), 0, st, p,
+                       count);
+    return hipGetLastError();
+}
+
+hipError_t launch_ser_forward(int B, int n, int hkv, const int32_t* idx1, const float* w1,
+                              int s2, const int32_t* idx2, const float* w2, int s3,
+                              int32_t* idx_out, float* w_out, int s1, hipStream_t st) {
+    SerArgs a{idx1, w1, idx2, w2, idx_out, w_out, n, hkv, s1, s2, s3, B * n * hkv};
+    switch (pow2_ceil(s2 * s3)) {
+        case 1: return run_fwd<1>(a, st);
+        case 2: return run_fwd<2>(a, st);
+        case 4: return run_fwd<4>(a, st);
+        case 8: return run_fwd<8>(a, st);
+        case 16: return run_fwd<16>(a, st);
+        case 32: return run_fwd<32>(a, st);
+        case 64: return run_fwd<64>(a, st);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+hipError_t launch_ser_backward(int B, int n, int hkv, const int32_t* idx1, const float* w1,
+                               int s2, const int32_t* idx2, const float* w2, int s3,
+                               const int32_t* idx_out, const float* w_out, int s1,
+                               const float* dw_out, float* dw1, float* dw2, double* ws1,
+                               double* ws2, hipStream_t st) {
+    const size_t rows = (size_t)B * n * hkv;
+    const bool aliased = dw1 == dw2;
+    hipError_t e = launch_zero_f64(ws1, rows * s2, st);
+    if (e == hipSuccess && !aliased) e = launch_zero_f64(ws2, rows * s3, st);
+    if (e != hipSuccess) return e;
+    SerBwdArgs a{idx1, w1, idx2, w2, idx_out, w_out, dw_out, ws1, aliased ? ws1 : ws2,
+                 n, hkv, s1, s2, s3, (int)rows};
+    switch (pow2_ceil(s2 * s3)) {
+        case 1: e = run_bwd<1>(a, st); break;
+        case 2: e = run_bwd<2>(a, st); break;
+        case 4: e = run_bwd<4>(a, st); break;
+        case 8: e = run_bwd<8>(a, st); break;
+        case 16: e = run_bwd<16>(a, st); break;
+        case 32: e = run_bwd<32>(a, st); break;
+        case 64: e = run_bwd<64>(a, st); break;
+        default: return hipErrorInvalidValue;
+    }
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(round_f64_kernel, dim3(grid_for(rows * s2, 8192)), dim3(kBlock), 0, st,
+                       (const double*)ws1, dw1, rows * s2);
+    if (!aliased)
+        hipLaunchKernelGGL(round_f64_kernel, dim3(grid_for(rows * s3, 8192)), dim3(kBlock), 0, st,
+                           (const double*)ws2, dw2, rows * s3);
+    return hipGetLastError();
+}
+
+hipError_t launch_check_edges(int B, int n, int hkv, const int32_t* idx, const float* w, int s,
+                              unsigned long long* counts, hipStream_t st) {
+    const size_t count = (size_t)B * n * hkv * s;
+    if (!count) return hipSuccess;
+    hipLaunchKernelGGL(check_edges_kernel, dim3(grid_for(count, 4096)), dim3(kBlock), 0, st, n,
+                       hkv, idx, w, s, count, counts);
+    return hipGetLastError();
+}
+
+}  // namespace gm

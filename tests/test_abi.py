@@ -1,0 +1,113 @@
+"""The C-ABI library without a GPU: it loads, exports every call that
+include/gm.h declares, and rejects bad arguments on the host before any
+launch (these calls never reach HIP, so they run on a CPU-only machine)."""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+
+import pytest
+
+import sparse_dynamic_routing_amd as gm
+from sparse_dynamic_routing_amd import binding
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "gm.h")
+
+OK, NULL, SHAPE, UNSUP, WS, HIP, ALIGN, ALIAS = range(8)
+
+
+def declared():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(gm_[a-z_0-9]+)\s*\(", src)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return gm.load()
+
+
+def test_library_exports_every_declared_call(lib):
+    names = declared()
+    assert names, "no declarations found in gm.h"
+    assert set(names) == set(binding.EXPORTS)
+    for name in names:
+        assert hasattr(lib, name), name
+    assert lib.gm_abi_version() == 1
+
+
+def test_status_strings(lib):
+    for code in range(8):
+        assert lib.gm_status_string(code)
+    assert b"unknown" in lib.gm_status_string(99)
+
+
+P = ctypes.c_void_p
+
+
+def fake(addr):
+    """A non-NULL pointer value that is never dereferenced (the host checks
+    reject the call before any launch)."""
+    return P(addr)
+
+
+def test_ser_forward_argument_checks(lib):
+    a = fake(0x10000)
+    f = lib.gm_ser_forward
+    assert f(-1, 4, 1, a, a, 2, a, a, 2, a, a, 2, None) == SHAPE
+    assert f(1, 4, 1, a, a, 2, a, a, 2, a, a, 0, None) == UNSUP       # s1 = 0
+    assert f(1, 4, 1, a, a, 9, a, a, 8, a, a, 4, None) == UNSUP       # 72 candidates
+    assert f(1, 4, 1, a, a, 2, a, a, 2, a, a, 65, None) == UNSUP
+    assert f(1, 4, 1, None, a, 2, a, a, 2, a, a, 2, None) == NULL
+    assert f(1, 4, 1, fake(0x10002), a, 2, a, a, 2, fake(0x20000), fake(0x30000), 2,
+             None) == ALIGN
+    assert f(1, 4, 1, a, fake(0x40000), 2, a, fake(0x40000), 2, a, fake(0x50000), 2,
+             None) == ALIAS                                           # idx_out on idx1
+    assert f(0, 4, 1, None, None, 2, None, None, 2, None, None, 2, None) == OK  # empty
+    assert f(70000, 70000, 1, a, a, 2, a, a, 2, a, a, 2, None) == SHAPE  # > 2^31 units
+
+
+def test_sea_argument_checks(lib):
+    a, b, c = fake(0x100000), fake(0x200000), fake(0x300000)
+    i, w, o = fake(0x400000), fake(0x500000), fake(0x600000)
+    f = lib.gm_sea_forward
+    args = lambda hq=16, hkv=8, d=128, dt=1, s=4, q=a, oo=o: (  # noqa: E731
+        8, 4096, hq, hkv, d, dt, 0.1, q, b, c, i, w, s, oo, None)
+    assert f(*args(hq=12)) == UNSUP          # hq % hkv != 0
+    assert f(*args(hq=24)) == UNSUP          # 3 query heads per KV head
+    assert f(*args(d=96)) == UNSUP
+    assert f(*args(d=512)) == UNSUP
+    assert f(*args(dt=7)) == UNSUP
+    assert f(*args(s=0)) == UNSUP
+    assert f(*args(s=65)) == UNSUP
+    assert f(*args(q=None)) == NULL
+    assert f(*args(q=fake(0x100008))) == ALIGN
+    assert f(*args(oo=a)) == ALIAS           # o on q
+    g = lib.gm_sea_backward
+    bargs = [8, 4096, 16, 8, 128, 1, 0.1, a, b, c, i, w, 4, fake(0x700000),
+             fake(0x800000), fake(0x900000), fake(0xA00000), fake(0xB00000), None]
+    bad = list(bargs); bad[15] = None
+    assert g(*bad) == NULL
+    bad = list(bargs); bad[15] = fake(0x900004)
+    assert g(*bad) == ALIGN
+    bad = list(bargs); bad[14] = b            # dq on k
+    assert g(*bad) == ALIAS
+
+
+def test_ser_backward_workspace_checks(lib):
+    need = lib.gm_ser_backward_workspace_bytes(8, 4096, 8, 4, 4, 1)
+    assert need == 8 * 4096 * 8 * 4 * 8
+    assert lib.gm_ser_backward_workspace_bytes(8, 4096, 8, 4, 4, 0) == 2 * need
+    ptrs = [fake(0x1000000 * (k + 1)) for k in range(10)]
+    args = [8, 4096, 8, ptrs[0], ptrs[1], 4, ptrs[2], ptrs[3], 4, ptrs[4], ptrs[5], 4,
+            ptrs[6], ptrs[7], ptrs[7], ptrs[8], need - 8, None]
+    assert lib.gm_ser_backward(*args) == WS
+    args[16] = need; args[15] = None
+    assert lib.gm_ser_backward(*args) == WS
+    args[15] = fake(0x9000004)
+    assert lib.gm_ser_backward(*args) == ALIGN
+    args[15] = ptrs[8]
+    args[5] = 2                                # aliased outputs with s2 != s3
+    assert lib.gm_ser_backward(*args) == ALIAS

@@ -1,0 +1,196 @@
+"""GPU parity over shapes, dtypes and the degenerate cases of the method,
+through the C ABI, against the oracle on every output element.
+
+Sizes are small (the oracle finishes in well under a second) but span
+several workgroups and a ragged tail (token counts that are not a multiple
+of the units per workgroup).
+"""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+import cases
+import oracle
+import sparse_dynamic_routing_amd as gm
+from gpu_util import TOL, assert_close, assert_ser_match, dev, host, say
+
+pytestmark = pytest.mark.gpu
+
+SEA_SHAPES = [
+    # dtype, d, G, s, n
+    (torch.bfloat16, 128, 2, 4, 67),    # the measured layer's geometry
+    (torch.bfloat16, 128, 2, 2, 67),    # retrieving 2 per KV head
+    (torch.bfloat16, 128, 1, 3, 45),    # slot count not a power of two
+    (torch.bfloat16, 128, 4, 8, 33),    # two slot chunks per unit
+    (torch.bfloat16, 128, 2, 5, 33),    # ragged second chunk
+    (torch.bfloat16, 64, 8, 4, 40),
+    (torch.bfloat16, 256, 2, 4, 29),    # 32 lanes per row
+    (torch.bfloat16, 16, 16, 6, 50),    # 2 lanes per row, many units per wave
+    (torch.bfloat16, 32, 2, 64, 21),    # the widest slot count
+    (torch.float32, 16, 2, 2, 64),      # the tiny preset's geometry
+    (torch.float32, 128, 2, 4, 37),
+    (torch.float32, 256, 1, 3, 19),     # 64 lanes per row: one slot per chunk
+    (torch.float32, 32, 4, 9, 41),
+]
+
+
+def _sea_inputs(rng, dtype, d, G, s, n, B=2, hkv=2, pad=0.15, dead=0.1):
+    hq = G * hkv
+    q = torch.from_numpy(rng.standard_normal((B, n, hq, d), dtype=np.float32)).to(dtype)
+    k = torch.from_numpy(rng.standard_normal((B, n, hkv, d), dtype=np.float32)).to(dtype)
+    v = torch.from_numpy(rng.standard_normal((B, n, hkv, d), dtype=np.float32)).to(dtype)
+    do = torch.from_numpy(rng.standard_normal((B, n, hq, d), dtype=np.float32)).to(dtype)
+    idx, w = cases.edges(rng, B, n, hkv, s, pad_frac=pad, dead_frac=dead)
+    return q, k, v, do, idx, w
+
+
+@pytest.mark.parametrize("dtype,d,G,s,n", SEA_SHAPES,
+                         ids=[f"{str(c[0])[6:]}-d{c[1]}-G{c[2]}-s{c[3]}-n{c[4]}" for c in SEA_SHAPES])
+def test_sea_forward_backward_shapes(dtype, d, G, s, n):
+    say(f"case sea dtype={dtype} d={d} G={G} s={s} n={n}")
+    rng = np.random.default_rng(d * 1000 + G * 100 + s * 10 + n)
+    q, k, v, do, idx, w = _sea_inputs(rng, dtype, d, G, s, n)
+    o = gm.sea_forward(dev(q), dev(k), dev(v), dev(idx), dev(w))
+    dq, dk, dv, dw = gm.sea_backward(dev(q), dev(k), dev(v), dev(idx), dev(w), dev(do))
+    torch.cuda.synchronize()
+    orc = oracle.get()
+    X = TOL[dtype]
+    assert_close("o", host(o), orc.sea_forward(q, k, v, idx, w), X)
+    rdq, rdk, rdv, rdw = orc.sea_backward(q, k, v, idx, w, do)
+    assert_close("dq", host(dq), rdq, X)
+    assert_close("dk", host(dk), rdk, X)
+    assert_close("dv", host(dv), rdv, X)
+    assert_close("dw", host(dw), rdw, X)
+
+
+def test_sea_scale_argument_and_all_padding_rows():
+    """A caller-chosen scale, rows whose slots are all padding (o = 0 and no
+    gradient) and token 0 (every edge points at itself)."""
+    rng = np.random.default_rng(5)
+    q, k, v, do, idx, w = _sea_inputs(rng, torch.float32, 64, 2, 4, 30, pad=0.0, dead=0.0)
+    idx[:, 7] = 0; w[:, 7] = 0.0
+    idx[0, 11, 1] = 0; w[0, 11, 1] = 0.0
+    o = gm.sea_forward(dev(q), dev(k), dev(v), dev(idx), dev(w), scale=0.3)
+    grads = gm.sea_backward(dev(q), dev(k), dev(v), dev(idx), dev(w), dev(do), scale=0.3)
+    orc = oracle.get()
+    assert_close("o", host(o), orc.sea_forward(q, k, v, idx, w, scale=0.3), 1e-5)
+    for name, g, r in zip(("dq", "dk", "dv", "dw"), grads,
+                          orc.sea_backward(q, k, v, idx, w, do, scale=0.3)):
+        assert_close(name, host(g), r, 1e-5)
+    assert (host(o)[:, 7] == 0).all() and (host(grads[0])[:, 7] == 0).all()
+
+
+SER_SHAPES = [
+    # s1, s2, s3, n, ties
+    (4, 4, 4, 70, False),
+    (2, 4, 4, 70, True),      # the narrower budget: top-2 of 16
+    (4, 4, 4, 70, True),      # exact ties everywhere: lower index first
+    (3, 3, 5, 45, False),     # 15 candidates in a 16-lane team
+    (8, 8, 8, 33, True),      # a full wave of 64 candidates
+    (6, 1, 3, 40, False),     # more slots than candidates: padding
+    (1, 2, 2, 129, False),    # 32 units per workgroup, ragged tail
+    (5, 2, 3, 50, True),
+    (64, 8, 8, 12, False),    # the widest output
+]
+
+
+@pytest.mark.parametrize("s1,s2,s3,n,ties", SER_SHAPES,
+                         ids=[f"s{c[0]}-{c[1]}x{c[2]}-n{c[3]}{'-ties' if c[4] else ''}" for c in SER_SHAPES])
+def test_ser_forward_backward_shapes(s1, s2, s3, n, ties):
+    say(f"case ser s1={s1} s2={s2} s3={s3} n={n} ties={ties}")
+    rng = np.random.default_rng(s1 * 1000 + s2 * 100 + s3 * 10 + n)
+    B, hkv = 2, 3
+    idx1, w1 = cases.edges(rng, B, n, hkv, s2, pad_frac=0.1, ties=ties, dead_frac=0.05)
+    idx2, w2 = cases.edges(rng, B, n, hkv, s3, pad_frac=0.1, ties=ties, dead_frac=0.05)
+    io, wo = gm.ser_forward(dev(idx1), dev(w1), dev(idx2), dev(w2), s1)
+    orc = oracle.get()
+    rio, rwo = orc.ser_forward(idx1, w1, idx2, w2, s1)
+    assert_ser_match(host(io), host(wo), rio, rwo)
+    np.testing.assert_array_equal(host(wo), rwo)
+    dwo = rng.standard_normal(rio.shape).astype(np.float32)
+    d1, d2 = gm.ser_backward(dev(idx1), dev(w1), dev(idx2), dev(w2), io, wo, dev(dwo))
+    r1, r2 = orc.ser_backward(idx1, w1, idx2, w2, rio, rwo, dwo)
+    assert_close("dw1", host(d1), r1, 1e-5)
+    assert_close("dw2", host(d2), r2, 1e-5)
+    if s2 == s3:
+        idx2, w2 = idx1, w1
+        io, wo = gm.ser_forward(dev(idx1), dev(w1), dev(idx1), dev(w1), s1)
+        rio, rwo = orc.ser_forward(idx1, w1, idx1, w1, s1)
+        assert_ser_match(host(io), host(wo), rio, rwo)
+        da, _ = gm.ser_backward(dev(idx1), dev(w1), dev(idx1), dev(w1), io, wo, dev(dwo),
+                                aliased=True)
+        ra, _ = orc.ser_backward(idx1, w1, idx1, w1, rio, rwo, dwo, aliased=True)
+        assert_close("dw (aliased legs)", host(da), ra, 1e-5)
+
+
+def test_single_token_and_empty_inputs():
+    """n = 1 (every edge is the padding token itself) and zero-size calls,
+    which launch nothing and return success."""
+    rng = np.random.default_rng(9)
+    q, k, v, do, idx, w = _sea_inputs(rng, torch.bfloat16, 128, 2, 4, 1, pad=0.0, dead=0.0)
+    assert (idx == 0).all()
+    o = gm.sea_forward(dev(q), dev(k), dev(v), dev(idx), dev(w))
+    orc = oracle.get()
+    assert_close("o (n=1)", host(o), orc.sea_forward(q, k, v, idx, w), 2e-2)
+    io, wo = gm.ser_forward(dev(idx), dev(w), dev(idx), dev(w), 4)
+    rio, rwo = orc.ser_forward(idx, w, idx, w, 4)
+    assert_ser_match(host(io), host(wo), rio, rwo)
+    for B, n in ((0, 16), (2, 0)):
+        e_i = torch.zeros((B, n, 2, 4), dtype=torch.int32, device="cuda")
+        e_w = torch.zeros((B, n, 2, 4), dtype=torch.float32, device="cuda")
+        qq = torch.zeros((B, n, 4, 128), dtype=torch.bfloat16, device="cuda")
+        kk = torch.zeros((B, n, 2, 128), dtype=torch.bfloat16, device="cuda")
+        gm.ser_forward(e_i, e_w, e_i, e_w, 4)
+        gm.sea_forward(qq, kk, kk, e_i, e_w)
+        gm.sea_backward(qq, kk, kk, e_i, e_w, qq)
+        gm.ser_backward(e_i, e_w, e_i, e_w, e_i, e_w, e_w, aliased=True)
+    torch.cuda.synchronize()
+
+
+def test_forward_calls_are_bitwise_deterministic():
+    rng = np.random.default_rng(10)
+    q, k, v, do, idx, w = _sea_inputs(rng, torch.bfloat16, 128, 2, 4, 500, B=4, pad=0, dead=0)
+    args = [dev(x) for x in (q, k, v, idx, w)]
+    a = gm.ser_forward(args[3], args[4], args[3], args[4], 4)
+    b = gm.ser_forward(args[3], args[4], args[3], args[4], 4)
+    assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
+    o1 = gm.sea_forward(*args[:3], *a)
+    o2 = gm.sea_forward(*args[:3], *a)
+    assert torch.equal(o1, o2)
+
+
+def test_check_edges_counts():
+    rng = np.random.default_rng(11)
+    idx, w = cases.edges(rng, 2, 100, 3, 4, pad_frac=0.2)
+    bad, live = gm.check_edges(dev(idx), dev(w))
+    assert bad == 0 and live == int((w > 0).sum())
+    idx[1, 5, 2, 1] = 6          # index beyond its own token
+    w[0, 9, 0, 3] = -1.0         # negative weight
+    w[0, 10, 0, 0] = np.inf
+    bad, _ = gm.check_edges(dev(idx), dev(w))
+    assert bad == 3
+
+
+def test_errors_are_reported_before_any_launch():
+    idx = torch.zeros((1, 8, 2, 4), dtype=torch.int32, device="cuda")
+    w = torch.zeros((1, 8, 2, 4), dtype=torch.float32, device="cuda")
+    q = torch.zeros((1, 8, 4, 128), dtype=torch.bfloat16, device="cuda")
+    k = torch.zeros((1, 8, 2, 128), dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(gm.GMError, match="ALIAS"):
+        gm.gm_ser_forward(idx, w, idx, w, idx, w)
+    with pytest.raises(gm.GMError, match="UNSUPPORTED"):
+        gm.ser_forward(torch.zeros((1, 8, 2, 9), dtype=torch.int32, device="cuda"),
+                       torch.zeros((1, 8, 2, 9), dtype=torch.float32, device="cuda"),
+                       torch.zeros((1, 8, 2, 9), dtype=torch.int32, device="cuda"),
+                       torch.zeros((1, 8, 2, 9), dtype=torch.float32, device="cuda"), 4)
+    flat = torch.zeros(q.numel() + 8, dtype=torch.bfloat16, device="cuda")
+    misaligned = flat[1:1 + q.numel()].view(q.shape)      # 2 bytes past a 16-byte boundary
+    assert misaligned.is_contiguous() and misaligned.data_ptr() % 16 == 2
+    with pytest.raises(gm.GMError, match="ALIGN"):
+        gm.gm_sea_forward(misaligned, k, k, idx, w, q)
+    with pytest.raises(gm.GMError, match="UNSUPPORTED"):
+        gm.sea_forward(torch.zeros((1, 8, 6, 128), dtype=torch.bfloat16, device="cuda"),
+                       k, k, idx, w)
+    torch.cuda.synchronize()
