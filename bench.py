@@ -85,13 +85,14 @@ class Pass:
         self.dwa = torch.empty(es, **f32)
         self.dA = torch.empty(self.idx.shape, **f32)
         self.ws = gm.ser_workspace(self.idx, self.idx, aliased=True)
+        self.ws_sea = gm.sea_workspace(self.q, self.ia)
 
     def calls(self):
         return [
             lambda: gm.gm_ser_forward(self.idx, self.w, self.idx, self.w, self.ia, self.wa),
             lambda: gm.gm_sea_forward(self.q, self.k, self.v, self.ia, self.wa, self.o),
             lambda: gm.gm_sea_backward(self.q, self.k, self.v, self.ia, self.wa, self.dout,
-                                       self.dq, self.dk, self.dv, self.dwa),
+                                       self.dq, self.dk, self.dv, self.dwa, self.ws_sea),
             lambda: gm.gm_ser_backward(self.idx, self.w, self.idx, self.w, self.ia, self.wa,
                                        self.dwa, self.dA, self.dA, self.ws),
         ]

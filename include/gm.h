@@ -37,8 +37,8 @@
  *     edge pointers 4-byte aligned.
  *   - Determinism: gm_ser_forward and gm_sea_forward are bitwise
  *     deterministic.  gm_ser_backward accumulates in fp64 and rounds once.
- *     gm_sea_backward scatters dk/dv with fp32 atomic adds, so their last
- *     bits may vary between runs.
+ *     gm_sea_backward sums each dk/dv row over its incoming edges in an
+ *     order that may vary, so their last bits may vary between runs.
  */
 #ifndef GM_H
 #define GM_H
@@ -103,22 +103,35 @@ gm_status gm_sea_forward(int B, int n, int hq, int hkv, int d, gm_dtype dt,
                          hipStream_t stream);
 
 /*
+ * Bytes of device workspace gm_sea_backward needs for these sizes: per-edge
+ * softmax coefficients, the in-degree of every K/V row, row offsets and the
+ * reverse (target-sorted) edge list.
+ */
+size_t gm_sea_backward_workspace_bytes(int B, int n, int hq, int hkv, int s1);
+
+/*
  * Sparse edge attention, backward: chain rule of gm_sea_forward with the
  * indices held fixed (rit.work: indices get no gradient, learning goes
  * through the soft edge weights).
  *   in   q, k, v, idx, w, s1, scale as for the forward; dout [B][n][hq][d] dt
  *   out  dq [B][n][hq][d] fp32, dk, dv [B][n][hkv][d] fp32,
  *        dw [B][n][hkv][s1] fp32; no output may overlap an input.
+ *   ws   device workspace of gm_sea_backward_workspace_bytes(...) bytes,
+ *        256-byte aligned; its contents on entry do not matter.
  * With g_t = dout.v[idx_t], gbar = sum p_t g_t, dl_t = p_t (g_t - gbar):
  * dq = scale sum_t dl_t k[idx_t]; dk[idx_t] += scale dl_t q;
  * dv[idx_t] += p_t dout; dw_t = sum over the group's query heads of
- * dl_t / w_t.  Padding slots (w = 0) get and pass no gradient.
+ * dl_t / w_t.  Padding slots (w = 0) get and pass no gradient.  dk and dv
+ * are reduced per K/V row over its incoming edges (a target-sorted pass,
+ * no float atomics); the order of a row's edges may vary between runs.
+ * Also requires B*n*hkv*s1 < 2^31.
  */
 gm_status gm_sea_backward(int B, int n, int hq, int hkv, int d, gm_dtype dt,
                           float scale, const void* q, const void* k, const void* v,
                           const int32_t* idx, const float* w, int s1,
                           const void* dout, float* dq, float* dk, float* dv,
-                          float* dw, hipStream_t stream);
+                          float* dw, void* workspace, size_t workspace_bytes,
+                          hipStream_t stream);
 
 /*
  * Bytes of device workspace gm_ser_backward needs for these sizes

@@ -23,7 +23,8 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libgm.so")
 GM_F32, GM_BF16 = 0, 1
 STATUS = {0: "GM_OK", 1: "GM_ERR_NULL", 2: "GM_ERR_SHAPE", 3: "GM_ERR_UNSUPPORTED",
           4: "GM_ERR_WORKSPACE", 5: "GM_ERR_HIP", 6: "GM_ERR_ALIGN", 7: "GM_ERR_ALIAS"}
-EXPORTS = ("gm_ser_forward", "gm_sea_forward", "gm_sea_backward",
+EXPORTS = ("gm_ser_forward", "gm_sea_forward", "gm_sea_backward_workspace_bytes",
+           "gm_sea_backward",
            "gm_ser_backward_workspace_bytes", "gm_ser_backward", "gm_check_edges",
            "gm_status_string", "gm_abi_version")
 
@@ -49,8 +50,9 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     sig = {
         "gm_ser_forward": [_I, _I, _I, _P, _P, _I, _P, _P, _I, _P, _P, _I, _P],
         "gm_sea_forward": [_I, _I, _I, _I, _I, _I, _F, _P, _P, _P, _P, _P, _I, _P, _P],
+        "gm_sea_backward_workspace_bytes": [_I, _I, _I, _I, _I],
         "gm_sea_backward": [_I, _I, _I, _I, _I, _I, _F, _P, _P, _P, _P, _P, _I, _P,
-                            _P, _P, _P, _P, _P],
+                            _P, _P, _P, _P, _P, _Z, _P],
         "gm_ser_backward_workspace_bytes": [_I, _I, _I, _I, _I, _I],
         "gm_ser_backward": [_I, _I, _I, _P, _P, _I, _P, _P, _I, _P, _P, _I, _P, _P, _P,
                             _P, _Z, _P],
@@ -63,6 +65,7 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
         f.argtypes = args
         f.restype = _I
     lib.gm_ser_backward_workspace_bytes.restype = _Z
+    lib.gm_sea_backward_workspace_bytes.restype = _Z
     lib.gm_status_string.restype = ctypes.c_char_p
     _lib = lib
     return lib
@@ -129,7 +132,12 @@ def gm_sea_forward(q, k, v, idx, w, o, scale=None, stream=None) -> None:
           _ptr(idx), _ptr(w), s1, _ptr(o), _stream(stream))
 
 
-def gm_sea_backward(q, k, v, idx, w, dout, dq, dk, dv, dw, scale=None, stream=None) -> None:
+def gm_sea_backward_workspace_bytes(B, n, hq, hkv, s1) -> int:
+    return int(load().gm_sea_backward_workspace_bytes(B, n, hq, hkv, s1))
+
+
+def gm_sea_backward(q, k, v, idx, w, dout, dq, dk, dv, dw, workspace, scale=None,
+                    stream=None) -> None:
     B, n, hq, d = q.shape
     hkv, s1 = idx.shape[2], idx.shape[3]
     _need(q, "q", _ACT)
@@ -139,10 +147,11 @@ def gm_sea_backward(q, k, v, idx, w, dout, dq, dk, dv, dw, scale=None, stream=No
     _need(dq, "dq", (torch.float32,), q.shape)
     _need(dk, "dk", (torch.float32,), k.shape); _need(dv, "dv", (torch.float32,), v.shape)
     _need(dw, "dw", (torch.float32,), idx.shape)
+    _need(workspace, "workspace", (torch.uint8, torch.float64))
     scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
     _call("gm_sea_backward", B, n, hq, hkv, d, _act_dtype(q), scale, _ptr(q), _ptr(k), _ptr(v),
           _ptr(idx), _ptr(w), s1, _ptr(dout), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dw),
-          _stream(stream))
+          _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream))
 
 
 def gm_ser_backward_workspace_bytes(B, n, hkv, s2, s3, aliased) -> int:
@@ -188,13 +197,20 @@ def sea_forward(q, k, v, idx, w, scale=None, stream=None):
     return o
 
 
-def sea_backward(q, k, v, idx, w, dout, scale=None, stream=None):
+def sea_workspace(q, idx, device=None) -> torch.Tensor:
+    B, n, hq, _ = q.shape
+    nbytes = gm_sea_backward_workspace_bytes(B, n, hq, idx.shape[2], idx.shape[3])
+    return torch.empty(max(nbytes, 256), dtype=torch.uint8, device=device or q.device)
+
+
+def sea_backward(q, k, v, idx, w, dout, scale=None, workspace=None, stream=None):
     f32 = dict(dtype=torch.float32, device=q.device)
     dq = torch.empty(q.shape, **f32)
     dk = torch.empty(k.shape, **f32)
     dv = torch.empty(v.shape, **f32)
     dw = torch.empty(idx.shape, **f32)
-    gm_sea_backward(q, k, v, idx, w, dout, dq, dk, dv, dw, scale, stream)
+    ws = sea_workspace(q, idx) if workspace is None else workspace
+    gm_sea_backward(q, k, v, idx, w, dout, dq, dk, dv, dw, ws, scale, stream)
     return dq, dk, dv, dw
 
 

@@ -119,13 +119,20 @@ gm_status gm_sea_forward(int B, int n, int hq, int hkv, int d, gm_dtype dt, floa
                                              idx, w, s1, o, stream));
 }
 
+size_t gm_sea_backward_workspace_bytes(int B, int n, int hq, int hkv, int s1) {
+    if (check_units(B, n, hkv) != GM_OK || hkv <= 0 || hq <= 0 || hq % hkv || s1 < 1) return 0;
+    return gm::sea_backward_workspace_bytes((long long)B * n * hkv, s1, hq / hkv);
+}
+
 gm_status gm_sea_backward(int B, int n, int hq, int hkv, int d, gm_dtype dt, float scale,
                           const void* q, const void* k, const void* v, const int32_t* idx,
                           const float* w, int s1, const void* dout, float* dq, float* dk,
-                          float* dv, float* dw, hipStream_t stream) {
+                          float* dv, float* dw, void* workspace, size_t workspace_bytes,
+                          hipStream_t stream) {
     gm_status st = check_sea(B, n, hq, hkv, d, dt, s1);
     if (st != GM_OK) return st;
     if (empty(B, n, hkv)) return GM_OK;
+    if ((long long)B * n * hkv * s1 >= (long long)INT_MAX) return GM_ERR_SHAPE;
     if (!q || !k || !v || !dout || !dq || !dk || !dv || !dw) return GM_ERR_NULL;
     if ((st = check_edge_ptrs(idx, w)) != GM_OK) return st;
     if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(dout, 16) ||
@@ -136,16 +143,20 @@ gm_status gm_sea_backward(int B, int n, int hq, int hkv, int d, gm_dtype dt, flo
     const size_t ne = (size_t)B * n * hkv * s1;
     const void* ins[6] = {q, k, v, dout, idx, w};
     const size_t inb[6] = {nq * es, nk * es, nk * es, nq * es, ne * 4, ne * 4};
-    const void* outs[4] = {dq, dk, dv, dw};
-    const size_t outb[4] = {nq * 4, nk * 4, nk * 4, ne * 4};
-    for (int a = 0; a < 4; ++a) {
+    const size_t need = gm_sea_backward_workspace_bytes(B, n, hq, hkv, s1);
+    if (!workspace || workspace_bytes < need) return GM_ERR_WORKSPACE;
+    if (!aligned(workspace, 256)) return GM_ERR_ALIGN;
+    const void* outs[5] = {dq, dk, dv, dw, workspace};
+    const size_t outb[5] = {nq * 4, nk * 4, nk * 4, ne * 4, need};
+    for (int a = 0; a < 5; ++a) {
         for (int b = 0; b < 6; ++b)
             if (overlaps(outs[a], outb[a], ins[b], inb[b])) return GM_ERR_ALIAS;
-        for (int b = a + 1; b < 4; ++b)
+        for (int b = a + 1; b < 5; ++b)
             if (overlaps(outs[a], outb[a], outs[b], outb[b])) return GM_ERR_ALIAS;
     }
     return hip_status(gm::launch_sea_backward(B, n, hq, hkv, d, dt == GM_BF16, scale, q, k, v,
-                                              idx, w, s1, dout, dq, dk, dv, dw, stream));
+                                              idx, w, s1, dout, dq, dk, dv, dw, workspace,
+                                              stream));
 }
 
 size_t gm_ser_backward_workspace_bytes(int B, int n, int hkv, int s2, int s3, int aliased) {

@@ -25,10 +25,12 @@ hipError_t launch_sea_forward(int B, int n, int hq, int hkv, int d, bool bf16, f
                               const int32_t* idx, const float* w, int s, void* o,
                               hipStream_t st);
 
+size_t sea_backward_workspace_bytes(long long U, int s, int G);
 hipError_t launch_sea_backward(int B, int n, int hq, int hkv, int d, bool bf16, float scale,
                                const void* q, const void* k, const void* v,
                                const int32_t* idx, const float* w, int s, const void* dout,
-                               float* dq, float* dk, float* dv, float* dw, hipStream_t st);
+                               float* dq, float* dk, float* dv, float* dw, void* workspace,
+                               hipStream_t st);
 
 hipError_t launch_ser_backward(int B, int n, int hkv, const int32_t* idx1, const float* w1,
                                int s2, const int32_t* idx2, const float* w2, int s3,
@@ -39,7 +41,7 @@ hipError_t launch_ser_backward(int B, int n, int hkv, const int32_t* idx1, const
 hipError_t launch_check_edges(int B, int n, int hkv, const int32_t* idx, const float* w, int s,
                               unsigned long long* counts, hipStream_t st);
 
-// Zero `count` floats (or doubles) with a fill kernel (graph-capture safe).
+// Zero `count` 4-byte words (or doubles) with a fill kernel (graph-capture safe).
 hipError_t launch_zero_f32(float* p, size_t count, hipStream_t st);
 hipError_t launch_zero_f64(double* p, size_t count, hipStream_t st);
 

@@ -5,24 +5,61 @@
 // edge weights).  Per unit and query head, over the live slots t:
 //   p_t  = softmax(scale q.k_t + ln w_t)      (recomputed, log2 domain)
 //   g_t  = dout . v_t,  gbar = sum_t p_t g_t,  dl_t = p_t (g_t - gbar)
-//   dq   = scale sum_t dl_t k_t               (reduce-scattered, fp32 store)
-//   dk[idx_t] += scale dl_t q,  dv[idx_t] += p_t dout   (summed over the
-//                                              group's heads, then scattered)
+//   dq   = scale sum_t dl_t k_t
+//   dk[idx_t] += scale dl_t q,  dv[idx_t] += p_t dout   (over the group's heads)
 //   dw_t = sum_heads dl_t / w_t = sum_heads exp2(ls_t - M) / Z (g_t - gbar)
-// The last form never divides by w, so it is finite for tiny weights.
+// The last form never divides by w, so it stays finite for tiny weights.
 //
-// Mapping as in the forward: a team of R * P lanes per unit, one 16-byte
-// piece of a K/V/q/dout row per lane.  The dk/dv rows of a wave are written
-// to LDS and read back transposed, so each global fp32 atomic instruction
-// covers 64 consecutive floats of one row (two 128-byte lines) instead of
-// 64 scattered lanes.
+// The dk/dv scatter is done as a sort by target instead of float atomics
+// (the L2 retires roughly one atomic lane per channel per clock, which made
+// 1024 atomic lanes per unit the bottleneck):
+//   1. source pass, one team per unit (as the forward): dq and dw in
+//      registers; per (slot, head) the pair (scale*dl, p) goes to a
+//      coefficient array; the in-degree of each target row is counted.
+//   2. exclusive scan of the in-degrees -> row offsets (two small kernels).
+//   3. fill: every live edge id (unit * s + slot) is placed in its target
+//      row's segment of the reverse edge list.
+//   4. target pass, one team per K/V row: walks the row's incoming edges,
+//      gathers the source's q and dout rows and sums
+//      dk = sum coef.a * q, dv = sum coef.p * dout, then writes the row once
+//      (rows without incoming edges get zeros), so no zero-fill is needed.
+// Within a segment the edge order depends on the fill's atomics, so the
+// fp32 sums of dk/dv may differ in the last bits between runs.
 #include "gm_common.h"
 #include "gm_internal.h"
 
 #include <math.h>
 
 namespace gm {
+
 namespace {
+
+constexpr int kScanPerBlock = 4096;  // counts scanned by one 1024-thread block
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+struct Workspace {
+    float2* coef;   // [U * s * G]  (scale * dl, p) per edge and head
+    int* cnt;       // [U]  in-degree, then the fill cursor
+    int* off;       // [U + 1]  segment offsets
+    int* bsum;      // [ceil(U / kScanPerBlock)]
+    int* list;      // [U * s]  edge ids grouped by target row
+};
+
+struct WsLayout {
+    size_t coef, cnt, off, bsum, list, total;
+};
+
+WsLayout ws_layout(long long U, int s, int G) {
+    WsLayout l;
+    l.coef = 0;
+    l.cnt = l.coef + align256((size_t)U * s * G * sizeof(float2));
+    l.off = l.cnt + align256((size_t)U * sizeof(int));
+    l.bsum = l.off + align256((size_t)(U + 1) * sizeof(int));
+    l.list = l.bsum + align256((size_t)((U + kScanPerBlock - 1) / kScanPerBlock) * sizeof(int));
+    l.total = l.list + align256((size_t)U * s * sizeof(int));
+    return l;
+}
 
 struct SeaBwdArgs {
     const void* q;
@@ -35,63 +72,27 @@ struct SeaBwdArgs {
     float* dk;
     float* dv;
     float* dw;
-    int n, hq, hkv, d, s, U, log2d;
+    Workspace ws;
+    int n, hq, hkv, d, s, U;
     float scale;
-    TeamShape ts;
+    TeamShape ts;   // source pass
+    TeamShape tt;   // target pass (P = edges walked side by side)
 };
 
-// Per-wave staging of dk/dv rows (64 lanes x V floats each) and row targets.
-template <int V>
-struct Stage {
-    float dk[kBlock / kWave][kWave * V];
-    float dv[kBlock / kWave][kWave * V];
-    int tgt[kBlock / kWave][kWave];
-};
-
-// Write this lane's V floats of its slot row to LDS, then scatter the wave's
-// rows with contiguous atomics.  Every lane of the block must call this.
-template <int V, typename A>
-__device__ __forceinline__ void scatter_rows(Stage<V>& sm, const A (&dk)[V], const A (&dv)[V],
-                                             long long tgt_row, int R, int log2d, int d,
-                                             float* gdk, float* gdv) {
-    const int wave = threadIdx.x / kWave;
-    const int lane = threadIdx.x & (kWave - 1);
-#pragma unroll
-    for (int e = 0; e < V; ++e) {
-        sm.dk[wave][lane * V + e] = (float)dk[e];
-        sm.dv[wave][lane * V + e] = (float)dv[e];
-    }
-    if ((lane & (R - 1)) == 0) sm.tgt[wave][lane / R] = (int)tgt_row;
-    __syncthreads();
-#pragma unroll
-    for (int it = 0; it < V; ++it) {
-        const int f = it * kWave + lane;
-        const int row = f >> log2d;
-        const int col = f & (d - 1);
-        const int tr = sm.tgt[wave][row];
-        if (tr >= 0) {
-            const size_t o = (size_t)tr * d + col;
-            unsafeAtomicAdd(gdk + o, sm.dk[wave][f]);
-            unsafeAtomicAdd(gdv + o, sm.dv[wave][f]);
-        }
-    }
-    __syncthreads();
-}
-
+// ------------------------------------------------------------ source pass
 template <typename T, int G>
-__global__ __launch_bounds__(kBlock) void sea_bwd_kernel(SeaBwdArgs a) {
+__global__ __launch_bounds__(kBlock) void sea_bwd_src_kernel(SeaBwdArgs a) {
     using A = typename io<T>::acc;
     constexpr int V = io<T>::V;
     constexpr int LOG2V = ilog2(V);
-    __shared__ Stage<V> sm;
     const int R = a.ts.R, team = a.ts.team, P = a.ts.P;
     const int lane = threadIdx.x & (kWave - 1);
     const int tl = lane & (team - 1);
     const int r = tl & (R - 1);
     const int sl = tl >> a.ts.log2R;
     const long long gunit = ((long long)blockIdx.x * kBlock + threadIdx.x) / team;
-    const bool active = gunit < a.U;   // no early return: the block synchronises
-    const int unit = active ? (int)gunit : 0;
+    if (gunit >= a.U) return;  // whole team leaves together
+    const int unit = (int)gunit;
     const int h = unit % a.hkv;
     const int bi = unit / a.hkv;
     const int b = bi / a.n;
@@ -105,43 +106,36 @@ __global__ __launch_bounds__(kBlock) void sea_bwd_kernel(SeaBwdArgs a) {
     const size_t kv0 = (size_t)b * a.n * a.hkv + h;
     const int32_t* ip = a.idx + (size_t)unit * a.s;
     const float* wp = a.w + (size_t)unit * a.s;
+    float2* cp = a.ws.coef + (size_t)unit * a.s * G;
     const A c = (A)a.scale * (A)1.4426950408889634;
     const A sc = (A)a.scale;
     const A NEG = -INFINITY;
-    const bool storer = active && (sl >> LOG2V) == 0;
+    const bool storer = (sl >> LOG2V) == 0;
 
     if (a.ts.nchunk == 1) {
         const int t = sl;
         bool live = false;
         A lw = NEG;
-        long long tgt = -1;
         A kr[V], vr[V];
 #pragma unroll
         for (int e = 0; e < V; ++e) { kr[e] = 0; vr[e] = 0; }
-        if (active && t < a.s) {
+        if (t < a.s) {
             const float wt = wp[t];
             if (wt > 0.0f) {
                 live = true;
                 lw = alog2((A)wt);
-                tgt = (long long)(kv0 + (size_t)ip[t] * a.hkv);
-                load16(kp + tgt * d, kr);
-                load16(vp + tgt * d, vr);
+                const long long row = (long long)(kv0 + (size_t)ip[t] * a.hkv);
+                load16(kp + row * d, kr);
+                load16(vp + row * d, vr);
+                if (r == 0) atomicAdd(a.ws.cnt + row, 1);
             }
         }
-        A dka[V], dva[V];
-#pragma unroll
-        for (int e = 0; e < V; ++e) { dka[e] = 0; dva[e] = 0; }
         A dws = 0;
 #pragma unroll
         for (int g = 0; g < G; ++g) {
             A qg[V], dg[V];
-            if (active) {
-                load16(qp + g * d, qg);
-                load16(dop + g * d, dg);
-            } else {
-#pragma unroll
-                for (int e = 0; e < V; ++e) { qg[e] = 0; dg[e] = 0; }
-            }
+            load16(qp + g * d, qg);
+            load16(dop + g * d, dg);
             A sd = 0, gd = 0;
 #pragma unroll
             for (int e = 0; e < V; ++e) { sd += qg[e] * kr[e]; gd += dg[e] * vr[e]; }
@@ -162,31 +156,21 @@ __global__ __launch_bounds__(kBlock) void sea_bwd_kernel(SeaBwdArgs a) {
             int len;
             const int off = reduce_scatter(dqv, tl, R, team, len);
             if (storer) store_len(dqp + g * d + off, dqv, len);
-#pragma unroll
-            for (int e = 0; e < V; ++e) {
-                dka[e] += dls * qg[e];
-                dva[e] += p * dg[e];
-            }
+            if (live && r == 0) cp[t * G + g] = make_float2((float)dls, (float)p);
             if (live) dws += aexp2(ls - M) * invZ * (gd - gbar);
         }
-        if (active && r == 0 && t < a.s) a.dw[(size_t)unit * a.s + t] = (float)dws;
-        scatter_rows<V>(sm, dka, dva, tgt, R, a.log2d, a.d, a.dk, a.dv);
+        if (r == 0 && t < a.s) a.dw[(size_t)unit * a.s + t] = (float)dws;
         return;
     }
 
     // s > P: per head, pass 1 over the chunks finds the running max M, the
-    // sum Z and sum e*g; pass 2 recomputes p, dl and scatters each chunk.
-    // dw is accumulated with atomics here (the caller zero-filled it).
+    // sum Z and sum e*g; pass 2 recomputes p and dl.  dw is summed over the
+    // heads with atomics (the caller zero-filled it).
 #pragma unroll 1
     for (int g = 0; g < G; ++g) {
         A qg[V], dg[V];
-        if (active) {
-            load16(qp + g * d, qg);
-            load16(dop + g * d, dg);
-        } else {
-#pragma unroll
-            for (int e = 0; e < V; ++e) { qg[e] = 0; dg[e] = 0; }
-        }
+        load16(qp + g * d, qg);
+        load16(dop + g * d, dg);
         A M = NEG, Z = 0, Sg = 0;
 #pragma unroll 1
         for (int ch = 0; ch < a.ts.nchunk; ++ch) {
@@ -196,7 +180,7 @@ __global__ __launch_bounds__(kBlock) void sea_bwd_kernel(SeaBwdArgs a) {
             A kr[V], vr[V];
 #pragma unroll
             for (int e = 0; e < V; ++e) { kr[e] = 0; vr[e] = 0; }
-            if (active && t < a.s) {
+            if (t < a.s) {
                 const float wt = wp[t];
                 if (wt > 0.0f) {
                     live = true;
@@ -213,7 +197,7 @@ __global__ __launch_bounds__(kBlock) void sea_bwd_kernel(SeaBwdArgs a) {
             gd = sum_bits(gd, 1, R);
             const A l = live ? sd * c + lw : NEG;
             const A Mn = amax(M, max_bits(l, R, team));
-            if (Mn == NEG) continue;
+            if (Mn == NEG) continue;  // uniform over the team: nothing live yet
             const A alpha = aexp2(M - Mn);
             const A ex = live ? aexp2(l - Mn) : (A)0;
             Z = Z * alpha + sum_bits(ex, R, team);
@@ -228,41 +212,31 @@ __global__ __launch_bounds__(kBlock) void sea_bwd_kernel(SeaBwdArgs a) {
 #pragma unroll 1
         for (int ch = 0; ch < a.ts.nchunk; ++ch) {
             const int t = ch * P + sl;
-            bool live = false;
-            A lw = NEG;
-            long long tgt = -1;
+            if (t >= a.s) continue;
+            const float wt = wp[t];
+            if (!(wt > 0.0f)) continue;
+            const A lw = alog2((A)wt);
+            const long long row = (long long)(kv0 + (size_t)ip[t] * a.hkv);
             A kr[V], vr[V];
-#pragma unroll
-            for (int e = 0; e < V; ++e) { kr[e] = 0; vr[e] = 0; }
-            if (active && t < a.s) {
-                const float wt = wp[t];
-                if (wt > 0.0f) {
-                    live = true;
-                    lw = alog2((A)wt);
-                    tgt = (long long)(kv0 + (size_t)ip[t] * a.hkv);
-                    load16(kp + tgt * d, kr);
-                    load16(vp + tgt * d, vr);
-                }
-            }
+            load16(kp + row * d, kr);
+            load16(vp + row * d, vr);
             A sd = 0, gd = 0;
 #pragma unroll
             for (int e = 0; e < V; ++e) { sd += qg[e] * kr[e]; gd += dg[e] * vr[e]; }
+            // the row lanes of one slot are all here (same t): reduce them
             sd = sum_bits(sd, 1, R);
             gd = sum_bits(gd, 1, R);
             const A ls = sd * c;
-            const A p = live ? aexp2(ls + lw - M) * invZ : (A)0;
+            const A p = aexp2(ls + lw - M) * invZ;
             const A dls = p * (gd - gbar) * sc;
-            A dka[V], dva[V];
 #pragma unroll
-            for (int e = 0; e < V; ++e) {
-                dqv[e] += dls * kr[e];
-                dka[e] = dls * qg[e];
-                dva[e] = p * dg[e];
-            }
-            if (live && r == 0)
+            for (int e = 0; e < V; ++e) dqv[e] += dls * kr[e];
+            if (r == 0) {
+                cp[t * G + g] = make_float2((float)dls, (float)p);
                 unsafeAtomicAdd(a.dw + (size_t)unit * a.s + t,
                                 (float)(aexp2(ls - M) * invZ * (gd - gbar)));
-            scatter_rows<V>(sm, dka, dva, tgt, R, a.log2d, a.d, a.dk, a.dv);
+                if (g == 0) atomicAdd(a.ws.cnt + row, 1);
+            }
         }
         int len;
         const int off = reduce_scatter(dqv, tl, R, team, len);
@@ -270,47 +244,203 @@ __global__ __launch_bounds__(kBlock) void sea_bwd_kernel(SeaBwdArgs a) {
     }
 }
 
+// --------------------------------------------------------------- index build
+// Exclusive scan of cnt[0 .. U) into off, 4096 counts per block.
+__global__ __launch_bounds__(1024) void scan_local_kernel(const int* cnt, int* off, int* bsum,
+                                                          int U) {
+    __shared__ int part[1024 / kWave];
+    const int base = blockIdx.x * kScanPerBlock + threadIdx.x * 4;
+    int v[4], s = 0;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        v[e] = base + e < U ? cnt[base + e] : 0;
+        s += v[e];
+    }
+    // inclusive scan of the per-thread sums across the wave
+    const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
+    int inc = s;
+    for (int m = 1; m < kWave; m <<= 1) {
+        const int o = __shfl_up(inc, m, kWave);
+        if (lane >= m) inc += o;
+    }
+    if (lane == kWave - 1) part[wave] = inc;
+    __syncthreads();
+    int wbase = 0;
+    for (int k = 0; k < wave; ++k) wbase += part[k];
+    int run = wbase + inc - s;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        if (base + e < U) off[base + e] = run;
+        run += v[e];
+    }
+    if (threadIdx.x == 1023) bsum[blockIdx.x] = wbase + inc;
+}
+
+// Add the preceding blocks' totals; copy the offsets into the fill cursor.
+__global__ __launch_bounds__(1024) void scan_add_kernel(int* off, int* cursor, const int* bsum,
+                                                        int U) {
+    __shared__ int base_s;
+    if (threadIdx.x < kWave) {
+        int sum = 0;
+        for (int k = threadIdx.x; k < (int)blockIdx.x; k += kWave) sum += bsum[k];
+        for (int m = 32; m > 0; m >>= 1) sum += __shfl_xor(sum, m, kWave);
+        if (threadIdx.x == 0) base_s = sum;
+    }
+    __syncthreads();
+    const int base = base_s;
+    const int first = blockIdx.x * kScanPerBlock;
+    for (int e = threadIdx.x; e < kScanPerBlock; e += 1024) {
+        const int x = first + e;
+        if (x < U) {
+            const int o = off[x] + base;
+            off[x] = o;
+            cursor[x] = o;
+        }
+    }
+    if (blockIdx.x == gridDim.x - 1 && threadIdx.x == 0) off[U] = base + bsum[blockIdx.x];
+}
+
+// Place every live edge id (unit * s + slot) in its target row's segment.
+__global__ __launch_bounds__(kBlock) void edge_fill_kernel(const int32_t* idx, const float* w,
+                                                           int n, int hkv, int s, long long E,
+                                                           int* cursor, int* list) {
+    for (long long e = (long long)blockIdx.x * kBlock + threadIdx.x; e < E;
+         e += (long long)gridDim.x * kBlock) {
+        if (!(w[e] > 0.0f)) continue;
+        const int unit = (int)(e / s);
+        const int h = unit % hkv;
+        const int b = unit / hkv / n;
+        const int row = (b * n + idx[e]) * hkv + h;
+        const int pos = atomicAdd(cursor + row, 1);
+        list[pos] = (int)e;
+    }
+}
+
+// ------------------------------------------------------------ target pass
+// One team of R * P lanes per K/V row (b, j, h): P incoming edges side by
+// side, R lanes per 16-byte piece of a d-row, G query heads per edge.
 template <typename T, int G>
-hipError_t run(const SeaBwdArgs& a, hipStream_t st) {
-    const long long threads = (long long)a.U * a.ts.team;
-    const unsigned blocks = (unsigned)((threads + kBlock - 1) / kBlock);
-    hipLaunchKernelGGL((sea_bwd_kernel<T, G>), dim3(blocks), dim3(kBlock), 0, st, a);
+__global__ __launch_bounds__(kBlock) void sea_bwd_dst_kernel(SeaBwdArgs a) {
+    using A = typename io<T>::acc;
+    constexpr int V = io<T>::V;
+    constexpr int LOG2V = ilog2(V);
+    const int R = a.tt.R, team = a.tt.team, P = a.tt.P;
+    const int lane = threadIdx.x & (kWave - 1);
+    const int tl = lane & (team - 1);
+    const int r = tl & (R - 1);
+    const int sl = tl >> a.tt.log2R;
+    const long long grow = ((long long)blockIdx.x * kBlock + threadIdx.x) / team;
+    if (grow >= a.U) return;
+    const int row = (int)grow;
+    const int h = row % a.hkv;
+    const size_t d = (size_t)a.d;
+    const int beg = a.ws.off[row], end = a.ws.off[row + 1];
+    const T* qb = static_cast<const T*>(a.q) + (size_t)h * G * d + r * V;
+    const T* db = static_cast<const T*>(a.dout) + (size_t)h * G * d + r * V;
+    A ak[V], av[V];
+#pragma unroll
+    for (int e = 0; e < V; ++e) { ak[e] = 0; av[e] = 0; }
+#pragma unroll 1
+    for (int e0 = beg; e0 < end; e0 += P) {
+        const int ei = e0 + sl;
+        if (ei < end) {
+            const int eid = a.ws.list[ei];
+            const int unit = eid / a.s;
+            const size_t src = (size_t)(unit / a.hkv) * a.hq * d;   // (b*n + i) * hq * d
+            const float2* cf = a.ws.coef + (size_t)eid * G;
+#pragma unroll
+            for (int g = 0; g < G; ++g) {
+                const float2 ap = cf[g];
+                A qg[V], dg[V];
+                load16(qb + src + g * d, qg);
+                load16(db + src + g * d, dg);
+#pragma unroll
+                for (int e = 0; e < V; ++e) {
+                    ak[e] += (A)ap.x * qg[e];
+                    av[e] += (A)ap.y * dg[e];
+                }
+            }
+        }
+    }
+    int len;
+    const int off = reduce_scatter(ak, tl, R, team, len);
+    reduce_scatter(av, tl, R, team, len);
+    if ((sl >> LOG2V) == 0) {
+        float* dkp = a.dk + (size_t)row * d + r * V + off;
+        float* dvp = a.dv + (size_t)row * d + r * V + off;
+        store_len(dkp, ak, len);
+        store_len(dvp, av, len);
+    }
+}
+
+template <typename T, int G>
+hipError_t run(const SeaBwdArgs& a, long long E, hipStream_t st) {
+    const long long src_threads = (long long)a.U * a.ts.team;
+    hipLaunchKernelGGL((sea_bwd_src_kernel<T, G>),
+                       dim3((unsigned)((src_threads + kBlock - 1) / kBlock)), dim3(kBlock), 0, st,
+                       a);
+    const unsigned sblocks = (unsigned)((a.U + kScanPerBlock - 1) / kScanPerBlock);
+    hipLaunchKernelGGL(scan_local_kernel, dim3(sblocks), dim3(1024), 0, st,
+                       (const int*)a.ws.cnt, a.ws.off, a.ws.bsum, a.U);
+    hipLaunchKernelGGL(scan_add_kernel, dim3(sblocks), dim3(1024), 0, st, a.ws.off, a.ws.cnt,
+                       (const int*)a.ws.bsum, a.U);
+    long long fb = (E + kBlock - 1) / kBlock;
+    if (fb > 16384) fb = 16384;
+    hipLaunchKernelGGL(edge_fill_kernel, dim3((unsigned)fb), dim3(kBlock), 0, st, a.idx, a.w, a.n,
+                       a.hkv, a.s, E, a.ws.cnt, a.ws.list);
+    const long long dst_threads = (long long)a.U * a.tt.team;
+    hipLaunchKernelGGL((sea_bwd_dst_kernel<T, G>),
+                       dim3((unsigned)((dst_threads + kBlock - 1) / kBlock)), dim3(kBlock), 0, st,
+                       a);
     return hipGetLastError();
 }
 
 template <typename T>
-hipError_t dispatch_g(const SeaBwdArgs& a, int G, hipStream_t st) {
+hipError_t dispatch_g(const SeaBwdArgs& a, int G, long long E, hipStream_t st) {
     switch (G) {
-        case 1: return run<T, 1>(a, st);
-        case 2: return run<T, 2>(a, st);
-        case 4: return run<T, 4>(a, st);
-        case 8: return run<T, 8>(a, st);
-        case 16: return run<T, 16>(a, st);
+        case 1: return run<T, 1>(a, E, st);
+        case 2: return run<T, 2>(a, E, st);
+        case 4: return run<T, 4>(a, E, st);
+        case 8: return run<T, 8>(a, E, st);
+        case 16: return run<T, 16>(a, E, st);
         default: return hipErrorInvalidValue;
     }
 }
 
 }  // namespace
 
+size_t sea_backward_workspace_bytes(long long U, int s, int G) {
+    return ws_layout(U, s, G).total;
+}
+
 hipError_t launch_sea_backward(int B, int n, int hq, int hkv, int d, bool bf16, float scale,
                                const void* q, const void* k, const void* v,
                                const int32_t* idx, const float* w, int s, const void* dout,
-                               float* dq, float* dk, float* dv, float* dw, hipStream_t st) {
+                               float* dq, float* dk, float* dv, float* dw, void* workspace,
+                               hipStream_t st) {
+    const int G = hq / hkv;
     SeaBwdArgs a;
     a.q = q; a.k = k; a.v = v; a.dout = dout; a.idx = idx; a.w = w;
     a.dq = dq; a.dk = dk; a.dv = dv; a.dw = dw;
     a.n = n; a.hq = hq; a.hkv = hkv; a.d = d; a.s = s;
     a.U = B * n * hkv;
-    a.log2d = ilog2(d);
     a.scale = scale;
-    a.ts = sea_team(d, bf16 ? 2 : 4, s);
-    const size_t nkv = (size_t)B * n * hkv * d;
-    hipError_t e = launch_zero_f32(dk, nkv, st);
-    if (e == hipSuccess) e = launch_zero_f32(dv, nkv, st);
-    if (e == hipSuccess && a.ts.nchunk > 1) e = launch_zero_f32(dw, (size_t)B * n * hkv * s, st);
+    const int es = bf16 ? 2 : 4;
+    a.ts = sea_team(d, es, s);
+    // target pass: up to 8 incoming edges side by side (rows have ~s on average)
+    a.tt = sea_team(d, es, 8);
+    const WsLayout l = ws_layout(a.U, s, G);
+    char* base = static_cast<char*>(workspace);
+    a.ws.coef = reinterpret_cast<float2*>(base + l.coef);
+    a.ws.cnt = reinterpret_cast<int*>(base + l.cnt);
+    a.ws.off = reinterpret_cast<int*>(base + l.off);
+    a.ws.bsum = reinterpret_cast<int*>(base + l.bsum);
+    a.ws.list = reinterpret_cast<int*>(base + l.list);
+    hipError_t e = launch_zero_f32(reinterpret_cast<float*>(a.ws.cnt), (size_t)a.U, st);
+    if (e == hipSuccess && a.ts.nchunk > 1) e = launch_zero_f32(dw, (size_t)a.U * s, st);
     if (e != hipSuccess) return e;
-    const int G = hq / hkv;
-    return bf16 ? dispatch_g<bf16_t>(a, G, st) : dispatch_g<float>(a, G, st);
+    const long long E = (long long)a.U * s;
+    return bf16 ? dispatch_g<bf16_t>(a, G, E, st) : dispatch_g<float>(a, G, E, st);
 }
 
 }  // namespace gm

@@ -86,14 +86,21 @@ def test_sea_argument_checks(lib):
     assert f(*args(q=fake(0x100008))) == ALIGN
     assert f(*args(oo=a)) == ALIAS           # o on q
     g = lib.gm_sea_backward
+    need = lib.gm_sea_backward_workspace_bytes(8, 4096, 16, 8, 4)
+    assert need >= 8 * 4096 * 8 * 4 * (2 * 8 + 4)      # coefficients and edge list
+    ws = fake(0x40000000)
     bargs = [8, 4096, 16, 8, 128, 1, 0.1, a, b, c, i, w, 4, fake(0x700000),
-             fake(0x800000), fake(0x900000), fake(0xA00000), fake(0xB00000), None]
+             fake(0x800000), fake(0x900000), fake(0xA00000), fake(0xB00000), ws, need, None]
     bad = list(bargs); bad[15] = None
     assert g(*bad) == NULL
     bad = list(bargs); bad[15] = fake(0x900004)
     assert g(*bad) == ALIGN
     bad = list(bargs); bad[14] = b            # dq on k
     assert g(*bad) == ALIAS
+    bad = list(bargs); bad[19] = need - 1
+    assert g(*bad) == WS
+    bad = list(bargs); bad[18] = fake(0x40000010)
+    assert g(*bad) == ALIGN
 
 
 def test_ser_backward_workspace_checks(lib):

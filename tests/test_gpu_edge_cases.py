@@ -194,3 +194,17 @@ def test_errors_are_reported_before_any_launch():
         gm.sea_forward(torch.zeros((1, 8, 6, 128), dtype=torch.bfloat16, device="cuda"),
                        k, k, idx, w)
     torch.cuda.synchronize()
+
+
+def test_sea_backward_long_incoming_segments():
+    """Every edge of every token points at token 0 or 1, so two K/V rows per
+    pair receive thousands of incoming edges (as deep referral chains do)."""
+    rng = np.random.default_rng(12)
+    q, k, v, do, idx, w = _sea_inputs(rng, torch.bfloat16, 128, 2, 4, 700, pad=0.0, dead=0.0)
+    idx = np.minimum(rng.integers(0, 2, size=idx.shape), np.arange(700).reshape(1, 700, 1, 1))
+    idx = idx.astype(np.int32)
+    grads = gm.sea_backward(dev(q), dev(k), dev(v), dev(idx), dev(w), dev(do))
+    torch.cuda.synchronize()
+    ref = oracle.get().sea_backward(q, k, v, idx, w, do)
+    for name, g, r in zip(("dq", "dk", "dv", "dw"), grads, ref):
+        assert_close(name, host(g), r, 2e-2)
