@@ -57,6 +57,9 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="instead of the pass, run a plain device copy of MIB MiB "
+                         "(the known-size reference for hardware byte counters)")
     return ap.parse_args()
 
 
@@ -135,7 +138,7 @@ def cpu_baseline(ps: Pass, budget_s: float):
     act = {k: v.float().numpy() for k, v in ps.host_act.items()}
     done, spent = 0, 0.0
     pairs = [(b, h) for b in range(p.B) for h in range(p.hkv)]
-    while spent < budget_s and done < 4 * len(pairs):
+    while spent < budget_s and done < 16 * len(pairs):
         b, h = pairs[done % len(pairs)]
         sl = lambda x, g=0: np.ascontiguousarray(  # noqa: E731
             x[b:b + 1, :, h * g:(h + 1) * g] if g else x[b:b + 1, :, h:h + 1], dtype=None)
@@ -165,6 +168,16 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(2)
+    if a.copy_calibration:
+        n = a.copy_calibration * (1 << 20) // 4
+        src = torch.ones(n, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(a.warmup + a.steps):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes_read": n * 4, "bytes_written": n * 4,
+                          "launches": a.warmup + a.steps}))
+        return
     gm.load()
     p = synth.PRESETS["metric"]
     ps = Pass(p)

@@ -20,6 +20,10 @@ hipError_t launch_ser_forward(int B, int n, int hkv, const int32_t* idx1, const 
                               int s2, const int32_t* idx2, const float* w2, int s3,
                               int32_t* idx_out, float* w_out, int s1, hipStream_t st);
 
+// The 16-lane-row fast kernels apply: one d-row is 256 bytes, s <= 4, and
+// activation tensors are addressable with 32-bit byte offsets.
+bool sea_fast_shape(int B, int n, int hq, int hkv, int d, bool bf16, int s);
+
 hipError_t launch_sea_forward(int B, int n, int hq, int hkv, int d, bool bf16, float scale,
                               const void* q, const void* k, const void* v,
                               const int32_t* idx, const float* w, int s, void* o,
@@ -40,6 +44,12 @@ hipError_t launch_ser_backward(int B, int n, int hkv, const int32_t* idx1, const
 
 hipError_t launch_check_edges(int B, int n, int hkv, const int32_t* idx, const float* w, int s,
                               unsigned long long* counts, hipStream_t st);
+
+// Workgroups for a persistent XCD-aware kernel: as many as fit on the device
+// at once (occupancy x compute units), a multiple of 8 (one share per XCD),
+// and no more than the work needs (`items` units, `per_wg` per workgroup and
+// pass).  Device properties and occupancy are cached per device / kernel.
+int persistent_grid(const void* kernel, int items, int per_wg);
 
 // Zero `count` 4-byte words (or doubles) with a fill kernel (graph-capture safe).
 hipError_t launch_zero_f32(float* p, size_t count, hipStream_t st);

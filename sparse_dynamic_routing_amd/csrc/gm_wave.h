@@ -1,0 +1,194 @@
+// Wave64 building blocks for the gfx950 fast paths, where one d-row of K/V/q
+// (256 bytes: bf16 d=128 or fp32 d=64) is spread over one 16-lane row of the
+// wavefront (16 bytes per lane) and the P <= 4 edge slots of a unit sit in
+// consecutive rows.  Reductions inside a row use DPP (the permute is fused
+// into the add); reductions and exchanges across rows use gfx950's
+// v_permlane16_swap / v_permlane32_swap, so no LDS traffic, no lane-address
+// arithmetic and no selects are needed.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "gm_common.h"
+
+namespace gm {
+
+// DPP controls (gfx9 encoding).
+constexpr int kDppXor1 = 0xB1;         // quad_perm [1,0,3,2]
+constexpr int kDppXor2 = 0x4E;         // quad_perm [2,3,0,1]
+constexpr int kDppHalfMirror = 0x141;  // lane i <-> 7-i inside each 8
+constexpr int kDppMirror = 0x140;      // lane i <-> 15-i inside each 16
+
+template <int CTRL>
+__device__ __forceinline__ float dpp(float x) {
+    return __builtin_bit_cast(
+        float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, 0xF, 0xF, false));
+}
+template <int CTRL>
+__device__ __forceinline__ double dpp(double x) {
+    const uint64_t u = __builtin_bit_cast(uint64_t, x);
+    const int lo = __builtin_amdgcn_update_dpp(0, (int)(uint32_t)u, CTRL, 0xF, 0xF, false);
+    const int hi = __builtin_amdgcn_update_dpp(0, (int)(uint32_t)(u >> 32), CTRL, 0xF, 0xF, false);
+    return __builtin_bit_cast(double, ((uint64_t)(uint32_t)hi << 32) | (uint32_t)lo);
+}
+
+// Sum / max over the 16 lanes of each row; every lane gets the result.
+template <typename A>
+__device__ __forceinline__ A row_sum16(A x) {
+    x += dpp<kDppXor1>(x);
+    x += dpp<kDppXor2>(x);
+    x += dpp<kDppHalfMirror>(x);
+    x += dpp<kDppMirror>(x);
+    return x;
+}
+
+// Cross-row swaps.  swap16(a, b): odd rows of a trade places with even rows
+// of b; swap32(a, b): the upper 32 lanes of a trade with the lower 32 of b.
+__device__ __forceinline__ void swap16(float& a, float& b) {
+    const auto r = __builtin_amdgcn_permlane16_swap(__builtin_bit_cast(uint32_t, a),
+                                                    __builtin_bit_cast(uint32_t, b), false, false);
+    a = __builtin_bit_cast(float, (uint32_t)r[0]);
+    b = __builtin_bit_cast(float, (uint32_t)r[1]);
+}
+__device__ __forceinline__ void swap32(float& a, float& b) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(uint32_t, a),
+                                                    __builtin_bit_cast(uint32_t, b), false, false);
+    a = __builtin_bit_cast(float, (uint32_t)r[0]);
+    b = __builtin_bit_cast(float, (uint32_t)r[1]);
+}
+__device__ __forceinline__ void swap16(double& a, double& b) {
+    uint64_t ua = __builtin_bit_cast(uint64_t, a), ub = __builtin_bit_cast(uint64_t, b);
+    const auto lo = __builtin_amdgcn_permlane16_swap((uint32_t)ua, (uint32_t)ub, false, false);
+    const auto hi = __builtin_amdgcn_permlane16_swap((uint32_t)(ua >> 32), (uint32_t)(ub >> 32),
+                                                     false, false);
+    a = __builtin_bit_cast(double, ((uint64_t)(uint32_t)hi[0] << 32) | (uint32_t)lo[0]);
+    b = __builtin_bit_cast(double, ((uint64_t)(uint32_t)hi[1] << 32) | (uint32_t)lo[1]);
+}
+__device__ __forceinline__ void swap32(double& a, double& b) {
+    uint64_t ua = __builtin_bit_cast(uint64_t, a), ub = __builtin_bit_cast(uint64_t, b);
+    const auto lo = __builtin_amdgcn_permlane32_swap((uint32_t)ua, (uint32_t)ub, false, false);
+    const auto hi = __builtin_amdgcn_permlane32_swap((uint32_t)(ua >> 32), (uint32_t)(ub >> 32),
+                                                     false, false);
+    a = __builtin_bit_cast(double, ((uint64_t)(uint32_t)hi[0] << 32) | (uint32_t)lo[0]);
+    b = __builtin_bit_cast(double, ((uint64_t)(uint32_t)hi[1] << 32) | (uint32_t)lo[1]);
+}
+
+// Sum / max over the P rows (P in {1, 2, 4}) of a team; every lane gets it.
+template <int P, typename A>
+__device__ __forceinline__ A rows_sum(A x) {
+    if constexpr (P >= 2) { A a = x, b = x; swap16(a, b); x = a + b; }
+    if constexpr (P >= 4) { A a = x, b = x; swap32(a, b); x = a + b; }
+    return x;
+}
+template <int P, typename A>
+__device__ __forceinline__ A rows_max(A x) {
+    if constexpr (P >= 2) { A a = x, b = x; swap16(a, b); x = amax(a, b); }
+    if constexpr (P >= 4) { A a = x, b = x; swap32(a, b); x = amax(a, b); }
+    return x;
+}
+
+// Reduce-scatter a V-vector over the P rows of a team.  Afterwards x[0 .. V/P)
+// holds the sums of elements [off, off + V/P) of the vector, with
+// off = rs_offset<V, P>(row); V >= P.
+template <int P, int V, typename A>
+__device__ __forceinline__ void rows_reduce_scatter(A (&x)[V]) {
+    if constexpr (P >= 2) {
+        constexpr int h = V / 2;
+#pragma unroll
+        for (int e = 0; e < h; ++e) {
+            swap16(x[e], x[e + h]);
+            x[e] += x[e + h];
+        }
+    }
+    if constexpr (P >= 4) {
+        constexpr int h = V / 4;
+#pragma unroll
+        for (int e = 0; e < h; ++e) {
+            swap32(x[e], x[e + h]);
+            x[e] += x[e + h];
+        }
+    }
+}
+template <int V, int P>
+__device__ __forceinline__ int rs_offset(int row) {
+    int off = 0;
+    if constexpr (P >= 2) off += (row & 1) * (V / 2);
+    if constexpr (P >= 4) off += ((row >> 1) & 1) * (V / 4);
+    return off;
+}
+
+// Division of 0 <= x < 2^31 by an invariant divisor 1 <= d < 2^31 with a
+// multiply-high, add and shift (Granlund and Montgomery, "Division by
+// invariant integers using multiplication", 1994): with l = ceil(log2 d),
+// m = floor(2^32 (2^l - d) / d) + 1, q = (mulhi(m, x) + x) >> l.
+struct FastDiv {
+    uint32_t d, m, l;
+};
+inline FastDiv make_fastdiv(uint32_t d) {
+    FastDiv f;
+    f.d = d;
+    f.l = 0;
+    while ((1ull << f.l) < d) ++f.l;
+    f.m = (uint32_t)((((1ull << 32) * ((1ull << f.l) - d)) / d) + 1);
+    return f;
+}
+__device__ __forceinline__ uint32_t fdiv(uint32_t x, const FastDiv& f) {
+    return (__umulhi(f.m, x) + x) >> f.l;
+}
+
+// XCD-aware persistent schedule.  Work items 0 .. W-1 are in "pair-major"
+// order (all tokens of one (batch, KV head) pair, then the next pair).
+// Workgroups are dealt to the 8 XCDs round robin, so XCD x runs workgroups
+// x, x+8, ...; it gets the contiguous item range [x*C, (x+1)*C), C = ceil(W/8),
+// and its teams walk that range side by side, team k taking items
+// x*C + k, x*C + k + T, ... (T teams on the XCD).  At any moment an XCD is
+// inside one or two pairs, whose K/V rows then stay in its 4 MB L2.
+constexpr int kXcds = 8;
+struct Sched {
+    int u, step, end;
+};
+__device__ __forceinline__ Sched xcd_sched(int W, int team_size) {
+    const int x = blockIdx.x % kXcds;
+    const int wslot = blockIdx.x / kXcds;
+    const int teams_per_wg = kBlock / team_size;
+    const int nteams = (gridDim.x / kXcds) * teams_per_wg;
+    const int chunk = (W + kXcds - 1) / kXcds;
+    const int lo = x * chunk;
+    Sched s;
+    s.u = lo + wslot * teams_per_wg + (int)threadIdx.x / team_size;
+    s.step = nteams;
+    s.end = min(W, lo + chunk);
+    return s;
+}
+
+// Unpack 8 bf16 (one 16-byte piece) to fp32, and fp32 to a double vector.
+__device__ __forceinline__ void bf16x8_to_f32(const uint4& u, float (&x)[8]) {
+    x[0] = bf16_lo(u.x); x[1] = bf16_hi(u.x);
+    x[2] = bf16_lo(u.y); x[3] = bf16_hi(u.y);
+    x[4] = bf16_lo(u.z); x[5] = bf16_hi(u.z);
+    x[6] = bf16_lo(u.w); x[7] = bf16_hi(u.w);
+}
+
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+
+// Dot product of two 16-byte bf16 pieces, accumulated in fp32.
+__device__ __forceinline__ float dot_bf16x8(const uint4& a, const uint4& b) {
+    float s = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a.x),
+                                              __builtin_bit_cast(bf16x2_t, b.x), 0.0f, false);
+    s = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a.y),
+                                        __builtin_bit_cast(bf16x2_t, b.y), s, false);
+    s = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a.z),
+                                        __builtin_bit_cast(bf16x2_t, b.z), s, false);
+    s = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a.w),
+                                        __builtin_bit_cast(bf16x2_t, b.w), s, false);
+    return s;
+}
+
+// Two fp32 values to packed bf16 (hardware round to nearest even).
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+    const bf16x2_t v = {(__bf16)a, (__bf16)b};
+    return __builtin_bit_cast(uint32_t, v);
+}
+
+}  // namespace gm

@@ -27,6 +27,7 @@
 // fp32 sums of dk/dv may differ in the last bits between runs.
 #include "gm_common.h"
 #include "gm_internal.h"
+#include "gm_wave.h"
 
 #include <math.h>
 
@@ -373,12 +374,228 @@ __global__ __launch_bounds__(kBlock) void sea_bwd_dst_kernel(SeaBwdArgs a) {
     }
 }
 
-template <typename T, int G>
-hipError_t run(const SeaBwdArgs& a, long long E, hipStream_t st) {
-    const long long src_threads = (long long)a.U * a.ts.team;
-    hipLaunchKernelGGL((sea_bwd_src_kernel<T, G>),
-                       dim3((unsigned)((src_threads + kBlock - 1) / kBlock)), dim3(kBlock), 0, st,
-                       a);
+
+// ----------------------------------------------------------------- fast path
+// Same geometry as the forward's fast path: one 256-byte d-row per 16-lane
+// row, P = pow2(s) <= 4 slots (source pass) or P incoming edges (target
+// pass) in consecutive rows, persistent XCD-aware loops in pair-major order.
+struct SeaBwdFast {
+    const char* q;
+    const char* k;
+    const char* v;
+    const char* dout;
+    const int32_t* idx;
+    const float* w;
+    char* dq;
+    char* dk;
+    char* dv;
+    float* dw;
+    Workspace ws;
+    int n, hq, hkv, s, U;
+    float scale;
+    FastDiv fd_n, fd_hkv, fd_s;
+};
+
+struct Pos {
+    int unit, bi, kvrow0;
+};
+
+__device__ __forceinline__ Pos pos_of(int u, const SeaBwdFast& a) {
+    const int pair = (int)fdiv((uint32_t)u, a.fd_n);
+    const int i = u - pair * a.n;
+    const int b = (int)fdiv((uint32_t)pair, a.fd_hkv);
+    const int h = pair - b * a.hkv;
+    Pos p;
+    p.bi = b * a.n + i;
+    p.unit = p.bi * a.hkv + h;
+    p.kvrow0 = b * a.n * a.hkv + h;
+    return p;
+}
+
+template <typename A, int V>
+__device__ __forceinline__ void unpack16(const uint4& u, A (&x)[V]) {
+    if constexpr (V == 8) {
+        float f[8];
+        bf16x8_to_f32(u, f);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) x[e] = f[e];
+    } else {
+        x[0] = __uint_as_float(u.x); x[1] = __uint_as_float(u.y);
+        x[2] = __uint_as_float(u.z); x[3] = __uint_as_float(u.w);
+    }
+}
+
+template <int V, typename A>
+__device__ __forceinline__ A dot16(const uint4& a, const uint4& b) {
+    if constexpr (V == 8) {
+        return dot_bf16x8(a, b);
+    } else {
+        return (A)__uint_as_float(a.x) * (A)__uint_as_float(b.x) +
+               (A)__uint_as_float(a.y) * (A)__uint_as_float(b.y) +
+               (A)__uint_as_float(a.z) * (A)__uint_as_float(b.z) +
+               (A)__uint_as_float(a.w) * (A)__uint_as_float(b.w);
+    }
+}
+
+template <int L, typename A>
+__device__ __forceinline__ void store_f32(char* p, const A* x) {
+    store_n<L>(reinterpret_cast<float*>(p), x);
+}
+
+template <typename T, int G, int P>
+__global__ __launch_bounds__(kBlock) void sea_bwd_src_fast_kernel(SeaBwdFast a) {
+    using A = typename io<T>::acc;
+    constexpr int V = io<T>::V;
+    constexpr int ROW = 256;            // bytes of one bf16/fp32 input d-row
+    constexpr int FROW = ROW * 4 / (int)sizeof(T);   // bytes of the fp32 gradient row
+    constexpr int L = V / P;
+    const int lane = threadIdx.x & (kWave - 1);
+    const int r = lane & 15;
+    const int row = lane >> 4;
+    const int slot = row & (P - 1);
+    const A c = (A)a.scale * (A)1.4426950408889634;
+    const A sc = (A)a.scale;
+    const A NEG = -INFINITY;
+    Sched sch = xcd_sched(a.U, 16 * P);
+
+    auto fetch = [&](int u, Pos& pos, int& j, float& wt) {
+        j = 0;
+        wt = 0.0f;
+        if (u < sch.end) {
+            pos = pos_of(u, a);
+            if (slot < a.s) {
+                const int e = pos.unit * a.s + slot;
+                j = a.idx[e];
+                wt = a.w[e];
+            }
+        }
+    };
+    Pos pos{0, 0, 0};
+    int j;
+    float wt;
+    fetch(sch.u, pos, j, wt);
+    for (int u = sch.u; u < sch.end; u += sch.step) {
+        Pos npos = pos;
+        int nj;
+        float nwt;
+        fetch(u + sch.step, npos, nj, nwt);
+
+        const bool live = wt > 0.0f;
+        const int kvrow = pos.kvrow0 + (live ? j : 0) * a.hkv;
+        const uint32_t kvoff = (uint32_t)kvrow * ROW + r * 16;
+        const uint4 kr = *reinterpret_cast<const uint4*>(a.k + kvoff);
+        const uint4 vr = *reinterpret_cast<const uint4*>(a.v + kvoff);
+        const int h = pos.unit - pos.bi * a.hkv;
+        const uint32_t qrow = (uint32_t)(pos.bi * a.hq + h * G);
+        uint4 qr[G], dr[G];
+#pragma unroll
+        for (int g = 0; g < G; ++g) {
+            qr[g] = *reinterpret_cast<const uint4*>(a.q + (qrow + g) * ROW + r * 16);
+            dr[g] = *reinterpret_cast<const uint4*>(a.dout + (qrow + g) * ROW + r * 16);
+        }
+        if (live && r == 0) atomicAdd(a.ws.cnt + kvrow, 1);
+        const A lw = live ? (A)log2f(wt) : NEG;
+        A kf[V];
+        unpack16<A, V>(kr, kf);
+        A dws = 0;
+        float2* cp = a.ws.coef + ((size_t)pos.unit * a.s + slot) * G;
+#pragma unroll
+        for (int g = 0; g < G; ++g) {
+            const A sd = row_sum16(dot16<V, A>(qr[g], kr));
+            const A gd = row_sum16(dot16<V, A>(dr[g], vr));
+            const A ls = sd * c;
+            const A l = live ? ls + lw : NEG;
+            const A M = rows_max<P>(l);
+            A ex, invZ, pw;
+            if constexpr (V == 8) {
+                ex = live ? __builtin_amdgcn_exp2f(l - M) : 0.0f;
+                const A Z = rows_sum<P>(ex);
+                invZ = Z > 0.0f ? __builtin_amdgcn_rcpf(Z) : 0.0f;
+                pw = live ? __builtin_amdgcn_exp2f(ls - M) : 0.0f;
+            } else {
+                ex = live ? exp2(l - M) : 0.0;
+                const A Z = rows_sum<P>(ex);
+                invZ = Z > 0.0 ? 1.0 / Z : 0.0;
+                pw = live ? exp2(ls - M) : 0.0;
+            }
+            const A p = ex * invZ;
+            const A gbar = rows_sum<P>(p * gd);
+            const A dls = p * (gd - gbar) * sc;
+            A dqv[V];
+#pragma unroll
+            for (int e = 0; e < V; ++e) dqv[e] = dls * kf[e];
+            rows_reduce_scatter<P, V>(dqv);
+            store_f32<L>(a.dq + (qrow + g) * FROW + r * 16 * 4 / (int)sizeof(T) +
+                             rs_offset<V, P>(row) * 4,
+                         dqv);
+            if (live && r == 0) cp[g] = make_float2((float)dls, (float)p);
+            dws += pw * invZ * (gd - gbar);
+        }
+        if (r == 0 && slot < a.s) a.dw[(size_t)pos.unit * a.s + slot] = (float)dws;
+        pos = npos;
+        j = nj;
+        wt = nwt;
+    }
+}
+
+template <typename T, int G, int P>
+__global__ __launch_bounds__(kBlock) void sea_bwd_dst_fast_kernel(SeaBwdFast a) {
+    using A = typename io<T>::acc;
+    constexpr int V = io<T>::V;
+    constexpr int ROW = 256;
+    constexpr int FROW = ROW * 4 / (int)sizeof(T);
+    constexpr int L = V / P;
+    const int lane = threadIdx.x & (kWave - 1);
+    const int r = lane & 15;
+    const int row = lane >> 4;
+    const int slot = row & (P - 1);
+    Sched sch = xcd_sched(a.U, 16 * P);
+    for (int u = sch.u; u < sch.end; u += sch.step) {
+        const Pos pos = pos_of(u, a);
+        const int h = pos.unit - pos.bi * a.hkv;
+        const int beg = a.ws.off[pos.unit], end = a.ws.off[pos.unit + 1];
+        A ak[V], av[V];
+#pragma unroll
+        for (int e = 0; e < V; ++e) { ak[e] = 0; av[e] = 0; }
+        for (int e0 = beg; e0 < end; e0 += P) {
+            const int ei = e0 + slot;
+            if (ei < end) {
+                const int eid = a.ws.list[ei];
+                const int src = (int)fdiv((uint32_t)eid, a.fd_s);            // source unit
+                const int sbi = (int)fdiv((uint32_t)src, a.fd_hkv);          // its b*n + i
+                const uint32_t qrow = (uint32_t)(sbi * a.hq + h * G);
+                const float2* cf = a.ws.coef + (size_t)eid * G;
+                uint4 qr[G], dr[G];
+                float2 co[G];
+#pragma unroll
+                for (int g = 0; g < G; ++g) {
+                    qr[g] = *reinterpret_cast<const uint4*>(a.q + (qrow + g) * ROW + r * 16);
+                    dr[g] = *reinterpret_cast<const uint4*>(a.dout + (qrow + g) * ROW + r * 16);
+                    co[g] = cf[g];
+                }
+#pragma unroll
+                for (int g = 0; g < G; ++g) {
+                    A qf[V], df[V];
+                    unpack16<A, V>(qr[g], qf);
+                    unpack16<A, V>(dr[g], df);
+#pragma unroll
+                    for (int e = 0; e < V; ++e) {
+                        ak[e] += (A)co[g].x * qf[e];
+                        av[e] += (A)co[g].y * df[e];
+                    }
+                }
+            }
+        }
+        rows_reduce_scatter<P, V>(ak);
+        rows_reduce_scatter<P, V>(av);
+        const uint32_t o = (uint32_t)pos.unit * FROW + r * 16 * 4 / (int)sizeof(T) +
+                           rs_offset<V, P>(row) * 4;
+        store_f32<L>(a.dk + o, ak);
+        store_f32<L>(a.dv + o, av);
+    }
+}
+
+void launch_index(const SeaBwdArgs& a, long long E, hipStream_t st) {
     const unsigned sblocks = (unsigned)((a.U + kScanPerBlock - 1) / kScanPerBlock);
     hipLaunchKernelGGL(scan_local_kernel, dim3(sblocks), dim3(1024), 0, st,
                        (const int*)a.ws.cnt, a.ws.off, a.ws.bsum, a.U);
@@ -388,6 +605,15 @@ hipError_t run(const SeaBwdArgs& a, long long E, hipStream_t st) {
     if (fb > 16384) fb = 16384;
     hipLaunchKernelGGL(edge_fill_kernel, dim3((unsigned)fb), dim3(kBlock), 0, st, a.idx, a.w, a.n,
                        a.hkv, a.s, E, a.ws.cnt, a.ws.list);
+}
+
+template <typename T, int G>
+hipError_t run(const SeaBwdArgs& a, long long E, hipStream_t st) {
+    const long long src_threads = (long long)a.U * a.ts.team;
+    hipLaunchKernelGGL((sea_bwd_src_kernel<T, G>),
+                       dim3((unsigned)((src_threads + kBlock - 1) / kBlock)), dim3(kBlock), 0, st,
+                       a);
+    launch_index(a, E, st);
     const long long dst_threads = (long long)a.U * a.tt.team;
     hipLaunchKernelGGL((sea_bwd_dst_kernel<T, G>),
                        dim3((unsigned)((dst_threads + kBlock - 1) / kBlock)), dim3(kBlock), 0, st,
@@ -403,6 +629,40 @@ hipError_t dispatch_g(const SeaBwdArgs& a, int G, long long E, hipStream_t st) {
         case 4: return run<T, 4>(a, E, st);
         case 8: return run<T, 8>(a, E, st);
         case 16: return run<T, 16>(a, E, st);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+template <typename T, int G, int P, int PD>
+hipError_t run_fast(const SeaBwdArgs& g, const SeaBwdFast& a, long long E, hipStream_t st) {
+    const int nsrc = persistent_grid(reinterpret_cast<const void*>(
+                                         &sea_bwd_src_fast_kernel<T, G, P>),
+                                     a.U, kBlock / (16 * P));
+    hipLaunchKernelGGL((sea_bwd_src_fast_kernel<T, G, P>), dim3(nsrc), dim3(kBlock), 0, st, a);
+    launch_index(g, E, st);
+    const int ndst = persistent_grid(reinterpret_cast<const void*>(
+                                         &sea_bwd_dst_fast_kernel<T, G, PD>),
+                                     a.U, kBlock / (16 * PD));
+    hipLaunchKernelGGL((sea_bwd_dst_fast_kernel<T, G, PD>), dim3(ndst), dim3(kBlock), 0, st, a);
+    return hipGetLastError();
+}
+
+template <typename T, int G>
+hipError_t fast_p(const SeaBwdArgs& g, const SeaBwdFast& a, long long E, hipStream_t st) {
+    if (a.s <= 1) return run_fast<T, G, 1, 2>(g, a, E, st);
+    if (a.s <= 2) return run_fast<T, G, 2, 2>(g, a, E, st);
+    return run_fast<T, G, 4, 4>(g, a, E, st);
+}
+
+template <typename T>
+hipError_t dispatch_fast(const SeaBwdArgs& g, const SeaBwdFast& a, int G, long long E,
+                         hipStream_t st) {
+    switch (G) {
+        case 1: return fast_p<T, 1>(g, a, E, st);
+        case 2: return fast_p<T, 2>(g, a, E, st);
+        case 4: return fast_p<T, 4>(g, a, E, st);
+        case 8: return fast_p<T, 8>(g, a, E, st);
+        case 16: return fast_p<T, 16>(g, a, E, st);
         default: return hipErrorInvalidValue;
     }
 }
@@ -440,6 +700,21 @@ hipError_t launch_sea_backward(int B, int n, int hq, int hkv, int d, bool bf16, 
     if (e == hipSuccess && a.ts.nchunk > 1) e = launch_zero_f32(dw, (size_t)a.U * s, st);
     if (e != hipSuccess) return e;
     const long long E = (long long)a.U * s;
+    if (sea_fast_shape(B, n, hq, hkv, d, bf16, s) &&
+        (long long)B * n * hq * d * 4 < (1ll << 32)) {
+        SeaBwdFast f;
+        f.q = static_cast<const char*>(q); f.k = static_cast<const char*>(k);
+        f.v = static_cast<const char*>(v); f.dout = static_cast<const char*>(dout);
+        f.idx = idx; f.w = w;
+        f.dq = reinterpret_cast<char*>(dq); f.dk = reinterpret_cast<char*>(dk);
+        f.dv = reinterpret_cast<char*>(dv); f.dw = dw;
+        f.ws = a.ws;
+        f.n = n; f.hq = hq; f.hkv = hkv; f.s = s; f.U = a.U; f.scale = scale;
+        f.fd_n = make_fastdiv((uint32_t)n);
+        f.fd_hkv = make_fastdiv((uint32_t)hkv);
+        f.fd_s = make_fastdiv((uint32_t)s);
+        return bf16 ? dispatch_fast<bf16_t>(a, f, G, E, st) : dispatch_fast<float>(a, f, G, E, st);
+    }
     return bf16 ? dispatch_g<bf16_t>(a, G, E, st) : dispatch_g<float>(a, G, E, st);
 }
 

@@ -18,6 +18,7 @@
 // few FLOPs per byte (HBM-bound).
 #include "gm_common.h"
 #include "gm_internal.h"
+#include "gm_wave.h"
 
 #include <math.h>
 
@@ -170,6 +171,146 @@ __global__ __launch_bounds__(kBlock) void sea_fwd_kernel(SeaFwdArgs a) {
     }
 }
 
+
+// ----------------------------------------------------------------- fast path
+// One d-row = 256 bytes (bf16 d=128 or fp32 d=64) = one 16-lane row of the
+// wave, P = pow2(s) <= 4 slots in consecutive rows, so a team is 16P lanes and
+// a wave serves 4/P units at once.  Persistent XCD-aware loop over units in
+// pair-major order; the next unit's edge slot is fetched one unit ahead.
+struct SeaFwdFast {
+    const char* q;
+    const char* k;
+    const char* v;
+    const int32_t* idx;
+    const float* w;
+    char* o;
+    int n, hq, hkv, s, U;
+    float scale;
+    FastDiv fd_n, fd_hkv;
+};
+
+struct UnitPos {
+    int unit;      // (b*n + i)*hkv + h
+    int bi;        // b*n + i
+    int kvrow0;    // K/V row of token 0 of the pair: b*n*hkv + h
+};
+
+__device__ __forceinline__ UnitPos unit_pos(int u, int n, int hkv, const FastDiv& fd_n,
+                                            const FastDiv& fd_hkv) {
+    const int pair = (int)fdiv((uint32_t)u, fd_n);
+    const int i = u - pair * n;
+    const int b = (int)fdiv((uint32_t)pair, fd_hkv);
+    const int h = pair - b * hkv;
+    UnitPos p;
+    p.bi = b * n + i;
+    p.unit = p.bi * hkv + h;
+    p.kvrow0 = b * n * hkv + h;
+    return p;
+}
+
+template <typename T, int G, int P>
+__global__ __launch_bounds__(kBlock) void sea_fwd_fast_kernel(SeaFwdFast a) {
+    using A = typename io<T>::acc;
+    constexpr int V = io<T>::V;          // elements per lane (16 bytes)
+    constexpr int ROW = 256;             // bytes per d-row
+    const int lane = threadIdx.x & (kWave - 1);
+    const int r = lane & 15;
+    const int row = lane >> 4;
+    const int slot = row & (P - 1);
+    const A c = (A)a.scale * (A)1.4426950408889634;
+    const A NEG = -INFINITY;
+    Sched sc = xcd_sched(a.U, 16 * P);
+
+    // edge slot of unit u for this lane: (token index, weight); dead -> (0, 0)
+    auto fetch = [&](int u, UnitPos& pos, int& j, float& wt) {
+        j = 0;
+        wt = 0.0f;
+        if (u < sc.end) {
+            pos = unit_pos(u, a.n, a.hkv, a.fd_n, a.fd_hkv);
+            if (slot < a.s) {
+                const int e = pos.unit * a.s + slot;
+                j = a.idx[e];
+                wt = a.w[e];
+            }
+        }
+    };
+    UnitPos pos{0, 0, 0};
+    int j;
+    float wt;
+    fetch(sc.u, pos, j, wt);
+    for (int u = sc.u; u < sc.end; u += sc.step) {
+        UnitPos npos = pos;
+        int nj;
+        float nwt;
+        fetch(u + sc.step, npos, nj, nwt);
+
+        const bool live = wt > 0.0f;
+        const uint32_t kvoff = (uint32_t)(pos.kvrow0 + (live ? j : 0) * a.hkv) * ROW + r * 16;
+        const uint4 kr = *reinterpret_cast<const uint4*>(a.k + kvoff);
+        const uint4 vr = *reinterpret_cast<const uint4*>(a.v + kvoff);
+        const uint32_t qoff = (uint32_t)(pos.bi * a.hq + (pos.unit - pos.bi * a.hkv) * G) * ROW +
+                              r * 16;
+        uint4 qr[G];
+#pragma unroll
+        for (int g = 0; g < G; ++g) qr[g] = *reinterpret_cast<const uint4*>(a.q + qoff + g * ROW);
+        const A lw = live ? (A)log2f(wt) : NEG;
+        A vf[V];
+        if constexpr (V == 8) {
+            bf16x8_to_f32(vr, vf);
+        } else {
+            vf[0] = __uint_as_float(vr.x); vf[1] = __uint_as_float(vr.y);
+            vf[2] = __uint_as_float(vr.z); vf[3] = __uint_as_float(vr.w);
+        }
+#pragma unroll
+        for (int g = 0; g < G; ++g) {
+            A dot;
+            if constexpr (V == 8) {
+                dot = dot_bf16x8(qr[g], kr);
+            } else {
+                dot = (A)__uint_as_float(qr[g].x) * (A)__uint_as_float(kr.x) +
+                      (A)__uint_as_float(qr[g].y) * (A)__uint_as_float(kr.y) +
+                      (A)__uint_as_float(qr[g].z) * (A)__uint_as_float(kr.z) +
+                      (A)__uint_as_float(qr[g].w) * (A)__uint_as_float(kr.w);
+            }
+            dot = row_sum16(dot);
+            const A l = live ? dot * c + lw : NEG;
+            const A M = rows_max<P>(l);
+            A ex;
+            if constexpr (V == 8) ex = live ? __builtin_amdgcn_exp2f(l - M) : 0.0f;
+            else ex = live ? exp2(l - M) : 0.0;
+            const A Z = rows_sum<P>(ex);
+            A ov[V];
+#pragma unroll
+            for (int e = 0; e < V; ++e) ov[e] = ex * vf[e];
+            rows_reduce_scatter<P, V>(ov);
+            A inv;
+            if constexpr (V == 8) inv = Z > 0.0f ? __builtin_amdgcn_rcpf(Z) : 0.0f;
+            else inv = Z > 0.0 ? 1.0 / Z : 0.0;
+            constexpr int L = V / P;
+#pragma unroll
+            for (int e = 0; e < L; ++e) ov[e] *= inv;
+            char* op = a.o + qoff + g * ROW + rs_offset<V, P>(row) * (int)sizeof(T);
+            if constexpr (V == 8) {
+                if constexpr (L == 2) {
+                    *reinterpret_cast<uint32_t*>(op) = pack_bf16x2(ov[0], ov[1]);
+                } else if constexpr (L == 4) {
+                    *reinterpret_cast<uint2*>(op) =
+                        make_uint2(pack_bf16x2(ov[0], ov[1]), pack_bf16x2(ov[2], ov[3]));
+                } else {
+                    *reinterpret_cast<uint4*>(op) =
+                        make_uint4(pack_bf16x2(ov[0], ov[1]), pack_bf16x2(ov[2], ov[3]),
+                                   pack_bf16x2(ov[4], ov[5]), pack_bf16x2(ov[6], ov[7]));
+                }
+            } else {
+                store_n<L>(reinterpret_cast<float*>(op), ov);
+            }
+        }
+        pos = npos;
+        j = nj;
+        wt = nwt;
+    }
+}
+
 template <typename T, int G>
 hipError_t run(const SeaFwdArgs& a, hipStream_t st) {
     const long long threads = (long long)a.U * a.ts.team;
@@ -190,7 +331,40 @@ hipError_t dispatch_g(const SeaFwdArgs& a, int G, hipStream_t st) {
     }
 }
 
+template <typename T, int G, int P>
+hipError_t run_fast(const SeaFwdFast& a, hipStream_t st) {
+    const void* fn = reinterpret_cast<const void*>(&sea_fwd_fast_kernel<T, G, P>);
+    const int nwg = persistent_grid(fn, a.U, kBlock / (16 * P));
+    hipLaunchKernelGGL((sea_fwd_fast_kernel<T, G, P>), dim3(nwg), dim3(kBlock), 0, st, a);
+    return hipGetLastError();
+}
+
+template <typename T, int G>
+hipError_t fast_p(const SeaFwdFast& a, hipStream_t st) {
+    if (a.s <= 1) return run_fast<T, G, 1>(a, st);
+    if (a.s <= 2) return run_fast<T, G, 2>(a, st);
+    return run_fast<T, G, 4>(a, st);
+}
+
+template <typename T>
+hipError_t fast_g(const SeaFwdFast& a, int G, hipStream_t st) {
+    switch (G) {
+        case 1: return fast_p<T, 1>(a, st);
+        case 2: return fast_p<T, 2>(a, st);
+        case 4: return fast_p<T, 4>(a, st);
+        case 8: return fast_p<T, 8>(a, st);
+        case 16: return fast_p<T, 16>(a, st);
+        default: return hipErrorInvalidValue;
+    }
+}
+
 }  // namespace
+
+bool sea_fast_shape(int B, int n, int hq, int hkv, int d, bool bf16, int s) {
+    const long long es = bf16 ? 2 : 4;
+    const long long qbytes = (long long)B * n * hq * d * es;
+    return d * es == 256 && s <= 4 && qbytes < (1ll << 32);
+}
 
 hipError_t launch_sea_forward(int B, int n, int hq, int hkv, int d, bool bf16, float scale,
                               const void* q, const void* k, const void* v,
@@ -203,6 +377,15 @@ hipError_t launch_sea_forward(int B, int n, int hq, int hkv, int d, bool bf16, f
     a.scale = scale;
     a.ts = sea_team(d, bf16 ? 2 : 4, s);
     const int G = hq / hkv;
+    if (sea_fast_shape(B, n, hq, hkv, d, bf16, s)) {
+        SeaFwdFast f;
+        f.q = static_cast<const char*>(q); f.k = static_cast<const char*>(k);
+        f.v = static_cast<const char*>(v); f.idx = idx; f.w = w; f.o = static_cast<char*>(o);
+        f.n = n; f.hq = hq; f.hkv = hkv; f.s = s; f.U = a.U; f.scale = scale;
+        f.fd_n = make_fastdiv((uint32_t)n);
+        f.fd_hkv = make_fastdiv((uint32_t)hkv);
+        return bf16 ? fast_g<bf16_t>(f, G, st) : fast_g<float>(f, G, st);
+    }
     return bf16 ? dispatch_g<bf16_t>(a, G, st) : dispatch_g<float>(a, G, st);
 }
 

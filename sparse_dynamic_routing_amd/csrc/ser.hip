@@ -221,6 +221,29 @@ hipError_t run_bwd(const SerBwdArgs& a, hipStream_t st) {
 
 }  // namespace
 
+int persistent_grid(const void* kernel, int items, int per_wg) {
+    static int cus_by_dev[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
+    int cus = cus_by_dev[dev];
+    if (!cus) {
+        if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+            cus <= 0)
+            cus = 256;
+        cus_by_dev[dev] = cus;
+    }
+    int per_cu = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, kBlock, 0) != hipSuccess ||
+        per_cu <= 0)
+        per_cu = 1;
+    long long full = (long long)cus * per_cu;
+    full -= full % 8;
+    if (full < 8) full = 8;
+    long long need = ((long long)items + per_wg - 1) / per_wg;
+    need = (need + 7) / 8 * 8;
+    return (int)(need < full ? need : full);
+}
+
 hipError_t launch_zero_f32(float* p, size_t count, hipStream_t st) {
     if (!count) return hipSuccess;
     hipLaunchKernelGGL(zero_f32_kernel, dim3(grid_for(count / 4 + 1, 8192)), dim3(kBlock), 0, st,

@@ -33,6 +33,11 @@ SEA_SHAPES = [
     (torch.float32, 128, 2, 4, 37),
     (torch.float32, 256, 1, 3, 19),     # 64 lanes per row: one slot per chunk
     (torch.float32, 32, 4, 9, 41),
+    (torch.float32, 64, 2, 4, 37),      # fp32 rows of 256 bytes (fp64 arithmetic)
+    (torch.float32, 64, 4, 1, 26),
+    (torch.bfloat16, 128, 16, 1, 23),   # one slot, sixteen query heads
+    (torch.bfloat16, 128, 8, 2, 45),
+    (torch.bfloat16, 128, 2, 4, 1),     # fewer units than XCDs
 ]
 
 
