@@ -134,8 +134,9 @@ gm_status gm_sea_backward(int B, int n, int hq, int hkv, int d, gm_dtype dt,
                           hipStream_t stream);
 
 /*
- * Bytes of device workspace gm_ser_backward needs for these sizes
- * (fp64 accumulators for dw1 and dw2, one array when they alias).
+ * Bytes of device workspace gm_ser_backward needs for these sizes: fp64
+ * accumulators for dw1 and dw2 (`aliased` is accepted for symmetry with the
+ * call; both layouts need the two arrays).
  */
 size_t gm_ser_backward_workspace_bytes(int B, int n, int hkv, int s2, int s3,
                                        int aliased);

@@ -160,10 +160,10 @@ gm_status gm_sea_backward(int B, int n, int hq, int hkv, int d, gm_dtype dt, flo
 }
 
 size_t gm_ser_backward_workspace_bytes(int B, int n, int hkv, int s2, int s3, int aliased) {
+    (void)aliased;
     if (check_units(B, n, hkv) != GM_OK || s2 < 1 || s3 < 1) return 0;
     const size_t rows = (size_t)B * n * hkv;
-    const size_t a = rows * s2 * sizeof(double);
-    return aliased ? a : a + rows * s3 * sizeof(double);
+    return rows * s2 * sizeof(double) + rows * s3 * sizeof(double);
 }
 
 gm_status gm_ser_backward(int B, int n, int hkv, const int32_t* idx1, const float* w1, int s2,
@@ -199,7 +199,7 @@ gm_status gm_ser_backward(int B, int n, int hkv, const int32_t* idx1, const floa
         }
     }
     double* ws1 = static_cast<double*>(workspace);
-    double* ws2 = aliased ? ws1 : ws1 + rows * s2;
+    double* ws2 = ws1 + rows * s2;
     return hip_status(gm::launch_ser_backward(B, n, hkv, idx1, w1, s2, idx2, w2, s3, idx_out,
                                               w_out, s1, dw_out, dw1, dw2, ws1, ws2, stream));
 }

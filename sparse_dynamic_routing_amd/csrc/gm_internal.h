@@ -6,6 +6,8 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include "gm_wave.h"
+
 namespace gm {
 
 // Lane team of one unit in the SEA kernels: R lanes hold one d-row (16 bytes
@@ -44,6 +46,10 @@ hipError_t launch_ser_backward(int B, int n, int hkv, const int32_t* idx1, const
 
 hipError_t launch_check_edges(int B, int n, int hkv, const int32_t* idx, const float* w, int s,
                               unsigned long long* counts, hipStream_t st);
+
+struct SegPlan;
+// Segment plan of the XCD-aware schedule for B*hkv pairs of n tokens.
+void make_seg_plan(SegPlan& sp, int B, int n, int hkv);
 
 // Workgroups for a persistent XCD-aware kernel: as many as fit on the device
 // at once (occupancy x compute units), a multiple of 8 (one share per XCD),

@@ -137,29 +137,43 @@ __device__ __forceinline__ uint32_t fdiv(uint32_t x, const FastDiv& f) {
     return (__umulhi(f.m, x) + x) >> f.l;
 }
 
-// XCD-aware persistent schedule.  Work items 0 .. W-1 are in "pair-major"
-// order (all tokens of one (batch, KV head) pair, then the next pair).
-// Workgroups are dealt to the 8 XCDs round robin, so XCD x runs workgroups
-// x, x+8, ...; it gets the contiguous item range [x*C, (x+1)*C), C = ceil(W/8),
-// and its teams walk that range side by side, team k taking items
-// x*C + k, x*C + k + T, ... (T teams on the XCD).  At any moment an XCD is
-// inside one or two pairs, whose K/V rows then stay in its 4 MB L2.
+// XCD-aware persistent schedule over units (or K/V rows) of B*hkv (batch,
+// KV head) pairs of n tokens.  Each pair is cut into S = 2^lgS segments of
+// L = n / S tokens (S > 1 only when there are few pairs), and segment k goes
+// to XCD k % 8: workgroups are dealt to the 8 XCDs round robin, so XCD x runs
+// workgroups x, x+8, ... and takes segments x, x+8, ... in that order.  The
+// XCD's teams walk its items side by side, team t taking items t, t+T, ...
+// (T teams on the XCD), so at any moment an XCD is inside one or two pairs,
+// whose K/V rows stay in its 4 MB L2, while the 8 XCDs work on 8 different
+// pairs (different KV heads of a batch), which spreads the accesses of the
+// moment over all HBM channels.
 constexpr int kXcds = 8;
-struct Sched {
-    int u, step, end;
+struct SegPlan {
+    int n, hkv, nseg, lgS, L;
+    FastDiv fd_L, fd_hkv;
 };
-__device__ __forceinline__ Sched xcd_sched(int W, int team_size) {
+struct Sched {
+    int q, step, end;   // this team's item positions in its XCD's list
+    int x;              // XCD
+};
+__device__ __forceinline__ Sched xcd_sched(const SegPlan& sp, int team_size) {
     const int x = blockIdx.x % kXcds;
     const int wslot = blockIdx.x / kXcds;
     const int teams_per_wg = kBlock / team_size;
-    const int nteams = (gridDim.x / kXcds) * teams_per_wg;
-    const int chunk = (W + kXcds - 1) / kXcds;
-    const int lo = x * chunk;
     Sched s;
-    s.u = lo + wslot * teams_per_wg + (int)threadIdx.x / team_size;
-    s.step = nteams;
-    s.end = min(W, lo + chunk);
+    s.x = x;
+    s.q = wslot * teams_per_wg + (int)threadIdx.x / team_size;
+    s.step = (gridDim.x / kXcds) * teams_per_wg;
+    const int nseg_x = x < sp.nseg ? (sp.nseg - x + kXcds - 1) / kXcds : 0;
+    s.end = nseg_x * sp.L;
     return s;
+}
+// Item q of XCD x -> (pair, token).
+__device__ __forceinline__ void sched_item(const SegPlan& sp, int x, int q, int& pair, int& i) {
+    const int m = (int)fdiv((uint32_t)q, sp.fd_L);
+    const int k = x + kXcds * m;
+    pair = k >> sp.lgS;
+    i = (k & ((1 << sp.lgS) - 1)) * sp.L + (q - m * sp.L);
 }
 
 // Unpack 8 bf16 (one 16-byte piece) to fp32, and fp32 to a double vector.

@@ -41,14 +41,16 @@ size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 struct Workspace {
     float2* coef;   // [U * s * G]  (scale * dl, p) per edge and head
-    int* cnt;       // [U]  in-degree, then the fill cursor
-    int* off;       // [U + 1]  segment offsets
+    int* cnt;       // [U]  in-degree, then the fill cursor (long sequences)
+    int* off;       // [U + 1]  segment offsets (long sequences)
     int* bsum;      // [ceil(U / kScanPerBlock)]
     int* list;      // [U * s]  edge ids grouped by target row
+    int* beg;       // [U]  per K/V row in pair-major order: first list slot
+    int* len;       // [U]  ... and number of incoming edges
 };
 
 struct WsLayout {
-    size_t coef, cnt, off, bsum, list, total;
+    size_t coef, cnt, off, bsum, list, beg, len, total;
 };
 
 WsLayout ws_layout(long long U, int s, int G) {
@@ -58,7 +60,9 @@ WsLayout ws_layout(long long U, int s, int G) {
     l.off = l.cnt + align256((size_t)U * sizeof(int));
     l.bsum = l.off + align256((size_t)(U + 1) * sizeof(int));
     l.list = l.bsum + align256((size_t)((U + kScanPerBlock - 1) / kScanPerBlock) * sizeof(int));
-    l.total = l.list + align256((size_t)U * s * sizeof(int));
+    l.beg = l.list + align256((size_t)U * s * sizeof(int));
+    l.len = l.beg + align256((size_t)U * sizeof(int));
+    l.total = l.len + align256((size_t)U * sizeof(int));
     return l;
 }
 
@@ -375,6 +379,87 @@ __global__ __launch_bounds__(kBlock) void sea_bwd_dst_kernel(SeaBwdArgs a) {
 }
 
 
+
+// Reverse edge index of one (batch, KV head) pair per workgroup, in LDS:
+// count the live edges per target token (LDS atomics), exclusive scan, then
+// place every edge id in its target's segment.  The pair's edges occupy the
+// fixed list range [pair * n * s, (pair + 1) * n * s), so no scan across
+// pairs is needed.  beg/len are indexed by pair-major row pair * n + j.
+// Each thread takes 4 tokens per batch and issues all their (s <= 4) slot
+// loads before using any, so a batch costs one memory round trip.
+constexpr int kSortMaxN = 16384;
+constexpr int kSortTok = 4;
+__global__ __launch_bounds__(1024) void pair_sort_kernel(const int32_t* idx, const float* w,
+                                                         int n, int hkv, int s, int* beg,
+                                                         int* len, int* list) {
+    __shared__ int cnt[kSortMaxN];
+    __shared__ int part[1024 / kWave];
+    const int pair = blockIdx.x;
+    const int b = pair / hkv, h = pair - (pair / hkv) * hkv;
+    const int lbase = pair * n * s;
+    for (int j = threadIdx.x; j < n; j += 1024) cnt[j] = 0;
+    __syncthreads();
+    // the (up to 4 x 4) slots of this thread's tokens in one batch
+    auto load = [&](int i0, int (&tj)[kSortTok * 4], int (&te)[kSortTok * 4]) {
+#pragma unroll
+        for (int k = 0; k < kSortTok; ++k) {
+            const int i = i0 + k * 1024 + (int)threadIdx.x;
+            const int e0 = ((b * n + i) * hkv + h) * s;
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+                const int slot = k * 4 + t;
+                te[slot] = -1;
+                tj[slot] = 0;
+                if (i < n && t < s) {
+                    const int e = e0 + t;
+                    const float wt = w[e];
+                    tj[slot] = idx[e];
+                    te[slot] = wt > 0.0f ? e : -1;
+                }
+            }
+        }
+    };
+    for (int i0 = 0; i0 < n; i0 += 1024 * kSortTok) {
+        int tj[kSortTok * 4], te[kSortTok * 4];
+        load(i0, tj, te);
+#pragma unroll
+        for (int k = 0; k < kSortTok * 4; ++k)
+            if (te[k] >= 0) atomicAdd(&cnt[tj[k]], 1);
+    }
+    __syncthreads();
+    // exclusive scan of cnt[0 .. n): each thread scans a contiguous run
+    const int per = (n + 1023) / 1024;
+    const int j0 = threadIdx.x * per;
+    int run = 0;
+    for (int j = j0; j < j0 + per && j < n; ++j) run += cnt[j];
+    const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
+    int inc = run;
+    for (int m = 1; m < kWave; m <<= 1) {
+        const int o = __shfl_up(inc, m, kWave);
+        if (lane >= m) inc += o;
+    }
+    if (lane == kWave - 1) part[wave] = inc;
+    __syncthreads();
+    int base = 0;
+    for (int k = 0; k < wave; ++k) base += part[k];
+    base += inc - run;
+    for (int j = j0; j < j0 + per && j < n; ++j) {
+        const int c = cnt[j];
+        beg[pair * n + j] = lbase + base;
+        len[pair * n + j] = c;
+        cnt[j] = base;   // becomes the fill cursor
+        base += c;
+    }
+    __syncthreads();
+    for (int i0 = 0; i0 < n; i0 += 1024 * kSortTok) {
+        int tj[kSortTok * 4], te[kSortTok * 4];
+        load(i0, tj, te);
+#pragma unroll
+        for (int k = 0; k < kSortTok * 4; ++k)
+            if (te[k] >= 0) list[lbase + atomicAdd(&cnt[tj[k]], 1)] = te[k];
+    }
+}
+
 // ----------------------------------------------------------------- fast path
 // Same geometry as the forward's fast path: one 256-byte d-row per 16-lane
 // row, P = pow2(s) <= 4 slots (source pass) or P incoming edges (target
@@ -393,22 +478,25 @@ struct SeaBwdFast {
     Workspace ws;
     int n, hq, hkv, s, U;
     float scale;
-    FastDiv fd_n, fd_hkv, fd_s;
+    FastDiv fd_s, fd_hkv;
+    SegPlan sp;
+    int global_index;   // 1: in-degrees counted here, offsets from the global scan
 };
 
 struct Pos {
-    int unit, bi, kvrow0;
+    int unit, bi, kvrow0, prow;   // prow = pair * n + i (pair-major row)
 };
 
-__device__ __forceinline__ Pos pos_of(int u, const SeaBwdFast& a) {
-    const int pair = (int)fdiv((uint32_t)u, a.fd_n);
-    const int i = u - pair * a.n;
-    const int b = (int)fdiv((uint32_t)pair, a.fd_hkv);
-    const int h = pair - b * a.hkv;
+__device__ __forceinline__ Pos pos_of(const SegPlan& sp, int x, int q) {
+    int pair, i;
+    sched_item(sp, x, q, pair, i);
+    const int b = (int)fdiv((uint32_t)pair, sp.fd_hkv);
+    const int h = pair - b * sp.hkv;
     Pos p;
-    p.bi = b * a.n + i;
-    p.unit = p.bi * a.hkv + h;
-    p.kvrow0 = b * a.n * a.hkv + h;
+    p.bi = b * sp.n + i;
+    p.unit = p.bi * sp.hkv + h;
+    p.kvrow0 = b * sp.n * sp.hkv + h;
+    p.prow = pair * sp.n + i;
     return p;
 }
 
@@ -456,13 +544,13 @@ __global__ __launch_bounds__(kBlock) void sea_bwd_src_fast_kernel(SeaBwdFast a) 
     const A c = (A)a.scale * (A)1.4426950408889634;
     const A sc = (A)a.scale;
     const A NEG = -INFINITY;
-    Sched sch = xcd_sched(a.U, 16 * P);
+    const Sched sch = xcd_sched(a.sp, 16 * P);
 
     auto fetch = [&](int u, Pos& pos, int& j, float& wt) {
         j = 0;
         wt = 0.0f;
         if (u < sch.end) {
-            pos = pos_of(u, a);
+            pos = pos_of(a.sp, sch.x, u);
             if (slot < a.s) {
                 const int e = pos.unit * a.s + slot;
                 j = a.idx[e];
@@ -470,11 +558,11 @@ __global__ __launch_bounds__(kBlock) void sea_bwd_src_fast_kernel(SeaBwdFast a) 
             }
         }
     };
-    Pos pos{0, 0, 0};
+    Pos pos{0, 0, 0, 0};
     int j;
     float wt;
-    fetch(sch.u, pos, j, wt);
-    for (int u = sch.u; u < sch.end; u += sch.step) {
+    fetch(sch.q, pos, j, wt);
+    for (int u = sch.q; u < sch.end; u += sch.step) {
         Pos npos = pos;
         int nj;
         float nwt;
@@ -493,7 +581,7 @@ __global__ __launch_bounds__(kBlock) void sea_bwd_src_fast_kernel(SeaBwdFast a) 
             qr[g] = *reinterpret_cast<const uint4*>(a.q + (qrow + g) * ROW + r * 16);
             dr[g] = *reinterpret_cast<const uint4*>(a.dout + (qrow + g) * ROW + r * 16);
         }
-        if (live && r == 0) atomicAdd(a.ws.cnt + kvrow, 1);
+        if (a.global_index && live && r == 0) atomicAdd(a.ws.cnt + kvrow, 1);
         const A lw = live ? (A)log2f(wt) : NEG;
         A kf[V];
         unpack16<A, V>(kr, kf);
@@ -549,21 +637,46 @@ __global__ __launch_bounds__(kBlock) void sea_bwd_dst_fast_kernel(SeaBwdFast a) 
     const int r = lane & 15;
     const int row = lane >> 4;
     const int slot = row & (P - 1);
-    Sched sch = xcd_sched(a.U, 16 * P);
-    for (int u = sch.u; u < sch.end; u += sch.step) {
-        const Pos pos = pos_of(u, a);
-        const int h = pos.unit - pos.bi * a.hkv;
-        const int beg = a.ws.off[pos.unit], end = a.ws.off[pos.unit + 1];
+    const Sched sch = xcd_sched(a.sp, 16 * P);
+
+    // row header: output row, head, and its segment [beg, end) of the list
+    struct Hdr {
+        int unit, h, beg, end;
+    };
+    auto header = [&](int u) {
+        Hdr hd{0, 0, 0, 0};
+        if (u < sch.end) {
+            const Pos pos = pos_of(a.sp, sch.x, u);
+            hd.unit = pos.unit;
+            hd.h = pos.unit - pos.bi * a.hkv;
+            if (a.global_index) {
+                hd.beg = a.ws.off[pos.unit];
+                hd.end = a.ws.off[pos.unit + 1];
+            } else {
+                hd.beg = a.ws.beg[pos.prow];
+                hd.end = hd.beg + a.ws.len[pos.prow];
+            }
+        }
+        return hd;
+    };
+    auto edge_at = [&](int ei, int end) { return ei < end ? a.ws.list[ei] : -1; };
+
+    Hdr h0 = header(sch.q);
+    Hdr h1 = header(sch.q + sch.step);
+    int e0 = edge_at(h0.beg + slot, h0.end);
+    for (int u = sch.q; u < sch.end; u += sch.step) {
+        const Hdr h2 = header(u + 2 * sch.step);
+        const int e1 = edge_at(h1.beg + slot, h1.end);
         A ak[V], av[V];
 #pragma unroll
         for (int e = 0; e < V; ++e) { ak[e] = 0; av[e] = 0; }
-        for (int e0 = beg; e0 < end; e0 += P) {
-            const int ei = e0 + slot;
-            if (ei < end) {
-                const int eid = a.ws.list[ei];
-                const int src = (int)fdiv((uint32_t)eid, a.fd_s);            // source unit
-                const int sbi = (int)fdiv((uint32_t)src, a.fd_hkv);          // its b*n + i
-                const uint32_t qrow = (uint32_t)(sbi * a.hq + h * G);
+        int eid = e0;
+        for (int e0pos = h0.beg; e0pos < h0.end; e0pos += P) {
+            if (e0pos != h0.beg) eid = edge_at(e0pos + slot, h0.end);
+            if (eid >= 0) {
+                const int src = (int)fdiv((uint32_t)eid, a.fd_s);      // source unit
+                const int sbi = (int)fdiv((uint32_t)src, a.fd_hkv);    // its b*n + i
+                const uint32_t qrow = (uint32_t)(sbi * a.hq + h0.h * G);
                 const float2* cf = a.ws.coef + (size_t)eid * G;
                 uint4 qr[G], dr[G];
                 float2 co[G];
@@ -588,10 +701,13 @@ __global__ __launch_bounds__(kBlock) void sea_bwd_dst_fast_kernel(SeaBwdFast a) 
         }
         rows_reduce_scatter<P, V>(ak);
         rows_reduce_scatter<P, V>(av);
-        const uint32_t o = (uint32_t)pos.unit * FROW + r * 16 * 4 / (int)sizeof(T) +
+        const uint32_t o = (uint32_t)h0.unit * FROW + r * 16 * 4 / (int)sizeof(T) +
                            rs_offset<V, P>(row) * 4;
         store_f32<L>(a.dk + o, ak);
         store_f32<L>(a.dv + o, av);
+        h0 = h1;
+        h1 = h2;
+        e0 = e1;
     }
 }
 
@@ -638,8 +754,16 @@ hipError_t run_fast(const SeaBwdArgs& g, const SeaBwdFast& a, long long E, hipSt
     const int nsrc = persistent_grid(reinterpret_cast<const void*>(
                                          &sea_bwd_src_fast_kernel<T, G, P>),
                                      a.U, kBlock / (16 * P));
+    if (a.global_index) {
+        const hipError_t e = launch_zero_f32(reinterpret_cast<float*>(a.ws.cnt), (size_t)a.U, st);
+        if (e != hipSuccess) return e;
+    }
     hipLaunchKernelGGL((sea_bwd_src_fast_kernel<T, G, P>), dim3(nsrc), dim3(kBlock), 0, st, a);
-    launch_index(g, E, st);
+    if (a.global_index)
+        launch_index(g, E, st);
+    else
+        hipLaunchKernelGGL(pair_sort_kernel, dim3((unsigned)((long long)g.U / a.n)), dim3(1024), 0,
+                           st, a.idx, a.w, a.n, a.hkv, a.s, a.ws.beg, a.ws.len, a.ws.list);
     const int ndst = persistent_grid(reinterpret_cast<const void*>(
                                          &sea_bwd_dst_fast_kernel<T, G, PD>),
                                      a.U, kBlock / (16 * PD));
@@ -696,9 +820,8 @@ hipError_t launch_sea_backward(int B, int n, int hq, int hkv, int d, bool bf16, 
     a.ws.off = reinterpret_cast<int*>(base + l.off);
     a.ws.bsum = reinterpret_cast<int*>(base + l.bsum);
     a.ws.list = reinterpret_cast<int*>(base + l.list);
-    hipError_t e = launch_zero_f32(reinterpret_cast<float*>(a.ws.cnt), (size_t)a.U, st);
-    if (e == hipSuccess && a.ts.nchunk > 1) e = launch_zero_f32(dw, (size_t)a.U * s, st);
-    if (e != hipSuccess) return e;
+    a.ws.beg = reinterpret_cast<int*>(base + l.beg);
+    a.ws.len = reinterpret_cast<int*>(base + l.len);
     const long long E = (long long)a.U * s;
     if (sea_fast_shape(B, n, hq, hkv, d, bf16, s) &&
         (long long)B * n * hq * d * 4 < (1ll << 32)) {
@@ -710,11 +833,15 @@ hipError_t launch_sea_backward(int B, int n, int hq, int hkv, int d, bool bf16, 
         f.dv = reinterpret_cast<char*>(dv); f.dw = dw;
         f.ws = a.ws;
         f.n = n; f.hq = hq; f.hkv = hkv; f.s = s; f.U = a.U; f.scale = scale;
-        f.fd_n = make_fastdiv((uint32_t)n);
         f.fd_hkv = make_fastdiv((uint32_t)hkv);
         f.fd_s = make_fastdiv((uint32_t)s);
+        make_seg_plan(f.sp, B, n, hkv);
+        f.global_index = n > kSortMaxN;
         return bf16 ? dispatch_fast<bf16_t>(a, f, G, E, st) : dispatch_fast<float>(a, f, G, E, st);
     }
+    hipError_t e = launch_zero_f32(reinterpret_cast<float*>(a.ws.cnt), (size_t)a.U, st);
+    if (e == hipSuccess && a.ts.nchunk > 1) e = launch_zero_f32(dw, (size_t)a.U * s, st);
+    if (e != hipSuccess) return e;
     return bf16 ? dispatch_g<bf16_t>(a, G, E, st) : dispatch_g<float>(a, G, E, st);
 }
 

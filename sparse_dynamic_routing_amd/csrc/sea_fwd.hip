@@ -186,7 +186,7 @@ struct SeaFwdFast {
     char* o;
     int n, hq, hkv, s, U;
     float scale;
-    FastDiv fd_n, fd_hkv;
+    SegPlan sp;
 };
 
 struct UnitPos {
@@ -195,11 +195,11 @@ struct UnitPos {
     int kvrow0;    // K/V row of token 0 of the pair: b*n*hkv + h
 };
 
-__device__ __forceinline__ UnitPos unit_pos(int u, int n, int hkv, const FastDiv& fd_n,
-                                            const FastDiv& fd_hkv) {
-    const int pair = (int)fdiv((uint32_t)u, fd_n);
-    const int i = u - pair * n;
-    const int b = (int)fdiv((uint32_t)pair, fd_hkv);
+__device__ __forceinline__ UnitPos unit_pos(const SegPlan& sp, int x, int q) {
+    int pair, i;
+    sched_item(sp, x, q, pair, i);
+    const int n = sp.n, hkv = sp.hkv;
+    const int b = (int)fdiv((uint32_t)pair, sp.fd_hkv);
     const int h = pair - b * hkv;
     UnitPos p;
     p.bi = b * n + i;
@@ -219,14 +219,14 @@ __global__ __launch_bounds__(kBlock) void sea_fwd_fast_kernel(SeaFwdFast a) {
     const int slot = row & (P - 1);
     const A c = (A)a.scale * (A)1.4426950408889634;
     const A NEG = -INFINITY;
-    Sched sc = xcd_sched(a.U, 16 * P);
+    const Sched sc = xcd_sched(a.sp, 16 * P);
 
-    // edge slot of unit u for this lane: (token index, weight); dead -> (0, 0)
+    // edge slot of item u for this lane: (token index, weight); dead -> (0, 0)
     auto fetch = [&](int u, UnitPos& pos, int& j, float& wt) {
         j = 0;
         wt = 0.0f;
         if (u < sc.end) {
-            pos = unit_pos(u, a.n, a.hkv, a.fd_n, a.fd_hkv);
+            pos = unit_pos(a.sp, sc.x, u);
             if (slot < a.s) {
                 const int e = pos.unit * a.s + slot;
                 j = a.idx[e];
@@ -237,8 +237,8 @@ __global__ __launch_bounds__(kBlock) void sea_fwd_fast_kernel(SeaFwdFast a) {
     UnitPos pos{0, 0, 0};
     int j;
     float wt;
-    fetch(sc.u, pos, j, wt);
-    for (int u = sc.u; u < sc.end; u += sc.step) {
+    fetch(sc.q, pos, j, wt);
+    for (int u = sc.q; u < sc.end; u += sc.step) {
         UnitPos npos = pos;
         int nj;
         float nwt;
@@ -382,8 +382,7 @@ hipError_t launch_sea_forward(int B, int n, int hq, int hkv, int d, bool bf16, f
         f.q = static_cast<const char*>(q); f.k = static_cast<const char*>(k);
         f.v = static_cast<const char*>(v); f.idx = idx; f.w = w; f.o = static_cast<char*>(o);
         f.n = n; f.hq = hq; f.hkv = hkv; f.s = s; f.U = a.U; f.scale = scale;
-        f.fd_n = make_fastdiv((uint32_t)n);
-        f.fd_hkv = make_fastdiv((uint32_t)hkv);
+        make_seg_plan(f.sp, B, n, hkv);
         return bf16 ? fast_g<bf16_t>(f, G, st) : fast_g<float>(f, G, st);
     }
     return bf16 ? dispatch_g<bf16_t>(a, G, st) : dispatch_g<float>(a, G, st);

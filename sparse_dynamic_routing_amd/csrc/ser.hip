@@ -28,6 +28,7 @@
 // once to fp32.  When dw1 and dw2 alias, one workspace receives both.
 #include "gm_common.h"
 #include "gm_internal.h"
+#include "gm_wave.h"
 
 namespace gm {
 namespace {
@@ -149,6 +150,195 @@ __global__ __launch_bounds__(kBlock) void ser_bwd_kernel(SerBwdArgs a) {
     unsafeAtomicAdd(a.ws2 + r2 * a.s3 + lc, g * (double)x);
 }
 
+
+// ----------------------------------------------------- one lane per unit
+// For s2, s3 <= 4 (at most 16 candidates) a lane holds a whole unit: its
+// leg-1 row, the leg-2 rows it points to and all candidates live in
+// registers (static indices, candidate k = 4a + c), so the merge and the
+// ranking need no cross-lane traffic and a wave serves 64 units.  The merge
+// scans the candidates in path order (a, c) and adds each path weight to the
+// first candidate with the same target, from 0 and in double: the order and
+// precision of the definition, hence bit-exact fp32 weights.
+struct SerUnitArgs {
+    const int32_t* idx1;
+    const float* w1;
+    const int32_t* idx2;
+    const float* w2;
+    int32_t* idx_out;
+    float* w_out;
+    const float* dw_out;   // backward only
+    double* ws1;           // backward: dw1 per leg-1 slot (plain stores)
+    double* ws2;           // backward: dw2 per leg-2 slot (atomics)
+    int n, hkv, s1, s2, s3, U;
+    FastDiv fd_hkv, fd_n;
+    int vec_out;           // forward: outputs 16-byte aligned, s1 == 4
+};
+
+constexpr int kSmax = 4;
+constexpr int kCand = kSmax * kSmax;
+
+// Token i of unit u (u = (b*n + i)*hkv + h); the row of token j of the same
+// (b, h) is u + (j - i) * hkv.
+__device__ __forceinline__ int token_of(int u, const SerUnitArgs& a) {
+    const int bi = (int)fdiv((uint32_t)u, a.fd_hkv);
+    return bi - (int)fdiv((uint32_t)bi, a.fd_n) * a.n;
+}
+
+// Load the unit's paths: m[k] target, x[k] leg-1 weight, y[k] leg-2 weight,
+// r2[a] leg-2 row; invalid candidates get m = -1.
+__device__ __forceinline__ void load_paths(const SerUnitArgs& a, int u, int (&m)[kCand],
+                                           float (&x)[kSmax], float (&y)[kCand],
+                                           int (&r2)[kSmax]) {
+    const int i = token_of(u, a);
+    int j[kSmax];
+#pragma unroll
+    for (int aa = 0; aa < kSmax; ++aa) {
+        j[aa] = 0;
+        x[aa] = 0.0f;
+        if (aa < a.s2) {
+            j[aa] = a.idx1[(size_t)u * a.s2 + aa];
+            x[aa] = a.w1[(size_t)u * a.s2 + aa];
+        }
+        r2[aa] = u + (j[aa] - i) * a.hkv;
+    }
+#pragma unroll
+    for (int aa = 0; aa < kSmax; ++aa) {
+#pragma unroll
+        for (int c = 0; c < kSmax; ++c) {
+            const int k = aa * kSmax + c;
+            m[k] = -1;
+            y[k] = 0.0f;
+            if (aa < a.s2 && c < a.s3) {
+                m[k] = a.idx2[(size_t)r2[aa] * a.s3 + c];
+                y[k] = a.w2[(size_t)r2[aa] * a.s3 + c];
+            }
+        }
+    }
+}
+
+__global__ __launch_bounds__(kBlock) void ser_fwd_unit_kernel(SerUnitArgs a) {
+    const int u = blockIdx.x * kBlock + threadIdx.x;
+    if (u >= a.U) return;
+    int m[kCand];
+    float x[kSmax], y[kCand];
+    int r2[kSmax];
+    load_paths(a, u, m, x, y, r2);
+    // merge in path order
+    double acc[kCand];
+    bool own[kCand];
+#pragma unroll
+    for (int k = 0; k < kCand; ++k) {
+        const double cw = (double)x[k / kSmax] * (double)y[k];
+        bool matched = false;
+#pragma unroll
+        for (int k2 = 0; k2 < k; ++k2) {
+            const bool hit = !matched && m[k] >= 0 && m[k2] == m[k];
+            acc[k2] = hit ? acc[k2] + cw : acc[k2];
+            matched = matched || hit;
+        }
+        own[k] = m[k] >= 0 && !matched;
+        acc[k] = own[k] ? 0.0 + cw : 0.0;
+    }
+    float key[kCand];
+    bool cand[kCand];
+    int nd = 0;
+#pragma unroll
+    for (int k = 0; k < kCand; ++k) {
+        key[k] = (float)acc[k];
+        cand[k] = own[k] && key[k] > 0.0f;
+        nd += cand[k];
+    }
+    // rank: larger weight first, then lower index
+    int om[kSmax];
+    float ow[kSmax];
+#pragma unroll
+    for (int r = 0; r < kSmax; ++r) { om[r] = 0; ow[r] = 0.0f; }
+    const size_t ob = (size_t)u * a.s1;
+#pragma unroll
+    for (int k = 0; k < kCand; ++k) {
+        int rank = 0;
+#pragma unroll
+        for (int k2 = 0; k2 < kCand; ++k2) {
+            if (k2 == k) continue;
+            rank += cand[k2] && (key[k2] > key[k] || (key[k2] == key[k] && m[k2] < m[k]));
+        }
+        if (a.s1 <= kSmax) {
+#pragma unroll
+            for (int r = 0; r < kSmax; ++r) {
+                const bool put = cand[k] && rank == r;
+                om[r] = put ? m[k] : om[r];
+                ow[r] = put ? key[k] : ow[r];
+            }
+        } else if (cand[k] && rank < a.s1) {
+            a.idx_out[ob + rank] = m[k];
+            a.w_out[ob + rank] = key[k];
+        }
+    }
+    if (a.s1 <= kSmax) {
+        if (a.vec_out) {
+            *reinterpret_cast<int4*>(a.idx_out + ob) = make_int4(om[0], om[1], om[2], om[3]);
+            *reinterpret_cast<float4*>(a.w_out + ob) = make_float4(ow[0], ow[1], ow[2], ow[3]);
+        } else {
+#pragma unroll
+            for (int r = 0; r < kSmax; ++r) {
+                if (r < a.s1) {
+                    a.idx_out[ob + r] = om[r];
+                    a.w_out[ob + r] = ow[r];
+                }
+            }
+        }
+    } else {
+        for (int p = nd; p < a.s1; ++p) {
+            a.idx_out[ob + p] = 0;
+            a.w_out[ob + p] = 0.0f;
+        }
+    }
+}
+
+__global__ __launch_bounds__(kBlock) void ser_bwd_unit_kernel(SerUnitArgs a) {
+    const int u = blockIdx.x * kBlock + threadIdx.x;
+    if (u >= a.U) return;
+    int m[kCand];
+    float x[kSmax], y[kCand];
+    int r2[kSmax];
+    load_paths(a, u, m, x, y, r2);
+    const size_t ob = (size_t)u * a.s1;
+    double d1[kSmax];
+#pragma unroll
+    for (int aa = 0; aa < kSmax; ++aa) d1[aa] = 0.0;
+    // gradient of each path: sum of dw_out over retained slots with its target
+    for (int t = 0; t < a.s1; ++t) {
+        const float wt = a.w_out[ob + t];
+        if (!(wt > 0.0f)) continue;
+        const int mt = a.idx_out[ob + t];
+        const double gt = (double)a.dw_out[ob + t];
+#pragma unroll
+        for (int k = 0; k < kCand; ++k) {
+            const int aa = k / kSmax;
+            if (m[k] == mt && x[aa] > 0.0f && y[k] > 0.0f) {
+                d1[aa] += gt * (double)y[k];
+                unsafeAtomicAdd(a.ws2 + (size_t)r2[aa] * a.s3 + (k % kSmax), gt * (double)x[aa]);
+            }
+        }
+    }
+#pragma unroll
+    for (int aa = 0; aa < kSmax; ++aa)
+        if (aa < a.s2) a.ws1[(size_t)u * a.s2 + aa] = d1[aa];
+}
+
+// dw1 = ws1, dw2 = ws2 rounded to fp32; when they alias, dw = ws1 + ws2.
+__global__ __launch_bounds__(kBlock) void ser_bwd_finish_kernel(const double* ws1,
+                                                                const double* ws2, float* dw1,
+                                                                float* dw2, size_t n1, size_t n2,
+                                                                int aliased) {
+    const size_t stride = (size_t)gridDim.x * kBlock;
+    for (size_t e = (size_t)blockIdx.x * kBlock + threadIdx.x; e < n1; e += stride)
+        dw1[e] = aliased ? (float)(ws1[e] + ws2[e]) : (float)ws1[e];
+    if (!aliased)
+        for (size_t e = (size_t)blockIdx.x * kBlock + threadIdx.x; e < n2; e += stride)
+            dw2[e] = (float)ws2[e];
+}
+
 __global__ __launch_bounds__(kBlock) void round_f64_kernel(const double* src, float* dst,
                                                            size_t count) {
     for (size_t e = (size_t)blockIdx.x * kBlock + threadIdx.x; e < count;
@@ -221,6 +411,20 @@ hipError_t run_bwd(const SerBwdArgs& a, hipStream_t st) {
 
 }  // namespace
 
+void make_seg_plan(SegPlan& sp, int B, int n, int hkv) {
+    const long long npairs = (long long)B * hkv;
+    int lgS = 0;
+    while ((npairs << lgS) % kXcds != 0 && (npairs << lgS) < 64 && (n % (2 << lgS)) == 0)
+        ++lgS;
+    sp.n = n;
+    sp.hkv = hkv;
+    sp.lgS = lgS;
+    sp.nseg = (int)(npairs << lgS);
+    sp.L = n >> lgS;
+    sp.fd_L = make_fastdiv((uint32_t)(sp.L > 0 ? sp.L : 1));
+    sp.fd_hkv = make_fastdiv((uint32_t)(hkv > 0 ? hkv : 1));
+}
+
 int persistent_grid(const void* kernel, int items, int per_wg) {
     static int cus_by_dev[64];
     int dev = 0;
@@ -261,6 +465,15 @@ hipError_t launch_zero_f64(double* p, size_t count, hipStream_t st) {
 hipError_t launch_ser_forward(int B, int n, int hkv, const int32_t* idx1, const float* w1,
                               int s2, const int32_t* idx2, const float* w2, int s3,
                               int32_t* idx_out, float* w_out, int s1, hipStream_t st) {
+    if (s2 <= kSmax && s3 <= kSmax) {
+        SerUnitArgs u{idx1, w1, idx2, w2, idx_out, w_out, nullptr, nullptr, nullptr,
+                      n, hkv, s1, s2, s3, B * n * hkv,
+                      make_fastdiv((uint32_t)hkv), make_fastdiv((uint32_t)n),
+                      s1 == 4 && (((uintptr_t)idx_out | (uintptr_t)w_out) & 15) == 0};
+        hipLaunchKernelGGL(ser_fwd_unit_kernel, dim3((unsigned)((u.U + kBlock - 1) / kBlock)),
+                           dim3(kBlock), 0, st, u);
+        return hipGetLastError();
+    }
     SerArgs a{idx1, w1, idx2, w2, idx_out, w_out, n, hkv, s1, s2, s3, B * n * hkv};
     switch (pow2_ceil(s2 * s3)) {
         case 1: return run_fwd<1>(a, st);
@@ -281,6 +494,21 @@ hipError_t launch_ser_backward(int B, int n, int hkv, const int32_t* idx1, const
                                double* ws2, hipStream_t st) {
     const size_t rows = (size_t)B * n * hkv;
     const bool aliased = dw1 == dw2;
+    if (s2 <= kSmax && s3 <= kSmax) {
+        // ws1: dw1 (every slot stored), ws2: dw2 (zeroed, then atomics)
+        hipError_t e = launch_zero_f64(ws2, rows * s3, st);
+        if (e != hipSuccess) return e;
+        SerUnitArgs u{idx1, w1, idx2, w2, const_cast<int32_t*>(idx_out),
+                      const_cast<float*>(w_out), dw_out, ws1, ws2,
+                      n, hkv, s1, s2, s3, (int)rows,
+                      make_fastdiv((uint32_t)hkv), make_fastdiv((uint32_t)n), 0};
+        hipLaunchKernelGGL(ser_bwd_unit_kernel, dim3((unsigned)((rows + kBlock - 1) / kBlock)),
+                           dim3(kBlock), 0, st, u);
+        hipLaunchKernelGGL(ser_bwd_finish_kernel, dim3(grid_for(rows * s2, 8192)), dim3(kBlock), 0,
+                           st, (const double*)ws1, (const double*)ws2, dw1, dw2, rows * s2,
+                           rows * s3, (int)aliased);
+        return hipGetLastError();
+    }
     hipError_t e = launch_zero_f64(ws1, rows * s2, st);
     if (e == hipSuccess && !aliased) e = launch_zero_f64(ws2, rows * s3, st);
     if (e != hipSuccess) return e;
