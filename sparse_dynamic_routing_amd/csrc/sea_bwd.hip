@@ -390,11 +390,17 @@ __global__ __launch_bounds__(kBlock) void sea_bwd_dst_kernel(SeaBwdArgs a) {
 constexpr int kSortMaxN = 16384;
 constexpr int kSortTok = 4;
 __global__ __launch_bounds__(1024) void pair_sort_kernel(const int32_t* idx, const float* w,
-                                                         int n, int hkv, int s, int* beg,
-                                                         int* len, int* list) {
+                                                         int n, int hkv, int s, int vec,
+                                                         int* beg, int* len, int* list) {
     __shared__ int cnt[kSortMaxN];
     __shared__ int part[1024 / kWave];
-    const int pair = blockIdx.x;
+    // workgroup x + 8k runs on XCD x; when the pairs tile the 8 XCDs evenly,
+    // XCD x takes consecutive pairs (all KV heads of one batch), so an edge
+    // line read there serves all the heads it holds
+    const int npairs = gridDim.x;   // one workgroup per pair
+    int pair = (int)blockIdx.x;
+    if (npairs % kXcds == 0)
+        pair = ((int)blockIdx.x % kXcds) * (npairs / kXcds) + (int)blockIdx.x / kXcds;
     const int b = pair / hkv, h = pair - (pair / hkv) * hkv;
     const int lbase = pair * n * s;
     for (int j = threadIdx.x; j < n; j += 1024) cnt[j] = 0;
@@ -405,6 +411,21 @@ __global__ __launch_bounds__(1024) void pair_sort_kernel(const int32_t* idx, con
         for (int k = 0; k < kSortTok; ++k) {
             const int i = i0 + k * 1024 + (int)threadIdx.x;
             const int e0 = ((b * n + i) * hkv + h) * s;
+            if (vec) {   // s == 4, 16-byte aligned rows: one load each
+                int4 j4 = make_int4(0, 0, 0, 0);
+                float4 w4 = make_float4(0.f, 0.f, 0.f, 0.f);
+                if (i < n) {
+                    j4 = *reinterpret_cast<const int4*>(idx + e0);
+                    w4 = *reinterpret_cast<const float4*>(w + e0);
+                }
+                tj[k * 4 + 0] = j4.x; tj[k * 4 + 1] = j4.y;
+                tj[k * 4 + 2] = j4.z; tj[k * 4 + 3] = j4.w;
+                te[k * 4 + 0] = w4.x > 0.0f ? e0 + 0 : -1;
+                te[k * 4 + 1] = w4.y > 0.0f ? e0 + 1 : -1;
+                te[k * 4 + 2] = w4.z > 0.0f ? e0 + 2 : -1;
+                te[k * 4 + 3] = w4.w > 0.0f ? e0 + 3 : -1;
+                continue;
+            }
 #pragma unroll
             for (int t = 0; t < 4; ++t) {
                 const int slot = k * 4 + t;
@@ -428,10 +449,10 @@ __global__ __launch_bounds__(1024) void pair_sort_kernel(const int32_t* idx, con
     }
     __syncthreads();
     // exclusive scan of cnt[0 .. n): each thread scans a contiguous run
-    const int per = (n + 1023) / 1024;
-    const int j0 = threadIdx.x * per;
+    const int run_len = (n + 1023) / 1024;
+    const int j0 = threadIdx.x * run_len;
     int run = 0;
-    for (int j = j0; j < j0 + per && j < n; ++j) run += cnt[j];
+    for (int j = j0; j < j0 + run_len && j < n; ++j) run += cnt[j];
     const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
     int inc = run;
     for (int m = 1; m < kWave; m <<= 1) {
@@ -443,7 +464,7 @@ __global__ __launch_bounds__(1024) void pair_sort_kernel(const int32_t* idx, con
     int base = 0;
     for (int k = 0; k < wave; ++k) base += part[k];
     base += inc - run;
-    for (int j = j0; j < j0 + per && j < n; ++j) {
+    for (int j = j0; j < j0 + run_len && j < n; ++j) {
         const int c = cnt[j];
         beg[pair * n + j] = lbase + base;
         len[pair * n + j] = c;
@@ -763,7 +784,9 @@ hipError_t run_fast(const SeaBwdArgs& g, const SeaBwdFast& a, long long E, hipSt
         launch_index(g, E, st);
     else
         hipLaunchKernelGGL(pair_sort_kernel, dim3((unsigned)((long long)g.U / a.n)), dim3(1024), 0,
-                           st, a.idx, a.w, a.n, a.hkv, a.s, a.ws.beg, a.ws.len, a.ws.list);
+                           st, a.idx, a.w, a.n, a.hkv, a.s,
+                           (int)(a.s == 4 && (((uintptr_t)a.idx | (uintptr_t)a.w) & 15) == 0),
+                           a.ws.beg, a.ws.len, a.ws.list);
     const int ndst = persistent_grid(reinterpret_cast<const void*>(
                                          &sea_bwd_dst_fast_kernel<T, G, PD>),
                                      a.U, kBlock / (16 * PD));

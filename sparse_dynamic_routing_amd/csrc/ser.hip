@@ -172,6 +172,7 @@ struct SerUnitArgs {
     int n, hkv, s1, s2, s3, U;
     FastDiv fd_hkv, fd_n;
     int vec_out;           // forward: outputs 16-byte aligned, s1 == 4
+    int vec_in;            // legs 16-byte aligned, s2 == s3 == 4: one load per row
 };
 
 constexpr int kSmax = 4;
@@ -191,6 +192,22 @@ __device__ __forceinline__ void load_paths(const SerUnitArgs& a, int u, int (&m)
                                            int (&r2)[kSmax]) {
     const int i = token_of(u, a);
     int j[kSmax];
+    if (a.vec_in) {
+        const int4 ji = *reinterpret_cast<const int4*>(a.idx1 + (size_t)u * 4);
+        const float4 xi = *reinterpret_cast<const float4*>(a.w1 + (size_t)u * 4);
+        j[0] = ji.x; j[1] = ji.y; j[2] = ji.z; j[3] = ji.w;
+        x[0] = xi.x; x[1] = xi.y; x[2] = xi.z; x[3] = xi.w;
+#pragma unroll
+        for (int aa = 0; aa < kSmax; ++aa) r2[aa] = u + (j[aa] - i) * a.hkv;
+#pragma unroll
+        for (int aa = 0; aa < kSmax; ++aa) {
+            const int4 mi = *reinterpret_cast<const int4*>(a.idx2 + (size_t)r2[aa] * 4);
+            const float4 yi = *reinterpret_cast<const float4*>(a.w2 + (size_t)r2[aa] * 4);
+            m[aa * 4 + 0] = mi.x; m[aa * 4 + 1] = mi.y; m[aa * 4 + 2] = mi.z; m[aa * 4 + 3] = mi.w;
+            y[aa * 4 + 0] = yi.x; y[aa * 4 + 1] = yi.y; y[aa * 4 + 2] = yi.z; y[aa * 4 + 3] = yi.w;
+        }
+        return;
+    }
 #pragma unroll
     for (int aa = 0; aa < kSmax; ++aa) {
         j[aa] = 0;
@@ -307,11 +324,9 @@ __global__ __launch_bounds__(kBlock) void ser_bwd_unit_kernel(SerUnitArgs a) {
 #pragma unroll
     for (int aa = 0; aa < kSmax; ++aa) d1[aa] = 0.0;
     // gradient of each path: sum of dw_out over retained slots with its target
-    for (int t = 0; t < a.s1; ++t) {
-        const float wt = a.w_out[ob + t];
-        if (!(wt > 0.0f)) continue;
-        const int mt = a.idx_out[ob + t];
-        const double gt = (double)a.dw_out[ob + t];
+    auto slot = [&](int mt, float wt, float gt_) {
+        if (!(wt > 0.0f)) return;
+        const double gt = (double)gt_;
 #pragma unroll
         for (int k = 0; k < kCand; ++k) {
             const int aa = k / kSmax;
@@ -320,6 +335,17 @@ __global__ __launch_bounds__(kBlock) void ser_bwd_unit_kernel(SerUnitArgs a) {
                 unsafeAtomicAdd(a.ws2 + (size_t)r2[aa] * a.s3 + (k % kSmax), gt * (double)x[aa]);
             }
         }
+    };
+    if (a.vec_out) {
+        const int4 mt = *reinterpret_cast<const int4*>(a.idx_out + ob);
+        const float4 wt = *reinterpret_cast<const float4*>(a.w_out + ob);
+        const float4 gt = *reinterpret_cast<const float4*>(a.dw_out + ob);
+        slot(mt.x, wt.x, gt.x);
+        slot(mt.y, wt.y, gt.y);
+        slot(mt.z, wt.z, gt.z);
+        slot(mt.w, wt.w, gt.w);
+    } else {
+        for (int t = 0; t < a.s1; ++t) slot(a.idx_out[ob + t], a.w_out[ob + t], a.dw_out[ob + t]);
     }
 #pragma unroll
     for (int aa = 0; aa < kSmax; ++aa)
@@ -469,7 +495,10 @@ hipError_t launch_ser_forward(int B, int n, int hkv, const int32_t* idx1, const 
         SerUnitArgs u{idx1, w1, idx2, w2, idx_out, w_out, nullptr, nullptr, nullptr,
                       n, hkv, s1, s2, s3, B * n * hkv,
                       make_fastdiv((uint32_t)hkv), make_fastdiv((uint32_t)n),
-                      s1 == 4 && (((uintptr_t)idx_out | (uintptr_t)w_out) & 15) == 0};
+                      s1 == 4 && (((uintptr_t)idx_out | (uintptr_t)w_out) & 15) == 0,
+                      s2 == 4 && s3 == 4 &&
+                          (((uintptr_t)idx1 | (uintptr_t)w1 | (uintptr_t)idx2 | (uintptr_t)w2) &
+                           15) == 0};
         hipLaunchKernelGGL(ser_fwd_unit_kernel, dim3((unsigned)((u.U + kBlock - 1) / kBlock)),
                            dim3(kBlock), 0, st, u);
         return hipGetLastError();
@@ -501,7 +530,12 @@ hipError_t launch_ser_backward(int B, int n, int hkv, const int32_t* idx1, const
         SerUnitArgs u{idx1, w1, idx2, w2, const_cast<int32_t*>(idx_out),
                       const_cast<float*>(w_out), dw_out, ws1, ws2,
                       n, hkv, s1, s2, s3, (int)rows,
-                      make_fastdiv((uint32_t)hkv), make_fastdiv((uint32_t)n), 0};
+                      make_fastdiv((uint32_t)hkv), make_fastdiv((uint32_t)n),
+                      s1 == 4 && (((uintptr_t)idx_out | (uintptr_t)w_out | (uintptr_t)dw_out) &
+                                  15) == 0,
+                      s2 == 4 && s3 == 4 &&
+                          (((uintptr_t)idx1 | (uintptr_t)w1 | (uintptr_t)idx2 | (uintptr_t)w2) &
+                           15) == 0};
         hipLaunchKernelGGL(ser_bwd_unit_kernel, dim3((unsigned)((rows + kBlock - 1) / kBlock)),
                            dim3(kBlock), 0, st, u);
         hipLaunchKernelGGL(ser_bwd_finish_kernel, dim3(grid_for(rows * s2, 8192)), dim3(kBlock), 0,
