@@ -163,7 +163,9 @@ size_t gm_ser_backward_workspace_bytes(int B, int n, int hkv, int s2, int s3, in
     (void)aliased;
     if (check_units(B, n, hkv) != GM_OK || s2 < 1 || s3 < 1) return 0;
     const size_t rows = (size_t)B * n * hkv;
-    return rows * s2 * sizeof(double) + rows * s3 * sizeof(double);
+    const size_t acc = rows * s2 * sizeof(double) + rows * s3 * sizeof(double);
+    const size_t pull = gm::ser_backward_pull_bytes((long long)rows, s2);
+    return acc > pull ? acc : pull;
 }
 
 gm_status gm_ser_backward(int B, int n, int hkv, const int32_t* idx1, const float* w1, int s2,

@@ -44,6 +44,16 @@ hipError_t launch_ser_backward(int B, int n, int hkv, const int32_t* idx1, const
                                const float* dw_out, float* dw1, float* dw2, double* ws1,
                                double* ws2, hipStream_t st);
 
+// Reverse (target-sorted) index of an edge tensor [B][n][hkv][s], s <= 4:
+// beg/len per pair-major row (pair * n + j), list of edge ids; list needs
+// B*n*hkv*s entries, beg and len B*n*hkv each.
+bool edge_index_supported(int n, int s);
+hipError_t launch_edge_index(int B, int n, int hkv, const int32_t* idx, const float* w, int s,
+                             int* beg, int* len, int* list, hipStream_t st);
+
+// Workspace of the pull-style SER backward (reverse index of leg 1).
+size_t ser_backward_pull_bytes(long long rows, int s2);
+
 hipError_t launch_check_edges(int B, int n, int hkv, const int32_t* idx, const float* w, int s,
                               unsigned long long* counts, hipStream_t st);
 

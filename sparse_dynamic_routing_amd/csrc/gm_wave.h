@@ -205,4 +205,40 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
     return __builtin_bit_cast(uint32_t, v);
 }
 
+// Streaming (non-temporal) stores of outputs nobody reads soon, so they do
+// not push gathered rows out of the L2.
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+
+template <int L, typename A>
+__device__ __forceinline__ void store_f32_nt(char* p, const A* x) {
+    if constexpr (L == 1) {
+        __builtin_nontemporal_store((float)x[0], reinterpret_cast<float*>(p));
+    } else if constexpr (L == 2) {
+        const f32x2_t v = {(float)x[0], (float)x[1]};
+        __builtin_nontemporal_store(v, reinterpret_cast<f32x2_t*>(p));
+    } else {
+#pragma unroll
+        for (int e = 0; e < L; e += 4) {
+            const f32x4_t v = {(float)x[e], (float)x[e + 1], (float)x[e + 2], (float)x[e + 3]};
+            __builtin_nontemporal_store(v, reinterpret_cast<f32x4_t*>(p + 4 * e));
+        }
+    }
+}
+
+__device__ __forceinline__ void store_u32_nt(char* p, uint32_t a) {
+    __builtin_nontemporal_store(a, reinterpret_cast<uint32_t*>(p));
+}
+__device__ __forceinline__ void store_u32x2_nt(char* p, uint32_t a, uint32_t b) {
+    const u32x2_t v = {a, b};
+    __builtin_nontemporal_store(v, reinterpret_cast<u32x2_t*>(p));
+}
+__device__ __forceinline__ void store_u32x4_nt(char* p, uint32_t a, uint32_t b, uint32_t c,
+                                               uint32_t d) {
+    const u32x4_t v = {a, b, c, d};
+    __builtin_nontemporal_store(v, reinterpret_cast<u32x4_t*>(p));
+}
+
 }  // namespace gm

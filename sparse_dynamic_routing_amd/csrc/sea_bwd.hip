@@ -380,107 +380,6 @@ __global__ __launch_bounds__(kBlock) void sea_bwd_dst_kernel(SeaBwdArgs a) {
 
 
 
-// Reverse edge index of one (batch, KV head) pair per workgroup, in LDS:
-// count the live edges per target token (LDS atomics), exclusive scan, then
-// place every edge id in its target's segment.  The pair's edges occupy the
-// fixed list range [pair * n * s, (pair + 1) * n * s), so no scan across
-// pairs is needed.  beg/len are indexed by pair-major row pair * n + j.
-// Each thread takes 4 tokens per batch and issues all their (s <= 4) slot
-// loads before using any, so a batch costs one memory round trip.
-constexpr int kSortMaxN = 16384;
-constexpr int kSortTok = 4;
-__global__ __launch_bounds__(1024) void pair_sort_kernel(const int32_t* idx, const float* w,
-                                                         int n, int hkv, int s, int vec,
-                                                         int* beg, int* len, int* list) {
-    __shared__ int cnt[kSortMaxN];
-    __shared__ int part[1024 / kWave];
-    // workgroup x + 8k runs on XCD x; when the pairs tile the 8 XCDs evenly,
-    // XCD x takes consecutive pairs (all KV heads of one batch), so an edge
-    // line read there serves all the heads it holds
-    const int npairs = gridDim.x;   // one workgroup per pair
-    int pair = (int)blockIdx.x;
-    if (npairs % kXcds == 0)
-        pair = ((int)blockIdx.x % kXcds) * (npairs / kXcds) + (int)blockIdx.x / kXcds;
-    const int b = pair / hkv, h = pair - (pair / hkv) * hkv;
-    const int lbase = pair * n * s;
-    for (int j = threadIdx.x; j < n; j += 1024) cnt[j] = 0;
-    __syncthreads();
-    // the (up to 4 x 4) slots of this thread's tokens in one batch
-    auto load = [&](int i0, int (&tj)[kSortTok * 4], int (&te)[kSortTok * 4]) {
-#pragma unroll
-        for (int k = 0; k < kSortTok; ++k) {
-            const int i = i0 + k * 1024 + (int)threadIdx.x;
-            const int e0 = ((b * n + i) * hkv + h) * s;
-            if (vec) {   // s == 4, 16-byte aligned rows: one load each
-                int4 j4 = make_int4(0, 0, 0, 0);
-                float4 w4 = make_float4(0.f, 0.f, 0.f, 0.f);
-                if (i < n) {
-                    j4 = *reinterpret_cast<const int4*>(idx + e0);
-                    w4 = *reinterpret_cast<const float4*>(w + e0);
-                }
-                tj[k * 4 + 0] = j4.x; tj[k * 4 + 1] = j4.y;
-                tj[k * 4 + 2] = j4.z; tj[k * 4 + 3] = j4.w;
-                te[k * 4 + 0] = w4.x > 0.0f ? e0 + 0 : -1;
-                te[k * 4 + 1] = w4.y > 0.0f ? e0 + 1 : -1;
-                te[k * 4 + 2] = w4.z > 0.0f ? e0 + 2 : -1;
-                te[k * 4 + 3] = w4.w > 0.0f ? e0 + 3 : -1;
-                continue;
-            }
-#pragma unroll
-            for (int t = 0; t < 4; ++t) {
-                const int slot = k * 4 + t;
-                te[slot] = -1;
-                tj[slot] = 0;
-                if (i < n && t < s) {
-                    const int e = e0 + t;
-                    const float wt = w[e];
-                    tj[slot] = idx[e];
-                    te[slot] = wt > 0.0f ? e : -1;
-                }
-            }
-        }
-    };
-    for (int i0 = 0; i0 < n; i0 += 1024 * kSortTok) {
-        int tj[kSortTok * 4], te[kSortTok * 4];
-        load(i0, tj, te);
-#pragma unroll
-        for (int k = 0; k < kSortTok * 4; ++k)
-            if (te[k] >= 0) atomicAdd(&cnt[tj[k]], 1);
-    }
-    __syncthreads();
-    // exclusive scan of cnt[0 .. n): each thread scans a contiguous run
-    const int run_len = (n + 1023) / 1024;
-    const int j0 = threadIdx.x * run_len;
-    int run = 0;
-    for (int j = j0; j < j0 + run_len && j < n; ++j) run += cnt[j];
-    const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
-    int inc = run;
-    for (int m = 1; m < kWave; m <<= 1) {
-        const int o = __shfl_up(inc, m, kWave);
-        if (lane >= m) inc += o;
-    }
-    if (lane == kWave - 1) part[wave] = inc;
-    __syncthreads();
-    int base = 0;
-    for (int k = 0; k < wave; ++k) base += part[k];
-    base += inc - run;
-    for (int j = j0; j < j0 + run_len && j < n; ++j) {
-        const int c = cnt[j];
-        beg[pair * n + j] = lbase + base;
-        len[pair * n + j] = c;
-        cnt[j] = base;   // becomes the fill cursor
-        base += c;
-    }
-    __syncthreads();
-    for (int i0 = 0; i0 < n; i0 += 1024 * kSortTok) {
-        int tj[kSortTok * 4], te[kSortTok * 4];
-        load(i0, tj, te);
-#pragma unroll
-        for (int k = 0; k < kSortTok * 4; ++k)
-            if (te[k] >= 0) list[lbase + atomicAdd(&cnt[tj[k]], 1)] = te[k];
-    }
-}
-
 // ----------------------------------------------------------------- fast path
 // Same geometry as the forward's fast path: one 256-byte d-row per 16-lane
 // row, P = pow2(s) <= 4 slots (source pass) or P incoming edges (target
@@ -634,7 +533,7 @@ __global__ __launch_bounds__(kBlock) void sea_bwd_src_fast_kernel(SeaBwdFast a) 
 #pragma unroll
             for (int e = 0; e < V; ++e) dqv[e] = dls * kf[e];
             rows_reduce_scatter<P, V>(dqv);
-            store_f32<L>(a.dq + (qrow + g) * FROW + r * 16 * 4 / (int)sizeof(T) +
+            store_f32_nt<L>(a.dq + (qrow + g) * FROW + r * 16 * 4 / (int)sizeof(T) +
                              rs_offset<V, P>(row) * 4,
                          dqv);
             if (live && r == 0) cp[g] = make_float2((float)dls, (float)p);
@@ -724,8 +623,8 @@ __global__ __launch_bounds__(kBlock) void sea_bwd_dst_fast_kernel(SeaBwdFast a) 
         rows_reduce_scatter<P, V>(av);
         const uint32_t o = (uint32_t)h0.unit * FROW + r * 16 * 4 / (int)sizeof(T) +
                            rs_offset<V, P>(row) * 4;
-        store_f32<L>(a.dk + o, ak);
-        store_f32<L>(a.dv + o, av);
+        store_f32_nt<L>(a.dk + o, ak);
+        store_f32_nt<L>(a.dv + o, av);
         h0 = h1;
         h1 = h2;
         e0 = e1;
@@ -780,13 +679,13 @@ hipError_t run_fast(const SeaBwdArgs& g, const SeaBwdFast& a, long long E, hipSt
         if (e != hipSuccess) return e;
     }
     hipLaunchKernelGGL((sea_bwd_src_fast_kernel<T, G, P>), dim3(nsrc), dim3(kBlock), 0, st, a);
-    if (a.global_index)
+    if (a.global_index) {
         launch_index(g, E, st);
-    else
-        hipLaunchKernelGGL(pair_sort_kernel, dim3((unsigned)((long long)g.U / a.n)), dim3(1024), 0,
-                           st, a.idx, a.w, a.n, a.hkv, a.s,
-                           (int)(a.s == 4 && (((uintptr_t)a.idx | (uintptr_t)a.w) & 15) == 0),
-                           a.ws.beg, a.ws.len, a.ws.list);
+    } else {
+        const hipError_t e = launch_edge_index(a.U / (a.n * a.hkv), a.n, a.hkv, a.idx, a.w, a.s,
+                                               a.ws.beg, a.ws.len, a.ws.list, st);
+        if (e != hipSuccess) return e;
+    }
     const int ndst = persistent_grid(reinterpret_cast<const void*>(
                                          &sea_bwd_dst_fast_kernel<T, G, PD>),
                                      a.U, kBlock / (16 * PD));
@@ -859,7 +758,7 @@ hipError_t launch_sea_backward(int B, int n, int hq, int hkv, int d, bool bf16, 
         f.fd_hkv = make_fastdiv((uint32_t)hkv);
         f.fd_s = make_fastdiv((uint32_t)s);
         make_seg_plan(f.sp, B, n, hkv);
-        f.global_index = n > kSortMaxN;
+        f.global_index = !edge_index_supported(n, s);
         return bf16 ? dispatch_fast<bf16_t>(a, f, G, E, st) : dispatch_fast<float>(a, f, G, E, st);
     }
     hipError_t e = launch_zero_f32(reinterpret_cast<float*>(a.ws.cnt), (size_t)a.U, st);

@@ -292,17 +292,15 @@ __global__ __launch_bounds__(kBlock) void sea_fwd_fast_kernel(SeaFwdFast a) {
             char* op = a.o + qoff + g * ROW + rs_offset<V, P>(row) * (int)sizeof(T);
             if constexpr (V == 8) {
                 if constexpr (L == 2) {
-                    *reinterpret_cast<uint32_t*>(op) = pack_bf16x2(ov[0], ov[1]);
+                    store_u32_nt(op, pack_bf16x2(ov[0], ov[1]));
                 } else if constexpr (L == 4) {
-                    *reinterpret_cast<uint2*>(op) =
-                        make_uint2(pack_bf16x2(ov[0], ov[1]), pack_bf16x2(ov[2], ov[3]));
+                    store_u32x2_nt(op, pack_bf16x2(ov[0], ov[1]), pack_bf16x2(ov[2], ov[3]));
                 } else {
-                    *reinterpret_cast<uint4*>(op) =
-                        make_uint4(pack_bf16x2(ov[0], ov[1]), pack_bf16x2(ov[2], ov[3]),
+                    store_u32x4_nt(op, pack_bf16x2(ov[0], ov[1]), pack_bf16x2(ov[2], ov[3]),
                                    pack_bf16x2(ov[4], ov[5]), pack_bf16x2(ov[6], ov[7]));
                 }
             } else {
-                store_n<L>(reinterpret_cast<float*>(op), ov);
+                store_f32_nt<L>(op, ov);
             }
         }
         pos = npos;

@@ -352,6 +352,137 @@ __global__ __launch_bounds__(kBlock) void ser_bwd_unit_kernel(SerUnitArgs a) {
         if (aa < a.s2) a.ws1[(size_t)u * a.s2 + aa] = d1[aa];
 }
 
+
+// ------------------------------------------------- pull-style SER backward
+// One lane per row r.  dw1 of row r comes from r's own paths (as above);
+// dw2 of row r, i.e. the gradient of r's leg-2 slots, is pulled from the
+// units whose leg-1 edges point at r, found in the reverse index of leg 1:
+// for such an edge (unit i, slot a) with weight x and each leg-2 slot c of r
+// with target m_c, the contribution is x * (sum of dw_out over i's retained
+// slots with target m_c).  Every row is written once; no atomics.
+struct SerPullArgs {
+    const int32_t* idx1;
+    const float* w1;
+    const int32_t* idx2;
+    const float* w2;
+    const int32_t* idx_out;
+    const float* w_out;
+    const float* dw_out;
+    float* dw1;
+    float* dw2;
+    const int* beg;
+    const int* len;
+    const int* list;
+    int n, hkv, s1, s2, s3, U, aliased;
+    FastDiv fd_hkv, fd_n, fd_s2;
+};
+
+// Retained slots of A' row u: target, weight (> 0 means retained), gradient.
+__device__ __forceinline__ void load_aprime(const SerPullArgs& a, int u, int (&mt)[kSmax],
+                                            float (&wt)[kSmax], float (&gt)[kSmax]) {
+    const size_t ob = (size_t)u * a.s1;
+#pragma unroll
+    for (int t = 0; t < kSmax; ++t) {
+        mt[t] = -1;
+        wt[t] = 0.0f;
+        gt[t] = 0.0f;
+        if (t < a.s1) {
+            mt[t] = a.idx_out[ob + t];
+            wt[t] = a.w_out[ob + t];
+            gt[t] = a.dw_out[ob + t];
+        }
+    }
+}
+
+__device__ __forceinline__ double path_grad(int m, const int (&mt)[kSmax],
+                                            const float (&wt)[kSmax], const float (&gt)[kSmax]) {
+    double g = 0.0;
+#pragma unroll
+    for (int t = 0; t < kSmax; ++t)
+        if (wt[t] > 0.0f && mt[t] == m) g += (double)gt[t];
+    return g;
+}
+
+__global__ __launch_bounds__(kBlock) void ser_bwd_pull_kernel(SerPullArgs a) {
+    const int u = blockIdx.x * kBlock + threadIdx.x;
+    if (u >= a.U) return;
+    SerUnitArgs ua{a.idx1, a.w1, a.idx2, a.w2, nullptr, nullptr, nullptr, nullptr, nullptr,
+                   a.n, a.hkv, a.s1, a.s2, a.s3, a.U, a.fd_hkv, a.fd_n, 0, 0};
+    int m[kCand];
+    float x[kSmax], y[kCand];
+    int r2[kSmax];
+    load_paths(ua, u, m, x, y, r2);
+    int mt[kSmax];
+    float wt[kSmax], gt[kSmax];
+    load_aprime(a, u, mt, wt, gt);
+    double d1[kSmax], d2[kSmax];
+#pragma unroll
+    for (int aa = 0; aa < kSmax; ++aa) {
+        d1[aa] = 0.0;
+        d2[aa] = 0.0;
+        if (!(x[aa] > 0.0f)) continue;
+#pragma unroll
+        for (int c = 0; c < kSmax; ++c) {
+            const int k = aa * kSmax + c;
+            if (m[k] >= 0 && y[k] > 0.0f) d1[aa] += path_grad(m[k], mt, wt, gt) * (double)y[k];
+        }
+    }
+    // this row's own leg-2 slots
+    int m2[kSmax];
+    float y2[kSmax];
+#pragma unroll
+    for (int c = 0; c < kSmax; ++c) {
+        m2[c] = -1;
+        y2[c] = 0.0f;
+        if (c < a.s3) {
+            m2[c] = a.idx2[(size_t)u * a.s3 + c];
+            y2[c] = a.w2[(size_t)u * a.s3 + c];
+        }
+    }
+    // incoming leg-1 edges, four per round trip
+    const int bi = (int)fdiv((uint32_t)u, a.fd_hkv);
+    const int b = (int)fdiv((uint32_t)bi, a.fd_n);
+    const int i = bi - b * a.n;
+    const int pair = b * a.hkv + (u - bi * a.hkv);
+    const int e_beg = a.beg[pair * a.n + i], e_end = e_beg + a.len[pair * a.n + i];
+    for (int e0 = e_beg; e0 < e_end; e0 += 4) {
+        int eid[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) eid[q] = e0 + q < e_end ? a.list[e0 + q] : -1;
+        float xs[4];
+        int mts[4][kSmax];
+        float wts[4][kSmax], gts[4][kSmax];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            xs[q] = 0.0f;
+            if (eid[q] >= 0) {
+                xs[q] = a.w1[eid[q]];
+                load_aprime(a, (int)fdiv((uint32_t)eid[q], a.fd_s2), mts[q], wts[q], gts[q]);
+            } else {
+#pragma unroll
+                for (int t = 0; t < kSmax; ++t) { mts[q][t] = -1; wts[q][t] = 0.0f; gts[q][t] = 0.0f; }
+            }
+        }
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+#pragma unroll
+            for (int c = 0; c < kSmax; ++c)
+                if (y2[c] > 0.0f) d2[c] += path_grad(m2[c], mts[q], wts[q], gts[q]) * (double)xs[q];
+        }
+    }
+    if (a.aliased) {
+#pragma unroll
+        for (int k = 0; k < kSmax; ++k)
+            if (k < a.s2) a.dw1[(size_t)u * a.s2 + k] = (float)(d1[k] + d2[k]);
+    } else {
+#pragma unroll
+        for (int k = 0; k < kSmax; ++k) {
+            if (k < a.s2) a.dw1[(size_t)u * a.s2 + k] = (float)d1[k];
+            if (k < a.s3) a.dw2[(size_t)u * a.s3 + k] = (float)d2[k];
+        }
+    }
+}
+
 // dw1 = ws1, dw2 = ws2 rounded to fp32; when they alias, dw = ws1 + ws2.
 __global__ __launch_bounds__(kBlock) void ser_bwd_finish_kernel(const double* ws1,
                                                                 const double* ws2, float* dw1,
@@ -451,6 +582,10 @@ void make_seg_plan(SegPlan& sp, int B, int n, int hkv) {
     sp.fd_hkv = make_fastdiv((uint32_t)(hkv > 0 ? hkv : 1));
 }
 
+size_t ser_backward_pull_bytes(long long rows, int s2) {
+    return (size_t)rows * (2 + s2) * sizeof(int);
+}
+
 int persistent_grid(const void* kernel, int items, int per_wg) {
     static int cus_by_dev[64];
     int dev = 0;
@@ -523,6 +658,21 @@ hipError_t launch_ser_backward(int B, int n, int hkv, const int32_t* idx1, const
                                double* ws2, hipStream_t st) {
     const size_t rows = (size_t)B * n * hkv;
     const bool aliased = dw1 == dw2;
+    if (s1 <= kSmax && s2 <= kSmax && s3 <= kSmax && edge_index_supported(n, s2)) {
+        // reverse index of leg 1 in the workspace, then one pass, no atomics
+        int* beg = reinterpret_cast<int*>(ws1);
+        int* len = beg + rows;
+        int* list = len + rows;
+        hipError_t e = launch_edge_index(B, n, hkv, idx1, w1, s2, beg, len, list, st);
+        if (e != hipSuccess) return e;
+        SerPullArgs pa{idx1, w1, idx2, w2, idx_out, w_out, dw_out, dw1, dw2, beg, len, list,
+                       n, hkv, s1, s2, s3, (int)rows, (int)aliased,
+                       make_fastdiv((uint32_t)hkv), make_fastdiv((uint32_t)n),
+                       make_fastdiv((uint32_t)s2)};
+        hipLaunchKernelGGL(ser_bwd_pull_kernel, dim3((unsigned)((rows + kBlock - 1) / kBlock)),
+                           dim3(kBlock), 0, st, pa);
+        return hipGetLastError();
+    }
     if (s2 <= kSmax && s3 <= kSmax) {
         // ws1: dw1 (every slot stored), ws2: dw2 (zeroed, then atomics)
         hipError_t e = launch_zero_f64(ws2, rows * s3, st);
