@@ -178,6 +178,23 @@ struct SerUnitArgs {
 constexpr int kSmax = 4;
 constexpr int kCand = kSmax * kSmax;
 
+// Unit of this lane when units are split into 8 contiguous chunks, one per
+// XCD (workgroups are dealt to XCDs round robin): every chunk holds whole
+// batches (or a contiguous part of one), i.e. all KV heads of its tokens, so
+// the small edge rows it gathers share cache lines and stay in its L2.
+// Launch with kXcds * ceil(ceil(U / 8) / kBlock) workgroups; -1: no unit.
+__device__ __forceinline__ int xcd_unit(int U) {
+    const int chunk = (U + kXcds - 1) / kXcds;
+    const int x = blockIdx.x % kXcds;
+    const int q = (int)(blockIdx.x / kXcds) * kBlock + (int)threadIdx.x;
+    const int u = x * chunk + q;
+    return (q < chunk && u < U) ? u : -1;
+}
+inline unsigned xcd_unit_grid(int U) {
+    const int chunk = (U + kXcds - 1) / kXcds;
+    return (unsigned)(kXcds * ((chunk + kBlock - 1) / kBlock));
+}
+
 // Token i of unit u (u = (b*n + i)*hkv + h); the row of token j of the same
 // (b, h) is u + (j - i) * hkv.
 __device__ __forceinline__ int token_of(int u, const SerUnitArgs& a) {
@@ -234,8 +251,8 @@ __device__ __forceinline__ void load_paths(const SerUnitArgs& a, int u, int (&m)
 }
 
 __global__ __launch_bounds__(kBlock) void ser_fwd_unit_kernel(SerUnitArgs a) {
-    const int u = blockIdx.x * kBlock + threadIdx.x;
-    if (u >= a.U) return;
+    const int u = xcd_unit(a.U);
+    if (u < 0) return;
     int m[kCand];
     float x[kSmax], y[kCand];
     int r2[kSmax];
@@ -375,12 +392,22 @@ struct SerPullArgs {
     const int* list;
     int n, hkv, s1, s2, s3, U, aliased;
     FastDiv fd_hkv, fd_n, fd_s2;
+    int vec_in, vec_ap;   // 16-byte rows: legs (s2 == s3 == 4), A' (s1 == 4)
 };
 
 // Retained slots of A' row u: target, weight (> 0 means retained), gradient.
 __device__ __forceinline__ void load_aprime(const SerPullArgs& a, int u, int (&mt)[kSmax],
                                             float (&wt)[kSmax], float (&gt)[kSmax]) {
     const size_t ob = (size_t)u * a.s1;
+    if (a.vec_ap) {
+        const int4 m4 = *reinterpret_cast<const int4*>(a.idx_out + ob);
+        const float4 w4 = *reinterpret_cast<const float4*>(a.w_out + ob);
+        const float4 g4 = *reinterpret_cast<const float4*>(a.dw_out + ob);
+        mt[0] = m4.x; mt[1] = m4.y; mt[2] = m4.z; mt[3] = m4.w;
+        wt[0] = w4.x; wt[1] = w4.y; wt[2] = w4.z; wt[3] = w4.w;
+        gt[0] = g4.x; gt[1] = g4.y; gt[2] = g4.z; gt[3] = g4.w;
+        return;
+    }
 #pragma unroll
     for (int t = 0; t < kSmax; ++t) {
         mt[t] = -1;
@@ -404,10 +431,10 @@ __device__ __forceinline__ double path_grad(int m, const int (&mt)[kSmax],
 }
 
 __global__ __launch_bounds__(kBlock) void ser_bwd_pull_kernel(SerPullArgs a) {
-    const int u = blockIdx.x * kBlock + threadIdx.x;
-    if (u >= a.U) return;
+    const int u = xcd_unit(a.U);
+    if (u < 0) return;
     SerUnitArgs ua{a.idx1, a.w1, a.idx2, a.w2, nullptr, nullptr, nullptr, nullptr, nullptr,
-                   a.n, a.hkv, a.s1, a.s2, a.s3, a.U, a.fd_hkv, a.fd_n, 0, 0};
+                   a.n, a.hkv, a.s1, a.s2, a.s3, a.U, a.fd_hkv, a.fd_n, 0, a.vec_in};
     int m[kCand];
     float x[kSmax], y[kCand];
     int r2[kSmax];
@@ -634,8 +661,7 @@ hipError_t launch_ser_forward(int B, int n, int hkv, const int32_t* idx1, const 
                       s2 == 4 && s3 == 4 &&
                           (((uintptr_t)idx1 | (uintptr_t)w1 | (uintptr_t)idx2 | (uintptr_t)w2) &
                            15) == 0};
-        hipLaunchKernelGGL(ser_fwd_unit_kernel, dim3((unsigned)((u.U + kBlock - 1) / kBlock)),
-                           dim3(kBlock), 0, st, u);
+        hipLaunchKernelGGL(ser_fwd_unit_kernel, dim3(xcd_unit_grid(u.U)), dim3(kBlock), 0, st, u);
         return hipGetLastError();
     }
     SerArgs a{idx1, w1, idx2, w2, idx_out, w_out, n, hkv, s1, s2, s3, B * n * hkv};
@@ -668,9 +694,14 @@ hipError_t launch_ser_backward(int B, int n, int hkv, const int32_t* idx1, const
         SerPullArgs pa{idx1, w1, idx2, w2, idx_out, w_out, dw_out, dw1, dw2, beg, len, list,
                        n, hkv, s1, s2, s3, (int)rows, (int)aliased,
                        make_fastdiv((uint32_t)hkv), make_fastdiv((uint32_t)n),
-                       make_fastdiv((uint32_t)s2)};
-        hipLaunchKernelGGL(ser_bwd_pull_kernel, dim3((unsigned)((rows + kBlock - 1) / kBlock)),
-                           dim3(kBlock), 0, st, pa);
+                       make_fastdiv((uint32_t)s2),
+                       s2 == 4 && s3 == 4 &&
+                           (((uintptr_t)idx1 | (uintptr_t)w1 | (uintptr_t)idx2 | (uintptr_t)w2) &
+                            15) == 0,
+                       s1 == 4 && (((uintptr_t)idx_out | (uintptr_t)w_out | (uintptr_t)dw_out) &
+                                   15) == 0};
+        hipLaunchKernelGGL(ser_bwd_pull_kernel, dim3(xcd_unit_grid((int)rows)), dim3(kBlock), 0,
+                           st, pa);
         return hipGetLastError();
     }
     if (s2 <= kSmax && s3 <= kSmax) {
