@@ -81,10 +81,14 @@ __device__ __forceinline__ A rows_sum(A x) {
     if constexpr (P >= 4) { A a = x, b = x; swap32(a, b); x = a + b; }
     return x;
 }
+// (compare-select: values coming out of a lane swap would otherwise be
+// canonicalised before a v_max; -inf is the only non-finite value here)
+template <typename A>
+__device__ __forceinline__ A sel_max(A a, A b) { return a > b ? a : b; }
 template <int P, typename A>
 __device__ __forceinline__ A rows_max(A x) {
-    if constexpr (P >= 2) { A a = x, b = x; swap16(a, b); x = amax(a, b); }
-    if constexpr (P >= 4) { A a = x, b = x; swap32(a, b); x = amax(a, b); }
+    if constexpr (P >= 2) { A a = x, b = x; swap16(a, b); x = sel_max(a, b); }
+    if constexpr (P >= 4) { A a = x, b = x; swap32(a, b); x = sel_max(a, b); }
     return x;
 }
 
@@ -116,6 +120,17 @@ __device__ __forceinline__ int rs_offset(int row) {
     if constexpr (P >= 2) off += (row & 1) * (V / 2);
     if constexpr (P >= 4) off += ((row >> 1) & 1) * (V / 4);
     return off;
+}
+
+// Value of lane `src` (a constant) in every lane (v_readlane to a scalar).
+__device__ __forceinline__ float bcast_lane(float x, int src) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), src));
+}
+__device__ __forceinline__ double bcast_lane(double x, int src) {
+    const uint64_t u = __builtin_bit_cast(uint64_t, x);
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)u, src);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(u >> 32), src);
+    return __builtin_bit_cast(double, ((uint64_t)hi << 32) | lo);
 }
 
 // Division of 0 <= x < 2^31 by an invariant divisor 1 <= d < 2^31 with a
