@@ -631,192 +631,6 @@ __global__ __launch_bounds__(kBlock) void sea_bwd_dst_fast_kernel(SeaBwdFast a) 
     }
 }
 
-
-// --------------------------------------------------- one unit / row per wave
-// Source pass for s in {3, 4}: the unit index is wave-uniform (scalar index
-// math); K and V are read per slot row for the dot products, and K once more
-// "transposed" (E elements of every slot's row per lane, one 256-byte row per
-// load) so that dq[E*l ..] = scale * sum_t dl_t K_t[E*l ..] needs no
-// cross-row reduction once dl_t is broadcast with readlane.
-template <typename T, int G>
-__global__ __launch_bounds__(kBlock) void sea_bwd_src_wave_kernel(SeaBwdFast a) {
-    using A = typename io<T>::acc;
-    constexpr int V = io<T>::V;
-    constexpr int E = V / 4;
-    constexpr int ROW = 256;
-    constexpr int FROW = ROW * 4 / (int)sizeof(T);
-    const int lane = threadIdx.x & (kWave - 1);
-    const int r = lane & 15;
-    const int row = lane >> 4;
-    const A c = (A)a.scale * (A)1.4426950408889634;
-    const A sc = (A)a.scale;
-    const A NEG = -INFINITY;
-    const uint32_t lane_off = (uint32_t)lane * (E * (uint32_t)sizeof(T));
-    const Sched sc0 = xcd_sched(a.sp, kWave);
-    const int q0 = __builtin_amdgcn_readfirstlane(sc0.q);
-    for (int u = q0; u < sc0.end; u += sc0.step) {
-        const Pos pos = pos_of(a.sp, sc0.x, u);
-        int jj[4];
-        float ww[4];
-#pragma unroll
-        for (int t = 0; t < 4; ++t) {
-            jj[t] = 0;
-            ww[t] = 0.0f;
-            if (t < a.s) {
-                jj[t] = a.idx[pos.unit * a.s + t];
-                ww[t] = a.w[pos.unit * a.s + t];
-            }
-        }
-        const int jm = row == 0 ? jj[0] : row == 1 ? jj[1] : row == 2 ? jj[2] : jj[3];
-        const float wm = row == 0 ? ww[0] : row == 1 ? ww[1] : row == 2 ? ww[2] : ww[3];
-        const bool live = wm > 0.0f;
-        const int kvrow = pos.kvrow0 + (live ? jm : 0) * a.hkv;
-        const uint32_t kvoff = (uint32_t)kvrow * ROW + r * 16;
-        const uint4 kr = *reinterpret_cast<const uint4*>(a.k + kvoff);
-        const uint4 vr = *reinterpret_cast<const uint4*>(a.v + kvoff);
-        if (a.global_index && live && r == 0) atomicAdd(a.ws.cnt + kvrow, 1);
-        A kt[4][E];
-#pragma unroll
-        for (int t = 0; t < 4; ++t) {
-            const int jt = ww[t] > 0.0f ? jj[t] : 0;
-            const char* krow = a.k + (size_t)((uint32_t)(pos.kvrow0 + jt * a.hkv) * ROW);
-            if constexpr (E == 2) {
-                const uint32_t x = *reinterpret_cast<const uint32_t*>(krow + lane_off);
-                kt[t][0] = bf16_lo(x);
-                kt[t][1] = bf16_hi(x);
-            } else {
-                kt[t][0] = *reinterpret_cast<const float*>(krow + lane_off);
-            }
-        }
-        const int h = pos.unit - pos.bi * a.hkv;
-        const uint32_t qrow = (uint32_t)(pos.bi * a.hq + h * G);
-        uint4 qr[G], dr[G];
-#pragma unroll
-        for (int g = 0; g < G; ++g) {
-            qr[g] = *reinterpret_cast<const uint4*>(a.q + (size_t)((qrow + g) * ROW) + r * 16);
-            dr[g] = *reinterpret_cast<const uint4*>(a.dout + (size_t)((qrow + g) * ROW) + r * 16);
-        }
-        const A lw = live ? (A)log2f(wm) : NEG;
-        A dws = 0;
-        float2* cp = a.ws.coef + ((size_t)pos.unit * a.s + row) * G;
-#pragma unroll
-        for (int g = 0; g < G; ++g) {
-            const A sd = row_sum16(dot16<V, A>(qr[g], kr));
-            const A gd = row_sum16(dot16<V, A>(dr[g], vr));
-            const A ls = sd * c;
-            const A l = live ? ls + lw : NEG;
-            const A M = rows_max<4>(l);
-            A ex, invZ, pw;
-            if constexpr (V == 8) {
-                ex = live ? __builtin_amdgcn_exp2f(l - M) : 0.0f;
-                const A Z = rows_sum<4>(ex);
-                invZ = Z > 0.0f ? __builtin_amdgcn_rcpf(Z) : 0.0f;
-                pw = live ? __builtin_amdgcn_exp2f(ls - M) : 0.0f;
-            } else {
-                ex = live ? exp2(l - M) : 0.0;
-                const A Z = rows_sum<4>(ex);
-                invZ = Z > 0.0 ? 1.0 / Z : 0.0;
-                pw = live ? exp2(ls - M) : 0.0;
-            }
-            const A p = ex * invZ;
-            const A gbar = rows_sum<4>(p * gd);
-            const A dls = p * (gd - gbar) * sc;
-            A dt[4];
-            dt[0] = bcast_lane(dls, 0);
-            dt[1] = bcast_lane(dls, 16);
-            dt[2] = bcast_lane(dls, 32);
-            dt[3] = bcast_lane(dls, 48);
-            A dqv[E];
-#pragma unroll
-            for (int e = 0; e < E; ++e)
-                dqv[e] = dt[0] * kt[0][e] + dt[1] * kt[1][e] + dt[2] * kt[2][e] + dt[3] * kt[3][e];
-            char* dqb = a.dq + (size_t)((qrow + g) * FROW);
-            store_f32_nt<E>(dqb + lane * (E * 4), dqv);
-            if (live && r == 0) cp[g] = make_float2((float)dls, (float)p);
-            dws += pw * invZ * (gd - gbar);
-        }
-        if (r == 0 && row < a.s) a.dw[(size_t)pos.unit * a.s + row] = (float)dws;
-    }
-}
-
-// Target pass, one K/V row per wave: its incoming edges are taken four at a
-// time; edge ids and their coefficients are wave-uniform (scalar loads), and
-// each lane accumulates E elements of every edge's q and dout rows (one
-// 256-byte row per load), so no reduction is needed before the store.
-template <typename T, int G>
-__global__ __launch_bounds__(kBlock) void sea_bwd_dst_wave_kernel(SeaBwdFast a) {
-    using A = typename io<T>::acc;
-    constexpr int V = io<T>::V;
-    constexpr int E = V / 4;
-    constexpr int ROW = 256;
-    constexpr int FROW = ROW * 4 / (int)sizeof(T);
-    const int lane = threadIdx.x & (kWave - 1);
-    const uint32_t lane_off = (uint32_t)lane * (E * (uint32_t)sizeof(T));
-    const Sched sc0 = xcd_sched(a.sp, kWave);
-    const int q0 = __builtin_amdgcn_readfirstlane(sc0.q);
-    for (int u = q0; u < sc0.end; u += sc0.step) {
-        const Pos pos = pos_of(a.sp, sc0.x, u);
-        const int h = pos.unit - pos.bi * a.hkv;
-        int beg, end;
-        if (a.global_index) {
-            beg = a.ws.off[pos.unit];
-            end = a.ws.off[pos.unit + 1];
-        } else {
-            beg = a.ws.beg[pos.prow];
-            end = beg + a.ws.len[pos.prow];
-        }
-        A ak[E], av[E];
-#pragma unroll
-        for (int e = 0; e < E; ++e) { ak[e] = 0; av[e] = 0; }
-        for (int e0 = beg; e0 < end; e0 += 4) {
-            int eid[4];
-#pragma unroll
-            for (int q = 0; q < 4; ++q) eid[q] = e0 + q < end ? a.ws.list[e0 + q] : -1;
-            uint32_t qv[4][G], dv2[4][G];
-            float2 co[4][G];
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                const int src = eid[q] >= 0 ? (int)fdiv((uint32_t)eid[q], a.fd_s) : 0;
-                const int sbi = (int)fdiv((uint32_t)src, a.fd_hkv);
-                const uint32_t qrow = (uint32_t)(sbi * a.hq + h * G);
-#pragma unroll
-                for (int g = 0; g < G; ++g) {
-                    co[q][g] = eid[q] >= 0 ? a.ws.coef[(size_t)eid[q] * G + g] : make_float2(0.f, 0.f);
-                    const char* qb = a.q + (size_t)((qrow + g) * ROW);
-                    const char* db = a.dout + (size_t)((qrow + g) * ROW);
-                    if constexpr (E == 2) {
-                        qv[q][g] = *reinterpret_cast<const uint32_t*>(qb + lane_off);
-                        dv2[q][g] = *reinterpret_cast<const uint32_t*>(db + lane_off);
-                    } else {
-                        qv[q][g] = *reinterpret_cast<const uint32_t*>(qb + lane_off);
-                        dv2[q][g] = *reinterpret_cast<const uint32_t*>(db + lane_off);
-                    }
-                }
-            }
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-#pragma unroll
-                for (int g = 0; g < G; ++g) {
-                    const A ca = (A)co[q][g].x, cpb = (A)co[q][g].y;
-                    if constexpr (E == 2) {
-                        ak[0] += ca * (A)bf16_lo(qv[q][g]);
-                        ak[1] += ca * (A)bf16_hi(qv[q][g]);
-                        av[0] += cpb * (A)bf16_lo(dv2[q][g]);
-                        av[1] += cpb * (A)bf16_hi(dv2[q][g]);
-                    } else {
-                        ak[0] += ca * (A)__uint_as_float(qv[q][g]);
-                        av[0] += cpb * (A)__uint_as_float(dv2[q][g]);
-                    }
-                }
-            }
-        }
-        char* dkb = a.dk + (size_t)((uint32_t)pos.unit * FROW);
-        char* dvb = a.dv + (size_t)((uint32_t)pos.unit * FROW);
-        store_f32_nt<E>(dkb + lane * (E * 4), ak);
-        store_f32_nt<E>(dvb + lane * (E * 4), av);
-    }
-}
-
 void launch_index(const SeaBwdArgs& a, long long E, hipStream_t st) {
     const unsigned sblocks = (unsigned)((a.U + kScanPerBlock - 1) / kScanPerBlock);
     hipLaunchKernelGGL(scan_local_kernel, dim3(sblocks), dim3(1024), 0, st,
@@ -857,17 +671,14 @@ hipError_t dispatch_g(const SeaBwdArgs& a, int G, long long E, hipStream_t st) {
 
 template <typename T, int G, int P, int PD>
 hipError_t run_fast(const SeaBwdArgs& g, const SeaBwdFast& a, long long E, hipStream_t st) {
-    const void* src_fn = P == 4 ? reinterpret_cast<const void*>(&sea_bwd_src_wave_kernel<T, G>)
-                                : reinterpret_cast<const void*>(&sea_bwd_src_fast_kernel<T, G, P>);
-    const int nsrc = persistent_grid(src_fn, a.U, kBlock / (16 * P));
+    const int nsrc = persistent_grid(reinterpret_cast<const void*>(
+                                         &sea_bwd_src_fast_kernel<T, G, P>),
+                                     a.U, kBlock / (16 * P));
     if (a.global_index) {
         const hipError_t e = launch_zero_f32(reinterpret_cast<float*>(a.ws.cnt), (size_t)a.U, st);
         if (e != hipSuccess) return e;
     }
-    if constexpr (P == 4)
-        hipLaunchKernelGGL((sea_bwd_src_wave_kernel<T, G>), dim3(nsrc), dim3(kBlock), 0, st, a);
-    else
-        hipLaunchKernelGGL((sea_bwd_src_fast_kernel<T, G, P>), dim3(nsrc), dim3(kBlock), 0, st, a);
+    hipLaunchKernelGGL((sea_bwd_src_fast_kernel<T, G, P>), dim3(nsrc), dim3(kBlock), 0, st, a);
     if (a.global_index) {
         launch_index(g, E, st);
     } else {
@@ -876,9 +687,9 @@ hipError_t run_fast(const SeaBwdArgs& g, const SeaBwdFast& a, long long E, hipSt
         if (e != hipSuccess) return e;
     }
     const int ndst = persistent_grid(reinterpret_cast<const void*>(
-                                         &sea_bwd_dst_wave_kernel<T, G>),
-                                     a.U, kBlock / kWave);
-    hipLaunchKernelGGL((sea_bwd_dst_wave_kernel<T, G>), dim3(ndst), dim3(kBlock), 0, st, a);
+                                         &sea_bwd_dst_fast_kernel<T, G, PD>),
+                                     a.U, kBlock / (16 * PD));
+    hipLaunchKernelGGL((sea_bwd_dst_fast_kernel<T, G, PD>), dim3(ndst), dim3(kBlock), 0, st, a);
     return hipGetLastError();
 }
 

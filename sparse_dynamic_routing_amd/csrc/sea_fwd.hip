@@ -329,111 +329,6 @@ hipError_t dispatch_g(const SeaFwdArgs& a, int G, hipStream_t st) {
     }
 }
 
-
-// One unit per wave (s in {3, 4}): the unit index is wave-uniform, so its
-// decomposition and the row addresses live in scalar registers.  Lane
-// (row t, r) loads the 16-byte piece r of slot t's K row for the scores (as
-// above); V is read "transposed": for every slot, lane l loads elements
-// [E*l, E*l + E) of the V row (E = d / 64; one row per load instruction, 256
-// contiguous bytes), and after the softmax the four slot probabilities are
-// broadcast with readlane, so o[E*l .. E*l + E) = sum_t p_t V_t[...] needs no
-// cross-row reduction at all.
-template <typename T, int G>
-__global__ __launch_bounds__(kBlock) void sea_fwd_wave_kernel(SeaFwdFast a) {
-    using A = typename io<T>::acc;
-    constexpr int V = io<T>::V;          // elements per 16 bytes
-    constexpr int E = V / 4;             // elements per lane of a transposed row
-    constexpr int ROW = 256;
-    const int lane = threadIdx.x & (kWave - 1);
-    const int r = lane & 15;
-    const int row = lane >> 4;
-    const A c = (A)a.scale * (A)1.4426950408889634;
-    const A NEG = -INFINITY;
-    const Sched sc0 = xcd_sched(a.sp, kWave);
-    const int q0 = __builtin_amdgcn_readfirstlane(sc0.q);
-    for (int u = q0; u < sc0.end; u += sc0.step) {
-        const UnitPos pos = unit_pos(a.sp, sc0.x, u);
-        int jj[4];
-        float ww[4];
-#pragma unroll
-        for (int t = 0; t < 4; ++t) {
-            jj[t] = 0;
-            ww[t] = 0.0f;
-            if (t < a.s) {
-                jj[t] = a.idx[pos.unit * a.s + t];
-                ww[t] = a.w[pos.unit * a.s + t];
-            }
-        }
-        // this lane's slot for the scores
-        const int jm = row == 0 ? jj[0] : row == 1 ? jj[1] : row == 2 ? jj[2] : jj[3];
-        const float wm = row == 0 ? ww[0] : row == 1 ? ww[1] : row == 2 ? ww[2] : ww[3];
-        const bool live = wm > 0.0f;
-        const uint32_t kvoff = (uint32_t)(pos.kvrow0 + (live ? jm : 0) * a.hkv) * ROW + r * 16;
-        const uint4 kr = *reinterpret_cast<const uint4*>(a.k + kvoff);
-        // V rows, transposed: E elements per lane per slot
-        const uint32_t lane_off = (uint32_t)lane * (E * (uint32_t)sizeof(T));
-        A vt[4][E];
-#pragma unroll
-        for (int t = 0; t < 4; ++t) {
-            const int jt = ww[t] > 0.0f ? jj[t] : 0;
-            const char* vrow = a.v + (size_t)((uint32_t)(pos.kvrow0 + jt * a.hkv) * ROW);
-            const char* vp = vrow + lane_off;
-            if constexpr (E == 2) {
-                const uint32_t x = *reinterpret_cast<const uint32_t*>(vp);
-                vt[t][0] = bf16_lo(x);
-                vt[t][1] = bf16_hi(x);
-            } else {
-                vt[t][0] = *reinterpret_cast<const float*>(vp);
-            }
-        }
-        const int h = pos.unit - pos.bi * a.hkv;
-        const uint32_t qrow = (uint32_t)(pos.bi * a.hq + h * G);
-        uint4 qr[G];
-#pragma unroll
-        for (int g = 0; g < G; ++g) {
-            const char* qb = a.q + (size_t)((qrow + g) * ROW);
-            qr[g] = *reinterpret_cast<const uint4*>(qb + r * 16);
-        }
-        const A lw = live ? (A)log2f(wm) : NEG;
-#pragma unroll
-        for (int g = 0; g < G; ++g) {
-            A dot;
-            if constexpr (V == 8) {
-                dot = dot_bf16x8(qr[g], kr);
-            } else {
-                dot = (A)__uint_as_float(qr[g].x) * (A)__uint_as_float(kr.x) +
-                      (A)__uint_as_float(qr[g].y) * (A)__uint_as_float(kr.y) +
-                      (A)__uint_as_float(qr[g].z) * (A)__uint_as_float(kr.z) +
-                      (A)__uint_as_float(qr[g].w) * (A)__uint_as_float(kr.w);
-            }
-            dot = row_sum16(dot);
-            const A l = live ? dot * c + lw : NEG;
-            const A M = rows_max<4>(l);
-            A ex;
-            if constexpr (V == 8) ex = live ? __builtin_amdgcn_exp2f(l - M) : 0.0f;
-            else ex = live ? exp2(l - M) : 0.0;
-            const A Z = rows_sum<4>(ex);
-            A inv;
-            if constexpr (V == 8) inv = Z > 0.0f ? __builtin_amdgcn_rcpf(Z) : 0.0f;
-            else inv = Z > 0.0 ? 1.0 / Z : 0.0;
-            const A pm = ex * inv;
-            A pt[4];
-            pt[0] = bcast_lane(pm, 0);
-            pt[1] = bcast_lane(pm, 16);
-            pt[2] = bcast_lane(pm, 32);
-            pt[3] = bcast_lane(pm, 48);
-            A ov[E];
-#pragma unroll
-            for (int e = 0; e < E; ++e)
-                ov[e] = pt[0] * vt[0][e] + pt[1] * vt[1][e] + pt[2] * vt[2][e] + pt[3] * vt[3][e];
-            char* ob = a.o + (size_t)((qrow + g) * ROW);
-            char* op = ob + lane_off;
-            if constexpr (E == 2) store_u32_nt(op, pack_bf16x2(ov[0], ov[1]));
-            else store_f32_nt<1>(op, ov);
-        }
-    }
-}
-
 template <typename T, int G, int P>
 hipError_t run_fast(const SeaFwdFast& a, hipStream_t st) {
     const void* fn = reinterpret_cast<const void*>(&sea_fwd_fast_kernel<T, G, P>);
@@ -443,18 +338,10 @@ hipError_t run_fast(const SeaFwdFast& a, hipStream_t st) {
 }
 
 template <typename T, int G>
-hipError_t run_wave(const SeaFwdFast& a, hipStream_t st) {
-    const void* fn = reinterpret_cast<const void*>(&sea_fwd_wave_kernel<T, G>);
-    const int nwg = persistent_grid(fn, a.U, kBlock / kWave);
-    hipLaunchKernelGGL((sea_fwd_wave_kernel<T, G>), dim3(nwg), dim3(kBlock), 0, st, a);
-    return hipGetLastError();
-}
-
-template <typename T, int G>
 hipError_t fast_p(const SeaFwdFast& a, hipStream_t st) {
     if (a.s <= 1) return run_fast<T, G, 1>(a, st);
     if (a.s <= 2) return run_fast<T, G, 2>(a, st);
-    return run_wave<T, G>(a, st);
+    return run_fast<T, G, 4>(a, st);
 }
 
 template <typename T>
