@@ -48,6 +48,41 @@ BYTES_PER_UNIT = {
     "gm_ser_backward": 32 + 32 + 16 + 16,               # A, A', dw', dw
 }
 CALLS = list(BYTES_PER_UNIT)
+# kernels each call launches (name prefixes as the profiler reports them)
+CALL_KERNELS = {
+    "gm_ser_forward": ["ser_fwd"],
+    "gm_sea_forward": ["sea_fwd"],
+    "gm_sea_backward": ["sea_bwd_src", "edge_index", "sea_bwd_dst"],
+    "gm_ser_backward": ["edge_index", "ser_bwd"],
+}
+PROFILE = os.path.join(ROOT, "profiles", "metric_pass_kernels.md")
+
+
+def profiled_traffic(call: str):
+    """Calibrated HBM bytes per launch of `call` from the committed counter
+    summary, or None when it is missing or the kernels changed since."""
+    from sparse_dynamic_routing_amd.profile_summary import source_hash
+    if not os.path.exists(PROFILE):
+        return None
+    kernels, hsh = {}, None
+    for line in open(PROFILE):
+        line = line.strip()
+        if line.startswith("source_hash:"):
+            hsh = line.split(":", 1)[1].strip()
+        elif line.startswith("kernel:"):
+            parts = [x.strip() for x in line.split("|")]
+            name = parts[0].split(":", 1)[1].strip()
+            kv = dict(x.split("=") for x in parts[1:])
+            kernels[name] = float(kv["fetch_bytes"]) + float(kv["write_bytes"])
+    if hsh != source_hash():
+        return None
+    total = 0.0
+    for prefix in CALL_KERNELS[call]:
+        hits = [v for k, v in kernels.items() if k.split("<")[0].startswith(prefix)]
+        if not hits:
+            return None
+        total += sum(hits) / len(hits)
+    return total
 
 
 def parse():
@@ -208,8 +243,10 @@ def main():
         "pass_algorithmic_GBps": pass_bytes / (ms * 1e-3) / 1e9,
         "pass_frac_of_peak": pass_bytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS,
         "per_call_ms": per_call,
-        "roofline": {"kernel": dom, "bound": "hbm", "achieved": dom_gbs, "peak": PEAK_HBM_GBS,
-                     "unit": "GB/s", "frac": dom_gbs / PEAK_HBM_GBS, "traffic": None,
+        "roofline": {"kernel": dom, "kernels": CALL_KERNELS[dom], "bound": "hbm",
+                     "achieved": dom_gbs, "peak": PEAK_HBM_GBS,
+                     "unit": "GB/s", "frac": dom_gbs / PEAK_HBM_GBS,
+                     "traffic": profiled_traffic(dom),
                      "bytes_per_unit": BYTES_PER_UNIT[dom], "units_per_launch": U},
         "wall_s_timed": wall,
     }
