@@ -220,6 +220,41 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
     return __builtin_bit_cast(uint32_t, v);
 }
 
+// exp2 / log2 / reciprocal: the hardware approximations in fp32 (about 1 ulp),
+// the libm functions in fp64.
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ __forceinline__ double fast_exp2(double x) { return exp2(x); }
+__device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
+__device__ __forceinline__ double fast_log2(double x) { return log2(x); }
+__device__ __forceinline__ float fast_rcp(float x) { return __builtin_amdgcn_rcpf(x); }
+__device__ __forceinline__ double fast_rcp(double x) { return 1.0 / x; }
+
+// One 16-byte piece of a d-row (8 bf16 or 4 fp32) in the accumulation type,
+// and the dot product of two pieces.
+template <typename A, int V>
+__device__ __forceinline__ void unpack16(const uint4& u, A (&x)[V]) {
+    if constexpr (V == 8) {
+        float f[8];
+        bf16x8_to_f32(u, f);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) x[e] = f[e];
+    } else {
+        x[0] = __uint_as_float(u.x); x[1] = __uint_as_float(u.y);
+        x[2] = __uint_as_float(u.z); x[3] = __uint_as_float(u.w);
+    }
+}
+template <int V, typename A>
+__device__ __forceinline__ A dot16(const uint4& a, const uint4& b) {
+    if constexpr (V == 8) {
+        return dot_bf16x8(a, b);
+    } else {
+        return (A)__uint_as_float(a.x) * (A)__uint_as_float(b.x) +
+               (A)__uint_as_float(a.y) * (A)__uint_as_float(b.y) +
+               (A)__uint_as_float(a.z) * (A)__uint_as_float(b.z) +
+               (A)__uint_as_float(a.w) * (A)__uint_as_float(b.w);
+    }
+}
+
 // Streaming (non-temporal) stores of outputs nobody reads soon, so they do
 // not push gathered rows out of the L2.
 typedef float f32x2_t __attribute__((ext_vector_type(2)));

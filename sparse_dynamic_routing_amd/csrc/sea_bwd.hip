@@ -420,31 +420,6 @@ __device__ __forceinline__ Pos pos_of(const SegPlan& sp, int x, int q) {
     return p;
 }
 
-template <typename A, int V>
-__device__ __forceinline__ void unpack16(const uint4& u, A (&x)[V]) {
-    if constexpr (V == 8) {
-        float f[8];
-        bf16x8_to_f32(u, f);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) x[e] = f[e];
-    } else {
-        x[0] = __uint_as_float(u.x); x[1] = __uint_as_float(u.y);
-        x[2] = __uint_as_float(u.z); x[3] = __uint_as_float(u.w);
-    }
-}
-
-template <int V, typename A>
-__device__ __forceinline__ A dot16(const uint4& a, const uint4& b) {
-    if constexpr (V == 8) {
-        return dot_bf16x8(a, b);
-    } else {
-        return (A)__uint_as_float(a.x) * (A)__uint_as_float(b.x) +
-               (A)__uint_as_float(a.y) * (A)__uint_as_float(b.y) +
-               (A)__uint_as_float(a.z) * (A)__uint_as_float(b.z) +
-               (A)__uint_as_float(a.w) * (A)__uint_as_float(b.w);
-    }
-}
-
 template <int L, typename A>
 __device__ __forceinline__ void store_f32(char* p, const A* x) {
     store_n<L>(reinterpret_cast<float*>(p), x);

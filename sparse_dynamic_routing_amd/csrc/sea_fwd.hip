@@ -187,6 +187,7 @@ struct SeaFwdFast {
     int n, hq, hkv, s, U;
     float scale;
     SegPlan sp;
+    int vec;   // s == 4 and 16-byte aligned edge rows: one load per row
 };
 
 struct UnitPos {
@@ -329,6 +330,117 @@ hipError_t dispatch_g(const SeaFwdArgs& a, int G, hipStream_t st) {
     }
 }
 
+// One unit per 16-lane row, four units per wavefront.  Lane r of the row
+// holds bytes [16r, 16r + 16) of every 256-byte d-row the unit touches (its
+// G query rows, and the K and V rows of its S edge slots, side by side in
+// registers).  The only cross-lane step is the 16-lane DPP sum of each
+// score; the softmax over the slots and the weighted sum of the V rows are
+// lane-local.  Slots t >= s (when s < S) are dead.  Rows never exchange
+// data, so rows of one wavefront may leave the item loop at different times.
+template <typename T, int G, int S, bool VEC>
+__global__ __launch_bounds__(kBlock) void sea_fwd_row_kernel(SeaFwdFast a) {
+    using A = typename io<T>::acc;
+    constexpr int V = io<T>::V;
+    constexpr int ROW = 256;
+    constexpr int GC = G < 4 ? G : 4;   // query rows held at once
+    const int r = threadIdx.x & 15;
+    const A c = (A)a.scale * (A)1.4426950408889634;
+    const A NEG = -INFINITY;
+    const Sched sc = xcd_sched(a.sp, 16);
+    if (sc.q >= sc.end) return;
+
+    struct Item {
+        UnitPos pos;
+        int j[S];
+        float wt[S];
+    };
+    // the item's edge slots; past the end the last item is read again (a
+    // valid address, so the load needs no branch) and never used
+    auto fetch = [&](int u) {
+        Item it;
+        it.pos = unit_pos(a.sp, sc.x, u < sc.end ? u : sc.end - 1);
+        if constexpr (VEC) {
+            const int4 j4 = *reinterpret_cast<const int4*>(a.idx + (size_t)it.pos.unit * 4);
+            const float4 w4 = *reinterpret_cast<const float4*>(a.w + (size_t)it.pos.unit * 4);
+            it.j[0] = j4.x; it.j[1] = j4.y; it.j[2] = j4.z; it.j[3] = j4.w;
+            it.wt[0] = w4.x; it.wt[1] = w4.y; it.wt[2] = w4.z; it.wt[3] = w4.w;
+        } else {
+            const size_t e0 = (size_t)it.pos.unit * a.s;
+#pragma unroll
+            for (int t = 0; t < S; ++t) {
+                const int tt = t < a.s ? t : a.s - 1;
+                it.j[t] = a.idx[e0 + tt];
+                const float wv = a.w[e0 + tt];
+                it.wt[t] = t < a.s ? wv : 0.0f;
+            }
+        }
+        return it;
+    };
+
+    Item cur = fetch(sc.q);
+    for (int u = sc.q; u < sc.end; u += sc.step) {
+        const Item nxt = fetch(u + sc.step);
+        bool live[S];
+        uint4 kr[S], vr[S];
+#pragma unroll
+        for (int t = 0; t < S; ++t) {
+            live[t] = cur.wt[t] > 0.0f;
+            const uint32_t off =
+                (uint32_t)(cur.pos.kvrow0 + (live[t] ? cur.j[t] : 0) * a.hkv) * ROW + r * 16;
+            kr[t] = *reinterpret_cast<const uint4*>(a.k + off);
+            vr[t] = *reinterpret_cast<const uint4*>(a.v + off);
+        }
+        const uint32_t qoff =
+            (uint32_t)(cur.pos.bi * a.hq + (cur.pos.unit - cur.pos.bi * a.hkv) * G) * ROW + r * 16;
+        A lw[S];
+#pragma unroll
+        for (int t = 0; t < S; ++t) lw[t] = live[t] ? fast_log2((A)cur.wt[t]) : NEG;
+#pragma unroll
+        for (int g0 = 0; g0 < G; g0 += GC) {
+            uint4 qr[GC];
+#pragma unroll
+            for (int g = 0; g < GC; ++g)
+                qr[g] = *reinterpret_cast<const uint4*>(a.q + qoff + (g0 + g) * ROW);
+#pragma unroll
+            for (int g = 0; g < GC; ++g) {
+                A l[S], M = NEG;
+#pragma unroll
+                for (int t = 0; t < S; ++t) {
+                    const A dot = row_sum16(dot16<V, A>(qr[g], kr[t]));
+                    l[t] = live[t] ? dot * c + lw[t] : NEG;
+                    M = l[t] > M ? l[t] : M;
+                }
+                A p[S], Z = 0;
+#pragma unroll
+                for (int t = 0; t < S; ++t) {
+                    p[t] = live[t] ? fast_exp2(l[t] - M) : (A)0;
+                    Z += p[t];
+                }
+                const A inv = Z > (A)0 ? fast_rcp(Z) : (A)0;
+                A o[V];
+#pragma unroll
+                for (int e = 0; e < V; ++e) o[e] = 0;
+#pragma unroll
+                for (int t = 0; t < S; ++t) {
+                    A vf[V];
+                    unpack16<A, V>(vr[t], vf);
+                    const A pt = p[t] * inv;
+#pragma unroll
+                    for (int e = 0; e < V; ++e) o[e] += pt * vf[e];
+                }
+                char* op = a.o + qoff + (g0 + g) * ROW;
+                if constexpr (V == 8) {
+                    store_u32x4_nt(op, pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3]),
+                                   pack_bf16x2(o[4], o[5]), pack_bf16x2(o[6], o[7]));
+                } else {
+                    store_f32_nt<4>(op, o);
+                }
+            }
+        }
+        cur = nxt;
+    }
+}
+
 template <typename T, int G, int P>
 hipError_t run_fast(const SeaFwdFast& a, hipStream_t st) {
     const void* fn = reinterpret_cast<const void*>(&sea_fwd_fast_kernel<T, G, P>);
@@ -337,11 +449,20 @@ hipError_t run_fast(const SeaFwdFast& a, hipStream_t st) {
     return hipGetLastError();
 }
 
+template <typename T, int G, int S, bool VEC>
+hipError_t run_row(const SeaFwdFast& a, hipStream_t st) {
+    const void* fn = reinterpret_cast<const void*>(&sea_fwd_row_kernel<T, G, S, VEC>);
+    const int nwg = persistent_grid(fn, a.U, kBlock / 16);
+    hipLaunchKernelGGL((sea_fwd_row_kernel<T, G, S, VEC>), dim3(nwg), dim3(kBlock), 0, st, a);
+    return hipGetLastError();
+}
+
 template <typename T, int G>
 hipError_t fast_p(const SeaFwdFast& a, hipStream_t st) {
-    if (a.s <= 1) return run_fast<T, G, 1>(a, st);
-    if (a.s <= 2) return run_fast<T, G, 2>(a, st);
-    return run_fast<T, G, 4>(a, st);
+    if (a.s <= 1) return run_row<T, G, 1, false>(a, st);
+    if (a.s <= 2) return run_row<T, G, 2, false>(a, st);
+    if (a.vec) return run_row<T, G, 4, true>(a, st);
+    return run_row<T, G, 4, false>(a, st);
 }
 
 template <typename T>
@@ -381,6 +502,7 @@ hipError_t launch_sea_forward(int B, int n, int hq, int hkv, int d, bool bf16, f
         f.v = static_cast<const char*>(v); f.idx = idx; f.w = w; f.o = static_cast<char*>(o);
         f.n = n; f.hq = hq; f.hkv = hkv; f.s = s; f.U = a.U; f.scale = scale;
         make_seg_plan(f.sp, B, n, hkv);
+        f.vec = s == 4 && (((uintptr_t)idx | (uintptr_t)w) & 15) == 0;
         return bf16 ? fast_g<bf16_t>(f, G, st) : fast_g<float>(f, G, st);
     }
     return bf16 ? dispatch_g<bf16_t>(a, G, st) : dispatch_g<float>(a, G, st);
