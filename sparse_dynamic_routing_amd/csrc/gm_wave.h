@@ -255,6 +255,23 @@ __device__ __forceinline__ A dot16(const uint4& a, const uint4& b) {
     }
 }
 
+// Split piece of a 256-byte d-row for lane r of a 16-lane row: bytes
+// [8r, 8r + 8) and [128 + 8r, 128 + 8r + 8) for bf16 (elements 4r .. 4r+3
+// and 64 + 4r .. 64 + 4r + 3), bytes [16r, 16r + 16) for fp32 (elements
+// 4r .. 4r+3).  With this mapping the lane's fp32 results for a bf16 row are
+// two 16-byte runs at 16r and 256 + 16r of the 512-byte fp32 row, so each
+// store instruction of the row covers 256 contiguous bytes.
+template <int V>
+__device__ __forceinline__ uint4 load_split(const char* row, int r) {
+    if constexpr (V == 8) {
+        const uint2 lo = *reinterpret_cast<const uint2*>(row + r * 8);
+        const uint2 hi = *reinterpret_cast<const uint2*>(row + 128 + r * 8);
+        return make_uint4(lo.x, lo.y, hi.x, hi.y);
+    } else {
+        return *reinterpret_cast<const uint4*>(row + r * 16);
+    }
+}
+
 // Streaming (non-temporal) stores of outputs nobody reads soon, so they do
 // not push gathered rows out of the L2.
 typedef float f32x2_t __attribute__((ext_vector_type(2)));
@@ -276,6 +293,13 @@ __device__ __forceinline__ void store_f32_nt(char* p, const A* x) {
             __builtin_nontemporal_store(v, reinterpret_cast<f32x4_t*>(p + 4 * e));
         }
     }
+}
+
+// fp32 results of lane r for a split piece (see load_split), streaming stores.
+template <int V, typename A>
+__device__ __forceinline__ void store_split_f32_nt(char* frow, int r, const A (&x)[V]) {
+    store_f32_nt<4>(frow + r * 16, x);
+    if constexpr (V == 8) store_f32_nt<4>(frow + 256 + r * 16, x + 4);
 }
 
 __device__ __forceinline__ void store_u32_nt(char* p, uint32_t a) {

@@ -401,6 +401,7 @@ struct SeaBwdFast {
     FastDiv fd_s, fd_hkv;
     SegPlan sp;
     int global_index;   // 1: in-degrees counted here, offsets from the global scan
+    int vec;            // s == 4 and 16-byte aligned edge rows: one load per row
 };
 
 struct Pos {
@@ -518,6 +519,164 @@ __global__ __launch_bounds__(kBlock) void sea_bwd_src_fast_kernel(SeaBwdFast a) 
         pos = npos;
         j = nj;
         wt = nwt;
+    }
+}
+
+// Source pass with one unit per 16-lane row, four units per wavefront: lane
+// r holds bytes [16r, 16r + 16) of the unit's G query and upstream-gradient
+// rows and of the K and V rows of its S edge slots (registers).  Scores and
+// the dout.v products are 16-lane DPP sums; the softmax, dl, dq and dw are
+// lane-local.  Lane t < S writes slot t's per-edge coefficients and dw.
+// GLOBAL: also count the in-degree of every K/V row (global index path).
+template <typename T, int G, int S, bool VEC, bool GLOBAL>
+__global__ __launch_bounds__(kBlock) void sea_bwd_src_row_kernel(SeaBwdFast a) {
+    using A = typename io<T>::acc;
+    constexpr int V = io<T>::V;
+    constexpr int ROW = 256;                          // bytes of an input d-row
+    constexpr int FROW = ROW * 4 / (int)sizeof(T);    // bytes of an fp32 gradient row
+    constexpr int GC = G < 2 ? G : 2;                 // query heads held at once
+    const int r = threadIdx.x & 15;
+    const A c = (A)a.scale * (A)1.4426950408889634;
+    const A sc = (A)a.scale;
+    const A NEG = -INFINITY;
+    const Sched sch = xcd_sched(a.sp, 16);
+    if (sch.q >= sch.end) return;
+
+    struct Item {
+        Pos pos;
+        int j[S];
+        float wt[S];
+    };
+    auto fetch = [&](int u) {
+        Item it;
+        it.pos = pos_of(a.sp, sch.x, u < sch.end ? u : sch.end - 1);
+        if constexpr (VEC) {
+            const int4 j4 = *reinterpret_cast<const int4*>(a.idx + (size_t)it.pos.unit * 4);
+            const float4 w4 = *reinterpret_cast<const float4*>(a.w + (size_t)it.pos.unit * 4);
+            it.j[0] = j4.x; it.j[1] = j4.y; it.j[2] = j4.z; it.j[3] = j4.w;
+            it.wt[0] = w4.x; it.wt[1] = w4.y; it.wt[2] = w4.z; it.wt[3] = w4.w;
+        } else {
+            const size_t e0 = (size_t)it.pos.unit * a.s;
+#pragma unroll
+            for (int t = 0; t < S; ++t) {
+                const int tt = t < a.s ? t : a.s - 1;
+                it.j[t] = a.idx[e0 + tt];
+                const float wv = a.w[e0 + tt];
+                it.wt[t] = t < a.s ? wv : 0.0f;
+            }
+        }
+        return it;
+    };
+
+    Item cur = fetch(sch.q);
+    for (int u = sch.q; u < sch.end; u += sch.step) {
+        const Item nxt = fetch(u + sch.step);
+        bool live[S];
+        int kvrow[S];
+        uint4 kr[S], vr[S];
+#pragma unroll
+        for (int t = 0; t < S; ++t) {
+            live[t] = cur.wt[t] > 0.0f;
+            kvrow[t] = cur.pos.kvrow0 + (live[t] ? cur.j[t] : 0) * a.hkv;
+            const uint32_t off = (uint32_t)kvrow[t] * ROW;
+            kr[t] = load_split<V>(a.k + off, r);
+            vr[t] = load_split<V>(a.v + off, r);
+        }
+        const int h = cur.pos.unit - cur.pos.bi * a.hkv;
+        const uint32_t qrow = (uint32_t)(cur.pos.bi * a.hq + h * G);
+        if constexpr (GLOBAL) {
+#pragma unroll
+            for (int t = 0; t < S; ++t)
+                if (r == t && live[t]) atomicAdd(a.ws.cnt + kvrow[t], 1);
+        }
+        A lw[S], dws[S];
+#pragma unroll
+        for (int t = 0; t < S; ++t) {
+            lw[t] = live[t] ? fast_log2((A)cur.wt[t]) : NEG;
+            dws[t] = 0;
+        }
+        // coefficients (scale * dl, p) of this lane's slot, one per head
+        A my_dl[G], my_p[G];
+#pragma unroll
+        for (int g0 = 0; g0 < G; g0 += GC) {
+            uint4 qr[GC], dr[GC];
+#pragma unroll
+            for (int g = 0; g < GC; ++g) {
+                qr[g] = load_split<V>(a.q + (qrow + g0 + g) * ROW, r);
+                dr[g] = load_split<V>(a.dout + (qrow + g0 + g) * ROW, r);
+            }
+#pragma unroll
+            for (int g = 0; g < GC; ++g) {
+                A ls[S], l[S], gd[S], M = NEG;
+#pragma unroll
+                for (int t = 0; t < S; ++t) {
+                    ls[t] = row_sum16(dot16<V, A>(qr[g], kr[t])) * c;
+                    gd[t] = row_sum16(dot16<V, A>(dr[g], vr[t]));
+                    l[t] = live[t] ? ls[t] + lw[t] : NEG;
+                    M = l[t] > M ? l[t] : M;
+                }
+                A ex[S], Z = 0;
+#pragma unroll
+                for (int t = 0; t < S; ++t) {
+                    ex[t] = live[t] ? fast_exp2(l[t] - M) : (A)0;
+                    Z += ex[t];
+                }
+                const A invZ = Z > (A)0 ? fast_rcp(Z) : (A)0;
+                A p[S], gbar = 0;
+#pragma unroll
+                for (int t = 0; t < S; ++t) {
+                    p[t] = ex[t] * invZ;
+                    gbar += p[t] * gd[t];
+                }
+                A dls[S];
+#pragma unroll
+                for (int t = 0; t < S; ++t) {
+                    dls[t] = p[t] * (gd[t] - gbar) * sc;
+                    // dl / w = exp(l - M) / (Z w) = exp(scale * dot - M) / Z
+                    const A pw = live[t] ? fast_exp2(ls[t] - M) : (A)0;
+                    dws[t] += pw * invZ * (gd[t] - gbar);
+                }
+                A sel_dl = dls[0], sel_p = p[0];
+#pragma unroll
+                for (int t = 1; t < S; ++t) {
+                    sel_dl = r == t ? dls[t] : sel_dl;
+                    sel_p = r == t ? p[t] : sel_p;
+                }
+                my_dl[g0 + g] = sel_dl;
+                my_p[g0 + g] = sel_p;
+                // dq of this head: sum over the slots of scale * dl * k
+                A dq[V];
+#pragma unroll
+                for (int e = 0; e < V; ++e) dq[e] = 0;
+#pragma unroll
+                for (int t = 0; t < S; ++t) {
+                    A kf[V];
+                    unpack16<A, V>(kr[t], kf);
+#pragma unroll
+                    for (int e = 0; e < V; ++e) dq[e] += dls[t] * kf[e];
+                }
+                store_split_f32_nt<V>(a.dq + (qrow + g0 + g) * FROW, r, dq);
+            }
+        }
+        // lane t < s: coefficients of slot t (live slots only; the target
+        // pass reads live edges only) and its dw
+        bool my_live = live[0];
+        A my_dw = dws[0];
+#pragma unroll
+        for (int t = 1; t < S; ++t) {
+            my_live = r == t ? live[t] : my_live;
+            my_dw = r == t ? dws[t] : my_dw;
+        }
+        const size_t my_e = (size_t)cur.pos.unit * a.s + r;
+        if (r < a.s) {
+            if (my_live) {
+                float2* cp = a.ws.coef + my_e * G;
+#pragma unroll
+                for (int g = 0; g < G; ++g) cp[g] = make_float2((float)my_dl[g], (float)my_p[g]);
+            }
+            a.dw[my_e] = (float)my_dw;
+        }
+        cur = nxt;
     }
 }
 
@@ -644,19 +803,19 @@ hipError_t dispatch_g(const SeaBwdArgs& a, int G, long long E, hipStream_t st) {
     }
 }
 
-template <typename T, int G, int P, int PD>
+template <typename T, int G, int S, bool VEC, int PD>
 hipError_t run_fast(const SeaBwdArgs& g, const SeaBwdFast& a, long long E, hipStream_t st) {
-    const int nsrc = persistent_grid(reinterpret_cast<const void*>(
-                                         &sea_bwd_src_fast_kernel<T, G, P>),
-                                     a.U, kBlock / (16 * P));
     if (a.global_index) {
         const hipError_t e = launch_zero_f32(reinterpret_cast<float*>(a.ws.cnt), (size_t)a.U, st);
         if (e != hipSuccess) return e;
-    }
-    hipLaunchKernelGGL((sea_bwd_src_fast_kernel<T, G, P>), dim3(nsrc), dim3(kBlock), 0, st, a);
-    if (a.global_index) {
+        const void* fn = reinterpret_cast<const void*>(&sea_bwd_src_row_kernel<T, G, S, VEC, true>);
+        hipLaunchKernelGGL((sea_bwd_src_row_kernel<T, G, S, VEC, true>),
+                           dim3(persistent_grid(fn, a.U, kBlock / 16)), dim3(kBlock), 0, st, a);
         launch_index(g, E, st);
     } else {
+        const void* fn = reinterpret_cast<const void*>(&sea_bwd_src_row_kernel<T, G, S, VEC, false>);
+        hipLaunchKernelGGL((sea_bwd_src_row_kernel<T, G, S, VEC, false>),
+                           dim3(persistent_grid(fn, a.U, kBlock / 16)), dim3(kBlock), 0, st, a);
         const hipError_t e = launch_edge_index(a.U / (a.n * a.hkv), a.n, a.hkv, a.idx, a.w, a.s,
                                                a.ws.beg, a.ws.len, a.ws.list, st);
         if (e != hipSuccess) return e;
@@ -670,9 +829,10 @@ hipError_t run_fast(const SeaBwdArgs& g, const SeaBwdFast& a, long long E, hipSt
 
 template <typename T, int G>
 hipError_t fast_p(const SeaBwdArgs& g, const SeaBwdFast& a, long long E, hipStream_t st) {
-    if (a.s <= 1) return run_fast<T, G, 1, 2>(g, a, E, st);
-    if (a.s <= 2) return run_fast<T, G, 2, 2>(g, a, E, st);
-    return run_fast<T, G, 4, 4>(g, a, E, st);
+    if (a.s <= 1) return run_fast<T, G, 1, false, 2>(g, a, E, st);
+    if (a.s <= 2) return run_fast<T, G, 2, false, 2>(g, a, E, st);
+    if (a.vec) return run_fast<T, G, 4, true, 4>(g, a, E, st);
+    return run_fast<T, G, 4, false, 4>(g, a, E, st);
 }
 
 template <typename T>
@@ -734,6 +894,7 @@ hipError_t launch_sea_backward(int B, int n, int hq, int hkv, int d, bool bf16, 
         f.fd_s = make_fastdiv((uint32_t)s);
         make_seg_plan(f.sp, B, n, hkv);
         f.global_index = !edge_index_supported(n, s);
+        f.vec = s == 4 && (((uintptr_t)idx | (uintptr_t)w) & 15) == 0;
         return bf16 ? dispatch_fast<bf16_t>(a, f, G, E, st) : dispatch_fast<float>(a, f, G, E, st);
     }
     hipError_t e = launch_zero_f32(reinterpret_cast<float*>(a.ws.cnt), (size_t)a.U, st);
