@@ -329,6 +329,102 @@ __global__ __launch_bounds__(kBlock) void ser_fwd_unit_kernel(SerUnitArgs a) {
     }
 }
 
+// ---------------------------------------- s1 = s2 = s3 = 4, aligned rows
+// Straight-line version of the lane-per-unit forward.  Merge: every path
+// weight is added, in path order, to each earlier candidate (the weight when
+// the targets match, else 0.0, which leaves these non-negative sums
+// unchanged), so the first candidate of each target receives its paths'
+// weights in the order and precision of the definition; later duplicates
+// are not candidates.  Ranking: a selection network over 64-bit keys
+// (weight bits << 32 | ~target; 0 = no candidate) orders larger weights
+// first and, among equal weights, lower targets first; positive fp32
+// weights compare like their bit patterns.
+__device__ __forceinline__ void load_paths_vec(const SerUnitArgs& a, int u, int (&m)[kCand],
+                                               float (&x)[kSmax], float (&y)[kCand]) {
+    const int i = token_of(u, a);
+    const int4 ji = *reinterpret_cast<const int4*>(a.idx1 + (size_t)u * 4);
+    const float4 xi = *reinterpret_cast<const float4*>(a.w1 + (size_t)u * 4);
+    const int j[4] = {ji.x, ji.y, ji.z, ji.w};
+    x[0] = xi.x; x[1] = xi.y; x[2] = xi.z; x[3] = xi.w;
+#pragma unroll
+    for (int aa = 0; aa < kSmax; ++aa) {
+        const int r2 = u + (j[aa] - i) * a.hkv;
+        const int4 mi = *reinterpret_cast<const int4*>(a.idx2 + (size_t)r2 * 4);
+        const float4 yi = *reinterpret_cast<const float4*>(a.w2 + (size_t)r2 * 4);
+        m[aa * 4 + 0] = mi.x; m[aa * 4 + 1] = mi.y; m[aa * 4 + 2] = mi.z; m[aa * 4 + 3] = mi.w;
+        y[aa * 4 + 0] = yi.x; y[aa * 4 + 1] = yi.y; y[aa * 4 + 2] = yi.z; y[aa * 4 + 3] = yi.w;
+    }
+}
+
+// compare-exchange: k[i] >= k[j] afterwards
+__device__ __forceinline__ void cx(uint64_t& hi, uint64_t& lo) {
+    const bool sw = lo > hi;
+    const uint64_t t = sw ? lo : hi;
+    lo = sw ? hi : lo;
+    hi = t;
+}
+__device__ __forceinline__ void sort4_desc(uint64_t* k) {
+    cx(k[0], k[1]); cx(k[2], k[3]);
+    cx(k[0], k[2]); cx(k[1], k[3]);
+    cx(k[1], k[2]);
+}
+// top 4 of two descending runs of 4, descending, into a
+__device__ __forceinline__ void merge_top4(uint64_t* a, const uint64_t* b) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) a[i] = a[i] > b[3 - i] ? a[i] : b[3 - i];   // bitonic
+    cx(a[0], a[2]); cx(a[1], a[3]);
+    cx(a[0], a[1]); cx(a[2], a[3]);
+}
+
+__global__ __launch_bounds__(kBlock) void ser_fwd_vec_kernel(SerUnitArgs a) {
+    const int u = xcd_unit(a.U);
+    if (u < 0) return;
+    int m[kCand];
+    float x[kSmax], y[kCand];
+    load_paths_vec(a, u, m, x, y);
+    // a candidate that repeats an earlier target gets bit 31 of its target
+    // set (targets are >= 0): it then matches no later candidate, whose
+    // weight goes to the earlier, first candidate of the target instead
+    double cw[kCand], acc[kCand];
+#pragma unroll
+    for (int k = 0; k < kCand; ++k) {
+        cw[k] = (double)x[k / kSmax] * (double)y[k];
+        acc[k] = cw[k];
+    }
+#pragma unroll
+    for (int k = 1; k < kCand; ++k) {
+        uint32_t dup = 0;
+#pragma unroll
+        for (int k2 = 0; k2 < k; ++k2) {
+            const bool same = m[k2] == m[k];
+            acc[k2] += same ? cw[k] : 0.0;
+            dup |= same ? 0x80000000u : 0u;
+        }
+        m[k] = (int)((uint32_t)m[k] | dup);
+    }
+    uint64_t key[kCand];
+#pragma unroll
+    for (int k = 0; k < kCand; ++k) {
+        const float wk = (float)acc[k];
+        key[k] = m[k] >= 0 && wk > 0.0f
+                     ? ((uint64_t)__float_as_uint(wk) << 32) | (uint32_t)~(uint32_t)m[k]
+                     : 0ull;
+    }
+    sort4_desc(key + 0); sort4_desc(key + 4); sort4_desc(key + 8); sort4_desc(key + 12);
+    merge_top4(key + 0, key + 4);
+    merge_top4(key + 8, key + 12);
+    merge_top4(key + 0, key + 8);
+    int om[4];
+    float ow[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        om[r] = key[r] ? (int)~(uint32_t)key[r] : 0;
+        ow[r] = key[r] ? __uint_as_float((uint32_t)(key[r] >> 32)) : 0.0f;
+    }
+    *reinterpret_cast<int4*>(a.idx_out + (size_t)u * 4) = make_int4(om[0], om[1], om[2], om[3]);
+    *reinterpret_cast<float4*>(a.w_out + (size_t)u * 4) = make_float4(ow[0], ow[1], ow[2], ow[3]);
+}
+
 __global__ __launch_bounds__(kBlock) void ser_bwd_unit_kernel(SerUnitArgs a) {
     const int u = blockIdx.x * kBlock + threadIdx.x;
     if (u >= a.U) return;
@@ -661,7 +757,12 @@ hipError_t launch_ser_forward(int B, int n, int hkv, const int32_t* idx1, const 
                       s2 == 4 && s3 == 4 &&
                           (((uintptr_t)idx1 | (uintptr_t)w1 | (uintptr_t)idx2 | (uintptr_t)w2) &
                            15) == 0};
-        hipLaunchKernelGGL(ser_fwd_unit_kernel, dim3(xcd_unit_grid(u.U)), dim3(kBlock), 0, st, u);
+        if (s1 == 4 && u.vec_out && u.vec_in)
+            hipLaunchKernelGGL(ser_fwd_vec_kernel, dim3(xcd_unit_grid(u.U)), dim3(kBlock), 0, st,
+                               u);
+        else
+            hipLaunchKernelGGL(ser_fwd_unit_kernel, dim3(xcd_unit_grid(u.U)), dim3(kBlock), 0, st,
+                               u);
         return hipGetLastError();
     }
     SerArgs a{idx1, w1, idx2, w2, idx_out, w_out, n, hkv, s1, s2, s3, B * n * hkv};
