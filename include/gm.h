@@ -36,7 +36,9 @@
  *     hq / hkv in {1, 2, 4, 8, 16}; activation pointers 16-byte aligned,
  *     edge pointers 4-byte aligned.
  *   - Determinism: gm_ser_forward and gm_sea_forward are bitwise
- *     deterministic.  gm_ser_backward accumulates in fp64 and rounds once.
+ *     deterministic.  gm_ser_backward accumulates in fp64, in an order that
+ *     may vary, and rounds once, so a result differs between runs only when
+ *     the fp64 sums straddle an fp32 rounding boundary.
  *     gm_sea_backward sums each dk/dv row over its incoming edges in an
  *     order that may vary, so their last bits may vary between runs.
  */
@@ -150,7 +152,8 @@ size_t gm_ser_backward_workspace_bytes(int B, int n, int hkv, int s2, int s3,
  *   out  dw1 [B][n][hkv][s2], dw2 [B][n][hkv][s3] fp32.  dw1 == dw2 is
  *        allowed (A' = Sparsify(A A), s2 == s3): the sum of both is written.
  *   ws   device workspace of gm_ser_backward_workspace_bytes(...) bytes,
- *        8-byte aligned.
+ *        8-byte aligned (16-byte alignment enables the partial-sum path of
+ *        s1 = s2 = s3 = 4, n <= 4096).
  * For each path (a, c) with w1 > 0 and w2 > 0 whose target equals a
  * retained slot t (w_out_t > 0): dw1[i,a] += dw_out_t w2[j,c] and
  * dw2[j,c] += dw_out_t w1[i,a].  Slots with zero weight get 0.

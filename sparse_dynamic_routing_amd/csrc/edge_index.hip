@@ -161,7 +161,7 @@ hipError_t launch_edge_index(int B, int n, int hkv, const int32_t* idx, const fl
     // the LDS needs more, every range at most kRangeMax targets
     const int k_lds = pow2_at_least((n + kRangeMax - 1) / kRangeMax);
     int k_par = pow2_at_least((256 + a.npairs - 1) / a.npairs);
-    if (k_par > 8) k_par = 8;
+    if (k_par > 2) k_par = 2;
     a.K = k_lds > k_par ? k_lds : k_par;
     while (a.K > 1 && a.K > n) a.K >>= 1;
     a.vec = s == 4 && (((uintptr_t)idx | (uintptr_t)w) & 15) == 0;

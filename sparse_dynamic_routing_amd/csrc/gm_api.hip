@@ -165,7 +165,12 @@ size_t gm_ser_backward_workspace_bytes(int B, int n, int hkv, int s2, int s3, in
     const size_t rows = (size_t)B * n * hkv;
     const size_t acc = rows * s2 * sizeof(double) + rows * s3 * sizeof(double);
     const size_t pull = gm::ser_backward_pull_bytes((long long)rows, s2);
-    return acc > pull ? acc : pull;
+    size_t need = acc > pull ? acc : pull;
+    if (s2 == 4 && s3 == 4) {
+        const size_t part = gm::ser_backward_part_bytes(B, n, hkv);
+        if (part > need) need = part;
+    }
+    return need;
 }
 
 gm_status gm_ser_backward(int B, int n, int hkv, const int32_t* idx1, const float* w1, int s2,

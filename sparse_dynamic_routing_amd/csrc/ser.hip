@@ -606,6 +606,128 @@ __global__ __launch_bounds__(kBlock) void ser_bwd_pull_kernel(SerPullArgs a) {
     }
 }
 
+// ------------------------- SER backward by source chunks, s1 = s2 = s3 = 4
+// No reverse index.  Pass 1: one 1024-thread workgroup per (pair, chunk c of
+// 1024 source tokens), one source per thread.  The thread recomputes the
+// gradient of each of its 16 paths from its own rows and adds
+// x * (path gradient) into an fp64 LDS accumulator of the path's leg-1
+// target row (j <= i, so rows [0, end of the chunk)), with LDS atomics;
+// when dw1 and dw2 alias, its own-row part dw1 goes into the same
+// accumulator, else it is rounded and written at once.  The workgroup then
+// writes its accumulator rows as an fp64 partial.  Pass 2: one thread per
+// row sums the partials of the chunks at or above the row's own chunk, in
+// chunk order, and rounds once.  The chunks of a pair run on one XCD, so
+// the leg-2 rows they gather stay in its L2.
+constexpr int kSerThreads = 1024;   // sources per chunk
+constexpr int kSerPartRows = 4096;  // rows of one pair in LDS (128 KiB of fp64 x 4)
+
+struct SerPartArgs {
+    SerUnitArgs u;
+    const int32_t* idx_out;
+    const float* w_out;
+    const float* dw_out;
+    float* dw1;
+    float* dw2;
+    double* part;
+    int nch, npairs, aliased;
+};
+
+// offset (in rows) of chunk c's partial inside its pair's block, and the
+// pair's block size: chunk c covers rows [0, min(n, 1024 (c + 1)))
+__host__ __device__ inline long long part_row_off(int n, int c) {
+    long long off = 0;
+    for (int k = 0; k < c; ++k) off += (k + 1) * kSerThreads < n ? (k + 1) * kSerThreads : n;
+    return off;
+}
+
+__global__ __launch_bounds__(kSerThreads) void ser_bwd_part_kernel(SerPartArgs a) {
+    __shared__ double acc[kSerPartRows * 4];
+    const int total = a.npairs * a.nch;
+    int lin = (int)blockIdx.x;
+    if (total % kXcds == 0)
+        lin = ((int)blockIdx.x % kXcds) * (total / kXcds) + (int)blockIdx.x / kXcds;
+    const int pair = lin / a.nch, c = lin - (lin / a.nch) * a.nch;
+    const int n = a.u.n, hkv = a.u.hkv;
+    const int b = pair / hkv, h = pair - (pair / hkv) * hkv;
+    const int i0 = c * kSerThreads;
+    const int thi = i0 + kSerThreads < n ? i0 + kSerThreads : n;
+    for (int e = threadIdx.x; e < thi * 4; e += kSerThreads) acc[e] = 0.0;
+    __syncthreads();
+
+    const int i = i0 + (int)threadIdx.x;
+    if (i < thi) {
+        const int u = (b * n + i) * hkv + h;
+        int m[kCand];
+        float x[kSmax], y[kCand];
+        load_paths_vec(a.u, u, m, x, y);
+        const int4 j4 = *reinterpret_cast<const int4*>(a.u.idx1 + (size_t)u * 4);
+        const int j[4] = {j4.x, j4.y, j4.z, j4.w};
+        const int4 m4 = *reinterpret_cast<const int4*>(a.idx_out + (size_t)u * 4);
+        const float4 w4 = *reinterpret_cast<const float4*>(a.w_out + (size_t)u * 4);
+        const float4 g4 = *reinterpret_cast<const float4*>(a.dw_out + (size_t)u * 4);
+        const int mt[kSmax] = {m4.x, m4.y, m4.z, m4.w};
+        const float wt[kSmax] = {w4.x, w4.y, w4.z, w4.w};
+        const float gt[kSmax] = {g4.x, g4.y, g4.z, g4.w};
+        double pg[kCand];
+#pragma unroll
+        for (int k = 0; k < kCand; ++k)
+            pg[k] = x[k / kSmax] > 0.0f && y[k] > 0.0f ? path_grad(m[k], mt, wt, gt) : 0.0;
+        // own row: dw1[i, a] = sum_c g(a, c) w2[j_a, c]
+        double d1[kSmax];
+#pragma unroll
+        for (int aa = 0; aa < kSmax; ++aa) {
+            d1[aa] = 0.0;
+#pragma unroll
+            for (int cc = 0; cc < kSmax; ++cc)
+                d1[aa] += pg[aa * kSmax + cc] * (double)y[aa * kSmax + cc];
+        }
+        if (a.aliased) {
+#pragma unroll
+            for (int aa = 0; aa < kSmax; ++aa)
+                if (d1[aa] != 0.0) atomicAdd(acc + i * 4 + aa, d1[aa]);
+        } else {
+            *reinterpret_cast<float4*>(a.dw1 + (size_t)u * 4) =
+                make_float4((float)d1[0], (float)d1[1], (float)d1[2], (float)d1[3]);
+        }
+        // leg-2 slots of the target rows: dw2[j_a, c] += g(a, c) w1[i, a]
+#pragma unroll
+        for (int aa = 0; aa < kSmax; ++aa) {
+#pragma unroll
+            for (int cc = 0; cc < kSmax; ++cc) {
+                const double g = pg[aa * kSmax + cc];
+                if (g != 0.0) atomicAdd(acc + j[aa] * 4 + cc, g * (double)x[aa]);
+            }
+        }
+    }
+    __syncthreads();
+    double* dst = a.part + (part_row_off(n, a.nch) * pair + part_row_off(n, c)) * 4;
+    for (int e = threadIdx.x; e < thi * 2; e += kSerThreads)
+        reinterpret_cast<double2*>(dst)[e] = reinterpret_cast<const double2*>(acc)[e];
+}
+
+// one thread per row u = (b n + r) hkv + h: sum of the partials of chunks
+// floor(r / 1024) .. nch - 1, in that order
+__global__ __launch_bounds__(kBlock) void ser_bwd_part_sum_kernel(SerPartArgs a) {
+    const long long U = (long long)a.npairs * a.u.n;
+    const long long u = (long long)blockIdx.x * kBlock + threadIdx.x;
+    if (u >= U) return;
+    const int n = a.u.n, hkv = a.u.hkv;
+    const int bi = (int)(u / hkv), h = (int)(u - (long long)bi * hkv);
+    const int b = bi / n, r = bi - b * n;
+    const int pair = b * hkv + h;
+    const long long base = part_row_off(n, a.nch) * pair;
+    double d[4] = {0.0, 0.0, 0.0, 0.0};
+    for (int c = r / kSerThreads; c < a.nch; ++c) {
+        const double* p = a.part + (base + part_row_off(n, c) + r) * 4;
+        const double2 lo = *reinterpret_cast<const double2*>(p);
+        const double2 hi = *reinterpret_cast<const double2*>(p + 2);
+        d[0] += lo.x; d[1] += lo.y; d[2] += hi.x; d[3] += hi.y;
+    }
+    float* out = a.aliased ? a.dw1 : a.dw2;
+    *reinterpret_cast<float4*>(out + u * 4) =
+        make_float4((float)d[0], (float)d[1], (float)d[2], (float)d[3]);
+}
+
 // dw1 = ws1, dw2 = ws2 rounded to fp32; when they alias, dw = ws1 + ws2.
 __global__ __launch_bounds__(kBlock) void ser_bwd_finish_kernel(const double* ws1,
                                                                 const double* ws2, float* dw1,
@@ -705,6 +827,14 @@ void make_seg_plan(SegPlan& sp, int B, int n, int hkv) {
     sp.fd_hkv = make_fastdiv((uint32_t)(hkv > 0 ? hkv : 1));
 }
 
+bool ser_backward_part_fits(int n) { return n >= 1 && n <= kSerPartRows; }
+
+size_t ser_backward_part_bytes(int B, int n, int hkv) {
+    if (!ser_backward_part_fits(n)) return 0;
+    const int nch = (n + kSerThreads - 1) / kSerThreads;
+    return (size_t)B * hkv * (size_t)part_row_off(n, nch) * 4 * sizeof(double);
+}
+
 size_t ser_backward_pull_bytes(long long rows, int s2) {
     return (size_t)rows * (2 + s2) * sizeof(int);
 }
@@ -785,6 +915,27 @@ hipError_t launch_ser_backward(int B, int n, int hkv, const int32_t* idx1, const
                                double* ws2, hipStream_t st) {
     const size_t rows = (size_t)B * n * hkv;
     const bool aliased = dw1 == dw2;
+    const bool vec4 = s1 == 4 && s2 == 4 && s3 == 4 &&
+                      (((uintptr_t)idx1 | (uintptr_t)w1 | (uintptr_t)idx2 | (uintptr_t)w2 |
+                        (uintptr_t)idx_out | (uintptr_t)w_out | (uintptr_t)dw_out |
+                        (uintptr_t)dw1 | (uintptr_t)dw2) & 15) == 0;
+    if (vec4 && ser_backward_part_fits(n) && ((uintptr_t)ws1 & 15) == 0) {
+        SerPartArgs pa;
+        pa.u = SerUnitArgs{idx1, w1, idx2, w2, nullptr, nullptr, nullptr, nullptr, nullptr,
+                           n, hkv, s1, s2, s3, (int)rows,
+                           make_fastdiv((uint32_t)hkv), make_fastdiv((uint32_t)n), 1, 1};
+        pa.idx_out = idx_out; pa.w_out = w_out; pa.dw_out = dw_out;
+        pa.dw1 = dw1; pa.dw2 = dw2;
+        pa.part = ws1;
+        pa.nch = (n + kSerThreads - 1) / kSerThreads;
+        pa.npairs = B * hkv;
+        pa.aliased = aliased;
+        hipLaunchKernelGGL(ser_bwd_part_kernel, dim3((unsigned)(pa.npairs * pa.nch)),
+                           dim3(kSerThreads), 0, st, pa);
+        hipLaunchKernelGGL(ser_bwd_part_sum_kernel, dim3((unsigned)((rows + kBlock - 1) / kBlock)),
+                           dim3(kBlock), 0, st, pa);
+        return hipGetLastError();
+    }
     if (s1 <= kSmax && s2 <= kSmax && s3 <= kSmax && edge_index_supported(n, s2)) {
         // reverse index of leg 1 in the workspace, then one pass, no atomics
         int* beg = reinterpret_cast<int*>(ws1);

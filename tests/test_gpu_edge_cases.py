@@ -130,6 +130,32 @@ def test_ser_forward_backward_shapes(s1, s2, s3, n, ties):
         assert_close("dw (aliased legs)", host(da), ra, 1e-5)
 
 
+@pytest.mark.parametrize("n", [1024, 1025, 2500, 4096, 4097])
+def test_ser_backward_source_chunks(n):
+    """s1 = s2 = s3 = 4 backward across the 1024-source chunk boundaries of
+    the partial-sum path (n <= 4096), and just past its limit (n = 4097,
+    reverse-index path); separate and aliased legs."""
+    say(f"case ser backward chunks n={n}")
+    rng = np.random.default_rng(4000 + n)
+    B, hkv = 1, 2
+    idx1, w1 = cases.edges(rng, B, n, hkv, 4, pad_frac=0.05, dead_frac=0.05)
+    idx2, w2 = cases.edges(rng, B, n, hkv, 4, pad_frac=0.05, dead_frac=0.05)
+    orc = oracle.get()
+    for legs in ("separate", "aliased"):
+        if legs == "aliased":
+            idx2, w2 = idx1, w1
+        io, wo = gm.ser_forward(dev(idx1), dev(w1), dev(idx2), dev(w2), 4)
+        rio, rwo = orc.ser_forward(idx1, w1, idx2, w2, 4)
+        assert_ser_match(host(io), host(wo), rio, rwo)
+        dwo = rng.standard_normal(rio.shape).astype(np.float32)
+        d1, d2 = gm.ser_backward(dev(idx1), dev(w1), dev(idx2), dev(w2), io, wo, dev(dwo),
+                                 aliased=legs == "aliased")
+        r1, r2 = orc.ser_backward(idx1, w1, idx2, w2, rio, rwo, dwo, aliased=legs == "aliased")
+        assert_close(f"dw1 ({legs})", host(d1), r1, 1e-5)
+        if legs == "separate":
+            assert_close("dw2", host(d2), r2, 1e-5)
+
+
 def test_single_token_and_empty_inputs():
     """n = 1 (every edge is the padding token itself) and zero-size calls,
     which launch nothing and return success."""
