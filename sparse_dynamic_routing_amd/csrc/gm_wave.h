@@ -1,10 +1,11 @@
-// Wave64 building blocks for the gfx950 fast paths, where one d-row of K/V/q
+// Wave64 building blocks for the gfx950 fast paths.  One d-row of K/V/q
 // (256 bytes: bf16 d=128 or fp32 d=64) is spread over one 16-lane row of the
-// wavefront (16 bytes per lane) and the P <= 4 edge slots of a unit sit in
-// consecutive rows.  Reductions inside a row use DPP (the permute is fused
-// into the add); reductions and exchanges across rows use gfx950's
-// v_permlane16_swap / v_permlane32_swap, so no LDS traffic, no lane-address
-// arithmetic and no selects are needed.
+// wavefront (16 bytes per lane).  The forward and the source pass hold one
+// unit per row and its edge slots in registers; the target pass puts the
+// P <= 4 incoming edges of a unit in consecutive rows.  Sums inside a row
+// use DPP (the permute is fused into the add); reductions across rows use
+// gfx950's v_permlane16_swap / v_permlane32_swap, so no LDS traffic and no
+// lane-address arithmetic are needed.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -74,24 +75,6 @@ __device__ __forceinline__ void swap32(double& a, double& b) {
     b = __builtin_bit_cast(double, ((uint64_t)(uint32_t)hi[1] << 32) | (uint32_t)lo[1]);
 }
 
-// Sum / max over the P rows (P in {1, 2, 4}) of a team; every lane gets it.
-template <int P, typename A>
-__device__ __forceinline__ A rows_sum(A x) {
-    if constexpr (P >= 2) { A a = x, b = x; swap16(a, b); x = a + b; }
-    if constexpr (P >= 4) { A a = x, b = x; swap32(a, b); x = a + b; }
-    return x;
-}
-// (compare-select: values coming out of a lane swap would otherwise be
-// canonicalised before a v_max; -inf is the only non-finite value here)
-template <typename A>
-__device__ __forceinline__ A sel_max(A a, A b) { return a > b ? a : b; }
-template <int P, typename A>
-__device__ __forceinline__ A rows_max(A x) {
-    if constexpr (P >= 2) { A a = x, b = x; swap16(a, b); x = sel_max(a, b); }
-    if constexpr (P >= 4) { A a = x, b = x; swap32(a, b); x = sel_max(a, b); }
-    return x;
-}
-
 // Reduce-scatter a V-vector over the P rows of a team.  Afterwards x[0 .. V/P)
 // holds the sums of elements [off, off + V/P) of the vector, with
 // off = rs_offset<V, P>(row); V >= P.
@@ -120,17 +103,6 @@ __device__ __forceinline__ int rs_offset(int row) {
     if constexpr (P >= 2) off += (row & 1) * (V / 2);
     if constexpr (P >= 4) off += ((row >> 1) & 1) * (V / 4);
     return off;
-}
-
-// Value of lane `src` (a constant) in every lane (v_readlane to a scalar).
-__device__ __forceinline__ float bcast_lane(float x, int src) {
-    return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), src));
-}
-__device__ __forceinline__ double bcast_lane(double x, int src) {
-    const uint64_t u = __builtin_bit_cast(uint64_t, x);
-    const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)u, src);
-    const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(u >> 32), src);
-    return __builtin_bit_cast(double, ((uint64_t)hi << 32) | lo);
 }
 
 // Division of 0 <= x < 2^31 by an invariant divisor 1 <= d < 2^31 with a
@@ -302,13 +274,6 @@ __device__ __forceinline__ void store_split_f32_nt(char* frow, int r, const A (&
     if constexpr (V == 8) store_f32_nt<4>(frow + 256 + r * 16, x + 4);
 }
 
-__device__ __forceinline__ void store_u32_nt(char* p, uint32_t a) {
-    __builtin_nontemporal_store(a, reinterpret_cast<uint32_t*>(p));
-}
-__device__ __forceinline__ void store_u32x2_nt(char* p, uint32_t a, uint32_t b) {
-    const u32x2_t v = {a, b};
-    __builtin_nontemporal_store(v, reinterpret_cast<u32x2_t*>(p));
-}
 __device__ __forceinline__ void store_u32x4_nt(char* p, uint32_t a, uint32_t b, uint32_t c,
                                                uint32_t d) {
     const u32x4_t v = {a, b, c, d};

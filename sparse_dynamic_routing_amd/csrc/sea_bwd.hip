@@ -426,102 +426,6 @@ __device__ __forceinline__ void store_f32(char* p, const A* x) {
     store_n<L>(reinterpret_cast<float*>(p), x);
 }
 
-template <typename T, int G, int P>
-__global__ __launch_bounds__(kBlock) void sea_bwd_src_fast_kernel(SeaBwdFast a) {
-    using A = typename io<T>::acc;
-    constexpr int V = io<T>::V;
-    constexpr int ROW = 256;            // bytes of one bf16/fp32 input d-row
-    constexpr int FROW = ROW * 4 / (int)sizeof(T);   // bytes of the fp32 gradient row
-    constexpr int L = V / P;
-    const int lane = threadIdx.x & (kWave - 1);
-    const int r = lane & 15;
-    const int row = lane >> 4;
-    const int slot = row & (P - 1);
-    const A c = (A)a.scale * (A)1.4426950408889634;
-    const A sc = (A)a.scale;
-    const A NEG = -INFINITY;
-    const Sched sch = xcd_sched(a.sp, 16 * P);
-
-    auto fetch = [&](int u, Pos& pos, int& j, float& wt) {
-        j = 0;
-        wt = 0.0f;
-        if (u < sch.end) {
-            pos = pos_of(a.sp, sch.x, u);
-            if (slot < a.s) {
-                const int e = pos.unit * a.s + slot;
-                j = a.idx[e];
-                wt = a.w[e];
-            }
-        }
-    };
-    Pos pos{0, 0, 0, 0};
-    int j;
-    float wt;
-    fetch(sch.q, pos, j, wt);
-    for (int u = sch.q; u < sch.end; u += sch.step) {
-        Pos npos = pos;
-        int nj;
-        float nwt;
-        fetch(u + sch.step, npos, nj, nwt);
-
-        const bool live = wt > 0.0f;
-        const int kvrow = pos.kvrow0 + (live ? j : 0) * a.hkv;
-        const uint32_t kvoff = (uint32_t)kvrow * ROW + r * 16;
-        const uint4 kr = *reinterpret_cast<const uint4*>(a.k + kvoff);
-        const uint4 vr = *reinterpret_cast<const uint4*>(a.v + kvoff);
-        const int h = pos.unit - pos.bi * a.hkv;
-        const uint32_t qrow = (uint32_t)(pos.bi * a.hq + h * G);
-        uint4 qr[G], dr[G];
-#pragma unroll
-        for (int g = 0; g < G; ++g) {
-            qr[g] = *reinterpret_cast<const uint4*>(a.q + (qrow + g) * ROW + r * 16);
-            dr[g] = *reinterpret_cast<const uint4*>(a.dout + (qrow + g) * ROW + r * 16);
-        }
-        if (a.global_index && live && r == 0) atomicAdd(a.ws.cnt + kvrow, 1);
-        const A lw = live ? (A)log2f(wt) : NEG;
-        A kf[V];
-        unpack16<A, V>(kr, kf);
-        A dws = 0;
-        float2* cp = a.ws.coef + ((size_t)pos.unit * a.s + slot) * G;
-#pragma unroll
-        for (int g = 0; g < G; ++g) {
-            const A sd = row_sum16(dot16<V, A>(qr[g], kr));
-            const A gd = row_sum16(dot16<V, A>(dr[g], vr));
-            const A ls = sd * c;
-            const A l = live ? ls + lw : NEG;
-            const A M = rows_max<P>(l);
-            A ex, invZ, pw;
-            if constexpr (V == 8) {
-                ex = live ? __builtin_amdgcn_exp2f(l - M) : 0.0f;
-                const A Z = rows_sum<P>(ex);
-                invZ = Z > 0.0f ? __builtin_amdgcn_rcpf(Z) : 0.0f;
-                pw = live ? __builtin_amdgcn_exp2f(ls - M) : 0.0f;
-            } else {
-                ex = live ? exp2(l - M) : 0.0;
-                const A Z = rows_sum<P>(ex);
-                invZ = Z > 0.0 ? 1.0 / Z : 0.0;
-                pw = live ? exp2(ls - M) : 0.0;
-            }
-            const A p = ex * invZ;
-            const A gbar = rows_sum<P>(p * gd);
-            const A dls = p * (gd - gbar) * sc;
-            A dqv[V];
-#pragma unroll
-            for (int e = 0; e < V; ++e) dqv[e] = dls * kf[e];
-            rows_reduce_scatter<P, V>(dqv);
-            store_f32_nt<L>(a.dq + (qrow + g) * FROW + r * 16 * 4 / (int)sizeof(T) +
-                             rs_offset<V, P>(row) * 4,
-                         dqv);
-            if (live && r == 0) cp[g] = make_float2((float)dls, (float)p);
-            dws += pw * invZ * (gd - gbar);
-        }
-        if (r == 0 && slot < a.s) a.dw[(size_t)pos.unit * a.s + slot] = (float)dws;
-        pos = npos;
-        j = nj;
-        wt = nwt;
-    }
-}
-
 // Source pass with one unit per 16-lane row, four units per wavefront: lane
 // r holds bytes [16r, 16r + 16) of the unit's G query and upstream-gradient
 // rows and of the K and V rows of its S edge slots (registers).  Scores and

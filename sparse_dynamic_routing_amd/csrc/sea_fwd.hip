@@ -209,107 +209,6 @@ __device__ __forceinline__ UnitPos unit_pos(const SegPlan& sp, int x, int q) {
     return p;
 }
 
-template <typename T, int G, int P>
-__global__ __launch_bounds__(kBlock) void sea_fwd_fast_kernel(SeaFwdFast a) {
-    using A = typename io<T>::acc;
-    constexpr int V = io<T>::V;          // elements per lane (16 bytes)
-    constexpr int ROW = 256;             // bytes per d-row
-    const int lane = threadIdx.x & (kWave - 1);
-    const int r = lane & 15;
-    const int row = lane >> 4;
-    const int slot = row & (P - 1);
-    const A c = (A)a.scale * (A)1.4426950408889634;
-    const A NEG = -INFINITY;
-    const Sched sc = xcd_sched(a.sp, 16 * P);
-
-    // edge slot of item u for this lane: (token index, weight); dead -> (0, 0)
-    auto fetch = [&](int u, UnitPos& pos, int& j, float& wt) {
-        j = 0;
-        wt = 0.0f;
-        if (u < sc.end) {
-            pos = unit_pos(a.sp, sc.x, u);
-            if (slot < a.s) {
-                const int e = pos.unit * a.s + slot;
-                j = a.idx[e];
-                wt = a.w[e];
-            }
-        }
-    };
-    UnitPos pos{0, 0, 0};
-    int j;
-    float wt;
-    fetch(sc.q, pos, j, wt);
-    for (int u = sc.q; u < sc.end; u += sc.step) {
-        UnitPos npos = pos;
-        int nj;
-        float nwt;
-        fetch(u + sc.step, npos, nj, nwt);
-
-        const bool live = wt > 0.0f;
-        const uint32_t kvoff = (uint32_t)(pos.kvrow0 + (live ? j : 0) * a.hkv) * ROW + r * 16;
-        const uint4 kr = *reinterpret_cast<const uint4*>(a.k + kvoff);
-        const uint4 vr = *reinterpret_cast<const uint4*>(a.v + kvoff);
-        const uint32_t qoff = (uint32_t)(pos.bi * a.hq + (pos.unit - pos.bi * a.hkv) * G) * ROW +
-                              r * 16;
-        uint4 qr[G];
-#pragma unroll
-        for (int g = 0; g < G; ++g) qr[g] = *reinterpret_cast<const uint4*>(a.q + qoff + g * ROW);
-        const A lw = live ? (A)log2f(wt) : NEG;
-        A vf[V];
-        if constexpr (V == 8) {
-            bf16x8_to_f32(vr, vf);
-        } else {
-            vf[0] = __uint_as_float(vr.x); vf[1] = __uint_as_float(vr.y);
-            vf[2] = __uint_as_float(vr.z); vf[3] = __uint_as_float(vr.w);
-        }
-#pragma unroll
-        for (int g = 0; g < G; ++g) {
-            A dot;
-            if constexpr (V == 8) {
-                dot = dot_bf16x8(qr[g], kr);
-            } else {
-                dot = (A)__uint_as_float(qr[g].x) * (A)__uint_as_float(kr.x) +
-                      (A)__uint_as_float(qr[g].y) * (A)__uint_as_float(kr.y) +
-                      (A)__uint_as_float(qr[g].z) * (A)__uint_as_float(kr.z) +
-                      (A)__uint_as_float(qr[g].w) * (A)__uint_as_float(kr.w);
-            }
-            dot = row_sum16(dot);
-            const A l = live ? dot * c + lw : NEG;
-            const A M = rows_max<P>(l);
-            A ex;
-            if constexpr (V == 8) ex = live ? __builtin_amdgcn_exp2f(l - M) : 0.0f;
-            else ex = live ? exp2(l - M) : 0.0;
-            const A Z = rows_sum<P>(ex);
-            A ov[V];
-#pragma unroll
-            for (int e = 0; e < V; ++e) ov[e] = ex * vf[e];
-            rows_reduce_scatter<P, V>(ov);
-            A inv;
-            if constexpr (V == 8) inv = Z > 0.0f ? __builtin_amdgcn_rcpf(Z) : 0.0f;
-            else inv = Z > 0.0 ? 1.0 / Z : 0.0;
-            constexpr int L = V / P;
-#pragma unroll
-            for (int e = 0; e < L; ++e) ov[e] *= inv;
-            char* op = a.o + qoff + g * ROW + rs_offset<V, P>(row) * (int)sizeof(T);
-            if constexpr (V == 8) {
-                if constexpr (L == 2) {
-                    store_u32_nt(op, pack_bf16x2(ov[0], ov[1]));
-                } else if constexpr (L == 4) {
-                    store_u32x2_nt(op, pack_bf16x2(ov[0], ov[1]), pack_bf16x2(ov[2], ov[3]));
-                } else {
-                    store_u32x4_nt(op, pack_bf16x2(ov[0], ov[1]), pack_bf16x2(ov[2], ov[3]),
-                                   pack_bf16x2(ov[4], ov[5]), pack_bf16x2(ov[6], ov[7]));
-                }
-            } else {
-                store_f32_nt<L>(op, ov);
-            }
-        }
-        pos = npos;
-        j = nj;
-        wt = nwt;
-    }
-}
-
 template <typename T, int G>
 hipError_t run(const SeaFwdArgs& a, hipStream_t st) {
     const long long threads = (long long)a.U * a.ts.team;
@@ -439,14 +338,6 @@ __global__ __launch_bounds__(kBlock) void sea_fwd_row_kernel(SeaFwdFast a) {
         }
         cur = nxt;
     }
-}
-
-template <typename T, int G, int P>
-hipError_t run_fast(const SeaFwdFast& a, hipStream_t st) {
-    const void* fn = reinterpret_cast<const void*>(&sea_fwd_fast_kernel<T, G, P>);
-    const int nwg = persistent_grid(fn, a.U, kBlock / (16 * P));
-    hipLaunchKernelGGL((sea_fwd_fast_kernel<T, G, P>), dim3(nwg), dim3(kBlock), 0, st, a);
-    return hipGetLastError();
 }
 
 template <typename T, int G, int S, bool VEC>
