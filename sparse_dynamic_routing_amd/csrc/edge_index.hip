@@ -140,6 +140,112 @@ __global__ __launch_bounds__(kIndexThreads) void edge_index_kernel(IndexArgs a) 
     }
 }
 
+// Single-pass variant for n <= kIndexThreads * kTok: each thread holds its
+// kTok tokens' edges in registers from one load, the range's list is
+// placed in LDS and then copied out with coalesced stores, and beg/len are
+// written row-contiguously.  Every load is unconditional (a clamped valid
+// address, masked afterwards), so the loads of a thread issue back to back.
+constexpr int kOneRows = kIndexThreads * kTok;   // 4096 tokens: targets of a range
+constexpr int kOneList = kOneRows * kSlotMax;    // edges of a pair
+
+template <bool VEC>
+__global__ __launch_bounds__(kIndexThreads) void edge_index_one_kernel(IndexArgs a) {
+    __shared__ int cnt[kOneRows];    // count, then fill cursor (range-relative)
+    __shared__ int rlen[kOneRows];
+    __shared__ int sorted[kOneList];
+    __shared__ int part[kIndexThreads / kWave];
+    __shared__ int range_total;
+    const int total = a.npairs * a.K;
+    int lin = (int)blockIdx.x;
+    if (total % kXcds == 0)
+        lin = ((int)blockIdx.x % kXcds) * (total / kXcds) + (int)blockIdx.x / kXcds;
+    const int pair = lin / a.K, kq = lin - (lin / a.K) * a.K;
+    const int n = a.n, s = a.s, hkv = a.hkv;
+    const int jlo = (int)((long long)kq * n / a.K), jhi = (int)((long long)(kq + 1) * n / a.K);
+    const int nr = jhi - jlo;
+    const int b = pair / hkv, h = pair - (pair / hkv) * hkv;
+    const int lbase = pair * n * s;
+    for (int j = threadIdx.x; j < nr; j += kIndexThreads) cnt[j] = 0;
+    __syncthreads();
+
+    int tj[kTok * kSlotMax], te[kTok * kSlotMax];
+#pragma unroll
+    for (int k = 0; k < kTok; ++k) {
+        const int iv = k * kIndexThreads + (int)threadIdx.x;
+        const bool ok = iv < n;
+        const int i = ok ? iv : n - 1;
+        const int e0 = ((b * n + i) * hkv + h) * s;
+        if constexpr (VEC) {
+            const int4 j4 = *reinterpret_cast<const int4*>(a.idx + e0);
+            const float4 w4 = *reinterpret_cast<const float4*>(a.w + e0);
+            tj[k * 4 + 0] = j4.x; tj[k * 4 + 1] = j4.y;
+            tj[k * 4 + 2] = j4.z; tj[k * 4 + 3] = j4.w;
+            te[k * 4 + 0] = ok && w4.x > 0.0f ? e0 + 0 : -1;
+            te[k * 4 + 1] = ok && w4.y > 0.0f ? e0 + 1 : -1;
+            te[k * 4 + 2] = ok && w4.z > 0.0f ? e0 + 2 : -1;
+            te[k * 4 + 3] = ok && w4.w > 0.0f ? e0 + 3 : -1;
+        } else {
+#pragma unroll
+            for (int t = 0; t < kSlotMax; ++t) {
+                const int sl = k * kSlotMax + t;
+                const int e = e0 + (t < s ? t : s - 1);
+                tj[sl] = a.idx[e];
+                te[sl] = ok && t < s && a.w[e] > 0.0f ? e : -1;
+            }
+        }
+    }
+    int below = 0;
+#pragma unroll
+    for (int k = 0; k < kTok * kSlotMax; ++k) {
+        if (te[k] < 0) continue;
+        if (tj[k] < jlo) ++below;
+        else if (tj[k] < jhi) atomicAdd(&cnt[tj[k] - jlo], 1);
+    }
+    const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
+    for (int m = 32; m > 0; m >>= 1) below += __shfl_xor(below, m, kWave);
+    if (lane == 0) part[wave] = below;
+    __syncthreads();
+    int below_all = 0;
+    for (int k = 0; k < kIndexThreads / kWave; ++k) below_all += part[k];
+    __syncthreads();
+
+    // exclusive scan of the counts: each thread scans a contiguous run
+    const int run_len = (nr + kIndexThreads - 1) / kIndexThreads;
+    const int j0 = threadIdx.x * run_len;
+    int run = 0;
+    for (int j = j0; j < j0 + run_len && j < nr; ++j) run += cnt[j];
+    int inc = run;
+    for (int m = 1; m < kWave; m <<= 1) {
+        const int o = __shfl_up(inc, m, kWave);
+        if (lane >= m) inc += o;
+    }
+    if (lane == kWave - 1) part[wave] = inc;
+    __syncthreads();
+    int base = 0;
+    for (int k = 0; k < wave; ++k) base += part[k];
+    if (threadIdx.x == kIndexThreads - 1) range_total = base + inc;
+    base += inc - run;
+    for (int j = j0; j < j0 + run_len && j < nr; ++j) {
+        const int c = cnt[j];
+        rlen[j] = c;
+        cnt[j] = base;
+        base += c;
+    }
+    __syncthreads();
+    const int gbase = lbase + below_all;   // list slot of the range's first edge
+    for (int j = threadIdx.x; j < nr; j += kIndexThreads) {
+        a.beg[pair * n + jlo + j] = gbase + cnt[j];
+        a.len[pair * n + jlo + j] = rlen[j];
+    }
+    __syncthreads();
+#pragma unroll
+    for (int k = 0; k < kTok * kSlotMax; ++k)
+        if (te[k] >= 0 && tj[k] >= jlo && tj[k] < jhi)
+            sorted[atomicAdd(&cnt[tj[k] - jlo], 1)] = te[k];
+    __syncthreads();
+    for (int p = threadIdx.x; p < range_total; p += kIndexThreads) a.list[gbase + p] = sorted[p];
+}
+
 int pow2_at_least(long long x) {
     int p = 1;
     while (p < x) p <<= 1;
@@ -157,8 +263,8 @@ hipError_t launch_edge_index(int B, int n, int hkv, const int32_t* idx, const fl
     IndexArgs a;
     a.idx = idx; a.w = w; a.n = n; a.hkv = hkv; a.s = s;
     a.npairs = B * hkv;
-    // enough workgroups to fill the device, at most 8 ranges per pair unless
-    // the LDS needs more, every range at most kRangeMax targets
+    // two ranges per pair for parallelism when there are few pairs, more
+    // only when the LDS needs them (every range at most kRangeMax targets)
     const int k_lds = pow2_at_least((n + kRangeMax - 1) / kRangeMax);
     int k_par = pow2_at_least((256 + a.npairs - 1) / a.npairs);
     if (k_par > 2) k_par = 2;
@@ -166,8 +272,15 @@ hipError_t launch_edge_index(int B, int n, int hkv, const int32_t* idx, const fl
     while (a.K > 1 && a.K > n) a.K >>= 1;
     a.vec = s == 4 && (((uintptr_t)idx | (uintptr_t)w) & 15) == 0;
     a.beg = beg; a.len = len; a.list = list;
-    hipLaunchKernelGGL(edge_index_kernel, dim3((unsigned)(a.npairs * a.K)), dim3(kIndexThreads), 0,
-                       st, a);
+    const dim3 grid((unsigned)(a.npairs * a.K));
+    if (n <= kOneRows) {
+        if (a.vec)
+            hipLaunchKernelGGL(edge_index_one_kernel<true>, grid, dim3(kIndexThreads), 0, st, a);
+        else
+            hipLaunchKernelGGL(edge_index_one_kernel<false>, grid, dim3(kIndexThreads), 0, st, a);
+    } else {
+        hipLaunchKernelGGL(edge_index_kernel, grid, dim3(kIndexThreads), 0, st, a);
+    }
     return hipGetLastError();
 }
 
