@@ -48,12 +48,14 @@ BYTES_PER_UNIT = {
     "gm_ser_backward": 32 + 32 + 16 + 16,               # A, A', dw', dw
 }
 CALLS = list(BYTES_PER_UNIT)
-# kernels each call launches (name prefixes as the profiler reports them)
+# kernels each call launches on this workload (base names as the profiler
+# reports them, template arguments dropped)
 CALL_KERNELS = {
-    "gm_ser_forward": ["ser_fwd"],
-    "gm_sea_forward": ["sea_fwd"],
-    "gm_sea_backward": ["sea_bwd_src", "edge_index", "sea_bwd_dst"],
-    "gm_ser_backward": ["edge_index", "ser_bwd"],
+    "gm_ser_forward": ["ser_fwd_vec_kernel"],
+    "gm_sea_forward": ["sea_fwd_row_kernel"],
+    "gm_sea_backward": ["sea_bwd_src_row_kernel", "edge_index_one_kernel",
+                        "sea_bwd_dst_fast_kernel"],
+    "gm_ser_backward": ["ser_bwd_part_kernel", "ser_bwd_part_sum_kernel"],
 }
 PROFILE = os.path.join(ROOT, "profiles", "metric_pass_kernels.md")
 
@@ -77,11 +79,11 @@ def profiled_traffic(call: str):
     if hsh != source_hash():
         return None
     total = 0.0
-    for prefix in CALL_KERNELS[call]:
-        hits = [v for k, v in kernels.items() if k.split("<")[0].startswith(prefix)]
-        if not hits:
+    for name in CALL_KERNELS[call]:
+        hits = [v for k, v in kernels.items() if k.split("<")[0] == name]
+        if len(hits) != 1:
             return None
-        total += sum(hits) / len(hits)
+        total += hits[0]
     return total
 
 
