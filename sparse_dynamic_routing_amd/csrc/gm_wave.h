@@ -244,6 +244,27 @@ __device__ __forceinline__ uint4 load_split(const char* row, int r) {
     }
 }
 
+// Streaming (non-temporal) 16-byte loads of rows read once, so they do not
+// push reused (gathered) rows out of the L2.
+typedef uint32_t u32x2_ld_t __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4_ld_t __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint4 load_nt16(const char* p) {
+    const u32x4_ld_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_ld_t*>(p));
+    return make_uint4(v.x, v.y, v.z, v.w);
+}
+template <int V>
+__device__ __forceinline__ uint4 load_split_nt(const char* row, int r) {
+    if constexpr (V == 8) {
+        const u32x2_ld_t lo =
+            __builtin_nontemporal_load(reinterpret_cast<const u32x2_ld_t*>(row + r * 8));
+        const u32x2_ld_t hi =
+            __builtin_nontemporal_load(reinterpret_cast<const u32x2_ld_t*>(row + 128 + r * 8));
+        return make_uint4(lo.x, lo.y, hi.x, hi.y);
+    } else {
+        return load_nt16(row + r * 16);
+    }
+}
+
 // Streaming (non-temporal) stores of outputs nobody reads soon, so they do
 // not push gathered rows out of the L2.
 typedef float f32x2_t __attribute__((ext_vector_type(2)));

@@ -506,8 +506,8 @@ __global__ __launch_bounds__(kBlock) void sea_bwd_src_row_kernel(SeaBwdFast a) {
             uint4 qr[GC], dr[GC];
 #pragma unroll
             for (int g = 0; g < GC; ++g) {
-                qr[g] = load_split<V>(a.q + (qrow + g0 + g) * ROW, r);
-                dr[g] = load_split<V>(a.dout + (qrow + g0 + g) * ROW, r);
+                qr[g] = load_split_nt<V>(a.q + (qrow + g0 + g) * ROW, r);
+                dr[g] = load_split_nt<V>(a.dout + (qrow + g0 + g) * ROW, r);
             }
 #pragma unroll
             for (int g = 0; g < GC; ++g) {

@@ -299,7 +299,7 @@ __global__ __launch_bounds__(kBlock) void sea_fwd_row_kernel(SeaFwdFast a) {
             uint4 qr[GC];
 #pragma unroll
             for (int g = 0; g < GC; ++g)
-                qr[g] = *reinterpret_cast<const uint4*>(a.q + qoff + (g0 + g) * ROW);
+                qr[g] = load_nt16(a.q + qoff + (g0 + g) * ROW);
 #pragma unroll
             for (int g = 0; g < GC; ++g) {
                 A l[S], M = NEG;
