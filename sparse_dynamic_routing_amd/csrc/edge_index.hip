@@ -258,6 +258,8 @@ bool edge_index_supported(int n, int s) {
     return s <= kSlotMax && (long long)(n + kRangeMax - 1) / kRangeMax <= 64;
 }
 
+bool edge_index_one_pass(int n) { return n <= kOneRows; }
+
 hipError_t launch_edge_index(int B, int n, int hkv, const int32_t* idx, const float* w, int s,
                              int* beg, int* len, int* list, hipStream_t st) {
     IndexArgs a;

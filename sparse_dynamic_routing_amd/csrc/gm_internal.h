@@ -48,6 +48,8 @@ hipError_t launch_ser_backward(int B, int n, int hkv, const int32_t* idx1, const
 // beg/len per pair-major row (pair * n + j), list of edge ids; list needs
 // B*n*hkv*s entries, beg and len B*n*hkv each.
 bool edge_index_supported(int n, int s);
+// n small enough for the single-pass index (one load pass per pair)
+bool edge_index_one_pass(int n);
 hipError_t launch_edge_index(int B, int n, int hkv, const int32_t* idx, const float* w, int s,
                              int* beg, int* len, int* list, hipStream_t st);
 

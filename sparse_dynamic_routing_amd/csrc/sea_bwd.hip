@@ -797,7 +797,10 @@ hipError_t launch_sea_backward(int B, int n, int hq, int hkv, int d, bool bf16, 
         f.fd_hkv = make_fastdiv((uint32_t)hkv);
         f.fd_s = make_fastdiv((uint32_t)s);
         make_seg_plan(f.sp, B, n, hkv);
-        f.global_index = !edge_index_supported(n, s);
+        // beyond 4096 tokens the per-pair LDS index reads every token of a
+        // pair in each of its few workgroups; the global count/scan/fill
+        // index spreads over the whole device instead
+        f.global_index = !edge_index_supported(n, s) || !edge_index_one_pass(n);
         f.vec = s == 4 && (((uintptr_t)idx | (uintptr_t)w) & 15) == 0;
         return bf16 ? dispatch_fast<bf16_t>(a, f, G, E, st) : dispatch_fast<float>(a, f, G, E, st);
     }

@@ -936,7 +936,9 @@ hipError_t launch_ser_backward(int B, int n, int hkv, const int32_t* idx1, const
                            dim3(kBlock), 0, st, pa);
         return hipGetLastError();
     }
-    if (s1 <= kSmax && s2 <= kSmax && s3 <= kSmax && edge_index_supported(n, s2)) {
+    // the reverse index of leg 1 pays off only where it is built in one
+    // pass per pair (n <= 4096); longer sequences take the fp64-atomic path
+    if (s1 <= kSmax && s2 <= kSmax && s3 <= kSmax && edge_index_one_pass(n)) {
         // reverse index of leg 1 in the workspace, then one pass, no atomics
         int* beg = reinterpret_cast<int*>(ws1);
         int* len = beg + rows;

@@ -134,7 +134,7 @@ def test_ser_forward_backward_shapes(s1, s2, s3, n, ties):
 def test_ser_backward_source_chunks(n):
     """s1 = s2 = s3 = 4 backward across the 1024-source chunk boundaries of
     the partial-sum path (n <= 4096), and just past its limit (n = 4097,
-    reverse-index path); separate and aliased legs."""
+    fp64-atomic path); separate and aliased legs."""
     say(f"case ser backward chunks n={n}")
     rng = np.random.default_rng(4000 + n)
     B, hkv = 1, 2
