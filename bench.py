@@ -13,9 +13,13 @@ before timing starts; outputs and workspace are preallocated.
 Prints one JSON line: units (tokens x KV heads) per second, the pass's
 algorithmic HBM bandwidth, per-call times from HIP events on the launch
 stream, the roofline entry of the dominant call, and the CPU oracle's rate
-on a bounded sample of the same workload (rank 0, N=1).
+on a bounded sample of the same workload (rank 0, N=1).  Beside the warm
+headline it reports a cold pass (a 512 MiB scratch write before each pass
+evicts the L2s and the MALL) and the pass's counter bytes (calibrated
+FETCH_SIZE + WRITE_SIZE from the committed profile, when it matches the
+kernel sources) against its compulsory bytes.
 
-    python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu-baseline]
+    python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu-baseline] [--no-cold]
 """
 from __future__ import annotations
 
@@ -93,6 +97,8 @@ def parse():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-cold", action="store_true",
+                    help="skip the cold-cache passes (profiler runs of the warm pass)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="instead of the pass, run a plain device copy of MIB MiB "
@@ -164,6 +170,27 @@ def time_gpu(ps: Pass, steps: int, warmup: int):
     return total_ms / steps, per_call, wall
 
 
+def time_cold(ps: Pass, steps: int, flush_mib: int = 512):
+    """Mean time of one pass when a `flush_mib` MiB scratch buffer is written
+    before it (evicting the 4 MB L2s and the 256 MB MALL); only the pass is
+    timed (HIP events around it on the launch stream)."""
+    calls = ps.calls()
+    scratch = torch.empty(flush_mib * (1 << 20) // 4, dtype=torch.float32, device="cuda")
+    times = []
+    for s in range(steps + 1):
+        scratch.fill_(float(s))
+        st, en = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        st.record()
+        for c in calls:
+            c()
+        en.record()
+        torch.cuda.synchronize()
+        if s:                                    # the first is a warm-up
+            times.append(st.elapsed_time(en))
+    del scratch
+    return float(np.mean(times))
+
+
 def cpu_baseline(ps: Pass, budget_s: float):
     """The oracle, single-threaded, on whole (batch, KV head) pairs of the same
     workload, in pair order, until the time budget is spent (whole pairs)."""
@@ -222,7 +249,11 @@ def main():
     ms, per_call, wall = time_gpu(ps, a.steps, a.warmup)
     U = p.units
     pass_bytes = sum(BYTES_PER_UNIT.values()) * U
+    cold_ms = None if a.no_cold else time_cold(ps, max(5, a.steps // 5))
     dom = max(per_call, key=per_call.get)
+    traffic = {c: profiled_traffic(c) for c in CALLS}
+    counter_bytes = (sum(traffic.values()) if all(v is not None for v in traffic.values())
+                     else None)
     dom_gbs = BYTES_PER_UNIT[dom] * U / (per_call[dom] * 1e-3) / 1e9
     line = {
         "metric": METRIC,
@@ -245,10 +276,19 @@ def main():
         "pass_algorithmic_GBps": pass_bytes / (ms * 1e-3) / 1e9,
         "pass_frac_of_peak": pass_bytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS,
         "per_call_ms": per_call,
+        "cold": None if cold_ms is None else {
+            "ms_per_step": cold_ms, "value": U / (cold_ms * 1e-3),
+            "flush": "512 MiB scratch written before each pass"},
+        "pass_counter": None if counter_bytes is None else {
+            "bytes": counter_bytes,
+            "GBps": counter_bytes / (ms * 1e-3) / 1e9,
+            "frac_of_peak": counter_bytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS,
+            "over_compulsory": counter_bytes / pass_bytes,
+            "source": "profiles/metric_pass_kernels.md (calibrated FETCH_SIZE + WRITE_SIZE)"},
         "roofline": {"kernel": dom, "kernels": CALL_KERNELS[dom], "bound": "hbm",
                      "achieved": dom_gbs, "peak": PEAK_HBM_GBS,
                      "unit": "GB/s", "frac": dom_gbs / PEAK_HBM_GBS,
-                     "traffic": profiled_traffic(dom),
+                     "traffic": traffic[dom],
                      "bytes_per_unit": BYTES_PER_UNIT[dom], "units_per_launch": U},
         "wall_s_timed": wall,
     }
