@@ -15,7 +15,8 @@ algorithmic HBM bandwidth, per-call times from HIP events on the launch
 stream, the roofline entry of the dominant call, and the CPU oracle's rate
 on a bounded sample of the same workload (rank 0, N=1).  Beside the warm
 headline it reports a cold pass (a 512 MiB scratch write before each pass
-evicts the L2s and the MALL) and the pass's counter bytes (calibrated
+evicts the L2s and the MALL), the pass replayed from a HIP graph, and the
+pass's counter bytes (calibrated
 FETCH_SIZE + WRITE_SIZE from the committed profile, when it matches the
 kernel sources) against its compulsory bytes.
 
@@ -98,7 +99,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-cold", action="store_true",
-                    help="skip the cold-cache passes (profiler runs of the warm pass)")
+                    help="skip the cold-cache and graph-replay passes (profiler runs of the "
+                         "warm eager pass)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="instead of the pass, run a plain device copy of MIB MiB "
@@ -191,6 +193,32 @@ def time_cold(ps: Pass, steps: int, flush_mib: int = 512):
     return float(np.mean(times))
 
 
+def time_graph(ps: Pass, steps: int):
+    """Mean time of one pass replayed from a HIP graph that captured the four
+    calls (HIP events around `steps` back-to-back replays)."""
+    calls = ps.calls()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        for c in calls:
+            c()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for c in calls:
+            c()
+    g.replay()
+    torch.cuda.synchronize()
+    st, en = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    st.record()
+    for _ in range(steps):
+        g.replay()
+    en.record()
+    torch.cuda.synchronize()
+    return st.elapsed_time(en) / steps
+
+
 def cpu_baseline(ps: Pass, budget_s: float):
     """The oracle, single-threaded, on whole (batch, KV head) pairs of the same
     workload, in pair order, until the time budget is spent (whole pairs)."""
@@ -250,6 +278,7 @@ def main():
     U = p.units
     pass_bytes = sum(BYTES_PER_UNIT.values()) * U
     cold_ms = None if a.no_cold else time_cold(ps, max(5, a.steps // 5))
+    graph_ms = None if a.no_cold else time_graph(ps, a.steps)
     dom = max(per_call, key=per_call.get)
     traffic = {c: profiled_traffic(c) for c in CALLS}
     counter_bytes = (sum(traffic.values()) if all(v is not None for v in traffic.values())
@@ -279,6 +308,9 @@ def main():
         "cold": None if cold_ms is None else {
             "ms_per_step": cold_ms, "value": U / (cold_ms * 1e-3),
             "flush": "512 MiB scratch written before each pass"},
+        "graph": None if graph_ms is None else {
+            "ms_per_step": graph_ms, "value": U / (graph_ms * 1e-3),
+            "how": "the four calls captured once in a HIP graph, replayed back to back"},
         "pass_counter": None if counter_bytes is None else {
             "bytes": counter_bytes,
             "GBps": counter_bytes / (ms * 1e-3) / 1e9,

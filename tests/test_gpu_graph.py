@@ -1,0 +1,105 @@
+"""The four calls captured in a HIP graph (torch.cuda.CUDAGraph) and replayed.
+
+Every call only launches kernels on the caller's stream (zero-fills are
+kernels, not memsets; workspaces come from the caller), so a whole layer pass
+can be captured once and replayed.  Each replay is checked against the eager
+result of the same pass, with other eager work and synchronisations between
+replays.  Outputs whose sums run in an order that varies between runs (dk, dv
+and the SER gradients: fp32 sums over up to ~100 incoming edges, which two
+eager runs already reproduce only to a few 1e-6) are compared to 1e-5
+relative and absolute; the rest must be identical.
+"""
+from __future__ import annotations
+
+import pytest
+import torch
+
+import sparse_dynamic_routing_amd as gm
+import synth
+from gpu_util import say
+
+pytestmark = pytest.mark.gpu
+
+
+class LayerPass:
+    """Inputs, preallocated outputs and workspaces of one SER+SEA fwd+bwd pass."""
+
+    def __init__(self, B, n, hq=16, hkv=8, d=128, s=4, seed=synth.BASE_SEED + 40):
+        idx, w = synth.edges(seed, B, n, hkv, s, mode="mixed")
+        cu = lambda x: torch.from_numpy(x).cuda()  # noqa: E731
+        self.idx, self.w = cu(idx), cu(w)
+        qs, ks = (B, n, hq, d), (B, n, hkv, d)
+        act = lambda name, shape: synth.normal(seed, name, shape, torch.bfloat16,  # noqa: E731
+                                               device="cuda")
+        self.q, self.k, self.v, self.dout = act("q", qs), act("k", ks), act("v", ks), act("dout", qs)
+        f32 = dict(dtype=torch.float32, device="cuda")
+        self.ia = torch.empty(idx.shape, dtype=torch.int32, device="cuda")
+        self.wa = torch.empty(idx.shape, **f32)
+        self.o = torch.empty_like(self.q)
+        self.dq = torch.empty(qs, **f32)
+        self.dk = torch.empty(ks, **f32)
+        self.dv = torch.empty(ks, **f32)
+        self.dwa = torch.empty(idx.shape, **f32)
+        self.dA = torch.empty(idx.shape, **f32)
+        self.ws_sea = gm.sea_workspace(self.q, self.ia)
+        self.ws_ser = gm.ser_workspace(self.idx, self.idx, aliased=True)
+
+    def outputs(self):
+        return {"ia": self.ia, "wa": self.wa, "o": self.o, "dq": self.dq, "dk": self.dk,
+                "dv": self.dv, "dwa": self.dwa, "dA": self.dA}
+
+    def run(self):
+        gm.gm_ser_forward(self.idx, self.w, self.idx, self.w, self.ia, self.wa)
+        gm.gm_sea_forward(self.q, self.k, self.v, self.ia, self.wa, self.o)
+        gm.gm_sea_backward(self.q, self.k, self.v, self.ia, self.wa, self.dout, self.dq, self.dk,
+                           self.dv, self.dwa, self.ws_sea)
+        gm.gm_ser_backward(self.idx, self.w, self.idx, self.w, self.ia, self.wa, self.dwa,
+                           self.dA, self.dA, self.ws_ser)
+
+    def poison(self):
+        for t in self.outputs().values():
+            if t.dtype == torch.int32:
+                t.fill_(-7)
+            else:
+                t.fill_(float("nan"))
+
+
+ORDER_VARIES = {"dk", "dv", "dA"}
+
+
+@pytest.mark.parametrize("B,n", [(2, 2048), (1, 8192)],
+                         ids=["n2048-one-pass-index", "n8192-global-index"])
+def test_layer_pass_graph_replays_match_eager(B, n):
+    say(f"case graph replay B={B} n={n}")
+    lp = LayerPass(B, n)
+    lp.run()
+    torch.cuda.synchronize()
+    ref = {k: v.clone() for k, v in lp.outputs().items()}
+    other = LayerPass(1, 512, seed=synth.BASE_SEED + 41)   # unrelated eager work
+
+    g = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        lp.run()                                # warm-up on the capture stream
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g):
+        lp.run()
+    torch.cuda.synchronize()
+
+    for rep in range(3):
+        lp.poison()
+        other.run()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        say(f"  replay {rep}")
+        for name, t in lp.outputs().items():
+            if name in ORDER_VARIES:
+                err = (t - ref[name]).abs()
+                bound = 1e-5 + 1e-5 * ref[name].abs()
+                assert bool((err <= bound).all()), (
+                    f"replay {rep}: {name} max |diff| {err.max().item():.3e}")
+            else:
+                assert torch.equal(t, ref[name]), f"replay {rep}: {name} differs from eager"
