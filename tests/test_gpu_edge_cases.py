@@ -156,6 +156,45 @@ def test_ser_backward_source_chunks(n):
             assert_close("dw2", host(d2), r2, 1e-5)
 
 
+def _unaligned(x: np.ndarray) -> torch.Tensor:
+    """x on the GPU, starting 4 bytes past a 16-byte boundary (contiguous)."""
+    flat = torch.empty(x.size + 1, dtype=torch.from_numpy(x[:0].copy()).dtype, device="cuda")
+    t = flat[1:].view(x.shape)
+    t.copy_(torch.from_numpy(np.ascontiguousarray(x)))
+    assert t.data_ptr() % 16 != 0
+    return t
+
+
+def test_unaligned_edge_rows_take_the_scalar_loads():
+    """s = 4 edges whose rows are not 16-byte aligned: the forward, source and
+    index kernels load slots one by one, SER forward and backward take their
+    general lane-per-unit / reverse-index paths; results as for the oracle."""
+    say("case unaligned s=4 edges")
+    rng = np.random.default_rng(77)
+    dtype, d, G, s, n, B, hkv = torch.bfloat16, 128, 2, 4, 300, 2, 2
+    q, k, v, do, idx, w = _sea_inputs(rng, dtype, d, G, s, n, B=B, hkv=hkv)
+    orc = oracle.get()
+    ui, uw = _unaligned(idx), _unaligned(w)
+    io, wo = gm.ser_forward(ui, uw, ui, uw, s)
+    rio, rwo = orc.ser_forward(idx, w, idx, w, s)
+    assert_ser_match(host(io), host(wo), rio, rwo)
+    np.testing.assert_array_equal(host(wo), rwo)
+    ai, aw = _unaligned(rio), _unaligned(rwo)
+    o = gm.sea_forward(dev(q), dev(k), dev(v), ai, aw)
+    dq, dk, dv, dw = gm.sea_backward(dev(q), dev(k), dev(v), ai, aw, dev(do))
+    X = TOL[dtype]
+    assert_close("o", host(o), orc.sea_forward(q, k, v, rio, rwo), X)
+    rdq, rdk, rdv, rdw = orc.sea_backward(q, k, v, rio, rwo, do)
+    assert_close("dq", host(dq), rdq, X)
+    assert_close("dk", host(dk), rdk, X)
+    assert_close("dv", host(dv), rdv, X)
+    assert_close("dw", host(dw), rdw, X)
+    dwo = rng.standard_normal(rio.shape).astype(np.float32)
+    da, _ = gm.ser_backward(ui, uw, ui, uw, ai, aw, _unaligned(dwo), aliased=True)
+    ra, _ = orc.ser_backward(idx, w, idx, w, rio, rwo, dwo, aliased=True)
+    assert_close("dw (aliased legs)", host(da), ra, 1e-5)
+
+
 def test_single_token_and_empty_inputs():
     """n = 1 (every edge is the padding token itself) and zero-size calls,
     which launch nothing and return success."""
