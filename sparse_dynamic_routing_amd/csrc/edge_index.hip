@@ -246,6 +246,218 @@ __global__ __launch_bounds__(kIndexThreads) void edge_index_one_kernel(IndexArgs
     for (int p = threadIdx.x; p < range_total; p += kIndexThreads) a.list[gbase + p] = sorted[p];
 }
 
+// ------------------------------------------- index of long sequences
+// For n > kOneRows the per-pair workgroups above would each read every
+// token of a pair; instead the edges are first partitioned by target bucket
+// (kBucket rows) with only workgroup-local atomics, then each bucket is
+// sorted in LDS like a short sequence:
+//   count:   workgroup (pair, chunk of kOneRows source tokens) counts its
+//            live edges per bucket (LDS) into counts[pair][bucket][chunk];
+//   scan:    per pair, exclusive offsets in (bucket, chunk) order, so each
+//            bucket's edges and, inside it, each chunk's are contiguous;
+//   scatter: the count workgroups again, each edge to
+//            offset + (LDS cursor of its bucket) in staging, as (edge, target);
+//   sort:    workgroup (pair, bucket) counts the bucket's rows in LDS, writes
+//            beg/len and places the edges (through LDS when they fit).
+// The list of pair p is again [p * n * s, (p + 1) * n * s).
+constexpr int kBucket = 512;        // target rows per bucket (far edges crowd the first
+                                    // rows: at n = 65536 the first 512 rows of a pair
+                                    // collect ~16k edges, about what LDS can stage)
+constexpr int kMaxBuckets = 2048;   // n <= 2^20
+
+struct LongIndexArgs {
+    const int32_t* idx;
+    const float* w;
+    int n, hkv, s, npairs, nb, nch, vec;
+    int* counts;   // [npairs][nb][nch]
+    int* offs;     // [npairs][nb][nch]
+    int* tot;      // [npairs]
+    int2* stage;   // [npairs * n * s]
+    int* beg;
+    int* len;
+    int* list;
+};
+
+// targets and edge ids (-1: dead) of the kTok tokens i0 + k * kIndexThreads
+// + threadIdx.x of pair (b, h); unconditional loads from clamped addresses
+template <bool VEC>
+__device__ __forceinline__ void load_tokens(const LongIndexArgs& a, int b, int h, int i0,
+                                            int (&tj)[kTok * kSlotMax],
+                                            int (&te)[kTok * kSlotMax]) {
+    const int n = a.n, s = a.s, hkv = a.hkv;
+#pragma unroll
+    for (int k = 0; k < kTok; ++k) {
+        const int iv = i0 + k * kIndexThreads + (int)threadIdx.x;
+        const bool ok = iv < n;
+        const int i = ok ? iv : n - 1;
+        const int e0 = ((b * n + i) * hkv + h) * s;
+        if constexpr (VEC) {
+            const int4 j4 = *reinterpret_cast<const int4*>(a.idx + e0);
+            const float4 w4 = *reinterpret_cast<const float4*>(a.w + e0);
+            tj[k * 4 + 0] = j4.x; tj[k * 4 + 1] = j4.y;
+            tj[k * 4 + 2] = j4.z; tj[k * 4 + 3] = j4.w;
+            te[k * 4 + 0] = ok && w4.x > 0.0f ? e0 + 0 : -1;
+            te[k * 4 + 1] = ok && w4.y > 0.0f ? e0 + 1 : -1;
+            te[k * 4 + 2] = ok && w4.z > 0.0f ? e0 + 2 : -1;
+            te[k * 4 + 3] = ok && w4.w > 0.0f ? e0 + 3 : -1;
+        } else {
+#pragma unroll
+            for (int t = 0; t < kSlotMax; ++t) {
+                const int sl = k * kSlotMax + t;
+                const int e = e0 + (t < s ? t : s - 1);
+                tj[sl] = a.idx[e];
+                te[sl] = ok && t < s && a.w[e] > 0.0f ? e : -1;
+            }
+        }
+    }
+}
+
+// workgroup x + 8k runs on XCD x: XCD x takes consecutive items
+__device__ __forceinline__ int xcd_item(int total) {
+    int lin = (int)blockIdx.x;
+    if (total % kXcds == 0)
+        lin = ((int)blockIdx.x % kXcds) * (total / kXcds) + (int)blockIdx.x / kXcds;
+    return lin;
+}
+
+template <bool VEC, bool SCATTER>
+__global__ __launch_bounds__(kIndexThreads) void long_index_pass_kernel(LongIndexArgs a) {
+    __shared__ int hist[kMaxBuckets];
+    const int lin = xcd_item(a.npairs * a.nch);
+    const int pair = lin / a.nch, c = lin - (lin / a.nch) * a.nch;
+    const int b = pair / a.hkv, h = pair - (pair / a.hkv) * a.hkv;
+    for (int k = threadIdx.x; k < a.nb; k += kIndexThreads)
+        hist[k] = SCATTER ? a.offs[((size_t)pair * a.nb + k) * a.nch + c] : 0;
+    __syncthreads();
+    int tj[kTok * kSlotMax], te[kTok * kSlotMax];
+    load_tokens<VEC>(a, b, h, c * kOneRows, tj, te);
+    const size_t sbase = (size_t)pair * a.n * a.s;
+#pragma unroll
+    for (int k = 0; k < kTok * kSlotMax; ++k) {
+        if (te[k] < 0 || (unsigned)tj[k] >= (unsigned)a.n) continue;   // dead (or invalid)
+        const int bk = tj[k] / kBucket;
+        const int pos = atomicAdd(&hist[bk], 1);
+        if constexpr (SCATTER) a.stage[sbase + pos] = make_int2(te[k], tj[k]);
+    }
+    if constexpr (!SCATTER) {
+        __syncthreads();
+        for (int k = threadIdx.x; k < a.nb; k += kIndexThreads)
+            a.counts[((size_t)pair * a.nb + k) * a.nch + c] = hist[k];
+    }
+}
+
+// per pair: exclusive scan of counts in (bucket, chunk) order
+__global__ __launch_bounds__(kIndexThreads) void long_index_scan_kernel(LongIndexArgs a) {
+    __shared__ int part[kIndexThreads / kWave];
+    const int pair = blockIdx.x;
+    const int N = a.nb * a.nch;
+    const int* cnt = a.counts + (size_t)pair * N;
+    int* off = a.offs + (size_t)pair * N;
+    const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
+    const int run_len = (N + kIndexThreads - 1) / kIndexThreads;
+    const int j0 = threadIdx.x * run_len;
+    int run = 0;
+    for (int j = j0; j < j0 + run_len && j < N; ++j) run += cnt[j];
+    int inc = run;
+    for (int m = 1; m < kWave; m <<= 1) {
+        const int o = __shfl_up(inc, m, kWave);
+        if (lane >= m) inc += o;
+    }
+    if (lane == kWave - 1) part[wave] = inc;
+    __syncthreads();
+    int base = 0;
+    for (int k = 0; k < wave; ++k) base += part[k];
+    if (threadIdx.x == kIndexThreads - 1) a.tot[pair] = base + inc;
+    base += inc - run;
+    for (int j = j0; j < j0 + run_len && j < N; ++j) {
+        off[j] = base;
+        base += cnt[j];
+    }
+}
+
+// per (pair, bucket): counting sort of the bucket's edges by target row
+__global__ __launch_bounds__(kIndexThreads) void long_index_sort_kernel(LongIndexArgs a) {
+    __shared__ int cnt[kBucket];
+    __shared__ int rlen[kBucket];
+    __shared__ int sorted[kOneList];
+    __shared__ int part[kIndexThreads / kWave];
+    const int lin = xcd_item(a.npairs * a.nb);
+    const int pair = lin / a.nb, bk = lin - (lin / a.nb) * a.nb;
+    const int n = a.n;
+    const int jlo = bk * kBucket, jhi = jlo + kBucket < n ? jlo + kBucket : n;
+    const int nr = jhi - jlo;
+    const int* offp = a.offs + (size_t)pair * a.nb * a.nch;
+    const int ebeg = offp[(size_t)bk * a.nch];
+    const int eend = bk + 1 < a.nb ? offp[(size_t)(bk + 1) * a.nch] : a.tot[pair];
+    const int ne = eend - ebeg;
+    const size_t lbase = (size_t)pair * n * a.s;
+    const int2* st = a.stage + lbase + ebeg;
+    for (int j = threadIdx.x; j < nr; j += kIndexThreads) cnt[j] = 0;
+    __syncthreads();
+    // kUnroll independent loads per thread before their LDS atomics: the
+    // first buckets collect most far edges, so their loops are long
+    constexpr int kUnroll = 8;
+    for (int p0 = 0; p0 < ne; p0 += kIndexThreads * kUnroll) {
+        int row[kUnroll];
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u) {
+            const int p = p0 + u * kIndexThreads + (int)threadIdx.x;
+            row[u] = p < ne ? st[p < ne ? p : 0].y - jlo : -1;
+        }
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u)
+            if (row[u] >= 0) atomicAdd(&cnt[row[u]], 1);
+    }
+    __syncthreads();
+    const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
+    const int run_len = (nr + kIndexThreads - 1) / kIndexThreads;
+    const int j0 = threadIdx.x * run_len;
+    int run = 0;
+    for (int j = j0; j < j0 + run_len && j < nr; ++j) run += cnt[j];
+    int inc = run;
+    for (int m = 1; m < kWave; m <<= 1) {
+        const int o = __shfl_up(inc, m, kWave);
+        if (lane >= m) inc += o;
+    }
+    if (lane == kWave - 1) part[wave] = inc;
+    __syncthreads();
+    int base = 0;
+    for (int k = 0; k < wave; ++k) base += part[k];
+    base += inc - run;
+    for (int j = j0; j < j0 + run_len && j < nr; ++j) {
+        const int c = cnt[j];
+        rlen[j] = c;
+        cnt[j] = base;
+        base += c;
+    }
+    __syncthreads();
+    const size_t gbase = lbase + ebeg;   // list slot of the bucket's first edge
+    for (int j = threadIdx.x; j < nr; j += kIndexThreads) {
+        a.beg[(size_t)pair * n + jlo + j] = (int)(gbase + cnt[j]);
+        a.len[(size_t)pair * n + jlo + j] = rlen[j];
+    }
+    __syncthreads();
+    const bool staged = ne <= kOneList;
+    for (int p0 = 0; p0 < ne; p0 += kIndexThreads * kUnroll) {
+        int2 v[kUnroll];
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u) {
+            const int p = p0 + u * kIndexThreads + (int)threadIdx.x;
+            v[u] = st[p < ne ? p : 0];
+        }
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u) {
+            if (p0 + u * kIndexThreads + (int)threadIdx.x >= ne) continue;
+            const int pos = atomicAdd(&cnt[v[u].y - jlo], 1);
+            if (staged) sorted[pos] = v[u].x;
+            else a.list[gbase + pos] = v[u].x;
+        }
+    }
+    __syncthreads();
+    if (staged)
+        for (int p = threadIdx.x; p < ne; p += kIndexThreads) a.list[gbase + p] = sorted[p];
+}
+
 int pow2_at_least(long long x) {
     int p = 1;
     while (p < x) p <<= 1;
@@ -283,6 +495,31 @@ hipError_t launch_edge_index(int B, int n, int hkv, const int32_t* idx, const fl
     } else {
         hipLaunchKernelGGL(edge_index_kernel, grid, dim3(kIndexThreads), 0, st, a);
     }
+    return hipGetLastError();
+}
+
+hipError_t launch_edge_index_long(int B, int n, int hkv, const int32_t* idx, const float* w,
+                                  int s, int* beg, int* len, int* list, int* counts, int* offs,
+                                  int* tot, int2* stage, hipStream_t st) {
+    LongIndexArgs a;
+    a.idx = idx; a.w = w; a.n = n; a.hkv = hkv; a.s = s;
+    a.npairs = B * hkv;
+    a.nb = (n + kBucket - 1) / kBucket;
+    a.nch = (n + kOneRows - 1) / kOneRows;
+    if (a.nb > kMaxBuckets || s > kSlotMax) return hipErrorInvalidValue;
+    a.vec = s == 4 && (((uintptr_t)idx | (uintptr_t)w) & 15) == 0;
+    a.counts = counts;
+    a.offs = offs;
+    a.tot = tot;
+    a.stage = stage;
+    a.beg = beg; a.len = len; a.list = list;
+    const dim3 gpass((unsigned)(a.npairs * a.nch)), th(kIndexThreads);
+    if (a.vec) hipLaunchKernelGGL((long_index_pass_kernel<true, false>), gpass, th, 0, st, a);
+    else hipLaunchKernelGGL((long_index_pass_kernel<false, false>), gpass, th, 0, st, a);
+    hipLaunchKernelGGL(long_index_scan_kernel, dim3((unsigned)a.npairs), th, 0, st, a);
+    if (a.vec) hipLaunchKernelGGL((long_index_pass_kernel<true, true>), gpass, th, 0, st, a);
+    else hipLaunchKernelGGL((long_index_pass_kernel<false, true>), gpass, th, 0, st, a);
+    hipLaunchKernelGGL(long_index_sort_kernel, dim3((unsigned)(a.npairs * a.nb)), th, 0, st, a);
     return hipGetLastError();
 }
 

@@ -50,6 +50,13 @@ hipError_t launch_ser_backward(int B, int n, int hkv, const int32_t* idx1, const
 bool edge_index_supported(int n, int s);
 // n small enough for the single-pass index (one load pass per pair)
 bool edge_index_one_pass(int n);
+// The same index for n > 4096 (s <= 4, n <= 2^20) in four passes without
+// per-edge global atomics: counts and offs need B*hkv * ceil(n/512) *
+// ceil(n/4096) ints each (at most B*n*hkv), tot B*hkv ints, stage B*n*hkv*s
+// int2 entries.
+hipError_t launch_edge_index_long(int B, int n, int hkv, const int32_t* idx, const float* w,
+                                  int s, int* beg, int* len, int* list, int* counts, int* offs,
+                                  int* tot, int2* stage, hipStream_t st);
 hipError_t launch_edge_index(int B, int n, int hkv, const int32_t* idx, const float* w, int s,
                              int* beg, int* len, int* list, hipStream_t st);
 

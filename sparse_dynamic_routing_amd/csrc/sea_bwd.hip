@@ -716,6 +716,16 @@ hipError_t run_fast(const SeaBwdArgs& g, const SeaBwdFast& a, long long E, hipSt
         hipLaunchKernelGGL((sea_bwd_src_row_kernel<T, G, S, VEC, true>),
                            dim3(persistent_grid(fn, a.U, kBlock / 16)), dim3(kBlock), 0, st, a);
         launch_index(g, E, st);
+    } else if (!edge_index_one_pass(a.n)) {
+        // long sequences: the partitioned index first; its staging area is
+        // the coefficient buffer, which the source pass writes afterwards
+        const hipError_t e = launch_edge_index_long(
+            a.U / (a.n * a.hkv), a.n, a.hkv, a.idx, a.w, a.s, a.ws.beg, a.ws.len, a.ws.list,
+            a.ws.cnt, a.ws.off, a.ws.bsum, reinterpret_cast<int2*>(a.ws.coef), st);
+        if (e != hipSuccess) return e;
+        const void* fn = reinterpret_cast<const void*>(&sea_bwd_src_row_kernel<T, G, S, VEC, false>);
+        hipLaunchKernelGGL((sea_bwd_src_row_kernel<T, G, S, VEC, false>),
+                           dim3(persistent_grid(fn, a.U, kBlock / 16)), dim3(kBlock), 0, st, a);
     } else {
         const void* fn = reinterpret_cast<const void*>(&sea_bwd_src_row_kernel<T, G, S, VEC, false>);
         hipLaunchKernelGGL((sea_bwd_src_row_kernel<T, G, S, VEC, false>),
@@ -797,10 +807,7 @@ hipError_t launch_sea_backward(int B, int n, int hq, int hkv, int d, bool bf16, 
         f.fd_hkv = make_fastdiv((uint32_t)hkv);
         f.fd_s = make_fastdiv((uint32_t)s);
         make_seg_plan(f.sp, B, n, hkv);
-        // beyond 4096 tokens the per-pair LDS index reads every token of a
-        // pair in each of its few workgroups; the global count/scan/fill
-        // index spreads over the whole device instead
-        f.global_index = !edge_index_supported(n, s) || !edge_index_one_pass(n);
+        f.global_index = !edge_index_supported(n, s);
         f.vec = s == 4 && (((uintptr_t)idx | (uintptr_t)w) & 15) == 0;
         return bf16 ? dispatch_fast<bf16_t>(a, f, G, E, st) : dispatch_fast<float>(a, f, G, E, st);
     }

@@ -156,6 +156,24 @@ def test_ser_backward_source_chunks(n):
             assert_close("dw2", host(d2), r2, 1e-5)
 
 
+@pytest.mark.parametrize("n,s", [(4097, 4), (9000, 4), (12289, 3)])
+def test_sea_backward_partitioned_index(n, s):
+    """n > 4096: the reverse edge index is built by target bucket (4096 rows)
+    and source chunk (4096 tokens); ragged last bucket and chunk, s = 4 (16-byte
+    edge rows) and s = 3; every output compared."""
+    say(f"case sea backward partitioned index n={n} s={s}")
+    rng = np.random.default_rng(5000 + n + s)
+    dtype = torch.bfloat16
+    q, k, v, do, idx, w = _sea_inputs(rng, dtype, 128, 2, s, n, B=1, hkv=2)
+    dq, dk, dv, dw = gm.sea_backward(dev(q), dev(k), dev(v), dev(idx), dev(w), dev(do))
+    rdq, rdk, rdv, rdw = oracle.get().sea_backward(q, k, v, idx, w, do)
+    X = TOL[dtype]
+    assert_close("dq", host(dq), rdq, X)
+    assert_close("dk", host(dk), rdk, X)
+    assert_close("dv", host(dv), rdv, X)
+    assert_close("dw", host(dw), rdw, X)
+
+
 def _unaligned(x: np.ndarray) -> torch.Tensor:
     """x on the GPU, starting 4 bytes past a 16-byte boundary (contiguous)."""
     flat = torch.empty(x.size + 1, dtype=torch.from_numpy(x[:0].copy()).dtype, device="cuda")
