@@ -2,17 +2,14 @@
 // backward passes: for every (batch, KV head) pair and target token j, the
 // list of live edge ids e = unit * s + slot with idx[e] == j.
 //
-// Counting sort in LDS, no global atomics (device-scope atomics on this
-// multi-XCD part are performed at the memory side and are slow).  The pair's
-// targets are split into K ranges of n/K tokens; one 1024-thread workgroup
-// per (pair, range) reads all of the pair's edges (the K workgroups of a pair
-// run on one XCD, so the re-reads hit its L2), counts the edges into its
-// range with LDS atomics and the edges below its range in registers, scans
-// its counts, writes beg/len of its rows and places its edges.  The pair's
-// list occupies the fixed range [pair * n * s, (pair + 1) * n * s), so no
-// scan across pairs is needed.  beg and len are indexed by the pair-major
-// row pair * n + j.  The order of edges inside one target's segment follows
-// the LDS atomics and may vary between runs.
+// Counting sorts in LDS; no per-edge global atomics (device-scope atomics on
+// this multi-XCD part are slow, and a returning one per edge bounds the
+// build).  n <= 4096: one 1024-thread workgroup per (pair, target half)
+// loads the pair's edges once and sorts its half in LDS.  Longer sequences:
+// a bucket partition, then an LDS sort per bucket (below).  The pair's list
+// occupies the fixed range [pair * n * s, (pair + 1) * n * s); beg and len
+// are indexed by the pair-major row pair * n + j.  The order of edges inside
+// one target's segment follows the LDS atomics and may vary between runs.
 #include "gm_common.h"
 #include "gm_internal.h"
 #include "gm_wave.h"
@@ -21,7 +18,6 @@ namespace gm {
 namespace {
 
 constexpr int kIndexThreads = 1024;
-constexpr int kRangeMax = 16384;   // targets per workgroup (64 KiB of LDS counts)
 constexpr int kTok = 4;            // tokens per thread per batch
 constexpr int kSlotMax = 4;        // fast loads for s <= 4
 
@@ -33,112 +29,6 @@ struct IndexArgs {
     int* len;
     int* list;
 };
-
-__global__ __launch_bounds__(kIndexThreads) void edge_index_kernel(IndexArgs a) {
-    __shared__ int cnt[kRangeMax];
-    __shared__ int part[kIndexThreads / kWave];
-    // workgroup x + 8k runs on XCD x; when the work tiles the XCDs evenly,
-    // XCD x takes consecutive (pair, range) items: all ranges of its pairs
-    const int total = a.npairs * a.K;
-    int lin = (int)blockIdx.x;
-    if (total % kXcds == 0)
-        lin = ((int)blockIdx.x % kXcds) * (total / kXcds) + (int)blockIdx.x / kXcds;
-    const int pair = lin / a.K, kq = lin - (lin / a.K) * a.K;
-    const int n = a.n, s = a.s, hkv = a.hkv;
-    const int jlo = (int)((long long)kq * n / a.K), jhi = (int)((long long)(kq + 1) * n / a.K);
-    const int b = pair / hkv, h = pair - (pair / hkv) * hkv;
-    const int lbase = pair * n * s;
-    for (int j = threadIdx.x; j < jhi - jlo; j += kIndexThreads) cnt[j] = 0;
-    __syncthreads();
-
-    // targets and edge ids (-1: dead or not this workgroup's) of 4 tokens
-    auto load = [&](int i0, int (&tj)[kTok * kSlotMax], int (&te)[kTok * kSlotMax]) {
-#pragma unroll
-        for (int k = 0; k < kTok; ++k) {
-            const int i = i0 + k * kIndexThreads + (int)threadIdx.x;
-            const int e0 = ((b * n + i) * hkv + h) * s;
-            if (a.vec) {   // s == 4 and 16-byte aligned rows
-                int4 j4 = make_int4(0, 0, 0, 0);
-                float4 w4 = make_float4(0.f, 0.f, 0.f, 0.f);
-                if (i < n) {
-                    j4 = *reinterpret_cast<const int4*>(a.idx + e0);
-                    w4 = *reinterpret_cast<const float4*>(a.w + e0);
-                }
-                tj[k * 4 + 0] = j4.x; tj[k * 4 + 1] = j4.y;
-                tj[k * 4 + 2] = j4.z; tj[k * 4 + 3] = j4.w;
-                te[k * 4 + 0] = w4.x > 0.0f ? e0 + 0 : -1;
-                te[k * 4 + 1] = w4.y > 0.0f ? e0 + 1 : -1;
-                te[k * 4 + 2] = w4.z > 0.0f ? e0 + 2 : -1;
-                te[k * 4 + 3] = w4.w > 0.0f ? e0 + 3 : -1;
-                continue;
-            }
-#pragma unroll
-            for (int t = 0; t < kSlotMax; ++t) {
-                const int sl = k * kSlotMax + t;
-                tj[sl] = 0;
-                te[sl] = -1;
-                if (i < n && t < s) {
-                    tj[sl] = a.idx[e0 + t];
-                    te[sl] = a.w[e0 + t] > 0.0f ? e0 + t : -1;
-                }
-            }
-        }
-    };
-
-    int below = 0;
-    for (int i0 = 0; i0 < n; i0 += kIndexThreads * kTok) {
-        int tj[kTok * kSlotMax], te[kTok * kSlotMax];
-        load(i0, tj, te);
-#pragma unroll
-        for (int k = 0; k < kTok * kSlotMax; ++k) {
-            if (te[k] < 0) continue;
-            if (tj[k] < jlo) ++below;
-            else if (tj[k] < jhi) atomicAdd(&cnt[tj[k] - jlo], 1);
-        }
-    }
-    // block sum of `below`
-    const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
-    for (int m = 32; m > 0; m >>= 1) below += __shfl_xor(below, m, kWave);
-    if (lane == 0) part[wave] = below;
-    __syncthreads();
-    int below_all = 0;
-    for (int k = 0; k < kIndexThreads / kWave; ++k) below_all += part[k];
-    __syncthreads();
-
-    // exclusive scan of the range's counts: each thread scans a contiguous run
-    const int nr = jhi - jlo;
-    const int run_len = (nr + kIndexThreads - 1) / kIndexThreads;
-    const int j0 = threadIdx.x * run_len;
-    int run = 0;
-    for (int j = j0; j < j0 + run_len && j < nr; ++j) run += cnt[j];
-    int inc = run;
-    for (int m = 1; m < kWave; m <<= 1) {
-        const int o = __shfl_up(inc, m, kWave);
-        if (lane >= m) inc += o;
-    }
-    if (lane == kWave - 1) part[wave] = inc;
-    __syncthreads();
-    int base = below_all;
-    for (int k = 0; k < wave; ++k) base += part[k];
-    base += inc - run;
-    for (int j = j0; j < j0 + run_len && j < nr; ++j) {
-        const int c = cnt[j];
-        a.beg[pair * n + jlo + j] = lbase + base;
-        a.len[pair * n + jlo + j] = c;
-        cnt[j] = base;   // becomes the fill cursor
-        base += c;
-    }
-    __syncthreads();
-
-    for (int i0 = 0; i0 < n; i0 += kIndexThreads * kTok) {
-        int tj[kTok * kSlotMax], te[kTok * kSlotMax];
-        load(i0, tj, te);
-#pragma unroll
-        for (int k = 0; k < kTok * kSlotMax; ++k)
-            if (te[k] >= 0 && tj[k] >= jlo && tj[k] < jhi)
-                a.list[lbase + atomicAdd(&cnt[tj[k] - jlo], 1)] = te[k];
-    }
-}
 
 // Single-pass variant for n <= kIndexThreads * kTok: each thread holds its
 // kTok tokens' edges in registers from one load, the range's list is
@@ -458,43 +348,29 @@ __global__ __launch_bounds__(kIndexThreads) void long_index_sort_kernel(LongInde
         for (int p = threadIdx.x; p < ne; p += kIndexThreads) a.list[gbase + p] = sorted[p];
 }
 
-int pow2_at_least(long long x) {
-    int p = 1;
-    while (p < x) p <<= 1;
-    return p;
-}
-
 }  // namespace
 
 bool edge_index_supported(int n, int s) {
-    return s <= kSlotMax && (long long)(n + kRangeMax - 1) / kRangeMax <= 64;
+    return s <= kSlotMax && (long long)n <= (long long)kBucket * kMaxBuckets;
 }
 
 bool edge_index_one_pass(int n) { return n <= kOneRows; }
 
 hipError_t launch_edge_index(int B, int n, int hkv, const int32_t* idx, const float* w, int s,
                              int* beg, int* len, int* list, hipStream_t st) {
+    if (n > kOneRows || s > kSlotMax) return hipErrorInvalidValue;
     IndexArgs a;
     a.idx = idx; a.w = w; a.n = n; a.hkv = hkv; a.s = s;
     a.npairs = B * hkv;
-    // two ranges per pair for parallelism when there are few pairs, more
-    // only when the LDS needs them (every range at most kRangeMax targets)
-    const int k_lds = pow2_at_least((n + kRangeMax - 1) / kRangeMax);
-    int k_par = pow2_at_least((256 + a.npairs - 1) / a.npairs);
-    if (k_par > 2) k_par = 2;
-    a.K = k_lds > k_par ? k_lds : k_par;
-    while (a.K > 1 && a.K > n) a.K >>= 1;
+    // two target halves per pair when there are few pairs (parallelism)
+    a.K = a.npairs < 256 && n >= 2 ? 2 : 1;
     a.vec = s == 4 && (((uintptr_t)idx | (uintptr_t)w) & 15) == 0;
     a.beg = beg; a.len = len; a.list = list;
     const dim3 grid((unsigned)(a.npairs * a.K));
-    if (n <= kOneRows) {
-        if (a.vec)
-            hipLaunchKernelGGL(edge_index_one_kernel<true>, grid, dim3(kIndexThreads), 0, st, a);
-        else
-            hipLaunchKernelGGL(edge_index_one_kernel<false>, grid, dim3(kIndexThreads), 0, st, a);
-    } else {
-        hipLaunchKernelGGL(edge_index_kernel, grid, dim3(kIndexThreads), 0, st, a);
-    }
+    if (a.vec)
+        hipLaunchKernelGGL(edge_index_one_kernel<true>, grid, dim3(kIndexThreads), 0, st, a);
+    else
+        hipLaunchKernelGGL(edge_index_one_kernel<false>, grid, dim3(kIndexThreads), 0, st, a);
     return hipGetLastError();
 }
 
