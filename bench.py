@@ -21,6 +21,7 @@ FETCH_SIZE + WRITE_SIZE from the committed profile, when it matches the
 kernel sources) against its compulsory bytes.
 
     python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu-baseline] [--no-cold]
+    python bench.py --config {sea2,ser_sea4,stack21,long64k}   (other workloads)
 """
 from __future__ import annotations
 
@@ -64,6 +65,26 @@ CALL_KERNELS = {
 }
 PROFILE = os.path.join(ROOT, "profiles", "metric_pass_kernels.md")
 
+# The other configurations: the stages one step runs (edges carried from one
+# SER step to the next), and compulsory bytes per unit of each stage at the
+# configuration's slot counts (G = 2, d = 128, bf16 activations).
+CONFIG_STAGES = {
+    "metric": ["ser_fwd", "sea_fwd", "sea_bwd", "ser_bwd"],
+    "sea2": ["sea_fwd"],
+    "ser_sea4": ["ser_fwd", "sea_fwd"],
+    "stack21": ["ser_fwd", "ser_fwd", "sea_fwd"],   # one of the 21 layers
+    "long64k": ["ser_fwd", "sea_fwd", "sea_bwd", "ser_bwd"],
+}
+
+
+def stage_bytes(stage: str, p: synth.Preset) -> int:
+    """Compulsory bytes per unit of one stage (edges: 8 bytes per slot)."""
+    s1 = p.s1
+    return {"ser_fwd": 8 * p.s2 + 8 * s1,
+            "sea_fwd": 512 + 8 * s1 + 512 + 512,
+            "sea_bwd": 512 + 512 + 8 * s1 + 512 + 1024 + 4 * s1 + 1024,
+            "ser_bwd": 8 * p.s2 + 8 * s1 + 4 * s1 + 4 * p.s2}[stage]
+
 
 def profiled_traffic(call: str):
     """Calibrated HBM bytes per launch of `call` from the committed counter
@@ -97,6 +118,9 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", default="metric", choices=list(CONFIG_STAGES),
+                    help="workload: the measured pass (default) or one of the other "
+                         "configurations, timed on its own stages (no CPU baseline)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-cold", action="store_true",
                     help="skip the cold-cache and graph-replay passes (profiler runs of the "
@@ -134,6 +158,31 @@ class Pass:
         self.dA = torch.empty(self.idx.shape, **f32)
         self.ws = gm.ser_workspace(self.idx, self.idx, aliased=True)
         self.ws_sea = gm.sea_workspace(self.q, self.ia)
+        if p.ser_steps > 1:   # the first of two chained SER steps writes here
+            self.ia1 = torch.empty(es, dtype=torch.int32, device="cuda")
+            self.wa1 = torch.empty(es, **f32)
+
+    def stage_calls(self, stages):
+        """(label, call) for the stages of one step of a configuration."""
+        out, edges = [], (self.idx, self.w)     # edges entering the next SER step
+        n_ser = stages.count("ser_fwd")
+        for k, st in enumerate(stages):
+            if st == "ser_fwd":
+                ser_no = stages[:k + 1].count("ser_fwd")
+                dst = (self.ia, self.wa) if ser_no == n_ser else (self.ia1, self.wa1)
+                src = edges
+                out.append((f"gm_ser_forward#{ser_no}",
+                            lambda s_=src, d_=dst: gm.gm_ser_forward(*s_, *s_, *d_)))
+                edges = dst
+            elif st == "sea_fwd":
+                e = (self.ia, self.wa) if n_ser else (self.idx, self.w)
+                out.append(("gm_sea_forward",
+                            lambda e_=e: gm.gm_sea_forward(self.q, self.k, self.v, *e_, self.o)))
+            elif st == "sea_bwd":
+                out.append(("gm_sea_backward", self.calls()[2]))
+            else:
+                out.append(("gm_ser_backward", self.calls()[3]))
+        return out
 
     def calls(self):
         return [
@@ -219,6 +268,66 @@ def time_graph(ps: Pass, steps: int):
     return st.elapsed_time(en) / steps
 
 
+def run_config(a):
+    """Time one of the other configurations on its own stages (warm, HIP
+    events around each stage) and print one JSON line for it."""
+    p = synth.PRESETS[a.config]
+    stages = CONFIG_STAGES[a.config]
+    ps = Pass(p)
+    calls = ps.stage_calls(stages)
+    for _ in range(a.warmup):
+        for _, c in calls:
+            c()
+    torch.cuda.synchronize()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(calls) + 1)]
+          for _ in range(a.steps)]
+    for s_ in range(a.steps):
+        ev[s_][0].record()
+        for i, (_, c) in enumerate(calls):
+            c()
+            ev[s_][i + 1].record()
+    torch.cuda.synchronize()
+    per_stage = {lab: float(np.mean([ev[s_][i].elapsed_time(ev[s_][i + 1])
+                                     for s_ in range(a.steps)]))
+                 for i, (lab, _) in enumerate(calls)}
+    ms = float(np.mean([ev[s_][0].elapsed_time(ev[s_][-1]) for s_ in range(a.steps)]))
+    U = p.units
+    step_bytes = sum(stage_bytes(st, p) for st in stages) * U
+    counter = profiled_step_bytes(a.config)
+    print(json.dumps({
+        "config": a.config, "stages": stages, "units_per_step": U,
+        "shape": {"B": p.B, "n": p.n, "hq": p.hq, "hkv": p.hkv, "d": p.d,
+                  "s1": p.s1, "s2": p.s2, "dtype": str(p.dtype).replace("torch.", "")},
+        "ms_per_step": ms, "value": U / (ms * 1e-3), "unit": "tokens·KV-heads/s",
+        "per_stage_ms": per_stage,
+        "compulsory_bytes_per_unit": step_bytes // U,
+        "algorithmic_GBps": step_bytes / (ms * 1e-3) / 1e9,
+        "algorithmic_frac_of_peak": step_bytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS,
+        "counter": None if counter is None else {
+            "bytes": counter, "GBps": counter / (ms * 1e-3) / 1e9,
+            "frac_of_peak": counter / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS,
+            "over_compulsory": counter / step_bytes,
+            "source": f"profiles/{a.config}_kernels.md"},
+        "steps": a.steps, "warmup": a.warmup, "data": "synthetic"}), flush=True)
+
+
+def profiled_step_bytes(config: str):
+    """Counter bytes per step from profiles/<config>_kernels.md, or None when
+    it is missing or the kernel sources changed since."""
+    from sparse_dynamic_routing_amd.profile_summary import source_hash
+    path = os.path.join(ROOT, "profiles", f"{config}_kernels.md")
+    if not os.path.exists(path):
+        return None
+    hsh, per_step = None, None
+    for line in open(path):
+        line = line.strip()
+        if line.startswith("source_hash:"):
+            hsh = line.split(":", 1)[1].strip()
+        elif line.startswith("bytes_per_step:"):
+            per_step = float(line.split(":", 1)[1])
+    return per_step if hsh == source_hash() else None
+
+
 def cpu_baseline(ps: Pass, budget_s: float):
     """The oracle, single-threaded, on whole (batch, KV head) pairs of the same
     workload, in pair order, until the time budget is spent (whole pairs)."""
@@ -271,6 +380,9 @@ def main():
                           "launches": a.warmup + a.steps}))
         return
     gm.load()
+    if a.config != "metric":
+        run_config(a)
+        return
     p = synth.PRESETS["metric"]
     ps = Pass(p)
     torch.cuda.synchronize()

@@ -78,6 +78,13 @@ def main():
     ap.add_argument("--copy-write", required=True)
     ap.add_argument("--copy-mib", type=int, required=True)
     ap.add_argument("--command", required=True)
+    ap.add_argument("--title", default="the measured layer pass")
+    ap.add_argument("--workload", default="B=8, n=4096, 16 q / 8 KV heads, d=128, "
+                    "s1=s2=s3=4, bf16 activations\n(one SER fwd + SEA fwd + SEA bwd + "
+                    "SER bwd per step)")
+    ap.add_argument("--steps-run", type=int, default=7,
+                    help="steps the profiled program ran, warm-up included "
+                         "(to turn launches into launches per step)")
     a = ap.parse_args()
 
     ks = kernel_stats(a.trace)
@@ -87,9 +94,8 @@ def main():
     cname = max(cf, key=lambda k: cf[k])          # the copy kernel reads the most
     f_scale = cf[cname] / copy_bytes
     w_scale = cw[cname] / copy_bytes
-    print("# Kernel durations and HBM traffic of the measured layer pass\n")
-    print("Workload: B=8, n=4096, 16 q / 8 KV heads, d=128, s1=s2=s3=4, bf16 activations")
-    print("(one SER fwd + SEA fwd + SEA bwd + SER bwd per step).\n")
+    print(f"# Kernel durations and HBM traffic of {a.title}\n")
+    print(f"Workload: {a.workload}.\n")
     print(f"Command (kernel trace): `{a.command}`\n")
     print(f"Counter runs: the same command with `--pmc FETCH_SIZE`, then `--pmc WRITE_SIZE`;"
           f" calibration: `python3 bench.py --copy-calibration {a.copy_mib} --steps 5"
@@ -110,8 +116,11 @@ def main():
     print(f"source_hash: {source_hash()}")
     print(f"fetch_scale: {f_scale:.6f}")
     print(f"write_scale: {w_scale:.6f}")
+    per_step = 0.0
     for k, calls, us, fb, wb in rows:
         print(f"kernel: {k} | us={us:.3f} | fetch_bytes={fb:.0f} | write_bytes={wb:.0f}")
+        per_step += (fb + wb) * calls / a.steps_run
+    print(f"bytes_per_step: {per_step:.0f}")
     print("```")
 
 
