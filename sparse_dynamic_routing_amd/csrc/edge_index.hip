@@ -28,6 +28,7 @@ struct IndexArgs {
     int* beg;
     int* len;
     int* list;
+    int* head;     // [pair-major row * 4] or null
 };
 
 // Single-pass variant for n <= kIndexThreads * kTok: each thread holds its
@@ -134,6 +135,18 @@ __global__ __launch_bounds__(kIndexThreads) void edge_index_one_kernel(IndexArgs
             sorted[atomicAdd(&cnt[tj[k] - jlo], 1)] = te[k];
     __syncthreads();
     for (int p = threadIdx.x; p < range_total; p += kIndexThreads) a.list[gbase + p] = sorted[p];
+    if (a.head) {
+        // cnt[j] is now the end of row j's run in `sorted`
+        for (int j = threadIdx.x; j < nr; j += kIndexThreads) {
+            const int l = rlen[j], b0 = cnt[j] - l;
+            int4 hd;
+            hd.x = l > 0 ? sorted[b0] : -1;
+            hd.y = l > 1 ? sorted[b0 + 1] : -1;
+            hd.z = l > 2 ? sorted[b0 + 2] : -1;
+            hd.w = l > 3 ? sorted[b0 + 3] : -1;
+            reinterpret_cast<int4*>(a.head)[pair * n + jlo + j] = hd;
+        }
+    }
 }
 
 // ------------------------------------------- index of long sequences
@@ -166,6 +179,7 @@ struct LongIndexArgs {
     int* beg;
     int* len;
     int* list;
+    int* head;     // [pair-major row * 4] or null
 };
 
 // targets and edge ids (-1: dead) of the kTok tokens i0 + k * kIndexThreads
@@ -269,6 +283,7 @@ __global__ __launch_bounds__(kIndexThreads) void long_index_scan_kernel(LongInde
 __global__ __launch_bounds__(kIndexThreads) void long_index_sort_kernel(LongIndexArgs a) {
     __shared__ int cnt[kBucket];
     __shared__ int rlen[kBucket];
+    __shared__ int rbeg[kBucket];
     __shared__ int sorted[kOneList];
     __shared__ int part[kIndexThreads / kWave];
     const int lin = xcd_item(a.npairs * a.nb);
@@ -325,6 +340,9 @@ __global__ __launch_bounds__(kIndexThreads) void long_index_sort_kernel(LongInde
     for (int j = threadIdx.x; j < nr; j += kIndexThreads) {
         a.beg[(size_t)pair * n + jlo + j] = (int)(gbase + cnt[j]);
         a.len[(size_t)pair * n + jlo + j] = rlen[j];
+        rbeg[j] = cnt[j];
+        if (a.head)   // slots the placement below leaves empty
+            for (int t = rlen[j]; t < 4; ++t) a.head[((size_t)pair * n + jlo + j) * 4 + t] = -1;
     }
     __syncthreads();
     const bool staged = ne <= kOneList;
@@ -338,9 +356,12 @@ __global__ __launch_bounds__(kIndexThreads) void long_index_sort_kernel(LongInde
 #pragma unroll
         for (int u = 0; u < kUnroll; ++u) {
             if (p0 + u * kIndexThreads + (int)threadIdx.x >= ne) continue;
-            const int pos = atomicAdd(&cnt[v[u].y - jlo], 1);
+            const int rw = v[u].y - jlo;
+            const int pos = atomicAdd(&cnt[rw], 1);
             if (staged) sorted[pos] = v[u].x;
             else a.list[gbase + pos] = v[u].x;
+            if (a.head && pos - rbeg[rw] < 4)
+                a.head[((size_t)pair * n + jlo + rw) * 4 + (pos - rbeg[rw])] = v[u].x;
         }
     }
     __syncthreads();
@@ -357,7 +378,7 @@ bool edge_index_supported(int n, int s) {
 bool edge_index_one_pass(int n) { return n <= kOneRows; }
 
 hipError_t launch_edge_index(int B, int n, int hkv, const int32_t* idx, const float* w, int s,
-                             int* beg, int* len, int* list, hipStream_t st) {
+                             int* beg, int* len, int* list, int* head, hipStream_t st) {
     if (n > kOneRows || s > kSlotMax) return hipErrorInvalidValue;
     IndexArgs a;
     a.idx = idx; a.w = w; a.n = n; a.hkv = hkv; a.s = s;
@@ -365,7 +386,7 @@ hipError_t launch_edge_index(int B, int n, int hkv, const int32_t* idx, const fl
     // two target halves per pair when there are few pairs (parallelism)
     a.K = a.npairs < 256 && n >= 2 ? 2 : 1;
     a.vec = s == 4 && (((uintptr_t)idx | (uintptr_t)w) & 15) == 0;
-    a.beg = beg; a.len = len; a.list = list;
+    a.beg = beg; a.len = len; a.list = list; a.head = head;
     const dim3 grid((unsigned)(a.npairs * a.K));
     if (a.vec)
         hipLaunchKernelGGL(edge_index_one_kernel<true>, grid, dim3(kIndexThreads), 0, st, a);
@@ -375,8 +396,8 @@ hipError_t launch_edge_index(int B, int n, int hkv, const int32_t* idx, const fl
 }
 
 hipError_t launch_edge_index_long(int B, int n, int hkv, const int32_t* idx, const float* w,
-                                  int s, int* beg, int* len, int* list, int* counts, int* offs,
-                                  int* tot, int2* stage, hipStream_t st) {
+                                  int s, int* beg, int* len, int* list, int* head, int* counts,
+                                  int* offs, int* tot, int2* stage, hipStream_t st) {
     LongIndexArgs a;
     a.idx = idx; a.w = w; a.n = n; a.hkv = hkv; a.s = s;
     a.npairs = B * hkv;
@@ -388,7 +409,7 @@ hipError_t launch_edge_index_long(int B, int n, int hkv, const int32_t* idx, con
     a.offs = offs;
     a.tot = tot;
     a.stage = stage;
-    a.beg = beg; a.len = len; a.list = list;
+    a.beg = beg; a.len = len; a.list = list; a.head = head;
     const dim3 gpass((unsigned)(a.npairs * a.nch)), th(kIndexThreads);
     if (a.vec) hipLaunchKernelGGL((long_index_pass_kernel<true, false>), gpass, th, 0, st, a);
     else hipLaunchKernelGGL((long_index_pass_kernel<false, false>), gpass, th, 0, st, a);

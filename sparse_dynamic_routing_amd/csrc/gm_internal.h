@@ -53,12 +53,13 @@ bool edge_index_one_pass(int n);
 // The same index for n > 4096 (s <= 4, n <= 2^20) in four passes without
 // per-edge global atomics: counts and offs need B*hkv * ceil(n/512) *
 // ceil(n/4096) ints each (at most B*n*hkv), tot B*hkv ints, stage B*n*hkv*s
-// int2 entries.
+// int2 entries.  Both write, when head is not null, each row's first four
+// list entries (-1 padded) to head[4 * pair-major row].
 hipError_t launch_edge_index_long(int B, int n, int hkv, const int32_t* idx, const float* w,
-                                  int s, int* beg, int* len, int* list, int* counts, int* offs,
-                                  int* tot, int2* stage, hipStream_t st);
+                                  int s, int* beg, int* len, int* list, int* head, int* counts,
+                                  int* offs, int* tot, int2* stage, hipStream_t st);
 hipError_t launch_edge_index(int B, int n, int hkv, const int32_t* idx, const float* w, int s,
-                             int* beg, int* len, int* list, hipStream_t st);
+                             int* beg, int* len, int* list, int* head, hipStream_t st);
 
 // Workspace of the pull-style SER backward (reverse index of leg 1).
 size_t ser_backward_pull_bytes(long long rows, int s2);

@@ -47,10 +47,11 @@ struct Workspace {
     int* list;      // [U * s]  edge ids grouped by target row
     int* beg;       // [U]  per K/V row in pair-major order: first list slot
     int* len;       // [U]  ... and number of incoming edges
+    int* head;      // [U * 4]  per row in pair-major order: its first 4 edge ids, -1 padded
 };
 
 struct WsLayout {
-    size_t coef, cnt, off, bsum, list, beg, len, total;
+    size_t coef, cnt, off, bsum, list, beg, len, head, total;
 };
 
 WsLayout ws_layout(long long U, int s, int G) {
@@ -62,7 +63,8 @@ WsLayout ws_layout(long long U, int s, int G) {
     l.list = l.bsum + align256((size_t)((U + kScanPerBlock - 1) / kScanPerBlock) * sizeof(int));
     l.beg = l.list + align256((size_t)U * s * sizeof(int));
     l.len = l.beg + align256((size_t)U * sizeof(int));
-    l.total = l.len + align256((size_t)U * sizeof(int));
+    l.head = l.len + align256((size_t)U * sizeof(int));
+    l.total = l.head + align256((size_t)U * 4 * sizeof(int));
     return l;
 }
 
@@ -669,6 +671,86 @@ __global__ __launch_bounds__(kBlock) void sea_bwd_dst_fast_kernel(SeaBwdFast a) 
     }
 }
 
+// Target pass, dispatched rather than persistent: the workgroups of XCD x
+// take the items of x's list in order, one item per P 16-lane rows, so the
+// hardware dispatcher, which starts workgroups in order as others retire,
+// keeps each XCD's working window inside about one pair however unevenly
+// the in-degrees fall (a persistent grid's teams drift apart and spread the
+// window over two pairs, whose gathered rows do not fit one L2).  The row's
+// first edge ids come from its head record, loaded together with its
+// length, so a team waits on two round trips (ids, then the gathered rows);
+// further passes load their ids before waiting on the current gathers.
+template <typename T, int G, int P>
+__global__ __launch_bounds__(kBlock) void sea_bwd_dst_row_kernel(SeaBwdFast a) {
+    using A = typename io<T>::acc;
+    constexpr int V = io<T>::V;
+    constexpr int ROW = 256;
+    constexpr int FROW = ROW * 4 / (int)sizeof(T);
+    constexpr int L = V / P;
+    static_assert(P == 2 || P == 4, "two or four 16-lane rows per target row");
+    const int lane = threadIdx.x & (kWave - 1);
+    const int r = lane & 15;
+    const int row = lane >> 4;
+    const int slot = row & (P - 1);
+    constexpr int TPW = 4 / P;   // rows per wavefront, one per 16P lanes
+    const int x = blockIdx.x % kXcds;
+    const int q = ((int)(blockIdx.x / kXcds) * (kBlock / kWave) + (int)threadIdx.x / kWave) * TPW +
+                  row / P;
+    const int nseg_x = x < a.sp.nseg ? (a.sp.nseg - x + kXcds - 1) / kXcds : 0;
+    if (q >= nseg_x * a.sp.L) return;
+    const Pos pos = pos_of(a.sp, x, q);
+    const int h = pos.unit - pos.bi * a.hkv;
+    int eid = a.ws.head[(size_t)pos.prow * 4 + slot];
+    const int beg = a.ws.beg[pos.prow];
+    const int len = a.ws.len[pos.prow];
+    if (slot >= len) eid = -1;
+    const uint32_t qbase = (uint32_t)h * G;
+
+    A ak[V], av[V];
+#pragma unroll
+    for (int e = 0; e < V; ++e) { ak[e] = 0; av[e] = 0; }
+    for (int p0 = 0;;) {
+        uint4 qr[G], dr[G];
+        float2 co[G];
+        if (eid >= 0) {
+            const int src = (int)fdiv((uint32_t)eid, a.fd_s);      // source unit
+            const int sbi = (int)fdiv((uint32_t)src, a.fd_hkv);    // its b*n + i
+            const uint32_t qrow = (uint32_t)sbi * a.hq + qbase;
+            const float2* cf = a.ws.coef + (size_t)eid * G;
+#pragma unroll
+            for (int g = 0; g < G; ++g) {
+                qr[g] = *reinterpret_cast<const uint4*>(a.q + (qrow + g) * ROW + r * 16);
+                dr[g] = *reinterpret_cast<const uint4*>(a.dout + (qrow + g) * ROW + r * 16);
+                co[g] = cf[g];
+            }
+        }
+        const int pn = p0 + P;
+        const int enext = pn + slot < len ? a.ws.list[beg + pn + slot] : -1;
+        if (eid >= 0) {
+#pragma unroll
+            for (int g = 0; g < G; ++g) {
+                A qf[V], df[V];
+                unpack16<A, V>(qr[g], qf);
+                unpack16<A, V>(dr[g], df);
+#pragma unroll
+                for (int e = 0; e < V; ++e) {
+                    ak[e] += (A)co[g].x * qf[e];
+                    av[e] += (A)co[g].y * df[e];
+                }
+            }
+        }
+        if (pn >= len) break;
+        p0 = pn;
+        eid = enext;
+    }
+    rows_reduce_scatter<P, V>(ak);
+    rows_reduce_scatter<P, V>(av);
+    const uint32_t o = (uint32_t)pos.unit * FROW + r * 16 * 4 / (int)sizeof(T) +
+                       rs_offset<V, P>(row) * 4;
+    store_f32_nt<L>(a.dk + o, ak);
+    store_f32_nt<L>(a.dv + o, av);
+}
+
 void launch_index(const SeaBwdArgs& a, long long E, hipStream_t st) {
     const unsigned sblocks = (unsigned)((a.U + kScanPerBlock - 1) / kScanPerBlock);
     hipLaunchKernelGGL(scan_local_kernel, dim3(sblocks), dim3(1024), 0, st,
@@ -721,7 +803,7 @@ hipError_t run_fast(const SeaBwdArgs& g, const SeaBwdFast& a, long long E, hipSt
         // the coefficient buffer, which the source pass writes afterwards
         const hipError_t e = launch_edge_index_long(
             a.U / (a.n * a.hkv), a.n, a.hkv, a.idx, a.w, a.s, a.ws.beg, a.ws.len, a.ws.list,
-            a.ws.cnt, a.ws.off, a.ws.bsum, reinterpret_cast<int2*>(a.ws.coef), st);
+            a.ws.head, a.ws.cnt, a.ws.off, a.ws.bsum, reinterpret_cast<int2*>(a.ws.coef), st);
         if (e != hipSuccess) return e;
         const void* fn = reinterpret_cast<const void*>(&sea_bwd_src_row_kernel<T, G, S, VEC, false>);
         hipLaunchKernelGGL((sea_bwd_src_row_kernel<T, G, S, VEC, false>),
@@ -731,8 +813,16 @@ hipError_t run_fast(const SeaBwdArgs& g, const SeaBwdFast& a, long long E, hipSt
         hipLaunchKernelGGL((sea_bwd_src_row_kernel<T, G, S, VEC, false>),
                            dim3(persistent_grid(fn, a.U, kBlock / 16)), dim3(kBlock), 0, st, a);
         const hipError_t e = launch_edge_index(a.U / (a.n * a.hkv), a.n, a.hkv, a.idx, a.w, a.s,
-                                               a.ws.beg, a.ws.len, a.ws.list, st);
+                                               a.ws.beg, a.ws.len, a.ws.list, a.ws.head, st);
         if (e != hipSuccess) return e;
+    }
+    if (!a.global_index) {
+        const long long per_x = (long long)((a.sp.nseg + kXcds - 1) / kXcds) * a.sp.L;
+        const long long rows_per_block = kBlock / kWave * (4 / PD);
+        const long long blocks = kXcds * ((per_x + rows_per_block - 1) / rows_per_block);
+        hipLaunchKernelGGL((sea_bwd_dst_row_kernel<T, G, PD>), dim3((unsigned)blocks),
+                           dim3(kBlock), 0, st, a);
+        return hipGetLastError();
     }
     const int ndst = persistent_grid(reinterpret_cast<const void*>(
                                          &sea_bwd_dst_fast_kernel<T, G, PD>),
@@ -793,6 +883,7 @@ hipError_t launch_sea_backward(int B, int n, int hq, int hkv, int d, bool bf16, 
     a.ws.list = reinterpret_cast<int*>(base + l.list);
     a.ws.beg = reinterpret_cast<int*>(base + l.beg);
     a.ws.len = reinterpret_cast<int*>(base + l.len);
+    a.ws.head = reinterpret_cast<int*>(base + l.head);
     const long long E = (long long)a.U * s;
     if (sea_fast_shape(B, n, hq, hkv, d, bf16, s) &&
         (long long)B * n * hq * d * 4 < (1ll << 32)) {
