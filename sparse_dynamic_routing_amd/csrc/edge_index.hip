@@ -5,7 +5,10 @@
 // Counting sorts in LDS; no per-edge global atomics (device-scope atomics on
 // this multi-XCD part are slow, and a returning one per edge bounds the
 // build).  n <= 4096: one 1024-thread workgroup per (pair, target half)
-// loads the pair's edges once and sorts its half in LDS.  Longer sequences:
+// loads the pair's edges once and sorts its half in LDS; the edges come
+// either from idx/w (rows of all KV heads interleaved, 16 bytes used per
+// 128-byte line) or from a compact per-pair copy of the live targets that
+// the SEA backward's source pass writes as it goes.  Longer sequences:
 // a bucket partition, then an LDS sort per bucket (below).  The pair's list
 // occupies the fixed range [pair * n * s, (pair + 1) * n * s); beg and len
 // are indexed by the pair-major row pair * n + j.  The order of edges inside
@@ -24,6 +27,7 @@ constexpr int kSlotMax = 4;        // fast loads for s <= 4
 struct IndexArgs {
     const int32_t* idx;
     const float* w;
+    const int* tgt;   // pair-major live targets (-1 dead) instead of idx/w, or null
     int n, hkv, s, K, npairs, vec;
     int* beg;
     int* len;
@@ -66,7 +70,23 @@ __global__ __launch_bounds__(kIndexThreads) void edge_index_one_kernel(IndexArgs
         const bool ok = iv < n;
         const int i = ok ? iv : n - 1;
         const int e0 = ((b * n + i) * hkv + h) * s;
-        if constexpr (VEC) {
+        if (a.tgt) {
+            // compact rows: the live targets of this pair, contiguous per token
+            const int* tr = a.tgt + (size_t)(pair * n + i) * s;
+            if constexpr (VEC) {
+                const int4 t4 = *reinterpret_cast<const int4*>(tr);
+                tj[k * 4 + 0] = t4.x; tj[k * 4 + 1] = t4.y;
+                tj[k * 4 + 2] = t4.z; tj[k * 4 + 3] = t4.w;
+            } else {
+#pragma unroll
+                for (int t = 0; t < kSlotMax; ++t) tj[k * kSlotMax + t] = tr[t < s ? t : s - 1];
+            }
+#pragma unroll
+            for (int t = 0; t < kSlotMax; ++t) {
+                const int sl = k * kSlotMax + t;
+                te[sl] = ok && t < s && tj[sl] >= 0 ? e0 + t : -1;
+            }
+        } else if constexpr (VEC) {
             const int4 j4 = *reinterpret_cast<const int4*>(a.idx + e0);
             const float4 w4 = *reinterpret_cast<const float4*>(a.w + e0);
             tj[k * 4 + 0] = j4.x; tj[k * 4 + 1] = j4.y;
@@ -378,14 +398,16 @@ bool edge_index_supported(int n, int s) {
 bool edge_index_one_pass(int n) { return n <= kOneRows; }
 
 hipError_t launch_edge_index(int B, int n, int hkv, const int32_t* idx, const float* w, int s,
-                             int* beg, int* len, int* list, int* head, hipStream_t st) {
+                             const int* tgt, int* beg, int* len, int* list, int* head,
+                             hipStream_t st) {
     if (n > kOneRows || s > kSlotMax) return hipErrorInvalidValue;
     IndexArgs a;
-    a.idx = idx; a.w = w; a.n = n; a.hkv = hkv; a.s = s;
+    a.idx = idx; a.w = w; a.tgt = tgt; a.n = n; a.hkv = hkv; a.s = s;
     a.npairs = B * hkv;
     // two target halves per pair when there are few pairs (parallelism)
     a.K = a.npairs < 256 && n >= 2 ? 2 : 1;
-    a.vec = s == 4 && (((uintptr_t)idx | (uintptr_t)w) & 15) == 0;
+    a.vec = s == 4 && (tgt ? ((uintptr_t)tgt & 15) == 0
+                           : (((uintptr_t)idx | (uintptr_t)w) & 15) == 0);
     a.beg = beg; a.len = len; a.list = list; a.head = head;
     const dim3 grid((unsigned)(a.npairs * a.K));
     if (a.vec)

@@ -58,8 +58,11 @@ bool edge_index_one_pass(int n);
 hipError_t launch_edge_index_long(int B, int n, int hkv, const int32_t* idx, const float* w,
                                   int s, int* beg, int* len, int* list, int* head, int* counts,
                                   int* offs, int* tot, int2* stage, hipStream_t st);
+// tgt, when not null, holds the live targets per pair-major source row
+// (tgt[row * s + t], -1 for a dead slot) and replaces idx and w.
 hipError_t launch_edge_index(int B, int n, int hkv, const int32_t* idx, const float* w, int s,
-                             int* beg, int* len, int* list, int* head, hipStream_t st);
+                             const int* tgt, int* beg, int* len, int* list, int* head,
+                             hipStream_t st);
 
 // Workspace of the pull-style SER backward (reverse index of leg 1).
 size_t ser_backward_pull_bytes(long long rows, int s2);

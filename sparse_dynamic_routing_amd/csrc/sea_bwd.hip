@@ -48,10 +48,11 @@ struct Workspace {
     int* beg;       // [U]  per K/V row in pair-major order: first list slot
     int* len;       // [U]  ... and number of incoming edges
     int* head;      // [U * 4]  per row in pair-major order: its first 4 edge ids, -1 padded
+    int* tgt;       // [U * s]  per source row in pair-major order: target of each slot, -1 dead
 };
 
 struct WsLayout {
-    size_t coef, cnt, off, bsum, list, beg, len, head, total;
+    size_t coef, cnt, off, bsum, list, beg, len, head, tgt, total;
 };
 
 WsLayout ws_layout(long long U, int s, int G) {
@@ -64,7 +65,8 @@ WsLayout ws_layout(long long U, int s, int G) {
     l.beg = l.list + align256((size_t)U * s * sizeof(int));
     l.len = l.beg + align256((size_t)U * sizeof(int));
     l.head = l.len + align256((size_t)U * sizeof(int));
-    l.total = l.head + align256((size_t)U * 4 * sizeof(int));
+    l.tgt = l.head + align256((size_t)U * 4 * sizeof(int));
+    l.total = l.tgt + align256((size_t)U * s * sizeof(int));
     return l;
 }
 
@@ -403,6 +405,7 @@ struct SeaBwdFast {
     FastDiv fd_s, fd_hkv;
     SegPlan sp;
     int global_index;   // 1: in-degrees counted here, offsets from the global scan
+    int write_tgt;      // 1: the source pass writes ws.tgt for the single-pass index
     int vec;            // s == 4 and 16-byte aligned edge rows: one load per row
 };
 
@@ -581,6 +584,12 @@ __global__ __launch_bounds__(kBlock) void sea_bwd_src_row_kernel(SeaBwdFast a) {
                 for (int g = 0; g < G; ++g) cp[g] = make_float2((float)my_dl[g], (float)my_p[g]);
             }
             a.dw[my_e] = (float)my_dw;
+            if (a.write_tgt) {
+                int my_j = cur.j[0];
+#pragma unroll
+                for (int t = 1; t < S; ++t) my_j = r == t ? cur.j[t] : my_j;
+                a.ws.tgt[(size_t)cur.pos.prow * a.s + r] = my_live ? my_j : -1;
+            }
         }
         cur = nxt;
     }
@@ -813,7 +822,8 @@ hipError_t run_fast(const SeaBwdArgs& g, const SeaBwdFast& a, long long E, hipSt
         hipLaunchKernelGGL((sea_bwd_src_row_kernel<T, G, S, VEC, false>),
                            dim3(persistent_grid(fn, a.U, kBlock / 16)), dim3(kBlock), 0, st, a);
         const hipError_t e = launch_edge_index(a.U / (a.n * a.hkv), a.n, a.hkv, a.idx, a.w, a.s,
-                                               a.ws.beg, a.ws.len, a.ws.list, a.ws.head, st);
+                                               a.ws.tgt, a.ws.beg, a.ws.len, a.ws.list,
+                                               a.ws.head, st);
         if (e != hipSuccess) return e;
     }
     if (!a.global_index) {
@@ -884,6 +894,7 @@ hipError_t launch_sea_backward(int B, int n, int hq, int hkv, int d, bool bf16, 
     a.ws.beg = reinterpret_cast<int*>(base + l.beg);
     a.ws.len = reinterpret_cast<int*>(base + l.len);
     a.ws.head = reinterpret_cast<int*>(base + l.head);
+    a.ws.tgt = reinterpret_cast<int*>(base + l.tgt);
     const long long E = (long long)a.U * s;
     if (sea_fast_shape(B, n, hq, hkv, d, bf16, s) &&
         (long long)B * n * hq * d * 4 < (1ll << 32)) {
@@ -899,6 +910,7 @@ hipError_t launch_sea_backward(int B, int n, int hq, int hkv, int d, bool bf16, 
         f.fd_s = make_fastdiv((uint32_t)s);
         make_seg_plan(f.sp, B, n, hkv);
         f.global_index = !edge_index_supported(n, s);
+        f.write_tgt = !f.global_index && edge_index_one_pass(n);
         f.vec = s == 4 && (((uintptr_t)idx | (uintptr_t)w) & 15) == 0;
         return bf16 ? dispatch_fast<bf16_t>(a, f, G, E, st) : dispatch_fast<float>(a, f, G, E, st);
     }

@@ -943,7 +943,7 @@ hipError_t launch_ser_backward(int B, int n, int hkv, const int32_t* idx1, const
         int* beg = reinterpret_cast<int*>(ws1);
         int* len = beg + rows;
         int* list = len + rows;
-        hipError_t e = launch_edge_index(B, n, hkv, idx1, w1, s2, beg, len, list, nullptr, st);
+        hipError_t e = launch_edge_index(B, n, hkv, idx1, w1, s2, nullptr, beg, len, list, nullptr, st);
         if (e != hipSuccess) return e;
         SerPullArgs pa{idx1, w1, idx2, w2, idx_out, w_out, dw_out, dw1, dw2, beg, len, list,
                        n, hkv, s1, s2, s3, (int)rows, (int)aliased,
