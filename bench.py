@@ -2,8 +2,8 @@
 
 One step = one pass of the whole hot path over one batch of synthetic input:
   gm_ser_forward   A' = Sparsify_4(A A)             (16 two-hop candidates)
-  gm_sea_forward   o = SEA(q, k, v, A')
-  gm_sea_backward  dq, dk, dv, dw' from dout
+  gm_sea_forward   o = SEA(q, k, v, A'), saving p / w per slot (32 B/unit)
+  gm_sea_backward  dq, dk, dv, dw' from dout and the saved p / w
   gm_ser_backward  dw (both legs are A, so both contributions land in dw)
 on B=8 sequences of n=4096 tokens, 16 query / 8 KV heads, d=128, bf16
 activations, fp32 edges and gradients, edges half local (previous 64
@@ -46,11 +46,13 @@ PEAK_HBM_GBS = 8000.0
 
 # Algorithmic (compulsory) bytes per unit: every input byte read once, every
 # output byte written once; K/V counted once per unit (unique rows).
-# G = 2 query heads per KV head, d = 128, bf16 activations, fp32 gradients.
+# G = 2 query heads per KV head, d = 128, bf16 activations, fp32 gradients;
+# the forward's saved p / w (G * s1 fp32) is written once and read once.
 BYTES_PER_UNIT = {
     "gm_ser_forward": 32 + 32,                          # A row + A' row
-    "gm_sea_forward": 512 + 32 + 512 + 512,             # q, A', K+V, o
-    "gm_sea_backward": 512 + 512 + 32 + 512 + 1024 + 16 + 1024,  # q dO A' KV dq dw' dK dV
+    "gm_sea_forward": 512 + 32 + 512 + 512 + 32,        # q, A', K+V, o, p / w
+    "gm_sea_backward": 512 + 512 + 32 + 512 + 32 + 1024 + 16 + 1024,
+    #                  q    dO    A'   KV  p/w   dq   dw'   dK dV
     "gm_ser_backward": 32 + 32 + 16 + 16,               # A, A', dw', dw
 }
 CALLS = list(BYTES_PER_UNIT)
@@ -78,11 +80,14 @@ CONFIG_STAGES = {
 
 
 def stage_bytes(stage: str, p: synth.Preset) -> int:
-    """Compulsory bytes per unit of one stage (edges: 8 bytes per slot)."""
+    """Compulsory bytes per unit of one stage (edges: 8 bytes per slot; the
+    forward saves p / w, 4 bytes per query head and slot, only when a
+    backward follows)."""
     s1 = p.s1
+    st = 4 * (p.hq // p.hkv) * s1 if p.backward else 0
     return {"ser_fwd": 8 * p.s2 + 8 * s1,
-            "sea_fwd": 512 + 8 * s1 + 512 + 512,
-            "sea_bwd": 512 + 512 + 8 * s1 + 512 + 1024 + 4 * s1 + 1024,
+            "sea_fwd": 512 + 8 * s1 + 512 + 512 + st,
+            "sea_bwd": 512 + 512 + 8 * s1 + 512 + st + 1024 + 4 * s1 + 1024,
             "ser_bwd": 8 * p.s2 + 8 * s1 + 4 * s1 + 4 * p.s2}[stage]
 
 
@@ -151,6 +156,9 @@ class Pass:
         self.ia = torch.empty(es, dtype=torch.int32, device="cuda")
         self.wa = torch.empty(es, **f32)
         self.o = torch.empty_like(self.q)
+        # p / w per query head and slot, saved by the forward for the backward
+        self.stats = (torch.empty((p.B, p.hkv, p.n, p.hq // p.hkv, p.s1), **f32)
+                      if p.backward else None)
         self.dq = torch.empty(qs, **f32)
         self.dk = torch.empty(ks, **f32)
         self.dv = torch.empty(ks, **f32)
@@ -177,7 +185,8 @@ class Pass:
             elif st == "sea_fwd":
                 e = (self.ia, self.wa) if n_ser else (self.idx, self.w)
                 out.append(("gm_sea_forward",
-                            lambda e_=e: gm.gm_sea_forward(self.q, self.k, self.v, *e_, self.o)))
+                            lambda e_=e: gm.gm_sea_forward(self.q, self.k, self.v, *e_, self.o,
+                                                           stats=self.stats)))
             elif st == "sea_bwd":
                 out.append(("gm_sea_backward", self.calls()[2]))
             else:
@@ -187,9 +196,11 @@ class Pass:
     def calls(self):
         return [
             lambda: gm.gm_ser_forward(self.idx, self.w, self.idx, self.w, self.ia, self.wa),
-            lambda: gm.gm_sea_forward(self.q, self.k, self.v, self.ia, self.wa, self.o),
+            lambda: gm.gm_sea_forward(self.q, self.k, self.v, self.ia, self.wa, self.o,
+                                      stats=self.stats),
             lambda: gm.gm_sea_backward(self.q, self.k, self.v, self.ia, self.wa, self.dout,
-                                       self.dq, self.dk, self.dv, self.dwa, self.ws_sea),
+                                       self.dq, self.dk, self.dv, self.dwa, self.ws_sea,
+                                       stats=self.stats),
             lambda: gm.gm_ser_backward(self.idx, self.w, self.idx, self.w, self.ia, self.wa,
                                        self.dwa, self.dA, self.dA, self.ws),
         ]

@@ -95,6 +95,13 @@ gm_status gm_ser_forward(int B, int n, int hkv,
  *        idx, w [B][n][hkv][s1]
  *        scale: multiplies q.k (normally 1/sqrt(d))
  *   out  o [B][n][hq][d] dtype dt
+ *        stats [B][hkv][n][hq/hkv][s1] fp32 (KV-head-major, so that each
+ *        pass writes and reads it in contiguous rows), optional (NULL: not
+ *        written; else 16-byte aligned, overlapping nothing): for query
+ *        head hkv_index*G + g, p_t / w_t of every live slot, i.e.
+ *        exp(scale*q.k[idx_t]) / sum_u w_u exp(scale*q.k[idx_u]), and 0 for
+ *        a dead slot.  gm_sea_backward takes it to skip the softmax
+ *        recomputation (and the q reads it needs).
  * o[hq] = sum_t p_t v[idx_t], p = softmax over live slots (w_t > 0) of
  * scale*q.k[idx_t] + ln w_t; a unit with no live slot gets o = 0.
  * Arithmetic is fp32 for bf16 inputs and fp64 for fp32 inputs.
@@ -102,7 +109,7 @@ gm_status gm_ser_forward(int B, int n, int hkv,
 gm_status gm_sea_forward(int B, int n, int hq, int hkv, int d, gm_dtype dt,
                          float scale, const void* q, const void* k, const void* v,
                          const int32_t* idx, const float* w, int s1, void* o,
-                         hipStream_t stream);
+                         float* stats, hipStream_t stream);
 
 /*
  * Bytes of device workspace gm_sea_backward needs for these sizes: per-edge
@@ -115,7 +122,11 @@ size_t gm_sea_backward_workspace_bytes(int B, int n, int hq, int hkv, int s1);
  * Sparse edge attention, backward: chain rule of gm_sea_forward with the
  * indices held fixed (rit.work: indices get no gradient, learning goes
  * through the soft edge weights).
- *   in   q, k, v, idx, w, s1, scale as for the forward; dout [B][n][hq][d] dt
+ *   in   q, k, v, idx, w, s1, scale as for the forward; dout [B][n][hq][d] dt;
+ *        stats: NULL, or what gm_sea_forward wrote for these q, k, idx, w
+ *        and scale (16-byte aligned).  With bf16 inputs the backward then
+ *        takes p_t = stats_t * w_t and dl_t / w_t from it instead of
+ *        recomputing the scores; fp32 inputs always recompute in fp64.
  *   out  dq [B][n][hq][d] fp32, dk, dv [B][n][hkv][d] fp32,
  *        dw [B][n][hkv][s1] fp32; no output may overlap an input.
  *   ws   device workspace of gm_sea_backward_workspace_bytes(...) bytes,
@@ -131,8 +142,8 @@ size_t gm_sea_backward_workspace_bytes(int B, int n, int hq, int hkv, int s1);
 gm_status gm_sea_backward(int B, int n, int hq, int hkv, int d, gm_dtype dt,
                           float scale, const void* q, const void* k, const void* v,
                           const int32_t* idx, const float* w, int s1,
-                          const void* dout, float* dq, float* dk, float* dv,
-                          float* dw, void* workspace, size_t workspace_bytes,
+                          const void* dout, const float* stats, float* dq, float* dk,
+                          float* dv, float* dw, void* workspace, size_t workspace_bytes,
                           hipStream_t stream);
 
 /*

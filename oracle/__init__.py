@@ -56,7 +56,7 @@ class Oracle:
         lib.oracle_sea_forward.argtypes = [
             ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
             ctypes.c_double, _f64p, _f64p, _f64p, _i32p, _f64p, ctypes.c_int,
-            _f64p, _i64p]
+            _f64p, _f64p, _i64p]
         lib.oracle_sea_backward.argtypes = [
             ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
             ctypes.c_double, _f64p, _f64p, _f64p, _i32p, _f64p, ctypes.c_int,
@@ -109,21 +109,24 @@ class Oracle:
         self._check(rc, "ser_forward")
         return (io, wo, we) if exact else (io, wo)
 
-    def sea_forward(self, q, k, v, idx, w, scale=None, count=False):
-        """o [B,n,hq,d] float64 (and the K/V row count if ``count``)."""
+    def sea_forward(self, q, k, v, idx, w, scale=None, count=False, probs=False):
+        """o [B,n,hq,d] float64; with ``probs`` also p [B,n,hq,s] (0 on dead
+        slots); with ``count`` also the K/V row count (last)."""
         q = self._np(q, np.float64); k = self._np(k, np.float64); v = self._np(v, np.float64)
         idx = self._np(idx, np.int32); w = self._np(w, np.float64)
         B, n, hq, d = q.shape
         hkv, s = idx.shape[2], idx.shape[3]
         scale = 1.0 / np.sqrt(d) if scale is None else float(scale)
         o = np.empty_like(q)
+        p = np.empty((B, n, hq, s), np.float64) if probs else None
         rows = ctypes.c_longlong(0)
         rc = self.lib.oracle_sea_forward(
             B, n, hq, hkv, d, scale, self._p(q, _f64p), self._p(k, _f64p),
             self._p(v, _f64p), self._p(idx, _i32p), self._p(w, _f64p), s,
-            self._p(o, _f64p), ctypes.byref(rows))
+            self._p(o, _f64p), self._p(p, _f64p) if probs else None, ctypes.byref(rows))
         self._check(rc, "sea_forward")
-        return (o, rows.value) if count else o
+        out = (o,) + ((p,) if probs else ()) + ((rows.value,) if count else ())
+        return out if len(out) > 1 else o
 
     def sea_backward(self, q, k, v, idx, w, dout, scale=None):
         """(dq, dk, dv, dw) in float64."""

@@ -145,14 +145,15 @@ int oracle_ser_forward(int B, int n, int hkv,
  *   l_t = scale * sum_c q[hq,c] k[idx_t,h,c] + ln w_t
  *   p_t = exp(l_t - max l) / sum_u exp(l_u - max l)
  *   o[hq,c] = sum_t p_t v[idx_t,h,c]
- * A unit with no live slot outputs 0.  kv_rows (may be NULL) receives the
- * number of (unit, slot) key/value rows read, the access count behind the
- * "KV access reduction" finding.
+ * A unit with no live slot outputs 0.  p_out (may be NULL) receives p_t per
+ * (b, i, query head, slot), 0 for dead slots.  kv_rows (may be NULL)
+ * receives the number of (unit, slot) key/value rows read, the access count
+ * behind the "KV access reduction" finding.
  */
 int oracle_sea_forward(int B, int n, int hq, int hkv, int d, double scale,
                        const double* q, const double* k, const double* v,
                        const int32_t* idx, const double* w, int s,
-                       double* o, long long* kv_rows) {
+                       double* o, double* p_out, long long* kv_rows) {
     if (hkv <= 0 || hq % hkv != 0 || s < 1 || d < 1) return ORACLE_ERR_ARGS;
     int G = hq / hkv;
     long long rows_read = 0;
@@ -171,7 +172,10 @@ int oracle_sea_forward(int B, int n, int hq, int hkv, int d, double scale,
             int head = h * G + g;
             const double* qv = q + (((size_t)b * n + i) * hq + head) * d;
             double* ov = o + (((size_t)b * n + i) * hq + head) * d;
+            double* pv = p_out ? p_out + (((size_t)b * n + i) * hq + head) * s : NULL;
             for (int c = 0; c < d; ++c) ov[c] = 0.0;
+            if (pv)
+                for (int t = 0; t < s; ++t) pv[t] = 0.0;
             double mx = -INFINITY;
             int live = 0;
             for (int t = 0; t < s; ++t) {
@@ -191,6 +195,7 @@ int oracle_sea_forward(int B, int n, int hq, int hkv, int d, double scale,
             for (int t = 0; t < s; ++t) {
                 if (!(w[r * s + t] > 0.0)) continue;
                 double p = exp(l[t] - mx) / z;
+                if (pv) pv[t] = p;
                 const double* vv = v + row(b, idx[r * s + t], h, n, hkv) * d;
                 for (int c = 0; c < d; ++c) ov[c] += p * vv[c];
             }

@@ -10,4 +10,5 @@ from .binding import (  # noqa: F401
     EXPORTS, GMError, check_edges, gm_check_edges, gm_sea_backward, gm_sea_forward,
     gm_sea_backward_workspace_bytes, gm_ser_backward, gm_ser_backward_workspace_bytes, gm_ser_forward,
     load, sea_backward, sea_forward, sea_workspace, ser_backward, ser_forward, ser_workspace,
+    stats_as_query_heads,
 )

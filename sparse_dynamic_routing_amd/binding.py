@@ -49,9 +49,9 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib = ctypes.CDLL(path)
     sig = {
         "gm_ser_forward": [_I, _I, _I, _P, _P, _I, _P, _P, _I, _P, _P, _I, _P],
-        "gm_sea_forward": [_I, _I, _I, _I, _I, _I, _F, _P, _P, _P, _P, _P, _I, _P, _P],
+        "gm_sea_forward": [_I, _I, _I, _I, _I, _I, _F, _P, _P, _P, _P, _P, _I, _P, _P, _P],
         "gm_sea_backward_workspace_bytes": [_I, _I, _I, _I, _I],
-        "gm_sea_backward": [_I, _I, _I, _I, _I, _I, _F, _P, _P, _P, _P, _P, _I, _P,
+        "gm_sea_backward": [_I, _I, _I, _I, _I, _I, _F, _P, _P, _P, _P, _P, _I, _P, _P,
                             _P, _P, _P, _P, _P, _Z, _P],
         "gm_ser_backward_workspace_bytes": [_I, _I, _I, _I, _I, _I],
         "gm_ser_backward": [_I, _I, _I, _P, _P, _I, _P, _P, _I, _P, _P, _I, _P, _P, _P,
@@ -120,16 +120,20 @@ def gm_ser_forward(idx1, w1, idx2, w2, idx_out, w_out, stream=None) -> None:
           _ptr(idx_out), _ptr(w_out), s1, _stream(stream))
 
 
-def gm_sea_forward(q, k, v, idx, w, o, scale=None, stream=None) -> None:
+def gm_sea_forward(q, k, v, idx, w, o, scale=None, stream=None, stats=None) -> None:
+    """``stats`` (optional, [B, hkv, n, hq // hkv, s1] fp32) receives p / w
+    per query head and slot."""
     B, n, hq, d = q.shape
     hkv, s1 = idx.shape[2], idx.shape[3]
     _need(q, "q", _ACT)
     _need(k, "k", (q.dtype,), (B, n, hkv, d)); _need(v, "v", (q.dtype,), (B, n, hkv, d))
     _need(idx, "idx", (torch.int32,), (B, n, hkv, s1)); _need(w, "w", (torch.float32,), idx.shape)
     _need(o, "o", (q.dtype,), q.shape)
+    if stats is not None:
+        _need(stats, "stats", (torch.float32,), (B, hkv, n, hq // hkv, s1))
     scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
     _call("gm_sea_forward", B, n, hq, hkv, d, _act_dtype(q), scale, _ptr(q), _ptr(k), _ptr(v),
-          _ptr(idx), _ptr(w), s1, _ptr(o), _stream(stream))
+          _ptr(idx), _ptr(w), s1, _ptr(o), _ptr(stats), _stream(stream))
 
 
 def gm_sea_backward_workspace_bytes(B, n, hq, hkv, s1) -> int:
@@ -137,7 +141,8 @@ def gm_sea_backward_workspace_bytes(B, n, hq, hkv, s1) -> int:
 
 
 def gm_sea_backward(q, k, v, idx, w, dout, dq, dk, dv, dw, workspace, scale=None,
-                    stream=None) -> None:
+                    stream=None, stats=None) -> None:
+    """``stats``: optional, what gm_sea_forward wrote for the same inputs."""
     B, n, hq, d = q.shape
     hkv, s1 = idx.shape[2], idx.shape[3]
     _need(q, "q", _ACT)
@@ -148,10 +153,13 @@ def gm_sea_backward(q, k, v, idx, w, dout, dq, dk, dv, dw, workspace, scale=None
     _need(dk, "dk", (torch.float32,), k.shape); _need(dv, "dv", (torch.float32,), v.shape)
     _need(dw, "dw", (torch.float32,), idx.shape)
     _need(workspace, "workspace", (torch.uint8, torch.float64))
+    if stats is not None:
+        _need(stats, "stats", (torch.float32,), (B, hkv, n, hq // hkv, s1))
     scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
     _call("gm_sea_backward", B, n, hq, hkv, d, _act_dtype(q), scale, _ptr(q), _ptr(k), _ptr(v),
-          _ptr(idx), _ptr(w), s1, _ptr(dout), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dw),
-          _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream))
+          _ptr(idx), _ptr(w), s1, _ptr(dout), _ptr(stats), _ptr(dq), _ptr(dk), _ptr(dv),
+          _ptr(dw), _ptr(workspace), workspace.numel() * workspace.element_size(),
+          _stream(stream))
 
 
 def gm_ser_backward_workspace_bytes(B, n, hkv, s2, s3, aliased) -> int:
@@ -191,10 +199,16 @@ def ser_forward(idx1, w1, idx2, w2, s1, stream=None):
     return idx_out, w_out
 
 
-def sea_forward(q, k, v, idx, w, scale=None, stream=None):
+def sea_forward(q, k, v, idx, w, scale=None, stream=None, save_stats=False):
+    """o, or (o, stats) with ``save_stats`` (stats [B, hkv, n, G, s1]: p / w
+    per query head and slot, for sea_backward)."""
     o = torch.empty_like(q)
-    gm_sea_forward(q, k, v, idx, w, o, scale, stream)
-    return o
+    B, n, hq, _ = q.shape
+    hkv, s1 = idx.shape[2], idx.shape[3]
+    stats = (torch.empty((B, hkv, n, hq // hkv, s1), dtype=torch.float32, device=q.device)
+             if save_stats else None)
+    gm_sea_forward(q, k, v, idx, w, o, scale, stream, stats)
+    return (o, stats) if save_stats else o
 
 
 def sea_workspace(q, idx, device=None) -> torch.Tensor:
@@ -203,14 +217,14 @@ def sea_workspace(q, idx, device=None) -> torch.Tensor:
     return torch.empty(max(nbytes, 256), dtype=torch.uint8, device=device or q.device)
 
 
-def sea_backward(q, k, v, idx, w, dout, scale=None, workspace=None, stream=None):
+def sea_backward(q, k, v, idx, w, dout, scale=None, workspace=None, stream=None, stats=None):
     f32 = dict(dtype=torch.float32, device=q.device)
     dq = torch.empty(q.shape, **f32)
     dk = torch.empty(k.shape, **f32)
     dv = torch.empty(v.shape, **f32)
     dw = torch.empty(idx.shape, **f32)
     ws = sea_workspace(q, idx) if workspace is None else workspace
-    gm_sea_backward(q, k, v, idx, w, dout, dq, dk, dv, dw, ws, scale, stream)
+    gm_sea_backward(q, k, v, idx, w, dout, dq, dk, dv, dw, ws, scale, stream, stats)
     return dq, dk, dv, dw
 
 
@@ -238,3 +252,9 @@ def check_edges(idx, w, stream=None):
     gm_check_edges(idx, w, counts, stream)
     c = counts.cpu()
     return int(c[0]), int(c[1])
+
+
+def stats_as_query_heads(stats: torch.Tensor) -> torch.Tensor:
+    """The saved statistics [B, hkv, n, G, s1] viewed as [B, n, hq, s1]."""
+    B, hkv, n, G, s1 = stats.shape
+    return stats.permute(0, 2, 1, 3, 4).reshape(B, n, hkv * G, s1)

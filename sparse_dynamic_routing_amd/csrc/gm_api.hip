@@ -62,7 +62,7 @@ bool overlaps(const void* a, size_t an, const void* b, size_t bn) {
 
 extern "C" {
 
-int gm_abi_version(void) { return 1; }
+int gm_abi_version(void) { return 2; }
 
 const char* gm_status_string(gm_status s) {
     switch (s) {
@@ -101,22 +101,27 @@ gm_status gm_ser_forward(int B, int n, int hkv, const int32_t* idx1, const float
 
 gm_status gm_sea_forward(int B, int n, int hq, int hkv, int d, gm_dtype dt, float scale,
                          const void* q, const void* k, const void* v, const int32_t* idx,
-                         const float* w, int s1, void* o, hipStream_t stream) {
+                         const float* w, int s1, void* o, float* stats, hipStream_t stream) {
     gm_status st = check_sea(B, n, hq, hkv, d, dt, s1);
     if (st != GM_OK) return st;
     if (empty(B, n, hkv)) return GM_OK;
     if (!q || !k || !v || !o) return GM_ERR_NULL;
     if ((st = check_edge_ptrs(idx, w)) != GM_OK) return st;
-    if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16))
+    if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) ||
+        (stats && !aligned(stats, 16)))
         return GM_ERR_ALIGN;
     const size_t es = dt == GM_BF16 ? 2 : 4;
     const size_t qb = (size_t)B * n * hq * d * es, kb = (size_t)B * n * hkv * d * es;
+    const size_t eb = (size_t)B * n * hkv * s1 * 4, sb = (size_t)B * n * hq * s1 * 4;
     if (overlaps(o, qb, q, qb) || overlaps(o, qb, k, kb) || overlaps(o, qb, v, kb) ||
-        overlaps(o, qb, idx, (size_t)B * n * hkv * s1 * 4) ||
-        overlaps(o, qb, w, (size_t)B * n * hkv * s1 * 4))
+        overlaps(o, qb, idx, eb) || overlaps(o, qb, w, eb))
+        return GM_ERR_ALIAS;
+    if (stats && (overlaps(stats, sb, q, qb) || overlaps(stats, sb, k, kb) ||
+                  overlaps(stats, sb, v, kb) || overlaps(stats, sb, idx, eb) ||
+                  overlaps(stats, sb, w, eb) || overlaps(stats, sb, o, qb)))
         return GM_ERR_ALIAS;
     return hip_status(gm::launch_sea_forward(B, n, hq, hkv, d, dt == GM_BF16, scale, q, k, v,
-                                             idx, w, s1, o, stream));
+                                             idx, w, s1, o, stats, stream));
 }
 
 size_t gm_sea_backward_workspace_bytes(int B, int n, int hq, int hkv, int s1) {
@@ -126,9 +131,9 @@ size_t gm_sea_backward_workspace_bytes(int B, int n, int hq, int hkv, int s1) {
 
 gm_status gm_sea_backward(int B, int n, int hq, int hkv, int d, gm_dtype dt, float scale,
                           const void* q, const void* k, const void* v, const int32_t* idx,
-                          const float* w, int s1, const void* dout, float* dq, float* dk,
-                          float* dv, float* dw, void* workspace, size_t workspace_bytes,
-                          hipStream_t stream) {
+                          const float* w, int s1, const void* dout, const float* stats,
+                          float* dq, float* dk, float* dv, float* dw, void* workspace,
+                          size_t workspace_bytes, hipStream_t stream) {
     gm_status st = check_sea(B, n, hq, hkv, d, dt, s1);
     if (st != GM_OK) return st;
     if (empty(B, n, hkv)) return GM_OK;
@@ -136,27 +141,30 @@ gm_status gm_sea_backward(int B, int n, int hq, int hkv, int d, gm_dtype dt, flo
     if (!q || !k || !v || !dout || !dq || !dk || !dv || !dw) return GM_ERR_NULL;
     if ((st = check_edge_ptrs(idx, w)) != GM_OK) return st;
     if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(dout, 16) ||
-        !aligned(dq, 16) || !aligned(dk, 16) || !aligned(dv, 16) || !aligned(dw, 4))
+        !aligned(dq, 16) || !aligned(dk, 16) || !aligned(dv, 16) || !aligned(dw, 4) ||
+        (stats && !aligned(stats, 16)))
         return GM_ERR_ALIGN;
     const size_t es = dt == GM_BF16 ? 2 : 4;
     const size_t nq = (size_t)B * n * hq * d, nk = (size_t)B * n * hkv * d;
     const size_t ne = (size_t)B * n * hkv * s1;
-    const void* ins[6] = {q, k, v, dout, idx, w};
-    const size_t inb[6] = {nq * es, nk * es, nk * es, nq * es, ne * 4, ne * 4};
+    const size_t ns = (size_t)B * n * hq * s1;
+    const void* ins[7] = {q, k, v, dout, idx, w, stats};
+    const size_t inb[7] = {nq * es, nk * es, nk * es, nq * es, ne * 4, ne * 4,
+                           stats ? ns * 4 : 0};
     const size_t need = gm_sea_backward_workspace_bytes(B, n, hq, hkv, s1);
     if (!workspace || workspace_bytes < need) return GM_ERR_WORKSPACE;
     if (!aligned(workspace, 256)) return GM_ERR_ALIGN;
     const void* outs[5] = {dq, dk, dv, dw, workspace};
     const size_t outb[5] = {nq * 4, nk * 4, nk * 4, ne * 4, need};
     for (int a = 0; a < 5; ++a) {
-        for (int b = 0; b < 6; ++b)
-            if (overlaps(outs[a], outb[a], ins[b], inb[b])) return GM_ERR_ALIAS;
+        for (int b = 0; b < 7; ++b)
+            if (inb[b] && overlaps(outs[a], outb[a], ins[b], inb[b])) return GM_ERR_ALIAS;
         for (int b = a + 1; b < 5; ++b)
             if (overlaps(outs[a], outb[a], outs[b], outb[b])) return GM_ERR_ALIAS;
     }
     return hip_status(gm::launch_sea_backward(B, n, hq, hkv, d, dt == GM_BF16, scale, q, k, v,
-                                              idx, w, s1, dout, dq, dk, dv, dw, workspace,
-                                              stream));
+                                              idx, w, s1, dout, stats, dq, dk, dv, dw,
+                                              workspace, stream));
 }
 
 size_t gm_ser_backward_workspace_bytes(int B, int n, int hkv, int s2, int s3, int aliased) {

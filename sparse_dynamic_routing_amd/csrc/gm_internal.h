@@ -29,14 +29,14 @@ bool sea_fast_shape(int B, int n, int hq, int hkv, int d, bool bf16, int s);
 hipError_t launch_sea_forward(int B, int n, int hq, int hkv, int d, bool bf16, float scale,
                               const void* q, const void* k, const void* v,
                               const int32_t* idx, const float* w, int s, void* o,
-                              hipStream_t st);
+                              float* stats, hipStream_t st);
 
 size_t sea_backward_workspace_bytes(long long U, int s, int G);
 hipError_t launch_sea_backward(int B, int n, int hq, int hkv, int d, bool bf16, float scale,
                                const void* q, const void* k, const void* v,
                                const int32_t* idx, const float* w, int s, const void* dout,
-                               float* dq, float* dk, float* dv, float* dw, void* workspace,
-                               hipStream_t st);
+                               const float* stats, float* dq, float* dk, float* dv, float* dw,
+                               void* workspace, hipStream_t st);
 
 hipError_t launch_ser_backward(int B, int n, int hkv, const int32_t* idx1, const float* w1,
                                int s2, const int32_t* idx2, const float* w2, int s3,

@@ -25,6 +25,8 @@
 //      (rows without incoming edges get zeros), so no zero-fill is needed.
 // Within a segment the edge order depends on the fill's atomics, so the
 // fp32 sums of dk/dv may differ in the last bits between runs.
+#include <type_traits>
+
 #include "gm_common.h"
 #include "gm_internal.h"
 #include "gm_wave.h"
@@ -393,6 +395,7 @@ struct SeaBwdFast {
     const char* k;
     const char* v;
     const char* dout;
+    const float* stats;   // [B][hkv][n][G][s] p / w from the forward, or null
     const int32_t* idx;
     const float* w;
     char* dq;
@@ -437,7 +440,9 @@ __device__ __forceinline__ void store_f32(char* p, const A* x) {
 // the dout.v products are 16-lane DPP sums; the softmax, dl, dq and dw are
 // lane-local.  Lane t < S writes slot t's per-edge coefficients and dw.
 // GLOBAL: also count the in-degree of every K/V row (global index path).
-template <typename T, int G, int S, bool VEC, bool GLOBAL>
+// SAVED: the softmax comes from the forward's p / w statistics (p = stat * w),
+// so q is not read here and no scores are formed.
+template <typename T, int G, int S, bool VEC, bool GLOBAL, bool SAVED>
 __global__ __launch_bounds__(kBlock) void sea_bwd_src_row_kernel(SeaBwdFast a) {
     using A = typename io<T>::acc;
     constexpr int V = io<T>::V;
@@ -509,41 +514,64 @@ __global__ __launch_bounds__(kBlock) void sea_bwd_src_row_kernel(SeaBwdFast a) {
 #pragma unroll
         for (int g0 = 0; g0 < G; g0 += GC) {
             uint4 qr[GC], dr[GC];
+            float st[GC][S];
 #pragma unroll
             for (int g = 0; g < GC; ++g) {
-                qr[g] = load_split_nt<V>(a.q + (qrow + g0 + g) * ROW, r);
+                if constexpr (SAVED) {
+                    const float* sp = a.stats + ((size_t)cur.pos.prow * G + g0 + g) * a.s;
+                    if constexpr (VEC) {
+                        const float4 s4 = *reinterpret_cast<const float4*>(sp);
+                        st[g][0] = s4.x; st[g][1] = s4.y; st[g][2] = s4.z; st[g][3] = s4.w;
+                    } else {
+#pragma unroll
+                        for (int t = 0; t < S; ++t) st[g][t] = sp[t < a.s ? t : a.s - 1];
+                    }
+                } else {
+                    qr[g] = load_split_nt<V>(a.q + (qrow + g0 + g) * ROW, r);
+                }
                 dr[g] = load_split_nt<V>(a.dout + (qrow + g0 + g) * ROW, r);
             }
 #pragma unroll
             for (int g = 0; g < GC; ++g) {
-                A ls[S], l[S], gd[S], M = NEG;
+                A gd[S], p[S], pw[S];
+                if constexpr (SAVED) {
 #pragma unroll
-                for (int t = 0; t < S; ++t) {
-                    ls[t] = row_sum16(dot16<V, A>(qr[g], kr[t])) * c;
-                    gd[t] = row_sum16(dot16<V, A>(dr[g], vr[t]));
-                    l[t] = live[t] ? ls[t] + lw[t] : NEG;
-                    M = l[t] > M ? l[t] : M;
-                }
-                A ex[S], Z = 0;
+                    for (int t = 0; t < S; ++t) {
+                        gd[t] = row_sum16(dot16<V, A>(dr[g], vr[t]));
+                        pw[t] = live[t] ? (A)st[g][t] : (A)0;
+                        p[t] = pw[t] * (A)cur.wt[t];
+                    }
+                } else {
+                    A ls[S], l[S], M = NEG;
 #pragma unroll
-                for (int t = 0; t < S; ++t) {
-                    ex[t] = live[t] ? fast_exp2(l[t] - M) : (A)0;
-                    Z += ex[t];
-                }
-                const A invZ = Z > (A)0 ? fast_rcp(Z) : (A)0;
-                A p[S], gbar = 0;
+                    for (int t = 0; t < S; ++t) {
+                        ls[t] = row_sum16(dot16<V, A>(qr[g], kr[t])) * c;
+                        gd[t] = row_sum16(dot16<V, A>(dr[g], vr[t]));
+                        l[t] = live[t] ? ls[t] + lw[t] : NEG;
+                        M = l[t] > M ? l[t] : M;
+                    }
+                    A ex[S], Z = 0;
 #pragma unroll
-                for (int t = 0; t < S; ++t) {
-                    p[t] = ex[t] * invZ;
-                    gbar += p[t] * gd[t];
+                    for (int t = 0; t < S; ++t) {
+                        ex[t] = live[t] ? fast_exp2(l[t] - M) : (A)0;
+                        Z += ex[t];
+                    }
+                    const A invZ = Z > (A)0 ? fast_rcp(Z) : (A)0;
+#pragma unroll
+                    for (int t = 0; t < S; ++t) {
+                        p[t] = ex[t] * invZ;
+                        // dl / w = exp(l - M) / (Z w) = exp(scale * dot - M) / Z
+                        pw[t] = live[t] ? fast_exp2(ls[t] - M) * invZ : (A)0;
+                    }
                 }
+                A gbar = 0;
+#pragma unroll
+                for (int t = 0; t < S; ++t) gbar += p[t] * gd[t];
                 A dls[S];
 #pragma unroll
                 for (int t = 0; t < S; ++t) {
                     dls[t] = p[t] * (gd[t] - gbar) * sc;
-                    // dl / w = exp(l - M) / (Z w) = exp(scale * dot - M) / Z
-                    const A pw = live[t] ? fast_exp2(ls[t] - M) : (A)0;
-                    dws[t] += pw * invZ * (gd[t] - gbar);
+                    dws[t] += pw[t] * (gd[t] - gbar);
                 }
                 A sel_dl = dls[0], sel_p = p[0];
 #pragma unroll
@@ -798,14 +826,29 @@ hipError_t dispatch_g(const SeaBwdArgs& a, int G, long long E, hipStream_t st) {
     }
 }
 
+template <typename T, int G, int S, bool VEC, bool GLOBAL>
+void launch_src(const SeaBwdFast& a, hipStream_t st) {
+    // the saved statistics replace the recomputed softmax for bf16 inputs;
+    // fp32 inputs keep their fp64 recomputation
+    if (std::is_same<T, bf16_t>::value && a.stats) {
+        const void* fn =
+            reinterpret_cast<const void*>(&sea_bwd_src_row_kernel<T, G, S, VEC, GLOBAL, true>);
+        hipLaunchKernelGGL((sea_bwd_src_row_kernel<T, G, S, VEC, GLOBAL, true>),
+                           dim3(persistent_grid(fn, a.U, kBlock / 16)), dim3(kBlock), 0, st, a);
+    } else {
+        const void* fn =
+            reinterpret_cast<const void*>(&sea_bwd_src_row_kernel<T, G, S, VEC, GLOBAL, false>);
+        hipLaunchKernelGGL((sea_bwd_src_row_kernel<T, G, S, VEC, GLOBAL, false>),
+                           dim3(persistent_grid(fn, a.U, kBlock / 16)), dim3(kBlock), 0, st, a);
+    }
+}
+
 template <typename T, int G, int S, bool VEC, int PD>
 hipError_t run_fast(const SeaBwdArgs& g, const SeaBwdFast& a, long long E, hipStream_t st) {
     if (a.global_index) {
         const hipError_t e = launch_zero_f32(reinterpret_cast<float*>(a.ws.cnt), (size_t)a.U, st);
         if (e != hipSuccess) return e;
-        const void* fn = reinterpret_cast<const void*>(&sea_bwd_src_row_kernel<T, G, S, VEC, true>);
-        hipLaunchKernelGGL((sea_bwd_src_row_kernel<T, G, S, VEC, true>),
-                           dim3(persistent_grid(fn, a.U, kBlock / 16)), dim3(kBlock), 0, st, a);
+        launch_src<T, G, S, VEC, true>(a, st);
         launch_index(g, E, st);
     } else if (!edge_index_one_pass(a.n)) {
         // long sequences: the partitioned index first; its staging area is
@@ -814,13 +857,9 @@ hipError_t run_fast(const SeaBwdArgs& g, const SeaBwdFast& a, long long E, hipSt
             a.U / (a.n * a.hkv), a.n, a.hkv, a.idx, a.w, a.s, a.ws.beg, a.ws.len, a.ws.list,
             a.ws.head, a.ws.cnt, a.ws.off, a.ws.bsum, reinterpret_cast<int2*>(a.ws.coef), st);
         if (e != hipSuccess) return e;
-        const void* fn = reinterpret_cast<const void*>(&sea_bwd_src_row_kernel<T, G, S, VEC, false>);
-        hipLaunchKernelGGL((sea_bwd_src_row_kernel<T, G, S, VEC, false>),
-                           dim3(persistent_grid(fn, a.U, kBlock / 16)), dim3(kBlock), 0, st, a);
+        launch_src<T, G, S, VEC, false>(a, st);
     } else {
-        const void* fn = reinterpret_cast<const void*>(&sea_bwd_src_row_kernel<T, G, S, VEC, false>);
-        hipLaunchKernelGGL((sea_bwd_src_row_kernel<T, G, S, VEC, false>),
-                           dim3(persistent_grid(fn, a.U, kBlock / 16)), dim3(kBlock), 0, st, a);
+        launch_src<T, G, S, VEC, false>(a, st);
         const hipError_t e = launch_edge_index(a.U / (a.n * a.hkv), a.n, a.hkv, a.idx, a.w, a.s,
                                                a.ws.tgt, a.ws.beg, a.ws.len, a.ws.list,
                                                a.ws.head, st);
@@ -871,8 +910,8 @@ size_t sea_backward_workspace_bytes(long long U, int s, int G) {
 hipError_t launch_sea_backward(int B, int n, int hq, int hkv, int d, bool bf16, float scale,
                                const void* q, const void* k, const void* v,
                                const int32_t* idx, const float* w, int s, const void* dout,
-                               float* dq, float* dk, float* dv, float* dw, void* workspace,
-                               hipStream_t st) {
+                               const float* stats, float* dq, float* dk, float* dv, float* dw,
+                               void* workspace, hipStream_t st) {
     const int G = hq / hkv;
     SeaBwdArgs a;
     a.q = q; a.k = k; a.v = v; a.dout = dout; a.idx = idx; a.w = w;
@@ -901,6 +940,7 @@ hipError_t launch_sea_backward(int B, int n, int hq, int hkv, int d, bool bf16, 
         SeaBwdFast f;
         f.q = static_cast<const char*>(q); f.k = static_cast<const char*>(k);
         f.v = static_cast<const char*>(v); f.dout = static_cast<const char*>(dout);
+        f.stats = (s == 4 && ((uintptr_t)stats & 15)) ? nullptr : stats;
         f.idx = idx; f.w = w;
         f.dq = reinterpret_cast<char*>(dq); f.dk = reinterpret_cast<char*>(dk);
         f.dv = reinterpret_cast<char*>(dv); f.dw = dw;

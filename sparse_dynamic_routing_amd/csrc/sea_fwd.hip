@@ -44,6 +44,7 @@ struct SeaFwdArgs {
     const int32_t* idx;
     const float* w;
     void* o;
+    float* stats;   // [B][hkv][n][G][s] p / w per live slot (0 dead), or null
     int n, hq, hkv, d, s, U;
     float scale;
     TeamShape ts;
@@ -65,6 +66,7 @@ __global__ __launch_bounds__(kBlock) void sea_fwd_kernel(SeaFwdArgs a) {
     const int h = unit % a.hkv;
     const int bi = unit / a.hkv;          // b * n + i
     const int b = bi / a.n;
+    const size_t srow = ((size_t)b * a.hkv + h) * a.n + (bi - b * a.n);   // pair-major row
     const size_t d = (size_t)a.d;
     const T* qp = static_cast<const T*>(a.q) + ((size_t)bi * a.hq + (size_t)h * G) * d + r * V;
     T* op = static_cast<T*>(a.o) + ((size_t)bi * a.hq + (size_t)h * G) * d + r * V;
@@ -113,6 +115,9 @@ __global__ __launch_bounds__(kBlock) void sea_fwd_kernel(SeaFwdArgs a) {
             int len;
             const int off = reduce_scatter(ov, tl, R, team, len);
             const A inv = Z > 0 ? (A)1 / Z : (A)0;
+            if (a.stats && r == 0 && t < a.s)
+                a.stats[(srow * G + g) * a.s + t] =
+                    live ? (float)(aexp2(dot * c - M) * inv) : 0.0f;
 #pragma unroll
             for (int e = 0; e < V; ++e) ov[e] *= inv;
             if (storer) store_len(op + g * d + off, ov, len);
@@ -168,6 +173,28 @@ __global__ __launch_bounds__(kBlock) void sea_fwd_kernel(SeaFwdArgs a) {
 #pragma unroll
         for (int e = 0; e < V; ++e) ov[e] *= inv;
         if (storer) store_len(op + g * d + off, ov, len);
+        if (a.stats) {
+            // p / w of every slot needs the final M and Z: the scores again
+#pragma unroll 1
+            for (int ch = 0; ch < a.ts.nchunk; ++ch) {
+                const int t = ch * P + sl;
+                bool live = false;
+                A kr[V];
+#pragma unroll
+                for (int e = 0; e < V; ++e) kr[e] = 0;
+                if (t < a.s && wp[t] > 0.0f) {
+                    live = true;
+                    load16(kp + (kv0 + (size_t)ip[t] * a.hkv) * d, kr);
+                }
+                A dot = 0;
+#pragma unroll
+                for (int e = 0; e < V; ++e) dot += qg[e] * kr[e];
+                dot = sum_bits(dot, 1, R);
+                if (r == 0 && t < a.s)
+                    a.stats[(srow * G + g) * a.s + t] =
+                        live ? (float)(aexp2(dot * c - M) * inv) : 0.0f;
+            }
+        }
     }
 }
 
@@ -184,6 +211,7 @@ struct SeaFwdFast {
     const int32_t* idx;
     const float* w;
     char* o;
+    float* stats;   // [B][hkv][n][G][s] p / w per live slot (0 dead), or null
     int n, hq, hkv, s, U;
     float scale;
     SegPlan sp;
@@ -194,6 +222,7 @@ struct UnitPos {
     int unit;      // (b*n + i)*hkv + h
     int bi;        // b*n + i
     int kvrow0;    // K/V row of token 0 of the pair: b*n*hkv + h
+    int prow;      // pair-major row: (b*hkv + h)*n + i
 };
 
 __device__ __forceinline__ UnitPos unit_pos(const SegPlan& sp, int x, int q) {
@@ -206,6 +235,7 @@ __device__ __forceinline__ UnitPos unit_pos(const SegPlan& sp, int x, int q) {
     p.bi = b * n + i;
     p.unit = p.bi * hkv + h;
     p.kvrow0 = b * n * hkv + h;
+    p.prow = pair * n + i;
     return p;
 }
 
@@ -302,11 +332,11 @@ __global__ __launch_bounds__(kBlock) void sea_fwd_row_kernel(SeaFwdFast a) {
                 qr[g] = load_nt16(a.q + qoff + (g0 + g) * ROW);
 #pragma unroll
             for (int g = 0; g < GC; ++g) {
-                A l[S], M = NEG;
+                A l[S], sd[S], M = NEG;
 #pragma unroll
                 for (int t = 0; t < S; ++t) {
-                    const A dot = row_sum16(dot16<V, A>(qr[g], kr[t]));
-                    l[t] = live[t] ? dot * c + lw[t] : NEG;
+                    sd[t] = row_sum16(dot16<V, A>(qr[g], kr[t])) * c;
+                    l[t] = live[t] ? sd[t] + lw[t] : NEG;
                     M = l[t] > M ? l[t] : M;
                 }
                 A p[S], Z = 0;
@@ -316,6 +346,21 @@ __global__ __launch_bounds__(kBlock) void sea_fwd_row_kernel(SeaFwdFast a) {
                     Z += p[t];
                 }
                 const A inv = Z > (A)0 ? fast_rcp(Z) : (A)0;
+                if (a.stats) {
+                    // lane t < s: p / w of slot t (the backward's softmax
+                    // without q)
+                    A mine = sd[0];
+                    bool ml = live[0];
+#pragma unroll
+                    for (int t = 1; t < S; ++t) {
+                        mine = r == t ? sd[t] : mine;
+                        ml = r == t ? live[t] : ml;
+                    }
+                    if (r < a.s)
+                        __builtin_nontemporal_store(
+                            ml ? (float)(fast_exp2(mine - M) * inv) : 0.0f,
+                            a.stats + ((size_t)cur.pos.prow * G + g0 + g) * a.s + r);
+                }
                 A o[V];
 #pragma unroll
                 for (int e = 0; e < V; ++e) o[e] = 0;
@@ -379,9 +424,9 @@ bool sea_fast_shape(int B, int n, int hq, int hkv, int d, bool bf16, int s) {
 hipError_t launch_sea_forward(int B, int n, int hq, int hkv, int d, bool bf16, float scale,
                               const void* q, const void* k, const void* v,
                               const int32_t* idx, const float* w, int s, void* o,
-                              hipStream_t st) {
+                              float* stats, hipStream_t st) {
     SeaFwdArgs a;
-    a.q = q; a.k = k; a.v = v; a.idx = idx; a.w = w; a.o = o;
+    a.q = q; a.k = k; a.v = v; a.idx = idx; a.w = w; a.o = o; a.stats = stats;
     a.n = n; a.hq = hq; a.hkv = hkv; a.d = d; a.s = s;
     a.U = B * n * hkv;
     a.scale = scale;
@@ -391,6 +436,7 @@ hipError_t launch_sea_forward(int B, int n, int hq, int hkv, int d, bool bf16, f
         SeaFwdFast f;
         f.q = static_cast<const char*>(q); f.k = static_cast<const char*>(k);
         f.v = static_cast<const char*>(v); f.idx = idx; f.w = w; f.o = static_cast<char*>(o);
+        f.stats = stats;
         f.n = n; f.hq = hq; f.hkv = hkv; f.s = s; f.U = a.U; f.scale = scale;
         make_seg_plan(f.sp, B, n, hkv);
         f.vec = s == 4 && (((uintptr_t)idx | (uintptr_t)w) & 15) == 0;

@@ -79,6 +79,30 @@ def ser_backward(idx1, w1, idx2, w2, idx_out, w_out, dw_out):
     return dw1, dw2
 
 
+def sea_probs(q, k, idx, w, scale=None):
+    """Dense attention probabilities P [B, hq, n, n] of the masked causal
+    attention with bias ln W (rows with no live edge are 0)."""
+    q = np.asarray(q, np.float64); k = np.asarray(k, np.float64)
+    B, n, hq, d = q.shape
+    hkv = k.shape[2]
+    G = hq // hkv
+    scale = 1.0 / np.sqrt(d) if scale is None else scale
+    P = np.zeros((B, hq, n, n))
+    for b in range(B):
+        for h in range(hkv):
+            W = adjacency(idx, np.where(w > 0, w, 0.0), b, h, n)
+            with np.errstate(divide="ignore"):
+                bias = np.where(W > 0, np.log(np.where(W > 0, W, 1.0)), -np.inf)
+            for g in range(G):
+                S = scale * q[b, :, h * G + g, :] @ k[b, :, h, :].T + bias
+                mx = S.max(axis=1, keepdims=True)
+                alive = np.isfinite(mx)
+                E = np.where(alive, np.exp(S - np.where(alive, mx, 0.0)), 0.0)
+                Z = E.sum(axis=1, keepdims=True)
+                P[b, h * G + g] = np.where(Z > 0, E / np.where(Z > 0, Z, 1.0), 0.0)
+    return P
+
+
 def sea(q, k, v, idx, w, dout=None, scale=None):
     """Dense masked attention with additive bias ln W; optional backward.
 

@@ -104,8 +104,10 @@ class Inputs:
         self.dout = synth.normal(p.seed, "dout", qs, p.dtype, layer, where) if p.backward else None
 
 
-def run_gpu(inp: Inputs):
-    """One pass of the path on the GPU; returns device tensors by name."""
+def run_gpu(inp: Inputs, stats: bool = False):
+    """One pass of the path on the GPU; returns device tensors by name.  With
+    ``stats`` the forward saves its p / w statistics and the backward uses
+    them."""
     p = inp.p
     out = {}
     idx, w = dev(inp.idx), dev(inp.w)
@@ -115,10 +117,15 @@ def run_gpu(inp: Inputs):
         out["idx"], out["w"] = ia, wa
     else:
         ia, wa = idx, w
-    out["o"] = gm.sea_forward(q, k, v, ia, wa)
+    st = None
+    if stats:
+        out["o"], st = gm.sea_forward(q, k, v, ia, wa, save_stats=True)
+        out["stats"] = st
+    else:
+        out["o"] = gm.sea_forward(q, k, v, ia, wa)
     if p.backward:
         do = dev(inp.dout)
-        dq, dk, dv, dw = gm.sea_backward(q, k, v, ia, wa, do)
+        dq, dk, dv, dw = gm.sea_backward(q, k, v, ia, wa, do, stats=st)
         out.update(dq=dq, dk=dk, dv=dv, dwp=dw)
         if p.ser:
             dA, _ = gm.ser_backward(idx, w, idx, w, ia, wa, dw, aliased=True)
@@ -141,7 +148,9 @@ def run_oracle_pair(inp: Inputs, b: int, h: int):
         ref["idx"], ref["w"] = ia, wa
     else:
         ia, wa = idx, w
-    ref["o"] = orc.sea_forward(q, k, v, ia, wa)
+    ref["o"], ref["p"] = orc.sea_forward(q, k, v, ia, wa, probs=True)
+    ref["live"] = np.repeat(wa > 0, G, axis=2)
+    ref["wq"] = np.repeat(wa, G, axis=2)          # each query head's slot weights
     if p.backward:
         do = pair(host(inp.dout), b, h, G)
         dq, dk, dv, dw = orc.sea_backward(q, k, v, ia, wa, do)
@@ -159,6 +168,12 @@ def compare_pair(p: synth.Preset, got: dict, ref: dict, b: int, h: int):
         assert_ser_match(pair(host(got["idx"]), b, h), pair(host(got["w"]), b, h),
                          ref["idx"], ref["w"])
     assert_close("o", pair(host(got["o"]), b, h, G), ref["o"], X)
+    if "stats" in got:
+        # p / w per slot: times the GPU's own slot weights it is p
+        st = pair(host(gm.stats_as_query_heads(got["stats"])), b, h, G)
+        assert (st[~ref["live"]] == 0).all(), "statistics of dead slots must be 0"
+        wq = np.repeat(pair(host(got["w"]), b, h), G, axis=2) if "w" in got else ref["wq"]
+        assert_close("p (statistics * w)", st * wq, ref["p"], 1e-4)
     if "dq" in ref:
         assert_close("dq", pair(host(got["dq"]), b, h, G), ref["dq"], X)
         assert_close("dk", pair(host(got["dk"]), b, h), ref["dk"], X)

@@ -35,7 +35,7 @@ def test_library_exports_every_declared_call(lib):
     assert set(names) == set(binding.EXPORTS)
     for name in names:
         assert hasattr(lib, name), name
-    assert lib.gm_abi_version() == 1
+    assert lib.gm_abi_version() == 2
 
 
 def test_status_strings(lib):
@@ -73,8 +73,8 @@ def test_sea_argument_checks(lib):
     a, b, c = fake(0x100000), fake(0x200000), fake(0x300000)
     i, w, o = fake(0x400000), fake(0x500000), fake(0x600000)
     f = lib.gm_sea_forward
-    args = lambda hq=16, hkv=8, d=128, dt=1, s=4, q=a, oo=o: (  # noqa: E731
-        8, 4096, hq, hkv, d, dt, 0.1, q, b, c, i, w, s, oo, None)
+    args = lambda hq=16, hkv=8, d=128, dt=1, s=4, q=a, oo=o, st=None: (  # noqa: E731
+        8, 4096, hq, hkv, d, dt, 0.1, q, b, c, i, w, s, oo, st, None)
     assert f(*args(hq=12)) == UNSUP          # hq % hkv != 0
     assert f(*args(hq=24)) == UNSUP          # 3 query heads per KV head
     assert f(*args(d=96)) == UNSUP
@@ -85,22 +85,28 @@ def test_sea_argument_checks(lib):
     assert f(*args(q=None)) == NULL
     assert f(*args(q=fake(0x100008))) == ALIGN
     assert f(*args(oo=a)) == ALIAS           # o on q
+    assert f(*args(st=fake(0x700008))) == ALIGN       # statistics: 16-byte aligned
+    assert f(*args(st=b)) == ALIAS           # statistics on k
     g = lib.gm_sea_backward
     need = lib.gm_sea_backward_workspace_bytes(8, 4096, 16, 8, 4)
     assert need >= 8 * 4096 * 8 * 4 * (2 * 8 + 4)      # coefficients and edge list
     ws = fake(0x40000000)
-    bargs = [8, 4096, 16, 8, 128, 1, 0.1, a, b, c, i, w, 4, fake(0x700000),
+    bargs = [8, 4096, 16, 8, 128, 1, 0.1, a, b, c, i, w, 4, fake(0x700000), None,
              fake(0x800000), fake(0x900000), fake(0xA00000), fake(0xB00000), ws, need, None]
-    bad = list(bargs); bad[15] = None
+    bad = list(bargs); bad[16] = None
     assert g(*bad) == NULL
-    bad = list(bargs); bad[15] = fake(0x900004)
+    bad = list(bargs); bad[16] = fake(0x900004)
     assert g(*bad) == ALIGN
-    bad = list(bargs); bad[14] = b            # dq on k
+    bad = list(bargs); bad[15] = b            # dq on k
     assert g(*bad) == ALIAS
-    bad = list(bargs); bad[19] = need - 1
+    bad = list(bargs); bad[20] = need - 1
     assert g(*bad) == WS
-    bad = list(bargs); bad[18] = fake(0x40000010)
+    bad = list(bargs); bad[19] = fake(0x40000010)
     assert g(*bad) == ALIGN
+    bad = list(bargs); bad[14] = fake(0xC00004)   # statistics misaligned
+    assert g(*bad) == ALIGN
+    bad = list(bargs); bad[14] = fake(0x800000)   # dq on the statistics
+    assert g(*bad) == ALIAS
 
 
 def test_ser_backward_workspace_checks(lib):

@@ -54,20 +54,35 @@ def _sea_inputs(rng, dtype, d, G, s, n, B=2, hkv=2, pad=0.15, dead=0.1):
 @pytest.mark.parametrize("dtype,d,G,s,n", SEA_SHAPES,
                          ids=[f"{str(c[0])[6:]}-d{c[1]}-G{c[2]}-s{c[3]}-n{c[4]}" for c in SEA_SHAPES])
 def test_sea_forward_backward_shapes(dtype, d, G, s, n):
+    """Each shape twice: the backward recomputing the softmax, and taking the
+    forward's p / w statistics (which must also match the oracle's p)."""
     say(f"case sea dtype={dtype} d={d} G={G} s={s} n={n}")
     rng = np.random.default_rng(d * 1000 + G * 100 + s * 10 + n)
     q, k, v, do, idx, w = _sea_inputs(rng, dtype, d, G, s, n)
-    o = gm.sea_forward(dev(q), dev(k), dev(v), dev(idx), dev(w))
-    dq, dk, dv, dw = gm.sea_backward(dev(q), dev(k), dev(v), dev(idx), dev(w), dev(do))
-    torch.cuda.synchronize()
     orc = oracle.get()
     X = TOL[dtype]
-    assert_close("o", host(o), orc.sea_forward(q, k, v, idx, w), X)
+    ro, rp = orc.sea_forward(q, k, v, idx, w, probs=True)
     rdq, rdk, rdv, rdw = orc.sea_backward(q, k, v, idx, w, do)
-    assert_close("dq", host(dq), rdq, X)
-    assert_close("dk", host(dk), rdk, X)
-    assert_close("dv", host(dv), rdv, X)
-    assert_close("dw", host(dw), rdw, X)
+    for with_stats in (False, True):
+        say(f"  stats={with_stats}")
+        st = None
+        if with_stats:
+            o, st = gm.sea_forward(dev(q), dev(k), dev(v), dev(idx), dev(w), save_stats=True)
+        else:
+            o = gm.sea_forward(dev(q), dev(k), dev(v), dev(idx), dev(w))
+        dq, dk, dv, dw = gm.sea_backward(dev(q), dev(k), dev(v), dev(idx), dev(w), dev(do),
+                                         stats=st)
+        torch.cuda.synchronize()
+        assert_close("o", host(o), ro, X)
+        if with_stats:
+            live = np.repeat(w > 0, G, axis=2)
+            hs = host(gm.stats_as_query_heads(st))
+            assert (hs[~live] == 0).all()
+            assert_close("p (statistics * w)", hs * np.repeat(w, G, axis=2), rp, 1e-4)
+        assert_close("dq", host(dq), rdq, X)
+        assert_close("dk", host(dk), rdk, X)
+        assert_close("dv", host(dv), rdv, X)
+        assert_close("dw", host(dw), rdw, X)
 
 
 def test_sea_scale_argument_and_all_padding_rows():
@@ -158,20 +173,25 @@ def test_ser_backward_source_chunks(n):
 
 @pytest.mark.parametrize("n,s", [(4097, 4), (9000, 4), (12289, 3)])
 def test_sea_backward_partitioned_index(n, s):
-    """n > 4096: the reverse edge index is built by target bucket (4096 rows)
+    """n > 4096: the reverse edge index is built by target bucket (512 rows)
     and source chunk (4096 tokens); ragged last bucket and chunk, s = 4 (16-byte
-    edge rows) and s = 3; every output compared."""
+    edge rows) and s = 3; every output compared, with the softmax recomputed
+    and with the forward's statistics."""
     say(f"case sea backward partitioned index n={n} s={s}")
     rng = np.random.default_rng(5000 + n + s)
     dtype = torch.bfloat16
     q, k, v, do, idx, w = _sea_inputs(rng, dtype, 128, 2, s, n, B=1, hkv=2)
-    dq, dk, dv, dw = gm.sea_backward(dev(q), dev(k), dev(v), dev(idx), dev(w), dev(do))
     rdq, rdk, rdv, rdw = oracle.get().sea_backward(q, k, v, idx, w, do)
     X = TOL[dtype]
-    assert_close("dq", host(dq), rdq, X)
-    assert_close("dk", host(dk), rdk, X)
-    assert_close("dv", host(dv), rdv, X)
-    assert_close("dw", host(dw), rdw, X)
+    _, st = gm.sea_forward(dev(q), dev(k), dev(v), dev(idx), dev(w), save_stats=True)
+    for stats in (None, st):
+        say(f"  stats={stats is not None}")
+        dq, dk, dv, dw = gm.sea_backward(dev(q), dev(k), dev(v), dev(idx), dev(w), dev(do),
+                                         stats=stats)
+        assert_close("dq", host(dq), rdq, X)
+        assert_close("dk", host(dk), rdk, X)
+        assert_close("dv", host(dv), rdv, X)
+        assert_close("dw", host(dw), rdw, X)
 
 
 def _unaligned(x: np.ndarray) -> torch.Tensor:

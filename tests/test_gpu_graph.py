@@ -36,6 +36,7 @@ class LayerPass:
         self.ia = torch.empty(idx.shape, dtype=torch.int32, device="cuda")
         self.wa = torch.empty(idx.shape, **f32)
         self.o = torch.empty_like(self.q)
+        self.stats = torch.empty((B, hkv, n, hq // hkv, s), dtype=torch.float32, device="cuda")
         self.dq = torch.empty(qs, **f32)
         self.dk = torch.empty(ks, **f32)
         self.dv = torch.empty(ks, **f32)
@@ -45,14 +46,14 @@ class LayerPass:
         self.ws_ser = gm.ser_workspace(self.idx, self.idx, aliased=True)
 
     def outputs(self):
-        return {"ia": self.ia, "wa": self.wa, "o": self.o, "dq": self.dq, "dk": self.dk,
-                "dv": self.dv, "dwa": self.dwa, "dA": self.dA}
+        return {"ia": self.ia, "wa": self.wa, "o": self.o, "stats": self.stats, "dq": self.dq,
+                "dk": self.dk, "dv": self.dv, "dwa": self.dwa, "dA": self.dA}
 
     def run(self):
         gm.gm_ser_forward(self.idx, self.w, self.idx, self.w, self.ia, self.wa)
-        gm.gm_sea_forward(self.q, self.k, self.v, self.ia, self.wa, self.o)
+        gm.gm_sea_forward(self.q, self.k, self.v, self.ia, self.wa, self.o, stats=self.stats)
         gm.gm_sea_backward(self.q, self.k, self.v, self.ia, self.wa, self.dout, self.dq, self.dk,
-                           self.dv, self.dwa, self.ws_sea)
+                           self.dv, self.dwa, self.ws_sea, stats=self.stats)
         gm.gm_ser_backward(self.idx, self.w, self.idx, self.w, self.ia, self.wa, self.dwa,
                            self.dA, self.dA, self.ws_ser)
 

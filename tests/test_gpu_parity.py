@@ -19,24 +19,29 @@ from gpu_util import (TOL, Inputs, assert_close, assert_ser_match, compare_pair,
 pytestmark = pytest.mark.gpu
 
 
-def test_tiny_preset_whole_chain():
+@pytest.mark.parametrize("stats", [False, True], ids=["recompute", "stats"])
+def test_tiny_preset_whole_chain(stats):
     """tiny: batch 1, n=64, 4 q / 2 KV heads, d=16, fp32, s=2; one SER step
     then SEA forward and backward, then SER backward; all outputs compared."""
     p = synth.PRESETS["tiny"]
-    say(f"case tiny {p}")
+    say(f"case tiny stats={stats} {p}")
     inp = Inputs(p)
-    got = run_gpu(inp)
+    got = run_gpu(inp, stats=stats)
     for b, h in pairs_for(p.B, p.hkv, count=p.B * p.hkv):
         say(f"  pair b={b} h={h}")
         compare_pair(p, got, run_oracle_pair(inp, b, h), b, h)
 
 
-@pytest.mark.parametrize("name", ["sea2", "ser_sea4", "metric", "long64k"])
-def test_full_size_preset_sampled_pairs(name):
+@pytest.mark.parametrize("name,stats", [("sea2", False), ("ser_sea4", True), ("metric", False),
+                                        ("metric", True), ("long64k", True)],
+                         ids=["sea2", "ser_sea4-stats", "metric", "metric-stats", "long64k-stats"])
+def test_full_size_preset_sampled_pairs(name, stats):
+    """stats: the forward saves p / w and the backward uses it (as the
+    measured pass does)."""
     p = synth.PRESETS[name]
-    say(f"case {name} {p}")
+    say(f"case {name} stats={stats} {p}")
     inp = Inputs(p)
-    got = run_gpu(inp)
+    got = run_gpu(inp, stats=stats)
     for b, h in pairs_for(p.B, p.hkv, count=3 if p.n <= 4096 else 2):
         say(f"  pair b={b} h={h}")
         compare_pair(p, got, run_oracle_pair(inp, b, h), b, h)

@@ -32,6 +32,8 @@ MUTANTS = [
      "l[t] = scale * dot + log(wt);", "l[t] = dot + log(wt);"),
     ("sea: interleaved GQA head mapping", "oracle_sea_forward",
      "int head = h * G + g;", "int head = g * hkv + h;"),
+    ("sea: probability reported at the next slot", "oracle_sea_forward",
+     "if (pv) pv[t] = p;", "if (pv) pv[(t + 1) % s] = p;"),
     ("sea bwd: softmax backward sign", "oracle_sea_backward",
      "double dl = p[t] * (gt[t] - gbar);", "double dl = p[t] * (gt[t] + gbar);"),
     ("sea bwd: dk without the score scale", "oracle_sea_backward",
@@ -62,6 +64,7 @@ PINS = [
     pins.test_sea_tiny_config_dense,
     pins.test_sea_forward_backward_match_dense,
     pins.test_sea_single_slot_closed_form,
+    pins.test_sea_slot_probabilities_match_dense,
     pins.test_sea_zero_query_closed_form,
     pins.test_sea_constant_values_and_conservation,
     pins.test_sea_finite_differences,

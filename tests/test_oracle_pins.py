@@ -236,6 +236,36 @@ def test_sea_forward_backward_match_dense(orc):
             np.testing.assert_allclose(a, b_, rtol=1e-10, atol=1e-12)
 
 
+def test_sea_slot_probabilities_match_dense(orc):
+    """The per-slot probabilities the oracle reports: summed over the slots
+    that share a target they are the dense attention probabilities, dead
+    slots get 0, and they rebuild the output o = sum_t p_t v[idx_t]."""
+    rng = np.random.default_rng(37)
+    for case in range(30):
+        hkv = int(rng.integers(1, 3)); G = int(rng.integers(1, 4))
+        B, n, s = int(rng.integers(1, 3)), int(rng.integers(1, 25)), int(rng.integers(1, 6))
+        q, k, v, idx, w, _ = _sea_case(rng, B=B, n=n, hq=hkv * G, hkv=hkv, d=8, s=s,
+                                       pad=0.25 * (case % 3 == 0), ties=bool(case % 2),
+                                       dead=0.2 * (case % 4 == 0))
+        o, p = orc.sea_forward(q, k, v, idx, w, probs=True)
+        P = dense_ref.sea_probs(q, k, idx, w)
+        live = np.repeat(w > 0, G, axis=2)                  # [B, n, hq, s]
+        assert (p[~live] == 0).all()
+        tgt = np.repeat(idx, G, axis=2)
+        for b in range(B):
+            for i in range(n):
+                for hh in range(hkv * G):
+                    acc = {}
+                    for t in range(s):
+                        if live[b, i, hh, t]:
+                            acc[tgt[b, i, hh, t]] = acc.get(tgt[b, i, hh, t], 0.0) + p[b, i, hh, t]
+                    for j, pj in acc.items():
+                        assert abs(pj - P[b, hh, i, j]) <= 1e-12, (case, b, i, hh, j)
+        vg = v[np.arange(B)[:, None, None, None], idx, np.arange(hkv)[None, None, :, None]]
+        ob = np.einsum("bnhgt,bnhtd->bnhgd", p.reshape(B, n, hkv, G, s), vg)
+        np.testing.assert_allclose(ob.reshape(o.shape), o, rtol=1e-12, atol=1e-12)
+
+
 def test_sea_tiny_config_dense(orc):
     p = synth.PRESETS["tiny"]
     idx, w = synth.edges(p.seed, p.B, p.n, p.hkv, p.s1, mode=p.mode)
