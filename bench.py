@@ -21,7 +21,7 @@ FETCH_SIZE + WRITE_SIZE from the committed profile, when it matches the
 kernel sources) against its compulsory bytes.
 
     python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu-baseline] [--no-cold]
-    python bench.py --config {sea2,ser_sea4,stack21,long64k}   (other workloads)
+    python bench.py --config {sea2,ser_sea4,stack21,long64k,theia}   (other workloads)
 """
 from __future__ import annotations
 
@@ -76,6 +76,7 @@ CONFIG_STAGES = {
     "ser_sea4": ["ser_fwd", "sea_fwd"],
     "stack21": ["ser_fwd", "ser_fwd", "sea_fwd"],   # one of the 21 layers
     "long64k": ["ser_fwd", "sea_fwd", "sea_bwd", "ser_bwd"],
+    "theia": ["ser_fwd", "sea_fwd", "sea_bwd", "ser_bwd"],   # (s1, s2, s3) = (2, 4, 4)
 }
 
 

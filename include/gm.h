@@ -164,7 +164,7 @@ size_t gm_ser_backward_workspace_bytes(int B, int n, int hkv, int s2, int s3,
  *        allowed (A' = Sparsify(A A), s2 == s3): the sum of both is written.
  *   ws   device workspace of gm_ser_backward_workspace_bytes(...) bytes,
  *        8-byte aligned (16-byte alignment enables the partial-sum path of
- *        s1 = s2 = s3 = 4, n <= 4096).
+ *        s2 = s3 = 4, s1 = 4 or 2, n <= 4096).
  * For each path (a, c) with w1 > 0 and w2 > 0 whose target equals a
  * retained slot t (w_out_t > 0): dw1[i,a] += dw_out_t w2[j,c] and
  * dw2[j,c] += dw_out_t w1[i,a].  Slots with zero weight get 0.

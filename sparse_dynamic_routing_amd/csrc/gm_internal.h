@@ -66,7 +66,8 @@ hipError_t launch_edge_index(int B, int n, int hkv, const int32_t* idx, const fl
 
 // Workspace of the pull-style SER backward (reverse index of leg 1).
 size_t ser_backward_pull_bytes(long long rows, int s2);
-// fp64 partials of the source-chunk SER backward (s1 = s2 = s3 = 4, n <= 4096)
+// fp64 partials of the source-chunk SER backward (s2 = s3 = 4, s1 = 4 or 2,
+// n <= 4096)
 bool ser_backward_part_fits(int n);
 size_t ser_backward_part_bytes(int B, int n, int hkv);
 

@@ -329,7 +329,7 @@ __global__ __launch_bounds__(kBlock) void ser_fwd_unit_kernel(SerUnitArgs a) {
     }
 }
 
-// ---------------------------------------- s1 = s2 = s3 = 4, aligned rows
+// ------------------------- s2 = s3 = 4 legs, s1 = 4 or 2, aligned rows
 // Straight-line version of the lane-per-unit forward.  Merge: every path
 // weight is added, in path order, to each earlier candidate (the weight when
 // the targets match, else 0.0, which leaves these non-negative sums
@@ -376,7 +376,10 @@ __device__ __forceinline__ void merge_top4(uint64_t* a, const uint64_t* b) {
     cx(a[0], a[1]); cx(a[2], a[3]);
 }
 
+// S1: retained slots (4, or 2 for the narrower top-2-of-16 budget).
+template <int S1>
 __global__ __launch_bounds__(kBlock) void ser_fwd_vec_kernel(SerUnitArgs a) {
+    static_assert(S1 == 2 || S1 == 4, "vector stores of 2 or 4 slots");
     const int u = xcd_unit(a.U);
     if (u < 0) return;
     int m[kCand];
@@ -421,8 +424,15 @@ __global__ __launch_bounds__(kBlock) void ser_fwd_vec_kernel(SerUnitArgs a) {
         om[r] = key[r] ? (int)~(uint32_t)key[r] : 0;
         ow[r] = key[r] ? __uint_as_float((uint32_t)(key[r] >> 32)) : 0.0f;
     }
-    *reinterpret_cast<int4*>(a.idx_out + (size_t)u * 4) = make_int4(om[0], om[1], om[2], om[3]);
-    *reinterpret_cast<float4*>(a.w_out + (size_t)u * 4) = make_float4(ow[0], ow[1], ow[2], ow[3]);
+    if constexpr (S1 == 4) {
+        *reinterpret_cast<int4*>(a.idx_out + (size_t)u * 4) =
+            make_int4(om[0], om[1], om[2], om[3]);
+        *reinterpret_cast<float4*>(a.w_out + (size_t)u * 4) =
+            make_float4(ow[0], ow[1], ow[2], ow[3]);
+    } else {
+        *reinterpret_cast<int2*>(a.idx_out + (size_t)u * 2) = make_int2(om[0], om[1]);
+        *reinterpret_cast<float2*>(a.w_out + (size_t)u * 2) = make_float2(ow[0], ow[1]);
+    }
 }
 
 __global__ __launch_bounds__(kBlock) void ser_bwd_unit_kernel(SerUnitArgs a) {
@@ -606,7 +616,7 @@ __global__ __launch_bounds__(kBlock) void ser_bwd_pull_kernel(SerPullArgs a) {
     }
 }
 
-// ------------------------- SER backward by source chunks, s1 = s2 = s3 = 4
+// -------------- SER backward by source chunks, s2 = s3 = 4, s1 = 4 or 2
 // No reverse index.  Pass 1: one 1024-thread workgroup per (pair, chunk c of
 // 1024 source tokens), one source per thread.  The thread recomputes the
 // gradient of each of its 16 paths from its own rows and adds
@@ -662,12 +672,24 @@ __global__ __launch_bounds__(kSerThreads) void ser_bwd_part_kernel(SerPartArgs a
         load_paths_vec(a.u, u, m, x, y);
         const int4 j4 = *reinterpret_cast<const int4*>(a.u.idx1 + (size_t)u * 4);
         const int j[4] = {j4.x, j4.y, j4.z, j4.w};
-        const int4 m4 = *reinterpret_cast<const int4*>(a.idx_out + (size_t)u * 4);
-        const float4 w4 = *reinterpret_cast<const float4*>(a.w_out + (size_t)u * 4);
-        const float4 g4 = *reinterpret_cast<const float4*>(a.dw_out + (size_t)u * 4);
-        const int mt[kSmax] = {m4.x, m4.y, m4.z, m4.w};
-        const float wt[kSmax] = {w4.x, w4.y, w4.z, w4.w};
-        const float gt[kSmax] = {g4.x, g4.y, g4.z, g4.w};
+        // retained slots of A' (s1 = 4, or 2 with the rest dead)
+        int mt[kSmax];
+        float wt[kSmax], gt[kSmax];
+        if (a.u.s1 == 4) {
+            const int4 m4 = *reinterpret_cast<const int4*>(a.idx_out + (size_t)u * 4);
+            const float4 w4 = *reinterpret_cast<const float4*>(a.w_out + (size_t)u * 4);
+            const float4 g4 = *reinterpret_cast<const float4*>(a.dw_out + (size_t)u * 4);
+            mt[0] = m4.x; mt[1] = m4.y; mt[2] = m4.z; mt[3] = m4.w;
+            wt[0] = w4.x; wt[1] = w4.y; wt[2] = w4.z; wt[3] = w4.w;
+            gt[0] = g4.x; gt[1] = g4.y; gt[2] = g4.z; gt[3] = g4.w;
+        } else {
+            const int2 m2 = *reinterpret_cast<const int2*>(a.idx_out + (size_t)u * 2);
+            const float2 w2 = *reinterpret_cast<const float2*>(a.w_out + (size_t)u * 2);
+            const float2 g2 = *reinterpret_cast<const float2*>(a.dw_out + (size_t)u * 2);
+            mt[0] = m2.x; mt[1] = m2.y; mt[2] = -1; mt[3] = -1;
+            wt[0] = w2.x; wt[1] = w2.y; wt[2] = 0.0f; wt[3] = 0.0f;
+            gt[0] = g2.x; gt[1] = g2.y; gt[2] = 0.0f; gt[3] = 0.0f;
+        }
         double pg[kCand];
 #pragma unroll
         for (int k = 0; k < kCand; ++k)
@@ -887,9 +909,13 @@ hipError_t launch_ser_forward(int B, int n, int hkv, const int32_t* idx1, const 
                       s2 == 4 && s3 == 4 &&
                           (((uintptr_t)idx1 | (uintptr_t)w1 | (uintptr_t)idx2 | (uintptr_t)w2) &
                            15) == 0};
+        const bool out8 = (((uintptr_t)idx_out | (uintptr_t)w_out) & 7) == 0;
         if (s1 == 4 && u.vec_out && u.vec_in)
-            hipLaunchKernelGGL(ser_fwd_vec_kernel, dim3(xcd_unit_grid(u.U)), dim3(kBlock), 0, st,
-                               u);
+            hipLaunchKernelGGL(ser_fwd_vec_kernel<4>, dim3(xcd_unit_grid(u.U)), dim3(kBlock), 0,
+                               st, u);
+        else if (s1 == 2 && out8 && u.vec_in)
+            hipLaunchKernelGGL(ser_fwd_vec_kernel<2>, dim3(xcd_unit_grid(u.U)), dim3(kBlock), 0,
+                               st, u);
         else
             hipLaunchKernelGGL(ser_fwd_unit_kernel, dim3(xcd_unit_grid(u.U)), dim3(kBlock), 0, st,
                                u);
@@ -915,10 +941,12 @@ hipError_t launch_ser_backward(int B, int n, int hkv, const int32_t* idx1, const
                                double* ws2, hipStream_t st) {
     const size_t rows = (size_t)B * n * hkv;
     const bool aliased = dw1 == dw2;
-    const bool vec4 = s1 == 4 && s2 == 4 && s3 == 4 &&
+    // the source-chunk path: legs of 4 slots, A' of 4 or 2, vector-aligned rows
+    const bool vec4 = (s1 == 4 || s1 == 2) && s2 == 4 && s3 == 4 &&
                       (((uintptr_t)idx1 | (uintptr_t)w1 | (uintptr_t)idx2 | (uintptr_t)w2 |
-                        (uintptr_t)idx_out | (uintptr_t)w_out | (uintptr_t)dw_out |
-                        (uintptr_t)dw1 | (uintptr_t)dw2) & 15) == 0;
+                        (uintptr_t)dw1 | (uintptr_t)dw2) & 15) == 0 &&
+                      (((uintptr_t)idx_out | (uintptr_t)w_out | (uintptr_t)dw_out) &
+                       (s1 == 4 ? 15 : 7)) == 0;
     if (vec4 && ser_backward_part_fits(n) && ((uintptr_t)ws1 & 15) == 0) {
         SerPartArgs pa;
         pa.u = SerUnitArgs{idx1, w1, idx2, w2, nullptr, nullptr, nullptr, nullptr, nullptr,

@@ -136,5 +136,9 @@ PRESETS = {
         # the measured layer pass: ser_sea4's shape plus both backwards.
         Preset("metric", 8, 4096, 16, 8, 128, torch.bfloat16, 4, 4, 4, "mixed",
                BASE_SEED + 2, ser=True, backward=True),
+        # the narrower budget (s1, s2, s3) = (2, 4, 4): top-2 of 16 two-hop
+        # candidates, then SEA at s1 = 2; the metric pass's shape otherwise.
+        Preset("theia", 8, 4096, 16, 8, 128, torch.bfloat16, 2, 4, 4, "mixed",
+               BASE_SEED + 5, ser=True, backward=True),
     ]
 }

@@ -33,8 +33,9 @@ def test_tiny_preset_whole_chain(stats):
 
 
 @pytest.mark.parametrize("name,stats", [("sea2", False), ("ser_sea4", True), ("metric", False),
-                                        ("metric", True), ("long64k", True)],
-                         ids=["sea2", "ser_sea4-stats", "metric", "metric-stats", "long64k-stats"])
+                                        ("metric", True), ("long64k", True), ("theia", True)],
+                         ids=["sea2", "ser_sea4-stats", "metric", "metric-stats", "long64k-stats",
+                              "theia-stats"])
 def test_full_size_preset_sampled_pairs(name, stats):
     """stats: the forward saves p / w and the backward uses it (as the
     measured pass does)."""
@@ -47,9 +48,11 @@ def test_full_size_preset_sampled_pairs(name, stats):
         compare_pair(p, got, run_oracle_pair(inp, b, h), b, h)
 
 
-def test_ser_forward_full_size_every_row():
-    """SER forward of the 4096-token, s=4 preset: every row bit-exact."""
-    p = synth.PRESETS["ser_sea4"]
+@pytest.mark.parametrize("name", ["ser_sea4", "theia"])
+def test_ser_forward_full_size_every_row(name):
+    """SER forward of the 4096-token presets (top-4 and top-2 of 16): every
+    row bit-exact."""
+    p = synth.PRESETS[name]
     idx, w = synth.edges(p.seed, p.B, p.n, p.hkv, p.s2, mode=p.mode)
     say(f"case ser_forward full {idx.shape}")
     io, wo = gm.ser_forward(dev(idx), dev(w), dev(idx), dev(w), p.s1)
