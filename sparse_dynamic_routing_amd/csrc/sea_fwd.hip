@@ -324,6 +324,8 @@ __global__ __launch_bounds__(kBlock) void sea_fwd_row_kernel(SeaFwdFast a) {
         A lw[S];
 #pragma unroll
         for (int t = 0; t < S; ++t) lw[t] = live[t] ? fast_log2((A)cur.wt[t]) : NEG;
+        const bool st_one = G * a.s <= 16;   // the unit's statistics in one store
+        float st_val = 0.0f;
 #pragma unroll
         for (int g0 = 0; g0 < G; g0 += GC) {
             uint4 qr[GC];
@@ -347,19 +349,22 @@ __global__ __launch_bounds__(kBlock) void sea_fwd_row_kernel(SeaFwdFast a) {
                 }
                 const A inv = Z > (A)0 ? fast_rcp(Z) : (A)0;
                 if (a.stats) {
-                    // lane t < s: p / w of slot t (the backward's softmax
-                    // without q)
+                    // p / w of slot t (the backward's softmax without q):
+                    // when the unit's G * s values fit the 16 lanes, lane
+                    // g * s + t keeps it for one store per row after the
+                    // heads; otherwise lane t stores it per head
+                    const int t0 = st_one ? r - (g0 + g) * a.s : r;
                     A mine = sd[0];
                     bool ml = live[0];
 #pragma unroll
                     for (int t = 1; t < S; ++t) {
-                        mine = r == t ? sd[t] : mine;
-                        ml = r == t ? live[t] : ml;
+                        mine = t0 == t ? sd[t] : mine;
+                        ml = t0 == t ? live[t] : ml;
                     }
-                    if (r < a.s)
+                    if (t0 >= 0 && t0 < a.s) st_val = ml ? (float)(fast_exp2(mine - M) * inv) : 0.0f;
+                    if (!st_one && t0 >= 0 && t0 < a.s)
                         __builtin_nontemporal_store(
-                            ml ? (float)(fast_exp2(mine - M) * inv) : 0.0f,
-                            a.stats + ((size_t)cur.pos.prow * G + g0 + g) * a.s + r);
+                            st_val, a.stats + ((size_t)cur.pos.prow * G + g0 + g) * a.s + t0);
                 }
                 A o[V];
 #pragma unroll
@@ -381,6 +386,8 @@ __global__ __launch_bounds__(kBlock) void sea_fwd_row_kernel(SeaFwdFast a) {
                 }
             }
         }
+        if (a.stats && st_one && r < G * a.s)
+            __builtin_nontemporal_store(st_val, a.stats + (size_t)cur.pos.prow * G * a.s + r);
         cur = nxt;
     }
 }

@@ -650,6 +650,7 @@ __host__ __device__ inline long long part_row_off(int n, int c) {
     return off;
 }
 
+template <int S1>
 __global__ __launch_bounds__(kSerThreads) void ser_bwd_part_kernel(SerPartArgs a) {
     __shared__ double acc[kSerPartRows * 4];
     const int total = a.npairs * a.nch;
@@ -675,7 +676,7 @@ __global__ __launch_bounds__(kSerThreads) void ser_bwd_part_kernel(SerPartArgs a
         // retained slots of A' (s1 = 4, or 2 with the rest dead)
         int mt[kSmax];
         float wt[kSmax], gt[kSmax];
-        if (a.u.s1 == 4) {
+        if constexpr (S1 == 4) {
             const int4 m4 = *reinterpret_cast<const int4*>(a.idx_out + (size_t)u * 4);
             const float4 w4 = *reinterpret_cast<const float4*>(a.w_out + (size_t)u * 4);
             const float4 g4 = *reinterpret_cast<const float4*>(a.dw_out + (size_t)u * 4);
@@ -958,8 +959,12 @@ hipError_t launch_ser_backward(int B, int n, int hkv, const int32_t* idx1, const
         pa.nch = (n + kSerThreads - 1) / kSerThreads;
         pa.npairs = B * hkv;
         pa.aliased = aliased;
-        hipLaunchKernelGGL(ser_bwd_part_kernel, dim3((unsigned)(pa.npairs * pa.nch)),
-                           dim3(kSerThreads), 0, st, pa);
+        if (s1 == 4)
+            hipLaunchKernelGGL(ser_bwd_part_kernel<4>, dim3((unsigned)(pa.npairs * pa.nch)),
+                               dim3(kSerThreads), 0, st, pa);
+        else
+            hipLaunchKernelGGL(ser_bwd_part_kernel<2>, dim3((unsigned)(pa.npairs * pa.nch)),
+                               dim3(kSerThreads), 0, st, pa);
         hipLaunchKernelGGL(ser_bwd_part_sum_kernel, dim3((unsigned)((rows + kBlock - 1) / kBlock)),
                            dim3(kBlock), 0, st, pa);
         return hipGetLastError();
