@@ -22,6 +22,7 @@ kernel sources) against its compulsory bytes.
 
     python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu-baseline] [--no-cold]
     python bench.py --config {sea2,ser_sea4,stack21,long64k,theia}   (other workloads)
+    python bench.py --config decode   (latency of one decode step)
 """
 from __future__ import annotations
 
@@ -124,7 +125,7 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--config", default="metric", choices=list(CONFIG_STAGES),
+    ap.add_argument("--config", default="metric", choices=list(CONFIG_STAGES) + ["decode"],
                     help="workload: the measured pass (default) or one of the other "
                          "configurations, timed on its own stages (no CPU baseline)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -323,6 +324,61 @@ def run_config(a):
         "steps": a.steps, "warmup": a.warmup, "data": "synthetic"}), flush=True)
 
 
+def run_decode(a):
+    """Latency of one decode step (gm_decode_step) on the metric shape: B = 8
+    sequences whose newest token sits at position 4095 of a 4,096-token
+    cache, 16 q / 8 KV heads, d = 128, bf16, (s1, s2, s3) = (4, 4, 4), leg 1 =
+    the cache's own row of that token.  One JSON line."""
+    p = synth.PRESETS["metric"]
+    idx, w = synth.edges(p.seed, p.B, p.n, p.hkv, p.s2, mode=p.mode)
+    cu = lambda t: t.contiguous().cuda()  # noqa: E731
+    idx, w = cu(torch.from_numpy(idx)), cu(torch.from_numpy(w))
+    k = cu(synth.normal(p.seed, "k", (p.B, p.n, p.hkv, p.d), p.dtype))
+    v = cu(synth.normal(p.seed, "v", (p.B, p.n, p.hkv, p.d), p.dtype))
+    q = cu(synth.normal(p.seed, "q", (p.B, p.hq, p.d), p.dtype))
+    i1, w1 = idx[:, -1].contiguous(), w[:, -1].contiguous()
+    io = torch.empty((p.B, p.hkv, p.s1), dtype=torch.int32, device="cuda")
+    wo = torch.empty((p.B, p.hkv, p.s1), dtype=torch.float32, device="cuda")
+    o = torch.empty_like(q)
+    step = lambda: gm.gm_decode_step(i1, w1, idx, w, q, k, v, io, wo, o)  # noqa: E731
+    for _ in range(a.warmup):
+        step()
+    torch.cuda.synchronize()
+    st, en = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    st.record()
+    for _ in range(a.steps):
+        step()
+    en.record()
+    torch.cuda.synchronize()
+    ms = st.elapsed_time(en) / a.steps
+    g = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g):
+        for _ in range(16):
+            step()
+    g.replay()
+    torch.cuda.synchronize()
+    st.record()
+    for _ in range(max(1, a.steps // 16)):
+        g.replay()
+    en.record()
+    torch.cuda.synchronize()
+    gms = st.elapsed_time(en) / (max(1, a.steps // 16) * 16)
+    print(json.dumps({
+        "config": "decode", "units_per_step": p.B * p.hkv, "tokens_per_step": p.B,
+        "cache_tokens": p.n, "shape": {"B": p.B, "hq": p.hq, "hkv": p.hkv, "d": p.d,
+                                       "s1": p.s1, "s2": p.s2, "s3": p.s3, "dtype": "bfloat16"},
+        "us_per_step": ms * 1e3, "tokens_per_s": p.B / (ms * 1e-3),
+        "graph_us_per_step": gms * 1e3,
+        "how": "back-to-back steps on one stream (HIP events); graph: 16 steps per replay",
+        "steps": a.steps, "warmup": a.warmup, "data": "synthetic"}), flush=True)
+
+
 def profiled_step_bytes(config: str):
     """Counter bytes per step from profiles/<config>_kernels.md, or None when
     it is missing or the kernel sources changed since."""
@@ -392,6 +448,9 @@ def main():
                           "launches": a.warmup + a.steps}))
         return
     gm.load()
+    if a.config == "decode":
+        run_decode(a)
+        return
     if a.config != "metric":
         run_config(a)
         return

@@ -178,6 +178,33 @@ gm_status gm_ser_backward(int B, int n, int hkv,
                           hipStream_t stream);
 
 /*
+ * One decode step of the sparse layer (inference; ai.info "Why This Matters":
+ * long-context inference): SER then SEA for the newest token of each of B
+ * sequences, against caches of the earlier tokens' edge rows and K/V rows.
+ * Per (b, KV head h):
+ *   A'_b = Sparsify_s1(A1_b . A2_cache)   as gm_ser_forward for one row: the
+ *          token's leg-1 slots a point at cache rows j_a, whose s3 slots give
+ *          the two-hop targets; same merge, ranking and padding rules, and
+ *          bitwise the weights gm_ser_forward produces for that row
+ *   o_b  = SEA(q_b, k_cache, v_cache, A'_b)  as gm_sea_forward for one row
+ *   in   idx1, w1 [B][hkv][s2] the token's leg-1 row (indices into the cache);
+ *        idx2, w2 [B][T][hkv][s3] the edge cache (leg 2);
+ *        q [B][hq][d]; k, v [B][T][hkv][d] the K/V cache, dtype dt (the
+ *        token's own row written at its position before the call)
+ *   out  idx_out, w_out [B][hkv][s1]; o [B][hq][d] dtype dt
+ * Indices must address filled cache rows (not checked on the device; out of
+ * range is undefined behaviour).  Limits as gm_ser_forward and
+ * gm_sea_forward (T plays n); activation pointers 16-byte aligned, edge
+ * pointers 4-byte aligned; no output may overlap an input or another output.
+ * One launch; no workspace.
+ */
+gm_status gm_decode_step(int B, int T, int hq, int hkv, int d, gm_dtype dt, float scale,
+                         const int32_t* idx1, const float* w1, int s2,
+                         const int32_t* idx2, const float* w2, int s3, int s1,
+                         const void* q, const void* k, const void* v,
+                         int32_t* idx_out, float* w_out, void* o, hipStream_t stream);
+
+/*
  * Debug validator of an edge tensor.  Adds to counts[0] the number of slots
  * whose index lies outside [0, i] or whose weight is negative or not finite,
  * and to counts[1] the number of live slots (w > 0), i.e. the key/value rows

@@ -7,7 +7,8 @@ backward, as hand-written HIP kernels behind the C ABI of include/gm.h
 the first call does, and raises if it is not built.
 """
 from .binding import (  # noqa: F401
-    EXPORTS, GMError, check_edges, gm_check_edges, gm_sea_backward, gm_sea_forward,
+    EXPORTS, GMError, check_edges, decode_step, gm_check_edges, gm_decode_step,
+    gm_sea_backward, gm_sea_forward,
     gm_sea_backward_workspace_bytes, gm_ser_backward, gm_ser_backward_workspace_bytes, gm_ser_forward,
     load, sea_backward, sea_forward, sea_workspace, ser_backward, ser_forward, ser_workspace,
     stats_as_query_heads,

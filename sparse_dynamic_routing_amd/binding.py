@@ -24,7 +24,7 @@ GM_F32, GM_BF16 = 0, 1
 STATUS = {0: "GM_OK", 1: "GM_ERR_NULL", 2: "GM_ERR_SHAPE", 3: "GM_ERR_UNSUPPORTED",
           4: "GM_ERR_WORKSPACE", 5: "GM_ERR_HIP", 6: "GM_ERR_ALIGN", 7: "GM_ERR_ALIAS"}
 EXPORTS = ("gm_ser_forward", "gm_sea_forward", "gm_sea_backward_workspace_bytes",
-           "gm_sea_backward",
+           "gm_sea_backward", "gm_decode_step",
            "gm_ser_backward_workspace_bytes", "gm_ser_backward", "gm_check_edges",
            "gm_status_string", "gm_abi_version")
 
@@ -53,6 +53,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
         "gm_sea_backward_workspace_bytes": [_I, _I, _I, _I, _I],
         "gm_sea_backward": [_I, _I, _I, _I, _I, _I, _F, _P, _P, _P, _P, _P, _I, _P, _P,
                             _P, _P, _P, _P, _P, _Z, _P],
+        "gm_decode_step": [_I, _I, _I, _I, _I, _I, _F, _P, _P, _I, _P, _P, _I, _I, _P, _P,
+                           _P, _P, _P, _P, _P],
         "gm_ser_backward_workspace_bytes": [_I, _I, _I, _I, _I, _I],
         "gm_ser_backward": [_I, _I, _I, _P, _P, _I, _P, _P, _I, _P, _P, _I, _P, _P, _P,
                             _P, _Z, _P],
@@ -162,6 +164,29 @@ def gm_sea_backward(q, k, v, idx, w, dout, dq, dk, dv, dw, workspace, scale=None
           _stream(stream))
 
 
+def gm_decode_step(idx1, w1, idx2, w2, q, k, v, idx_out, w_out, o, scale=None,
+                   stream=None) -> None:
+    """One decode step: idx1/w1 [B, hkv, s2] (the new tokens' leg-1 rows),
+    idx2/w2 [B, T, hkv, s3] (edge cache), q [B, hq, d], k/v [B, T, hkv, d]
+    -> idx_out/w_out [B, hkv, s1], o [B, hq, d]."""
+    B, hkv, s2 = idx1.shape
+    T, s3 = idx2.shape[1], idx2.shape[3]
+    hq, d = q.shape[1], q.shape[2]
+    s1 = idx_out.shape[2]
+    _need(idx1, "idx1", (torch.int32,)); _need(w1, "w1", (torch.float32,), idx1.shape)
+    _need(idx2, "idx2", (torch.int32,), (B, T, hkv, s3))
+    _need(w2, "w2", (torch.float32,), idx2.shape)
+    _need(q, "q", _ACT, (B, hq, d))
+    _need(k, "k", (q.dtype,), (B, T, hkv, d)); _need(v, "v", (q.dtype,), (B, T, hkv, d))
+    _need(idx_out, "idx_out", (torch.int32,), (B, hkv, s1))
+    _need(w_out, "w_out", (torch.float32,), idx_out.shape)
+    _need(o, "o", (q.dtype,), q.shape)
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    _call("gm_decode_step", B, T, hq, hkv, d, _act_dtype(q), scale, _ptr(idx1), _ptr(w1), s2,
+          _ptr(idx2), _ptr(w2), s3, s1, _ptr(q), _ptr(k), _ptr(v), _ptr(idx_out), _ptr(w_out),
+          _ptr(o), _stream(stream))
+
+
 def gm_ser_backward_workspace_bytes(B, n, hkv, s2, s3, aliased) -> int:
     return int(load().gm_ser_backward_workspace_bytes(B, n, hkv, s2, s3, int(bool(aliased))))
 
@@ -258,3 +283,13 @@ def stats_as_query_heads(stats: torch.Tensor) -> torch.Tensor:
     """The saved statistics [B, hkv, n, G, s1] viewed as [B, n, hq, s1]."""
     B, hkv, n, G, s1 = stats.shape
     return stats.permute(0, 2, 1, 3, 4).reshape(B, n, hkv * G, s1)
+
+
+def decode_step(idx1, w1, idx2, w2, q, k, v, s1, scale=None, stream=None):
+    """(idx_out, w_out, o) of one decode step (see gm_decode_step)."""
+    B, hkv, _ = idx1.shape
+    idx_out = torch.empty((B, hkv, s1), dtype=torch.int32, device=q.device)
+    w_out = torch.empty((B, hkv, s1), dtype=torch.float32, device=q.device)
+    o = torch.empty_like(q)
+    gm_decode_step(idx1, w1, idx2, w2, q, k, v, idx_out, w_out, o, scale, stream)
+    return idx_out, w_out, o

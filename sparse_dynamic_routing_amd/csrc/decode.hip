@@ -1,0 +1,226 @@
+// Decode step: SER then SEA for the newest token of each sequence, against
+// caches of earlier edge rows and K/V rows (inference; page "Graph Machine:
+// Towards Better Pretraining via Edges", ai.info, "Why This Matters":
+// long-context inference, where KV access is the binding cost).
+//
+// One 64-lane wavefront per (batch, KV head) unit, one launch per step:
+//   lane k < s2*s3 holds candidate path k = (a, c): the token's leg-1 slot a
+//   points at row j_a of the edge cache, whose slot c names target m; its
+//   weight is w1[a] * w2[j_a][c] in fp64.  The first lane of each target
+//   adds the later lanes of the same target in path order (the definition's
+//   order and precision, so the weights are bit-identical to the training
+//   pass), later ones drop out; each lane's rank among positive keys
+//   (weight desc, target asc) comes from one sweep over the lanes, and rank
+//   r < s1 writes output slot r (padding (0, 0) after the last candidate).
+//   SEA then reads the kept slots' K/V cache rows in 16-byte pieces (lane l
+//   holds piece l of each d-row; the query rows are loaded while SER runs),
+//   four slots per step, each score a wavefront sum, with an online softmax
+//   per query head.
+// Everything is latency: a step reads ~s2*s3 edge entries and 2*s1 K/V rows
+// per unit.
+#include "gm_common.h"
+#include "gm_internal.h"
+#include "gm_wave.h"
+
+namespace gm {
+namespace {
+
+struct DecodeArgs {
+    const int32_t* idx1;    // [B][hkv][s2] the token's leg-1 row
+    const float* w1;
+    const int32_t* idx2;    // [B][T][hkv][s3] edge cache (leg 2)
+    const float* w2;
+    const void* q;          // [B][hq][d]
+    const void* k;          // [B][T][hkv][d]
+    const void* v;
+    int32_t* idx_out;       // [B][hkv][s1]
+    float* w_out;
+    void* o;                // [B][hq][d]
+    int B, T, hq, hkv, d, s1, s2, s3;
+    float scale;
+};
+
+// sum over the wavefront: DPP inside each 16-lane row, then the rows
+// combined with the permlane swaps (no LDS round trip)
+template <typename A>
+__device__ __forceinline__ A wave_sum(A x) {
+    x = row_sum16(x);
+    A a = x, b = x;
+    swap16(a, b);
+    x = a + b;
+    a = x;
+    b = x;
+    swap32(a, b);
+    return a + b;
+}
+
+// value of lane k (k uniform): v_readlane, no LDS round trip
+__device__ __forceinline__ int lane_i(int x, int k) { return __builtin_amdgcn_readlane(x, k); }
+__device__ __forceinline__ float lane_f(float x, int k) {
+    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), k));
+}
+__device__ __forceinline__ double lane_d(double x, int k) {
+    const uint64_t u = __builtin_bit_cast(uint64_t, x);
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)u, k);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(u >> 32), k);
+    return __builtin_bit_cast(double, ((uint64_t)hi << 32) | lo);
+}
+
+template <typename T, int G>
+__global__ __launch_bounds__(kWave) void decode_kernel(DecodeArgs a) {
+    using A = typename io<T>::acc;
+    constexpr int V = io<T>::V;            // elements per 16-byte piece
+    const int unit = (int)blockIdx.x;       // b * hkv + h
+    const int b = unit / a.hkv, h = unit - (unit / a.hkv) * a.hkv;
+    const int lane = (int)threadIdx.x;
+    const int nc = a.s2 * a.s3;
+    const int R = a.d / V;                  // 16-byte pieces per d-row (<= 64)
+    const bool piece = lane < R;
+
+    // the token's query rows (independent of SER: in flight meanwhile)
+    const T* qb = static_cast<const T*>(a.q) + ((size_t)b * a.hq + (size_t)h * G) * a.d;
+    A qf[G][V];
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+#pragma unroll
+        for (int e = 0; e < V; ++e) qf[g][e] = 0;
+        if (piece) load16(qb + (size_t)g * a.d + lane * V, qf[g]);
+    }
+
+    // SER: lane k < s2*s3 holds path k = (a, c)
+    int m = -1;
+    double cw = 0.0;
+    if (lane < nc) {
+        const int aa = lane / a.s3, c = lane - (lane / a.s3) * a.s3;
+        const int j = a.idx1[(size_t)unit * a.s2 + aa];
+        const float x = a.w1[(size_t)unit * a.s2 + aa];
+        const size_t r2 = ((size_t)b * a.T + j) * a.hkv + h;
+        m = a.idx2[r2 * a.s3 + c];
+        cw = (double)x * (double)a.w2[r2 * a.s3 + c];
+    }
+    // merge: the first lane of a target sums its later lanes in path order
+    double acc = cw;
+    bool dup = false;
+    for (int k2 = 0; k2 < nc; ++k2) {
+        const int mk = lane_i(m, k2);
+        const double ck = lane_d(cw, k2);
+        if (mk == m) {
+            if (k2 < lane) dup = true;
+            if (k2 > lane) acc += ck;
+        }
+    }
+    const float key = (float)acc;
+    const bool cand = lane < nc && !dup && key > 0.0f;
+    // rank among the candidates: larger weight first, then the lower target
+    const uint64_t cmask = __ballot(cand);
+    int rank = 0;
+    for (int k2 = 0; k2 < nc; ++k2) {
+        if (!((cmask >> k2) & 1)) continue;
+        const float kk = lane_f(key, k2);
+        const int mk = lane_i(m, k2);
+        if (kk > key || (kk == key && mk < m)) ++rank;
+    }
+    const size_t ob = (size_t)unit * a.s1;
+    if (cand && rank < a.s1) {
+        a.idx_out[ob + rank] = m;
+        a.w_out[ob + rank] = key;
+    }
+    const int ncand = __popcll(cmask);
+    for (int r = ncand + lane; r < a.s1; r += kWave) {
+        a.idx_out[ob + r] = 0;
+        a.w_out[ob + r] = 0.0f;
+    }
+    const int live = ncand < a.s1 ? ncand : a.s1;
+
+    // SEA over the live slots (slot r = the lane of rank r), four slots per
+    // step with their K and V pieces loaded together, online softmax per head
+    const T* kb = static_cast<const T*>(a.k);
+    const T* vb = static_cast<const T*>(a.v);
+    const A c = (A)a.scale * (A)1.4426950408889634;   // scale * log2(e)
+    A M[G], Z[G], ov[G][V];
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+        M[g] = -INFINITY;
+        Z[g] = 0;
+#pragma unroll
+        for (int e = 0; e < V; ++e) ov[g][e] = 0;
+    }
+    for (int r0 = 0; r0 < live; r0 += 4) {
+        A kf[4][V], vf[4][V], lw[4];
+        bool on[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int r = r0 + u;
+            on[u] = r < live;
+#pragma unroll
+            for (int e = 0; e < V; ++e) { kf[u][e] = 0; vf[u][e] = 0; }
+            lw[u] = 0;
+            if (on[u]) {
+                const int src = __ffsll(__ballot(cand && rank == r)) - 1;
+                const int j = lane_i(m, src);
+                lw[u] = alog2((A)lane_f(key, src));
+                const size_t kr = (((size_t)b * a.T + j) * a.hkv + h) * a.d + (size_t)lane * V;
+                if (piece) {
+                    load16(kb + kr, kf[u]);
+                    load16(vb + kr, vf[u]);
+                }
+            }
+        }
+#pragma unroll
+        for (int g = 0; g < G; ++g) {
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                if (!on[u]) continue;
+                A dot = 0;
+#pragma unroll
+                for (int e = 0; e < V; ++e) dot += qf[g][e] * kf[u][e];
+                const A l = wave_sum(dot) * c + lw[u];
+                const A Mn = l > M[g] ? l : M[g];
+                const A alpha = aexp2(M[g] - Mn);   // 0 on the first slot (M = -inf)
+                const A p = aexp2(l - Mn);
+                Z[g] = Z[g] * alpha + p;
+#pragma unroll
+                for (int e = 0; e < V; ++e) ov[g][e] = ov[g][e] * alpha + p * vf[u][e];
+                M[g] = Mn;
+            }
+        }
+    }
+    T* obase = static_cast<T*>(a.o) + ((size_t)b * a.hq + (size_t)h * G) * a.d;
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+        const A inv = Z[g] > (A)0 ? (A)1 / Z[g] : (A)0;
+        A y[V];
+#pragma unroll
+        for (int e = 0; e < V; ++e) y[e] = ov[g][e] * inv;
+        if (piece) store_n<V>(obase + (size_t)g * a.d + lane * V, y);
+    }
+}
+
+}  // namespace
+
+hipError_t launch_decode_step(int B, int T, int hq, int hkv, int d, bool bf16, float scale,
+                              const int32_t* idx1, const float* w1, int s2,
+                              const int32_t* idx2, const float* w2, int s3, int s1,
+                              const void* q, const void* k, const void* v, int32_t* idx_out,
+                              float* w_out, void* o, hipStream_t st) {
+    DecodeArgs a{idx1, w1, idx2, w2, q, k, v, idx_out, w_out, o,
+                 B, T, hq, hkv, d, s1, s2, s3, scale};
+    const dim3 grid((unsigned)(B * hkv));
+    auto go = [&](auto tag) {
+        using T = decltype(tag);
+        switch (hq / hkv) {
+            case 1: hipLaunchKernelGGL((decode_kernel<T, 1>), grid, dim3(kWave), 0, st, a); break;
+            case 2: hipLaunchKernelGGL((decode_kernel<T, 2>), grid, dim3(kWave), 0, st, a); break;
+            case 4: hipLaunchKernelGGL((decode_kernel<T, 4>), grid, dim3(kWave), 0, st, a); break;
+            case 8: hipLaunchKernelGGL((decode_kernel<T, 8>), grid, dim3(kWave), 0, st, a); break;
+            case 16:
+                hipLaunchKernelGGL((decode_kernel<T, 16>), grid, dim3(kWave), 0, st, a);
+                break;
+            default: return hipErrorInvalidValue;
+        }
+        return hipGetLastError();
+    };
+    return bf16 ? go(bf16_t{}) : go(float{});
+}
+
+}  // namespace gm

@@ -62,7 +62,7 @@ bool overlaps(const void* a, size_t an, const void* b, size_t bn) {
 
 extern "C" {
 
-int gm_abi_version(void) { return 2; }
+int gm_abi_version(void) { return 3; }
 
 const char* gm_status_string(gm_status s) {
     switch (s) {
@@ -122,6 +122,42 @@ gm_status gm_sea_forward(int B, int n, int hq, int hkv, int d, gm_dtype dt, floa
         return GM_ERR_ALIAS;
     return hip_status(gm::launch_sea_forward(B, n, hq, hkv, d, dt == GM_BF16, scale, q, k, v,
                                              idx, w, s1, o, stats, stream));
+}
+
+gm_status gm_decode_step(int B, int T, int hq, int hkv, int d, gm_dtype dt, float scale,
+                         const int32_t* idx1, const float* w1, int s2, const int32_t* idx2,
+                         const float* w2, int s3, int s1, const void* q, const void* k,
+                         const void* v, int32_t* idx_out, float* w_out, void* o,
+                         hipStream_t stream) {
+    gm_status st = check_sea(B, T, hq, hkv, d, dt, s1);
+    if (st != GM_OK) return st;
+    if ((st = check_ser(B, T, hkv, s1, s2, s3)) != GM_OK) return st;
+    if ((long long)B * hkv == 0) return GM_OK;
+    if (T < 1) return GM_ERR_SHAPE;
+    if (!q || !k || !v || !o) return GM_ERR_NULL;
+    if ((st = check_edge_ptrs(idx1, w1)) != GM_OK) return st;
+    if ((st = check_edge_ptrs(idx2, w2)) != GM_OK) return st;
+    if (!idx_out || !w_out) return GM_ERR_NULL;
+    if (!aligned(idx_out, 4) || !aligned(w_out, 4)) return GM_ERR_ALIGN;
+    if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16))
+        return GM_ERR_ALIGN;
+    const size_t es = dt == GM_BF16 ? 2 : 4;
+    const size_t units = (size_t)B * hkv;
+    const size_t qb = (size_t)B * hq * d * es, kb = (size_t)B * T * hkv * d * es;
+    const void* ins[7] = {idx1, w1, idx2, w2, q, k, v};
+    const size_t inb[7] = {units * s2 * 4, units * s2 * 4, units * T * s3 * 4,
+                           units * T * s3 * 4, qb, kb, kb};
+    const void* outs[3] = {idx_out, w_out, o};
+    const size_t outb[3] = {units * s1 * 4, units * s1 * 4, qb};
+    for (int a = 0; a < 3; ++a) {
+        for (int b = 0; b < 7; ++b)
+            if (overlaps(outs[a], outb[a], ins[b], inb[b])) return GM_ERR_ALIAS;
+        for (int b = a + 1; b < 3; ++b)
+            if (overlaps(outs[a], outb[a], outs[b], outb[b])) return GM_ERR_ALIAS;
+    }
+    return hip_status(gm::launch_decode_step(B, T, hq, hkv, d, dt == GM_BF16, scale, idx1, w1,
+                                             s2, idx2, w2, s3, s1, q, k, v, idx_out, w_out, o,
+                                             stream));
 }
 
 size_t gm_sea_backward_workspace_bytes(int B, int n, int hq, int hkv, int s1) {

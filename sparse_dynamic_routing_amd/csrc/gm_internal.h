@@ -31,6 +31,13 @@ hipError_t launch_sea_forward(int B, int n, int hq, int hkv, int d, bool bf16, f
                               const int32_t* idx, const float* w, int s, void* o,
                               float* stats, hipStream_t st);
 
+// One decode step (SER + SEA of one new token per sequence against caches).
+hipError_t launch_decode_step(int B, int T, int hq, int hkv, int d, bool bf16, float scale,
+                              const int32_t* idx1, const float* w1, int s2,
+                              const int32_t* idx2, const float* w2, int s3, int s1,
+                              const void* q, const void* k, const void* v, int32_t* idx_out,
+                              float* w_out, void* o, hipStream_t st);
+
 size_t sea_backward_workspace_bytes(long long U, int s, int G);
 hipError_t launch_sea_backward(int B, int n, int hq, int hkv, int d, bool bf16, float scale,
                                const void* q, const void* k, const void* v,

@@ -35,7 +35,7 @@ def test_library_exports_every_declared_call(lib):
     assert set(names) == set(binding.EXPORTS)
     for name in names:
         assert hasattr(lib, name), name
-    assert lib.gm_abi_version() == 2
+    assert lib.gm_abi_version() == 3
 
 
 def test_status_strings(lib):
@@ -107,6 +107,24 @@ def test_sea_argument_checks(lib):
     assert g(*bad) == ALIGN
     bad = list(bargs); bad[14] = fake(0x800000)   # dq on the statistics
     assert g(*bad) == ALIAS
+
+
+def test_decode_step_argument_checks(lib):
+    f = lib.gm_decode_step
+    i1, w1, i2, w2 = fake(0x100000), fake(0x200000), fake(0x1000000), fake(0x2000000)
+    q, k, v = fake(0x300000), fake(0x10000000), fake(0x20000000)
+    io, wo, o = fake(0x400000), fake(0x500000), fake(0x600000)
+    args = lambda B=8, T=4096, hq=16, hkv=8, d=128, dt=1, s2=4, s3=4, s1=4, qq=q, oo=o: (  # noqa
+        B, T, hq, hkv, d, dt, 0.1, i1, w1, s2, i2, w2, s3, s1, qq, k, v, io, wo, oo, None)
+    assert f(*args(hq=12)) == UNSUP
+    assert f(*args(d=96)) == UNSUP
+    assert f(*args(s2=9, s3=8)) == UNSUP       # 72 candidates
+    assert f(*args(s1=65)) == UNSUP
+    assert f(*args(T=0)) == SHAPE              # an empty cache with tokens to decode
+    assert f(*args(B=0)) == OK                 # nothing to decode
+    assert f(*args(qq=None)) == NULL
+    assert f(*args(qq=fake(0x300008))) == ALIGN
+    assert f(*args(oo=q)) == ALIAS             # o on q
 
 
 def test_ser_backward_workspace_checks(lib):
