@@ -8,7 +8,8 @@
 // loads the pair's edges once and sorts its half in LDS; the edges come
 // either from idx/w (rows of all KV heads interleaved, 16 bytes used per
 // 128-byte line) or from a compact per-pair copy of the live targets that
-// the SEA backward's source pass writes as it goes.  Longer sequences:
+// the SEA backward's source pass writes as it goes (both index builders
+// take either source).  Longer sequences:
 // a bucket partition, then an LDS sort per bucket (below).  The pair's list
 // occupies the fixed range [pair * n * s, (pair + 1) * n * s); beg and len
 // are indexed by the pair-major row pair * n + j.  The order of edges inside
@@ -191,6 +192,7 @@ constexpr int kMaxBuckets = 2048;   // n <= 2^20
 struct LongIndexArgs {
     const int32_t* idx;
     const float* w;
+    const int* tgt;   // pair-major live targets (-1 dead) instead of idx/w, or null
     int n, hkv, s, npairs, nb, nch, vec;
     int* counts;   // [npairs][nb][nch]
     int* offs;     // [npairs][nb][nch]
@@ -215,7 +217,23 @@ __device__ __forceinline__ void load_tokens(const LongIndexArgs& a, int b, int h
         const bool ok = iv < n;
         const int i = ok ? iv : n - 1;
         const int e0 = ((b * n + i) * hkv + h) * s;
-        if constexpr (VEC) {
+        if (a.tgt) {
+            // compact rows: the live targets of this pair, contiguous per token
+            const int* tr = a.tgt + ((size_t)(b * hkv + h) * n + i) * s;
+            if constexpr (VEC) {
+                const int4 t4 = *reinterpret_cast<const int4*>(tr);
+                tj[k * 4 + 0] = t4.x; tj[k * 4 + 1] = t4.y;
+                tj[k * 4 + 2] = t4.z; tj[k * 4 + 3] = t4.w;
+            } else {
+#pragma unroll
+                for (int t = 0; t < kSlotMax; ++t) tj[k * kSlotMax + t] = tr[t < s ? t : s - 1];
+            }
+#pragma unroll
+            for (int t = 0; t < kSlotMax; ++t) {
+                const int sl = k * kSlotMax + t;
+                te[sl] = ok && t < s && tj[sl] >= 0 ? e0 + t : -1;
+            }
+        } else if constexpr (VEC) {
             const int4 j4 = *reinterpret_cast<const int4*>(a.idx + e0);
             const float4 w4 = *reinterpret_cast<const float4*>(a.w + e0);
             tj[k * 4 + 0] = j4.x; tj[k * 4 + 1] = j4.y;
@@ -418,15 +436,17 @@ hipError_t launch_edge_index(int B, int n, int hkv, const int32_t* idx, const fl
 }
 
 hipError_t launch_edge_index_long(int B, int n, int hkv, const int32_t* idx, const float* w,
-                                  int s, int* beg, int* len, int* list, int* head, int* counts,
-                                  int* offs, int* tot, int2* stage, hipStream_t st) {
+                                  int s, const int* tgt, int* beg, int* len, int* list,
+                                  int* head, int* counts, int* offs, int* tot, int2* stage,
+                                  hipStream_t st) {
     LongIndexArgs a;
-    a.idx = idx; a.w = w; a.n = n; a.hkv = hkv; a.s = s;
+    a.idx = idx; a.w = w; a.tgt = tgt; a.n = n; a.hkv = hkv; a.s = s;
     a.npairs = B * hkv;
     a.nb = (n + kBucket - 1) / kBucket;
     a.nch = (n + kOneRows - 1) / kOneRows;
     if (a.nb > kMaxBuckets || s > kSlotMax) return hipErrorInvalidValue;
-    a.vec = s == 4 && (((uintptr_t)idx | (uintptr_t)w) & 15) == 0;
+    a.vec = s == 4 && (tgt ? ((uintptr_t)tgt & 15) == 0
+                           : (((uintptr_t)idx | (uintptr_t)w) & 15) == 0);
     a.counts = counts;
     a.offs = offs;
     a.tot = tot;

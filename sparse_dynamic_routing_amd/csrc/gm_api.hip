@@ -162,7 +162,7 @@ gm_status gm_decode_step(int B, int T, int hq, int hkv, int d, gm_dtype dt, floa
 
 size_t gm_sea_backward_workspace_bytes(int B, int n, int hq, int hkv, int s1) {
     if (check_units(B, n, hkv) != GM_OK || hkv <= 0 || hq <= 0 || hq % hkv || s1 < 1) return 0;
-    return gm::sea_backward_workspace_bytes((long long)B * n * hkv, s1, hq / hkv);
+    return gm::sea_backward_workspace_bytes((long long)B * n * hkv, s1, hq / hkv, n);
 }
 
 gm_status gm_sea_backward(int B, int n, int hq, int hkv, int d, gm_dtype dt, float scale,

@@ -38,7 +38,7 @@ hipError_t launch_decode_step(int B, int T, int hq, int hkv, int d, bool bf16, f
                               const void* q, const void* k, const void* v, int32_t* idx_out,
                               float* w_out, void* o, hipStream_t st);
 
-size_t sea_backward_workspace_bytes(long long U, int s, int G);
+size_t sea_backward_workspace_bytes(long long U, int s, int G, int n);
 hipError_t launch_sea_backward(int B, int n, int hq, int hkv, int d, bool bf16, float scale,
                                const void* q, const void* k, const void* v,
                                const int32_t* idx, const float* w, int s, const void* dout,
@@ -63,10 +63,11 @@ bool edge_index_one_pass(int n);
 // int2 entries.  Both write, when head is not null, each row's first four
 // list entries (-1 padded) to head[4 * pair-major row].
 hipError_t launch_edge_index_long(int B, int n, int hkv, const int32_t* idx, const float* w,
-                                  int s, int* beg, int* len, int* list, int* head, int* counts,
-                                  int* offs, int* tot, int2* stage, hipStream_t st);
-// tgt, when not null, holds the live targets per pair-major source row
-// (tgt[row * s + t], -1 for a dead slot) and replaces idx and w.
+                                  int s, const int* tgt, int* beg, int* len, int* list,
+                                  int* head, int* counts, int* offs, int* tot, int2* stage,
+                                  hipStream_t st);
+// In both, tgt, when not null, holds the live targets per pair-major source
+// row (tgt[row * s + t], -1 for a dead slot) and replaces idx and w.
 hipError_t launch_edge_index(int B, int n, int hkv, const int32_t* idx, const float* w, int s,
                              const int* tgt, int* beg, int* len, int* list, int* head,
                              hipStream_t st);

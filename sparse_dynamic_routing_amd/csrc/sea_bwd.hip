@@ -51,13 +51,14 @@ struct Workspace {
     int* len;       // [U]  ... and number of incoming edges
     int* head;      // [U * 4]  per row in pair-major order: its first 4 edge ids, -1 padded
     int* tgt;       // [U * s]  per source row in pair-major order: target of each slot, -1 dead
+    int2* stage;    // [U * s]  (edge, target) staging of the partitioned index (n > 4096)
 };
 
 struct WsLayout {
-    size_t coef, cnt, off, bsum, list, beg, len, head, tgt, total;
+    size_t coef, cnt, off, bsum, list, beg, len, head, tgt, stage, total;
 };
 
-WsLayout ws_layout(long long U, int s, int G) {
+WsLayout ws_layout(long long U, int s, int G, int n) {
     WsLayout l;
     l.coef = 0;
     l.cnt = l.coef + align256((size_t)U * s * G * sizeof(float2));
@@ -68,7 +69,9 @@ WsLayout ws_layout(long long U, int s, int G) {
     l.len = l.beg + align256((size_t)U * sizeof(int));
     l.head = l.len + align256((size_t)U * sizeof(int));
     l.tgt = l.head + align256((size_t)U * 4 * sizeof(int));
-    l.total = l.tgt + align256((size_t)U * s * sizeof(int));
+    l.stage = l.tgt + align256((size_t)U * s * sizeof(int));
+    const bool partitioned = !edge_index_one_pass(n) && edge_index_supported(n, s);
+    l.total = l.stage + (partitioned ? align256((size_t)U * s * sizeof(int2)) : 0);
     return l;
 }
 
@@ -851,13 +854,13 @@ hipError_t run_fast(const SeaBwdArgs& g, const SeaBwdFast& a, long long E, hipSt
         launch_src<T, G, S, VEC, true>(a, st);
         launch_index(g, E, st);
     } else if (!edge_index_one_pass(a.n)) {
-        // long sequences: the partitioned index first; its staging area is
-        // the coefficient buffer, which the source pass writes afterwards
-        const hipError_t e = launch_edge_index_long(
-            a.U / (a.n * a.hkv), a.n, a.hkv, a.idx, a.w, a.s, a.ws.beg, a.ws.len, a.ws.list,
-            a.ws.head, a.ws.cnt, a.ws.off, a.ws.bsum, reinterpret_cast<int2*>(a.ws.coef), st);
-        if (e != hipSuccess) return e;
+        // long sequences: the partitioned index, from the source pass's
+        // compact targets
         launch_src<T, G, S, VEC, false>(a, st);
+        const hipError_t e = launch_edge_index_long(
+            a.U / (a.n * a.hkv), a.n, a.hkv, a.idx, a.w, a.s, a.ws.tgt, a.ws.beg, a.ws.len,
+            a.ws.list, a.ws.head, a.ws.cnt, a.ws.off, a.ws.bsum, a.ws.stage, st);
+        if (e != hipSuccess) return e;
     } else {
         launch_src<T, G, S, VEC, false>(a, st);
         const hipError_t e = launch_edge_index(a.U / (a.n * a.hkv), a.n, a.hkv, a.idx, a.w, a.s,
@@ -903,8 +906,8 @@ hipError_t dispatch_fast(const SeaBwdArgs& g, const SeaBwdFast& a, int G, long l
 
 }  // namespace
 
-size_t sea_backward_workspace_bytes(long long U, int s, int G) {
-    return ws_layout(U, s, G).total;
+size_t sea_backward_workspace_bytes(long long U, int s, int G, int n) {
+    return ws_layout(U, s, G, n).total;
 }
 
 hipError_t launch_sea_backward(int B, int n, int hq, int hkv, int d, bool bf16, float scale,
@@ -923,7 +926,7 @@ hipError_t launch_sea_backward(int B, int n, int hq, int hkv, int d, bool bf16, 
     a.ts = sea_team(d, es, s);
     // target pass: up to 8 incoming edges side by side (rows have ~s on average)
     a.tt = sea_team(d, es, 8);
-    const WsLayout l = ws_layout(a.U, s, G);
+    const WsLayout l = ws_layout(a.U, s, G, n);
     char* base = static_cast<char*>(workspace);
     a.ws.coef = reinterpret_cast<float2*>(base + l.coef);
     a.ws.cnt = reinterpret_cast<int*>(base + l.cnt);
@@ -934,6 +937,7 @@ hipError_t launch_sea_backward(int B, int n, int hq, int hkv, int d, bool bf16, 
     a.ws.len = reinterpret_cast<int*>(base + l.len);
     a.ws.head = reinterpret_cast<int*>(base + l.head);
     a.ws.tgt = reinterpret_cast<int*>(base + l.tgt);
+    a.ws.stage = reinterpret_cast<int2*>(base + l.stage);
     const long long E = (long long)a.U * s;
     if (sea_fast_shape(B, n, hq, hkv, d, bf16, s) &&
         (long long)B * n * hq * d * 4 < (1ll << 32)) {
@@ -950,7 +954,7 @@ hipError_t launch_sea_backward(int B, int n, int hq, int hkv, int d, bool bf16, 
         f.fd_s = make_fastdiv((uint32_t)s);
         make_seg_plan(f.sp, B, n, hkv);
         f.global_index = !edge_index_supported(n, s);
-        f.write_tgt = !f.global_index && edge_index_one_pass(n);
+        f.write_tgt = !f.global_index;
         f.vec = s == 4 && (((uintptr_t)idx | (uintptr_t)w) & 15) == 0;
         return bf16 ? dispatch_fast<bf16_t>(a, f, G, E, st) : dispatch_fast<float>(a, f, G, E, st);
     }
