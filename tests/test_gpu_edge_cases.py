@@ -145,12 +145,13 @@ def test_ser_forward_backward_shapes(s1, s2, s3, n, ties):
         assert_close("dw (aliased legs)", host(da), ra, 1e-5)
 
 
-@pytest.mark.parametrize("n", [1024, 1025, 2500, 4096, 4097])
-def test_ser_backward_source_chunks(n):
-    """s1 = s2 = s3 = 4 backward across the 1024-source chunk boundaries of
-    the partial-sum path (n <= 4096), and just past its limit (n = 4097,
-    fp64-atomic path); separate and aliased legs."""
-    say(f"case ser backward chunks n={n}")
+@pytest.mark.parametrize("n,s1", [(1024, 4), (1025, 4), (2500, 4), (3000, 2), (4096, 4),
+                                  (4097, 4), (9000, 4), (13000, 2)])
+def test_ser_backward_source_chunks(n, s1):
+    """s2 = s3 = 4 backward across the 1024-source chunk boundaries of the
+    partial-sum path (n <= 4096; whole-pair LDS accumulators) and past its
+    limit (the fp64-atomic path); s1 = 4 and 2, separate and aliased legs."""
+    say(f"case ser backward chunks n={n} s1={s1}")
     rng = np.random.default_rng(4000 + n)
     B, hkv = 1, 2
     idx1, w1 = cases.edges(rng, B, n, hkv, 4, pad_frac=0.05, dead_frac=0.05)
@@ -159,8 +160,8 @@ def test_ser_backward_source_chunks(n):
     for legs in ("separate", "aliased"):
         if legs == "aliased":
             idx2, w2 = idx1, w1
-        io, wo = gm.ser_forward(dev(idx1), dev(w1), dev(idx2), dev(w2), 4)
-        rio, rwo = orc.ser_forward(idx1, w1, idx2, w2, 4)
+        io, wo = gm.ser_forward(dev(idx1), dev(w1), dev(idx2), dev(w2), s1)
+        rio, rwo = orc.ser_forward(idx1, w1, idx2, w2, s1)
         assert_ser_match(host(io), host(wo), rio, rwo)
         dwo = rng.standard_normal(rio.shape).astype(np.float32)
         d1, d2 = gm.ser_backward(dev(idx1), dev(w1), dev(idx2), dev(w2), io, wo, dev(dwo),
