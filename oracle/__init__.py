@@ -65,8 +65,15 @@ class Oracle:
             ctypes.c_int, ctypes.c_int, ctypes.c_int,
             _i32p, _f64p, ctypes.c_int, _i32p, _f64p, ctypes.c_int,
             _i32p, _f64p, ctypes.c_int, _f64p, _f64p, _f64p]
+        lib.oracle_leg_mix_forward.argtypes = [
+            ctypes.c_int, ctypes.c_int, ctypes.c_int, _i32p, _f64p, ctypes.c_int, _f64p,
+            ctypes.c_int, _i32p, _f32p]
+        lib.oracle_leg_mix_backward.argtypes = [
+            ctypes.c_int, ctypes.c_int, ctypes.c_int, _i32p, _f64p, ctypes.c_int, _f64p,
+            _i32p, _f64p, ctypes.c_int, _f64p, _f64p, _f64p]
         for f in ("oracle_ser_forward", "oracle_sea_forward",
-                  "oracle_sea_backward", "oracle_ser_backward"):
+                  "oracle_sea_backward", "oracle_ser_backward",
+                  "oracle_leg_mix_forward", "oracle_leg_mix_backward"):
             getattr(lib, f).restype = ctypes.c_int
         self.lib = lib
 
@@ -168,6 +175,38 @@ class Oracle:
             self._p(dw_out, _f64p), self._p(dw1, _f64p), self._p(dw2, _f64p))
         self._check(rc, "ser_backward")
         return dw1, dw2
+
+    def leg_mix_forward(self, idx, w, alpha, s):
+        """Leg of s slots from K stored edges mixed by alpha [hkv, K].
+        Returns (idx int32, w float32)."""
+        idx = self._np(idx, np.int32); w = self._np(w, np.float64)
+        alpha = self._np(alpha, np.float64)
+        B, n, hkv, K = idx.shape
+        assert w.shape == idx.shape and alpha.shape == (hkv, K)
+        io = np.empty((B, n, hkv, s), np.int32)
+        wo = np.empty((B, n, hkv, s), np.float32)
+        rc = self.lib.oracle_leg_mix_forward(B, n, hkv, self._p(idx, _i32p), self._p(w, _f64p), K,
+                                             self._p(alpha, _f64p), s, self._p(io, _i32p),
+                                             self._p(wo, _f32p))
+        self._check(rc, "leg_mix_forward")
+        return io, wo
+
+    def leg_mix_backward(self, idx, w, alpha, idx_out, w_out, dleg):
+        """(dw [B,n,hkv,K], dalpha [hkv,K]) in float64."""
+        idx = self._np(idx, np.int32); w = self._np(w, np.float64)
+        alpha = self._np(alpha, np.float64)
+        idx_out = self._np(idx_out, np.int32); w_out = self._np(w_out, np.float64)
+        dleg = self._np(dleg, np.float64)
+        B, n, hkv, K = idx.shape
+        s = idx_out.shape[-1]
+        dw = np.empty(idx.shape, np.float64)
+        da = np.empty((hkv, K), np.float64)
+        rc = self.lib.oracle_leg_mix_backward(
+            B, n, hkv, self._p(idx, _i32p), self._p(w, _f64p), K, self._p(alpha, _f64p),
+            self._p(idx_out, _i32p), self._p(w_out, _f64p), s, self._p(dleg, _f64p),
+            self._p(dw, _f64p), self._p(da, _f64p))
+        self._check(rc, "leg_mix_backward")
+        return dw, da
 
 
 _default: Oracle | None = None

@@ -24,6 +24,9 @@
  *   Backward of both through the soft weights only: indices carry no
  *        gradient, and only retained edges receive one ([rit.work] what was
  *        done; [ai.info] Methodology, "only retained weights get gradients").
+ *   Leg construction: a token's stored edges mixed into a leg and
+ *        sparsified ([ai.info] Methodology, referral paragraph; the mixing
+ *        itself is a reading, stated at the function), forward and backward.
  *
  * Layouts (row-major): q, o, dout, dq [B,n,hq,d]; k, v, dk, dv [B,n,hkv,d];
  * edges idx [B,n,hkv,s] int32 and w [B,n,hkv,s].  Query head hq reads KV head
@@ -336,6 +339,105 @@ int oracle_ser_backward(int B, int n, int hkv,
                     dw1[r1 * s2 + a] += gt * y;
                     dw2[r2 * s3 + c] += gt * x;
                 }
+            }
+        }
+    }
+    return 0;
+}
+
+/*
+ * Leg construction ([ai.info] Methodology, referral paragraph: referral
+ * first mixes the stored edges into pairs and sparsifies each leg, and only
+ * then composes the legs).  The pages give no mixing formula; reading: a leg
+ * is a non-negative mixture of a token's K stored edges with one mixing
+ * weight per (KV head, stored slot), then the same sparsification as SER:
+ * For each unit (b, i, h), over the stored slots k = 0..K-1 in order:
+ *   m = idx[i,k];  acc[m] += alpha[h,k] * w[i,k]      (duplicates merged)
+ *   key[m] = acc[m] rounded to fp32; keep the s largest positive keys, equal
+ *   keys to the lower index; unused slots (0, 0).
+ * Indices are copied, never read through, so only 0 <= idx <= i is asked.
+ */
+int oracle_leg_mix_forward(int B, int n, int hkv, const int32_t* idx, const double* w, int K,
+                           const double* alpha, int s, int32_t* idx_out, float* w_out) {
+    if (B < 0 || n < 0 || hkv < 0 || K < 1 || s < 1 || K > ORACLE_MAX_CAND)
+        return ORACLE_ERR_ARGS;
+    int32_t cand_m[ORACLE_MAX_CAND];
+    double cand_acc[ORACLE_MAX_CAND];
+    float cand_key[ORACLE_MAX_CAND];
+    int taken[ORACLE_MAX_CAND];
+    for (int b = 0; b < B; ++b)
+    for (int i = 0; i < n; ++i)
+    for (int h = 0; h < hkv; ++h) {
+        size_t r = row(b, i, h, n, hkv);
+        int ncand = 0;
+        for (int k = 0; k < K; ++k) {
+            int m = idx[r * K + k];
+            if (m < 0 || m > i) return ORACLE_ERR_INDEX;
+            int found = -1;
+            for (int e = 0; e < ncand; ++e)
+                if (cand_m[e] == m) { found = e; break; }
+            if (found < 0) {
+                found = ncand++;
+                cand_m[found] = m;
+                cand_acc[found] = 0.0;
+            }
+            cand_acc[found] += alpha[(size_t)h * K + k] * w[r * K + k];
+        }
+        for (int e = 0; e < ncand; ++e) {
+            cand_key[e] = (float)cand_acc[e];
+            taken[e] = 0;
+        }
+        for (int slot = 0; slot < s; ++slot) {
+            int best = -1;
+            for (int e = 0; e < ncand; ++e) {
+                if (taken[e] || !(cand_key[e] > 0.0f)) continue;
+                if (best < 0 || cand_key[e] > cand_key[best] ||
+                    (cand_key[e] == cand_key[best] && cand_m[e] < cand_m[best]))
+                    best = e;
+            }
+            size_t o = r * s + slot;
+            if (best < 0) {
+                idx_out[o] = 0;
+                w_out[o] = 0.0f;
+            } else {
+                taken[best] = 1;
+                idx_out[o] = cand_m[best];
+                w_out[o] = cand_key[best];
+            }
+        }
+    }
+    return 0;
+}
+
+/*
+ * Leg construction backward, with the selection (the retained leg slots)
+ * held fixed, as for SER: for each unit and stored slot k with
+ * alpha[h,k] > 0 and w[i,k] > 0, and each retained slot t of the leg
+ * (w_out_t > 0) whose index equals idx[i,k]:
+ *   dw[i,k] += dleg_t * alpha[h,k]        dalpha[h,k] += dleg_t * w[i,k]
+ * (dalpha sums over every unit of the KV head).  Both outputs are
+ * overwritten first.
+ */
+int oracle_leg_mix_backward(int B, int n, int hkv, const int32_t* idx, const double* w, int K,
+                            const double* alpha, const int32_t* idx_out, const double* w_out,
+                            int s, const double* dleg, double* dw, double* dalpha) {
+    if (B < 0 || n < 0 || hkv < 0 || K < 1 || s < 1) return ORACLE_ERR_ARGS;
+    memset(dw, 0, (size_t)B * n * hkv * K * sizeof(double));
+    memset(dalpha, 0, (size_t)hkv * K * sizeof(double));
+    for (int b = 0; b < B; ++b)
+    for (int i = 0; i < n; ++i)
+    for (int h = 0; h < hkv; ++h) {
+        size_t r = row(b, i, h, n, hkv);
+        for (int k = 0; k < K; ++k) {
+            int m = idx[r * K + k];
+            double a = alpha[(size_t)h * K + k], x = w[r * K + k];
+            if (m < 0 || m > i) return ORACLE_ERR_INDEX;
+            if (!(a > 0.0) || !(x > 0.0)) continue;
+            for (int t = 0; t < s; ++t) {
+                if (!(w_out[r * s + t] > 0.0) || idx_out[r * s + t] != m) continue;
+                double g = dleg[r * s + t];
+                dw[r * K + k] += g * a;
+                dalpha[(size_t)h * K + k] += g * x;
             }
         }
     }

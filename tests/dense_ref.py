@@ -152,3 +152,52 @@ def sea(q, k, v, idx, w, dout=None, scale=None):
     if dout is None:
         return o
     return o, dq, dk, dv, dw
+
+
+def leg_mix(idx, w, alpha, s):
+    """Leg construction as dense rows: L[i] = sum_k alpha[h, k] w[i, k]
+    e_{idx[i, k]}; top-s of each row over its positive fp32-rounded entries.
+    Returns (idx, w, kth, next) like ser_forward."""
+    B, n, hkv, K = idx.shape
+    io = np.zeros((B, n, hkv, s), np.int32)
+    wo = np.zeros((B, n, hkv, s), np.float32)
+    kth = np.zeros((B, n, hkv), np.float64)
+    nxt = np.zeros((B, n, hkv), np.float64)
+    for b in range(B):
+        for h in range(hkv):
+            mixed = w[b, :, h, :].astype(np.float64) * np.asarray(alpha, np.float64)[h][None, :]
+            L = np.zeros((n, n), np.float64)
+            rows = np.repeat(np.arange(n), K)
+            np.add.at(L, (rows, idx[b, :, h, :].reshape(-1).astype(np.int64)), mixed.reshape(-1))
+            key = L.astype(np.float32)
+            for i in range(n):
+                cols = np.nonzero(key[i] > 0)[0]
+                order = cols[np.lexsort((cols, -key[i, cols].astype(np.float64)))]
+                keep = order[:s]
+                io[b, i, h, :len(keep)] = keep
+                wo[b, i, h, :len(keep)] = key[i, keep]
+                if len(order) >= s:
+                    kth[b, i, h] = key[i, order[s - 1]]
+                if len(order) > s:
+                    nxt[b, i, h] = key[i, order[s]]
+    return io, wo, kth, nxt
+
+
+def leg_mix_backward(idx, w, alpha, idx_out, w_out, dleg):
+    """Through the dense mixture: dL = M o dLeg (retained entries); then
+    dw[i, k] = alpha[h, k] dL[i, idx[i, k]] and dalpha[h, k] = sum_i w[i, k]
+    dL[i, idx[i, k]], over slots with alpha > 0 and w > 0."""
+    B, n, hkv, K = idx.shape
+    alpha = np.asarray(alpha, np.float64)
+    dw = np.zeros(idx.shape, np.float64)
+    da = np.zeros((hkv, K), np.float64)
+    for b in range(B):
+        for h in range(hkv):
+            G = adjacency(idx_out, np.where(w_out > 0, dleg, 0.0), b, h, n)
+            for i in range(n):
+                for k in range(K):
+                    if w[b, i, h, k] > 0 and alpha[h, k] > 0:
+                        g = G[i, idx[b, i, h, k]]
+                        dw[b, i, h, k] = alpha[h, k] * g
+                        da[h, k] += w[b, i, h, k] * g
+    return dw, da

@@ -44,6 +44,14 @@ MUTANTS = [
      "dv[src + c] += p[t] * dov[c];", "dv[src + c] += dl * dov[c];"),
     ("sea bwd: dq from v instead of k", "oracle_sea_backward",
      "dqv[c] += scale * dl * kv[c];", "dqv[c] += scale * dl * v[src + c];"),
+    ("leg: mixing weight dropped", "oracle_leg_mix_forward",
+     "cand_acc[found] += alpha[(size_t)h * K + k] * w[r * K + k];",
+     "cand_acc[found] += w[r * K + k];"),
+    ("leg: mixing weight of the wrong head", "oracle_leg_mix_forward",
+     "cand_acc[found] += alpha[(size_t)h * K + k] * w[r * K + k];",
+     "cand_acc[found] += alpha[(size_t)(hkv - 1 - h) * K + k] * w[r * K + k];"),
+    ("leg bwd: dalpha from the mixing weight", "oracle_leg_mix_backward",
+     "dalpha[(size_t)h * K + k] += g * x;", "dalpha[(size_t)h * K + k] += g * a;"),
     ("ser bwd: leg operands swapped", "oracle_ser_backward",
      "dw1[r1 * s2 + a] += gt * y;", "dw1[r1 * s2 + a] += gt * x;"),
     ("ser bwd: padding slots of A' pass gradient", "oracle_ser_backward",
@@ -69,6 +77,9 @@ PINS = [
     pins.test_sea_constant_values_and_conservation,
     pins.test_sea_finite_differences,
     pins.test_ser_forward_1000_random_small_cases,
+    pins.test_leg_mix_matches_dense_mixture,
+    pins.test_leg_mix_single_slot_closed_form,
+    pins.test_leg_mix_backward_matches_dense_and_differences,
 ]
 
 

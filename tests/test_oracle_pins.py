@@ -388,3 +388,87 @@ def test_kv_access_fraction_matches_printed_values(orc):
         per_query = rows / n
         assert per_query == s
         assert round(100 * per_query / ((n + 1) / 2), 3) == printed
+
+
+# ------------------------------------------------------ leg construction
+def _leg_case(rng, B, n, hkv, K, ties=False, pad=0.0, dead=0.0, zero_alpha=0.0):
+    idx, w = cases.edges(rng, B, n, hkv, K, pad_frac=pad, ties=ties, dead_frac=dead)
+    alpha = (rng.choice(cases.TIE_WEIGHTS, size=(hkv, K)) if ties
+             else rng.random((hkv, K)) + 0.05)
+    if zero_alpha:
+        alpha = np.where(rng.random(alpha.shape) < zero_alpha, 0.0, alpha)
+    return idx, w, alpha.astype(np.float32).astype(np.float64)
+
+
+def test_leg_mix_matches_dense_mixture(orc):
+    """Leg construction against dense rows sum_k alpha_k w_k e_{idx_k}, top-s:
+    random shapes, padding, dead slots, zero mixing weights, duplicates and
+    exact ties (dyadic weights)."""
+    rng = np.random.default_rng(2024)
+    for case in range(300):
+        B, hkv = (int(x) for x in rng.integers(1, 3, size=2))
+        n, K, s = int(rng.integers(1, 20)), int(rng.integers(1, 12)), int(rng.integers(1, 6))
+        idx, w, alpha = _leg_case(rng, B, n, hkv, K, ties=bool(case % 2),
+                                  pad=0.2 * (case % 3 == 0), dead=0.2 * (case % 5 == 0),
+                                  zero_alpha=0.2 * (case % 4 == 0))
+        io, wo = orc.leg_mix_forward(idx, w, alpha, s)
+        ref_io, ref_wo, kth, nxt = dense_ref.leg_mix(idx, w, alpha, s)
+        assert_ser_equal(io, wo, ref_io, ref_wo, kth, nxt)
+
+
+def test_leg_mix_single_slot_closed_form(orc):
+    """K = 1: the leg is the stored edge with weight alpha * w when positive,
+    else padding."""
+    rng = np.random.default_rng(5)
+    idx, w, alpha = _leg_case(rng, 2, 15, 3, 1, dead=0.3, zero_alpha=0.3)
+    io, wo = orc.leg_mix_forward(idx, w, alpha, 2)
+    prod = (w[..., 0].astype(np.float64) * alpha[None, None, :, 0]).astype(np.float32)
+    live = prod > 0
+    np.testing.assert_array_equal(io[..., 0], np.where(live, idx[..., 0], 0))
+    np.testing.assert_array_equal(wo[..., 0], np.where(live, prod, 0.0))
+    assert (io[..., 1] == 0).all() and (wo[..., 1] == 0).all()
+
+
+def test_leg_mix_backward_matches_dense_and_differences(orc):
+    """Backward against the dense mixture's chain rule, and central
+    differences of the kept weight sum (selection fixed, no near ties)."""
+    rng = np.random.default_rng(99)
+    for case in range(40):
+        B, hkv, n, K, s = 1, 2, int(rng.integers(2, 14)), int(rng.integers(1, 9)), 3
+        idx, w, alpha = _leg_case(rng, B, n, hkv, K, pad=0.1, dead=0.1, zero_alpha=0.1)
+        io, wo = orc.leg_mix_forward(idx, w, alpha, s)
+        dleg = rng.standard_normal(io.shape)
+        dw, da = orc.leg_mix_backward(idx, w, alpha, io, wo, dleg)
+        rdw, rda = dense_ref.leg_mix_backward(idx, w, alpha, io, wo, dleg)
+        np.testing.assert_allclose(dw, rdw, rtol=1e-12, atol=1e-14)
+        np.testing.assert_allclose(da, rda, rtol=1e-12, atol=1e-14)
+    # central differences of f = sum_t dleg_t * (exact kept weight of slot t)
+    rng = np.random.default_rng(7)
+    idx, w, alpha = _leg_case(rng, 1, 10, 2, 6)
+    io, wo = orc.leg_mix_forward(idx, w, alpha, 3)
+    dleg = rng.standard_normal(io.shape)
+    dw, da = orc.leg_mix_backward(idx, w, alpha, io, wo, dleg)
+
+    def f(w_, a_):
+        tot = 0.0
+        for b in range(1):
+            for i in range(10):
+                for h in range(2):
+                    for t in range(3):
+                        if wo[b, i, h, t] > 0:
+                            m = io[b, i, h, t]
+                            sel = idx[b, i, h] == m
+                            tot += dleg[b, i, h, t] * float((w_[b, i, h] * a_[h])[sel].sum())
+        return tot
+    eps = 1e-6
+    wd = w.astype(np.float64)
+    for (b, i, h, k) in [(0, 3, 0, 1), (0, 9, 1, 5), (0, 6, 1, 0)]:
+        if wd[b, i, h, k] <= 0:
+            continue
+        p, m = wd.copy(), wd.copy()
+        p[b, i, h, k] += eps; m[b, i, h, k] -= eps
+        assert abs((f(p, alpha) - f(m, alpha)) / (2 * eps) - dw[b, i, h, k]) < 1e-6
+    for (h, k) in [(0, 2), (1, 4)]:
+        p, m = alpha.copy(), alpha.copy()
+        p[h, k] += eps; m[h, k] -= eps
+        assert abs((f(wd, p) - f(wd, m)) / (2 * eps) - da[h, k]) < 1e-6
