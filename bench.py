@@ -23,6 +23,7 @@ kernel sources) against its compulsory bytes.
     python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu-baseline] [--no-cold]
     python bench.py --config {sea2,ser_sea4,stack21,long64k,theia}   (other workloads)
     python bench.py --config decode   (latency of one decode step)
+    python bench.py --config legmix   (leg construction, two legs fwd + bwd)
 """
 from __future__ import annotations
 
@@ -125,7 +126,8 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--config", default="metric", choices=list(CONFIG_STAGES) + ["decode"],
+    ap.add_argument("--config", default="metric",
+                    choices=list(CONFIG_STAGES) + ["decode", "legmix"],
                     help="workload: the measured pass (default) or one of the other "
                          "configurations, timed on its own stages (no CPU baseline)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -379,6 +381,48 @@ def run_decode(a):
         "steps": a.steps, "warmup": a.warmup, "data": "synthetic"}), flush=True)
 
 
+def run_legmix(a):
+    """Leg construction at the metric shape: K = 16 stored edges per unit
+    (B = 8, n = 4096, 8 KV heads, local/far mix) mixed into the two legs of
+    s = 4 slots the referral composes, forward and backward of both legs.
+    One JSON line (per-call times from HIP events)."""
+    p = synth.PRESETS["metric"]
+    K, s = 16, 4
+    idx, w = synth.edges(p.seed, p.B, p.n, p.hkv, K, mode=p.mode)
+    rng = np.random.default_rng(p.seed)
+    cu = lambda t: torch.from_numpy(t).contiguous().cuda()  # noqa: E731
+    idx, w = cu(idx), cu(w)
+    alphas = [cu((rng.random((p.hkv, K)) + 0.05).astype(np.float32)) for _ in range(2)]
+    shp = (p.B, p.n, p.hkv, s)
+    legs = [(torch.empty(shp, dtype=torch.int32, device="cuda"),
+             torch.empty(shp, dtype=torch.float32, device="cuda")) for _ in range(2)]
+    dleg = cu(rng.standard_normal(shp).astype(np.float32))
+    dws = [torch.empty(idx.shape, dtype=torch.float32, device="cuda") for _ in range(2)]
+    das = [torch.empty((p.hkv, K), dtype=torch.float32, device="cuda") for _ in range(2)]
+    nbytes = gm.gm_leg_mix_backward_workspace_bytes(p.B, p.n, p.hkv, K)
+    ws = torch.empty(max(nbytes, 8) // 8, dtype=torch.float64, device="cuda")
+    fwd = lambda: [gm.gm_leg_mix_forward(idx, w, alphas[l], *legs[l]) for l in range(2)]  # noqa
+    bwd = lambda: [gm.gm_leg_mix_backward(idx, w, alphas[l], *legs[l], dleg, dws[l], das[l],  # noqa
+                                          ws) for l in range(2)]
+    for _ in range(a.warmup):
+        fwd(); bwd()
+    torch.cuda.synchronize()
+    e = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+    tf = tb = 0.0
+    for _ in range(a.steps):
+        e[0].record(); fwd(); e[1].record(); bwd(); e[2].record()
+        torch.cuda.synchronize()
+        tf += e[0].elapsed_time(e[1]); tb += e[1].elapsed_time(e[2])
+    U = p.B * p.n * p.hkv
+    print(json.dumps({
+        "config": "legmix", "units_per_step": U, "K": K, "s": s, "legs": 2,
+        "forward_us": tf / a.steps * 1e3, "backward_us": tb / a.steps * 1e3,
+        "units_per_s": U / ((tf + tb) / a.steps * 1e-3),
+        "compulsory_bytes_per_unit": {"forward": 2 * (8 * K + 8 * s),
+                                      "backward": 2 * (8 * K + 12 * s + 4 * K)},
+        "steps": a.steps, "warmup": a.warmup, "data": "synthetic"}), flush=True)
+
+
 def profiled_step_bytes(config: str):
     """Counter bytes per step from profiles/<config>_kernels.md, or None when
     it is missing or the kernel sources changed since."""
@@ -450,6 +494,9 @@ def main():
     gm.load()
     if a.config == "decode":
         run_decode(a)
+        return
+    if a.config == "legmix":
+        run_legmix(a)
         return
     if a.config != "metric":
         run_config(a)

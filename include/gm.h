@@ -178,6 +178,48 @@ gm_status gm_ser_backward(int B, int n, int hkv,
                           hipStream_t stream);
 
 /*
+ * Leg construction (ai.info Methodology, referral paragraph: referral mixes
+ * the stored edges into pairs and sparsifies each leg before composing
+ * them).  The pages give no mixing formula; reading: a leg is a
+ * non-negative mixture of a token's K stored edges with one weight per
+ * (KV head, stored slot):
+ *   leg[i] = Sparsify_s( sum_k alpha[h][k] * w[i][k] e_{idx[i][k]} )
+ * merged in slot order in fp64, then SER's selection rules (top s by fp32
+ * weight, ties to the lower index, padding (0, 0)).  Call it once per leg.
+ *   in   idx, w [B][n][hkv][K] the stored edges (1 <= K <= 64, causal);
+ *        alpha [hkv][K] fp32 >= 0 (a learned parametrization that keeps
+ *        it non-negative is the caller's)
+ *   out  idx_out, w_out [B][n][hkv][s] (1 <= s <= 64)
+ * Bitwise deterministic.  Edge pointers 4-byte aligned; outputs must not
+ * overlap inputs.
+ */
+gm_status gm_leg_mix_forward(int B, int n, int hkv, const int32_t* idx, const float* w, int K,
+                             const float* alpha, int s, int32_t* idx_out, float* w_out,
+                             hipStream_t stream);
+
+/* Bytes of device workspace gm_leg_mix_backward needs (fp64 partial sums). */
+size_t gm_leg_mix_backward_workspace_bytes(int B, int n, int hkv, int K);
+
+/*
+ * Leg construction backward, the selection held fixed (only retained leg
+ * slots pass gradient, as for SER): for each stored slot k with
+ * alpha[h][k] > 0 and w[i][k] > 0 and each retained leg slot t (w_out > 0)
+ * with the same index:
+ *   dw[i][k] += dleg[i][t] * alpha[h][k]     dalpha[h][k] += dleg[i][t] * w[i][k]
+ *   in   idx, w, K, alpha as for the forward; idx_out, w_out, s: its output;
+ *        dleg [B][n][hkv][s] fp32
+ *   out  dw [B][n][hkv][K], dalpha [hkv][K] fp32, both overwritten
+ *   ws   device workspace of gm_leg_mix_backward_workspace_bytes(...)
+ *        bytes, 8-byte aligned
+ * dalpha is summed in fp64 in a fixed order and rounded once: bitwise
+ * deterministic.
+ */
+gm_status gm_leg_mix_backward(int B, int n, int hkv, const int32_t* idx, const float* w, int K,
+                              const float* alpha, const int32_t* idx_out, const float* w_out,
+                              int s, const float* dleg, float* dw, float* dalpha, void* workspace,
+                              size_t workspace_bytes, hipStream_t stream);
+
+/*
  * One decode step of the sparse layer (inference; ai.info "Why This Matters":
  * long-context inference): SER then SEA for the newest token of each of B
  * sequences, against caches of the earlier tokens' edge rows and K/V rows.

@@ -24,7 +24,8 @@ GM_F32, GM_BF16 = 0, 1
 STATUS = {0: "GM_OK", 1: "GM_ERR_NULL", 2: "GM_ERR_SHAPE", 3: "GM_ERR_UNSUPPORTED",
           4: "GM_ERR_WORKSPACE", 5: "GM_ERR_HIP", 6: "GM_ERR_ALIGN", 7: "GM_ERR_ALIAS"}
 EXPORTS = ("gm_ser_forward", "gm_sea_forward", "gm_sea_backward_workspace_bytes",
-           "gm_sea_backward", "gm_decode_step",
+           "gm_sea_backward", "gm_decode_step", "gm_leg_mix_forward",
+           "gm_leg_mix_backward_workspace_bytes", "gm_leg_mix_backward",
            "gm_ser_backward_workspace_bytes", "gm_ser_backward", "gm_check_edges",
            "gm_status_string", "gm_abi_version")
 
@@ -55,6 +56,10 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
                             _P, _P, _P, _P, _P, _Z, _P],
         "gm_decode_step": [_I, _I, _I, _I, _I, _I, _F, _P, _P, _I, _P, _P, _I, _I, _P, _P,
                            _P, _P, _P, _P, _P],
+        "gm_leg_mix_forward": [_I, _I, _I, _P, _P, _I, _P, _I, _P, _P, _P],
+        "gm_leg_mix_backward_workspace_bytes": [_I, _I, _I, _I],
+        "gm_leg_mix_backward": [_I, _I, _I, _P, _P, _I, _P, _P, _P, _I, _P, _P, _P, _P, _Z,
+                                _P],
         "gm_ser_backward_workspace_bytes": [_I, _I, _I, _I, _I, _I],
         "gm_ser_backward": [_I, _I, _I, _P, _P, _I, _P, _P, _I, _P, _P, _I, _P, _P, _P,
                             _P, _Z, _P],
@@ -68,6 +73,7 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
         f.restype = _I
     lib.gm_ser_backward_workspace_bytes.restype = _Z
     lib.gm_sea_backward_workspace_bytes.restype = _Z
+    lib.gm_leg_mix_backward_workspace_bytes.restype = _Z
     lib.gm_status_string.restype = ctypes.c_char_p
     _lib = lib
     return lib
@@ -187,6 +193,39 @@ def gm_decode_step(idx1, w1, idx2, w2, q, k, v, idx_out, w_out, o, scale=None,
           _ptr(o), _stream(stream))
 
 
+def gm_leg_mix_forward(idx, w, alpha, idx_out, w_out, stream=None) -> None:
+    """One leg [B, n, hkv, s] from the stored edges [B, n, hkv, K] mixed by
+    alpha [hkv, K]."""
+    B, n, hkv, K = idx.shape
+    s = idx_out.shape[3]
+    _need(idx, "idx", (torch.int32,)); _need(w, "w", (torch.float32,), idx.shape)
+    _need(alpha, "alpha", (torch.float32,), (hkv, K))
+    _need(idx_out, "idx_out", (torch.int32,), (B, n, hkv, s))
+    _need(w_out, "w_out", (torch.float32,), idx_out.shape)
+    _call("gm_leg_mix_forward", B, n, hkv, _ptr(idx), _ptr(w), K, _ptr(alpha), s,
+          _ptr(idx_out), _ptr(w_out), _stream(stream))
+
+
+def gm_leg_mix_backward_workspace_bytes(B, n, hkv, K) -> int:
+    return int(load().gm_leg_mix_backward_workspace_bytes(B, n, hkv, K))
+
+
+def gm_leg_mix_backward(idx, w, alpha, idx_out, w_out, dleg, dw, dalpha, workspace,
+                        stream=None) -> None:
+    B, n, hkv, K = idx.shape
+    s = idx_out.shape[3]
+    _need(idx, "idx", (torch.int32,)); _need(w, "w", (torch.float32,), idx.shape)
+    _need(alpha, "alpha", (torch.float32,), (hkv, K))
+    _need(idx_out, "idx_out", (torch.int32,), (B, n, hkv, s))
+    _need(w_out, "w_out", (torch.float32,), idx_out.shape)
+    _need(dleg, "dleg", (torch.float32,), idx_out.shape)
+    _need(dw, "dw", (torch.float32,), idx.shape); _need(dalpha, "dalpha", (torch.float32,), (hkv, K))
+    _need(workspace, "workspace", (torch.uint8, torch.float64))
+    _call("gm_leg_mix_backward", B, n, hkv, _ptr(idx), _ptr(w), K, _ptr(alpha), _ptr(idx_out),
+          _ptr(w_out), s, _ptr(dleg), _ptr(dw), _ptr(dalpha), _ptr(workspace),
+          workspace.numel() * workspace.element_size(), _stream(stream))
+
+
 def gm_ser_backward_workspace_bytes(B, n, hkv, s2, s3, aliased) -> int:
     return int(load().gm_ser_backward_workspace_bytes(B, n, hkv, s2, s3, int(bool(aliased))))
 
@@ -293,3 +332,23 @@ def decode_step(idx1, w1, idx2, w2, q, k, v, s1, scale=None, stream=None):
     o = torch.empty_like(q)
     gm_decode_step(idx1, w1, idx2, w2, q, k, v, idx_out, w_out, o, scale, stream)
     return idx_out, w_out, o
+
+
+def leg_mix(idx, w, alpha, s, stream=None):
+    """(idx_out, w_out) of one leg (see gm_leg_mix_forward)."""
+    B, n, hkv, _ = idx.shape
+    idx_out = torch.empty((B, n, hkv, s), dtype=torch.int32, device=idx.device)
+    w_out = torch.empty((B, n, hkv, s), dtype=torch.float32, device=idx.device)
+    gm_leg_mix_forward(idx, w, alpha, idx_out, w_out, stream)
+    return idx_out, w_out
+
+
+def leg_mix_backward(idx, w, alpha, idx_out, w_out, dleg, stream=None):
+    """(dw, dalpha) of one leg (see gm_leg_mix_backward)."""
+    B, n, hkv, K = idx.shape
+    dw = torch.empty(idx.shape, dtype=torch.float32, device=idx.device)
+    dalpha = torch.empty((hkv, K), dtype=torch.float32, device=idx.device)
+    nbytes = gm_leg_mix_backward_workspace_bytes(B, n, hkv, K)
+    ws = torch.empty(max(nbytes, 8) // 8, dtype=torch.float64, device=idx.device)
+    gm_leg_mix_backward(idx, w, alpha, idx_out, w_out, dleg, dw, dalpha, ws, stream)
+    return dw, dalpha

@@ -62,7 +62,7 @@ bool overlaps(const void* a, size_t an, const void* b, size_t bn) {
 
 extern "C" {
 
-int gm_abi_version(void) { return 3; }
+int gm_abi_version(void) { return 4; }
 
 const char* gm_status_string(gm_status s) {
     switch (s) {
@@ -122,6 +122,69 @@ gm_status gm_sea_forward(int B, int n, int hq, int hkv, int d, gm_dtype dt, floa
         return GM_ERR_ALIAS;
     return hip_status(gm::launch_sea_forward(B, n, hq, hkv, d, dt == GM_BF16, scale, q, k, v,
                                              idx, w, s1, o, stats, stream));
+}
+
+gm_status gm_leg_mix_forward(int B, int n, int hkv, const int32_t* idx, const float* w, int K,
+                             const float* alpha, int s, int32_t* idx_out, float* w_out,
+                             hipStream_t stream) {
+    gm_status st = check_units(B, n, hkv);
+    if (st != GM_OK) return st;
+    if (K < 1 || K > 64 || s < 1 || s > 64) return GM_ERR_UNSUPPORTED;
+    if (empty(B, n, hkv)) return GM_OK;
+    if ((st = check_edge_ptrs(idx, w)) != GM_OK) return st;
+    if ((st = check_edge_ptrs(idx_out, w_out)) != GM_OK) return st;
+    if (!alpha) return GM_ERR_NULL;
+    if (!aligned(alpha, 4)) return GM_ERR_ALIGN;
+    const size_t rows = (size_t)B * n * hkv;
+    const void* ins[3] = {idx, w, alpha};
+    const size_t inb[3] = {rows * K * 4, rows * K * 4, (size_t)hkv * K * 4};
+    const void* outs[2] = {idx_out, w_out};
+    const size_t outb[2] = {rows * s * 4, rows * s * 4};
+    for (int a = 0; a < 2; ++a) {
+        for (int b = 0; b < 3; ++b)
+            if (overlaps(outs[a], outb[a], ins[b], inb[b])) return GM_ERR_ALIAS;
+    }
+    if (overlaps(idx_out, outb[0], w_out, outb[1])) return GM_ERR_ALIAS;
+    return hip_status(
+        gm::launch_leg_mix_forward(B, n, hkv, idx, w, K, alpha, s, idx_out, w_out, stream));
+}
+
+size_t gm_leg_mix_backward_workspace_bytes(int B, int n, int hkv, int K) {
+    if (check_units(B, n, hkv) != GM_OK || K < 1 || K > 64) return 0;
+    return gm::leg_mix_backward_workspace_bytes(B, n, hkv, K);
+}
+
+gm_status gm_leg_mix_backward(int B, int n, int hkv, const int32_t* idx, const float* w, int K,
+                              const float* alpha, const int32_t* idx_out, const float* w_out,
+                              int s, const float* dleg, float* dw, float* dalpha, void* workspace,
+                              size_t workspace_bytes, hipStream_t stream) {
+    gm_status st = check_units(B, n, hkv);
+    if (st != GM_OK) return st;
+    if (K < 1 || K > 64 || s < 1 || s > 64) return GM_ERR_UNSUPPORTED;
+    if (empty(B, n, hkv)) return GM_OK;
+    if ((st = check_edge_ptrs(idx, w)) != GM_OK) return st;
+    if ((st = check_edge_ptrs(idx_out, w_out)) != GM_OK) return st;
+    if (!alpha || !dleg || !dw || !dalpha) return GM_ERR_NULL;
+    if (!aligned(alpha, 4) || !aligned(dleg, 4) || !aligned(dw, 4) || !aligned(dalpha, 4))
+        return GM_ERR_ALIGN;
+    const size_t need = gm_leg_mix_backward_workspace_bytes(B, n, hkv, K);
+    if (!workspace || workspace_bytes < need) return GM_ERR_WORKSPACE;
+    if (!aligned(workspace, 8)) return GM_ERR_ALIGN;
+    const size_t rows = (size_t)B * n * hkv;
+    const void* ins[6] = {idx, w, alpha, idx_out, w_out, dleg};
+    const size_t inb[6] = {rows * K * 4, rows * K * 4, (size_t)hkv * K * 4, rows * s * 4,
+                           rows * s * 4, rows * s * 4};
+    const void* outs[3] = {dw, dalpha, workspace};
+    const size_t outb[3] = {rows * K * 4, (size_t)hkv * K * 4, need};
+    for (int a = 0; a < 3; ++a) {
+        for (int b = 0; b < 6; ++b)
+            if (overlaps(outs[a], outb[a], ins[b], inb[b])) return GM_ERR_ALIAS;
+        for (int b = a + 1; b < 3; ++b)
+            if (overlaps(outs[a], outb[a], outs[b], outb[b])) return GM_ERR_ALIAS;
+    }
+    return hip_status(gm::launch_leg_mix_backward(B, n, hkv, idx, w, K, alpha, idx_out, w_out, s,
+                                                  dleg, dw, dalpha,
+                                                  static_cast<double*>(workspace), stream));
 }
 
 gm_status gm_decode_step(int B, int T, int hq, int hkv, int d, gm_dtype dt, float scale,

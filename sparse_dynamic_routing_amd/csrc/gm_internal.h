@@ -31,6 +31,16 @@ hipError_t launch_sea_forward(int B, int n, int hq, int hkv, int d, bool bf16, f
                               const int32_t* idx, const float* w, int s, void* o,
                               float* stats, hipStream_t st);
 
+// Leg construction (stored edges mixed into a leg), forward and backward.
+size_t leg_mix_backward_workspace_bytes(int B, int n, int hkv, int K);
+hipError_t launch_leg_mix_forward(int B, int n, int hkv, const int32_t* idx, const float* w,
+                                  int K, const float* alpha, int s, int32_t* idx_out,
+                                  float* w_out, hipStream_t st);
+hipError_t launch_leg_mix_backward(int B, int n, int hkv, const int32_t* idx, const float* w,
+                                   int K, const float* alpha, const int32_t* idx_out,
+                                   const float* w_out, int s, const float* dleg, float* dw,
+                                   float* dalpha, double* part, hipStream_t st);
+
 // One decode step (SER + SEA of one new token per sequence against caches).
 hipError_t launch_decode_step(int B, int T, int hq, int hkv, int d, bool bf16, float scale,
                               const int32_t* idx1, const float* w1, int s2,

@@ -1,0 +1,283 @@
+// Leg construction: a token's K stored edges mixed into one leg and
+// sparsified (page "Graph Machine: Towards Better Pretraining via Edges",
+// ai.info, Methodology, referral paragraph: the stored edges are mixed into
+// pairs and each leg is sparsified before the legs are composed).  The
+// mixing is a reading: leg weight of target m = sum over the stored slots k
+// pointing at m of alpha[h][k] * w[k], merged in slot order in fp64, then
+// SER's selection (top s by fp32 weight, ties to the lower index, (0, 0)
+// padding).
+//
+// Forward: a team of L = max(16, pow2(K)) lanes per unit, lane k holding
+// stored slot k; the first lane of each target sums the later lanes of that
+// target in slot order (the definition's order and precision, so the
+// weights are bit-identical to the oracle's), and each candidate's rank
+// comes from one sweep over the team (DPP row rotations for 16-lane teams,
+// shuffles for wider ones).
+// Backward: the same teams, each lane matching its slot against the leg's
+// retained slots: dw = alpha * dleg (own row, no scatter); dalpha sums
+// w * dleg over every unit of a KV head: each workgroup reduces its units
+// (one head, 64 tokens) in a fixed order into a partial, and a second
+// kernel adds the partials in a fixed order and rounds once (deterministic).
+#include "gm_common.h"
+#include "gm_internal.h"
+
+#include <utility>
+
+namespace gm {
+namespace {
+
+constexpr int kLegTokens = 64;   // tokens of one KV head per backward workgroup
+
+// Rotation inside a 16-lane row (DPP row_ror:D): every lane reads one lane
+// of its own row, so a team of 16 sweeps its partners without LDS.
+template <int D>
+__device__ __forceinline__ int ror_i(int x) {
+    return __builtin_amdgcn_update_dpp(0, x, 0x120 + D, 0xF, 0xF, false);
+}
+template <int D>
+__device__ __forceinline__ float ror_f(float x) {
+    return __int_as_float(ror_i<D>(__float_as_int(x)));
+}
+template <int D>
+__device__ __forceinline__ double ror_d(double x) {
+    const uint64_t u = __builtin_bit_cast(uint64_t, x);
+    const uint32_t lo = (uint32_t)ror_i<D>((int)(uint32_t)u);
+    const uint32_t hi = (uint32_t)ror_i<D>((int)(uint32_t)(u >> 32));
+    return __builtin_bit_cast(double, ((uint64_t)hi << 32) | lo);
+}
+
+struct Cand {
+    int k, m;
+    double cw, acc;
+    bool dup;
+    float key;
+    bool cand;
+    int rank;
+};
+// merge step against the partner D lanes away (its slot index read along)
+template <int D>
+__device__ __forceinline__ void merge_step(Cand& c) {
+    const int k2 = ror_i<D>(c.k);
+    const int mk = ror_i<D>(c.m);
+    const double ck = ror_d<D>(c.cw);
+    if (mk == c.m) {
+        if (k2 < c.k) c.dup = true;
+        else c.acc += ck;
+    }
+}
+template <int D>
+__device__ __forceinline__ void rank_step(Cand& c) {
+    const float kk = ror_f<D>(c.key);
+    const int mk = ror_i<D>(c.m);
+    const bool ck = ror_i<D>((int)c.cand) != 0;
+    if (ck && (kk > c.key || (kk == c.key && mk < c.m))) ++c.rank;
+}
+// later slots must be added in increasing slot order: the sweep runs in
+// whichever rotation direction visits them that way
+template <int... D>
+__device__ __forceinline__ void merge_up(Cand& c, std::integer_sequence<int, D...>) {
+    (merge_step<D + 1>(c), ...);
+}
+template <int... D>
+__device__ __forceinline__ void merge_down(Cand& c, std::integer_sequence<int, D...>) {
+    (merge_step<15 - D>(c), ...);
+}
+template <int... D>
+__device__ __forceinline__ void rank_all(Cand& c, std::integer_sequence<int, D...>) {
+    (rank_step<D + 1>(c), ...);
+}
+
+struct LegArgs {
+    const int32_t* idx;     // [B][n][hkv][K] stored edges
+    const float* w;
+    const float* alpha;     // [hkv][K]
+    int32_t* idx_out;       // [B][n][hkv][s] the leg
+    float* w_out;
+    const float* dleg;      // backward: [B][n][hkv][s]
+    float* dw;              // backward: [B][n][hkv][K]
+    float* dalpha;          // backward: [hkv][K]
+    double* part;           // backward: [hkv][nchunk][K]
+    int n, hkv, K, s, U, BN, nchunk;
+};
+
+template <int L>
+__global__ __launch_bounds__(kBlock) void leg_mix_fwd_kernel(LegArgs a) {
+    const int lane = (int)(threadIdx.x & (kWave - 1));
+    const int k = lane & (L - 1);
+    const long long gu = ((long long)blockIdx.x * kBlock + threadIdx.x) / L;
+    const bool in = gu < a.U;
+    const int u = in ? (int)gu : 0;
+    const int h = u % a.hkv;
+    const int base = lane & ~(L - 1);      // the team's first lane
+    int m = -1;
+    double cw = 0.0;
+    if (in && k < a.K) {
+        m = a.idx[(size_t)u * a.K + k];
+        cw = (double)a.alpha[(size_t)h * a.K + k] * (double)a.w[(size_t)u * a.K + k];
+    }
+    double acc = cw;
+    bool dup = false;
+    float key;
+    bool cand;
+    int rank = 0;
+    if constexpr (L == 16) {
+        // 16-lane rows: DPP rotations (every lane of the wave takes part,
+        // so no lane leaves before the sweeps)
+        Cand c{k, m, cw, cw, false, 0.0f, false, 0};
+        if (ror_i<1>(k) == ((k + 1) & 15))
+            merge_up(c, std::make_integer_sequence<int, 15>{});
+        else
+            merge_down(c, std::make_integer_sequence<int, 15>{});
+        c.key = (float)c.acc;
+        c.cand = in && k < a.K && !c.dup && c.key > 0.0f;
+        rank_all(c, std::make_integer_sequence<int, 15>{});
+        key = c.key;
+        cand = c.cand;
+        rank = c.rank;
+    } else {
+        for (int k2 = 0; k2 < a.K; ++k2) {
+            const int mk = __shfl(m, k2, L);
+            const double ck = __shfl(cw, k2, L);
+            if (mk == m) {
+                if (k2 < k) dup = true;
+                if (k2 > k) acc += ck;
+            }
+        }
+        key = (float)acc;
+        cand = in && k < a.K && !dup && key > 0.0f;
+        for (int k2 = 0; k2 < a.K; ++k2) {
+            const float kk = __shfl(key, k2, L);
+            const int mk = __shfl(m, k2, L);
+            const bool ck = __shfl((int)cand, k2, L) != 0;
+            if (ck && (kk > key || (kk == key && mk < m))) ++rank;
+        }
+    }
+    if (!in) return;
+    const size_t ob = (size_t)u * a.s;
+    if (cand && rank < a.s) {
+        a.idx_out[ob + rank] = m;
+        a.w_out[ob + rank] = key;
+    }
+    const uint64_t team = L == kWave ? ~0ull : ((1ull << L) - 1) << base;
+    const int ncand = __popcll(__ballot(cand) & team);
+    for (int r = ncand + k; r < a.s; r += L) {
+        a.idx_out[ob + r] = 0;
+        a.w_out[ob + r] = 0.0f;
+    }
+}
+
+// workgroup (h, chunk): the units (t, h) for the kLegTokens flattened tokens
+// t = b * n + i of the chunk; every thread of a team walks them in steps of
+// the workgroup's team count and keeps its slot's w * dleg sum in fp64
+template <int L>
+__global__ __launch_bounds__(kBlock) void leg_mix_bwd_kernel(LegArgs a) {
+    constexpr int kTeams = kBlock / L;
+    __shared__ double red[kTeams][L];
+    const int h = (int)blockIdx.x / a.nchunk, chunk = (int)blockIdx.x % a.nchunk;
+    const int team = (int)threadIdx.x / L, k = (int)threadIdx.x & (L - 1);
+    const float al = k < a.K ? a.alpha[(size_t)h * a.K + k] : 0.0f;
+    double da = 0.0;
+    const int t0 = chunk * kLegTokens;
+    const int t1 = t0 + kLegTokens < a.BN ? t0 + kLegTokens : a.BN;
+    for (int t = t0 + team; t < t1; t += kTeams) {
+        const int u = t * a.hkv + h;
+        if (k >= a.K) continue;
+        const int m = a.idx[(size_t)u * a.K + k];
+        const float x = a.w[(size_t)u * a.K + k];
+        double g = 0.0;
+        if (al > 0.0f && x > 0.0f) {
+            const size_t ob = (size_t)u * a.s;
+            for (int r = 0; r < a.s; ++r)
+                if (a.w_out[ob + r] > 0.0f && a.idx_out[ob + r] == m) g += (double)a.dleg[ob + r];
+        }
+        a.dw[(size_t)u * a.K + k] = (float)(g * (double)al);
+        da += g * (double)x;
+    }
+    red[team][k] = da;
+    __syncthreads();
+    if ((int)threadIdx.x < L && (int)threadIdx.x < a.K) {
+        double s = 0.0;
+        for (int q = 0; q < kTeams; ++q) s += red[q][threadIdx.x];
+        a.part[((size_t)h * a.nchunk + chunk) * a.K + threadIdx.x] = s;
+    }
+}
+
+// dalpha[h][k]: one wavefront per element; lane l adds chunks l, l + 64, ...
+// in order, then a fixed butterfly over the lanes; rounded once
+__global__ __launch_bounds__(kBlock) void leg_mix_alpha_kernel(LegArgs a) {
+    const int e = (int)((blockIdx.x * kBlock + threadIdx.x) / kWave);
+    const int lane = (int)(threadIdx.x & (kWave - 1));
+    if (e >= a.hkv * a.K) return;          // whole wavefronts
+    const int h = e / a.K, k = e - (e / a.K) * a.K;
+    double s = 0.0;
+    for (int c = lane; c < a.nchunk; c += kWave) s += a.part[((size_t)h * a.nchunk + c) * a.K + k];
+#pragma unroll
+    for (int o = 1; o < kWave; o <<= 1) s += __shfl_xor(s, o, kWave);
+    if (lane == 0) a.dalpha[e] = (float)s;
+}
+
+template <int L>
+void launch_fwd(const LegArgs& a, hipStream_t st) {
+    const long long threads = (long long)a.U * L;
+    hipLaunchKernelGGL(leg_mix_fwd_kernel<L>, dim3((unsigned)((threads + kBlock - 1) / kBlock)),
+                       dim3(kBlock), 0, st, a);
+}
+
+template <int L>
+void launch_bwd(const LegArgs& a, hipStream_t st) {
+    hipLaunchKernelGGL(leg_mix_bwd_kernel<L>, dim3((unsigned)(a.hkv * a.nchunk)), dim3(kBlock),
+                       0, st, a);
+    const long long lanes = (long long)a.hkv * a.K * kWave;
+    hipLaunchKernelGGL(leg_mix_alpha_kernel, dim3((unsigned)((lanes + kBlock - 1) / kBlock)),
+                       dim3(kBlock), 0, st, a);
+}
+
+template <bool FWD>
+hipError_t dispatch(const LegArgs& a, hipStream_t st) {
+    if (FWD && a.K <= 16) {   // 16-lane teams: the DPP sweeps
+        launch_fwd<16>(a, st);
+        return hipGetLastError();
+    }
+    switch (pow2_ceil(a.K)) {
+        case 1: FWD ? launch_fwd<1>(a, st) : launch_bwd<1>(a, st); break;
+        case 2: FWD ? launch_fwd<2>(a, st) : launch_bwd<2>(a, st); break;
+        case 4: FWD ? launch_fwd<4>(a, st) : launch_bwd<4>(a, st); break;
+        case 8: FWD ? launch_fwd<8>(a, st) : launch_bwd<8>(a, st); break;
+        case 16: FWD ? launch_fwd<16>(a, st) : launch_bwd<16>(a, st); break;
+        case 32: FWD ? launch_fwd<32>(a, st) : launch_bwd<32>(a, st); break;
+        case 64: FWD ? launch_fwd<64>(a, st) : launch_bwd<64>(a, st); break;
+        default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
+}  // namespace
+
+size_t leg_mix_backward_workspace_bytes(int B, int n, int hkv, int K) {
+    const long long chunks = ((long long)B * n + kLegTokens - 1) / kLegTokens;
+    return (size_t)hkv * (size_t)chunks * (size_t)K * sizeof(double);
+}
+
+hipError_t launch_leg_mix_forward(int B, int n, int hkv, const int32_t* idx, const float* w,
+                                  int K, const float* alpha, int s, int32_t* idx_out,
+                                  float* w_out, hipStream_t st) {
+    LegArgs a{};
+    a.idx = idx; a.w = w; a.alpha = alpha; a.idx_out = idx_out; a.w_out = w_out;
+    a.n = n; a.hkv = hkv; a.K = K; a.s = s; a.U = B * n * hkv; a.BN = B * n;
+    return dispatch<true>(a, st);
+}
+
+hipError_t launch_leg_mix_backward(int B, int n, int hkv, const int32_t* idx, const float* w,
+                                   int K, const float* alpha, const int32_t* idx_out,
+                                   const float* w_out, int s, const float* dleg, float* dw,
+                                   float* dalpha, double* part, hipStream_t st) {
+    LegArgs a{};
+    a.idx = idx; a.w = w; a.alpha = alpha; a.idx_out = const_cast<int32_t*>(idx_out);
+    a.w_out = const_cast<float*>(w_out); a.dleg = dleg; a.dw = dw; a.dalpha = dalpha;
+    a.part = part;
+    a.n = n; a.hkv = hkv; a.K = K; a.s = s; a.U = B * n * hkv; a.BN = B * n;
+    a.nchunk = (a.BN + kLegTokens - 1) / kLegTokens;
+    return dispatch<false>(a, st);
+}
+
+}  // namespace gm

@@ -35,7 +35,7 @@ def test_library_exports_every_declared_call(lib):
     assert set(names) == set(binding.EXPORTS)
     for name in names:
         assert hasattr(lib, name), name
-    assert lib.gm_abi_version() == 3
+    assert lib.gm_abi_version() == 4
 
 
 def test_status_strings(lib):
@@ -125,6 +125,27 @@ def test_decode_step_argument_checks(lib):
     assert f(*args(qq=None)) == NULL
     assert f(*args(qq=fake(0x300008))) == ALIGN
     assert f(*args(oo=q)) == ALIAS             # o on q
+
+
+def test_leg_mix_argument_checks(lib):
+    f, g = lib.gm_leg_mix_forward, lib.gm_leg_mix_backward
+    i, w, al = fake(0x100000), fake(0x200000), fake(0x300000)
+    io, wo = fake(0x400000), fake(0x500000)
+    assert f(8, 4096, 8, i, w, 65, al, 4, io, wo, None) == UNSUP     # K > 64
+    assert f(8, 4096, 8, i, w, 16, al, 0, io, wo, None) == UNSUP     # s < 1
+    assert f(8, 4096, 8, i, w, 16, None, 4, io, wo, None) == NULL
+    assert f(8, 4096, 8, i, w, 16, al, 4, i, wo, None) == ALIAS      # idx_out on idx
+    assert f(0, 4096, 8, None, None, 16, None, 4, None, None, None) == OK
+    need = lib.gm_leg_mix_backward_workspace_bytes(8, 4096, 8, 16)
+    assert need == 8 * 512 * 16 * 8                                   # fp64 partial per 64 tokens
+    dl, dw, da, ws = fake(0x600000), fake(0x10000000), fake(0x700000), fake(0x20000000)
+    args = [8, 4096, 8, i, w, 16, al, io, wo, 4, dl, dw, da, ws, need, None]
+    bad = list(args); bad[14] = need - 1
+    assert g(*bad) == WS
+    bad = list(args); bad[12] = None
+    assert g(*bad) == NULL
+    bad = list(args); bad[11] = w                                      # dw on w
+    assert g(*bad) == ALIAS
 
 
 def test_ser_backward_workspace_checks(lib):

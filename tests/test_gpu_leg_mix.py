@@ -1,0 +1,62 @@
+"""GPU parity of leg construction (gm_leg_mix_forward / _backward) against
+the oracle: legs bit-exact (indices and weights), dw and dalpha within 1e-5
+(fp32 rounding of fp64 sums; dalpha sums up to B*n terms)."""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+import cases
+import oracle
+import sparse_dynamic_routing_amd as gm
+from gpu_util import assert_close, assert_ser_match, dev, host, say
+
+pytestmark = pytest.mark.gpu
+
+LEG_CASES = [
+    # B, n, hkv, K, s, ties
+    (2, 70, 2, 16, 4, False),     # the stored-edge count of the K16 models
+    (2, 70, 2, 16, 4, True),      # exact ties: lower index first
+    (1, 50, 3, 24, 4, False),     # K24: 32-lane teams
+    (2, 33, 2, 5, 8, False),      # more slots than candidates: padding
+    (1, 40, 1, 64, 16, True),     # a full wave per unit
+    (3, 17, 2, 1, 2, False),      # one stored slot
+    (8, 4096, 8, 16, 4, False),   # full size: B = 8, n = 4096, 8 KV heads
+]
+
+
+@pytest.mark.parametrize("B,n,hkv,K,s,ties", LEG_CASES,
+                         ids=[f"B{c[0]}-n{c[1]}-h{c[2]}-K{c[3]}-s{c[4]}{'-ties' if c[5] else ''}"
+                              for c in LEG_CASES])
+def test_leg_mix_forward_backward(B, n, hkv, K, s, ties):
+    say(f"case leg mix B={B} n={n} hkv={hkv} K={K} s={s} ties={ties}")
+    rng = np.random.default_rng(B * 1000 + K * 10 + s)
+    idx, w = cases.edges(rng, B, n, hkv, K, pad_frac=0.1, dead_frac=0.05, ties=ties)
+    alpha = (rng.choice(cases.TIE_WEIGHTS, size=(hkv, K)) if ties
+             else rng.random((hkv, K)) + 0.05).astype(np.float32)
+    alpha[rng.random(alpha.shape) < 0.1] = 0.0
+    io, wo = gm.leg_mix(dev(idx), dev(w), dev(alpha), s)
+    dleg = rng.standard_normal((B, n, hkv, s)).astype(np.float32)
+    dw, da = gm.leg_mix_backward(dev(idx), dev(w), dev(alpha), io, wo, dev(dleg))
+    torch.cuda.synchronize()
+    orc = oracle.get()
+    rio, rwo = orc.leg_mix_forward(idx, w, alpha, s)
+    assert_ser_match(host(io), host(wo), rio, rwo)
+    np.testing.assert_array_equal(host(wo), rwo)
+    rdw, rda = orc.leg_mix_backward(idx, w, alpha, rio, rwo, dleg)
+    assert_close("dw", host(dw), rdw, 1e-5)
+    assert_close("dalpha", host(da), rda, 1e-5)
+
+
+def test_leg_mix_backward_deterministic():
+    """dalpha is reduced in a fixed order: two runs agree bitwise."""
+    rng = np.random.default_rng(3)
+    idx, w = cases.edges(rng, 4, 1000, 4, 16)
+    alpha = (rng.random((4, 16)) + 0.1).astype(np.float32)
+    io, wo = gm.leg_mix(dev(idx), dev(w), dev(alpha), 4)
+    dleg = dev(rng.standard_normal(io.shape).astype(np.float32))
+    a = gm.leg_mix_backward(dev(idx), dev(w), dev(alpha), io, wo, dleg)
+    b = gm.leg_mix_backward(dev(idx), dev(w), dev(alpha), io, wo, dleg)
+    torch.cuda.synchronize()
+    assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
