@@ -71,9 +71,12 @@ class Oracle:
         lib.oracle_leg_mix_backward.argtypes = [
             ctypes.c_int, ctypes.c_int, ctypes.c_int, _i32p, _f64p, ctypes.c_int, _f64p,
             _i32p, _f64p, ctypes.c_int, _f64p, _f64p, _f64p]
+        lib.oracle_dense_refresh.argtypes = [
+            ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+            ctypes.c_double, _f64p, _f64p, ctypes.c_int, _i32p, _f32p, _f64p]
         for f in ("oracle_ser_forward", "oracle_sea_forward",
                   "oracle_sea_backward", "oracle_ser_backward",
-                  "oracle_leg_mix_forward", "oracle_leg_mix_backward"):
+                  "oracle_leg_mix_forward", "oracle_leg_mix_backward", "oracle_dense_refresh"):
             getattr(lib, f).restype = ctypes.c_int
         self.lib = lib
 
@@ -207,6 +210,23 @@ class Oracle:
             self._p(dw, _f64p), self._p(da, _f64p))
         self._check(rc, "leg_mix_backward")
         return dw, da
+
+
+    def dense_refresh(self, q, k, s, scale=None):
+        """Refresh edges (idx int32, w float32 [B,n,hkv,s]) and the per-head
+        log-sum-exp (float64 [B,n,hq]) of dense causal attention."""
+        q = self._np(q, np.float64); k = self._np(k, np.float64)
+        B, n, hq, d = q.shape
+        hkv = k.shape[2]
+        scale = 1.0 / np.sqrt(d) if scale is None else float(scale)
+        io = np.empty((B, n, hkv, s), np.int32)
+        wo = np.empty((B, n, hkv, s), np.float32)
+        lse = np.empty((B, n, hq), np.float64)
+        rc = self.lib.oracle_dense_refresh(B, n, hq, hkv, d, scale, self._p(q, _f64p),
+                                           self._p(k, _f64p), s, self._p(io, _i32p),
+                                           self._p(wo, _f32p), self._p(lse, _f64p))
+        self._check(rc, "dense_refresh")
+        return io, wo, lse
 
 
 _default: Oracle | None = None

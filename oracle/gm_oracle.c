@@ -27,6 +27,9 @@
  *   Leg construction: a token's stored edges mixed into a leg and
  *        sparsified ([ai.info] Methodology, referral paragraph; the mixing
  *        itself is a reading, stated at the function), forward and backward.
+ *   Refresh edges: the top positions of a dense attention layer
+ *        ([ai.info] Methodology, referral paragraph; the ranking is a
+ *        reading, stated at the function).
  *
  * Layouts (row-major): q, o, dout, dq [B,n,hq,d]; k, v, dk, dv [B,n,hkv,d];
  * edges idx [B,n,hkv,s] int32 and w [B,n,hkv,s].  Query head hq reads KV head
@@ -40,6 +43,7 @@
 #include <math.h>
 #include <stdint.h>
 #include <stddef.h>
+#include <stdlib.h>
 #include <string.h>
 
 #define ORACLE_ERR_INDEX (-1)
@@ -441,5 +445,67 @@ int oracle_leg_mix_backward(int B, int n, int hkv, const int32_t* idx, const dou
             }
         }
     }
+    return 0;
+}
+
+/*
+ * Refresh edges from a dense attention layer ([ai.info] Methodology,
+ * referral paragraph: optional refresh edges pull in the top-k positions of
+ * the most recent dense-attention layer; Main Findings: refresh helps).  The
+ * pages do not define the ranking; reading: per unit (b, i, h) over the
+ * causal positions j <= i, the group-mean attention probability
+ *   pbar_j = (1/G) sum_g softmax_j(scale * q[i, h*G+g] . k[j, h])
+ * ranks the positions; keep the s largest (equal values to the lower index),
+ * weight = pbar_j rounded to fp32; unused slots (0, 0).  lse[b, i, hq]
+ * receives each query head's log-sum-exp of its scaled scores.
+ */
+int oracle_dense_refresh(int B, int n, int hq, int hkv, int d, double scale,
+                         const double* q, const double* k, int s,
+                         int32_t* idx_out, float* w_out, double* lse) {
+    if (B < 0 || n < 0 || hkv <= 0 || hq % hkv != 0 || d < 1 || s < 1) return ORACLE_ERR_ARGS;
+    int G = hq / hkv;
+    double* sc = (double*)malloc((size_t)n * sizeof(double));
+    double* pbar = (double*)malloc((size_t)n * sizeof(double));
+    int* taken = (int*)malloc((size_t)n * sizeof(int));
+    if (!sc || !pbar || !taken) { free(sc); free(pbar); free(taken); return ORACLE_ERR_ARGS; }
+    for (int b = 0; b < B; ++b)
+    for (int i = 0; i < n; ++i)
+    for (int h = 0; h < hkv; ++h) {
+        for (int j = 0; j <= i; ++j) pbar[j] = 0.0;
+        for (int g = 0; g < G; ++g) {
+            int head = h * G + g;
+            const double* qv = q + (((size_t)b * n + i) * hq + head) * d;
+            double mx = -INFINITY;
+            for (int j = 0; j <= i; ++j) {
+                const double* kv = k + row(b, j, h, n, hkv) * d;
+                double dot = 0.0;
+                for (int c = 0; c < d; ++c) dot += qv[c] * kv[c];
+                sc[j] = scale * dot;
+                if (sc[j] > mx) mx = sc[j];
+            }
+            double z = 0.0;
+            for (int j = 0; j <= i; ++j) z += exp(sc[j] - mx);
+            lse[((size_t)b * n + i) * hq + head] = mx + log(z);
+            for (int j = 0; j <= i; ++j) pbar[j] += exp(sc[j] - mx) / z / G;
+        }
+        size_t r = row(b, i, h, n, hkv);
+        for (int j = 0; j <= i; ++j) taken[j] = 0;
+        for (int slot = 0; slot < s; ++slot) {
+            int best = -1;
+            for (int j = 0; j <= i; ++j) {
+                if (taken[j] || !(pbar[j] > 0.0)) continue;
+                if (best < 0 || pbar[j] > pbar[best]) best = j;   /* j ascending: ties keep the lower */
+            }
+            if (best < 0) {
+                idx_out[r * s + slot] = 0;
+                w_out[r * s + slot] = 0.0f;
+            } else {
+                taken[best] = 1;
+                idx_out[r * s + slot] = best;
+                w_out[r * s + slot] = (float)pbar[best];
+            }
+        }
+    }
+    free(sc); free(pbar); free(taken);
     return 0;
 }

@@ -52,6 +52,11 @@ MUTANTS = [
      "cand_acc[found] += alpha[(size_t)(hkv - 1 - h) * K + k] * w[r * K + k];"),
     ("leg bwd: dalpha from the mixing weight", "oracle_leg_mix_backward",
      "dalpha[(size_t)h * K + k] += g * x;", "dalpha[(size_t)h * K + k] += g * a;"),
+    ("refresh: ranking by the last head only", "oracle_dense_refresh",
+     "for (int j = 0; j <= i; ++j) pbar[j] += exp(sc[j] - mx) / z / G;",
+     "for (int j = 0; j <= i; ++j) pbar[j] = exp(sc[j] - mx) / z;"),
+    ("refresh: unscaled scores", "oracle_dense_refresh",
+     "sc[j] = scale * dot;", "sc[j] = dot;"),
     ("ser bwd: leg operands swapped", "oracle_ser_backward",
      "dw1[r1 * s2 + a] += gt * y;", "dw1[r1 * s2 + a] += gt * x;"),
     ("ser bwd: padding slots of A' pass gradient", "oracle_ser_backward",
@@ -80,6 +85,7 @@ PINS = [
     pins.test_leg_mix_matches_dense_mixture,
     pins.test_leg_mix_single_slot_closed_form,
     pins.test_leg_mix_backward_matches_dense_and_differences,
+    pins.test_dense_refresh_matches_dense_attention,
 ]
 
 

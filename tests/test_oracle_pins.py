@@ -472,3 +472,55 @@ def test_leg_mix_backward_matches_dense_and_differences(orc):
         p, m = alpha.copy(), alpha.copy()
         p[h, k] += eps; m[h, k] -= eps
         assert abs((f(wd, p) - f(wd, m)) / (2 * eps) - da[h, k]) < 1e-6
+
+
+# --------------------------------------------------------- refresh edges
+def test_dense_refresh_matches_dense_attention(orc):
+    """Refresh edges against dense causal attention (tests/dense_ref.py with
+    every earlier position an edge of weight 1): the per-head log-sum-exp,
+    and the group-mean probabilities of the kept positions, which must be
+    the s largest (equal values to the lower index)."""
+    rng = np.random.default_rng(11)
+    for case in range(12):
+        hkv, G = int(rng.integers(1, 3)), int(rng.integers(1, 4))
+        B, n, d, s = 1 + case % 2, int(rng.integers(1, 30)), 8, int(rng.integers(1, 6))
+        q = rng.standard_normal((B, n, hkv * G, d))
+        k = rng.standard_normal((B, n, hkv, d))
+        if case % 3 == 0:
+            q[:, :, :, :] = np.round(q * 2) / 2           # repeated scores: ties
+            k[:, :, :, :] = np.round(k * 2) / 2
+        io, wo, lse = orc.dense_refresh(q, k, s)
+        full = np.broadcast_to(np.arange(n).reshape(1, n, 1, 1), (B, n, hkv, n)).copy()
+        full = np.minimum(full, np.arange(n).reshape(1, 1, 1, n)).astype(np.int32)
+        wfull = (np.arange(n).reshape(1, 1, 1, n) <= np.arange(n).reshape(1, n, 1, 1))
+        wfull = np.broadcast_to(wfull, (B, n, hkv, n)).astype(np.float32)
+        P = dense_ref.sea_probs(q, k, full, wfull)          # [B, hq, n, n]
+        pbar = P.reshape(B, hkv, G, n, n).mean(axis=2)       # [B, hkv, n, n]
+        scores = np.einsum("bihd,bjhd->bhij", q, np.repeat(k, G, axis=2)) / np.sqrt(d)
+        mask = np.tril(np.ones((n, n), bool))
+        ref_lse = np.log(np.where(mask, np.exp(scores), 0.0).sum(-1))
+        np.testing.assert_allclose(lse, ref_lse.transpose(0, 2, 1), rtol=1e-12, atol=1e-12)
+        for b in range(B):
+            for i in range(n):
+                for h in range(hkv):
+                    assert_valid_top(io[b, i, h], wo[b, i, h], pbar[b, h, i, :i + 1], s)
+
+
+def assert_valid_top(idx, w, row, s, rel=1e-9):
+    """idx/w is the top-s of ``row`` (values desc, equal values to the lower
+    index), with values equal when they agree within ``rel`` (the reference
+    rounds its sums differently)."""
+    m = min(s, len(row))
+    order = np.argsort(-row, kind="stable")
+    kth = row[order[m - 1]]
+    tol = rel * max(float(row.max()), 1e-300)
+    picked = idx[:m]
+    assert len(set(picked.tolist())) == m, picked
+    assert (row[picked] >= kth - tol).all(), (picked, row[picked], kth)
+    for a, b_ in zip(picked[:-1], picked[1:]):
+        va, vb = row[a], row[b_]
+        assert va >= vb - tol, (picked, row[picked])
+        if abs(va - vb) <= tol:
+            assert a < b_, (picked, row[picked])
+    np.testing.assert_allclose(w[:m], row[picked].astype(np.float32), rtol=1e-6)
+    assert (idx[m:] == 0).all() and (w[m:] == 0).all()
