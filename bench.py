@@ -45,6 +45,7 @@ import synth  # noqa: E402
 METRIC = ("SER+SEA fwd+bwd tokens·KV-heads/s at n=4096,s1=4; "
           "achieved HBM GB/s vs peak")
 PEAK_HBM_GBS = 8000.0
+PEAK_BF16_TFLOPS = 2500.0      # dense bf16 matrix-core peak (no sparsity)
 
 # Algorithmic (compulsory) bytes per unit: every input byte read once, every
 # output byte written once; K/V counted once per unit (unique rows).
@@ -127,7 +128,7 @@ def parse():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", default="metric",
-                    choices=list(CONFIG_STAGES) + ["decode", "legmix"],
+                    choices=list(CONFIG_STAGES) + ["decode", "legmix", "refresh"],
                     help="workload: the measured pass (default) or one of the other "
                          "configurations, timed on its own stages (no CPU baseline)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -423,6 +424,45 @@ def run_legmix(a):
         "steps": a.steps, "warmup": a.warmup, "data": "synthetic"}), flush=True)
 
 
+def run_refresh(a):
+    """Refresh edges from the dense layer of the measured model (B = 8,
+    n = 4096, 16 query / 8 KV heads, d = 128, bf16, s = 4): the full call
+    (lse pass + selection pass) and the selection alone (lse given, as when
+    the dense layer saves its own).  One JSON line; the score contraction is
+    priced against the bf16 matrix-core peak."""
+    p = synth.PRESETS["metric"]
+    s = 4
+    seed = synth.BASE_SEED + 40
+    q = synth.normal(seed, "q", (p.B, p.n, p.hq, p.d), torch.bfloat16, 0, "cuda")
+    k = synth.normal(seed, "k", (p.B, p.n, p.hkv, p.d), torch.bfloat16, 0, "cuda")
+    shp = (p.B, p.n, p.hkv, s)
+    io = torch.empty(shp, dtype=torch.int32, device="cuda")
+    wo = torch.empty(shp, dtype=torch.float32, device="cuda")
+    lse = torch.empty((p.B, p.n, p.hq), dtype=torch.float32, device="cuda")
+    full = lambda: gm.gm_dense_refresh(q, k, lse, io, wo)  # noqa: E731
+    sel = lambda: gm.gm_dense_refresh(q, k, lse, io, wo, lse_given=True)  # noqa: E731
+    for _ in range(a.warmup):
+        full(); sel()
+    torch.cuda.synchronize()
+    e = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+    tf = ts = 0.0
+    for _ in range(a.steps):
+        e[0].record(); full(); e[1].record(); sel(); e[2].record()
+        torch.cuda.synchronize()
+        tf += e[0].elapsed_time(e[1]); ts += e[1].elapsed_time(e[2])
+    tf, ts = tf / a.steps, ts / a.steps
+    pairs = p.B * p.hq * p.n * (p.n + 1) // 2          # causal (token, key, query head)
+    flops = 2 * p.d * pairs                            # one score contraction
+    print(json.dumps({
+        "config": "refresh", "B": p.B, "n": p.n, "hq": p.hq, "hkv": p.hkv, "d": p.d, "s": s,
+        "full_us": tf * 1e3, "select_us": ts * 1e3, "lse_pass_us": (tf - ts) * 1e3,
+        "tokens_per_s": p.B * p.n / (tf * 1e-3),
+        "score_flops_per_pass": flops,
+        "select_tflops": flops / (ts * 1e-3) / 1e12, "mfma_peak_tflops": PEAK_BF16_TFLOPS,
+        "scores_per_s": pairs / (ts * 1e-3),
+        "steps": a.steps, "warmup": a.warmup, "data": "synthetic"}), flush=True)
+
+
 def profiled_step_bytes(config: str):
     """Counter bytes per step from profiles/<config>_kernels.md, or None when
     it is missing or the kernel sources changed since."""
@@ -497,6 +537,9 @@ def main():
         return
     if a.config == "legmix":
         run_legmix(a)
+        return
+    if a.config == "refresh":
+        run_refresh(a)
         return
     if a.config != "metric":
         run_config(a)

@@ -247,6 +247,33 @@ gm_status gm_decode_step(int B, int T, int hq, int hkv, int d, gm_dtype dt, floa
                          int32_t* idx_out, float* w_out, void* o, hipStream_t stream);
 
 /*
+ * Refresh edges from a dense causal attention layer (ai.info Methodology,
+ * referral paragraph: optional refresh edges bring in the positions the most
+ * recent dense attention layer attends to most).  Per (b, token i, KV head h)
+ * with G = hq / hkv query heads q_g in the group:
+ *   lse_g = log sum_{j<=i} exp(scale q_g . k_j)
+ *   pbar_j = (1/G) sum_g exp(scale q_g . k_j - lse_g),   j <= i
+ * The s positions of largest pbar_j (equal values: the lower j first) with
+ * weight pbar_j, sorted by weight; slots past the i+1 positions hold (0, 0).
+ *   in   q [B][n][hq][d], k [B][n][hkv][d] bf16 (the dense layer's queries
+ *        and keys after any position encoding); lse_given != 0: lse holds
+ *        the layer's own per-head log-sum-exp (natural log) and only the
+ *        selection runs
+ *   out  idx_out [B][n][hkv][s] int32, w_out [B][n][hkv][s] fp32 (an edge
+ *        tensor as SER and SEA take it); lse [B][n][hq] fp32, written when
+ *        lse_given == 0
+ * Limits: dt GM_BF16 only; (d, G) in {64: 1,2,4,8; 128: 1,2,4; 256: 1,2};
+ * 1 <= s <= 8; scale positive and finite.  q, k 16-byte aligned; lse, idx_out, w_out 4-byte aligned;
+ * no output may overlap an input or another output.  Two launches (one with
+ * lse_given); no workspace.  Scores are fp32 sums of bf16 products on the
+ * matrix cores, so positions whose pbar differ by less than that rounding
+ * may come out in either order.
+ */
+gm_status gm_dense_refresh(int B, int n, int hq, int hkv, int d, gm_dtype dt, float scale,
+                           const void* q, const void* k, int s, int lse_given, float* lse,
+                           int32_t* idx_out, float* w_out, hipStream_t stream);
+
+/*
  * Debug validator of an edge tensor.  Adds to counts[0] the number of slots
  * whose index lies outside [0, i] or whose weight is negative or not finite,
  * and to counts[1] the number of live slots (w > 0), i.e. the key/value rows

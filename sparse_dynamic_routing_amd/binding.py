@@ -24,7 +24,7 @@ GM_F32, GM_BF16 = 0, 1
 STATUS = {0: "GM_OK", 1: "GM_ERR_NULL", 2: "GM_ERR_SHAPE", 3: "GM_ERR_UNSUPPORTED",
           4: "GM_ERR_WORKSPACE", 5: "GM_ERR_HIP", 6: "GM_ERR_ALIGN", 7: "GM_ERR_ALIAS"}
 EXPORTS = ("gm_ser_forward", "gm_sea_forward", "gm_sea_backward_workspace_bytes",
-           "gm_sea_backward", "gm_decode_step", "gm_leg_mix_forward",
+           "gm_sea_backward", "gm_decode_step", "gm_dense_refresh", "gm_leg_mix_forward",
            "gm_leg_mix_backward_workspace_bytes", "gm_leg_mix_backward",
            "gm_ser_backward_workspace_bytes", "gm_ser_backward", "gm_check_edges",
            "gm_status_string", "gm_abi_version")
@@ -56,6 +56,7 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
                             _P, _P, _P, _P, _P, _Z, _P],
         "gm_decode_step": [_I, _I, _I, _I, _I, _I, _F, _P, _P, _I, _P, _P, _I, _I, _P, _P,
                            _P, _P, _P, _P, _P],
+        "gm_dense_refresh": [_I, _I, _I, _I, _I, _I, _F, _P, _P, _I, _I, _P, _P, _P, _P],
         "gm_leg_mix_forward": [_I, _I, _I, _P, _P, _I, _P, _I, _P, _P, _P],
         "gm_leg_mix_backward_workspace_bytes": [_I, _I, _I, _I],
         "gm_leg_mix_backward": [_I, _I, _I, _P, _P, _I, _P, _P, _P, _I, _P, _P, _P, _P, _Z,
@@ -191,6 +192,24 @@ def gm_decode_step(idx1, w1, idx2, w2, q, k, v, idx_out, w_out, o, scale=None,
     _call("gm_decode_step", B, T, hq, hkv, d, _act_dtype(q), scale, _ptr(idx1), _ptr(w1), s2,
           _ptr(idx2), _ptr(w2), s3, s1, _ptr(q), _ptr(k), _ptr(v), _ptr(idx_out), _ptr(w_out),
           _ptr(o), _stream(stream))
+
+
+def gm_dense_refresh(q, k, lse, idx_out, w_out, lse_given=False, scale=None,
+                     stream=None) -> None:
+    """Refresh edges idx_out/w_out [B, n, hkv, s] from dense causal attention
+    over q [B, n, hq, d], k [B, n, hkv, d] (bf16); lse [B, n, hq] fp32 is
+    written, or read when ``lse_given``."""
+    B, n, hq, d = q.shape
+    hkv = k.shape[2]
+    s = idx_out.shape[3]
+    _need(q, "q", (torch.bfloat16,))
+    _need(k, "k", (torch.bfloat16,), (B, n, hkv, d))
+    _need(lse, "lse", (torch.float32,), (B, n, hq))
+    _need(idx_out, "idx_out", (torch.int32,), (B, n, hkv, s))
+    _need(w_out, "w_out", (torch.float32,), idx_out.shape)
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    _call("gm_dense_refresh", B, n, hq, hkv, d, GM_BF16, scale, _ptr(q), _ptr(k), s,
+          1 if lse_given else 0, _ptr(lse), _ptr(idx_out), _ptr(w_out), _stream(stream))
 
 
 def gm_leg_mix_forward(idx, w, alpha, idx_out, w_out, stream=None) -> None:
@@ -332,6 +351,20 @@ def decode_step(idx1, w1, idx2, w2, q, k, v, s1, scale=None, stream=None):
     o = torch.empty_like(q)
     gm_decode_step(idx1, w1, idx2, w2, q, k, v, idx_out, w_out, o, scale, stream)
     return idx_out, w_out, o
+
+
+def dense_refresh(q, k, s, lse=None, scale=None, stream=None):
+    """(idx_out, w_out, lse) of the refresh edges (see gm_dense_refresh); a
+    given ``lse`` (the dense layer's own) skips the first pass."""
+    B, n, hq, _ = q.shape
+    hkv = k.shape[2]
+    idx_out = torch.empty((B, n, hkv, s), dtype=torch.int32, device=q.device)
+    w_out = torch.empty((B, n, hkv, s), dtype=torch.float32, device=q.device)
+    given = lse is not None
+    if not given:
+        lse = torch.empty((B, n, hq), dtype=torch.float32, device=q.device)
+    gm_dense_refresh(q, k, lse, idx_out, w_out, given, scale, stream)
+    return idx_out, w_out, lse
 
 
 def leg_mix(idx, w, alpha, s, stream=None):

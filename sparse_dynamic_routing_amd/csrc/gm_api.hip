@@ -62,7 +62,7 @@ bool overlaps(const void* a, size_t an, const void* b, size_t bn) {
 
 extern "C" {
 
-int gm_abi_version(void) { return 4; }
+int gm_abi_version(void) { return 5; }
 
 const char* gm_status_string(gm_status s) {
     switch (s) {
@@ -221,6 +221,37 @@ gm_status gm_decode_step(int B, int T, int hq, int hkv, int d, gm_dtype dt, floa
     return hip_status(gm::launch_decode_step(B, T, hq, hkv, d, dt == GM_BF16, scale, idx1, w1,
                                              s2, idx2, w2, s3, s1, q, k, v, idx_out, w_out, o,
                                              stream));
+}
+
+gm_status gm_dense_refresh(int B, int n, int hq, int hkv, int d, gm_dtype dt, float scale,
+                           const void* q, const void* k, int s, int lse_given, float* lse,
+                           int32_t* idx_out, float* w_out, hipStream_t stream) {
+    gm_status st = check_units(B, n, hkv);
+    if (st != GM_OK) return st;
+    if (hq < 0) return GM_ERR_SHAPE;
+    if (hkv == 0) return empty(B, n, hkv) ? GM_OK : GM_ERR_SHAPE;
+    if (hq == 0 || hq % hkv != 0) return GM_ERR_UNSUPPORTED;
+    if (dt != GM_BF16 || !gm::dense_refresh_supported(d, hq / hkv, s)) return GM_ERR_UNSUPPORTED;
+    if (!(scale > 0.0f) || scale > 3.4e38f) return GM_ERR_UNSUPPORTED;   // positive and finite
+    if ((long long)B * n * hq * d >= (1ll << 46)) return GM_ERR_SHAPE;
+    if (empty(B, n, hkv)) return GM_OK;
+    if (!q || !k || !lse) return GM_ERR_NULL;
+    if ((st = check_edge_ptrs(idx_out, w_out)) != GM_OK) return st;
+    if (!aligned(q, 16) || !aligned(k, 16) || !aligned(lse, 4)) return GM_ERR_ALIGN;
+    const size_t qb = (size_t)B * n * hq * d * 2, kb = (size_t)B * n * hkv * d * 2;
+    const size_t lb = (size_t)B * n * hq * 4, eb = (size_t)B * n * hkv * s * 4;
+    const void* ins[2] = {q, k};
+    const size_t inb[2] = {qb, kb};
+    const void* outs[3] = {lse, idx_out, w_out};
+    const size_t outb[3] = {lb, eb, eb};
+    for (int a = 0; a < 3; ++a) {
+        for (int b = 0; b < 2; ++b)
+            if (overlaps(outs[a], outb[a], ins[b], inb[b])) return GM_ERR_ALIAS;
+        for (int b = a + 1; b < 3; ++b)
+            if (overlaps(outs[a], outb[a], outs[b], outb[b])) return GM_ERR_ALIAS;
+    }
+    return hip_status(gm::launch_dense_refresh(B, n, hq, hkv, d, scale, q, k, s, lse_given != 0,
+                                               lse, idx_out, w_out, stream));
 }
 
 size_t gm_sea_backward_workspace_bytes(int B, int n, int hq, int hkv, int s1) {

@@ -48,6 +48,14 @@ hipError_t launch_decode_step(int B, int T, int hq, int hkv, int d, bool bf16, f
                               const void* q, const void* k, const void* v, int32_t* idx_out,
                               float* w_out, void* o, hipStream_t st);
 
+// Refresh edges of a dense causal attention layer (bf16 q/k, MFMA scores):
+// the top-s positions per (batch, token, KV head) by group-mean probability,
+// and the per-head lse (computed first unless lse_given).
+bool dense_refresh_supported(int d, int G, int s);
+hipError_t launch_dense_refresh(int B, int n, int hq, int hkv, int d, float scale,
+                                const void* q, const void* k, int s, bool lse_given, float* lse,
+                                int32_t* idx_out, float* w_out, hipStream_t st);
+
 size_t sea_backward_workspace_bytes(long long U, int s, int G, int n);
 hipError_t launch_sea_backward(int B, int n, int hq, int hkv, int d, bool bf16, float scale,
                                const void* q, const void* k, const void* v,

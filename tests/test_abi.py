@@ -35,7 +35,7 @@ def test_library_exports_every_declared_call(lib):
     assert set(names) == set(binding.EXPORTS)
     for name in names:
         assert hasattr(lib, name), name
-    assert lib.gm_abi_version() == 4
+    assert lib.gm_abi_version() == 5
 
 
 def test_status_strings(lib):
@@ -125,6 +125,31 @@ def test_decode_step_argument_checks(lib):
     assert f(*args(qq=None)) == NULL
     assert f(*args(qq=fake(0x300008))) == ALIGN
     assert f(*args(oo=q)) == ALIAS             # o on q
+
+
+def test_dense_refresh_argument_checks(lib):
+    f = lib.gm_dense_refresh
+    q, k, ls = fake(0x1000000), fake(0x2000000), fake(0x300000)
+    io, wo = fake(0x400000), fake(0x500000)
+    args = lambda B=8, n=4096, hq=16, hkv=8, d=128, dt=1, s=4, qq=q, kk=k, l=ls, o=io, sc=0.1: (  # noqa
+        B, n, hq, hkv, d, dt, sc, qq, kk, s, 0, l, o, wo, None)
+    assert f(*args(sc=0.0)) == UNSUP
+    assert f(*args(sc=-0.1)) == UNSUP
+    assert f(*args(sc=float("inf"))) == UNSUP
+    assert f(*args(dt=0)) == UNSUP             # fp32 scores are not offered
+    assert f(*args(d=96)) == UNSUP
+    assert f(*args(d=256, hq=32)) == UNSUP     # G = 4 at d = 256: too many query registers
+    assert f(*args(s=9)) == UNSUP
+    assert f(*args(s=0)) == UNSUP
+    assert f(*args(hq=12)) == UNSUP
+    assert f(*args(n=-1)) == SHAPE
+    assert f(*args(B=0)) == OK                 # nothing to do
+    assert f(*args(kk=None)) == NULL
+    assert f(*args(l=None)) == NULL
+    assert f(*args(qq=fake(0x1000008))) == ALIGN
+    assert f(*args(o=fake(0x400002))) == ALIGN
+    assert f(*args(o=k)) == ALIAS              # idx_out on k
+    assert f(*args(l=fake(0x400000 + 4096))) == ALIAS   # lse on idx_out
 
 
 def test_leg_mix_argument_checks(lib):
