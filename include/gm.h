@@ -70,7 +70,7 @@ typedef enum { GM_F32 = 0, GM_BF16 = 1 } gm_dtype;
 /*
  * Sparse edge referral, forward: A' = Sparsify_s1(A1 A2)
  * (ai.info Key Contributions 3; Methodology: the first leg's indices fetch
- * the second leg's indices and weights; hard top-s selection).
+ * the second leg's indices and weights, then a hard cut to the s1 largest).
  *   in   idx1, w1  [B][n][hkv][s2]  leg 1 (row i of A1)
  *        idx2, w2  [B][n][hkv][s3]  leg 2 (row j of A2); may equal leg 1
  *   out  idx_out, w_out [B][n][hkv][s1]  must not overlap the legs
@@ -156,8 +156,8 @@ size_t gm_ser_backward_workspace_bytes(int B, int n, int hkv, int s2, int s3,
 
 /*
  * Sparse edge referral, backward: chain rule of gm_ser_forward with the
- * selection held fixed (ai.info Methodology: only retained weights get
- * gradients).
+ * selection held fixed (ai.info Methodology: gradients reach the kept
+ * weights alone).
  *   in   legs as for the forward; idx_out, w_out [B][n][hkv][s1] the A' the
  *        forward produced; dw_out [B][n][hkv][s1] the gradient of w_out
  *   out  dw1 [B][n][hkv][s2], dw2 [B][n][hkv][s3] fp32.  dw1 == dw2 is

@@ -23,7 +23,7 @@
  *        values ([ai.info] Key Contributions 3; Methodology, second job).
  *   Backward of both through the soft weights only: indices carry no
  *        gradient, and only retained edges receive one ([rit.work] what was
- *        done; [ai.info] Methodology, "only retained weights get gradients").
+ *        done; [ai.info] Methodology: gradients reach the kept weights alone).
  *   Leg construction: a token's stored edges mixed into a leg and
  *        sparsified ([ai.info] Methodology, referral paragraph; the mixing
  *        itself is a reading, stated at the function), forward and backward.
@@ -33,8 +33,8 @@
  *
  * Layouts (row-major): q, o, dout, dq [B,n,hq,d]; k, v, dk, dv [B,n,hkv,d];
  * edges idx [B,n,hkv,s] int32 and w [B,n,hkv,s].  Query head hq reads KV head
- * hq / (hq_count / hkv) (grouped heads, reading: edges are per KV head, the
- * pages count retrieval "per KV head").  Every floating value is double here;
+ * hq / (hq_count / hkv) (grouped heads, reading: edges are per KV head, since
+ * the pages count retrieved tokens for each KV head).  Every floating value is double here;
  * fp32 and bf16 inputs are exact in double.
  *
  * Return value of every function: 0, or a negative code when an input breaks
@@ -55,10 +55,10 @@ static size_t row(int b, int i, int h, int n, int hkv) {
 }
 
 /*
- * SER forward ([ai.info] Key Contributions 3: A' = Sparsify_s1(A1 A2),
- * "truncates the up-to-s2 s3 candidates back to s1"; Methodology: "uses the
- * first leg's indices to fetch the second leg's indices and weights,
- * composing two-hop paths into one-hop paths", "hard top-s selection";
+ * SER forward ([ai.info] Key Contributions 3: A' = Sparsify_s1(A1 A2), the
+ * s2*s3 candidates at most cut back to s1; Methodology: the first leg's
+ * indices select rows of the second leg, whose indices and weights turn each
+ * two-hop path into a one-hop edge, and a hard top-s keeps the budget;
  * [rit.work]: paths are merged and the heaviest addresses kept).
  *
  * For each unit (b, i, h):
@@ -302,7 +302,7 @@ int oracle_sea_backward(int B, int n, int hq, int hkv, int d, double scale,
 /*
  * SER backward: the chain rule through the forward's merge, with the
  * selection (the retained slots of A') held fixed ([ai.info] Methodology:
- * "only retained weights get gradients"; [rit.work]: hard selection keeps
+ * gradients reach the kept weights alone; [rit.work]: hard selection keeps
  * sparsity, only the kept variants get gradients).
  * For each unit (b, i, h), each path (a, c) with x = w1[i,a] > 0 and
  * y = w2[j,c] > 0 (j = idx1[i,a], m = idx2[j,c]) and each retained slot t of

@@ -3,8 +3,8 @@
 // Forward (ai.info "Graph Machine: Towards Better Pretraining via Edges",
 // Key Contributions 3: A' = Sparsify_s1(A1 A2) over the up-to s2*s3 two-hop
 // candidates; Methodology: the first leg's indices fetch the second leg's
-// indices and weights, hard top-s selection; rit.work article: paths to the
-// same address are merged and the heaviest kept).
+// indices and weights, then a hard cut to the s1 largest; rit.work article:
+// paths to the same address are merged and the heaviest kept).
 //
 // One lane per path: a team of L = pow2(s2*s3) lanes per unit (b, i, h);
 // lane a*s3 + c follows leg-1 slot a to token j and reads leg-2 slot c of
@@ -20,7 +20,7 @@
 //          their slot.  A ballot counts the owners; the remaining slots get
 //          the padding edge (0, 0.0f).
 //
-// Backward (ai.info Methodology: only retained weights get gradients): for
+// Backward (ai.info Methodology: gradients reach the kept weights alone): for
 // each path whose target is a retained slot t (w_out_t > 0) and whose two
 // leg weights are positive, dw1[i,a] += dw_out_t w2[j,c] and
 // dw2[j,c] += dw_out_t w1[i,a].  Contributions are added in fp64 with
