@@ -31,7 +31,8 @@
 // XCD keeps a fixed set of pairs.
 //
 // Two passes: the first keeps an online max/sum per (token, head) in base 2
-// (rescaled only on a new maximum) and writes lse (skipped when the caller
+// (rescaled only when a maximum passes the reference by a factor 2^16, a wavefront-
+// uniform branch that is rarely taken) and writes lse (skipped when the caller
 // passes the dense layer's own lse); the second recomputes the scores, forms
 // pbar and keeps the top list.  The four lanes of a token share, after
 // every 16 keys, the largest of their S-th kept values: a later key at or
@@ -67,6 +68,11 @@ struct RefreshArgs {
 // which changes no kept position (the largest probability of a token is at
 // least 1/n) and no log-sum-exp beyond 2^-126 relative
 __device__ __forceinline__ float fexp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+__device__ __forceinline__ float max4(float a, float b, float c, float d) {
+    return fmaxf(fmaxf(a, b), fmaxf(c, d));
+}
+constexpr float kSlack = 16.0f;
 
 // the largest of x over the four rows of the wavefront (lanes l%16 + 16c)
 __device__ __forceinline__ float max_over_rows(float x) {
@@ -269,11 +275,14 @@ __global__ __launch_bounds__(kRefWaves * kWave, 4) void refresh_kernel(RefreshAr
                             float x[4];
 #pragma unroll
                             for (int r = 0; r < 4; ++r) x[r] = live[r] ? sc[g][r] : -INFINITY;
-                            const float mx = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])) * a.c;
-                            // rescale only on a new maximum (rare once some keys are in)
-                            if (mx > m2[rt][g]) {
-                                z[rt][g] *= fexp2(m2[rt][g] - mx);
-                                m2[rt][g] = mx;
+                            const float mx = max4(x[0], x[1], x[2], x[3]) * a.c;
+                            // rescale only when some lane's maximum passes its
+                            // reference by kSlack (terms stay below 2^kSlack):
+                            // rare once a few hundred keys are in
+                            if (__builtin_amdgcn_ballot_w64(mx > m2[rt][g] + kSlack)) {
+                                const float mn = fmaxf(m2[rt][g], mx);
+                                z[rt][g] *= fexp2(m2[rt][g] - mn);
+                                m2[rt][g] = mn;
                             }
                             const float nm = -m2[rt][g];
                             z[rt][g] += (fexp2(fmaf(x[0], a.c, nm)) + fexp2(fmaf(x[1], a.c, nm))) +
@@ -288,7 +297,7 @@ __global__ __launch_bounds__(kRefWaves * kWave, 4) void refresh_kernel(RefreshAr
                             for (int g = 1; g < G; ++g) x += fexp2(fmaf(sc[g][r], a.c, -ls2[rt][g]));
                             pb[r] = live[r] ? x : 0.0f;
                         }
-                        const float mx = fmaxf(fmaxf(pb[0], pb[1]), fmaxf(pb[2], pb[3]));
+                        const float mx = max4(pb[0], pb[1], pb[2], pb[3]);
                         if (mx > thr[rt]) {
 #pragma unroll
                             for (int r = 0; r < 4; ++r)
