@@ -7,7 +7,9 @@
 // SER's selection (top s by fp32 weight, ties to the lower index, (0, 0)
 // padding).
 //
-// Forward: a team of L = max(16, pow2(K)) lanes per unit, lane k holding
+// Forward, K = 16 with 16-byte aligned rows and s = 4 or 2: one lane per
+// unit, SER's register network (below).  Otherwise a team of
+// L = max(16, pow2(K)) lanes per unit, lane k holding
 // stored slot k; the first lane of each target sums the later lanes of that
 // target in slot order (the definition's order and precision, so the
 // weights are bit-identical to the oracle's), and each candidate's rank
@@ -20,6 +22,7 @@
 // kernel adds the partials in a fixed order and rounds once (deterministic).
 #include "gm_common.h"
 #include "gm_internal.h"
+#include "gm_select.h"
 
 #include <utility>
 
@@ -216,6 +219,51 @@ __global__ __launch_bounds__(kBlock) void leg_mix_alpha_kernel(LegArgs a) {
     if (lane == 0) a.dalpha[e] = (float)s;
 }
 
+// K = 16 stored slots with 16-byte aligned rows: one lane per unit, the
+// whole row in registers (four 16-byte loads each of idx, w and the head's
+// alpha), merged and ranked by SER's register network; units chunked per XCD
+// as SER's are.  Same arithmetic and order as the team kernel, so the same
+// bits.
+template <int S>
+__global__ __launch_bounds__(kBlock) void leg_mix_vec_kernel(LegArgs a) {
+    static_assert(S == 2 || S == 4, "vector stores of 2 or 4 slots");
+    const int u = xcd_unit(a.U);
+    if (u < 0) return;
+    const int h = u % a.hkv;
+    int m[16];
+    double cw[16];
+    const int4* ir = reinterpret_cast<const int4*>(a.idx + (size_t)u * 16);
+    const float4* wr = reinterpret_cast<const float4*>(a.w + (size_t)u * 16);
+    const float4* ar = reinterpret_cast<const float4*>(a.alpha + (size_t)h * 16);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        const int4 i4 = ir[q];
+        const float4 w4 = wr[q], a4 = ar[q];
+        m[4 * q + 0] = i4.x; m[4 * q + 1] = i4.y; m[4 * q + 2] = i4.z; m[4 * q + 3] = i4.w;
+        cw[4 * q + 0] = (double)a4.x * (double)w4.x;
+        cw[4 * q + 1] = (double)a4.y * (double)w4.y;
+        cw[4 * q + 2] = (double)a4.z * (double)w4.z;
+        cw[4 * q + 3] = (double)a4.w * (double)w4.w;
+    }
+    uint64_t key[16];
+    top4_of_16(m, cw, key);
+    int om[4];
+    float ow[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        om[r] = key[r] ? (int)~(uint32_t)key[r] : 0;
+        ow[r] = key[r] ? __uint_as_float((uint32_t)(key[r] >> 32)) : 0.0f;
+    }
+    if constexpr (S == 4) {
+        *reinterpret_cast<int4*>(a.idx_out + (size_t)u * 4) = make_int4(om[0], om[1], om[2], om[3]);
+        *reinterpret_cast<float4*>(a.w_out + (size_t)u * 4) =
+            make_float4(ow[0], ow[1], ow[2], ow[3]);
+    } else {
+        *reinterpret_cast<int2*>(a.idx_out + (size_t)u * 2) = make_int2(om[0], om[1]);
+        *reinterpret_cast<float2*>(a.w_out + (size_t)u * 2) = make_float2(ow[0], ow[1]);
+    }
+}
+
 template <int L>
 void launch_fwd(const LegArgs& a, hipStream_t st) {
     const long long threads = (long long)a.U * L;
@@ -234,6 +282,17 @@ void launch_bwd(const LegArgs& a, hipStream_t st) {
 
 template <bool FWD>
 hipError_t dispatch(const LegArgs& a, hipStream_t st) {
+    const bool rows16 = ((uintptr_t)a.idx | (uintptr_t)a.w | (uintptr_t)a.alpha |
+                         (uintptr_t)a.idx_out | (uintptr_t)a.w_out) % 16 == 0;
+    if (FWD && a.K == 16 && (a.s == 4 || a.s == 2) && rows16) {   // lane per unit
+        if (a.s == 4)
+            hipLaunchKernelGGL(leg_mix_vec_kernel<4>, dim3(xcd_unit_grid(a.U)), dim3(kBlock), 0,
+                               st, a);
+        else
+            hipLaunchKernelGGL(leg_mix_vec_kernel<2>, dim3(xcd_unit_grid(a.U)), dim3(kBlock), 0,
+                               st, a);
+        return hipGetLastError();
+    }
     if (FWD && a.K <= 16) {   // 16-lane teams: the DPP sweeps
         launch_fwd<16>(a, st);
         return hipGetLastError();

@@ -28,6 +28,7 @@
 // once to fp32.  When dw1 and dw2 alias, one workspace receives both.
 #include "gm_common.h"
 #include "gm_internal.h"
+#include "gm_select.h"
 #include "gm_wave.h"
 
 namespace gm {
@@ -177,23 +178,6 @@ struct SerUnitArgs {
 
 constexpr int kSmax = 4;
 constexpr int kCand = kSmax * kSmax;
-
-// Unit of this lane when units are split into 8 contiguous chunks, one per
-// XCD (workgroups are dealt to XCDs round robin): every chunk holds whole
-// batches (or a contiguous part of one), i.e. all KV heads of its tokens, so
-// the small edge rows it gathers share cache lines and stay in its L2.
-// Launch with kXcds * ceil(ceil(U / 8) / kBlock) workgroups; -1: no unit.
-__device__ __forceinline__ int xcd_unit(int U) {
-    const int chunk = (U + kXcds - 1) / kXcds;
-    const int x = blockIdx.x % kXcds;
-    const int q = (int)(blockIdx.x / kXcds) * kBlock + (int)threadIdx.x;
-    const int u = x * chunk + q;
-    return (q < chunk && u < U) ? u : -1;
-}
-inline unsigned xcd_unit_grid(int U) {
-    const int chunk = (U + kXcds - 1) / kXcds;
-    return (unsigned)(kXcds * ((chunk + kBlock - 1) / kBlock));
-}
 
 // Token i of unit u (u = (b*n + i)*hkv + h); the row of token j of the same
 // (b, h) is u + (j - i) * hkv.
@@ -356,26 +340,6 @@ __device__ __forceinline__ void load_paths_vec(const SerUnitArgs& a, int u, int 
     }
 }
 
-// compare-exchange: k[i] >= k[j] afterwards
-__device__ __forceinline__ void cx(uint64_t& hi, uint64_t& lo) {
-    const bool sw = lo > hi;
-    const uint64_t t = sw ? lo : hi;
-    lo = sw ? hi : lo;
-    hi = t;
-}
-__device__ __forceinline__ void sort4_desc(uint64_t* k) {
-    cx(k[0], k[1]); cx(k[2], k[3]);
-    cx(k[0], k[2]); cx(k[1], k[3]);
-    cx(k[1], k[2]);
-}
-// top 4 of two descending runs of 4, descending, into a
-__device__ __forceinline__ void merge_top4(uint64_t* a, const uint64_t* b) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) a[i] = a[i] > b[3 - i] ? a[i] : b[3 - i];   // bitonic
-    cx(a[0], a[2]); cx(a[1], a[3]);
-    cx(a[0], a[1]); cx(a[2], a[3]);
-}
-
 // S1: retained slots (4, or 2 for the narrower top-2-of-16 budget).
 template <int S1>
 __global__ __launch_bounds__(kBlock) void ser_fwd_vec_kernel(SerUnitArgs a) {
@@ -385,38 +349,11 @@ __global__ __launch_bounds__(kBlock) void ser_fwd_vec_kernel(SerUnitArgs a) {
     int m[kCand];
     float x[kSmax], y[kCand];
     load_paths_vec(a, u, m, x, y);
-    // a candidate that repeats an earlier target gets bit 31 of its target
-    // set (targets are >= 0): it then matches no later candidate, whose
-    // weight goes to the earlier, first candidate of the target instead
-    double cw[kCand], acc[kCand];
+    double cw[kCand];
 #pragma unroll
-    for (int k = 0; k < kCand; ++k) {
-        cw[k] = (double)x[k / kSmax] * (double)y[k];
-        acc[k] = cw[k];
-    }
-#pragma unroll
-    for (int k = 1; k < kCand; ++k) {
-        uint32_t dup = 0;
-#pragma unroll
-        for (int k2 = 0; k2 < k; ++k2) {
-            const bool same = m[k2] == m[k];
-            acc[k2] += same ? cw[k] : 0.0;
-            dup |= same ? 0x80000000u : 0u;
-        }
-        m[k] = (int)((uint32_t)m[k] | dup);
-    }
+    for (int k = 0; k < kCand; ++k) cw[k] = (double)x[k / kSmax] * (double)y[k];
     uint64_t key[kCand];
-#pragma unroll
-    for (int k = 0; k < kCand; ++k) {
-        const float wk = (float)acc[k];
-        key[k] = m[k] >= 0 && wk > 0.0f
-                     ? ((uint64_t)__float_as_uint(wk) << 32) | (uint32_t)~(uint32_t)m[k]
-                     : 0ull;
-    }
-    sort4_desc(key + 0); sort4_desc(key + 4); sort4_desc(key + 8); sort4_desc(key + 12);
-    merge_top4(key + 0, key + 4);
-    merge_top4(key + 8, key + 12);
-    merge_top4(key + 0, key + 8);
+    top4_of_16(m, cw, key);
     int om[4];
     float ow[4];
 #pragma unroll

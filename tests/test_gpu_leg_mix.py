@@ -18,6 +18,7 @@ LEG_CASES = [
     # B, n, hkv, K, s, ties
     (2, 70, 2, 16, 4, False),     # the stored-edge count of the K16 models
     (2, 70, 2, 16, 4, True),      # exact ties: lower index first
+    (2, 70, 2, 16, 2, True),      # top-2 legs (the narrower budget), ties
     (1, 50, 3, 24, 4, False),     # K24: 32-lane teams
     (2, 33, 2, 5, 8, False),      # more slots than candidates: padding
     (1, 40, 1, 64, 16, True),     # a full wave per unit
@@ -60,3 +61,28 @@ def test_leg_mix_backward_deterministic():
     b = gm.leg_mix_backward(dev(idx), dev(w), dev(alpha), io, wo, dleg)
     torch.cuda.synchronize()
     assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
+
+
+def test_leg_mix_lane_and_team_kernels_agree():
+    """K = 16 with 16-byte aligned rows takes the lane-per-unit kernel; the
+    same rows one element off alignment take the 16-lane team kernel: both
+    give the same bits (and the oracle's)."""
+    rng = np.random.default_rng(21)
+    B, n, hkv, K = 2, 300, 4, 16
+    idx, w = cases.edges(rng, B, n, hkv, K, pad_frac=0.1, dead_frac=0.05, ties=True)
+    alpha = rng.choice(cases.TIE_WEIGHTS, size=(hkv, K)).astype(np.float32)
+    for s in (4, 2):
+        io, wo = gm.leg_mix(dev(idx), dev(w), dev(alpha), s)
+        # misaligned copies: rows start 4 bytes past a 16-byte boundary
+        ib = torch.zeros(idx.size + 1, dtype=torch.int32, device="cuda")
+        wb = torch.zeros(w.size + 1, dtype=torch.float32, device="cuda")
+        im = ib[1:].view(idx.shape)
+        wm = wb[1:].view(w.shape)
+        im.copy_(dev(idx)); wm.copy_(dev(w))
+        assert im.data_ptr() % 16 == 4
+        io2, wo2 = gm.leg_mix(im, wm, dev(alpha), s)
+        torch.cuda.synchronize()
+        assert torch.equal(io, io2) and torch.equal(wo, wo2)
+        rio, rwo = oracle.get().leg_mix_forward(idx, w, alpha, s)
+        np.testing.assert_array_equal(host(io), rio)
+        np.testing.assert_array_equal(host(wo), rwo)
