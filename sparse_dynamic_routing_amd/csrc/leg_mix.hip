@@ -206,14 +206,26 @@ __global__ __launch_bounds__(kBlock) void leg_mix_bwd_kernel(LegArgs a) {
 }
 
 // dalpha[h][k]: one wavefront per element; lane l adds chunks l, l + 64, ...
-// in order, then a fixed butterfly over the lanes; rounded once
+// into four running sums in a fixed pattern, then a fixed butterfly over the
+// lanes; rounded once
 __global__ __launch_bounds__(kBlock) void leg_mix_alpha_kernel(LegArgs a) {
     const int e = (int)((blockIdx.x * kBlock + threadIdx.x) / kWave);
     const int lane = (int)(threadIdx.x & (kWave - 1));
     if (e >= a.hkv * a.K) return;          // whole wavefronts
     const int h = e / a.K, k = e - (e / a.K) * a.K;
-    double s = 0.0;
-    for (int c = lane; c < a.nchunk; c += kWave) s += a.part[((size_t)h * a.nchunk + c) * a.K + k];
+    // four independent running sums (loads in flight together), combined in
+    // a fixed order
+    const double* pr = a.part + (size_t)h * a.nchunk * a.K + k;
+    double s0 = 0.0, s1 = 0.0, s2 = 0.0, s3 = 0.0;
+    int c = lane;
+    for (; c + 3 * kWave < a.nchunk; c += 4 * kWave) {
+        s0 += pr[(size_t)c * a.K];
+        s1 += pr[(size_t)(c + kWave) * a.K];
+        s2 += pr[(size_t)(c + 2 * kWave) * a.K];
+        s3 += pr[(size_t)(c + 3 * kWave) * a.K];
+    }
+    for (; c < a.nchunk; c += kWave) s0 += pr[(size_t)c * a.K];
+    double s = (s0 + s1) + (s2 + s3);
 #pragma unroll
     for (int o = 1; o < kWave; o <<= 1) s += __shfl_xor(s, o, kWave);
     if (lane == 0) a.dalpha[e] = (float)s;
@@ -264,6 +276,84 @@ __global__ __launch_bounds__(kBlock) void leg_mix_vec_kernel(LegArgs a) {
     }
 }
 
+// Backward for the same shapes: one lane per unit (u = workgroup * 256 +
+// thread), its stored row, the head's alpha and its leg row in registers.
+// g_k = sum of dleg over the retained leg slots with index m_k (fp64, slot
+// order); dw_k = g_k * alpha_k; the unit's dalpha terms w_k * g_k go to LDS,
+// and threads (h, k) add them over the workgroup's units of head h in unit
+// order into the partial of (h, workgroup, k), written for every head (0 if
+// the workgroup has none of its units); leg_mix_alpha_kernel then adds the
+// partials in workgroup order.  Deterministic.
+template <int S>
+__global__ __launch_bounds__(kBlock) void leg_mix_bwd_vec_kernel(LegArgs a) {
+    __shared__ double red[kBlock][17];   // 16 terms per unit, padded row
+    const int u0 = (int)blockIdx.x * kBlock;
+    const int u = u0 + (int)threadIdx.x;
+    const bool in = u < a.U;
+    double c[16];
+#pragma unroll
+    for (int k = 0; k < 16; ++k) c[k] = 0.0;
+    if (in) {
+        const int h = u % a.hkv;
+        int m[16];
+        float x[16], al[16];
+        const int4* ir = reinterpret_cast<const int4*>(a.idx + (size_t)u * 16);
+        const float4* wr = reinterpret_cast<const float4*>(a.w + (size_t)u * 16);
+        const float4* ar = reinterpret_cast<const float4*>(a.alpha + (size_t)h * 16);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const int4 i4 = ir[q];
+            const float4 w4 = wr[q], a4 = ar[q];
+            m[4 * q + 0] = i4.x; m[4 * q + 1] = i4.y; m[4 * q + 2] = i4.z; m[4 * q + 3] = i4.w;
+            x[4 * q + 0] = w4.x; x[4 * q + 1] = w4.y; x[4 * q + 2] = w4.z; x[4 * q + 3] = w4.w;
+            al[4 * q + 0] = a4.x; al[4 * q + 1] = a4.y; al[4 * q + 2] = a4.z; al[4 * q + 3] = a4.w;
+        }
+        int om[4];
+        float ow[4], og[4];
+        if constexpr (S == 4) {
+            const int4 i4 = *reinterpret_cast<const int4*>(a.idx_out + (size_t)u * 4);
+            const float4 w4 = *reinterpret_cast<const float4*>(a.w_out + (size_t)u * 4);
+            const float4 g4 = *reinterpret_cast<const float4*>(a.dleg + (size_t)u * 4);
+            om[0] = i4.x; om[1] = i4.y; om[2] = i4.z; om[3] = i4.w;
+            ow[0] = w4.x; ow[1] = w4.y; ow[2] = w4.z; ow[3] = w4.w;
+            og[0] = g4.x; og[1] = g4.y; og[2] = g4.z; og[3] = g4.w;
+        } else {
+            const int2 i2 = *reinterpret_cast<const int2*>(a.idx_out + (size_t)u * 2);
+            const float2 w2 = *reinterpret_cast<const float2*>(a.w_out + (size_t)u * 2);
+            const float2 g2 = *reinterpret_cast<const float2*>(a.dleg + (size_t)u * 2);
+            om[0] = i2.x; om[1] = i2.y; om[2] = 0; om[3] = 0;
+            ow[0] = w2.x; ow[1] = w2.y; ow[2] = 0.0f; ow[3] = 0.0f;
+            og[0] = g2.x; og[1] = g2.y; og[2] = 0.0f; og[3] = 0.0f;
+        }
+        float dwv[16];
+#pragma unroll
+        for (int k = 0; k < 16; ++k) {
+            double g = 0.0;
+#pragma unroll
+            for (int t = 0; t < S; ++t) g += ow[t] > 0.0f && om[t] == m[k] ? (double)og[t] : 0.0;
+            const bool on = al[k] > 0.0f && x[k] > 0.0f;
+            dwv[k] = on ? (float)(g * (double)al[k]) : 0.0f;
+            c[k] = on ? g * (double)x[k] : 0.0;
+        }
+        float4* dr = reinterpret_cast<float4*>(a.dw + (size_t)u * 16);
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+            dr[q] = make_float4(dwv[4 * q], dwv[4 * q + 1], dwv[4 * q + 2], dwv[4 * q + 3]);
+    }
+#pragma unroll
+    for (int k = 0; k < 16; ++k) red[threadIdx.x][k] = c[k];
+    __syncthreads();
+    // partial of (h, k): units u0 + l with (u0 + l) % hkv == h, in order
+    for (int e = (int)threadIdx.x; e < a.hkv * 16; e += kBlock) {
+        const int h = e / 16, k = e - (e / 16) * 16;
+        int l = h - u0 % a.hkv;
+        if (l < 0) l += a.hkv;
+        double sum = 0.0;
+        for (; l < kBlock; l += a.hkv) sum += red[l][k];
+        a.part[((size_t)h * a.nchunk + blockIdx.x) * 16 + k] = sum;
+    }
+}
+
 template <int L>
 void launch_fwd(const LegArgs& a, hipStream_t st) {
     const long long threads = (long long)a.U * L;
@@ -280,11 +370,34 @@ void launch_bwd(const LegArgs& a, hipStream_t st) {
                        dim3(kBlock), 0, st, a);
 }
 
+// K = 16, s = 4 or 2, every row 16-byte aligned: the lane-per-unit kernels
+bool lane_rows(const LegArgs& a, bool fwd) {
+    // stored rows, alpha and dw: 16-byte loads / stores; leg rows: s * 4 bytes
+    uintptr_t rows = (uintptr_t)a.idx | (uintptr_t)a.w | (uintptr_t)a.alpha;
+    uintptr_t legs = (uintptr_t)a.idx_out | (uintptr_t)a.w_out;
+    if (!fwd) {
+        rows |= (uintptr_t)a.dw;
+        legs |= (uintptr_t)a.dleg;
+    }
+    return a.K == 16 && (a.s == 4 || a.s == 2) && rows % 16 == 0 &&
+           legs % (uintptr_t)(a.s * 4) == 0;
+}
+
 template <bool FWD>
 hipError_t dispatch(const LegArgs& a, hipStream_t st) {
-    const bool rows16 = ((uintptr_t)a.idx | (uintptr_t)a.w | (uintptr_t)a.alpha |
-                         (uintptr_t)a.idx_out | (uintptr_t)a.w_out) % 16 == 0;
-    if (FWD && a.K == 16 && (a.s == 4 || a.s == 2) && rows16) {   // lane per unit
+    const bool rows16 = lane_rows(a, FWD);
+    if (!FWD && rows16) {
+        const dim3 grid((unsigned)((a.U + kBlock - 1) / kBlock));
+        if (a.s == 4)
+            hipLaunchKernelGGL(leg_mix_bwd_vec_kernel<4>, grid, dim3(kBlock), 0, st, a);
+        else
+            hipLaunchKernelGGL(leg_mix_bwd_vec_kernel<2>, grid, dim3(kBlock), 0, st, a);
+        const long long lanes = (long long)a.hkv * a.K * kWave;
+        hipLaunchKernelGGL(leg_mix_alpha_kernel, dim3((unsigned)((lanes + kBlock - 1) / kBlock)),
+                           dim3(kBlock), 0, st, a);
+        return hipGetLastError();
+    }
+    if (FWD && rows16) {   // lane per unit
         if (a.s == 4)
             hipLaunchKernelGGL(leg_mix_vec_kernel<4>, dim3(xcd_unit_grid(a.U)), dim3(kBlock), 0,
                                st, a);
@@ -312,8 +425,15 @@ hipError_t dispatch(const LegArgs& a, hipStream_t st) {
 
 }  // namespace
 
+// fp64 partials of dalpha: [hkv][chunks][K], chunks of 64 tokens of one head
+// (team kernels) or, for K = 16, of 256 units (lane-per-unit kernel),
+// whichever is more
 size_t leg_mix_backward_workspace_bytes(int B, int n, int hkv, int K) {
-    const long long chunks = ((long long)B * n + kLegTokens - 1) / kLegTokens;
+    long long chunks = ((long long)B * n + kLegTokens - 1) / kLegTokens;
+    if (K == 16) {
+        const long long wgs = ((long long)B * n * hkv + kBlock - 1) / kBlock;
+        if (wgs > chunks) chunks = wgs;
+    }
     return (size_t)hkv * (size_t)chunks * (size_t)K * sizeof(double);
 }
 
@@ -335,7 +455,8 @@ hipError_t launch_leg_mix_backward(int B, int n, int hkv, const int32_t* idx, co
     a.w_out = const_cast<float*>(w_out); a.dleg = dleg; a.dw = dw; a.dalpha = dalpha;
     a.part = part;
     a.n = n; a.hkv = hkv; a.K = K; a.s = s; a.U = B * n * hkv; a.BN = B * n;
-    a.nchunk = (a.BN + kLegTokens - 1) / kLegTokens;
+    a.nchunk = lane_rows(a, false) ? (a.U + kBlock - 1) / kBlock
+                                   : (a.BN + kLegTokens - 1) / kLegTokens;
     return dispatch<false>(a, st);
 }
 

@@ -162,7 +162,8 @@ def test_leg_mix_argument_checks(lib):
     assert f(8, 4096, 8, i, w, 16, al, 4, i, wo, None) == ALIAS      # idx_out on idx
     assert f(0, 4096, 8, None, None, 16, None, 4, None, None, None) == OK
     need = lib.gm_leg_mix_backward_workspace_bytes(8, 4096, 8, 16)
-    assert need == 8 * 512 * 16 * 8                                   # fp64 partial per 64 tokens
+    assert need == 8 * 1024 * 16 * 8           # fp64 partial per (head, 256 units) at K = 16
+    assert lib.gm_leg_mix_backward_workspace_bytes(8, 4096, 8, 24) == 8 * 512 * 24 * 8   # per 64 tokens
     dl, dw, da, ws = fake(0x600000), fake(0x10000000), fake(0x700000), fake(0x20000000)
     args = [8, 4096, 8, i, w, 16, al, io, wo, 4, dl, dw, da, ws, need, None]
     bad = list(args); bad[14] = need - 1

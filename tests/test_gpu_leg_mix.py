@@ -86,3 +86,13 @@ def test_leg_mix_lane_and_team_kernels_agree():
         rio, rwo = oracle.get().leg_mix_forward(idx, w, alpha, s)
         np.testing.assert_array_equal(host(io), rio)
         np.testing.assert_array_equal(host(wo), rwo)
+        # backward: lane kernel (aligned) and team kernel (misaligned rows)
+        dleg = rng.standard_normal(io.shape).astype(np.float32)
+        dw, da = gm.leg_mix_backward(dev(idx), dev(w), dev(alpha), io, wo, dev(dleg))
+        dw2, da2 = gm.leg_mix_backward(im, wm, dev(alpha), io, wo, dev(dleg))
+        torch.cuda.synchronize()
+        rdw, rda = oracle.get().leg_mix_backward(idx, w, alpha, rio, rwo, dleg)
+        for name, got in (("dw lane", dw), ("dw team", dw2)):
+            assert_close(name, host(got), rdw, 1e-5)
+        for name, got in (("dalpha lane", da), ("dalpha team", da2)):
+            assert_close(name, host(got), rda, 1e-5)
