@@ -1,4 +1,6 @@
-"""The four calls captured in a HIP graph (torch.cuda.CUDAGraph) and replayed.
+"""The library's calls captured in a HIP graph (torch.cuda.CUDAGraph) and
+replayed: the four calls of a layer pass, then leg construction, the decode
+step and the refresh edges.
 
 Every call only launches kernels on the caller's stream (zero-fills are
 kernels, not memsets; workspaces come from the caller), so a whole layer pass
@@ -104,3 +106,80 @@ def test_layer_pass_graph_replays_match_eager(B, n):
                     f"replay {rep}: {name} max |diff| {err.max().item():.3e}")
             else:
                 assert torch.equal(t, ref[name]), f"replay {rep}: {name} differs from eager"
+
+
+def _capture(fn):
+    """Warm up on a side stream, then capture fn() into a graph."""
+    g = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        fn()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g):
+        fn()
+    torch.cuda.synchronize()
+    return g
+
+
+def test_other_calls_graph_replays_match_eager():
+    """Leg construction (forward and backward), the decode step and the
+    refresh edges captured together and replayed three times against the
+    eager results (all bitwise: their sums run in a fixed order)."""
+    say("case graph replay: leg construction, decode step, refresh edges")
+    B, n, hkv, hq, d, K, s = 2, 1024, 4, 8, 128, 16, 4
+    seed = synth.BASE_SEED + 42
+    cu = lambda x: torch.from_numpy(x).cuda()  # noqa: E731
+    sidx, sw = synth.edges(seed, B, n, hkv, K, mode="mixed")
+    sidx, sw = cu(sidx), cu(sw)
+    alpha = torch.rand((hkv, K), generator=torch.Generator().manual_seed(5)).add_(0.05).cuda()
+    eidx, ew = synth.edges(seed + 1, B, n, hkv, s, mode="mixed")
+    eidx, ew = cu(eidx), cu(ew)
+    q = synth.normal(seed, "q", (B, n, hq, d), torch.bfloat16, device="cuda")
+    k = synth.normal(seed, "k", (B, n, hkv, d), torch.bfloat16, device="cuda")
+    v = synth.normal(seed, "v", (B, n, hkv, d), torch.bfloat16, device="cuda")
+    f32 = dict(dtype=torch.float32, device="cuda")
+    out = {
+        "li": torch.empty((B, n, hkv, s), dtype=torch.int32, device="cuda"),
+        "lw": torch.empty((B, n, hkv, s), **f32),
+        "dw": torch.empty((B, n, hkv, K), **f32),
+        "da": torch.empty((hkv, K), **f32),
+        "di": torch.empty((B, hkv, s), dtype=torch.int32, device="cuda"),
+        "dwt": torch.empty((B, hkv, s), **f32),
+        "do": torch.empty((B, hq, d), dtype=torch.bfloat16, device="cuda"),
+        "ri": torch.empty((B, n, hkv, s), dtype=torch.int32, device="cuda"),
+        "rw": torch.empty((B, n, hkv, s), **f32),
+        "lse": torch.empty((B, n, hq), **f32),
+    }
+    dleg = synth.normal(seed + 7, "dout", (B, n, hkv, s), torch.float32, device="cuda")
+    ws = torch.empty(max(gm.gm_leg_mix_backward_workspace_bytes(B, n, hkv, K), 8) // 8,
+                     dtype=torch.float64, device="cuda")
+    q1 = q[:, -1].contiguous()
+    i1, w1 = eidx[:, -1].contiguous(), ew[:, -1].contiguous()
+
+    def run():
+        gm.gm_leg_mix_forward(sidx, sw, alpha, out["li"], out["lw"])
+        gm.gm_leg_mix_backward(sidx, sw, alpha, out["li"], out["lw"], dleg, out["dw"],
+                               out["da"], ws)
+        gm.gm_decode_step(i1, w1, eidx, ew, q1, k, v, out["di"], out["dwt"], out["do"])
+        gm.gm_dense_refresh(q, k, out["lse"], out["ri"], out["rw"])
+
+    run()
+    torch.cuda.synchronize()
+    ref = {name: t.clone() for name, t in out.items()}
+    g = _capture(run)
+    other = LayerPass(1, 512, seed=synth.BASE_SEED + 41)
+    for rep in range(3):
+        for t in out.values():
+            if t.dtype == torch.int32:
+                t.fill_(-7)
+            else:
+                t.fill_(float("nan"))
+        other.run()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        say(f"  replay {rep}")
+        for name, t in out.items():
+            assert torch.equal(t, ref[name]), f"replay {rep}: {name} differs from eager"
