@@ -47,37 +47,4 @@ __device__ __forceinline__ void merge_top4(uint64_t* a, const uint64_t* b) {
     cx(a[0], a[1]); cx(a[2], a[3]);
 }
 
-// The 16 candidates (target m[k], fp64 weight cw[k], k in order) of one
-// unit: targets are merged by summing, in candidate order, into their first
-// candidate (later ones drop out), the sums rounded to fp32 and the 4
-// largest positive ones returned as keys, descending (0 for none).  Each
-// candidate's sum is finished before the next one starts, and each group of
-// four keys is sorted as soon as it exists, so little state is live at once
-// (one fp64 sum, a flag per candidate) and the kernel keeps
-// several wavefronts per SIMD.
-__device__ __forceinline__ void top4_of_16(const int (&m)[16], const double (&cw)[16],
-                                           uint64_t (&key)[16]) {
-    bool rep[16];   // candidate k repeats an earlier target
-#pragma unroll
-    for (int k = 0; k < 16; ++k) rep[k] = false;
-#pragma unroll
-    for (int k2 = 0; k2 < 16; ++k2) {
-        double acc = cw[k2];
-#pragma unroll
-        for (int k = k2 + 1; k < 16; ++k) {
-            const bool same = m[k] == m[k2];
-            acc += same ? cw[k] : 0.0;
-            rep[k] = rep[k] || same;
-        }
-        const float wk = (float)acc;
-        key[k2] = !rep[k2] && m[k2] >= 0 && wk > 0.0f
-                      ? ((uint64_t)__float_as_uint(wk) << 32) | (uint32_t)~(uint32_t)m[k2]
-                      : 0ull;
-        if ((k2 & 3) == 3) sort4_desc(key + (k2 - 3));
-    }
-    merge_top4(key + 0, key + 4);
-    merge_top4(key + 8, key + 12);
-    merge_top4(key + 0, key + 8);
-}
-
 }  // namespace gm

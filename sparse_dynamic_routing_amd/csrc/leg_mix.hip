@@ -233,9 +233,9 @@ __global__ __launch_bounds__(kBlock) void leg_mix_alpha_kernel(LegArgs a) {
 
 // K = 16 stored slots with 16-byte aligned rows: one lane per unit, the
 // whole row in registers (four 16-byte loads each of idx, w and the head's
-// alpha), merged and ranked by SER's register network; units chunked per XCD
-// as SER's are.  Same arithmetic and order as the team kernel, so the same
-// bits.
+// alpha), merged and ranked as in SER's forward (sorting network of
+// gm_select.h); units chunked per XCD as SER's are.  Same arithmetic and
+// order as the team kernel, so the same bits.
 template <int S>
 __global__ __launch_bounds__(kBlock) void leg_mix_vec_kernel(LegArgs a) {
     static_assert(S == 2 || S == 4, "vector stores of 2 or 4 slots");
@@ -257,8 +257,37 @@ __global__ __launch_bounds__(kBlock) void leg_mix_vec_kernel(LegArgs a) {
         cw[4 * q + 2] = (double)a4.z * (double)w4.z;
         cw[4 * q + 3] = (double)a4.w * (double)w4.w;
     }
+    // the merge and selection of SER's forward, written out here as there
+    // (98 registers; the same code as a shared inline function compiled to
+    // 256 registers and one wavefront per SIMD): a candidate that repeats an
+    // earlier target gets bit 31 of its target set and drops out, its weight
+    // added to the target's first candidate in slot order
+    double acc[16];
+#pragma unroll
+    for (int k = 0; k < 16; ++k) acc[k] = cw[k];
+#pragma unroll
+    for (int k = 1; k < 16; ++k) {
+        uint32_t dup = 0;
+#pragma unroll
+        for (int k2 = 0; k2 < k; ++k2) {
+            const bool same = m[k2] == m[k];
+            acc[k2] += same ? cw[k] : 0.0;
+            dup |= same ? 0x80000000u : 0u;
+        }
+        m[k] = (int)((uint32_t)m[k] | dup);
+    }
     uint64_t key[16];
-    top4_of_16(m, cw, key);
+#pragma unroll
+    for (int k = 0; k < 16; ++k) {
+        const float wk = (float)acc[k];
+        key[k] = m[k] >= 0 && wk > 0.0f
+                     ? ((uint64_t)__float_as_uint(wk) << 32) | (uint32_t)~(uint32_t)m[k]
+                     : 0ull;
+    }
+    sort4_desc(key + 0); sort4_desc(key + 4); sort4_desc(key + 8); sort4_desc(key + 12);
+    merge_top4(key + 0, key + 4);
+    merge_top4(key + 8, key + 12);
+    merge_top4(key + 0, key + 8);
     int om[4];
     float ow[4];
 #pragma unroll

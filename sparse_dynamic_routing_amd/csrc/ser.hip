@@ -349,11 +349,38 @@ __global__ __launch_bounds__(kBlock) void ser_fwd_vec_kernel(SerUnitArgs a) {
     int m[kCand];
     float x[kSmax], y[kCand];
     load_paths_vec(a, u, m, x, y);
-    double cw[kCand];
+    // a candidate that repeats an earlier target gets bit 31 of its target
+    // set (targets are >= 0): it then matches no later candidate, whose
+    // weight goes to the earlier, first candidate of the target instead
+    double cw[kCand], acc[kCand];
 #pragma unroll
-    for (int k = 0; k < kCand; ++k) cw[k] = (double)x[k / kSmax] * (double)y[k];
+    for (int k = 0; k < kCand; ++k) {
+        cw[k] = (double)x[k / kSmax] * (double)y[k];
+        acc[k] = cw[k];
+    }
+#pragma unroll
+    for (int k = 1; k < kCand; ++k) {
+        uint32_t dup = 0;
+#pragma unroll
+        for (int k2 = 0; k2 < k; ++k2) {
+            const bool same = m[k2] == m[k];
+            acc[k2] += same ? cw[k] : 0.0;
+            dup |= same ? 0x80000000u : 0u;
+        }
+        m[k] = (int)((uint32_t)m[k] | dup);
+    }
     uint64_t key[kCand];
-    top4_of_16(m, cw, key);
+#pragma unroll
+    for (int k = 0; k < kCand; ++k) {
+        const float wk = (float)acc[k];
+        key[k] = m[k] >= 0 && wk > 0.0f
+                     ? ((uint64_t)__float_as_uint(wk) << 32) | (uint32_t)~(uint32_t)m[k]
+                     : 0ull;
+    }
+    sort4_desc(key + 0); sort4_desc(key + 4); sort4_desc(key + 8); sort4_desc(key + 12);
+    merge_top4(key + 0, key + 4);
+    merge_top4(key + 8, key + 12);
+    merge_top4(key + 0, key + 8);
     int om[4];
     float ow[4];
 #pragma unroll
