@@ -414,13 +414,41 @@ def run_legmix(a):
         e[0].record(); fwd(); e[1].record(); bwd(); e[2].record()
         torch.cuda.synchronize()
         tf += e[0].elapsed_time(e[1]); tb += e[1].elapsed_time(e[2])
+    # the same calls replayed from HIP graphs: kernel time without the
+    # Python launch gaps of the eager loop above
+    def graph_us(fn, reps=20):
+        g = torch.cuda.CUDAGraph()
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            fn()
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        with torch.cuda.graph(g):
+            fn()
+        g.replay()
+        torch.cuda.synchronize()
+        t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        t0.record()
+        for _ in range(reps):
+            g.replay()
+        t1.record()
+        torch.cuda.synchronize()
+        return t0.elapsed_time(t1) / reps * 1e3
+    gf, gb = graph_us(fwd), graph_us(bwd)
     U = p.B * p.n * p.hkv
+    fwd_bytes = 2 * (8 * K + 8 * s)                 # both legs: stored row in, leg out
+    bwd_bytes = 2 * (8 * K + 12 * s + 4 * K)        # + leg row and dleg in, dw out
     print(json.dumps({
         "config": "legmix", "units_per_step": U, "K": K, "s": s, "legs": 2,
         "forward_us": tf / a.steps * 1e3, "backward_us": tb / a.steps * 1e3,
-        "units_per_s": U / ((tf + tb) / a.steps * 1e-3),
-        "compulsory_bytes_per_unit": {"forward": 2 * (8 * K + 8 * s),
-                                      "backward": 2 * (8 * K + 12 * s + 4 * K)},
+        "graph_forward_us": gf, "graph_backward_us": gb,
+        "units_per_s": U / ((gf + gb) * 1e-6),
+        "compulsory_bytes_per_unit": {"forward": fwd_bytes, "backward": bwd_bytes},
+        "roofline": {"kernel": "leg_mix_vec_kernel (both legs, graph replay)", "bound": "hbm",
+                     "achieved": fwd_bytes * U / (gf * 1e-6) / 1e9, "peak": PEAK_HBM_GBS,
+                     "unit": "GB/s",
+                     "frac": fwd_bytes * U / (gf * 1e-6) / 1e9 / PEAK_HBM_GBS},
         "steps": a.steps, "warmup": a.warmup, "data": "synthetic"}), flush=True)
 
 
@@ -460,6 +488,9 @@ def run_refresh(a):
         "score_flops_per_pass": flops,
         "select_tflops": flops / (ts * 1e-3) / 1e12, "mfma_peak_tflops": PEAK_BF16_TFLOPS,
         "scores_per_s": pairs / (ts * 1e-3),
+        "roofline": {"kernel": "refresh_kernel (selection pass)", "bound": "mfma",
+                     "achieved": flops / (ts * 1e-3) / 1e12, "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": flops / (ts * 1e-3) / 1e12 / PEAK_BF16_TFLOPS},
         "steps": a.steps, "warmup": a.warmup, "data": "synthetic"}), flush=True)
 
 
