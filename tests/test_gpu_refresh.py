@@ -79,6 +79,8 @@ REFRESH_CASES = [
     (3, 97, 3, 1, 128, 2, 1.0, 5),       # one head per group, less than one tile
     (1, 517, 1, 4, 64, 4, 3.0, 6),       # several key tiles, G = 4
     (2, 130, 2, 4, 128, 3, 1.0, 7),      # s not a power of two
+    (1, 300, 1, 2, 256, 8, 2.0, 13),     # d = 256 with the longest list (registers spill)
+    (2, 1000, 3, 1, 64, 5, 3.0, 14),     # three KV heads (pairs not a power of two), 4 tiles
 ]
 
 
