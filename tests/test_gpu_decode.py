@@ -26,6 +26,11 @@ DECODE_CASES = [
     (torch.bfloat16, 256, 1, 8, 8, 8, 2, 150),    # a full wave of candidates
     (torch.float32, 16, 16, 64, 8, 8, 2, 40),     # the widest output: padding
     (torch.bfloat16, 32, 8, 1, 2, 2, 5, 1),       # a one-token cache
+    # bf16, d = 128, <= 16 candidates: the kernel that loads every
+    # candidate's K/V rows while SER ranks them
+    (torch.bfloat16, 128, 1, 3, 3, 5, 2, 90),     # 15 candidates, one query head
+    (torch.bfloat16, 128, 4, 8, 2, 8, 3, 120),    # 16 candidates, more slots than kept ones
+    (torch.bfloat16, 128, 2, 1, 1, 1, 2, 10),     # a single candidate
 ]
 
 
