@@ -19,8 +19,9 @@
 // Everything is latency: a step reads ~s2*s3 edge entries and 2*s1 K/V rows
 // per unit.  For bf16, d = 128 and at most 16 candidates a second kernel
 // (decode16_kernel, below) loads every candidate's K/V rows while SER ranks
-// them: two dependent memory round trips instead of three (8.4 -> 6.5 us per
-// step of 8 sequences x 8 KV heads at a 4,096-token cache).
+// them, so the third memory round trip no longer waits for the merge and
+// ranking (8.4 -> 6.5 us per step of 8 sequences x 8 KV heads at a
+// 4,096-token cache).
 #include "gm_common.h"
 #include "gm_internal.h"
 #include "gm_wave.h"
@@ -201,8 +202,8 @@ __global__ __launch_bounds__(kWave) void decode_kernel(DecodeArgs a) {
 
 // bf16, d = 128, at most 16 candidate paths: the K/V rows of every
 // candidate are loaded while SER merges and ranks them, so the kept slots'
-// rows are already in registers when the ranking ends (two dependent memory
-// round trips instead of three).  Lanes form four 16-lane rows; row g holds
+// rows are already in registers when the ranking ends (the K/V round trip
+// overlaps the ranking instead of following it).  Lanes form four 16-lane rows; row g holds
 // piece r = lane % 16 (16 bytes) of candidates g, g + 4, g + 8, g + 12.
 // Scores of all candidates are 16-lane sums; the softmax runs over the kept
 // ones (the others get probability 0) and the rows' partial outputs are
