@@ -10,8 +10,9 @@
 //   adds the later lanes of the same target in path order (the definition's
 //   order and precision, so the weights are bit-identical to the training
 //   pass), later ones drop out; each lane's rank among positive keys
-//   (weight desc, target asc) comes from one sweep over the lanes, and rank
-//   r < s1 writes output slot r (padding (0, 0) after the last candidate).
+//   (weight desc, target asc) comes from one sweep over the lanes (DPP row
+//   rotations for up to 16 candidates, v_readlane beyond), and rank r < s1
+//   writes output slot r (padding (0, 0) after the last candidate).
 //   SEA then reads the kept slots' K/V cache rows in 16-byte pieces (lane l
 //   holds piece l of each d-row; the query rows are loaded while SER runs),
 //   four slots per step, each score a wavefront sum, with an online softmax
@@ -20,10 +21,11 @@
 // per unit.  For bf16, d = 128 and at most 16 candidates a second kernel
 // (decode16_kernel, below) loads every candidate's K/V rows while SER ranks
 // them, so the third memory round trip no longer waits for the merge and
-// ranking (8.4 -> 6.5 us per step of 8 sequences x 8 KV heads at a
-// 4,096-token cache).
+// ranking (8.4 -> 6.6 us per step of 8 sequences x 8 KV heads at a
+// 4,096-token cache; 5.9 us with the ranking by DPP rotations).
 #include "gm_common.h"
 #include "gm_internal.h"
+#include "gm_select.h"
 #include "gm_wave.h"
 
 namespace gm {
@@ -102,28 +104,36 @@ __global__ __launch_bounds__(kWave) void decode_kernel(DecodeArgs a) {
         m = a.idx2[r2 * a.s3 + c];
         cw = (double)x * (double)a.w2[r2 * a.s3 + c];
     }
-    // merge: the first lane of a target sums its later lanes in path order
-    double acc = cw;
-    bool dup = false;
-    for (int k2 = 0; k2 < nc; ++k2) {
-        const int mk = lane_i(m, k2);
-        const double ck = lane_d(cw, k2);
-        if (mk == m) {
-            if (k2 < lane) dup = true;
-            if (k2 > lane) acc += ck;
+    float key;
+    bool cand;
+    int rank = 0;
+    if (nc <= 16) {
+        // up to 16 candidates: DPP rotations inside the first 16-lane row
+        team16_merge_rank(lane & 15, m, cw, lane < nc, key, cand, rank);
+    } else {
+        // merge: the first lane of a target sums its later lanes in path order
+        double acc = cw;
+        bool dup = false;
+        for (int k2 = 0; k2 < nc; ++k2) {
+            const int mk = lane_i(m, k2);
+            const double ck = lane_d(cw, k2);
+            if (mk == m) {
+                if (k2 < lane) dup = true;
+                if (k2 > lane) acc += ck;
+            }
+        }
+        key = (float)acc;
+        cand = lane < nc && !dup && key > 0.0f;
+        // rank among the candidates: larger weight first, then the lower target
+        const uint64_t cm = __ballot(cand);
+        for (int k2 = 0; k2 < nc; ++k2) {
+            if (!((cm >> k2) & 1)) continue;
+            const float kk = lane_f(key, k2);
+            const int mk = lane_i(m, k2);
+            if (kk > key || (kk == key && mk < m)) ++rank;
         }
     }
-    const float key = (float)acc;
-    const bool cand = lane < nc && !dup && key > 0.0f;
-    // rank among the candidates: larger weight first, then the lower target
     const uint64_t cmask = __ballot(cand);
-    int rank = 0;
-    for (int k2 = 0; k2 < nc; ++k2) {
-        if (!((cmask >> k2) & 1)) continue;
-        const float kk = lane_f(key, k2);
-        const int mk = lane_i(m, k2);
-        if (kk > key || (kk == key && mk < m)) ++rank;
-    }
     const size_t ob = (size_t)unit * a.s1;
     if (cand && rank < a.s1) {
         a.idx_out[ob + rank] = m;
@@ -247,27 +257,14 @@ __global__ __launch_bounds__(kWave) void decode16_kernel(DecodeArgs a) {
         kr[i] = *reinterpret_cast<const uint4*>(kb + row);
         vr[i] = *reinterpret_cast<const uint4*>(vb + row);
     }
-    // merge and rank exactly as decode_kernel
-    double acc = cw;
-    bool dup = false;
-    for (int k2 = 0; k2 < nc; ++k2) {
-        const int mk = lane_i(m, k2);
-        const double ck = lane_d(cw, k2);
-        if (mk == m) {
-            if (k2 < lane) dup = true;
-            if (k2 > lane) acc += ck;
-        }
-    }
-    const float key = (float)acc;
-    const bool cand = lane < nc && !dup && key > 0.0f;
+    // merge and rank by DPP rotations inside the first 16-lane row (the
+    // candidates' lanes; the other rows sweep their own, unused, lanes):
+    // the same sums in the same order as decode_kernel's lane sweeps
+    float key;
+    bool cand;
+    int rank;
+    team16_merge_rank(lane & 15, m, cw, lane < nc, key, cand, rank);
     const uint64_t cmask = __ballot(cand);
-    int rank = 0;
-    for (int k2 = 0; k2 < nc; ++k2) {
-        if (!((cmask >> k2) & 1)) continue;
-        const float kk = lane_f(key, k2);
-        const int mk = lane_i(m, k2);
-        if (kk > key || (kk == key && mk < m)) ++rank;
-    }
     const size_t ob = (size_t)unit * a.s1;
     if (cand && rank < a.s1) {
         a.idx_out[ob + rank] = m;

@@ -31,65 +31,6 @@ namespace {
 
 constexpr int kLegTokens = 64;   // tokens of one KV head per backward workgroup
 
-// Rotation inside a 16-lane row (DPP row_ror:D): every lane reads one lane
-// of its own row, so a team of 16 sweeps its partners without LDS.
-template <int D>
-__device__ __forceinline__ int ror_i(int x) {
-    return __builtin_amdgcn_update_dpp(0, x, 0x120 + D, 0xF, 0xF, false);
-}
-template <int D>
-__device__ __forceinline__ float ror_f(float x) {
-    return __int_as_float(ror_i<D>(__float_as_int(x)));
-}
-template <int D>
-__device__ __forceinline__ double ror_d(double x) {
-    const uint64_t u = __builtin_bit_cast(uint64_t, x);
-    const uint32_t lo = (uint32_t)ror_i<D>((int)(uint32_t)u);
-    const uint32_t hi = (uint32_t)ror_i<D>((int)(uint32_t)(u >> 32));
-    return __builtin_bit_cast(double, ((uint64_t)hi << 32) | lo);
-}
-
-struct Cand {
-    int k, m;
-    double cw, acc;
-    bool dup;
-    float key;
-    bool cand;
-    int rank;
-};
-// merge step against the partner D lanes away (its slot index read along)
-template <int D>
-__device__ __forceinline__ void merge_step(Cand& c) {
-    const int k2 = ror_i<D>(c.k);
-    const int mk = ror_i<D>(c.m);
-    const double ck = ror_d<D>(c.cw);
-    if (mk == c.m) {
-        if (k2 < c.k) c.dup = true;
-        else c.acc += ck;
-    }
-}
-template <int D>
-__device__ __forceinline__ void rank_step(Cand& c) {
-    const float kk = ror_f<D>(c.key);
-    const int mk = ror_i<D>(c.m);
-    const bool ck = ror_i<D>((int)c.cand) != 0;
-    if (ck && (kk > c.key || (kk == c.key && mk < c.m))) ++c.rank;
-}
-// later slots must be added in increasing slot order: the sweep runs in
-// whichever rotation direction visits them that way
-template <int... D>
-__device__ __forceinline__ void merge_up(Cand& c, std::integer_sequence<int, D...>) {
-    (merge_step<D + 1>(c), ...);
-}
-template <int... D>
-__device__ __forceinline__ void merge_down(Cand& c, std::integer_sequence<int, D...>) {
-    (merge_step<15 - D>(c), ...);
-}
-template <int... D>
-__device__ __forceinline__ void rank_all(Cand& c, std::integer_sequence<int, D...>) {
-    (rank_step<D + 1>(c), ...);
-}
-
 struct LegArgs {
     const int32_t* idx;     // [B][n][hkv][K] stored edges
     const float* w;
@@ -126,17 +67,7 @@ __global__ __launch_bounds__(kBlock) void leg_mix_fwd_kernel(LegArgs a) {
     if constexpr (L == 16) {
         // 16-lane rows: DPP rotations (every lane of the wave takes part,
         // so no lane leaves before the sweeps)
-        Cand c{k, m, cw, cw, false, 0.0f, false, 0};
-        if (ror_i<1>(k) == ((k + 1) & 15))
-            merge_up(c, std::make_integer_sequence<int, 15>{});
-        else
-            merge_down(c, std::make_integer_sequence<int, 15>{});
-        c.key = (float)c.acc;
-        c.cand = in && k < a.K && !c.dup && c.key > 0.0f;
-        rank_all(c, std::make_integer_sequence<int, 15>{});
-        key = c.key;
-        cand = c.cand;
-        rank = c.rank;
+        team16_merge_rank(k, m, cw, in && k < a.K, key, cand, rank);
     } else {
         for (int k2 = 0; k2 < a.K; ++k2) {
             const int mk = __shfl(m, k2, L);
