@@ -414,9 +414,9 @@ def run_legmix(a):
         e[0].record(); fwd(); e[1].record(); bwd(); e[2].record()
         torch.cuda.synchronize()
         tf += e[0].elapsed_time(e[1]); tb += e[1].elapsed_time(e[2])
-    # the same calls replayed from HIP graphs: kernel time without the
-    # Python launch gaps of the eager loop above
-    def graph_us(fn, reps=20):
+    # the same calls replayed from HIP graphs (8 steps per graph): kernel
+    # time without the Python launch gaps of the eager loop above
+    def graph_us(fn, reps=10, per_graph=8):
         g = torch.cuda.CUDAGraph()
         side = torch.cuda.Stream()
         side.wait_stream(torch.cuda.current_stream())
@@ -425,7 +425,8 @@ def run_legmix(a):
         torch.cuda.current_stream().wait_stream(side)
         torch.cuda.synchronize()
         with torch.cuda.graph(g):
-            fn()
+            for _ in range(per_graph):
+                fn()
         g.replay()
         torch.cuda.synchronize()
         t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -434,7 +435,7 @@ def run_legmix(a):
             g.replay()
         t1.record()
         torch.cuda.synchronize()
-        return t0.elapsed_time(t1) / reps * 1e3
+        return t0.elapsed_time(t1) / (reps * per_graph) * 1e3
     gf, gb = graph_us(fwd), graph_us(bwd)
     U = p.B * p.n * p.hkv
     fwd_bytes = 2 * (8 * K + 8 * s)                 # both legs: stored row in, leg out
