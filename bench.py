@@ -80,6 +80,9 @@ CONFIG_STAGES = {
     "stack21": ["ser_fwd", "ser_fwd", "sea_fwd"],   # one of the 21 layers
     "long64k": ["ser_fwd", "sea_fwd", "sea_bwd", "ser_bwd"],
     "theia": ["ser_fwd", "sea_fwd", "sea_bwd", "ser_bwd"],   # (s1, s2, s3) = (2, 4, 4)
+    "d64": ["ser_fwd", "sea_fwd", "sea_bwd", "ser_bwd"],     # head dim 64
+    "d256": ["ser_fwd", "sea_fwd", "sea_bwd", "ser_bwd"],    # head dim 256
+    "fp32": ["ser_fwd", "sea_fwd", "sea_bwd", "ser_bwd"],    # fp32 activations
 }
 
 
@@ -88,10 +91,13 @@ def stage_bytes(stage: str, p: synth.Preset) -> int:
     forward saves p / w, 4 bytes per query head and slot, only when a
     backward follows)."""
     s1 = p.s1
-    st = 4 * (p.hq // p.hkv) * s1 if p.backward else 0
+    G = p.hq // p.hkv
+    es = 2 if p.dtype == torch.bfloat16 else 4
+    qrow, kv = G * p.d * es, 2 * p.d * es          # a unit's q (or o, dout); its K and V rows
+    st = 4 * G * s1 if p.backward else 0
     return {"ser_fwd": 8 * p.s2 + 8 * s1,
-            "sea_fwd": 512 + 8 * s1 + 512 + 512 + st,
-            "sea_bwd": 512 + 512 + 8 * s1 + 512 + st + 1024 + 4 * s1 + 1024,
+            "sea_fwd": qrow + 8 * s1 + kv + qrow + st,
+            "sea_bwd": 2 * qrow + 8 * s1 + kv + st + 4 * G * p.d + 4 * s1 + 8 * p.d,
             "ser_bwd": 8 * p.s2 + 8 * s1 + 4 * s1 + 4 * p.s2}[stage]
 
 

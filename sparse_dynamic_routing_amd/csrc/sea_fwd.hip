@@ -200,8 +200,8 @@ __global__ __launch_bounds__(kBlock) void sea_fwd_kernel(SeaFwdArgs a) {
 
 
 // ----------------------------------------------------------------- fast path
-// One d-row = 256 bytes (bf16 d=128 or fp32 d=64) = one 16-lane row of the
-// wave, P = pow2(s) <= 4 slots in consecutive rows, so a team is 16P lanes and
+// One d-row = 256 bytes (bf16 d=128 or fp32 d=64; the forward's row kernel
+// also takes 512) = one 16-lane row of the wave, P = pow2(s) <= 4 slots in consecutive rows, so a team is 16P lanes and
 // a wave serves 4/P units at once.  Persistent XCD-aware loop over units in
 // pair-major order; the next unit's edge slot is fetched one unit ahead.
 struct SeaFwdFast {
@@ -260,17 +260,18 @@ hipError_t dispatch_g(const SeaFwdArgs& a, int G, hipStream_t st) {
 }
 
 // One unit per 16-lane row, four units per wavefront.  Lane r of the row
-// holds bytes [16r, 16r + 16) of every 256-byte d-row the unit touches (its
-// G query rows, and the K and V rows of its S edge slots, side by side in
-// registers).  The only cross-lane step is the 16-lane DPP sum of each
-// score; the softmax over the slots and the weighted sum of the V rows are
-// lane-local.  Slots t >= s (when s < S) are dead.  Rows never exchange
+// holds bytes [256k + 16r, 256k + 16r + 16), k < R, of every (256 R)-byte
+// d-row the unit touches (its G query rows, and the K and V rows of its S
+// edge slots, side by side in registers): R = 1 for bf16 at d = 128 (and
+// fp32 at d = 64), R = 2 for bf16 at d = 256 and fp32 at d = 128.  The only
+// cross-lane step is the 16-lane DPP sum of each score; the softmax over the
+// slots and the weighted sum of the V rows are lane-local.  Slots t >= s (when s < S) are dead.  Rows never exchange
 // data, so rows of one wavefront may leave the item loop at different times.
-template <typename T, int G, int S, bool VEC>
+template <typename T, int G, int S, bool VEC, int R>
 __global__ __launch_bounds__(kBlock) void sea_fwd_row_kernel(SeaFwdFast a) {
     using A = typename io<T>::acc;
     constexpr int V = io<T>::V;
-    constexpr int ROW = 256;
+    constexpr int ROW = 256 * R;
     constexpr int GC = G < 4 ? G : 4;   // query rows held at once
     const int r = threadIdx.x & 15;
     const A c = (A)a.scale * (A)1.4426950408889634;
@@ -310,14 +311,17 @@ __global__ __launch_bounds__(kBlock) void sea_fwd_row_kernel(SeaFwdFast a) {
     for (int u = sc.q; u < sc.end; u += sc.step) {
         const Item nxt = fetch(u + sc.step);
         bool live[S];
-        uint4 kr[S], vr[S];
+        uint4 kr[S][R], vr[S][R];
 #pragma unroll
         for (int t = 0; t < S; ++t) {
             live[t] = cur.wt[t] > 0.0f;
             const uint32_t off =
                 (uint32_t)(cur.pos.kvrow0 + (live[t] ? cur.j[t] : 0) * a.hkv) * ROW + r * 16;
-            kr[t] = *reinterpret_cast<const uint4*>(a.k + off);
-            vr[t] = *reinterpret_cast<const uint4*>(a.v + off);
+#pragma unroll
+            for (int k = 0; k < R; ++k) {
+                kr[t][k] = *reinterpret_cast<const uint4*>(a.k + off + 256 * k);
+                vr[t][k] = *reinterpret_cast<const uint4*>(a.v + off + 256 * k);
+            }
         }
         const uint32_t qoff =
             (uint32_t)(cur.pos.bi * a.hq + (cur.pos.unit - cur.pos.bi * a.hkv) * G) * ROW + r * 16;
@@ -328,16 +332,21 @@ __global__ __launch_bounds__(kBlock) void sea_fwd_row_kernel(SeaFwdFast a) {
         float st_val = 0.0f;
 #pragma unroll
         for (int g0 = 0; g0 < G; g0 += GC) {
-            uint4 qr[GC];
+            uint4 qr[GC][R];
 #pragma unroll
             for (int g = 0; g < GC; ++g)
-                qr[g] = load_nt16(a.q + qoff + (g0 + g) * ROW);
+#pragma unroll
+                for (int k = 0; k < R; ++k)
+                    qr[g][k] = load_nt16(a.q + qoff + (g0 + g) * ROW + 256 * k);
 #pragma unroll
             for (int g = 0; g < GC; ++g) {
                 A l[S], sd[S], M = NEG;
 #pragma unroll
                 for (int t = 0; t < S; ++t) {
-                    sd[t] = row_sum16(dot16<V, A>(qr[g], kr[t])) * c;
+                    A dp = dot16<V, A>(qr[g][0], kr[t][0]);
+#pragma unroll
+                    for (int k = 1; k < R; ++k) dp += dot16<V, A>(qr[g][k], kr[t][k]);
+                    sd[t] = row_sum16(dp) * c;
                     l[t] = live[t] ? sd[t] + lw[t] : NEG;
                     M = l[t] > M ? l[t] : M;
                 }
@@ -366,23 +375,26 @@ __global__ __launch_bounds__(kBlock) void sea_fwd_row_kernel(SeaFwdFast a) {
                         __builtin_nontemporal_store(
                             st_val, a.stats + ((size_t)cur.pos.prow * G + g0 + g) * a.s + t0);
                 }
-                A o[V];
 #pragma unroll
-                for (int e = 0; e < V; ++e) o[e] = 0;
+                for (int k = 0; k < R; ++k) {
+                    A o[V];
 #pragma unroll
-                for (int t = 0; t < S; ++t) {
-                    A vf[V];
-                    unpack16<A, V>(vr[t], vf);
-                    const A pt = p[t] * inv;
+                    for (int e = 0; e < V; ++e) o[e] = 0;
 #pragma unroll
-                    for (int e = 0; e < V; ++e) o[e] += pt * vf[e];
-                }
-                char* op = a.o + qoff + (g0 + g) * ROW;
-                if constexpr (V == 8) {
-                    store_u32x4_nt(op, pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3]),
-                                   pack_bf16x2(o[4], o[5]), pack_bf16x2(o[6], o[7]));
-                } else {
-                    store_f32_nt<4>(op, o);
+                    for (int t = 0; t < S; ++t) {
+                        A vf[V];
+                        unpack16<A, V>(vr[t][k], vf);
+                        const A pt = p[t] * inv;
+#pragma unroll
+                        for (int e = 0; e < V; ++e) o[e] += pt * vf[e];
+                    }
+                    char* op = a.o + qoff + (g0 + g) * ROW + 256 * k;
+                    if constexpr (V == 8) {
+                        store_u32x4_nt(op, pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3]),
+                                       pack_bf16x2(o[4], o[5]), pack_bf16x2(o[6], o[7]));
+                    } else {
+                        store_f32_nt<4>(op, o);
+                    }
                 }
             }
         }
@@ -392,30 +404,30 @@ __global__ __launch_bounds__(kBlock) void sea_fwd_row_kernel(SeaFwdFast a) {
     }
 }
 
-template <typename T, int G, int S, bool VEC>
+template <typename T, int G, int S, bool VEC, int R>
 hipError_t run_row(const SeaFwdFast& a, hipStream_t st) {
-    const void* fn = reinterpret_cast<const void*>(&sea_fwd_row_kernel<T, G, S, VEC>);
+    const void* fn = reinterpret_cast<const void*>(&sea_fwd_row_kernel<T, G, S, VEC, R>);
     const int nwg = persistent_grid(fn, a.U, kBlock / 16);
-    hipLaunchKernelGGL((sea_fwd_row_kernel<T, G, S, VEC>), dim3(nwg), dim3(kBlock), 0, st, a);
+    hipLaunchKernelGGL((sea_fwd_row_kernel<T, G, S, VEC, R>), dim3(nwg), dim3(kBlock), 0, st, a);
     return hipGetLastError();
 }
 
-template <typename T, int G>
+template <typename T, int G, int R>
 hipError_t fast_p(const SeaFwdFast& a, hipStream_t st) {
-    if (a.s <= 1) return run_row<T, G, 1, false>(a, st);
-    if (a.s <= 2) return run_row<T, G, 2, false>(a, st);
-    if (a.vec) return run_row<T, G, 4, true>(a, st);
-    return run_row<T, G, 4, false>(a, st);
+    if (a.s <= 1) return run_row<T, G, 1, false, R>(a, st);
+    if (a.s <= 2) return run_row<T, G, 2, false, R>(a, st);
+    if (a.vec) return run_row<T, G, 4, true, R>(a, st);
+    return run_row<T, G, 4, false, R>(a, st);
 }
 
-template <typename T>
+template <typename T, int R>
 hipError_t fast_g(const SeaFwdFast& a, int G, hipStream_t st) {
     switch (G) {
-        case 1: return fast_p<T, 1>(a, st);
-        case 2: return fast_p<T, 2>(a, st);
-        case 4: return fast_p<T, 4>(a, st);
-        case 8: return fast_p<T, 8>(a, st);
-        case 16: return fast_p<T, 16>(a, st);
+        case 1: return fast_p<T, 1, R>(a, st);
+        case 2: return fast_p<T, 2, R>(a, st);
+        case 4: return fast_p<T, 4, R>(a, st);
+        case 8: return fast_p<T, 8, R>(a, st);
+        case 16: return fast_p<T, 16, R>(a, st);
         default: return hipErrorInvalidValue;
     }
 }
@@ -426,6 +438,14 @@ bool sea_fast_shape(int B, int n, int hq, int hkv, int d, bool bf16, int s) {
     const long long es = bf16 ? 2 : 4;
     const long long qbytes = (long long)B * n * hq * d * es;
     return d * es == 256 && s <= 4 && qbytes < (1ll << 32);
+}
+
+// the forward's row kernel also takes 512-byte rows (two pieces per lane)
+static int sea_fwd_row_pieces(int B, int n, int hq, int hkv, int d, bool bf16, int s) {
+    const long long es = bf16 ? 2 : 4;
+    const long long qbytes = (long long)B * n * hq * d * es;
+    if (s > 4 || qbytes >= (1ll << 32)) return 0;
+    return d * es == 256 ? 1 : d * es == 512 ? 2 : 0;
 }
 
 hipError_t launch_sea_forward(int B, int n, int hq, int hkv, int d, bool bf16, float scale,
@@ -439,7 +459,7 @@ hipError_t launch_sea_forward(int B, int n, int hq, int hkv, int d, bool bf16, f
     a.scale = scale;
     a.ts = sea_team(d, bf16 ? 2 : 4, s);
     const int G = hq / hkv;
-    if (sea_fast_shape(B, n, hq, hkv, d, bf16, s)) {
+    if (const int R = sea_fwd_row_pieces(B, n, hq, hkv, d, bf16, s)) {
         SeaFwdFast f;
         f.q = static_cast<const char*>(q); f.k = static_cast<const char*>(k);
         f.v = static_cast<const char*>(v); f.idx = idx; f.w = w; f.o = static_cast<char*>(o);
@@ -447,7 +467,8 @@ hipError_t launch_sea_forward(int B, int n, int hq, int hkv, int d, bool bf16, f
         f.n = n; f.hq = hq; f.hkv = hkv; f.s = s; f.U = a.U; f.scale = scale;
         make_seg_plan(f.sp, B, n, hkv);
         f.vec = s == 4 && (((uintptr_t)idx | (uintptr_t)w) & 15) == 0;
-        return bf16 ? fast_g<bf16_t>(f, G, st) : fast_g<float>(f, G, st);
+        if (R == 2) return bf16 ? fast_g<bf16_t, 2>(f, G, st) : fast_g<float, 2>(f, G, st);
+        return bf16 ? fast_g<bf16_t, 1>(f, G, st) : fast_g<float, 1>(f, G, st);
     }
     return bf16 ? dispatch_g<bf16_t>(a, G, st) : dispatch_g<float>(a, G, st);
 }

@@ -140,5 +140,13 @@ PRESETS = {
         # candidates, then SEA at s1 = 2; the metric pass's shape otherwise.
         Preset("theia", 8, 4096, 16, 8, 128, torch.bfloat16, 2, 4, 4, "mixed",
                BASE_SEED + 5, ser=True, backward=True),
+        # the measured pass at other head shapes and in fp32 (the general
+        # SEA kernels: rows other than 256 bytes)
+        Preset("d64", 8, 4096, 16, 8, 64, torch.bfloat16, 4, 4, 4, "mixed",
+               BASE_SEED + 6, ser=True, backward=True),
+        Preset("d256", 8, 4096, 16, 8, 256, torch.bfloat16, 4, 4, 4, "mixed",
+               BASE_SEED + 7, ser=True, backward=True),
+        Preset("fp32", 8, 4096, 16, 8, 128, torch.float32, 4, 4, 4, "mixed",
+               BASE_SEED + 8, ser=True, backward=True),
     ]
 }

@@ -26,11 +26,14 @@ SEA_SHAPES = [
     (torch.bfloat16, 128, 4, 8, 33),    # two slot chunks per unit
     (torch.bfloat16, 128, 2, 5, 33),    # ragged second chunk
     (torch.bfloat16, 64, 8, 4, 40),
-    (torch.bfloat16, 256, 2, 4, 29),    # 32 lanes per row
+    (torch.bfloat16, 256, 2, 4, 29),    # 32 lanes per row; forward: two pieces per lane
+    (torch.bfloat16, 256, 1, 1, 31),    # 512-byte rows, one slot
+    (torch.bfloat16, 256, 8, 2, 23),    # 512-byte rows, two query chunks
     (torch.bfloat16, 16, 16, 6, 50),    # 2 lanes per row, many units per wave
     (torch.bfloat16, 32, 2, 64, 21),    # the widest slot count
     (torch.float32, 16, 2, 2, 64),      # the tiny preset's geometry
     (torch.float32, 128, 2, 4, 37),
+    (torch.float32, 128, 16, 3, 19),    # 512-byte fp32 rows, four query chunks
     (torch.float32, 256, 1, 3, 19),     # 64 lanes per row: one slot per chunk
     (torch.float32, 32, 4, 9, 41),
     (torch.float32, 64, 2, 4, 37),      # fp32 rows of 256 bytes (fp64 arithmetic)

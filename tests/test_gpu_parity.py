@@ -33,9 +33,10 @@ def test_tiny_preset_whole_chain(stats):
 
 
 @pytest.mark.parametrize("name,stats", [("sea2", False), ("ser_sea4", True), ("metric", False),
-                                        ("metric", True), ("long64k", True), ("theia", True)],
+                                        ("metric", True), ("long64k", True), ("theia", True),
+                                        ("d64", True), ("d256", True), ("fp32", True)],
                          ids=["sea2", "ser_sea4-stats", "metric", "metric-stats", "long64k-stats",
-                              "theia-stats"])
+                              "theia-stats", "d64-stats", "d256-stats", "fp32-stats"])
 def test_full_size_preset_sampled_pairs(name, stats):
     """stats: the forward saves p / w and the backward uses it (as the
     measured pass does)."""
