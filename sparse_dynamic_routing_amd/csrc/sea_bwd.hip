@@ -437,6 +437,16 @@ __device__ __forceinline__ void store_f32(char* p, const A* x) {
     store_n<L>(reinterpret_cast<float*>(p), x);
 }
 
+// 16-lane sum of the product of two rows held as R parts per lane
+template <int V, typename A, int R>
+__device__ __forceinline__ A row_dot(const uint4 (&x)[R], const uint4 (&y)[R]) {
+    if constexpr (R == 1) {
+        return row_sum16(dot16<V, A>(x[0], y[0]));
+    } else {
+        return row_sum16(dot16<V, A>(x[0], y[0]) + dot16<V, A>(x[1], y[1]));
+    }
+}
+
 // Source pass with one unit per 16-lane row, four units per wavefront: lane
 // r holds bytes [16r, 16r + 16) of the unit's G query and upstream-gradient
 // rows and of the K and V rows of its S edge slots (registers).  Scores and
@@ -626,6 +636,207 @@ __global__ __launch_bounds__(kBlock) void sea_bwd_src_row_kernel(SeaBwdFast a) {
     }
 }
 
+// The source pass for 512-byte rows (bf16 d = 256, fp32 d = 128): as
+// sea_bwd_src_row_kernel, with lane r holding the split piece of each of the
+// R = 2 256-byte parts of every row it touches.  A separate kernel, so the
+// code of the 256-byte kernel stays as it is scheduled best.  Scores and
+// the dout.v products are 16-lane DPP sums; the softmax, dl, dq and dw are
+// lane-local.  Lane t < S writes slot t's per-edge coefficients and dw.
+// GLOBAL: also count the in-degree of every K/V row (global index path).
+// SAVED: the softmax comes from the forward's p / w statistics (p = stat * w),
+// so q is not read here and no scores are formed.
+template <typename T, int G, int S, bool VEC, bool GLOBAL, bool SAVED, int R>
+__global__ __launch_bounds__(kBlock) void sea_bwd_src_wide_kernel(SeaBwdFast a) {
+    using A = typename io<T>::acc;
+    constexpr int V = io<T>::V;
+    constexpr int ROW = 256 * R;                      // bytes of an input d-row
+    constexpr int FROW = ROW * 4 / (int)sizeof(T);    // bytes of an fp32 gradient row
+    constexpr int FPART = FROW / R;                   // fp32 bytes of one 256-byte part
+    constexpr int GC = G < 2 ? G : 2;                 // query heads held at once
+    const int r = threadIdx.x & 15;
+    const A c = (A)a.scale * (A)1.4426950408889634;
+    const A sc = (A)a.scale;
+    const A NEG = -INFINITY;
+    const Sched sch = xcd_sched(a.sp, 16);
+    if (sch.q >= sch.end) return;
+
+    struct Item {
+        Pos pos;
+        int j[S];
+        float wt[S];
+    };
+    auto fetch = [&](int u) {
+        Item it;
+        it.pos = pos_of(a.sp, sch.x, u < sch.end ? u : sch.end - 1);
+        if constexpr (VEC) {
+            const int4 j4 = *reinterpret_cast<const int4*>(a.idx + (size_t)it.pos.unit * 4);
+            const float4 w4 = *reinterpret_cast<const float4*>(a.w + (size_t)it.pos.unit * 4);
+            it.j[0] = j4.x; it.j[1] = j4.y; it.j[2] = j4.z; it.j[3] = j4.w;
+            it.wt[0] = w4.x; it.wt[1] = w4.y; it.wt[2] = w4.z; it.wt[3] = w4.w;
+        } else {
+            const size_t e0 = (size_t)it.pos.unit * a.s;
+#pragma unroll
+            for (int t = 0; t < S; ++t) {
+                const int tt = t < a.s ? t : a.s - 1;
+                it.j[t] = a.idx[e0 + tt];
+                const float wv = a.w[e0 + tt];
+                it.wt[t] = t < a.s ? wv : 0.0f;
+            }
+        }
+        return it;
+    };
+
+    Item cur = fetch(sch.q);
+    for (int u = sch.q; u < sch.end; u += sch.step) {
+        const Item nxt = fetch(u + sch.step);
+        bool live[S];
+        int kvrow[S];
+        uint4 kr[S][R], vr[S][R];
+#pragma unroll
+        for (int t = 0; t < S; ++t) {
+            live[t] = cur.wt[t] > 0.0f;
+            kvrow[t] = cur.pos.kvrow0 + (live[t] ? cur.j[t] : 0) * a.hkv;
+            const uint32_t off = (uint32_t)kvrow[t] * ROW;
+#pragma unroll
+            for (int k = 0; k < R; ++k) {
+                kr[t][k] = load_split<V>(a.k + off + 256 * k, r);
+                vr[t][k] = load_split<V>(a.v + off + 256 * k, r);
+            }
+        }
+        const int h = cur.pos.unit - cur.pos.bi * a.hkv;
+        const uint32_t qrow = (uint32_t)(cur.pos.bi * a.hq + h * G);
+        if constexpr (GLOBAL) {
+#pragma unroll
+            for (int t = 0; t < S; ++t)
+                if (r == t && live[t]) atomicAdd(a.ws.cnt + kvrow[t], 1);
+        }
+        A lw[S], dws[S];
+#pragma unroll
+        for (int t = 0; t < S; ++t) {
+            lw[t] = live[t] ? fast_log2((A)cur.wt[t]) : NEG;
+            dws[t] = 0;
+        }
+        // coefficients (scale * dl, p) of this lane's slot, one per head
+        A my_dl[G], my_p[G];
+#pragma unroll
+        for (int g0 = 0; g0 < G; g0 += GC) {
+            uint4 qr[GC][R], dr[GC][R];
+            float st[GC][S];
+#pragma unroll
+            for (int g = 0; g < GC; ++g) {
+                if constexpr (SAVED) {
+                    const float* sp = a.stats + ((size_t)cur.pos.prow * G + g0 + g) * a.s;
+                    if constexpr (VEC) {
+                        const float4 s4 = *reinterpret_cast<const float4*>(sp);
+                        st[g][0] = s4.x; st[g][1] = s4.y; st[g][2] = s4.z; st[g][3] = s4.w;
+                    } else {
+#pragma unroll
+                        for (int t = 0; t < S; ++t) st[g][t] = sp[t < a.s ? t : a.s - 1];
+                    }
+                } else {
+#pragma unroll
+                    for (int k = 0; k < R; ++k)
+                        qr[g][k] = load_split_nt<V>(a.q + (qrow + g0 + g) * ROW + 256 * k, r);
+                }
+#pragma unroll
+                for (int k = 0; k < R; ++k)
+                    dr[g][k] = load_split_nt<V>(a.dout + (qrow + g0 + g) * ROW + 256 * k, r);
+            }
+#pragma unroll
+            for (int g = 0; g < GC; ++g) {
+                A gd[S], p[S], pw[S];
+                if constexpr (SAVED) {
+#pragma unroll
+                    for (int t = 0; t < S; ++t) {
+                        gd[t] = row_dot<V, A, R>(dr[g], vr[t]);
+                        pw[t] = live[t] ? (A)st[g][t] : (A)0;
+                        p[t] = pw[t] * (A)cur.wt[t];
+                    }
+                } else {
+                    A ls[S], l[S], M = NEG;
+#pragma unroll
+                    for (int t = 0; t < S; ++t) {
+                        ls[t] = row_dot<V, A, R>(qr[g], kr[t]) * c;
+                        gd[t] = row_dot<V, A, R>(dr[g], vr[t]);
+                        l[t] = live[t] ? ls[t] + lw[t] : NEG;
+                        M = l[t] > M ? l[t] : M;
+                    }
+                    A ex[S], Z = 0;
+#pragma unroll
+                    for (int t = 0; t < S; ++t) {
+                        ex[t] = live[t] ? fast_exp2(l[t] - M) : (A)0;
+                        Z += ex[t];
+                    }
+                    const A invZ = Z > (A)0 ? fast_rcp(Z) : (A)0;
+#pragma unroll
+                    for (int t = 0; t < S; ++t) {
+                        p[t] = ex[t] * invZ;
+                        // dl / w = exp(l - M) / (Z w) = exp(scale * dot - M) / Z
+                        pw[t] = live[t] ? fast_exp2(ls[t] - M) * invZ : (A)0;
+                    }
+                }
+                A gbar = 0;
+#pragma unroll
+                for (int t = 0; t < S; ++t) gbar += p[t] * gd[t];
+                A dls[S];
+#pragma unroll
+                for (int t = 0; t < S; ++t) {
+                    dls[t] = p[t] * (gd[t] - gbar) * sc;
+                    dws[t] += pw[t] * (gd[t] - gbar);
+                }
+                A sel_dl = dls[0], sel_p = p[0];
+#pragma unroll
+                for (int t = 1; t < S; ++t) {
+                    sel_dl = r == t ? dls[t] : sel_dl;
+                    sel_p = r == t ? p[t] : sel_p;
+                }
+                my_dl[g0 + g] = sel_dl;
+                my_p[g0 + g] = sel_p;
+                // dq of this head: sum over the slots of scale * dl * k
+#pragma unroll
+                for (int k = 0; k < R; ++k) {
+                    A dq[V];
+#pragma unroll
+                    for (int e = 0; e < V; ++e) dq[e] = 0;
+#pragma unroll
+                    for (int t = 0; t < S; ++t) {
+                        A kf[V];
+                        unpack16<A, V>(kr[t][k], kf);
+#pragma unroll
+                        for (int e = 0; e < V; ++e) dq[e] += dls[t] * kf[e];
+                    }
+                    store_split_f32_nt<V>(a.dq + (qrow + g0 + g) * FROW + FPART * k, r, dq);
+                }
+            }
+        }
+        // lane t < s: coefficients of slot t (live slots only; the target
+        // pass reads live edges only) and its dw
+        bool my_live = live[0];
+        A my_dw = dws[0];
+#pragma unroll
+        for (int t = 1; t < S; ++t) {
+            my_live = r == t ? live[t] : my_live;
+            my_dw = r == t ? dws[t] : my_dw;
+        }
+        const size_t my_e = (size_t)cur.pos.unit * a.s + r;
+        if (r < a.s) {
+            if (my_live) {
+                float2* cp = a.ws.coef + my_e * G;
+#pragma unroll
+                for (int g = 0; g < G; ++g) cp[g] = make_float2((float)my_dl[g], (float)my_p[g]);
+            }
+            a.dw[my_e] = (float)my_dw;
+            if (a.write_tgt) {
+                int my_j = cur.j[0];
+#pragma unroll
+                for (int t = 1; t < S; ++t) my_j = r == t ? cur.j[t] : my_j;
+                a.ws.tgt[(size_t)cur.pos.prow * a.s + r] = my_live ? my_j : -1;
+            }
+        }
+        cur = nxt;
+    }
+}
+
 template <typename T, int G, int P>
 __global__ __launch_bounds__(kBlock) void sea_bwd_dst_fast_kernel(SeaBwdFast a) {
     using A = typename io<T>::acc;
@@ -725,12 +936,13 @@ __global__ __launch_bounds__(kBlock) void sea_bwd_dst_fast_kernel(SeaBwdFast a) 
 // pass than four wavefronts per workgroup; eight were slower)
 constexpr int kDstBlock = kWave;
 
-template <typename T, int G, int P>
+template <typename T, int G, int P, int R>
 __global__ __launch_bounds__(kDstBlock) void sea_bwd_dst_row_kernel(SeaBwdFast a) {
     using A = typename io<T>::acc;
     constexpr int V = io<T>::V;
-    constexpr int ROW = 256;
+    constexpr int ROW = 256 * R;                  // R 256-byte parts per d-row
     constexpr int FROW = ROW * 4 / (int)sizeof(T);
+    constexpr int FPART = FROW / R;
     constexpr int L = V / P;
     static_assert(P == 2 || P == 4, "two or four 16-lane rows per target row");
     const int lane = threadIdx.x & (kWave - 1);
@@ -751,11 +963,13 @@ __global__ __launch_bounds__(kDstBlock) void sea_bwd_dst_row_kernel(SeaBwdFast a
     if (slot >= len) eid = -1;
     const uint32_t qbase = (uint32_t)h * G;
 
-    A ak[V], av[V];
+    A ak[R][V], av[R][V];
 #pragma unroll
-    for (int e = 0; e < V; ++e) { ak[e] = 0; av[e] = 0; }
+    for (int k = 0; k < R; ++k)
+#pragma unroll
+        for (int e = 0; e < V; ++e) { ak[k][e] = 0; av[k][e] = 0; }
     for (int p0 = 0;;) {
-        uint4 qr[G], dr[G];
+        uint4 qr[G][R], dr[G][R];
         float2 co[G];
         if (eid >= 0) {
             const int src = (int)fdiv((uint32_t)eid, a.fd_s);      // source unit
@@ -764,8 +978,13 @@ __global__ __launch_bounds__(kDstBlock) void sea_bwd_dst_row_kernel(SeaBwdFast a
             const float2* cf = a.ws.coef + (size_t)eid * G;
 #pragma unroll
             for (int g = 0; g < G; ++g) {
-                qr[g] = *reinterpret_cast<const uint4*>(a.q + (qrow + g) * ROW + r * 16);
-                dr[g] = *reinterpret_cast<const uint4*>(a.dout + (qrow + g) * ROW + r * 16);
+#pragma unroll
+                for (int k = 0; k < R; ++k) {
+                    qr[g][k] = *reinterpret_cast<const uint4*>(a.q + (qrow + g) * ROW +
+                                                               256 * k + r * 16);
+                    dr[g][k] = *reinterpret_cast<const uint4*>(a.dout + (qrow + g) * ROW +
+                                                               256 * k + r * 16);
+                }
                 co[g] = cf[g];
             }
         }
@@ -773,27 +992,35 @@ __global__ __launch_bounds__(kDstBlock) void sea_bwd_dst_row_kernel(SeaBwdFast a
         const int enext = pn + slot < len ? a.ws.list[beg + pn + slot] : -1;
         if (eid >= 0) {
 #pragma unroll
-            for (int g = 0; g < G; ++g) {
-                A qf[V], df[V];
-                unpack16<A, V>(qr[g], qf);
-                unpack16<A, V>(dr[g], df);
+            for (int g = 0; g < G; ++g)
 #pragma unroll
-                for (int e = 0; e < V; ++e) {
-                    ak[e] += (A)co[g].x * qf[e];
-                    av[e] += (A)co[g].y * df[e];
+                for (int k = 0; k < R; ++k) {
+                    A qf[V], df[V];
+                    unpack16<A, V>(qr[g][k], qf);
+                    unpack16<A, V>(dr[g][k], df);
+#pragma unroll
+                    for (int e = 0; e < V; ++e) {
+                        ak[k][e] += (A)co[g].x * qf[e];
+                        av[k][e] += (A)co[g].y * df[e];
+                    }
                 }
-            }
         }
         if (pn >= len) break;
         p0 = pn;
         eid = enext;
     }
-    rows_reduce_scatter<P, V>(ak);
-    rows_reduce_scatter<P, V>(av);
+#pragma unroll
+    for (int k = 0; k < R; ++k) {
+        rows_reduce_scatter<P, V>(ak[k]);
+        rows_reduce_scatter<P, V>(av[k]);
+    }
     const uint32_t o = (uint32_t)pos.unit * FROW + r * 16 * 4 / (int)sizeof(T) +
                        rs_offset<V, P>(row) * 4;
-    store_f32_nt<L>(a.dk + o, ak);
-    store_f32_nt<L>(a.dv + o, av);
+#pragma unroll
+    for (int k = 0; k < R; ++k) {
+        store_f32_nt<L>(a.dk + o + FPART * k, ak[k]);
+        store_f32_nt<L>(a.dv + o + FPART * k, av[k]);
+    }
 }
 
 void launch_index(const SeaBwdArgs& a, long long E, hipStream_t st) {
@@ -834,40 +1061,72 @@ hipError_t dispatch_g(const SeaBwdArgs& a, int G, long long E, hipStream_t st) {
     }
 }
 
-template <typename T, int G, int S, bool VEC, bool GLOBAL>
-void launch_src(const SeaBwdFast& a, hipStream_t st) {
-    // the saved statistics replace the recomputed softmax for bf16 inputs;
-    // fp32 inputs keep their fp64 recomputation
-    if (std::is_same<T, bf16_t>::value && a.stats) {
+template <typename T, int G, int S, bool VEC, bool GLOBAL, bool SAVED, int R>
+void launch_src_k(const SeaBwdFast& a, hipStream_t st) {
+    if constexpr (R == 1) {
         const void* fn =
-            reinterpret_cast<const void*>(&sea_bwd_src_row_kernel<T, G, S, VEC, GLOBAL, true>);
-        hipLaunchKernelGGL((sea_bwd_src_row_kernel<T, G, S, VEC, GLOBAL, true>),
+            reinterpret_cast<const void*>(&sea_bwd_src_row_kernel<T, G, S, VEC, GLOBAL, SAVED>);
+        hipLaunchKernelGGL((sea_bwd_src_row_kernel<T, G, S, VEC, GLOBAL, SAVED>),
                            dim3(persistent_grid(fn, a.U, kBlock / 16)), dim3(kBlock), 0, st, a);
     } else {
-        const void* fn =
-            reinterpret_cast<const void*>(&sea_bwd_src_row_kernel<T, G, S, VEC, GLOBAL, false>);
-        hipLaunchKernelGGL((sea_bwd_src_row_kernel<T, G, S, VEC, GLOBAL, false>),
+        const void* fn = reinterpret_cast<const void*>(
+            &sea_bwd_src_wide_kernel<T, G, S, VEC, GLOBAL, SAVED, R>);
+        hipLaunchKernelGGL((sea_bwd_src_wide_kernel<T, G, S, VEC, GLOBAL, SAVED, R>),
                            dim3(persistent_grid(fn, a.U, kBlock / 16)), dim3(kBlock), 0, st, a);
     }
 }
 
+template <typename T, int G, int S, bool VEC, bool GLOBAL, int R>
+void launch_src(const SeaBwdFast& a, hipStream_t st) {
+    // the saved statistics replace the recomputed softmax for bf16 inputs;
+    // fp32 inputs keep their fp64 recomputation
+    if (std::is_same<T, bf16_t>::value && a.stats) {
+        launch_src_k<T, G, S, VEC, GLOBAL, true, R>(a, st);
+    } else {
+        launch_src_k<T, G, S, VEC, GLOBAL, false, R>(a, st);
+    }
+}
+
+// 512-byte rows (R = 2): the single-pass or partitioned index only (the
+// global-index target kernel takes 256-byte rows)
 template <typename T, int G, int S, bool VEC, int PD>
+hipError_t run_fast2(const SeaBwdArgs& g, const SeaBwdFast& a, long long E, hipStream_t st) {
+    (void)g; (void)E;
+    launch_src<T, G, S, VEC, false, 2>(a, st);
+    const hipError_t e =
+        edge_index_one_pass(a.n)
+            ? launch_edge_index(a.U / (a.n * a.hkv), a.n, a.hkv, a.idx, a.w, a.s, a.ws.tgt,
+                                a.ws.beg, a.ws.len, a.ws.list, a.ws.head, st)
+            : launch_edge_index_long(a.U / (a.n * a.hkv), a.n, a.hkv, a.idx, a.w, a.s,
+                                     a.ws.tgt, a.ws.beg, a.ws.len, a.ws.list, a.ws.head,
+                                     a.ws.cnt, a.ws.off, a.ws.bsum, a.ws.stage, st);
+    if (e != hipSuccess) return e;
+    const long long per_x = (long long)((a.sp.nseg + kXcds - 1) / kXcds) * a.sp.L;
+    const long long rows_per_block = kDstBlock / kWave * (4 / PD);
+    const long long blocks = kXcds * ((per_x + rows_per_block - 1) / rows_per_block);
+    hipLaunchKernelGGL((sea_bwd_dst_row_kernel<T, G, PD, 2>), dim3((unsigned)blocks),
+                       dim3(kDstBlock), 0, st, a);
+    return hipGetLastError();
+}
+
+template <typename T, int G, int S, bool VEC, int PD, int R>
 hipError_t run_fast(const SeaBwdArgs& g, const SeaBwdFast& a, long long E, hipStream_t st) {
+    if constexpr (R == 2) return run_fast2<T, G, S, VEC, PD>(g, a, E, st);
     if (a.global_index) {
         const hipError_t e = launch_zero_f32(reinterpret_cast<float*>(a.ws.cnt), (size_t)a.U, st);
         if (e != hipSuccess) return e;
-        launch_src<T, G, S, VEC, true>(a, st);
+        launch_src<T, G, S, VEC, true, 1>(a, st);
         launch_index(g, E, st);
     } else if (!edge_index_one_pass(a.n)) {
         // long sequences: the partitioned index, from the source pass's
         // compact targets
-        launch_src<T, G, S, VEC, false>(a, st);
+        launch_src<T, G, S, VEC, false, 1>(a, st);
         const hipError_t e = launch_edge_index_long(
             a.U / (a.n * a.hkv), a.n, a.hkv, a.idx, a.w, a.s, a.ws.tgt, a.ws.beg, a.ws.len,
             a.ws.list, a.ws.head, a.ws.cnt, a.ws.off, a.ws.bsum, a.ws.stage, st);
         if (e != hipSuccess) return e;
     } else {
-        launch_src<T, G, S, VEC, false>(a, st);
+        launch_src<T, G, S, VEC, false, 1>(a, st);
         const hipError_t e = launch_edge_index(a.U / (a.n * a.hkv), a.n, a.hkv, a.idx, a.w, a.s,
                                                a.ws.tgt, a.ws.beg, a.ws.len, a.ws.list,
                                                a.ws.head, st);
@@ -877,7 +1136,7 @@ hipError_t run_fast(const SeaBwdArgs& g, const SeaBwdFast& a, long long E, hipSt
         const long long per_x = (long long)((a.sp.nseg + kXcds - 1) / kXcds) * a.sp.L;
         const long long rows_per_block = kDstBlock / kWave * (4 / PD);
         const long long blocks = kXcds * ((per_x + rows_per_block - 1) / rows_per_block);
-        hipLaunchKernelGGL((sea_bwd_dst_row_kernel<T, G, PD>), dim3((unsigned)blocks),
+        hipLaunchKernelGGL((sea_bwd_dst_row_kernel<T, G, PD, 1>), dim3((unsigned)blocks),
                            dim3(kDstBlock), 0, st, a);
         return hipGetLastError();
     }
@@ -888,23 +1147,32 @@ hipError_t run_fast(const SeaBwdArgs& g, const SeaBwdFast& a, long long E, hipSt
     return hipGetLastError();
 }
 
-template <typename T, int G>
+template <typename T, int G, int R>
 hipError_t fast_p(const SeaBwdArgs& g, const SeaBwdFast& a, long long E, hipStream_t st) {
-    if (a.s <= 1) return run_fast<T, G, 1, false, 2>(g, a, E, st);
-    if (a.s <= 2) return run_fast<T, G, 2, false, 2>(g, a, E, st);
-    if (a.vec) return run_fast<T, G, 4, true, 4>(g, a, E, st);
-    return run_fast<T, G, 4, false, 4>(g, a, E, st);
+    if (a.s <= 1) return run_fast<T, G, 1, false, 2, R>(g, a, E, st);
+    if (a.s <= 2) return run_fast<T, G, 2, false, 2, R>(g, a, E, st);
+    if (a.vec) return run_fast<T, G, 4, true, 4, R>(g, a, E, st);
+    return run_fast<T, G, 4, false, 4, R>(g, a, E, st);
 }
 
 template <typename T>
-hipError_t dispatch_fast(const SeaBwdArgs& g, const SeaBwdFast& a, int G, long long E,
+hipError_t dispatch_fast(const SeaBwdArgs& g, const SeaBwdFast& a, int G, int R, long long E,
                          hipStream_t st) {
+    if (R == 2) {
+        switch (G) {
+            case 1: return fast_p<T, 1, 2>(g, a, E, st);
+            case 2: return fast_p<T, 2, 2>(g, a, E, st);
+            case 4: return fast_p<T, 4, 2>(g, a, E, st);
+            case 8: return fast_p<T, 8, 2>(g, a, E, st);
+            default: return hipErrorInvalidValue;
+        }
+    }
     switch (G) {
-        case 1: return fast_p<T, 1>(g, a, E, st);
-        case 2: return fast_p<T, 2>(g, a, E, st);
-        case 4: return fast_p<T, 4>(g, a, E, st);
-        case 8: return fast_p<T, 8>(g, a, E, st);
-        case 16: return fast_p<T, 16>(g, a, E, st);
+        case 1: return fast_p<T, 1, 1>(g, a, E, st);
+        case 2: return fast_p<T, 2, 1>(g, a, E, st);
+        case 4: return fast_p<T, 4, 1>(g, a, E, st);
+        case 8: return fast_p<T, 8, 1>(g, a, E, st);
+        case 16: return fast_p<T, 16, 1>(g, a, E, st);
         default: return hipErrorInvalidValue;
     }
 }
@@ -944,8 +1212,14 @@ hipError_t launch_sea_backward(int B, int n, int hq, int hkv, int d, bool bf16, 
     a.ws.tgt = reinterpret_cast<int*>(base + l.tgt);
     a.ws.stage = reinterpret_cast<int2*>(base + l.stage);
     const long long E = (long long)a.U * s;
-    if (sea_fast_shape(B, n, hq, hkv, d, bf16, s) &&
-        (long long)B * n * hq * d * 4 < (1ll << 32)) {
+    // row kernels: 256-byte rows with any index, 512-byte rows (G <= 8) with
+    // the single-pass or partitioned index
+    const int R = sea_fast_shape(B, n, hq, hkv, d, bf16, s) ? 1
+                  : sea_fast_shape(B, n, hq, hkv, d / 2, bf16, s) && G <= 8 &&
+                            edge_index_supported(n, s)
+                      ? 2
+                      : 0;
+    if (R && (long long)B * n * hq * d * 4 < (1ll << 32)) {
         SeaBwdFast f;
         f.q = static_cast<const char*>(q); f.k = static_cast<const char*>(k);
         f.v = static_cast<const char*>(v); f.dout = static_cast<const char*>(dout);
@@ -961,7 +1235,8 @@ hipError_t launch_sea_backward(int B, int n, int hq, int hkv, int d, bool bf16, 
         f.global_index = !edge_index_supported(n, s);
         f.write_tgt = !f.global_index;
         f.vec = s == 4 && (((uintptr_t)idx | (uintptr_t)w) & 15) == 0;
-        return bf16 ? dispatch_fast<bf16_t>(a, f, G, E, st) : dispatch_fast<float>(a, f, G, E, st);
+        return bf16 ? dispatch_fast<bf16_t>(a, f, G, R, E, st)
+                    : dispatch_fast<float>(a, f, G, R, E, st);
     }
     hipError_t e = launch_zero_f32(reinterpret_cast<float*>(a.ws.cnt), (size_t)a.U, st);
     if (e == hipSuccess && a.ts.nchunk > 1) e = launch_zero_f32(dw, (size_t)a.U * s, st);

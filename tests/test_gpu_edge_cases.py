@@ -175,16 +175,22 @@ def test_ser_backward_source_chunks(n, s1):
             assert_close("dw2", host(d2), r2, 1e-5)
 
 
-@pytest.mark.parametrize("n,s", [(4097, 4), (9000, 4), (12289, 3)])
-def test_sea_backward_partitioned_index(n, s):
+PARTITIONED = [(4097, 4, torch.bfloat16, 128), (9000, 4, torch.bfloat16, 128),
+               (12289, 3, torch.bfloat16, 128),
+               (5000, 4, torch.bfloat16, 256),    # 512-byte rows
+               (4500, 2, torch.float32, 128)]     # 512-byte fp32 rows
+
+
+@pytest.mark.parametrize("n,s,dtype,d", PARTITIONED,
+                         ids=[f"n{c[0]}-s{c[1]}-{str(c[2])[6:]}-d{c[3]}" for c in PARTITIONED])
+def test_sea_backward_partitioned_index(n, s, dtype, d):
     """n > 4096: the reverse edge index is built by target bucket (512 rows)
     and source chunk (4096 tokens); ragged last bucket and chunk, s = 4 (16-byte
     edge rows) and s = 3; every output compared, with the softmax recomputed
     and with the forward's statistics."""
-    say(f"case sea backward partitioned index n={n} s={s}")
+    say(f"case sea backward partitioned index n={n} s={s} dtype={dtype} d={d}")
     rng = np.random.default_rng(5000 + n + s)
-    dtype = torch.bfloat16
-    q, k, v, do, idx, w = _sea_inputs(rng, dtype, 128, 2, s, n, B=1, hkv=2)
+    q, k, v, do, idx, w = _sea_inputs(rng, dtype, d, 2, s, n, B=1, hkv=2)
     rdq, rdk, rdv, rdw = oracle.get().sea_backward(q, k, v, idx, w, do)
     X = TOL[dtype]
     _, st = gm.sea_forward(dev(q), dev(k), dev(v), dev(idx), dev(w), save_stats=True)
