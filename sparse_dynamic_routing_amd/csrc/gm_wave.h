@@ -252,6 +252,11 @@ __device__ __forceinline__ uint4 load_nt16(const char* p) {
     const u32x4_ld_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_ld_t*>(p));
     return make_uint4(v.x, v.y, v.z, v.w);
 }
+// 8 bytes in the low half of a 16-byte register group, the high half zero
+__device__ __forceinline__ uint4 load_nt8(const char* p) {
+    const u32x2_ld_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x2_ld_t*>(p));
+    return make_uint4(v.x, v.y, 0u, 0u);
+}
 template <int V>
 __device__ __forceinline__ uint4 load_split_nt(const char* row, int r) {
     if constexpr (V == 8) {

@@ -636,10 +636,12 @@ __global__ __launch_bounds__(kBlock) void sea_bwd_src_row_kernel(SeaBwdFast a) {
     }
 }
 
-// The source pass for 512-byte rows (bf16 d = 256, fp32 d = 128): as
-// sea_bwd_src_row_kernel, with lane r holding the split piece of each of the
-// R = 2 256-byte parts of every row it touches.  A separate kernel, so the
-// code of the 256-byte kernel stays as it is scheduled best.  Scores and
+// The source pass for 512-byte rows (R = 2: bf16 d = 256, fp32 d = 128)
+// and 128-byte rows (R = 0: bf16 d = 64): as sea_bwd_src_row_kernel, with
+// lane r holding the split piece of each of the two 256-byte parts of every
+// row it touches, or bytes [8r, 8r + 8) of a 128-byte row in the low half of
+// its registers (high half zero).  A separate kernel, so the code of the
+// 256-byte kernel stays as it is scheduled best.  Scores and
 // the dout.v products are 16-lane DPP sums; the softmax, dl, dq and dw are
 // lane-local.  Lane t < S writes slot t's per-edge coefficients and dw.
 // GLOBAL: also count the in-degree of every K/V row (global index path).
@@ -649,9 +651,10 @@ template <typename T, int G, int S, bool VEC, bool GLOBAL, bool SAVED, int R>
 __global__ __launch_bounds__(kBlock) void sea_bwd_src_wide_kernel(SeaBwdFast a) {
     using A = typename io<T>::acc;
     constexpr int V = io<T>::V;
-    constexpr int ROW = 256 * R;                      // bytes of an input d-row
+    constexpr int ROW = R == 0 ? 128 : 256 * R;       // bytes of an input d-row
+    constexpr int NP = R == 0 ? 1 : R;                // register parts per row
     constexpr int FROW = ROW * 4 / (int)sizeof(T);    // bytes of an fp32 gradient row
-    constexpr int FPART = FROW / R;                   // fp32 bytes of one 256-byte part
+    constexpr int FPART = FROW / NP;                  // fp32 bytes of one part
     constexpr int GC = G < 2 ? G : 2;                 // query heads held at once
     const int r = threadIdx.x & 15;
     const A c = (A)a.scale * (A)1.4426950408889634;
@@ -691,16 +694,23 @@ __global__ __launch_bounds__(kBlock) void sea_bwd_src_wide_kernel(SeaBwdFast a) 
         const Item nxt = fetch(u + sch.step);
         bool live[S];
         int kvrow[S];
-        uint4 kr[S][R], vr[S][R];
+        uint4 kr[S][NP], vr[S][NP];
 #pragma unroll
         for (int t = 0; t < S; ++t) {
             live[t] = cur.wt[t] > 0.0f;
             kvrow[t] = cur.pos.kvrow0 + (live[t] ? cur.j[t] : 0) * a.hkv;
             const uint32_t off = (uint32_t)kvrow[t] * ROW;
 #pragma unroll
-            for (int k = 0; k < R; ++k) {
-                kr[t][k] = load_split<V>(a.k + off + 256 * k, r);
-                vr[t][k] = load_split<V>(a.v + off + 256 * k, r);
+            for (int k = 0; k < NP; ++k) {
+                if constexpr (R == 0) {
+                    const uint2 k2 = *reinterpret_cast<const uint2*>(a.k + off + r * 8);
+                    const uint2 v2 = *reinterpret_cast<const uint2*>(a.v + off + r * 8);
+                    kr[t][k] = make_uint4(k2.x, k2.y, 0u, 0u);
+                    vr[t][k] = make_uint4(v2.x, v2.y, 0u, 0u);
+                } else {
+                    kr[t][k] = load_split<V>(a.k + off + 256 * k, r);
+                    vr[t][k] = load_split<V>(a.v + off + 256 * k, r);
+                }
             }
         }
         const int h = cur.pos.unit - cur.pos.bi * a.hkv;
@@ -720,7 +730,7 @@ __global__ __launch_bounds__(kBlock) void sea_bwd_src_wide_kernel(SeaBwdFast a) 
         A my_dl[G], my_p[G];
 #pragma unroll
         for (int g0 = 0; g0 < G; g0 += GC) {
-            uint4 qr[GC][R], dr[GC][R];
+            uint4 qr[GC][NP], dr[GC][NP];
             float st[GC][S];
 #pragma unroll
             for (int g = 0; g < GC; ++g) {
@@ -735,12 +745,14 @@ __global__ __launch_bounds__(kBlock) void sea_bwd_src_wide_kernel(SeaBwdFast a) 
                     }
                 } else {
 #pragma unroll
-                    for (int k = 0; k < R; ++k)
-                        qr[g][k] = load_split_nt<V>(a.q + (qrow + g0 + g) * ROW + 256 * k, r);
+                    for (int k = 0; k < NP; ++k)
+                        qr[g][k] = R == 0 ? load_nt8(a.q + (qrow + g0 + g) * ROW + r * 8)
+                                          : load_split_nt<V>(a.q + (qrow + g0 + g) * ROW + 256 * k, r);
                 }
 #pragma unroll
-                for (int k = 0; k < R; ++k)
-                    dr[g][k] = load_split_nt<V>(a.dout + (qrow + g0 + g) * ROW + 256 * k, r);
+                for (int k = 0; k < NP; ++k)
+                    dr[g][k] = R == 0 ? load_nt8(a.dout + (qrow + g0 + g) * ROW + r * 8)
+                                      : load_split_nt<V>(a.dout + (qrow + g0 + g) * ROW + 256 * k, r);
             }
 #pragma unroll
             for (int g = 0; g < GC; ++g) {
@@ -748,7 +760,7 @@ __global__ __launch_bounds__(kBlock) void sea_bwd_src_wide_kernel(SeaBwdFast a) 
                 if constexpr (SAVED) {
 #pragma unroll
                     for (int t = 0; t < S; ++t) {
-                        gd[t] = row_dot<V, A, R>(dr[g], vr[t]);
+                        gd[t] = row_dot<V, A, NP>(dr[g], vr[t]);
                         pw[t] = live[t] ? (A)st[g][t] : (A)0;
                         p[t] = pw[t] * (A)cur.wt[t];
                     }
@@ -756,8 +768,8 @@ __global__ __launch_bounds__(kBlock) void sea_bwd_src_wide_kernel(SeaBwdFast a) 
                     A ls[S], l[S], M = NEG;
 #pragma unroll
                     for (int t = 0; t < S; ++t) {
-                        ls[t] = row_dot<V, A, R>(qr[g], kr[t]) * c;
-                        gd[t] = row_dot<V, A, R>(dr[g], vr[t]);
+                        ls[t] = row_dot<V, A, NP>(qr[g], kr[t]) * c;
+                        gd[t] = row_dot<V, A, NP>(dr[g], vr[t]);
                         l[t] = live[t] ? ls[t] + lw[t] : NEG;
                         M = l[t] > M ? l[t] : M;
                     }
@@ -794,7 +806,7 @@ __global__ __launch_bounds__(kBlock) void sea_bwd_src_wide_kernel(SeaBwdFast a) 
                 my_p[g0 + g] = sel_p;
                 // dq of this head: sum over the slots of scale * dl * k
 #pragma unroll
-                for (int k = 0; k < R; ++k) {
+                for (int k = 0; k < NP; ++k) {
                     A dq[V];
 #pragma unroll
                     for (int e = 0; e < V; ++e) dq[e] = 0;
@@ -805,7 +817,12 @@ __global__ __launch_bounds__(kBlock) void sea_bwd_src_wide_kernel(SeaBwdFast a) 
 #pragma unroll
                         for (int e = 0; e < V; ++e) dq[e] += dls[t] * kf[e];
                     }
-                    store_split_f32_nt<V>(a.dq + (qrow + g0 + g) * FROW + FPART * k, r, dq);
+                    if constexpr (R == 0) {
+                        // the low half: elements [V/2 r, V/2 (r + 1)) of the row
+                        store_f32_nt<V / 2>(a.dq + (qrow + g0 + g) * FROW + r * (V / 2) * 4, dq);
+                    } else {
+                        store_split_f32_nt<V>(a.dq + (qrow + g0 + g) * FROW + FPART * k, r, dq);
+                    }
                 }
             }
         }
@@ -940,9 +957,13 @@ template <typename T, int G, int P, int R>
 __global__ __launch_bounds__(kDstBlock) void sea_bwd_dst_row_kernel(SeaBwdFast a) {
     using A = typename io<T>::acc;
     constexpr int V = io<T>::V;
-    constexpr int ROW = 256 * R;                  // R 256-byte parts per d-row
+    // R 256-byte parts per d-row; R = 0: a 128-byte row, lane r holding
+    // bytes [8r, 8r + 8) in the low half of its registers (bf16 only)
+    constexpr int ROW = R == 0 ? 128 : 256 * R;
+    constexpr int NP = R == 0 ? 1 : R;
     constexpr int FROW = ROW * 4 / (int)sizeof(T);
-    constexpr int FPART = FROW / R;
+    constexpr int FPART = FROW / NP;
+    static_assert(R > 0 || V / 2 >= P, "a 128-byte row needs V/2 >= P");
     constexpr int L = V / P;
     static_assert(P == 2 || P == 4, "two or four 16-lane rows per target row");
     const int lane = threadIdx.x & (kWave - 1);
@@ -963,13 +984,13 @@ __global__ __launch_bounds__(kDstBlock) void sea_bwd_dst_row_kernel(SeaBwdFast a
     if (slot >= len) eid = -1;
     const uint32_t qbase = (uint32_t)h * G;
 
-    A ak[R][V], av[R][V];
+    A ak[NP][V], av[NP][V];
 #pragma unroll
-    for (int k = 0; k < R; ++k)
+    for (int k = 0; k < NP; ++k)
 #pragma unroll
         for (int e = 0; e < V; ++e) { ak[k][e] = 0; av[k][e] = 0; }
     for (int p0 = 0;;) {
-        uint4 qr[G][R], dr[G][R];
+        uint4 qr[G][NP], dr[G][NP];
         float2 co[G];
         if (eid >= 0) {
             const int src = (int)fdiv((uint32_t)eid, a.fd_s);      // source unit
@@ -979,11 +1000,19 @@ __global__ __launch_bounds__(kDstBlock) void sea_bwd_dst_row_kernel(SeaBwdFast a
 #pragma unroll
             for (int g = 0; g < G; ++g) {
 #pragma unroll
-                for (int k = 0; k < R; ++k) {
-                    qr[g][k] = *reinterpret_cast<const uint4*>(a.q + (qrow + g) * ROW +
-                                                               256 * k + r * 16);
-                    dr[g][k] = *reinterpret_cast<const uint4*>(a.dout + (qrow + g) * ROW +
-                                                               256 * k + r * 16);
+                for (int k = 0; k < NP; ++k) {
+                    if constexpr (R == 0) {
+                        const uint2 q2 = *reinterpret_cast<const uint2*>(a.q + (qrow + g) * ROW + r * 8);
+                        const uint2 d2 =
+                            *reinterpret_cast<const uint2*>(a.dout + (qrow + g) * ROW + r * 8);
+                        qr[g][k] = make_uint4(q2.x, q2.y, 0u, 0u);
+                        dr[g][k] = make_uint4(d2.x, d2.y, 0u, 0u);
+                    } else {
+                        qr[g][k] = *reinterpret_cast<const uint4*>(a.q + (qrow + g) * ROW +
+                                                                   256 * k + r * 16);
+                        dr[g][k] = *reinterpret_cast<const uint4*>(a.dout + (qrow + g) * ROW +
+                                                                   256 * k + r * 16);
+                    }
                 }
                 co[g] = cf[g];
             }
@@ -994,7 +1023,7 @@ __global__ __launch_bounds__(kDstBlock) void sea_bwd_dst_row_kernel(SeaBwdFast a
 #pragma unroll
             for (int g = 0; g < G; ++g)
 #pragma unroll
-                for (int k = 0; k < R; ++k) {
+                for (int k = 0; k < NP; ++k) {
                     A qf[V], df[V];
                     unpack16<A, V>(qr[g][k], qf);
                     unpack16<A, V>(dr[g][k], df);
@@ -1009,15 +1038,27 @@ __global__ __launch_bounds__(kDstBlock) void sea_bwd_dst_row_kernel(SeaBwdFast a
         p0 = pn;
         eid = enext;
     }
+    if constexpr (R == 0) {
+        // only the low V/2 accumulators hold data
+        A hk[V / 2], hv[V / 2];
 #pragma unroll
-    for (int k = 0; k < R; ++k) {
+        for (int e = 0; e < V / 2; ++e) { hk[e] = ak[0][e]; hv[e] = av[0][e]; }
+        rows_reduce_scatter<P, V / 2>(hk);
+        rows_reduce_scatter<P, V / 2>(hv);
+        const uint32_t o = (uint32_t)pos.unit * FROW + r * (V / 2) * 4 + rs_offset<V / 2, P>(row) * 4;
+        store_f32_nt<V / 2 / P>(a.dk + o, hk);
+        store_f32_nt<V / 2 / P>(a.dv + o, hv);
+        return;
+    }
+#pragma unroll
+    for (int k = 0; k < NP; ++k) {
         rows_reduce_scatter<P, V>(ak[k]);
         rows_reduce_scatter<P, V>(av[k]);
     }
     const uint32_t o = (uint32_t)pos.unit * FROW + r * 16 * 4 / (int)sizeof(T) +
                        rs_offset<V, P>(row) * 4;
 #pragma unroll
-    for (int k = 0; k < R; ++k) {
+    for (int k = 0; k < NP; ++k) {
         store_f32_nt<L>(a.dk + o + FPART * k, ak[k]);
         store_f32_nt<L>(a.dv + o + FPART * k, av[k]);
     }
@@ -1089,10 +1130,10 @@ void launch_src(const SeaBwdFast& a, hipStream_t st) {
 
 // 512-byte rows (R = 2): the single-pass or partitioned index only (the
 // global-index target kernel takes 256-byte rows)
-template <typename T, int G, int S, bool VEC, int PD>
+template <typename T, int G, int S, bool VEC, int PD, int R>
 hipError_t run_fast2(const SeaBwdArgs& g, const SeaBwdFast& a, long long E, hipStream_t st) {
     (void)g; (void)E;
-    launch_src<T, G, S, VEC, false, 2>(a, st);
+    launch_src<T, G, S, VEC, false, R>(a, st);
     const hipError_t e =
         edge_index_one_pass(a.n)
             ? launch_edge_index(a.U / (a.n * a.hkv), a.n, a.hkv, a.idx, a.w, a.s, a.ws.tgt,
@@ -1104,14 +1145,14 @@ hipError_t run_fast2(const SeaBwdArgs& g, const SeaBwdFast& a, long long E, hipS
     const long long per_x = (long long)((a.sp.nseg + kXcds - 1) / kXcds) * a.sp.L;
     const long long rows_per_block = kDstBlock / kWave * (4 / PD);
     const long long blocks = kXcds * ((per_x + rows_per_block - 1) / rows_per_block);
-    hipLaunchKernelGGL((sea_bwd_dst_row_kernel<T, G, PD, 2>), dim3((unsigned)blocks),
+    hipLaunchKernelGGL((sea_bwd_dst_row_kernel<T, G, PD, R>), dim3((unsigned)blocks),
                        dim3(kDstBlock), 0, st, a);
     return hipGetLastError();
 }
 
 template <typename T, int G, int S, bool VEC, int PD, int R>
 hipError_t run_fast(const SeaBwdArgs& g, const SeaBwdFast& a, long long E, hipStream_t st) {
-    if constexpr (R == 2) return run_fast2<T, G, S, VEC, PD>(g, a, E, st);
+    if constexpr (R != 1) return run_fast2<T, G, S, VEC, PD, R>(g, a, E, st);
     if (a.global_index) {
         const hipError_t e = launch_zero_f32(reinterpret_cast<float*>(a.ws.cnt), (size_t)a.U, st);
         if (e != hipSuccess) return e;
@@ -1158,6 +1199,18 @@ hipError_t fast_p(const SeaBwdArgs& g, const SeaBwdFast& a, long long E, hipStre
 template <typename T>
 hipError_t dispatch_fast(const SeaBwdArgs& g, const SeaBwdFast& a, int G, int R, long long E,
                          hipStream_t st) {
+    if constexpr (std::is_same<T, bf16_t>::value) {
+        if (R == 0) {
+            switch (G) {
+                case 1: return fast_p<T, 1, 0>(g, a, E, st);
+                case 2: return fast_p<T, 2, 0>(g, a, E, st);
+                case 4: return fast_p<T, 4, 0>(g, a, E, st);
+                case 8: return fast_p<T, 8, 0>(g, a, E, st);
+                case 16: return fast_p<T, 16, 0>(g, a, E, st);
+                default: return hipErrorInvalidValue;
+            }
+        }
+    }
     if (R == 2) {
         switch (G) {
             case 1: return fast_p<T, 1, 2>(g, a, E, st);
@@ -1212,14 +1265,14 @@ hipError_t launch_sea_backward(int B, int n, int hq, int hkv, int d, bool bf16, 
     a.ws.tgt = reinterpret_cast<int*>(base + l.tgt);
     a.ws.stage = reinterpret_cast<int2*>(base + l.stage);
     const long long E = (long long)a.U * s;
-    // row kernels: 256-byte rows with any index, 512-byte rows (G <= 8) with
-    // the single-pass or partitioned index
-    const int R = sea_fast_shape(B, n, hq, hkv, d, bf16, s) ? 1
-                  : sea_fast_shape(B, n, hq, hkv, d / 2, bf16, s) && G <= 8 &&
-                            edge_index_supported(n, s)
-                      ? 2
-                      : 0;
-    if (R && (long long)B * n * hq * d * 4 < (1ll << 32)) {
+    // row kernels: 256-byte rows with any index; with the single-pass or
+    // partitioned index also 512-byte rows (G <= 8) and bf16 128-byte rows
+    const bool part = edge_index_supported(n, s);
+    const int R = sea_fast_shape(B, n, hq, hkv, d, bf16, s)                          ? 1
+                  : sea_fast_shape(B, n, hq, hkv, d / 2, bf16, s) && G <= 8 && part ? 2
+                  : bf16 && sea_fast_shape(B, n, hq, hkv, d * 2, bf16, s) && part   ? 0
+                                                                                    : -1;
+    if (R >= 0 && (long long)B * n * hq * d * 4 < (1ll << 32)) {
         SeaBwdFast f;
         f.q = static_cast<const char*>(q); f.k = static_cast<const char*>(k);
         f.v = static_cast<const char*>(v); f.dout = static_cast<const char*>(dout);

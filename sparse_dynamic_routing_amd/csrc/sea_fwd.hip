@@ -263,16 +263,21 @@ hipError_t dispatch_g(const SeaFwdArgs& a, int G, hipStream_t st) {
 // holds bytes [256k + 16r, 256k + 16r + 16), k < R, of every (256 R)-byte
 // d-row the unit touches (its G query rows, and the K and V rows of its S
 // edge slots, side by side in registers): R = 1 for bf16 at d = 128 (and
-// fp32 at d = 64), R = 2 for bf16 at d = 256 and fp32 at d = 128.  The only
-// cross-lane step is the 16-lane DPP sum of each score; the softmax over the
-// slots and the weighted sum of the V rows are lane-local.  Slots t >= s (when s < S) are dead.  Rows never exchange
-// data, so rows of one wavefront may leave the item loop at different times.
+// fp32 at d = 64), R = 2 for bf16 at d = 256 and fp32 at d = 128.  R = 0
+// takes 128-byte rows (bf16 d = 64, fp32 d = 32): lane r holds bytes
+// [8r, 8r + 8) in the low half of its registers, the high half zero.  The
+// only cross-lane step is the 16-lane DPP sum of each score; the softmax
+// over the slots and the weighted sum of the V rows are lane-local.  Slots
+// t >= s (when s < S) are dead.  Rows never exchange data, so rows of one
+// wavefront may leave the item loop at different times.
 template <typename T, int G, int S, bool VEC, int R>
 __global__ __launch_bounds__(kBlock) void sea_fwd_row_kernel(SeaFwdFast a) {
     using A = typename io<T>::acc;
     constexpr int V = io<T>::V;
-    constexpr int ROW = 256 * R;
-    constexpr int GC = G < 4 ? G : 4;   // query rows held at once
+    constexpr int ROW = R == 0 ? 128 : 256 * R;
+    constexpr int NP = R == 0 ? 1 : R;    // register parts per row
+    constexpr int LB = R == 0 ? 8 : 16;   // bytes of a part per lane
+    constexpr int GC = G < 4 ? G : 4;     // query rows held at once
     const int r = threadIdx.x & 15;
     const A c = (A)a.scale * (A)1.4426950408889634;
     const A NEG = -INFINITY;
@@ -311,20 +316,27 @@ __global__ __launch_bounds__(kBlock) void sea_fwd_row_kernel(SeaFwdFast a) {
     for (int u = sc.q; u < sc.end; u += sc.step) {
         const Item nxt = fetch(u + sc.step);
         bool live[S];
-        uint4 kr[S][R], vr[S][R];
+        uint4 kr[S][NP], vr[S][NP];
 #pragma unroll
         for (int t = 0; t < S; ++t) {
             live[t] = cur.wt[t] > 0.0f;
             const uint32_t off =
-                (uint32_t)(cur.pos.kvrow0 + (live[t] ? cur.j[t] : 0) * a.hkv) * ROW + r * 16;
+                (uint32_t)(cur.pos.kvrow0 + (live[t] ? cur.j[t] : 0) * a.hkv) * ROW + r * LB;
 #pragma unroll
-            for (int k = 0; k < R; ++k) {
-                kr[t][k] = *reinterpret_cast<const uint4*>(a.k + off + 256 * k);
-                vr[t][k] = *reinterpret_cast<const uint4*>(a.v + off + 256 * k);
+            for (int k = 0; k < NP; ++k) {
+                if constexpr (R == 0) {
+                    const uint2 k2 = *reinterpret_cast<const uint2*>(a.k + off);
+                    const uint2 v2 = *reinterpret_cast<const uint2*>(a.v + off);
+                    kr[t][k] = make_uint4(k2.x, k2.y, 0u, 0u);
+                    vr[t][k] = make_uint4(v2.x, v2.y, 0u, 0u);
+                } else {
+                    kr[t][k] = *reinterpret_cast<const uint4*>(a.k + off + 256 * k);
+                    vr[t][k] = *reinterpret_cast<const uint4*>(a.v + off + 256 * k);
+                }
             }
         }
         const uint32_t qoff =
-            (uint32_t)(cur.pos.bi * a.hq + (cur.pos.unit - cur.pos.bi * a.hkv) * G) * ROW + r * 16;
+            (uint32_t)(cur.pos.bi * a.hq + (cur.pos.unit - cur.pos.bi * a.hkv) * G) * ROW + r * LB;
         A lw[S];
 #pragma unroll
         for (int t = 0; t < S; ++t) lw[t] = live[t] ? fast_log2((A)cur.wt[t]) : NEG;
@@ -332,12 +344,13 @@ __global__ __launch_bounds__(kBlock) void sea_fwd_row_kernel(SeaFwdFast a) {
         float st_val = 0.0f;
 #pragma unroll
         for (int g0 = 0; g0 < G; g0 += GC) {
-            uint4 qr[GC][R];
+            uint4 qr[GC][NP];
 #pragma unroll
             for (int g = 0; g < GC; ++g)
 #pragma unroll
-                for (int k = 0; k < R; ++k)
-                    qr[g][k] = load_nt16(a.q + qoff + (g0 + g) * ROW + 256 * k);
+                for (int k = 0; k < NP; ++k)
+                    qr[g][k] = R == 0 ? load_nt8(a.q + qoff + (g0 + g) * ROW)
+                                      : load_nt16(a.q + qoff + (g0 + g) * ROW + 256 * k);
 #pragma unroll
             for (int g = 0; g < GC; ++g) {
                 A l[S], sd[S], M = NEG;
@@ -345,7 +358,7 @@ __global__ __launch_bounds__(kBlock) void sea_fwd_row_kernel(SeaFwdFast a) {
                 for (int t = 0; t < S; ++t) {
                     A dp = dot16<V, A>(qr[g][0], kr[t][0]);
 #pragma unroll
-                    for (int k = 1; k < R; ++k) dp += dot16<V, A>(qr[g][k], kr[t][k]);
+                    for (int k = 1; k < NP; ++k) dp += dot16<V, A>(qr[g][k], kr[t][k]);
                     sd[t] = row_sum16(dp) * c;
                     l[t] = live[t] ? sd[t] + lw[t] : NEG;
                     M = l[t] > M ? l[t] : M;
@@ -376,7 +389,7 @@ __global__ __launch_bounds__(kBlock) void sea_fwd_row_kernel(SeaFwdFast a) {
                             st_val, a.stats + ((size_t)cur.pos.prow * G + g0 + g) * a.s + t0);
                 }
 #pragma unroll
-                for (int k = 0; k < R; ++k) {
+                for (int k = 0; k < NP; ++k) {
                     A o[V];
 #pragma unroll
                     for (int e = 0; e < V; ++e) o[e] = 0;
@@ -389,7 +402,14 @@ __global__ __launch_bounds__(kBlock) void sea_fwd_row_kernel(SeaFwdFast a) {
                         for (int e = 0; e < V; ++e) o[e] += pt * vf[e];
                     }
                     char* op = a.o + qoff + (g0 + g) * ROW + 256 * k;
-                    if constexpr (V == 8) {
+                    if constexpr (R == 0) {
+                        if constexpr (V == 8) {
+                            const u32x2_t h = {pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3])};
+                            __builtin_nontemporal_store(h, reinterpret_cast<u32x2_t*>(op));
+                        } else {
+                            store_f32_nt<2>(op, o);
+                        }
+                    } else if constexpr (V == 8) {
                         store_u32x4_nt(op, pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3]),
                                        pack_bf16x2(o[4], o[5]), pack_bf16x2(o[6], o[7]));
                     } else {
@@ -440,12 +460,12 @@ bool sea_fast_shape(int B, int n, int hq, int hkv, int d, bool bf16, int s) {
     return d * es == 256 && s <= 4 && qbytes < (1ll << 32);
 }
 
-// the forward's row kernel also takes 512-byte rows (two pieces per lane)
+// the forward's row kernel takes 128-, 256- and 512-byte rows: its R, or -1
 static int sea_fwd_row_pieces(int B, int n, int hq, int hkv, int d, bool bf16, int s) {
     const long long es = bf16 ? 2 : 4;
     const long long qbytes = (long long)B * n * hq * d * es;
-    if (s > 4 || qbytes >= (1ll << 32)) return 0;
-    return d * es == 256 ? 1 : d * es == 512 ? 2 : 0;
+    if (s > 4 || qbytes >= (1ll << 32)) return -1;
+    return d * es == 128 ? 0 : d * es == 256 ? 1 : d * es == 512 ? 2 : -1;
 }
 
 hipError_t launch_sea_forward(int B, int n, int hq, int hkv, int d, bool bf16, float scale,
@@ -459,7 +479,7 @@ hipError_t launch_sea_forward(int B, int n, int hq, int hkv, int d, bool bf16, f
     a.scale = scale;
     a.ts = sea_team(d, bf16 ? 2 : 4, s);
     const int G = hq / hkv;
-    if (const int R = sea_fwd_row_pieces(B, n, hq, hkv, d, bf16, s)) {
+    if (const int R = sea_fwd_row_pieces(B, n, hq, hkv, d, bf16, s); R >= 0) {
         SeaFwdFast f;
         f.q = static_cast<const char*>(q); f.k = static_cast<const char*>(k);
         f.v = static_cast<const char*>(v); f.idx = idx; f.w = w; f.o = static_cast<char*>(o);
@@ -467,6 +487,7 @@ hipError_t launch_sea_forward(int B, int n, int hq, int hkv, int d, bool bf16, f
         f.n = n; f.hq = hq; f.hkv = hkv; f.s = s; f.U = a.U; f.scale = scale;
         make_seg_plan(f.sp, B, n, hkv);
         f.vec = s == 4 && (((uintptr_t)idx | (uintptr_t)w) & 15) == 0;
+        if (R == 0) return bf16 ? fast_g<bf16_t, 0>(f, G, st) : fast_g<float, 0>(f, G, st);
         if (R == 2) return bf16 ? fast_g<bf16_t, 2>(f, G, st) : fast_g<float, 2>(f, G, st);
         return bf16 ? fast_g<bf16_t, 1>(f, G, st) : fast_g<float, 1>(f, G, st);
     }

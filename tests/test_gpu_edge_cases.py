@@ -25,7 +25,10 @@ SEA_SHAPES = [
     (torch.bfloat16, 128, 1, 3, 45),    # slot count not a power of two
     (torch.bfloat16, 128, 4, 8, 33),    # two slot chunks per unit
     (torch.bfloat16, 128, 2, 5, 33),    # ragged second chunk
-    (torch.bfloat16, 64, 8, 4, 40),
+    (torch.bfloat16, 64, 8, 4, 40),     # 128-byte rows: low half of each lane's registers
+    (torch.bfloat16, 64, 1, 2, 29),
+    (torch.bfloat16, 64, 16, 1, 21),
+    (torch.float32, 32, 2, 4, 33),      # 128-byte fp32 rows (forward row kernel)
     (torch.bfloat16, 256, 2, 4, 29),    # 32 lanes per row; forward: two pieces per lane
     (torch.bfloat16, 256, 1, 1, 31),    # 512-byte rows, one slot
     (torch.bfloat16, 256, 8, 2, 23),    # 512-byte rows, two query chunks
@@ -178,6 +181,7 @@ def test_ser_backward_source_chunks(n, s1):
 PARTITIONED = [(4097, 4, torch.bfloat16, 128), (9000, 4, torch.bfloat16, 128),
                (12289, 3, torch.bfloat16, 128),
                (5000, 4, torch.bfloat16, 256),    # 512-byte rows
+               (4600, 3, torch.bfloat16, 64),     # 128-byte rows
                (4500, 2, torch.float32, 128)]     # 512-byte fp32 rows
 
 
