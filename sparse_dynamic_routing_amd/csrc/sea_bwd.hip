@@ -390,9 +390,10 @@ __global__ __launch_bounds__(kBlock) void sea_bwd_dst_kernel(SeaBwdArgs a) {
 
 
 // ----------------------------------------------------------------- fast path
-// Same geometry as the forward's fast path: one 256-byte d-row per 16-lane
-// row, P = pow2(s) <= 4 slots (source pass) or P incoming edges (target
-// pass) in consecutive rows, persistent XCD-aware loops in pair-major order.
+// Same geometry as the forward's fast path: one d-row (256 bytes; the wide
+// source kernel and the target row kernel also take 128 and 512) per 16-lane
+// row, one unit (source pass) or P incoming edges (target pass) per row,
+// XCD-aware schedules in pair-major order.
 struct SeaBwdFast {
     const char* q;
     const char* k;

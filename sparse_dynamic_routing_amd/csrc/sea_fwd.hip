@@ -200,10 +200,10 @@ __global__ __launch_bounds__(kBlock) void sea_fwd_kernel(SeaFwdArgs a) {
 
 
 // ----------------------------------------------------------------- fast path
-// One d-row = 256 bytes (bf16 d=128 or fp32 d=64; the forward's row kernel
-// also takes 512) = one 16-lane row of the wave, P = pow2(s) <= 4 slots in consecutive rows, so a team is 16P lanes and
-// a wave serves 4/P units at once.  Persistent XCD-aware loop over units in
-// pair-major order; the next unit's edge slot is fetched one unit ahead.
+// One d-row (256 bytes: bf16 d=128 or fp32 d=64; the row kernel also takes
+// 128- and 512-byte rows) = one 16-lane row of the wave.  Persistent
+// XCD-aware loop over units in pair-major order; the next unit's edge slots
+// are fetched one unit ahead.
 struct SeaFwdFast {
     const char* q;
     const char* k;

@@ -28,15 +28,42 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 
 
+def code_text(src: str) -> str:
+    """C/HIP source without its comments and with runs of whitespace folded,
+    so that editing a comment does not change what the hash says was
+    measured.  String literals are kept as they are."""
+    out, i, n = [], 0, len(src)
+    while i < n:
+        c = src[i]
+        if c == '"' or c == "'":
+            j = i + 1
+            while j < n and src[j] != c:
+                j += 2 if src[j] == "\\" else 1
+            out.append(src[i:j + 1])
+            i = j + 1
+        elif src.startswith("//", i):
+            j = src.find("\n", i)
+            i = n if j < 0 else j
+        elif src.startswith("/*", i):
+            j = src.find("*/", i + 2)
+            out.append(" ")
+            i = n if j < 0 else j + 2
+        else:
+            out.append(c)
+            i += 1
+    return " ".join("".join(out).split())
+
+
 def source_hash() -> str:
-    """sha256 over the HIP sources and the C header (what the counters measured)."""
+    """sha256 over the code (comments left out) of the HIP sources and the C
+    header: what the counters measured."""
     h = hashlib.sha256()
     files = sorted(glob.glob(os.path.join(PKG, "csrc", "*"))) + [
         os.path.join(ROOT, "include", "gm.h")]
     for f in files:
         h.update(os.path.basename(f).encode())
-        with open(f, "rb") as fh:
-            h.update(fh.read())
+        with open(f, encoding="utf-8") as fh:
+            h.update(code_text(fh.read()).encode())
     return h.hexdigest()[:16]
 
 

@@ -48,3 +48,16 @@ def test_committed_profiles_name_their_command_and_sources():
             assert "source_hash:" in text, f
     h = profile_summary.source_hash()
     assert len(h) == 16 and all(c in "0123456789abcdef" for c in h)
+
+
+def test_source_hash_ignores_comments_only():
+    """A comment edit leaves the code text (and so the profiles' hash) as it
+    is; a code edit, or a comment marker inside a string, does not."""
+    ct = profile_summary.code_text
+    a = 'int f(int x) {  // twice\n    return 2 * x; /* doubled */ }\n'
+    b = '// header\nint f(int x) {\n  return 2 * x;\n}'
+    assert ct(a) == ct(b)
+    assert ct(a) != ct(a.replace("2 * x", "3 * x"))
+    s = 'const char* m = "a // b"; // tail'
+    assert '"a // b"' in ct(s) and "tail" not in ct(s)
+    assert ct('x = 1; /* multi\nline */ y = 2;') == "x = 1; y = 2;"
