@@ -1193,11 +1193,8 @@ template <typename T, int G, int R>
 hipError_t fast_p(const SeaBwdArgs& g, const SeaBwdFast& a, long long E, hipStream_t st) {
     if (a.s <= 1) return run_fast<T, G, 1, false, 2, R>(g, a, E, st);
     if (a.s <= 2) return run_fast<T, G, 2, false, 2, R>(g, a, E, st);
-    // target pass: two incoming edges per pass and two K/V rows per
-    // wavefront also at s = 4 (rows average s incoming edges, so most take
-    // two passes; two rows per wavefront keep more gathers in flight)
-    if (a.vec) return run_fast<T, G, 4, true, 2, R>(g, a, E, st);
-    return run_fast<T, G, 4, false, 2, R>(g, a, E, st);
+    if (a.vec) return run_fast<T, G, 4, true, 4, R>(g, a, E, st);
+    return run_fast<T, G, 4, false, 4, R>(g, a, E, st);
 }
 
 template <typename T>
