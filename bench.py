@@ -13,9 +13,10 @@ before timing starts; outputs and workspace are preallocated.
 Prints one JSON line: units (tokens x KV heads) per second, the pass's
 algorithmic HBM bandwidth, per-call times from HIP events on the launch
 stream, the roofline entry of the dominant call, and the CPU oracle's rate
-on a bounded sample of the same workload (rank 0, N=1).  Beside the warm
-headline it reports a cold pass (a 512 MiB scratch write before each pass
-evicts the L2s and the MALL), the pass replayed from a HIP graph, and the
+on a bounded sample of the same workload (rank 0, N=1: one core, then all
+host cores).  The headline is the median cold pass (a 512 MiB scratch write
+before each pass evicts the L2s and the MALL) with p10/p90; beside it the
+warm pass (back to back), the pass replayed from a HIP graph, and the
 pass's counter bytes (calibrated
 FETCH_SIZE + WRITE_SIZE from the committed profile, when it matches the
 kernel sources) against its compulsory bytes.
@@ -59,6 +60,12 @@ BYTES_PER_UNIT = {
     "gm_ser_backward": 32 + 32 + 16 + 16,               # A, A', dw', dw
 }
 CALLS = list(BYTES_PER_UNIT)
+# The same model without the forward's saved p / w (the pages' path: 5,360
+# bytes per unit for the pass, 3,632 for the SEA backward), printed beside
+# the line's own figures.
+SURVEY_BYTES_PER_UNIT = {"gm_ser_forward": 64, "gm_sea_forward": 1568,
+                         "gm_sea_backward": 3632, "gm_ser_backward": 96}
+SURVEY_PASS_BYTES_PER_UNIT = sum(SURVEY_BYTES_PER_UNIT.values())
 # kernels each call launches on this workload (base names as the profiler
 # reports them, template arguments dropped)
 CALL_KERNELS = {
@@ -139,8 +146,8 @@ def parse():
                          "configurations, timed on its own stages (no CPU baseline)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-cold", action="store_true",
-                    help="skip the cold-cache and graph-replay passes (profiler runs of the "
-                         "warm eager pass)")
+                    help="time warm passes only (no flush between passes) and skip the graph "
+                         "replay: for profiler runs of the eager pass")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="instead of the pass, run a plain device copy of MIB MiB "
@@ -217,51 +224,46 @@ class Pass:
         ]
 
 
-def time_gpu(ps: Pass, steps: int, warmup: int):
+def time_steps(ps: Pass, steps: int, warmup: int, flush_mib: int = 0):
+    """Per-step and per-call times (ms, HIP events on the launch stream) of
+    `steps` passes after `warmup` untimed ones.  With `flush_mib` > 0 a
+    scratch buffer of that many MiB is written before every pass (evicting
+    the 4 MB L2s and the 256 MB MALL: a cold pass); only the pass itself lies
+    between its events.  The device is synchronised before and after the
+    timed steps; returns (per-step ms, {call: per-step ms}, wall seconds)."""
     calls = ps.calls()
-    for _ in range(warmup):
+    scratch = (torch.empty(flush_mib * (1 << 20) // 4, dtype=torch.float32, device="cuda")
+               if flush_mib else None)
+    for w in range(warmup):
+        if scratch is not None:
+            scratch.fill_(float(w))
         for c in calls:
             c()
-    torch.cuda.synchronize()
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(calls) + 1)]
           for _ in range(steps)]
-    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    start.record()
-    for s in range(steps):
-        ev[s][0].record()
+    for s_ in range(steps):
+        if scratch is not None:
+            scratch.fill_(float(s_ + 1))
+        ev[s_][0].record()
         for i, c in enumerate(calls):
             c()
-            ev[s][i + 1].record()
-    end.record()
+            ev[s_][i + 1].record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    total_ms = start.elapsed_time(end)
-    per_call = {name: float(np.mean([ev[s][i].elapsed_time(ev[s][i + 1]) for s in range(steps)]))
+    per_step = [ev[s_][0].elapsed_time(ev[s_][-1]) for s_ in range(steps)]
+    per_call = {name: [ev[s_][i].elapsed_time(ev[s_][i + 1]) for s_ in range(steps)]
                 for i, name in enumerate(CALLS)}
-    return total_ms / steps, per_call, wall
-
-
-def time_cold(ps: Pass, steps: int, flush_mib: int = 512):
-    """Mean time of one pass when a `flush_mib` MiB scratch buffer is written
-    before it (evicting the 4 MB L2s and the 256 MB MALL); only the pass is
-    timed (HIP events around it on the launch stream)."""
-    calls = ps.calls()
-    scratch = torch.empty(flush_mib * (1 << 20) // 4, dtype=torch.float32, device="cuda")
-    times = []
-    for s in range(steps + 1):
-        scratch.fill_(float(s))
-        st, en = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        st.record()
-        for c in calls:
-            c()
-        en.record()
-        torch.cuda.synchronize()
-        if s:                                    # the first is a warm-up
-            times.append(st.elapsed_time(en))
     del scratch
-    return float(np.mean(times))
+    return per_step, per_call, wall
+
+
+def stats_ms(xs):
+    """Median, p10, p90 and mean of a list of times."""
+    a = np.asarray(xs, dtype=np.float64)
+    return {"median": float(np.median(a)), "p10": float(np.percentile(a, 10)),
+            "p90": float(np.percentile(a, 90)), "mean": float(a.mean())}
 
 
 def time_graph(ps: Pass, steps: int):
@@ -518,36 +520,82 @@ def profiled_step_bytes(config: str):
     return per_step if hsh == source_hash() else None
 
 
+def _cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def _host_threads() -> int:
+    """Threads for the all-cores leg: the cores this process may run on,
+    at most 16 (one GPU's share of the host)."""
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:
+        n = os.cpu_count() or 1
+    return max(1, min(16, n))
+
+
 def cpu_baseline(ps: Pass, budget_s: float):
-    """The oracle, single-threaded, on whole (batch, KV head) pairs of the same
-    workload, in pair order, until the time budget is spent (whole pairs)."""
+    """The oracle as it stands (single-threaded C in fp64) on whole (batch, KV
+    head) pairs of the same workload: first on one core, pairs in order until
+    `budget_s` is spent; then on all host cores, the same functions on
+    disjoint pairs from a pool of threads (every stage is local to a pair;
+    the C calls release the interpreter lock), whole rounds of all pairs
+    until `budget_s` is spent.  The all-cores rate is the reported value."""
+    import concurrent.futures as cf
     import oracle
     orc = oracle.get()
     p = ps.p
     G = p.hq // p.hkv
     idx, w = ps.host_edges
     act = {k: v.float().numpy() for k, v in ps.host_act.items()}
-    done, spent = 0, 0.0
     pairs = [(b, h) for b in range(p.B) for h in range(p.hkv)]
-    while spent < budget_s and done < 16 * len(pairs):
-        b, h = pairs[done % len(pairs)]
+
+    def one_pair(bh):
+        b, h = bh
         sl = lambda x, g=0: np.ascontiguousarray(  # noqa: E731
-            x[b:b + 1, :, h * g:(h + 1) * g] if g else x[b:b + 1, :, h:h + 1], dtype=None)
+            x[b:b + 1, :, h * g:(h + 1) * g] if g else x[b:b + 1, :, h:h + 1])
         e_i, e_w = sl(idx), sl(w).astype(np.float64)
         q, k, v, do = (np.ascontiguousarray(sl(act[n], G if n in ("q", "dout") else 0),
                                             dtype=np.float64) for n in ("q", "k", "v", "dout"))
-        t0 = time.perf_counter()
         ia, wa = orc.ser_forward(e_i, e_w, e_i, e_w, p.s1)
         orc.sea_forward(q, k, v, ia, wa)
         dq, dk, dv, dwa = orc.sea_backward(q, k, v, ia, wa, do)
         orc.ser_backward(e_i, e_w, e_i, e_w, ia, wa, dwa, aliased=True)
+
+    done, spent = 0, 0.0
+    while spent < budget_s and done < 16 * len(pairs):
+        t0 = time.perf_counter()
+        one_pair(pairs[done % len(pairs)])
         spent += time.perf_counter() - t0
         done += 1
-    units = done * p.n
-    return {"value": units / spent, "unit": "tokens·KV-heads/s", "cores": 1,
-            "kind": "oracle",
-            "sample": f"{done} whole (batch, KV head) pairs of the measured workload "
-                      f"({units} units, {spent:.1f} s), single-threaded C oracle in fp64"}
+    one_rate = done * p.n / spent
+
+    nthr = _host_threads()
+    rounds, mspent = 0, 0.0
+    with cf.ThreadPoolExecutor(max_workers=nthr) as ex:
+        while mspent < budget_s and rounds < 16:
+            t0 = time.perf_counter()
+            list(ex.map(one_pair, pairs))
+            mspent += time.perf_counter() - t0
+            rounds += 1
+    all_units = rounds * len(pairs) * p.n
+    all_rate = all_units / mspent
+    return {"value": all_rate, "unit": "tokens·KV-heads/s", "cores": nthr, "kind": "oracle",
+            "sample": f"{rounds} rounds of all {len(pairs)} (batch, KV head) pairs of the "
+                      f"measured workload ({all_units} units, {mspent:.1f} s) on {nthr} "
+                      f"threads, each thread running the single-threaded C oracle (fp64) on "
+                      f"whole pairs",
+            "cpu_model": _cpu_model(),
+            "single_core": {"value": one_rate, "cores": 1,
+                            "sample": f"{done} whole pairs ({done * p.n} units, "
+                                      f"{spent:.1f} s) in order on one thread"},
+            "speedup_over_one_core": all_rate / one_rate}
 
 
 def main():
@@ -585,11 +633,18 @@ def main():
     p = synth.PRESETS["metric"]
     ps = Pass(p)
     torch.cuda.synchronize()
-    ms, per_call, wall = time_gpu(ps, a.steps, a.warmup)
     U = p.units
-    pass_bytes = sum(BYTES_PER_UNIT.values()) * U
-    cold_ms = None if a.no_cold else time_cold(ps, max(5, a.steps // 5))
+    # headline: cold passes (a 512 MiB write before each evicts L2s and MALL),
+    # median over the timed steps; warm (back-to-back) passes beside it
+    cold_steps, cold_calls, wall = time_steps(ps, a.steps, a.warmup,
+                                              flush_mib=0 if a.no_cold else 512)
+    warm_steps, warm_calls, _ = time_steps(ps, a.steps, a.warmup)
+    cold, warm = stats_ms(cold_steps), stats_ms(warm_steps)
+    ms = cold["median"]
+    per_call = {c: stats_ms(v)["median"] for c, v in cold_calls.items()}
     graph_ms = None if a.no_cold else time_graph(ps, a.steps)
+    pass_bytes = sum(BYTES_PER_UNIT.values()) * U
+    survey_pass_bytes = SURVEY_PASS_BYTES_PER_UNIT * U
     dom = max(per_call, key=per_call.get)
     traffic = {c: profiled_traffic(c) for c in CALLS}
     counter_bytes = (sum(traffic.values()) if all(v is not None for v in traffic.values())
@@ -613,15 +668,24 @@ def main():
                    "B": p.B, "n": p.n, "hq": p.hq, "hkv": p.hkv, "d": p.d,
                    "s1": p.s1, "s2": p.s2, "s3": p.s3, "units_per_step": U,
                    "parallelism": "single GPU"},
+        "timing": ("cold" if not a.no_cold else "warm") +
+                  ": median over the timed steps of HIP events around each pass"
+                  + (" (512 MiB written before each pass, outside its events)"
+                     if not a.no_cold else ""),
+        "ms_per_step_p10_p90": [cold["p10"], cold["p90"]],
         "pass_algorithmic_GBps": pass_bytes / (ms * 1e-3) / 1e9,
         "pass_frac_of_peak": pass_bytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS,
+        "pass_frac_of_peak_at_5360_B_per_unit":
+            survey_pass_bytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS,
         "per_call_ms": per_call,
-        "cold": None if cold_ms is None else {
-            "ms_per_step": cold_ms, "value": U / (cold_ms * 1e-3),
-            "flush": "512 MiB scratch written before each pass"},
+        "warm": {"ms_per_step": warm["median"], "p10": warm["p10"], "p90": warm["p90"],
+                 "mean": warm["mean"], "value": U / (warm["median"] * 1e-3),
+                 "per_call_ms": {c: stats_ms(v)["median"] for c, v in warm_calls.items()},
+                 "how": "the same passes back to back, no flush"},
+        "cold_mean_ms": cold["mean"],
         "graph": None if graph_ms is None else {
             "ms_per_step": graph_ms, "value": U / (graph_ms * 1e-3),
-            "how": "the four calls captured once in a HIP graph, replayed back to back"},
+            "how": "the four calls captured once in a HIP graph, replayed back to back (warm)"},
         "pass_counter": None if counter_bytes is None else {
             "bytes": counter_bytes,
             "GBps": counter_bytes / (ms * 1e-3) / 1e9,
@@ -632,7 +696,10 @@ def main():
                      "achieved": dom_gbs, "peak": PEAK_HBM_GBS,
                      "unit": "GB/s", "frac": dom_gbs / PEAK_HBM_GBS,
                      "traffic": traffic[dom],
-                     "bytes_per_unit": BYTES_PER_UNIT[dom], "units_per_launch": U},
+                     "bytes_per_unit": BYTES_PER_UNIT[dom], "units_per_launch": U,
+                     "frac_at_survey_bytes": (SURVEY_BYTES_PER_UNIT.get(dom, BYTES_PER_UNIT[dom])
+                                              * U / (per_call[dom] * 1e-3) / 1e9 / PEAK_HBM_GBS),
+                     "survey_bytes_per_unit": SURVEY_BYTES_PER_UNIT.get(dom)},
         "wall_s_timed": wall,
     }
     if not a.no_cpu_baseline:

@@ -32,15 +32,17 @@
  *     status and launches nothing.  Kernel launch failures return
  *     GM_ERR_HIP.
  *   - Limits: B, n, hkv >= 0 (zero sizes are a no-op), B*n*hkv < 2^31,
- *     1 <= s <= 64, s2*s3 <= 64, d in {16, 32, 64, 128, 256}, hq % hkv == 0,
- *     hq / hkv in {1, 2, 4, 8, 16}; activation pointers 16-byte aligned,
+ *     1 <= s <= 64, s2*s3 <= 64, d in {16, 32, 64, 128, 256}, hq % hkv == 0
+ *     (any group size G = hq / hkv; G in {1, 2, 4, 8, 16} takes the row
+ *     kernels, other sizes general kernels; gm_decode_step takes
+ *     G in {1, 2, 4, 8, 16} only); activation pointers 16-byte aligned,
  *     edge pointers 4-byte aligned.
- *   - Determinism: gm_ser_forward and gm_sea_forward are bitwise
- *     deterministic.  gm_ser_backward accumulates in fp64, in an order that
- *     may vary, and rounds once, so a result differs between runs only when
- *     the fp64 sums straddle an fp32 rounding boundary.
- *     gm_sea_backward sums each dk/dv row over its incoming edges in an
- *     order that may vary, so their last bits may vary between runs.
+ *   - Determinism: gm_ser_forward, gm_sea_forward and gm_sea_backward are
+ *     bitwise deterministic (the backward sums every dk/dv row over its
+ *     incoming edges in ascending edge-id order).  gm_ser_backward
+ *     accumulates in fp64, in an order that may vary, and rounds once, so a
+ *     result differs between runs only when the fp64 sums straddle an fp32
+ *     rounding boundary.
  */
 #ifndef GM_H
 #define GM_H
@@ -126,7 +128,11 @@ size_t gm_sea_backward_workspace_bytes(int B, int n, int hq, int hkv, int s1);
  *        stats: NULL, or what gm_sea_forward wrote for these q, k, idx, w
  *        and scale (16-byte aligned).  With bf16 inputs the backward then
  *        takes p_t = stats_t * w_t and dl_t / w_t from it instead of
- *        recomputing the scores; fp32 inputs always recompute in fp64.
+ *        recomputing the scores; fp32 inputs always recompute.
+ *        Precision: bf16 inputs are computed in fp32.  For fp32 inputs the
+ *        scores, softmax, g - gbar, dq, dw and the dk/dv row sums are fp64;
+ *        the per-edge coefficients (scale * dl, p) that the source-token
+ *        pass hands to the K/V-row pass are rounded to fp32 in between.
  *   out  dq [B][n][hq][d] fp32, dk, dv [B][n][hkv][d] fp32,
  *        dw [B][n][hkv][s1] fp32; no output may overlap an input.
  *   ws   device workspace of gm_sea_backward_workspace_bytes(...) bytes,
@@ -134,10 +140,14 @@ size_t gm_sea_backward_workspace_bytes(int B, int n, int hq, int hkv, int s1);
  * With g_t = dout.v[idx_t], gbar = sum p_t g_t, dl_t = p_t (g_t - gbar):
  * dq = scale sum_t dl_t k[idx_t]; dk[idx_t] += scale dl_t q;
  * dv[idx_t] += p_t dout; dw_t = sum over the group's query heads of
- * dl_t / w_t.  Padding slots (w = 0) get and pass no gradient.  dk and dv
- * are reduced per K/V row over its incoming edges (a target-sorted pass,
- * no float atomics); the order of a row's edges may vary between runs.
- * Also requires B*n*hkv*s1 < 2^31.
+ * dl_t / w_t.  g_t - gbar is formed as sum over u != t of p_u (g_t - g_u)
+ * (rows of more slots than one lane team holds: from the unnormalised sums,
+ * (g_t Z - sum_u e_u g_u) / Z), so a single live slot gets exactly 0 and a
+ * slot holding nearly all the mass loses little of dw to cancellation, however
+ * small its weight.  Padding slots (w = 0) get and pass
+ * no gradient.  dk and dv are reduced per K/V row over its incoming edges
+ * in ascending edge-id order (a target-sorted pass, no float atomics), so
+ * the call is bitwise deterministic.  Also requires B*n*hkv*s1 < 2^31.
  */
 gm_status gm_sea_backward(int B, int n, int hq, int hkv, int d, gm_dtype dt,
                           float scale, const void* q, const void* k, const void* v,

@@ -36,7 +36,6 @@ gm_status check_sea(int B, int n, int hq, int hkv, int d, gm_dtype dt, int s1) {
     if (hq < 0) return GM_ERR_SHAPE;
     if (hkv == 0) return empty(B, n, hkv) ? GM_OK : GM_ERR_SHAPE;
     if (hq % hkv != 0 || hq == 0) return GM_ERR_UNSUPPORTED;
-    if (!pow2_in(hq / hkv, 1, 16)) return GM_ERR_UNSUPPORTED;
     if (!pow2_in(d, 16, 256)) return GM_ERR_UNSUPPORTED;
     if (dt != GM_F32 && dt != GM_BF16) return GM_ERR_UNSUPPORTED;
     if (s1 < 1 || s1 > 64) return GM_ERR_UNSUPPORTED;
@@ -195,6 +194,9 @@ gm_status gm_decode_step(int B, int T, int hq, int hkv, int d, gm_dtype dt, floa
     gm_status st = check_sea(B, T, hq, hkv, d, dt, s1);
     if (st != GM_OK) return st;
     if ((st = check_ser(B, T, hkv, s1, s2, s3)) != GM_OK) return st;
+    // the decode kernel keeps the group's query rows in registers, built for
+    // these group sizes
+    if (hkv > 0 && !pow2_in(hq / hkv, 1, 16)) return GM_ERR_UNSUPPORTED;
     if ((long long)B * hkv == 0) return GM_OK;
     if (T < 1) return GM_ERR_SHAPE;
     if (!q || !k || !v || !o) return GM_ERR_NULL;

@@ -25,6 +25,9 @@ hipError_t launch_ser_forward(int B, int n, int hkv, const int32_t* idx1, const 
 // The 16-lane-row fast kernels apply: one d-row is 256 bytes, s <= 4, and
 // activation tensors are addressable with 32-bit byte offsets.
 bool sea_fast_shape(int B, int n, int hq, int hkv, int d, bool bf16, int s);
+// Group sizes (query heads per KV head) the row kernels are built for; other
+// sizes take the general kernels.
+bool sea_row_group(int G);
 
 hipError_t launch_sea_forward(int B, int n, int hq, int hkv, int d, bool bf16, float scale,
                               const void* q, const void* k, const void* v,

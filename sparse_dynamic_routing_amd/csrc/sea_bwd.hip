@@ -5,6 +5,8 @@
 // edge weights).  Per unit and query head, over the live slots t:
 //   p_t  = softmax(scale q.k_t + ln w_t)      (recomputed, log2 domain)
 //   g_t  = dout . v_t,  gbar = sum_t p_t g_t,  dl_t = p_t (g_t - gbar)
+//   (g_t - gbar is formed as sum_{u != t} p_u (g_t - g_u), free of the
+//   cancellation of the plain difference when p_t is close to 1)
 //   dq   = scale sum_t dl_t k_t
 //   dk[idx_t] += scale dl_t q,  dv[idx_t] += p_t dout   (over the group's heads)
 //   dw_t = sum_heads dl_t / w_t = sum_heads exp2(ls_t - M) / Z (g_t - gbar)
@@ -23,8 +25,9 @@
 //      gathers the source's q and dout rows and sums
 //      dk = sum coef.a * q, dv = sum coef.p * dout, then writes the row once
 //      (rows without incoming edges get zeros), so no zero-fill is needed.
-// Within a segment the edge order depends on the fill's atomics, so the
-// fp32 sums of dk/dv may differ in the last bits between runs.
+// Within a segment the edges are put in ascending id order after the fill,
+// so each dk/dv row is summed in the same order on every run (bitwise
+// deterministic).
 #include <type_traits>
 
 #include "gm_common.h"
@@ -94,8 +97,10 @@ struct SeaBwdArgs {
 };
 
 // ------------------------------------------------------------ source pass
-template <typename T, int G>
+template <typename T, int GT>
 __global__ __launch_bounds__(kBlock) void sea_bwd_src_kernel(SeaBwdArgs a) {
+    // GT > 0: the group size as a constant; 0: any group size, from the heads
+    const int G = GT > 0 ? GT : a.hq / a.hkv;
     using A = typename io<T>::acc;
     constexpr int V = io<T>::V;
     constexpr int LOG2V = ilog2(V);
@@ -162,8 +167,17 @@ __global__ __launch_bounds__(kBlock) void sea_bwd_src_kernel(SeaBwdArgs a) {
             const A Z = sum_bits(ex, R, team);
             const A invZ = Z > 0 ? (A)1 / Z : (A)0;
             const A p = ex * invZ;
-            const A gbar = sum_bits(p * gd, R, team);
-            const A dls = p * (gd - gbar) * sc;
+            // g_t - gbar as the sum over the other slots u of p_u (g_t - g_u)
+            // (no cancellation when one slot holds nearly all the mass)
+            A cg = 0;
+            const int lbase = lane - tl;
+#pragma unroll 1
+            for (int u = 0; u < P; ++u) {
+                const A pu = __shfl(p, lbase + u * R, kWave);
+                const A gu = __shfl(gd, lbase + u * R, kWave);
+                if (u != t) cg += pu * (gd - gu);
+            }
+            const A dls = p * cg * sc;
             A dqv[V];
 #pragma unroll
             for (int e = 0; e < V; ++e) dqv[e] = dls * kr[e];
@@ -171,7 +185,7 @@ __global__ __launch_bounds__(kBlock) void sea_bwd_src_kernel(SeaBwdArgs a) {
             const int off = reduce_scatter(dqv, tl, R, team, len);
             if (storer) store_len(dqp + g * d + off, dqv, len);
             if (live && r == 0) cp[t * G + g] = make_float2((float)dls, (float)p);
-            if (live) dws += aexp2(ls - M) * invZ * (gd - gbar);
+            if (live) dws += aexp2(ls - M) * invZ * cg;
         }
         if (r == 0 && t < a.s) a.dw[(size_t)unit * a.s + t] = (float)dws;
         return;
@@ -219,7 +233,6 @@ __global__ __launch_bounds__(kBlock) void sea_bwd_src_kernel(SeaBwdArgs a) {
             M = Mn;
         }
         const A invZ = Z > 0 ? (A)1 / Z : (A)0;
-        const A gbar = Sg * invZ;
         A dqv[V];
 #pragma unroll
         for (int e = 0; e < V; ++e) dqv[e] = 0;
@@ -242,13 +255,16 @@ __global__ __launch_bounds__(kBlock) void sea_bwd_src_kernel(SeaBwdArgs a) {
             gd = sum_bits(gd, 1, R);
             const A ls = sd * c;
             const A p = aexp2(ls + lw - M) * invZ;
-            const A dls = p * (gd - gbar) * sc;
+            // g_t - gbar from the unnormalised sums: exactly 0 for a single
+            // live slot (Z and Sg are then one term each)
+            const A cg = (gd * Z - Sg) * invZ;
+            const A dls = p * cg * sc;
 #pragma unroll
             for (int e = 0; e < V; ++e) dqv[e] += dls * kr[e];
             if (r == 0) {
                 cp[t * G + g] = make_float2((float)dls, (float)p);
                 unsafeAtomicAdd(a.dw + (size_t)unit * a.s + t,
-                                (float)(aexp2(ls - M) * invZ * (gd - gbar)));
+                                (float)(aexp2(ls - M) * invZ * cg));
                 if (g == 0) atomicAdd(a.ws.cnt + row, 1);
             }
         }
@@ -330,11 +346,35 @@ __global__ __launch_bounds__(kBlock) void edge_fill_kernel(const int32_t* idx, c
     }
 }
 
+// The fill's atomics leave each row's segment in an order that varies
+// between runs: copy every live edge to its row's start plus the number of
+// the segment's edges with a smaller id, so `out` lists each row's edges by
+// ascending id (the same on every run).
+__global__ __launch_bounds__(kBlock) void edge_order_kernel(const int32_t* idx, const float* w,
+                                                            int n, int hkv, int s, long long E,
+                                                            const int* off, const int* list,
+                                                            int* out) {
+    for (long long e = (long long)blockIdx.x * kBlock + threadIdx.x; e < E;
+         e += (long long)gridDim.x * kBlock) {
+        if (!(w[e] > 0.0f)) continue;
+        const int unit = (int)(e / s);
+        const int h = unit % hkv;
+        const int b = unit / hkv / n;
+        const int row = (b * n + idx[e]) * hkv + h;
+        const int b0 = off[row], b1 = off[row + 1];
+        int rk = 0;
+        for (int p = b0; p < b1; ++p) rk += list[p] < (int)e;
+        out[b0 + rk] = (int)e;
+    }
+}
+
 // ------------------------------------------------------------ target pass
 // One team of R * P lanes per K/V row (b, j, h): P incoming edges side by
 // side, R lanes per 16-byte piece of a d-row, G query heads per edge.
-template <typename T, int G>
+template <typename T, int GT>
 __global__ __launch_bounds__(kBlock) void sea_bwd_dst_kernel(SeaBwdArgs a) {
+    // GT > 0: the group size as a constant; 0: any group size, from the heads
+    const int G = GT > 0 ? GT : a.hq / a.hkv;
     using A = typename io<T>::acc;
     constexpr int V = io<T>::V;
     constexpr int LOG2V = ilog2(V);
@@ -431,6 +471,23 @@ __device__ __forceinline__ Pos pos_of(const SegPlan& sp, int x, int q) {
     p.kvrow0 = b * sp.n * sp.hkv + h;
     p.prow = pair * sp.n + i;
     return p;
+}
+
+// g_t - gbar with gbar = sum_u p_u g_u, written as sum over u != t of
+// p_u (g_t - g_u): the same value when the p sum to 1, without the
+// cancellation of the plain difference when one slot holds nearly all the
+// mass (exactly 0 when a single slot is live).  That difference times p / w
+// is dw, and p / w is large for small w.
+template <int S, typename A>
+__device__ __forceinline__ void centered_pairwise(const A (&p)[S], const A (&g)[S], A (&d)[S]) {
+#pragma unroll
+    for (int t = 0; t < S; ++t) {
+        A x = 0;
+#pragma unroll
+        for (int u = 0; u < S; ++u)
+            if (u != t) x += p[u] * (g[t] - g[u]);
+        d[t] = x;
+    }
 }
 
 template <int L, typename A>
@@ -578,14 +635,12 @@ __global__ __launch_bounds__(kBlock) void sea_bwd_src_row_kernel(SeaBwdFast a) {
                         pw[t] = live[t] ? fast_exp2(ls[t] - M) * invZ : (A)0;
                     }
                 }
-                A gbar = 0;
-#pragma unroll
-                for (int t = 0; t < S; ++t) gbar += p[t] * gd[t];
-                A dls[S];
+                A dg[S], dls[S];
+                centered_pairwise<S>(p, gd, dg);
 #pragma unroll
                 for (int t = 0; t < S; ++t) {
-                    dls[t] = p[t] * (gd[t] - gbar) * sc;
-                    dws[t] += pw[t] * (gd[t] - gbar);
+                    dls[t] = p[t] * dg[t] * sc;
+                    dws[t] += pw[t] * dg[t];
                 }
                 A sel_dl = dls[0], sel_p = p[0];
 #pragma unroll
@@ -788,14 +843,12 @@ __global__ __launch_bounds__(kBlock) void sea_bwd_src_wide_kernel(SeaBwdFast a) 
                         pw[t] = live[t] ? fast_exp2(ls[t] - M) * invZ : (A)0;
                     }
                 }
-                A gbar = 0;
-#pragma unroll
-                for (int t = 0; t < S; ++t) gbar += p[t] * gd[t];
-                A dls[S];
+                A dg[S], dls[S];
+                centered_pairwise<S>(p, gd, dg);
 #pragma unroll
                 for (int t = 0; t < S; ++t) {
-                    dls[t] = p[t] * (gd[t] - gbar) * sc;
-                    dws[t] += pw[t] * (gd[t] - gbar);
+                    dls[t] = p[t] * dg[t] * sc;
+                    dws[t] += pw[t] * dg[t];
                 }
                 A sel_dl = dls[0], sel_p = p[0];
 #pragma unroll
@@ -1075,6 +1128,11 @@ void launch_index(const SeaBwdArgs& a, long long E, hipStream_t st) {
     if (fb > 16384) fb = 16384;
     hipLaunchKernelGGL(edge_fill_kernel, dim3((unsigned)fb), dim3(kBlock), 0, st, a.idx, a.w, a.n,
                        a.hkv, a.s, E, a.ws.cnt, a.ws.list);
+    // the id-ordered list goes to ws.tgt (unused on these paths), which the
+    // target passes then read as their list
+    hipLaunchKernelGGL(edge_order_kernel, dim3((unsigned)fb), dim3(kBlock), 0, st, a.idx, a.w,
+                       a.n, a.hkv, a.s, E, (const int*)a.ws.off, (const int*)a.ws.list,
+                       a.ws.tgt);
 }
 
 template <typename T, int G>
@@ -1084,10 +1142,12 @@ hipError_t run(const SeaBwdArgs& a, long long E, hipStream_t st) {
                        dim3((unsigned)((src_threads + kBlock - 1) / kBlock)), dim3(kBlock), 0, st,
                        a);
     launch_index(a, E, st);
+    SeaBwdArgs t = a;
+    t.ws.list = a.ws.tgt;   // the id-ordered list
     const long long dst_threads = (long long)a.U * a.tt.team;
     hipLaunchKernelGGL((sea_bwd_dst_kernel<T, G>),
                        dim3((unsigned)((dst_threads + kBlock - 1) / kBlock)), dim3(kBlock), 0, st,
-                       a);
+                       t);
     return hipGetLastError();
 }
 
@@ -1099,7 +1159,7 @@ hipError_t dispatch_g(const SeaBwdArgs& a, int G, long long E, hipStream_t st) {
         case 4: return run<T, 4>(a, E, st);
         case 8: return run<T, 8>(a, E, st);
         case 16: return run<T, 16>(a, E, st);
-        default: return hipErrorInvalidValue;
+        default: return run<T, 0>(a, E, st);   // other group sizes
     }
 }
 
@@ -1185,7 +1245,9 @@ hipError_t run_fast(const SeaBwdArgs& g, const SeaBwdFast& a, long long E, hipSt
     const int ndst = persistent_grid(reinterpret_cast<const void*>(
                                          &sea_bwd_dst_fast_kernel<T, G, PD>),
                                      a.U, kBlock / (16 * PD));
-    hipLaunchKernelGGL((sea_bwd_dst_fast_kernel<T, G, PD>), dim3(ndst), dim3(kBlock), 0, st, a);
+    SeaBwdFast t = a;
+    t.ws.list = a.ws.tgt;   // the id-ordered list
+    hipLaunchKernelGGL((sea_bwd_dst_fast_kernel<T, G, PD>), dim3(ndst), dim3(kBlock), 0, st, t);
     return hipGetLastError();
 }
 
@@ -1273,7 +1335,7 @@ hipError_t launch_sea_backward(int B, int n, int hq, int hkv, int d, bool bf16, 
                   : sea_fast_shape(B, n, hq, hkv, d / 2, bf16, s) && G <= 8 && part ? 2
                   : bf16 && sea_fast_shape(B, n, hq, hkv, d * 2, bf16, s) && part   ? 0
                                                                                     : -1;
-    if (R >= 0 && (long long)B * n * hq * d * 4 < (1ll << 32)) {
+    if (R >= 0 && sea_row_group(G) && (long long)B * n * hq * d * 4 < (1ll << 32)) {
         SeaBwdFast f;
         f.q = static_cast<const char*>(q); f.k = static_cast<const char*>(k);
         f.v = static_cast<const char*>(v); f.dout = static_cast<const char*>(dout);

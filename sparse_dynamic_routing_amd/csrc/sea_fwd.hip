@@ -50,8 +50,10 @@ struct SeaFwdArgs {
     TeamShape ts;
 };
 
-template <typename T, int G>
+template <typename T, int GT>
 __global__ __launch_bounds__(kBlock) void sea_fwd_kernel(SeaFwdArgs a) {
+    // GT > 0: the group size as a constant; 0: any group size, from the heads
+    const int G = GT > 0 ? GT : a.hq / a.hkv;
     using A = typename io<T>::acc;
     constexpr int V = io<T>::V;
     constexpr int LOG2V = ilog2(V);
@@ -255,7 +257,7 @@ hipError_t dispatch_g(const SeaFwdArgs& a, int G, hipStream_t st) {
         case 4: return run<T, 4>(a, st);
         case 8: return run<T, 8>(a, st);
         case 16: return run<T, 16>(a, st);
-        default: return hipErrorInvalidValue;
+        default: return run<T, 0>(a, st);   // other group sizes
     }
 }
 
@@ -454,6 +456,8 @@ hipError_t fast_g(const SeaFwdFast& a, int G, hipStream_t st) {
 
 }  // namespace
 
+bool sea_row_group(int G) { return G == 1 || G == 2 || G == 4 || G == 8 || G == 16; }
+
 bool sea_fast_shape(int B, int n, int hq, int hkv, int d, bool bf16, int s) {
     const long long es = bf16 ? 2 : 4;
     const long long qbytes = (long long)B * n * hq * d * es;
@@ -479,7 +483,7 @@ hipError_t launch_sea_forward(int B, int n, int hq, int hkv, int d, bool bf16, f
     a.scale = scale;
     a.ts = sea_team(d, bf16 ? 2 : 4, s);
     const int G = hq / hkv;
-    if (const int R = sea_fwd_row_pieces(B, n, hq, hkv, d, bf16, s); R >= 0) {
+    if (const int R = sea_fwd_row_pieces(B, n, hq, hkv, d, bf16, s); R >= 0 && sea_row_group(G)) {
         SeaFwdFast f;
         f.q = static_cast<const char*>(q); f.k = static_cast<const char*>(k);
         f.v = static_cast<const char*>(v); f.idx = idx; f.w = w; f.o = static_cast<char*>(o);

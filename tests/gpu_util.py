@@ -45,15 +45,29 @@ def host(t: torch.Tensor) -> np.ndarray:
     return t.numpy()
 
 
-def assert_close(name, got, ref, X):
+def scaled_errors(got, ref):
+    """(max scaled error |got - ref| / max(1, |ref|), max absolute error)."""
+    got = np.asarray(got, np.float64); ref = np.asarray(ref, np.float64)
+    assert got.shape == ref.shape, (got.shape, ref.shape)
+    if not got.size:
+        return 0.0, 0.0
+    diff = np.abs(got - ref)
+    return float((diff / np.maximum(1.0, np.abs(ref))).max()), float(diff.max())
+
+
+def assert_close(name, got, ref, X, quiet=False):
     got = np.asarray(got, np.float64); ref = np.asarray(ref, np.float64)
     assert got.shape == ref.shape, (name, got.shape, ref.shape)
     err = np.abs(got - ref) / np.maximum(1.0, np.abs(ref))
     worst = float(err.max()) if err.size else 0.0
-    say(f"    {name}: max scaled error {worst:.3e} (bar {X:g})")
+    worst_abs = float(np.abs(got - ref).max()) if err.size else 0.0
+    if not quiet:
+        say(f"    {name}: max scaled error {worst:.3e}, max absolute error {worst_abs:.3e} "
+            f"(bar {X:g})")
     assert np.isfinite(got).all(), f"{name}: non-finite values"
     assert worst <= X, f"{name}: max scaled error {worst:.3e} > {X:g} at " \
         f"{np.unravel_index(int(err.argmax()), err.shape)}"
+    return worst, worst_abs
 
 
 def assert_ser_match(io, wo, rio, rwo, rwe=None, rel=1e-6):
@@ -102,6 +116,13 @@ class Inputs:
         self.k = synth.normal(p.seed, "k", ks, p.dtype, layer, where)
         self.v = synth.normal(p.seed, "v", ks, p.dtype, layer, where)
         self.dout = synth.normal(p.seed, "dout", qs, p.dtype, layer, where) if p.backward else None
+        self._host = {}
+
+    def host(self, name: str) -> np.ndarray:
+        """An activation as host fp32 numpy, converted once."""
+        if name not in self._host:
+            self._host[name] = host(getattr(self, name))
+        return self._host[name]
 
 
 def run_gpu(inp: Inputs, stats: bool = False):
@@ -140,8 +161,8 @@ def run_oracle_pair(inp: Inputs, b: int, h: int):
     orc = oracle.get()
     G = p.hq // p.hkv
     idx, w = pair(inp.idx, b, h), pair(inp.w, b, h)
-    q = pair(host(inp.q), b, h, G)
-    k, v = pair(host(inp.k), b, h), pair(host(inp.v), b, h)
+    q = pair(inp.host("q"), b, h, G)
+    k, v = pair(inp.host("k"), b, h), pair(inp.host("v"), b, h)
     ref = {}
     if p.ser:
         ia, wa = orc.ser_forward(idx, w, idx, w, p.s1)
@@ -152,7 +173,7 @@ def run_oracle_pair(inp: Inputs, b: int, h: int):
     ref["live"] = np.repeat(wa > 0, G, axis=2)
     ref["wq"] = np.repeat(wa, G, axis=2)          # each query head's slot weights
     if p.backward:
-        do = pair(host(inp.dout), b, h, G)
+        do = pair(inp.host("dout"), b, h, G)
         dq, dk, dv, dw = orc.sea_backward(q, k, v, ia, wa, do)
         ref.update(dq=dq, dk=dk, dv=dv, dwp=dw)
         if p.ser:
@@ -161,23 +182,52 @@ def run_oracle_pair(inp: Inputs, b: int, h: int):
     return ref
 
 
-def compare_pair(p: synth.Preset, got: dict, ref: dict, b: int, h: int):
+def download(got: dict) -> dict:
+    """Every output of run_gpu as host numpy (statistics per query head)."""
+    out = {}
+    for name, t in got.items():
+        out[name] = host(gm.stats_as_query_heads(t) if name == "stats" else t)
+    return out
+
+
+def compare_pair(p: synth.Preset, got: dict, ref: dict, b: int, h: int, worst=None,
+                 quiet=False):
+    """One (b, h) pair of a run against the oracle's recomputation of it.
+    ``got`` holds device tensors or (faster for many pairs) their download().
+    ``worst``, when given, collects the largest (scaled, absolute) error of
+    each output over the pairs compared."""
     G = p.hq // p.hkv
     X = TOL[p.dtype]
+    hst = lambda name: got[name] if isinstance(got[name], np.ndarray) else (  # noqa: E731
+        host(gm.stats_as_query_heads(got[name])) if name == "stats" else host(got[name]))
+
+    def check(name, g, r, bar):
+        e = assert_close(name, g, r, bar, quiet=quiet)
+        if worst is not None:
+            w0 = worst.get(name, (0.0, 0.0))
+            worst[name] = (max(w0[0], e[0]), max(w0[1], e[1]))
+
     if "idx" in ref:
-        assert_ser_match(pair(host(got["idx"]), b, h), pair(host(got["w"]), b, h),
-                         ref["idx"], ref["w"])
-    assert_close("o", pair(host(got["o"]), b, h, G), ref["o"], X)
+        if quiet:
+            gi, gw = pair(hst("idx"), b, h), pair(hst("w"), b, h)
+            assert (gi == ref["idx"]).all(), f"SER indices differ in pair ({b}, {h})"
+            np.testing.assert_allclose(gw, ref["w"], rtol=1e-5, atol=0)
+            if worst is not None:
+                worst["SER rows not bit-identical"] = worst.get(
+                    "SER rows not bit-identical", 0) + int((gw != ref["w"]).any(-1).sum())
+        else:
+            assert_ser_match(pair(hst("idx"), b, h), pair(hst("w"), b, h), ref["idx"], ref["w"])
+    check("o", pair(hst("o"), b, h, G), ref["o"], X)
     if "stats" in got:
         # p / w per slot: times the GPU's own slot weights it is p
-        st = pair(host(gm.stats_as_query_heads(got["stats"])), b, h, G)
+        st = pair(hst("stats"), b, h, G)
         assert (st[~ref["live"]] == 0).all(), "statistics of dead slots must be 0"
-        wq = np.repeat(pair(host(got["w"]), b, h), G, axis=2) if "w" in got else ref["wq"]
-        assert_close("p (statistics * w)", st * wq, ref["p"], 1e-4)
+        wq = np.repeat(pair(hst("w"), b, h), G, axis=2) if "w" in got else ref["wq"]
+        check("p (statistics * w)", st * wq, ref["p"], 1e-4)
     if "dq" in ref:
-        assert_close("dq", pair(host(got["dq"]), b, h, G), ref["dq"], X)
-        assert_close("dk", pair(host(got["dk"]), b, h), ref["dk"], X)
-        assert_close("dv", pair(host(got["dv"]), b, h), ref["dv"], X)
-        assert_close("dw (SEA)", pair(host(got["dwp"]), b, h), ref["dwp"], X)
+        check("dq", pair(hst("dq"), b, h, G), ref["dq"], X)
+        check("dk", pair(hst("dk"), b, h), ref["dk"], X)
+        check("dv", pair(hst("dv"), b, h), ref["dv"], X)
+        check("dw (SEA)", pair(hst("dwp"), b, h), ref["dwp"], X)
     if "dA" in ref:
-        assert_close("dw (SER)", pair(host(got["dA"]), b, h), ref["dA"], X)
+        check("dw (SER)", pair(hst("dA"), b, h), ref["dA"], X)

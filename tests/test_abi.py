@@ -76,7 +76,8 @@ def test_sea_argument_checks(lib):
     args = lambda hq=16, hkv=8, d=128, dt=1, s=4, q=a, oo=o, st=None: (  # noqa: E731
         8, 4096, hq, hkv, d, dt, 0.1, q, b, c, i, w, s, oo, st, None)
     assert f(*args(hq=12)) == UNSUP          # hq % hkv != 0
-    assert f(*args(hq=24)) == UNSUP          # 3 query heads per KV head
+    assert f(*args(hq=24, q=None)) == NULL   # 3 query heads per KV head: accepted (then NULL)
+    assert f(*args(hq=40, q=None)) == NULL   # 5 per KV head
     assert f(*args(d=96)) == UNSUP
     assert f(*args(d=512)) == UNSUP
     assert f(*args(dt=7)) == UNSUP

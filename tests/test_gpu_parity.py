@@ -1,8 +1,9 @@
 """GPU parity: the HIP path (through the C ABI) against the oracle.
 
-Full-size presets are compared on sampled (batch, KV head) pairs, which the
-oracle recomputes exactly (every stage is pair-local); the tiny preset and
-the SER forward of the 4096-token presets are compared everywhere.
+Every stage is local to a (batch, KV head) pair, so the oracle recomputes
+each pair of a full-size run exactly; the full-size presets are compared on
+every pair, element by element (the 21-layer stack on sampled pairs through
+all its layers).
 """
 from __future__ import annotations
 
@@ -13,8 +14,8 @@ import torch
 import oracle
 import sparse_dynamic_routing_amd as gm
 import synth
-from gpu_util import (TOL, Inputs, assert_close, assert_ser_match, compare_pair, dev, host,
-                      pairs_for, run_gpu, run_oracle_pair, say)
+from gpu_util import (TOL, Inputs, assert_close, assert_ser_match, compare_pair, dev, download,
+                      host, pairs_for, run_gpu, run_oracle_pair, say)
 
 pytestmark = pytest.mark.gpu
 
@@ -32,21 +33,32 @@ def test_tiny_preset_whole_chain(stats):
         compare_pair(p, got, run_oracle_pair(inp, b, h), b, h)
 
 
-@pytest.mark.parametrize("name,stats", [("sea2", False), ("ser_sea4", True), ("metric", False),
-                                        ("metric", True), ("long64k", True), ("theia", True),
-                                        ("d64", True), ("d256", True), ("fp32", True)],
-                         ids=["sea2", "ser_sea4-stats", "metric", "metric-stats", "long64k-stats",
-                              "theia-stats", "d64-stats", "d256-stats", "fp32-stats"])
-def test_full_size_preset_sampled_pairs(name, stats):
-    """stats: the forward saves p / w and the backward uses it (as the
-    measured pass does)."""
+FULL = [("sea2", False), ("ser_sea4", True), ("metric", False), ("metric", True),
+        ("long64k", True), ("theia", True), ("d64", True), ("d256", True), ("fp32", True)]
+
+
+@pytest.mark.parametrize("name,stats", FULL,
+                         ids=[f"{n}{'-stats' if s else ''}" for n, s in FULL])
+def test_full_size_preset_every_pair(name, stats):
+    """Every (batch, KV head) pair of the full-size run against the oracle,
+    element by element.  stats: the forward saves p / w and the backward
+    uses it (as the measured pass does).  The worst scaled and absolute
+    error of each output over all pairs is printed."""
     p = synth.PRESETS[name]
     say(f"case {name} stats={stats} {p}")
     inp = Inputs(p)
-    got = run_gpu(inp, stats=stats)
-    for b, h in pairs_for(p.B, p.hkv, count=3 if p.n <= 4096 else 2):
-        say(f"  pair b={b} h={h}")
-        compare_pair(p, got, run_oracle_pair(inp, b, h), b, h)
+    got = download(run_gpu(inp, stats=stats))
+    torch.cuda.empty_cache()
+    worst = {}
+    for b in range(p.B):
+        for h in range(p.hkv):
+            compare_pair(p, got, run_oracle_pair(inp, b, h), b, h, worst=worst, quiet=True)
+    say(f"  all {p.B * p.hkv} pairs within the bar (X = {TOL[p.dtype]:g}); worst over them:")
+    for out, e in worst.items():
+        if isinstance(e, tuple):
+            say(f"    {out}: max scaled error {e[0]:.3e}, max absolute error {e[1]:.3e}")
+        else:
+            say(f"    {out}: {e}")
 
 
 @pytest.mark.parametrize("name", ["ser_sea4", "theia"])
