@@ -64,7 +64,9 @@ typedef enum {
     GM_ERR_WORKSPACE = 4,    /* workspace missing or too small               */
     GM_ERR_HIP = 5,          /* a HIP launch or runtime call failed          */
     GM_ERR_ALIGN = 6,        /* a pointer is not aligned as required         */
-    GM_ERR_ALIAS = 7         /* an output overlaps an input it must not      */
+    GM_ERR_ALIAS = 7,        /* an output overlaps an input it must not      */
+    GM_ERR_TOO_LARGE = 8     /* the sizes need more than the fixed scratch of
+                                gm_sea_backward_noalloc                       */
 } gm_status;
 
 typedef enum { GM_F32 = 0, GM_BF16 = 1 } gm_dtype;
@@ -155,6 +157,33 @@ gm_status gm_sea_backward(int B, int n, int hq, int hkv, int d, gm_dtype dt,
                           const void* dout, const float* stats, float* dq, float* dk,
                           float* dv, float* dw, void* workspace, size_t workspace_bytes,
                           hipStream_t stream);
+
+/*
+ * gm_sea_backward without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation): the same kernels and results as
+ * gm_sea_backward (bitwise), with the workspace in a fixed array of
+ * GM_NOALLOC_SCRATCH_BYTES that the library holds on every GPU it runs on
+ * until the process ends.  The call itself allocates and frees nothing.
+ *   - Sizes whose gm_sea_backward_workspace_bytes(...) exceeds
+ *     GM_NOALLOC_SCRATCH_BYTES return GM_ERR_TOO_LARGE and launch nothing
+ *     (the measured layer, B = 8, n = 4096, 8 KV heads, G = 2, s1 = 4,
+ *     needs 32 MiB).
+ *   - Every call on one GPU shares that GPU's array: calls that may run at
+ *     the same time on one GPU (different streams, or threads) race and
+ *     must be ordered by the caller.
+ *   - The first call on a GPU looks up the array's device address
+ *     (hipGetSymbolAddress, with that GPU current); failure returns
+ *     GM_ERR_HIP.  The GPU is the one `stream` belongs to (the current one
+ *     for the null stream).
+ * Other arguments, checks and errors as gm_sea_backward.
+ */
+#define GM_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+gm_status gm_sea_backward_noalloc(int B, int n, int hq, int hkv, int d, gm_dtype dt,
+                                  float scale, const void* q, const void* k, const void* v,
+                                  const int32_t* idx, const float* w, int s1,
+                                  const void* dout, const float* stats, float* dq, float* dk,
+                                  float* dv, float* dw, hipStream_t stream);
 
 /*
  * Bytes of device workspace gm_ser_backward needs for these sizes: fp64

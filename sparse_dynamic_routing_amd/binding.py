@@ -22,9 +22,10 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libgm.so")
 
 GM_F32, GM_BF16 = 0, 1
 STATUS = {0: "GM_OK", 1: "GM_ERR_NULL", 2: "GM_ERR_SHAPE", 3: "GM_ERR_UNSUPPORTED",
-          4: "GM_ERR_WORKSPACE", 5: "GM_ERR_HIP", 6: "GM_ERR_ALIGN", 7: "GM_ERR_ALIAS"}
+          4: "GM_ERR_WORKSPACE", 5: "GM_ERR_HIP", 6: "GM_ERR_ALIGN", 7: "GM_ERR_ALIAS",
+          8: "GM_ERR_TOO_LARGE"}
 EXPORTS = ("gm_ser_forward", "gm_sea_forward", "gm_sea_backward_workspace_bytes",
-           "gm_sea_backward", "gm_decode_step", "gm_dense_refresh", "gm_leg_mix_forward",
+           "gm_sea_backward", "gm_sea_backward_noalloc", "gm_decode_step", "gm_dense_refresh", "gm_leg_mix_forward",
            "gm_leg_mix_backward_workspace_bytes", "gm_leg_mix_backward",
            "gm_ser_backward_workspace_bytes", "gm_ser_backward", "gm_check_edges",
            "gm_status_string", "gm_abi_version")
@@ -54,6 +55,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
         "gm_sea_backward_workspace_bytes": [_I, _I, _I, _I, _I],
         "gm_sea_backward": [_I, _I, _I, _I, _I, _I, _F, _P, _P, _P, _P, _P, _I, _P, _P,
                             _P, _P, _P, _P, _P, _Z, _P],
+        "gm_sea_backward_noalloc": [_I, _I, _I, _I, _I, _I, _F, _P, _P, _P, _P, _P, _I, _P,
+                                    _P, _P, _P, _P, _P, _P],
         "gm_decode_step": [_I, _I, _I, _I, _I, _I, _F, _P, _P, _I, _P, _P, _I, _I, _P, _P,
                            _P, _P, _P, _P, _P],
         "gm_dense_refresh": [_I, _I, _I, _I, _I, _I, _F, _P, _P, _I, _I, _P, _P, _P, _P],
@@ -169,6 +172,27 @@ def gm_sea_backward(q, k, v, idx, w, dout, dq, dk, dv, dw, workspace, scale=None
           _ptr(idx), _ptr(w), s1, _ptr(dout), _ptr(stats), _ptr(dq), _ptr(dk), _ptr(dv),
           _ptr(dw), _ptr(workspace), workspace.numel() * workspace.element_size(),
           _stream(stream))
+
+
+def gm_sea_backward_noalloc(q, k, v, idx, w, dout, dq, dk, dv, dw, scale=None, stream=None,
+                            stats=None) -> None:
+    """gm_sea_backward with the library's fixed per-GPU scratch instead of a
+    workspace (the call allocates nothing)."""
+    B, n, hq, d = q.shape
+    hkv, s1 = idx.shape[2], idx.shape[3]
+    _need(q, "q", _ACT)
+    _need(k, "k", (q.dtype,), (B, n, hkv, d)); _need(v, "v", (q.dtype,), (B, n, hkv, d))
+    _need(idx, "idx", (torch.int32,), (B, n, hkv, s1)); _need(w, "w", (torch.float32,), idx.shape)
+    _need(dout, "dout", (q.dtype,), q.shape)
+    _need(dq, "dq", (torch.float32,), q.shape)
+    _need(dk, "dk", (torch.float32,), k.shape); _need(dv, "dv", (torch.float32,), v.shape)
+    _need(dw, "dw", (torch.float32,), idx.shape)
+    if stats is not None:
+        _need(stats, "stats", (torch.float32,), (B, hkv, n, hq // hkv, s1))
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    _call("gm_sea_backward_noalloc", B, n, hq, hkv, d, _act_dtype(q), scale, _ptr(q), _ptr(k),
+          _ptr(v), _ptr(idx), _ptr(w), s1, _ptr(dout), _ptr(stats), _ptr(dq), _ptr(dk),
+          _ptr(dv), _ptr(dw), _stream(stream))
 
 
 def gm_decode_step(idx1, w1, idx2, w2, q, k, v, idx_out, w_out, o, scale=None,

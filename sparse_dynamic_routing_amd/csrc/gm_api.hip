@@ -7,7 +7,45 @@
 #include <limits.h>
 #include <stdint.h>
 
+#include <mutex>
+
+// Scratch space of gm_sea_backward_noalloc: one copy per GPU, held by the
+// loaded code object until the process ends.  Host code never names it
+// directly (its name is only a host-side stand-in); it takes the device
+// address that hipGetSymbolAddress returns for the call's GPU.
+static __device__ __align__(256) unsigned char scratch[GM_NOALLOC_SCRATCH_BYTES];
+
 namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mutex;
+void* g_scratch_ptr[kMaxDevices];   // device address of `scratch`, per device
+
+// Device address of `scratch` on the GPU that `stream` belongs to (the
+// current GPU for the null stream), looked up once per GPU with that GPU
+// current.
+gm_status scratch_address(hipStream_t stream, void** out) {
+    int dev = -1;
+    if (stream) {
+        if (hipStreamGetDevice(stream, &dev) != hipSuccess) return GM_ERR_HIP;
+    } else if (hipGetDevice(&dev) != hipSuccess) {
+        return GM_ERR_HIP;
+    }
+    if (dev < 0 || dev >= kMaxDevices) return GM_ERR_HIP;
+    std::lock_guard<std::mutex> lock(g_scratch_mutex);
+    if (!g_scratch_ptr[dev]) {
+        int cur = -1;
+        if (hipGetDevice(&cur) != hipSuccess) return GM_ERR_HIP;
+        if (cur != dev && hipSetDevice(dev) != hipSuccess) return GM_ERR_HIP;
+        void* p = nullptr;
+        const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (cur != dev && hipSetDevice(cur) != hipSuccess) return GM_ERR_HIP;
+        if (e != hipSuccess || !p) return GM_ERR_HIP;
+        g_scratch_ptr[dev] = p;
+    }
+    *out = g_scratch_ptr[dev];
+    return GM_OK;
+}
 
 using gm::TeamShape;
 
@@ -61,7 +99,7 @@ bool overlaps(const void* a, size_t an, const void* b, size_t bn) {
 
 extern "C" {
 
-int gm_abi_version(void) { return 5; }
+int gm_abi_version(void) { return 6; }
 
 const char* gm_status_string(gm_status s) {
     switch (s) {
@@ -73,6 +111,9 @@ const char* gm_status_string(gm_status s) {
         case GM_ERR_HIP: return "HIP launch or runtime error";
         case GM_ERR_ALIGN: return "pointer not aligned as required";
         case GM_ERR_ALIAS: return "an output overlaps an input";
+        case GM_ERR_TOO_LARGE:
+            return "sizes need more scratch than the fixed GM_NOALLOC_SCRATCH_BYTES of the "
+                   "allocation-free call (use the call with a workspace)";
     }
     return "unknown status";
 }
@@ -261,16 +302,21 @@ size_t gm_sea_backward_workspace_bytes(int B, int n, int hq, int hkv, int s1) {
     return gm::sea_backward_workspace_bytes((long long)B * n * hkv, s1, hq / hkv, n);
 }
 
-gm_status gm_sea_backward(int B, int n, int hq, int hkv, int d, gm_dtype dt, float scale,
-                          const void* q, const void* k, const void* v, const int32_t* idx,
-                          const float* w, int s1, const void* dout, const float* stats,
-                          float* dq, float* dk, float* dv, float* dw, void* workspace,
-                          size_t workspace_bytes, hipStream_t stream) {
-    gm_status st = check_sea(B, n, hq, hkv, d, dt, s1);
-    if (st != GM_OK) return st;
-    if (empty(B, n, hkv)) return GM_OK;
+}  // extern "C"
+
+namespace {
+
+// Every host-side check of gm_sea_backward; `workspace` null: the
+// allocation-free call, whose scratch is the library's own (no workspace
+// checks).  Returns GM_OK when the call may launch.
+gm_status sea_backward_checks(int B, int n, int hq, int hkv, int d, gm_dtype dt,
+                              const void* q, const void* k, const void* v, const int32_t* idx,
+                              const float* w, int s1, const void* dout, const float* stats,
+                              float* dq, float* dk, float* dv, float* dw, const void* workspace,
+                              size_t workspace_bytes) {
     if ((long long)B * n * hkv * s1 >= (long long)INT_MAX) return GM_ERR_SHAPE;
     if (!q || !k || !v || !dout || !dq || !dk || !dv || !dw) return GM_ERR_NULL;
+    gm_status st;
     if ((st = check_edge_ptrs(idx, w)) != GM_OK) return st;
     if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(dout, 16) ||
         !aligned(dq, 16) || !aligned(dk, 16) || !aligned(dv, 16) || !aligned(dw, 4) ||
@@ -284,19 +330,64 @@ gm_status gm_sea_backward(int B, int n, int hq, int hkv, int d, gm_dtype dt, flo
     const size_t inb[7] = {nq * es, nk * es, nk * es, nq * es, ne * 4, ne * 4,
                            stats ? ns * 4 : 0};
     const size_t need = gm_sea_backward_workspace_bytes(B, n, hq, hkv, s1);
-    if (!workspace || workspace_bytes < need) return GM_ERR_WORKSPACE;
-    if (!aligned(workspace, 256)) return GM_ERR_ALIGN;
+    if (workspace) {
+        if (workspace_bytes < need) return GM_ERR_WORKSPACE;
+        if (!aligned(workspace, 256)) return GM_ERR_ALIGN;
+    }
     const void* outs[5] = {dq, dk, dv, dw, workspace};
-    const size_t outb[5] = {nq * 4, nk * 4, nk * 4, ne * 4, need};
+    const size_t outb[5] = {nq * 4, nk * 4, nk * 4, ne * 4, workspace ? need : 0};
     for (int a = 0; a < 5; ++a) {
         for (int b = 0; b < 7; ++b)
-            if (inb[b] && overlaps(outs[a], outb[a], ins[b], inb[b])) return GM_ERR_ALIAS;
+            if (inb[b] && outb[a] && overlaps(outs[a], outb[a], ins[b], inb[b]))
+                return GM_ERR_ALIAS;
         for (int b = a + 1; b < 5; ++b)
-            if (overlaps(outs[a], outb[a], outs[b], outb[b])) return GM_ERR_ALIAS;
+            if (outb[a] && outb[b] && overlaps(outs[a], outb[a], outs[b], outb[b]))
+                return GM_ERR_ALIAS;
     }
+    return GM_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+gm_status gm_sea_backward(int B, int n, int hq, int hkv, int d, gm_dtype dt, float scale,
+                          const void* q, const void* k, const void* v, const int32_t* idx,
+                          const float* w, int s1, const void* dout, const float* stats,
+                          float* dq, float* dk, float* dv, float* dw, void* workspace,
+                          size_t workspace_bytes, hipStream_t stream) {
+    gm_status st = check_sea(B, n, hq, hkv, d, dt, s1);
+    if (st != GM_OK) return st;
+    if (empty(B, n, hkv)) return GM_OK;
+    if (!workspace) return GM_ERR_WORKSPACE;
+    if ((st = sea_backward_checks(B, n, hq, hkv, d, dt, q, k, v, idx, w, s1, dout, stats, dq, dk,
+                                  dv, dw, workspace, workspace_bytes)) != GM_OK)
+        return st;
     return hip_status(gm::launch_sea_backward(B, n, hq, hkv, d, dt == GM_BF16, scale, q, k, v,
                                               idx, w, s1, dout, stats, dq, dk, dv, dw,
                                               workspace, stream));
+}
+
+gm_status gm_sea_backward_noalloc(int B, int n, int hq, int hkv, int d, gm_dtype dt, float scale,
+                                  const void* q, const void* k, const void* v,
+                                  const int32_t* idx, const float* w, int s1, const void* dout,
+                                  const float* stats, float* dq, float* dk, float* dv, float* dw,
+                                  hipStream_t stream) {
+    gm_status st = check_sea(B, n, hq, hkv, d, dt, s1);
+    if (st != GM_OK) return st;
+    if (empty(B, n, hkv)) return GM_OK;
+    if ((st = sea_backward_checks(B, n, hq, hkv, d, dt, q, k, v, idx, w, s1, dout, stats, dq, dk,
+                                  dv, dw, nullptr, 0)) != GM_OK)
+        return st;
+    if (gm_sea_backward_workspace_bytes(B, n, hq, hkv, s1) > GM_NOALLOC_SCRATCH_BYTES)
+        return GM_ERR_TOO_LARGE;
+    void* ws = nullptr;
+    if ((st = scratch_address(stream, &ws)) != GM_OK) return st;
+    // the workspace's contents on entry do not matter (the kernels fill
+    // what they read): nothing to clear, and no allocation
+    return hip_status(gm::launch_sea_backward(B, n, hq, hkv, d, dt == GM_BF16, scale, q, k, v,
+                                              idx, w, s1, dout, stats, dq, dk, dv, dw, ws,
+                                              stream));
 }
 
 size_t gm_ser_backward_workspace_bytes(int B, int n, int hkv, int s2, int s3, int aliased) {

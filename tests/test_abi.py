@@ -35,11 +35,11 @@ def test_library_exports_every_declared_call(lib):
     assert set(names) == set(binding.EXPORTS)
     for name in names:
         assert hasattr(lib, name), name
-    assert lib.gm_abi_version() == 5
+    assert lib.gm_abi_version() == 6
 
 
 def test_status_strings(lib):
-    for code in range(8):
+    for code in range(9):
         assert lib.gm_status_string(code)
     assert b"unknown" in lib.gm_status_string(99)
 
@@ -192,3 +192,28 @@ def test_ser_backward_workspace_checks(lib):
     args[15] = ptrs[8]
     args[5] = 2                                # aliased outputs with s2 != s3
     assert lib.gm_ser_backward(*args) == ALIAS
+
+
+def test_sea_backward_noalloc_checks(lib):
+    """The allocation-free backward validates everything on the host first:
+    sizes whose workspace exceeds the fixed scratch are GM_ERR_TOO_LARGE, and
+    bad pointers are reported as for gm_sea_backward, before any GPU call."""
+    a, b, c = fake(0x100000), fake(0x200000), fake(0x300000)
+    i, w = fake(0x400000), fake(0x500000)
+    f = lib.gm_sea_backward_noalloc
+    f.argtypes = [ctypes.c_int] * 6 + [ctypes.c_float] + [P] * 5 + [ctypes.c_int] + [P] * 7
+    TOO_LARGE = 8
+    args = lambda B=8, n=4096, dq=fake(0x800000), dk=fake(0x900000): (  # noqa: E731
+        B, n, 16, 8, 128, 1, 0.1, a, b, c, i, w, 4, fake(0x700000), None,
+        dq, dk, fake(0xA00000), fake(0xB00000), None)
+    need = lib.gm_sea_backward_workspace_bytes(8, 4096, 16, 8, 4)
+    assert need <= 64 << 20                       # the measured layer fits the scratch
+    assert lib.gm_sea_backward_workspace_bytes(32, 4096, 16, 8, 4) > 64 << 20
+    far = [fake(k << 36) for k in range(1, 11)]   # regions that cannot overlap
+    big = (32, 4096, 16, 8, 128, 1, 0.1, *far[:5], 4, far[5], None, *far[6:10], None)
+    assert f(*big) == TOO_LARGE
+    assert f(*args(dq=None)) == NULL
+    assert f(*args(dk=fake(0x900004))) == ALIGN
+    assert f(*args(dq=b)) == ALIAS               # dq on k
+    assert f(*args(B=0)) == OK                   # empty: nothing to do
+    assert b"GM_NOALLOC_SCRATCH_BYTES" in lib.gm_status_string(TOO_LARGE)
