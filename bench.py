@@ -2,7 +2,8 @@
 
 One step = one pass of the whole hot path over one batch of synthetic input:
   gm_ser_forward   A' = Sparsify_4(A A)             (16 two-hop candidates)
-  gm_sea_forward   o = SEA(q, k, v, A'), saving p / w per slot (32 B/unit)
+  gm_sea_forward   o = SEA(q, k, v, A'), saving p / w per slot and a copy of
+                   the unit's edge row (64 B/unit)
   gm_sea_backward  dq, dk, dv, dw' from dout and the saved p / w
   gm_ser_backward  dw (both legs are A, so both contributions land in dw)
 on B=8 sequences of n=4096 tokens, 16 query / 8 KV heads, d=128, bf16
@@ -51,12 +52,14 @@ PEAK_BF16_TFLOPS = 2500.0      # dense bf16 matrix-core peak (no sparsity)
 # Algorithmic (compulsory) bytes per unit: every input byte read once, every
 # output byte written once; K/V counted once per unit (unique rows).
 # G = 2 query heads per KV head, d = 128, bf16 activations, fp32 gradients;
-# the forward's saved p / w (G * s1 fp32) is written once and read once.
+# the forward's saved p / w (G * s1 fp32) is written once and read once, and
+# so is its pair-major copy of the edge row (the backward reads the copy, not
+# the edge tensor).
 BYTES_PER_UNIT = {
     "gm_ser_forward": 32 + 32,                          # A row + A' row
-    "gm_sea_forward": 512 + 32 + 512 + 512 + 32,        # q, A', K+V, o, p / w
+    "gm_sea_forward": 512 + 32 + 512 + 512 + 32 + 32,   # q, A', K+V, o, p / w, A' copy
     "gm_sea_backward": 512 + 512 + 32 + 512 + 32 + 1024 + 16 + 1024,
-    #                  q    dO    A'   KV  p/w   dq   dw'   dK dV
+    #                  q    dO  A'copy KV  p/w   dq   dw'   dK dV
     "gm_ser_backward": 32 + 32 + 16 + 16,               # A, A', dw', dw
 }
 CALLS = list(BYTES_PER_UNIT)
@@ -95,15 +98,16 @@ CONFIG_STAGES = {
 
 def stage_bytes(stage: str, p: synth.Preset) -> int:
     """Compulsory bytes per unit of one stage (edges: 8 bytes per slot; the
-    forward saves p / w, 4 bytes per query head and slot, only when a
-    backward follows)."""
+    forward saves p / w, 4 bytes per query head and slot, and a copy of the
+    edge row, only when a backward follows; the backward reads that copy in
+    place of the edge row)."""
     s1 = p.s1
     G = p.hq // p.hkv
     es = 2 if p.dtype == torch.bfloat16 else 4
     qrow, kv = G * p.d * es, 2 * p.d * es          # a unit's q (or o, dout); its K and V rows
     st = 4 * G * s1 if p.backward else 0
     return {"ser_fwd": 8 * p.s2 + 8 * s1,
-            "sea_fwd": qrow + 8 * s1 + kv + qrow + st,
+            "sea_fwd": qrow + 8 * s1 + kv + qrow + st + (8 * s1 if p.backward else 0),
             "sea_bwd": 2 * qrow + 8 * s1 + kv + st + 4 * G * p.d + 4 * s1 + 8 * p.d,
             "ser_bwd": 8 * p.s2 + 8 * s1 + 4 * s1 + 4 * p.s2}[stage]
 
@@ -175,7 +179,7 @@ class Pass:
         self.wa = torch.empty(es, **f32)
         self.o = torch.empty_like(self.q)
         # p / w per query head and slot, saved by the forward for the backward
-        self.stats = (torch.empty((p.B, p.hkv, p.n, p.hq // p.hkv, p.s1), **f32)
+        self.stats = (torch.empty((p.B, p.hkv, p.n, p.hq // p.hkv + 2, p.s1), **f32)
                       if p.backward else None)
         self.dq = torch.empty(qs, **f32)
         self.dk = torch.empty(ks, **f32)

@@ -133,8 +133,9 @@ def gm_ser_forward(idx1, w1, idx2, w2, idx_out, w_out, stream=None) -> None:
 
 
 def gm_sea_forward(q, k, v, idx, w, o, scale=None, stream=None, stats=None) -> None:
-    """``stats`` (optional, [B, hkv, n, hq // hkv, s1] fp32) receives p / w
-    per query head and slot."""
+    """``stats`` (optional, [B, hkv, n, hq // hkv + 2, s1] fp32) receives p / w
+    per query head and slot, then a copy of the edge indices (int32 bits) and
+    weights, for gm_sea_backward."""
     B, n, hq, d = q.shape
     hkv, s1 = idx.shape[2], idx.shape[3]
     _need(q, "q", _ACT)
@@ -142,7 +143,7 @@ def gm_sea_forward(q, k, v, idx, w, o, scale=None, stream=None, stats=None) -> N
     _need(idx, "idx", (torch.int32,), (B, n, hkv, s1)); _need(w, "w", (torch.float32,), idx.shape)
     _need(o, "o", (q.dtype,), q.shape)
     if stats is not None:
-        _need(stats, "stats", (torch.float32,), (B, hkv, n, hq // hkv, s1))
+        _need(stats, "stats", (torch.float32,), (B, hkv, n, hq // hkv + 2, s1))
     scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
     _call("gm_sea_forward", B, n, hq, hkv, d, _act_dtype(q), scale, _ptr(q), _ptr(k), _ptr(v),
           _ptr(idx), _ptr(w), s1, _ptr(o), _ptr(stats), _stream(stream))
@@ -166,7 +167,7 @@ def gm_sea_backward(q, k, v, idx, w, dout, dq, dk, dv, dw, workspace, scale=None
     _need(dw, "dw", (torch.float32,), idx.shape)
     _need(workspace, "workspace", (torch.uint8, torch.float64))
     if stats is not None:
-        _need(stats, "stats", (torch.float32,), (B, hkv, n, hq // hkv, s1))
+        _need(stats, "stats", (torch.float32,), (B, hkv, n, hq // hkv + 2, s1))
     scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
     _call("gm_sea_backward", B, n, hq, hkv, d, _act_dtype(q), scale, _ptr(q), _ptr(k), _ptr(v),
           _ptr(idx), _ptr(w), s1, _ptr(dout), _ptr(stats), _ptr(dq), _ptr(dk), _ptr(dv),
@@ -188,7 +189,7 @@ def gm_sea_backward_noalloc(q, k, v, idx, w, dout, dq, dk, dv, dw, scale=None, s
     _need(dk, "dk", (torch.float32,), k.shape); _need(dv, "dv", (torch.float32,), v.shape)
     _need(dw, "dw", (torch.float32,), idx.shape)
     if stats is not None:
-        _need(stats, "stats", (torch.float32,), (B, hkv, n, hq // hkv, s1))
+        _need(stats, "stats", (torch.float32,), (B, hkv, n, hq // hkv + 2, s1))
     scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
     _call("gm_sea_backward_noalloc", B, n, hq, hkv, d, _act_dtype(q), scale, _ptr(q), _ptr(k),
           _ptr(v), _ptr(idx), _ptr(w), s1, _ptr(dout), _ptr(stats), _ptr(dq), _ptr(dk),
@@ -307,12 +308,12 @@ def ser_forward(idx1, w1, idx2, w2, s1, stream=None):
 
 
 def sea_forward(q, k, v, idx, w, scale=None, stream=None, save_stats=False):
-    """o, or (o, stats) with ``save_stats`` (stats [B, hkv, n, G, s1]: p / w
-    per query head and slot, for sea_backward)."""
+    """o, or (o, stats) with ``save_stats`` (stats [B, hkv, n, G + 2, s1]:
+    p / w per query head and slot, then the edge row, for sea_backward)."""
     o = torch.empty_like(q)
     B, n, hq, _ = q.shape
     hkv, s1 = idx.shape[2], idx.shape[3]
-    stats = (torch.empty((B, hkv, n, hq // hkv, s1), dtype=torch.float32, device=q.device)
+    stats = (torch.empty((B, hkv, n, hq // hkv + 2, s1), dtype=torch.float32, device=q.device)
              if save_stats else None)
     gm_sea_forward(q, k, v, idx, w, o, scale, stream, stats)
     return (o, stats) if save_stats else o
@@ -362,9 +363,17 @@ def check_edges(idx, w, stream=None):
 
 
 def stats_as_query_heads(stats: torch.Tensor) -> torch.Tensor:
-    """The saved statistics [B, hkv, n, G, s1] viewed as [B, n, hq, s1]."""
-    B, hkv, n, G, s1 = stats.shape
-    return stats.permute(0, 2, 1, 3, 4).reshape(B, n, hkv * G, s1)
+    """The p / w rows of the saved statistics [B, hkv, n, G + 2, s1] as
+    [B, n, hq, s1]."""
+    B, hkv, n, G2, s1 = stats.shape
+    return stats[:, :, :, :G2 - 2].permute(0, 2, 1, 3, 4).reshape(B, n, hkv * (G2 - 2), s1)
+
+
+def stats_edge_copy(stats: torch.Tensor):
+    """The edge copy in the saved statistics as (idx [B, n, hkv, s1] int32,
+    w [B, n, hkv, s1] fp32)."""
+    e = stats[:, :, :, -2:].permute(0, 2, 1, 3, 4)
+    return e[..., 0, :].contiguous().view(torch.int32), e[..., 1, :].contiguous()
 
 
 def decode_step(idx1, w1, idx2, w2, q, k, v, s1, scale=None, stream=None):

@@ -152,7 +152,8 @@ gm_status gm_sea_forward(int B, int n, int hq, int hkv, int d, gm_dtype dt, floa
         return GM_ERR_ALIGN;
     const size_t es = dt == GM_BF16 ? 2 : 4;
     const size_t qb = (size_t)B * n * hq * d * es, kb = (size_t)B * n * hkv * d * es;
-    const size_t eb = (size_t)B * n * hkv * s1 * 4, sb = (size_t)B * n * hq * s1 * 4;
+    const size_t eb = (size_t)B * n * hkv * s1 * 4;
+    const size_t sb = (size_t)B * n * (hq + 2 * hkv) * s1 * 4;   // (G + 2) rows per unit
     if (overlaps(o, qb, q, qb) || overlaps(o, qb, k, kb) || overlaps(o, qb, v, kb) ||
         overlaps(o, qb, idx, eb) || overlaps(o, qb, w, eb))
         return GM_ERR_ALIAS;
@@ -325,7 +326,7 @@ gm_status sea_backward_checks(int B, int n, int hq, int hkv, int d, gm_dtype dt,
     const size_t es = dt == GM_BF16 ? 2 : 4;
     const size_t nq = (size_t)B * n * hq * d, nk = (size_t)B * n * hkv * d;
     const size_t ne = (size_t)B * n * hkv * s1;
-    const size_t ns = (size_t)B * n * hq * s1;
+    const size_t ns = (size_t)B * n * (hq + 2 * hkv) * s1;   // statistics: (G + 2) rows per unit
     const void* ins[7] = {q, k, v, dout, idx, w, stats};
     const size_t inb[7] = {nq * es, nk * es, nk * es, nq * es, ne * 4, ne * 4,
                            stats ? ns * 4 : 0};

@@ -439,7 +439,7 @@ struct SeaBwdFast {
     const char* k;
     const char* v;
     const char* dout;
-    const float* stats;   // [B][hkv][n][G][s] p / w from the forward, or null
+    const float* stats;   // [B][hkv][n][G + 2][s] p / w, idx, w from the forward, or null
     const int32_t* idx;
     const float* w;
     char* dq;
@@ -535,7 +535,26 @@ __global__ __launch_bounds__(kBlock) void sea_bwd_src_row_kernel(SeaBwdFast a) {
     auto fetch = [&](int u) {
         Item it;
         it.pos = pos_of(a.sp, sch.x, u < sch.end ? u : sch.end - 1);
-        if constexpr (VEC) {
+        if constexpr (SAVED) {
+            // the forward's pair-major copy of the edge row: contiguous for
+            // the consecutive tokens of a wavefront, where the interleaved
+            // rows of the eight KV heads would bring whole lines to every XCD
+            const float* e = a.stats + ((size_t)it.pos.prow * (G + 2) + G) * a.s;
+            if constexpr (VEC) {
+                const int4 j4 = *reinterpret_cast<const int4*>(e);
+                const float4 w4 = *reinterpret_cast<const float4*>(e + 4);
+                it.j[0] = j4.x; it.j[1] = j4.y; it.j[2] = j4.z; it.j[3] = j4.w;
+                it.wt[0] = w4.x; it.wt[1] = w4.y; it.wt[2] = w4.z; it.wt[3] = w4.w;
+            } else {
+#pragma unroll
+                for (int t = 0; t < S; ++t) {
+                    const int tt = t < a.s ? t : a.s - 1;
+                    it.j[t] = __float_as_int(e[tt]);
+                    const float wv = e[a.s + tt];
+                    it.wt[t] = t < a.s ? wv : 0.0f;
+                }
+            }
+        } else if constexpr (VEC) {
             const int4 j4 = *reinterpret_cast<const int4*>(a.idx + (size_t)it.pos.unit * 4);
             const float4 w4 = *reinterpret_cast<const float4*>(a.w + (size_t)it.pos.unit * 4);
             it.j[0] = j4.x; it.j[1] = j4.y; it.j[2] = j4.z; it.j[3] = j4.w;
@@ -589,7 +608,7 @@ __global__ __launch_bounds__(kBlock) void sea_bwd_src_row_kernel(SeaBwdFast a) {
 #pragma unroll
             for (int g = 0; g < GC; ++g) {
                 if constexpr (SAVED) {
-                    const float* sp = a.stats + ((size_t)cur.pos.prow * G + g0 + g) * a.s;
+                    const float* sp = a.stats + ((size_t)cur.pos.prow * (G + 2) + g0 + g) * a.s;
                     if constexpr (VEC) {
                         const float4 s4 = *reinterpret_cast<const float4*>(sp);
                         st[g][0] = s4.x; st[g][1] = s4.y; st[g][2] = s4.z; st[g][3] = s4.w;
@@ -727,7 +746,26 @@ __global__ __launch_bounds__(kBlock) void sea_bwd_src_wide_kernel(SeaBwdFast a) 
     auto fetch = [&](int u) {
         Item it;
         it.pos = pos_of(a.sp, sch.x, u < sch.end ? u : sch.end - 1);
-        if constexpr (VEC) {
+        if constexpr (SAVED) {
+            // the forward's pair-major copy of the edge row: contiguous for
+            // the consecutive tokens of a wavefront, where the interleaved
+            // rows of the eight KV heads would bring whole lines to every XCD
+            const float* e = a.stats + ((size_t)it.pos.prow * (G + 2) + G) * a.s;
+            if constexpr (VEC) {
+                const int4 j4 = *reinterpret_cast<const int4*>(e);
+                const float4 w4 = *reinterpret_cast<const float4*>(e + 4);
+                it.j[0] = j4.x; it.j[1] = j4.y; it.j[2] = j4.z; it.j[3] = j4.w;
+                it.wt[0] = w4.x; it.wt[1] = w4.y; it.wt[2] = w4.z; it.wt[3] = w4.w;
+            } else {
+#pragma unroll
+                for (int t = 0; t < S; ++t) {
+                    const int tt = t < a.s ? t : a.s - 1;
+                    it.j[t] = __float_as_int(e[tt]);
+                    const float wv = e[a.s + tt];
+                    it.wt[t] = t < a.s ? wv : 0.0f;
+                }
+            }
+        } else if constexpr (VEC) {
             const int4 j4 = *reinterpret_cast<const int4*>(a.idx + (size_t)it.pos.unit * 4);
             const float4 w4 = *reinterpret_cast<const float4*>(a.w + (size_t)it.pos.unit * 4);
             it.j[0] = j4.x; it.j[1] = j4.y; it.j[2] = j4.z; it.j[3] = j4.w;
@@ -791,7 +829,7 @@ __global__ __launch_bounds__(kBlock) void sea_bwd_src_wide_kernel(SeaBwdFast a) 
 #pragma unroll
             for (int g = 0; g < GC; ++g) {
                 if constexpr (SAVED) {
-                    const float* sp = a.stats + ((size_t)cur.pos.prow * G + g0 + g) * a.s;
+                    const float* sp = a.stats + ((size_t)cur.pos.prow * (G + 2) + g0 + g) * a.s;
                     if constexpr (VEC) {
                         const float4 s4 = *reinterpret_cast<const float4*>(sp);
                         st[g][0] = s4.x; st[g][1] = s4.y; st[g][2] = s4.z; st[g][3] = s4.w;

@@ -37,6 +37,16 @@ TeamShape sea_team(int d, int elem_bytes, int s) {
 
 namespace {
 
+// The saved statistics of a unit (pair-major row `prow`) are (G + 2) rows
+// of s floats: p / w per query head, then the unit's edge indices (int32
+// bits) and weights, a pair-major copy of its edge row for the backward.
+__device__ __forceinline__ void store_edge_copy(float* stats, size_t prow, int G, int s, int t,
+                                                int j, float wt) {
+    float* e = stats + (prow * (G + 2) + G) * s;
+    e[t] = __int_as_float(j);
+    e[s + t] = wt;
+}
+
 struct SeaFwdArgs {
     const void* q;
     const void* k;
@@ -44,7 +54,7 @@ struct SeaFwdArgs {
     const int32_t* idx;
     const float* w;
     void* o;
-    float* stats;   // [B][hkv][n][G][s] p / w per live slot (0 dead), or null
+    float* stats;   // [B][hkv][n][G + 2][s]: p / w per live slot (0 dead), idx, w; or null
     int n, hq, hkv, d, s, U;
     float scale;
     TeamShape ts;
@@ -118,12 +128,13 @@ __global__ __launch_bounds__(kBlock) void sea_fwd_kernel(SeaFwdArgs a) {
             const int off = reduce_scatter(ov, tl, R, team, len);
             const A inv = Z > 0 ? (A)1 / Z : (A)0;
             if (a.stats && r == 0 && t < a.s)
-                a.stats[(srow * G + g) * a.s + t] =
+                a.stats[(srow * (G + 2) + g) * a.s + t] =
                     live ? (float)(aexp2(dot * c - M) * inv) : 0.0f;
 #pragma unroll
             for (int e = 0; e < V; ++e) ov[e] *= inv;
             if (storer) store_len(op + g * d + off, ov, len);
         }
+        if (a.stats && r == 0 && t < a.s) store_edge_copy(a.stats, srow, G, a.s, t, ip[t], wp[t]);
         return;
     }
 
@@ -192,9 +203,11 @@ __global__ __launch_bounds__(kBlock) void sea_fwd_kernel(SeaFwdArgs a) {
 #pragma unroll
                 for (int e = 0; e < V; ++e) dot += qg[e] * kr[e];
                 dot = sum_bits(dot, 1, R);
-                if (r == 0 && t < a.s)
-                    a.stats[(srow * G + g) * a.s + t] =
+                if (r == 0 && t < a.s) {
+                    a.stats[(srow * (G + 2) + g) * a.s + t] =
                         live ? (float)(aexp2(dot * c - M) * inv) : 0.0f;
+                    if (g == 0) store_edge_copy(a.stats, srow, G, a.s, t, ip[t], wp[t]);
+                }
             }
         }
     }
@@ -213,7 +226,7 @@ struct SeaFwdFast {
     const int32_t* idx;
     const float* w;
     char* o;
-    float* stats;   // [B][hkv][n][G][s] p / w per live slot (0 dead), or null
+    float* stats;   // [B][hkv][n][G + 2][s]: p / w per live slot (0 dead), idx, w; or null
     int n, hq, hkv, s, U;
     float scale;
     SegPlan sp;
@@ -342,8 +355,35 @@ __global__ __launch_bounds__(kBlock) void sea_fwd_row_kernel(SeaFwdFast a) {
         A lw[S];
 #pragma unroll
         for (int t = 0; t < S; ++t) lw[t] = live[t] ? fast_log2((A)cur.wt[t]) : NEG;
-        const bool st_one = G * a.s <= 16;   // the unit's statistics in one store
+        // the unit's statistics, p / w per head and slot, then its edge
+        // indices and weights, in one store per lane when they fit 16 lanes
+        const bool st_one = (G + 2) * a.s <= 16;
         float st_val = 0.0f;
+        if (a.stats) {
+            // lanes G s .. (G + 2) s - 1: the edge copy (index bits, then weight)
+            const int te = r - G * a.s;
+            float ev = 0.0f;
+#pragma unroll
+            for (int t = 0; t < S; ++t) {
+                if (t < a.s) {
+                    ev = te == t ? __int_as_float(cur.j[t]) : ev;
+                    ev = te == a.s + t ? cur.wt[t] : ev;
+                }
+            }
+            if (st_one) {
+                st_val = ev;
+            } else if (r < a.s) {
+                float* e = a.stats + ((size_t)cur.pos.prow * (G + 2) + G) * a.s;
+                float jv = 0.0f, wv = 0.0f;
+#pragma unroll
+                for (int t = 0; t < S; ++t) {
+                    jv = r == t ? __int_as_float(cur.j[t]) : jv;
+                    wv = r == t ? cur.wt[t] : wv;
+                }
+                __builtin_nontemporal_store(jv, e + r);
+                __builtin_nontemporal_store(wv, e + a.s + r);
+            }
+        }
 #pragma unroll
         for (int g0 = 0; g0 < G; g0 += GC) {
             uint4 qr[GC][NP];
@@ -388,7 +428,8 @@ __global__ __launch_bounds__(kBlock) void sea_fwd_row_kernel(SeaFwdFast a) {
                     if (t0 >= 0 && t0 < a.s) st_val = ml ? (float)(fast_exp2(mine - M) * inv) : 0.0f;
                     if (!st_one && t0 >= 0 && t0 < a.s)
                         __builtin_nontemporal_store(
-                            st_val, a.stats + ((size_t)cur.pos.prow * G + g0 + g) * a.s + t0);
+                            st_val,
+                            a.stats + ((size_t)cur.pos.prow * (G + 2) + g0 + g) * a.s + t0);
                 }
 #pragma unroll
                 for (int k = 0; k < NP; ++k) {
@@ -420,8 +461,9 @@ __global__ __launch_bounds__(kBlock) void sea_fwd_row_kernel(SeaFwdFast a) {
                 }
             }
         }
-        if (a.stats && st_one && r < G * a.s)
-            __builtin_nontemporal_store(st_val, a.stats + (size_t)cur.pos.prow * G * a.s + r);
+        if (a.stats && st_one && r < (G + 2) * a.s)
+            __builtin_nontemporal_store(st_val,
+                                        a.stats + (size_t)cur.pos.prow * (G + 2) * a.s + r);
         cur = nxt;
     }
 }

@@ -94,6 +94,8 @@ def test_sea_forward_backward_shapes(dtype, d, G, s, n):
             hs = host(gm.stats_as_query_heads(st))
             assert (hs[~live] == 0).all()
             assert_close("p (statistics * w)", hs * np.repeat(w, G, axis=2), rp, 1e-4)
+            ei, ew = gm.stats_edge_copy(st)      # the backward's copy of the edge rows
+            assert np.array_equal(host(ei), idx) and np.array_equal(host(ew), w)
         assert_close("dq", host(dq), rdq, X)
         assert_close("dk", host(dk), rdk, X)
         assert_close("dv", host(dv), rdv, X)
