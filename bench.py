@@ -62,16 +62,24 @@ BYTES_PER_UNIT = {
     #                  q    dO  A'copy KV  p/w   dq   dw'   dK dV
     "gm_ser_backward": 32 + 32 + 16 + 16,               # A, A', dw', dw
 }
-CALLS = list(BYTES_PER_UNIT)
+# with the fused forward (gm_ser_sea_forward): the SER row in, A' and the
+# SEA forward's outputs out, no A' read in between
+BYTES_PER_UNIT["gm_ser_sea_forward"] = (BYTES_PER_UNIT["gm_ser_forward"] +
+                                        BYTES_PER_UNIT["gm_sea_forward"] - 32)
+SEPARATE_CALLS = ["gm_ser_forward", "gm_sea_forward", "gm_sea_backward", "gm_ser_backward"]
+FUSED_CALLS = ["gm_ser_sea_forward", "gm_sea_backward", "gm_ser_backward"]
+CALLS = SEPARATE_CALLS
 # The same model without the forward's saved p / w (the pages' path: 5,360
 # bytes per unit for the pass, 3,632 for the SEA backward), printed beside
 # the line's own figures.
 SURVEY_BYTES_PER_UNIT = {"gm_ser_forward": 64, "gm_sea_forward": 1568,
                          "gm_sea_backward": 3632, "gm_ser_backward": 96}
 SURVEY_PASS_BYTES_PER_UNIT = sum(SURVEY_BYTES_PER_UNIT.values())
+SURVEY_BYTES_PER_UNIT["gm_ser_sea_forward"] = 64 + 1568 - 32
 # kernels each call launches on this workload (base names as the profiler
 # reports them, template arguments dropped)
 CALL_KERNELS = {
+    "gm_ser_sea_forward": ["ser_sea_fwd_row_kernel"],
     "gm_ser_forward": ["ser_fwd_vec_kernel"],
     "gm_sea_forward": ["sea_fwd_row_kernel"],
     "gm_sea_backward": ["sea_bwd_src_row_kernel", "edge_index_one_kernel",
@@ -153,6 +161,9 @@ def parse():
                     help="time warm passes only (no flush between passes) and skip the graph "
                          "replay: for profiler runs of the eager pass")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--fused", action="store_true",
+                    help="run SER and SEA forward as the one fused call gm_ser_sea_forward "
+                         "(measured slower than the two calls on this workload)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="instead of the pass, run a plain device copy of MIB MiB "
                          "(the known-size reference for hardware byte counters)")
@@ -215,7 +226,15 @@ class Pass:
                 out.append(("gm_ser_backward", self.calls()[3]))
         return out
 
-    def calls(self):
+    def calls(self, fused=False):
+        """The step's calls in order, named as in CALLS (FUSED_CALLS with the
+        fused forward)."""
+        if fused:
+            return [
+                lambda: gm.gm_ser_sea_forward(self.idx, self.w, self.idx, self.w, self.q,
+                                              self.k, self.v, self.ia, self.wa, self.o,
+                                              stats=self.stats),
+            ] + self.calls()[2:]
         return [
             lambda: gm.gm_ser_forward(self.idx, self.w, self.idx, self.w, self.ia, self.wa),
             lambda: gm.gm_sea_forward(self.q, self.k, self.v, self.ia, self.wa, self.o,
@@ -228,14 +247,15 @@ class Pass:
         ]
 
 
-def time_steps(ps: Pass, steps: int, warmup: int, flush_mib: int = 0):
+def time_steps(ps: Pass, steps: int, warmup: int, flush_mib: int = 0, fused: bool = False):
     """Per-step and per-call times (ms, HIP events on the launch stream) of
     `steps` passes after `warmup` untimed ones.  With `flush_mib` > 0 a
     scratch buffer of that many MiB is written before every pass (evicting
     the 4 MB L2s and the 256 MB MALL: a cold pass); only the pass itself lies
     between its events.  The device is synchronised before and after the
     timed steps; returns (per-step ms, {call: per-step ms}, wall seconds)."""
-    calls = ps.calls()
+    calls = ps.calls(fused)
+    names = FUSED_CALLS if fused else SEPARATE_CALLS
     scratch = (torch.empty(flush_mib * (1 << 20) // 4, dtype=torch.float32, device="cuda")
                if flush_mib else None)
     for w in range(warmup):
@@ -258,7 +278,7 @@ def time_steps(ps: Pass, steps: int, warmup: int, flush_mib: int = 0):
     wall = time.perf_counter() - t0
     per_step = [ev[s_][0].elapsed_time(ev[s_][-1]) for s_ in range(steps)]
     per_call = {name: [ev[s_][i].elapsed_time(ev[s_][i + 1]) for s_ in range(steps)]
-                for i, name in enumerate(CALLS)}
+                for i, name in enumerate(names)}
     del scratch
     return per_step, per_call, wall
 
@@ -270,10 +290,10 @@ def stats_ms(xs):
             "p90": float(np.percentile(a, 90)), "mean": float(a.mean())}
 
 
-def time_graph(ps: Pass, steps: int):
-    """Mean time of one pass replayed from a HIP graph that captured the four
-    calls (HIP events around `steps` back-to-back replays)."""
-    calls = ps.calls()
+def time_graph(ps: Pass, steps: int, fused: bool = False):
+    """Mean time of one pass replayed from a HIP graph that captured the
+    step's calls (HIP events around `steps` back-to-back replays)."""
+    calls = ps.calls(fused)
     side = torch.cuda.Stream()
     side.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(side):
@@ -640,17 +660,19 @@ def main():
     U = p.units
     # headline: cold passes (a 512 MiB write before each evicts L2s and MALL),
     # median over the timed steps; warm (back-to-back) passes beside it
+    fused = a.fused
+    calls_used = FUSED_CALLS if fused else SEPARATE_CALLS
     cold_steps, cold_calls, wall = time_steps(ps, a.steps, a.warmup,
-                                              flush_mib=0 if a.no_cold else 512)
-    warm_steps, warm_calls, _ = time_steps(ps, a.steps, a.warmup)
+                                              flush_mib=0 if a.no_cold else 512, fused=fused)
+    warm_steps, warm_calls, _ = time_steps(ps, a.steps, a.warmup, fused=fused)
     cold, warm = stats_ms(cold_steps), stats_ms(warm_steps)
     ms = cold["median"]
     per_call = {c: stats_ms(v)["median"] for c, v in cold_calls.items()}
-    graph_ms = None if a.no_cold else time_graph(ps, a.steps)
-    pass_bytes = sum(BYTES_PER_UNIT.values()) * U
+    graph_ms = None if a.no_cold else time_graph(ps, a.steps, fused=fused)
+    pass_bytes = sum(BYTES_PER_UNIT[c] for c in calls_used) * U
     survey_pass_bytes = SURVEY_PASS_BYTES_PER_UNIT * U
     dom = max(per_call, key=per_call.get)
-    traffic = {c: profiled_traffic(c) for c in CALLS}
+    traffic = {c: profiled_traffic(c) for c in calls_used}
     counter_bytes = (sum(traffic.values()) if all(v is not None for v in traffic.values())
                      else None)
     dom_gbs = BYTES_PER_UNIT[dom] * U / (per_call[dom] * 1e-3) / 1e9
@@ -672,6 +694,7 @@ def main():
                    "B": p.B, "n": p.n, "hq": p.hq, "hkv": p.hkv, "d": p.d,
                    "s1": p.s1, "s2": p.s2, "s3": p.s3, "units_per_step": U,
                    "parallelism": "single GPU"},
+        "calls": calls_used,
         "timing": ("cold" if not a.no_cold else "warm") +
                   ": median over the timed steps of HIP events around each pass"
                   + (" (512 MiB written before each pass, outside its events)"

@@ -99,13 +99,15 @@ gm_status gm_ser_forward(int B, int n, int hkv,
  *        idx, w [B][n][hkv][s1]
  *        scale: multiplies q.k (normally 1/sqrt(d))
  *   out  o [B][n][hq][d] dtype dt
- *        stats [B][hkv][n][hq/hkv][s1] fp32 (KV-head-major, so that each
- *        pass writes and reads it in contiguous rows), optional (NULL: not
- *        written; else 16-byte aligned, overlapping nothing): for query
- *        head hkv_index*G + g, p_t / w_t of every live slot, i.e.
- *        exp(scale*q.k[idx_t]) / sum_u w_u exp(scale*q.k[idx_u]), and 0 for
- *        a dead slot.  gm_sea_backward takes it to skip the softmax
- *        recomputation (and the q reads it needs).
+ *        stats [B][hkv][n][hq/hkv + 2][s1] fp32 (KV-head-major, so that
+ *        each pass writes and reads it in contiguous rows), optional (NULL:
+ *        not written; else 16-byte aligned, overlapping nothing): rows
+ *        g < G = hq/hkv hold, for query head hkv_index*G + g, p_t / w_t of
+ *        every live slot, i.e. exp(scale*q.k[idx_t]) / sum_u w_u
+ *        exp(scale*q.k[idx_u]), and 0 for a dead slot; row G holds idx (the
+ *        int32 bits) and row G + 1 w, a copy of the unit's edge row.
+ *        gm_sea_backward takes it to skip the softmax recomputation (and
+ *        the q reads it needs) and reads its edges from the copy.
  * o[hq] = sum_t p_t v[idx_t], p = softmax over live slots (w_t > 0) of
  * scale*q.k[idx_t] + ln w_t; a unit with no live slot gets o = 0.
  * Arithmetic is fp32 for bf16 inputs and fp64 for fp32 inputs.
@@ -114,6 +116,24 @@ gm_status gm_sea_forward(int B, int n, int hq, int hkv, int d, gm_dtype dt,
                          float scale, const void* q, const void* k, const void* v,
                          const int32_t* idx, const float* w, int s1, void* o,
                          float* stats, hipStream_t stream);
+
+/*
+ * gm_ser_forward then gm_sea_forward on its output, in one call: A' =
+ * Sparsify_s1(A1 A2) is written to idx_out / w_out as gm_ser_forward writes
+ * it (bitwise), and o (and, when given, stats) as gm_sea_forward writes them
+ * for that A' (ai.info Key Contributions 3: referral then attention in a
+ * sparse layer).  For bf16, d = 128, s1 = s2 = s3 = 4, 16-byte aligned edge
+ * rows and hq / hkv in {1, 2, 4, 8, 16} the two stages run as one kernel
+ * (A' stays in registers between them); other shapes run the two stages one
+ * after the other.  Arguments, limits and errors as the two calls; no output
+ * may overlap an input or another output.
+ */
+gm_status gm_ser_sea_forward(int B, int n, int hq, int hkv, int d, gm_dtype dt, float scale,
+                             const int32_t* idx1, const float* w1, int s2,
+                             const int32_t* idx2, const float* w2, int s3, int s1,
+                             const void* q, const void* k, const void* v,
+                             int32_t* idx_out, float* w_out, void* o, float* stats,
+                             hipStream_t stream);
 
 /*
  * Bytes of device workspace gm_sea_backward needs for these sizes: per-edge

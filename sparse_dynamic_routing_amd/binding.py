@@ -25,7 +25,7 @@ STATUS = {0: "GM_OK", 1: "GM_ERR_NULL", 2: "GM_ERR_SHAPE", 3: "GM_ERR_UNSUPPORTE
           4: "GM_ERR_WORKSPACE", 5: "GM_ERR_HIP", 6: "GM_ERR_ALIGN", 7: "GM_ERR_ALIAS",
           8: "GM_ERR_TOO_LARGE"}
 EXPORTS = ("gm_ser_forward", "gm_sea_forward", "gm_sea_backward_workspace_bytes",
-           "gm_sea_backward", "gm_sea_backward_noalloc", "gm_decode_step", "gm_dense_refresh", "gm_leg_mix_forward",
+           "gm_sea_backward", "gm_sea_backward_noalloc", "gm_ser_sea_forward", "gm_decode_step", "gm_dense_refresh", "gm_leg_mix_forward",
            "gm_leg_mix_backward_workspace_bytes", "gm_leg_mix_backward",
            "gm_ser_backward_workspace_bytes", "gm_ser_backward", "gm_check_edges",
            "gm_status_string", "gm_abi_version")
@@ -57,6 +57,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
                             _P, _P, _P, _P, _P, _Z, _P],
         "gm_sea_backward_noalloc": [_I, _I, _I, _I, _I, _I, _F, _P, _P, _P, _P, _P, _I, _P,
                                     _P, _P, _P, _P, _P, _P],
+        "gm_ser_sea_forward": [_I, _I, _I, _I, _I, _I, _F, _P, _P, _I, _P, _P, _I, _I, _P, _P,
+                               _P, _P, _P, _P, _P, _P],
         "gm_decode_step": [_I, _I, _I, _I, _I, _I, _F, _P, _P, _I, _P, _P, _I, _I, _P, _P,
                            _P, _P, _P, _P, _P],
         "gm_dense_refresh": [_I, _I, _I, _I, _I, _I, _F, _P, _P, _I, _I, _P, _P, _P, _P],
@@ -147,6 +149,28 @@ def gm_sea_forward(q, k, v, idx, w, o, scale=None, stream=None, stats=None) -> N
     scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
     _call("gm_sea_forward", B, n, hq, hkv, d, _act_dtype(q), scale, _ptr(q), _ptr(k), _ptr(v),
           _ptr(idx), _ptr(w), s1, _ptr(o), _ptr(stats), _stream(stream))
+
+
+def gm_ser_sea_forward(idx1, w1, idx2, w2, q, k, v, idx_out, w_out, o, scale=None, stream=None,
+                       stats=None) -> None:
+    """SER (A' into idx_out / w_out) then SEA (o, and stats when given) in
+    one call."""
+    B, n, hkv, s2 = idx1.shape
+    s3, s1 = idx2.shape[3], idx_out.shape[3]
+    hq, d = q.shape[2], q.shape[3]
+    _need(idx1, "idx1", (torch.int32,)); _need(w1, "w1", (torch.float32,), idx1.shape)
+    _need(idx2, "idx2", (torch.int32,), (B, n, hkv, s3)); _need(w2, "w2", (torch.float32,), idx2.shape)
+    _need(idx_out, "idx_out", (torch.int32,), (B, n, hkv, s1))
+    _need(w_out, "w_out", (torch.float32,), idx_out.shape)
+    _need(q, "q", _ACT, (B, n, hq, d))
+    _need(k, "k", (q.dtype,), (B, n, hkv, d)); _need(v, "v", (q.dtype,), (B, n, hkv, d))
+    _need(o, "o", (q.dtype,), q.shape)
+    if stats is not None:
+        _need(stats, "stats", (torch.float32,), (B, hkv, n, hq // hkv + 2, s1))
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    _call("gm_ser_sea_forward", B, n, hq, hkv, d, _act_dtype(q), scale, _ptr(idx1), _ptr(w1), s2,
+          _ptr(idx2), _ptr(w2), s3, s1, _ptr(q), _ptr(k), _ptr(v), _ptr(idx_out), _ptr(w_out),
+          _ptr(o), _ptr(stats), _stream(stream))
 
 
 def gm_sea_backward_workspace_bytes(B, n, hq, hkv, s1) -> int:
@@ -317,6 +341,19 @@ def sea_forward(q, k, v, idx, w, scale=None, stream=None, save_stats=False):
              if save_stats else None)
     gm_sea_forward(q, k, v, idx, w, o, scale, stream, stats)
     return (o, stats) if save_stats else o
+
+
+def ser_sea_forward(idx1, w1, idx2, w2, s1, q, k, v, scale=None, stream=None, save_stats=False):
+    """(idx_out, w_out, o[, stats]) of SER then SEA in one call."""
+    B, n, hkv, _ = idx1.shape
+    hq = q.shape[2]
+    io = torch.empty((B, n, hkv, s1), dtype=torch.int32, device=idx1.device)
+    wo = torch.empty((B, n, hkv, s1), dtype=torch.float32, device=idx1.device)
+    o = torch.empty_like(q)
+    stats = (torch.empty((B, hkv, n, hq // hkv + 2, s1), dtype=torch.float32, device=q.device)
+             if save_stats else None)
+    gm_ser_sea_forward(idx1, w1, idx2, w2, q, k, v, io, wo, o, scale, stream, stats)
+    return (io, wo, o, stats) if save_stats else (io, wo, o)
 
 
 def sea_workspace(q, idx, device=None) -> torch.Tensor:

@@ -165,6 +165,42 @@ gm_status gm_sea_forward(int B, int n, int hq, int hkv, int d, gm_dtype dt, floa
                                              idx, w, s1, o, stats, stream));
 }
 
+gm_status gm_ser_sea_forward(int B, int n, int hq, int hkv, int d, gm_dtype dt, float scale,
+                             const int32_t* idx1, const float* w1, int s2, const int32_t* idx2,
+                             const float* w2, int s3, int s1, const void* q, const void* k,
+                             const void* v, int32_t* idx_out, float* w_out, void* o,
+                             float* stats, hipStream_t stream) {
+    gm_status st = check_ser(B, n, hkv, s1, s2, s3);
+    if (st != GM_OK) return st;
+    if ((st = check_sea(B, n, hq, hkv, d, dt, s1)) != GM_OK) return st;
+    if (empty(B, n, hkv)) return GM_OK;
+    if ((st = check_edge_ptrs(idx1, w1)) != GM_OK) return st;
+    if ((st = check_edge_ptrs(idx2, w2)) != GM_OK) return st;
+    if ((st = check_edge_ptrs(idx_out, w_out)) != GM_OK) return st;
+    if (!q || !k || !v || !o) return GM_ERR_NULL;
+    if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) ||
+        (stats && !aligned(stats, 16)))
+        return GM_ERR_ALIGN;
+    const size_t es = dt == GM_BF16 ? 2 : 4;
+    const size_t rows = (size_t)B * n * hkv;
+    const size_t qb = (size_t)B * n * hq * d * es, kb = (size_t)B * n * hkv * d * es;
+    const size_t sb = (size_t)B * n * (hq + 2 * hkv) * s1 * 4;
+    const void* ins[7] = {idx1, w1, idx2, w2, q, k, v};
+    const size_t inb[7] = {rows * s2 * 4, rows * s2 * 4, rows * s3 * 4, rows * s3 * 4, qb, kb, kb};
+    const void* outs[4] = {idx_out, w_out, o, stats};
+    const size_t outb[4] = {rows * s1 * 4, rows * s1 * 4, qb, stats ? sb : 0};
+    for (int a = 0; a < 4; ++a) {
+        if (!outb[a]) continue;
+        for (int b = 0; b < 7; ++b)
+            if (overlaps(outs[a], outb[a], ins[b], inb[b])) return GM_ERR_ALIAS;
+        for (int b = a + 1; b < 4; ++b)
+            if (outb[b] && overlaps(outs[a], outb[a], outs[b], outb[b])) return GM_ERR_ALIAS;
+    }
+    return hip_status(gm::launch_ser_sea_forward(B, n, hq, hkv, d, dt == GM_BF16, scale, idx1, w1,
+                                                 s2, idx2, w2, s3, s1, q, k, v, idx_out, w_out,
+                                                 o, stats, stream));
+}
+
 gm_status gm_leg_mix_forward(int B, int n, int hkv, const int32_t* idx, const float* w, int K,
                              const float* alpha, int s, int32_t* idx_out, float* w_out,
                              hipStream_t stream) {

@@ -34,6 +34,19 @@ hipError_t launch_sea_forward(int B, int n, int hq, int hkv, int d, bool bf16, f
                               const int32_t* idx, const float* w, int s, void* o,
                               float* stats, hipStream_t st);
 
+// SER then SEA forward in one call: one fused kernel where
+// ser_sea_fused_shape holds (bf16, d = 128, s1 = s2 = s3 = 4, 16-byte aligned
+// edge rows, a row-kernel group size), else the two launches in sequence.
+bool ser_sea_fused_shape(int B, int n, int hq, int hkv, int d, bool bf16, int s1, int s2, int s3,
+                         const void* idx1, const void* w1, const void* idx2, const void* w2,
+                         const void* idx_out, const void* w_out);
+hipError_t launch_ser_sea_forward(int B, int n, int hq, int hkv, int d, bool bf16, float scale,
+                                  const int32_t* idx1, const float* w1, int s2,
+                                  const int32_t* idx2, const float* w2, int s3, int s1,
+                                  const void* q, const void* k, const void* v,
+                                  int32_t* idx_out, float* w_out, void* o, float* stats,
+                                  hipStream_t st);
+
 // Leg construction (stored edges mixed into a leg), forward and backward.
 size_t leg_mix_backward_workspace_bytes(int B, int n, int hkv, int K);
 hipError_t launch_leg_mix_forward(int B, int n, int hkv, const int32_t* idx, const float* w,

@@ -18,6 +18,7 @@
 // few FLOPs per byte (HBM-bound).
 #include "gm_common.h"
 #include "gm_internal.h"
+#include "gm_select.h"
 #include "gm_wave.h"
 
 #include <math.h>
@@ -496,6 +497,208 @@ hipError_t fast_g(const SeaFwdFast& a, int G, hipStream_t st) {
     }
 }
 
+
+// ------------------------------------------------- fused SER -> SEA forward
+// A' = Sparsify_4(A1 A2) and o = SEA(q, k, v, A') in one pass, for bf16,
+// d = 128, s1 = s2 = s3 = 4 (the measured layer): one unit per 16-lane row
+// as in sea_fwd_row_kernel, and lane k of the row holds the unit's two-hop
+// candidate k = 4a + c (leg-1 slot a, leg-2 slot c).  The row merges and
+// ranks its 16 candidates with the team code of gm_select.h (DPP row
+// rotations; fp64 sums in path order, so A' is bitwise what gm_ser_forward
+// writes), writes A', and goes on with the kept slots exactly as the SEA
+// row kernel.  The unit's leg-1 row is read two units ahead and its leg-2
+// rows one unit ahead, so the three dependent loads of a unit (leg 1, leg 2,
+// K/V) overlap other units' work; A' never goes through memory between the
+// two stages.
+struct SerSeaFwd {
+    SeaFwdFast f;          // SEA part; f.idx / f.w unused (A' is in registers)
+    const int32_t* idx1;
+    const float* w1;
+    const int32_t* idx2;
+    const float* w2;
+    int32_t* idx_out;
+    float* w_out;
+};
+
+template <int G>
+__global__ __launch_bounds__(kBlock) void ser_sea_fwd_row_kernel(SerSeaFwd a) {
+    using A = float;
+    constexpr int V = 8, S = 4;
+    constexpr int ROW = 256;
+    constexpr int GC = G < 4 ? G : 4;     // query rows held at once
+    const int r = threadIdx.x & 15;       // d-row piece, and candidate k = 4 aa + cc
+    const int aa = r >> 2, cc = r & 3;
+    const int rbase = threadIdx.x & (kWave - 1) & ~15;   // first lane of this 16-lane row
+    const A c = (A)a.f.scale * (A)1.4426950408889634;
+    const A NEG = -INFINITY;
+    const int hkv = a.f.hkv;
+    const Sched sc = xcd_sched(a.f.sp, 16);
+    if (sc.q >= sc.end) return;
+
+    struct Leg1 {
+        UnitPos pos;
+        int j;       // leg-1 slot aa: target token
+        float x;     // and weight
+    };
+    struct Leg2 {
+        UnitPos pos;
+        int m;       // candidate aa, cc: target token
+        double cw;   // path weight (exact fp32 x fp32 product)
+    };
+    // past the end the last item is read again (a valid address), never used
+    auto fetch1 = [&](int u) {
+        Leg1 l;
+        l.pos = unit_pos(a.f.sp, sc.x, u < sc.end ? u : sc.end - 1);
+        l.j = a.idx1[(size_t)l.pos.unit * S + aa];
+        l.x = a.w1[(size_t)l.pos.unit * S + aa];
+        return l;
+    };
+    auto fetch2 = [&](const Leg1& l) {
+        Leg2 t;
+        t.pos = l.pos;
+        const int u2 = l.pos.kvrow0 + l.j * hkv;   // unit (b, j, h)
+        t.m = a.idx2[(size_t)u2 * S + cc];
+        const float y = a.w2[(size_t)u2 * S + cc];
+        t.cw = (double)l.x * (double)y;
+        return t;
+    };
+
+    Leg1 l1 = fetch1(sc.q + sc.step);
+    Leg2 cur = fetch2(fetch1(sc.q));
+    for (int u = sc.q; u < sc.end; u += sc.step) {
+        const Leg1 l2 = fetch1(u + 2 * sc.step);
+        const Leg2 nxt = fetch2(l1);
+        // SER: merge and rank the row's 16 candidates
+        float key;
+        bool cand;
+        int rank;
+        team16_merge_rank(r, cur.m, cur.cw, true, key, cand, rank);
+        const bool kept = cand && rank < S;
+        int jt[S];
+        float wt[S];
+#pragma unroll
+        for (int t = 0; t < S; ++t) {
+            const uint64_t mk = __ballot(kept && rank == t);
+            const uint32_t seg = (uint32_t)(mk >> rbase) & 0xFFFFu;
+            const int src = rbase + (seg ? __ffs(seg) - 1 : 0);
+            const int mt = __shfl(cur.m, src, kWave);
+            const float kt = __shfl(key, src, kWave);
+            jt[t] = seg ? mt : 0;
+            wt[t] = seg ? kt : 0.0f;
+        }
+        if (r == 0)
+            *reinterpret_cast<int4*>(a.idx_out + (size_t)cur.pos.unit * S) =
+                make_int4(jt[0], jt[1], jt[2], jt[3]);
+        if (r == 1)
+            *reinterpret_cast<float4*>(a.w_out + (size_t)cur.pos.unit * S) =
+                make_float4(wt[0], wt[1], wt[2], wt[3]);
+
+        // SEA on the kept slots (as sea_fwd_row_kernel, 256-byte rows)
+        bool live[S];
+        uint4 kr[S], vr[S];
+#pragma unroll
+        for (int t = 0; t < S; ++t) {
+            live[t] = wt[t] > 0.0f;
+            const uint32_t off =
+                (uint32_t)(cur.pos.kvrow0 + (live[t] ? jt[t] : 0) * hkv) * ROW + r * 16;
+            kr[t] = *reinterpret_cast<const uint4*>(a.f.k + off);
+            vr[t] = *reinterpret_cast<const uint4*>(a.f.v + off);
+        }
+        const uint32_t qoff =
+            (uint32_t)(cur.pos.bi * a.f.hq + (cur.pos.unit - cur.pos.bi * hkv) * G) * ROW + r * 16;
+        A lw[S];
+#pragma unroll
+        for (int t = 0; t < S; ++t) lw[t] = live[t] ? fast_log2((A)wt[t]) : NEG;
+        constexpr bool st_one = (G + 2) * S <= 16;
+        float st_val = 0.0f;
+        if (a.f.stats) {
+            const int te = r - G * S;
+            float ev = 0.0f;
+#pragma unroll
+            for (int t = 0; t < S; ++t) {
+                ev = te == t ? __int_as_float(jt[t]) : ev;
+                ev = te == S + t ? wt[t] : ev;
+            }
+            if constexpr (st_one) {
+                st_val = ev;
+            } else if (r < S) {
+                float* e = a.f.stats + ((size_t)cur.pos.prow * (G + 2) + G) * S;
+                float jv = 0.0f, wv = 0.0f;
+#pragma unroll
+                for (int t = 0; t < S; ++t) {
+                    jv = r == t ? __int_as_float(jt[t]) : jv;
+                    wv = r == t ? wt[t] : wv;
+                }
+                __builtin_nontemporal_store(jv, e + r);
+                __builtin_nontemporal_store(wv, e + S + r);
+            }
+        }
+#pragma unroll
+        for (int g0 = 0; g0 < G; g0 += GC) {
+            uint4 qr[GC];
+#pragma unroll
+            for (int g = 0; g < GC; ++g) qr[g] = load_nt16(a.f.q + qoff + (g0 + g) * ROW);
+#pragma unroll
+            for (int g = 0; g < GC; ++g) {
+                A l[S], sd[S], M = NEG;
+#pragma unroll
+                for (int t = 0; t < S; ++t) {
+                    sd[t] = row_sum16(dot16<V, A>(qr[g], kr[t])) * c;
+                    l[t] = live[t] ? sd[t] + lw[t] : NEG;
+                    M = l[t] > M ? l[t] : M;
+                }
+                A p[S], Z = 0;
+#pragma unroll
+                for (int t = 0; t < S; ++t) {
+                    p[t] = live[t] ? fast_exp2(l[t] - M) : (A)0;
+                    Z += p[t];
+                }
+                const A inv = Z > (A)0 ? fast_rcp(Z) : (A)0;
+                if (a.f.stats) {
+                    const int t0 = st_one ? r - (g0 + g) * S : r;
+                    A mine = sd[0];
+                    bool ml = live[0];
+#pragma unroll
+                    for (int t = 1; t < S; ++t) {
+                        mine = t0 == t ? sd[t] : mine;
+                        ml = t0 == t ? live[t] : ml;
+                    }
+                    if (t0 >= 0 && t0 < S) st_val = ml ? (float)(fast_exp2(mine - M) * inv) : 0.0f;
+                    if (!st_one && t0 >= 0 && t0 < S)
+                        __builtin_nontemporal_store(
+                            st_val, a.f.stats + ((size_t)cur.pos.prow * (G + 2) + g0 + g) * S + t0);
+                }
+                A o[V];
+#pragma unroll
+                for (int e = 0; e < V; ++e) o[e] = 0;
+#pragma unroll
+                for (int t = 0; t < S; ++t) {
+                    A vf[V];
+                    unpack16<A, V>(vr[t], vf);
+                    const A pt = p[t] * inv;
+#pragma unroll
+                    for (int e = 0; e < V; ++e) o[e] += pt * vf[e];
+                }
+                store_u32x4_nt(a.f.o + qoff + (g0 + g) * ROW, pack_bf16x2(o[0], o[1]),
+                               pack_bf16x2(o[2], o[3]), pack_bf16x2(o[4], o[5]),
+                               pack_bf16x2(o[6], o[7]));
+            }
+        }
+        if (st_one && a.f.stats && r < (G + 2) * S)
+            __builtin_nontemporal_store(st_val, a.f.stats + (size_t)cur.pos.prow * (G + 2) * S + r);
+        cur = nxt;
+        l1 = l2;
+    }
+}
+
+template <int G>
+hipError_t run_ser_sea(const SerSeaFwd& a, hipStream_t st) {
+    const void* fn = reinterpret_cast<const void*>(&ser_sea_fwd_row_kernel<G>);
+    const int nwg = persistent_grid(fn, a.f.U, kBlock / 16);
+    hipLaunchKernelGGL((ser_sea_fwd_row_kernel<G>), dim3(nwg), dim3(kBlock), 0, st, a);
+    return hipGetLastError();
+}
+
 }  // namespace
 
 bool sea_row_group(int G) { return G == 1 || G == 2 || G == 4 || G == 8 || G == 16; }
@@ -538,6 +741,55 @@ hipError_t launch_sea_forward(int B, int n, int hq, int hkv, int d, bool bf16, f
         return bf16 ? fast_g<bf16_t, 1>(f, G, st) : fast_g<float, 1>(f, G, st);
     }
     return bf16 ? dispatch_g<bf16_t>(a, G, st) : dispatch_g<float>(a, G, st);
+}
+
+}  // namespace gm
+
+namespace gm {
+
+bool ser_sea_fused_shape(int B, int n, int hq, int hkv, int d, bool bf16, int s1, int s2, int s3,
+                         const void* idx1, const void* w1, const void* idx2, const void* w2,
+                         const void* idx_out, const void* w_out) {
+    const int G = hkv > 0 ? hq / hkv : 0;
+    return bf16 && d == 128 && s1 == 4 && s2 == 4 && s3 == 4 && sea_row_group(G) &&
+           (long long)B * n * hq * d * 2 < (1ll << 32) &&
+           (((uintptr_t)idx1 | (uintptr_t)w1 | (uintptr_t)idx2 | (uintptr_t)w2 |
+             (uintptr_t)idx_out | (uintptr_t)w_out) & 15) == 0;
+}
+
+hipError_t launch_ser_sea_forward(int B, int n, int hq, int hkv, int d, bool bf16, float scale,
+                                  const int32_t* idx1, const float* w1, int s2,
+                                  const int32_t* idx2, const float* w2, int s3, int s1,
+                                  const void* q, const void* k, const void* v,
+                                  int32_t* idx_out, float* w_out, void* o, float* stats,
+                                  hipStream_t st) {
+    if (!ser_sea_fused_shape(B, n, hq, hkv, d, bf16, s1, s2, s3, idx1, w1, idx2, w2, idx_out,
+                             w_out)) {
+        // other shapes: the two stages one after the other
+        const hipError_t e = launch_ser_forward(B, n, hkv, idx1, w1, s2, idx2, w2, s3, idx_out,
+                                                w_out, s1, st);
+        if (e != hipSuccess) return e;
+        return launch_sea_forward(B, n, hq, hkv, d, bf16, scale, q, k, v, idx_out, w_out, s1, o,
+                                  stats, st);
+    }
+    SerSeaFwd a;
+    a.f.q = static_cast<const char*>(q); a.f.k = static_cast<const char*>(k);
+    a.f.v = static_cast<const char*>(v); a.f.idx = idx_out; a.f.w = w_out;
+    a.f.o = static_cast<char*>(o);
+    a.f.stats = stats;
+    a.f.n = n; a.f.hq = hq; a.f.hkv = hkv; a.f.s = 4; a.f.U = B * n * hkv; a.f.scale = scale;
+    make_seg_plan(a.f.sp, B, n, hkv);
+    a.f.vec = 1;
+    a.idx1 = idx1; a.w1 = w1; a.idx2 = idx2; a.w2 = w2;
+    a.idx_out = idx_out; a.w_out = w_out;
+    switch (hq / hkv) {
+        case 1: return run_ser_sea<1>(a, st);
+        case 2: return run_ser_sea<2>(a, st);
+        case 4: return run_ser_sea<4>(a, st);
+        case 8: return run_ser_sea<8>(a, st);
+        case 16: return run_ser_sea<16>(a, st);
+        default: return hipErrorInvalidValue;
+    }
 }
 
 }  // namespace gm
