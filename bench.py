@@ -56,11 +56,11 @@ PEAK_BF16_TFLOPS = 2500.0      # dense bf16 matrix-core peak (no sparsity)
 # so is its pair-major copy of the edge row (the backward reads the copy, not
 # the edge tensor).
 BYTES_PER_UNIT = {
-    "gm_ser_forward": 32 + 32,                          # A row + A' row
+    "gm_ser_forward": 32 + 32 + 8,                      # A row + A' row + path map
     "gm_sea_forward": 512 + 32 + 512 + 512 + 32 + 32,   # q, A', K+V, o, p / w, A' copy
     "gm_sea_backward": 512 + 512 + 32 + 512 + 32 + 1024 + 16 + 1024,
     #                  q    dO  A'copy KV  p/w   dq   dw'   dK dV
-    "gm_ser_backward": 32 + 32 + 16 + 16,               # A, A', dw', dw
+    "gm_ser_backward": 32 + 8 + 16 + 16,                # A, path map, dw', dw
 }
 # with the fused forward (gm_ser_sea_forward): the SER row in, A' and the
 # SEA forward's outputs out, no A' read in between
@@ -114,10 +114,12 @@ def stage_bytes(stage: str, p: synth.Preset) -> int:
     es = 2 if p.dtype == torch.bfloat16 else 4
     qrow, kv = G * p.d * es, 2 * p.d * es          # a unit's q (or o, dout); its K and V rows
     st = 4 * G * s1 if p.backward else 0
-    return {"ser_fwd": 8 * p.s2 + 8 * s1,
+    pm = 8 if p.backward and max(p.s1, p.s2, p.s3) <= 4 else 0   # the SER path map
+    return {"ser_fwd": 8 * p.s2 + 8 * s1 + pm,
             "sea_fwd": qrow + 8 * s1 + kv + qrow + st + (8 * s1 if p.backward else 0),
             "sea_bwd": 2 * qrow + 8 * s1 + kv + st + 4 * G * p.d + 4 * s1 + 8 * p.d,
-            "ser_bwd": 8 * p.s2 + 8 * s1 + 4 * s1 + 4 * p.s2}[stage]
+            "ser_bwd": (8 * p.s2 + pm + 4 * s1 + 4 * p.s2 if pm
+                        else 8 * p.s2 + 8 * s1 + 4 * s1 + 4 * p.s2)}[stage]
 
 
 def profiled_traffic(call: str):
@@ -197,6 +199,9 @@ class Pass:
         self.dv = torch.empty(ks, **f32)
         self.dwa = torch.empty(es, **f32)
         self.dA = torch.empty(self.idx.shape, **f32)
+        # the SER forward's path map, read by the SER backward
+        self.paths = (torch.empty(self.idx.shape[:3], dtype=torch.int64, device="cuda")
+                      if p.backward and max(p.s1, p.s2, p.s3) <= 4 else None)
         self.ws = gm.ser_workspace(self.idx, self.idx, aliased=True)
         self.ws_sea = gm.sea_workspace(self.q, self.ia)
         if p.ser_steps > 1:   # the first of two chained SER steps writes here
@@ -212,8 +217,11 @@ class Pass:
                 ser_no = stages[:k + 1].count("ser_fwd")
                 dst = (self.ia, self.wa) if ser_no == n_ser else (self.ia1, self.wa1)
                 src = edges
+                # the last SER step's path map feeds the SER backward
+                pm = self.paths if ser_no == n_ser else None
                 out.append((f"gm_ser_forward#{ser_no}",
-                            lambda s_=src, d_=dst: gm.gm_ser_forward(*s_, *s_, *d_)))
+                            lambda s_=src, d_=dst, pm_=pm: gm.gm_ser_forward(*s_, *s_, *d_,
+                                                                            paths=pm_)))
                 edges = dst
             elif st == "sea_fwd":
                 e = (self.ia, self.wa) if n_ser else (self.idx, self.w)
@@ -233,17 +241,18 @@ class Pass:
             return [
                 lambda: gm.gm_ser_sea_forward(self.idx, self.w, self.idx, self.w, self.q,
                                               self.k, self.v, self.ia, self.wa, self.o,
-                                              stats=self.stats),
+                                              stats=self.stats, paths=self.paths),
             ] + self.calls()[2:]
         return [
-            lambda: gm.gm_ser_forward(self.idx, self.w, self.idx, self.w, self.ia, self.wa),
+            lambda: gm.gm_ser_forward(self.idx, self.w, self.idx, self.w, self.ia, self.wa,
+                                      paths=self.paths),
             lambda: gm.gm_sea_forward(self.q, self.k, self.v, self.ia, self.wa, self.o,
                                       stats=self.stats),
             lambda: gm.gm_sea_backward(self.q, self.k, self.v, self.ia, self.wa, self.dout,
                                        self.dq, self.dk, self.dv, self.dwa, self.ws_sea,
                                        stats=self.stats),
             lambda: gm.gm_ser_backward(self.idx, self.w, self.idx, self.w, self.ia, self.wa,
-                                       self.dwa, self.dA, self.dA, self.ws),
+                                       self.dwa, self.dA, self.dA, self.ws, paths=self.paths),
         ]
 
 

@@ -83,11 +83,19 @@ typedef enum { GM_F32 = 0, GM_BF16 = 1 } gm_dtype;
  * in (a, c) order), the sum is rounded to fp32, and the s1 targets of largest
  * positive weight are kept, equal weights ordered by lower index.  Slots are
  * written in that order; unused slots get (0, 0.0f).  Requires s2*s3 <= 64.
+ *   out  paths [B][n][hkv] uint64, optional (NULL: not written; only for
+ *        s1, s2, s3 <= 4, else GM_ERR_UNSUPPORTED; 8-byte aligned,
+ *        overlapping nothing): the path map of each unit, 4 bits per path
+ *        k = 4a + c at bits [4k, 4k + 4): the slot of A' that path's target
+ *        went to, or 15 when the path has a zero leg weight or its target
+ *        was not kept (and for k beyond the s2 x s3 paths, a >= s2 or
+ *        c >= s3).  gm_ser_backward takes it to skip regathering the
+ *        leg-2 indices and re-reading A'.
  */
 gm_status gm_ser_forward(int B, int n, int hkv,
                          const int32_t* idx1, const float* w1, int s2,
                          const int32_t* idx2, const float* w2, int s3,
-                         int32_t* idx_out, float* w_out, int s1,
+                         int32_t* idx_out, float* w_out, int s1, uint64_t* paths,
                          hipStream_t stream);
 
 /*
@@ -125,15 +133,15 @@ gm_status gm_sea_forward(int B, int n, int hq, int hkv, int d, gm_dtype dt,
  * sparse layer).  For bf16, d = 128, s1 = s2 = s3 = 4, 16-byte aligned edge
  * rows and hq / hkv in {1, 2, 4, 8, 16} the two stages run as one kernel
  * (A' stays in registers between them); other shapes run the two stages one
- * after the other.  Arguments, limits and errors as the two calls; no output
- * may overlap an input or another output.
+ * after the other.  Arguments (paths as gm_ser_forward's), limits and errors
+ * as the two calls; no output may overlap an input or another output.
  */
 gm_status gm_ser_sea_forward(int B, int n, int hq, int hkv, int d, gm_dtype dt, float scale,
                              const int32_t* idx1, const float* w1, int s2,
                              const int32_t* idx2, const float* w2, int s3, int s1,
                              const void* q, const void* k, const void* v,
                              int32_t* idx_out, float* w_out, void* o, float* stats,
-                             hipStream_t stream);
+                             uint64_t* paths, hipStream_t stream);
 
 /*
  * Bytes of device workspace gm_sea_backward needs for these sizes: per-edge
@@ -218,7 +226,11 @@ size_t gm_ser_backward_workspace_bytes(int B, int n, int hkv, int s2, int s3,
  * selection held fixed (ai.info Methodology: gradients reach the kept
  * weights alone).
  *   in   legs as for the forward; idx_out, w_out [B][n][hkv][s1] the A' the
- *        forward produced; dw_out [B][n][hkv][s1] the gradient of w_out
+ *        forward produced; dw_out [B][n][hkv][s1] the gradient of w_out;
+ *        paths: NULL, or the path map gm_ser_forward wrote for these legs
+ *        (s1, s2, s3 <= 4; 8-byte aligned).  With it the source-chunk path
+ *        (s2 = s3 = 4) reads each path's slot instead of gathering the
+ *        leg-2 indices and comparing them with A' (same results, bitwise).
  *   out  dw1 [B][n][hkv][s2], dw2 [B][n][hkv][s3] fp32.  dw1 == dw2 is
  *        allowed (A' = Sparsify(A A), s2 == s3): the sum of both is written.
  *   ws   device workspace of gm_ser_backward_workspace_bytes(...) bytes,
@@ -232,7 +244,7 @@ gm_status gm_ser_backward(int B, int n, int hkv,
                           const int32_t* idx1, const float* w1, int s2,
                           const int32_t* idx2, const float* w2, int s3,
                           const int32_t* idx_out, const float* w_out, int s1,
-                          const float* dw_out, float* dw1, float* dw2,
+                          const float* dw_out, const uint64_t* paths, float* dw1, float* dw2,
                           void* workspace, size_t workspace_bytes,
                           hipStream_t stream);
 

@@ -50,7 +50,7 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
         raise ImportError(f"{path} is not built; run `python -m sparse_dynamic_routing_amd.build`")
     lib = ctypes.CDLL(path)
     sig = {
-        "gm_ser_forward": [_I, _I, _I, _P, _P, _I, _P, _P, _I, _P, _P, _I, _P],
+        "gm_ser_forward": [_I, _I, _I, _P, _P, _I, _P, _P, _I, _P, _P, _I, _P, _P],
         "gm_sea_forward": [_I, _I, _I, _I, _I, _I, _F, _P, _P, _P, _P, _P, _I, _P, _P, _P],
         "gm_sea_backward_workspace_bytes": [_I, _I, _I, _I, _I],
         "gm_sea_backward": [_I, _I, _I, _I, _I, _I, _F, _P, _P, _P, _P, _P, _I, _P, _P,
@@ -58,7 +58,7 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
         "gm_sea_backward_noalloc": [_I, _I, _I, _I, _I, _I, _F, _P, _P, _P, _P, _P, _I, _P,
                                     _P, _P, _P, _P, _P, _P],
         "gm_ser_sea_forward": [_I, _I, _I, _I, _I, _I, _F, _P, _P, _I, _P, _P, _I, _I, _P, _P,
-                               _P, _P, _P, _P, _P, _P],
+                               _P, _P, _P, _P, _P, _P, _P],
         "gm_decode_step": [_I, _I, _I, _I, _I, _I, _F, _P, _P, _I, _P, _P, _I, _I, _P, _P,
                            _P, _P, _P, _P, _P],
         "gm_dense_refresh": [_I, _I, _I, _I, _I, _I, _F, _P, _P, _I, _I, _P, _P, _P, _P],
@@ -67,7 +67,7 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
         "gm_leg_mix_backward": [_I, _I, _I, _P, _P, _I, _P, _P, _P, _I, _P, _P, _P, _P, _Z,
                                 _P],
         "gm_ser_backward_workspace_bytes": [_I, _I, _I, _I, _I, _I],
-        "gm_ser_backward": [_I, _I, _I, _P, _P, _I, _P, _P, _I, _P, _P, _I, _P, _P, _P,
+        "gm_ser_backward": [_I, _I, _I, _P, _P, _I, _P, _P, _I, _P, _P, _I, _P, _P, _P, _P,
                             _P, _Z, _P],
         "gm_check_edges": [_I, _I, _I, _P, _P, _I, _P, _P],
         "gm_status_string": [_I],
@@ -122,7 +122,9 @@ _ACT = (torch.float32, torch.bfloat16)
 
 
 # --------------------------------------------------------------- C-named calls
-def gm_ser_forward(idx1, w1, idx2, w2, idx_out, w_out, stream=None) -> None:
+def gm_ser_forward(idx1, w1, idx2, w2, idx_out, w_out, stream=None, paths=None) -> None:
+    """``paths`` (optional, [B, n, hkv] int64) receives the path map that
+    gm_ser_backward can take."""
     B, n, hkv, s2 = idx1.shape
     s3, s1 = idx2.shape[-1], idx_out.shape[-1]
     _need(idx1, "idx1", (torch.int32,)); _need(w1, "w1", (torch.float32,), idx1.shape)
@@ -130,8 +132,10 @@ def gm_ser_forward(idx1, w1, idx2, w2, idx_out, w_out, stream=None) -> None:
     _need(w2, "w2", (torch.float32,), idx2.shape)
     _need(idx_out, "idx_out", (torch.int32,), (B, n, hkv, s1))
     _need(w_out, "w_out", (torch.float32,), idx_out.shape)
+    if paths is not None:
+        _need(paths, "paths", (torch.int64,), (B, n, hkv))
     _call("gm_ser_forward", B, n, hkv, _ptr(idx1), _ptr(w1), s2, _ptr(idx2), _ptr(w2), s3,
-          _ptr(idx_out), _ptr(w_out), s1, _stream(stream))
+          _ptr(idx_out), _ptr(w_out), s1, _ptr(paths), _stream(stream))
 
 
 def gm_sea_forward(q, k, v, idx, w, o, scale=None, stream=None, stats=None) -> None:
@@ -152,7 +156,7 @@ def gm_sea_forward(q, k, v, idx, w, o, scale=None, stream=None, stats=None) -> N
 
 
 def gm_ser_sea_forward(idx1, w1, idx2, w2, q, k, v, idx_out, w_out, o, scale=None, stream=None,
-                       stats=None) -> None:
+                       stats=None, paths=None) -> None:
     """SER (A' into idx_out / w_out) then SEA (o, and stats when given) in
     one call."""
     B, n, hkv, s2 = idx1.shape
@@ -167,10 +171,12 @@ def gm_ser_sea_forward(idx1, w1, idx2, w2, q, k, v, idx_out, w_out, o, scale=Non
     _need(o, "o", (q.dtype,), q.shape)
     if stats is not None:
         _need(stats, "stats", (torch.float32,), (B, hkv, n, hq // hkv + 2, s1))
+    if paths is not None:
+        _need(paths, "paths", (torch.int64,), (B, n, hkv))
     scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
     _call("gm_ser_sea_forward", B, n, hq, hkv, d, _act_dtype(q), scale, _ptr(idx1), _ptr(w1), s2,
           _ptr(idx2), _ptr(w2), s3, s1, _ptr(q), _ptr(k), _ptr(v), _ptr(idx_out), _ptr(w_out),
-          _ptr(o), _ptr(stats), _stream(stream))
+          _ptr(o), _ptr(stats), _ptr(paths), _stream(stream))
 
 
 def gm_sea_backward_workspace_bytes(B, n, hq, hkv, s1) -> int:
@@ -299,7 +305,8 @@ def gm_ser_backward_workspace_bytes(B, n, hkv, s2, s3, aliased) -> int:
 
 
 def gm_ser_backward(idx1, w1, idx2, w2, idx_out, w_out, dw_out, dw1, dw2, workspace,
-                    stream=None) -> None:
+                    stream=None, paths=None) -> None:
+    """``paths``: optional, the map gm_ser_forward wrote for the same legs."""
     B, n, hkv, s2 = idx1.shape
     s3, s1 = idx2.shape[-1], idx_out.shape[-1]
     _need(idx1, "idx1", (torch.int32,)); _need(w1, "w1", (torch.float32,), idx1.shape)
@@ -310,9 +317,11 @@ def gm_ser_backward(idx1, w1, idx2, w2, idx_out, w_out, dw_out, dw1, dw2, worksp
     _need(dw_out, "dw_out", (torch.float32,), idx_out.shape)
     _need(dw1, "dw1", (torch.float32,), idx1.shape); _need(dw2, "dw2", (torch.float32,), idx2.shape)
     _need(workspace, "workspace", (torch.uint8, torch.float64))
+    if paths is not None:
+        _need(paths, "paths", (torch.int64,), (B, n, hkv))
     _call("gm_ser_backward", B, n, hkv, _ptr(idx1), _ptr(w1), s2, _ptr(idx2), _ptr(w2), s3,
-          _ptr(idx_out), _ptr(w_out), s1, _ptr(dw_out), _ptr(dw1), _ptr(dw2), _ptr(workspace),
-          workspace.numel() * workspace.element_size(), _stream(stream))
+          _ptr(idx_out), _ptr(w_out), s1, _ptr(dw_out), _ptr(paths), _ptr(dw1), _ptr(dw2),
+          _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream))
 
 
 def gm_check_edges(idx, w, counts, stream=None) -> None:
@@ -323,12 +332,15 @@ def gm_check_edges(idx, w, counts, stream=None) -> None:
 
 
 # ------------------------------------------------------- allocating wrappers
-def ser_forward(idx1, w1, idx2, w2, s1, stream=None):
+def ser_forward(idx1, w1, idx2, w2, s1, stream=None, save_paths=False):
+    """(idx_out, w_out), with ``save_paths`` also the path map."""
     shape = tuple(idx1.shape[:3]) + (s1,)
     idx_out = torch.empty(shape, dtype=torch.int32, device=idx1.device)
     w_out = torch.empty(shape, dtype=torch.float32, device=idx1.device)
-    gm_ser_forward(idx1, w1, idx2, w2, idx_out, w_out, stream)
-    return idx_out, w_out
+    paths = (torch.empty(tuple(idx1.shape[:3]), dtype=torch.int64, device=idx1.device)
+             if save_paths else None)
+    gm_ser_forward(idx1, w1, idx2, w2, idx_out, w_out, stream, paths)
+    return (idx_out, w_out, paths) if save_paths else (idx_out, w_out)
 
 
 def sea_forward(q, k, v, idx, w, scale=None, stream=None, save_stats=False):
@@ -343,8 +355,9 @@ def sea_forward(q, k, v, idx, w, scale=None, stream=None, save_stats=False):
     return (o, stats) if save_stats else o
 
 
-def ser_sea_forward(idx1, w1, idx2, w2, s1, q, k, v, scale=None, stream=None, save_stats=False):
-    """(idx_out, w_out, o[, stats]) of SER then SEA in one call."""
+def ser_sea_forward(idx1, w1, idx2, w2, s1, q, k, v, scale=None, stream=None, save_stats=False,
+                    save_paths=False):
+    """(idx_out, w_out, o[, stats][, paths]) of SER then SEA in one call."""
     B, n, hkv, _ = idx1.shape
     hq = q.shape[2]
     io = torch.empty((B, n, hkv, s1), dtype=torch.int32, device=idx1.device)
@@ -352,8 +365,10 @@ def ser_sea_forward(idx1, w1, idx2, w2, s1, q, k, v, scale=None, stream=None, sa
     o = torch.empty_like(q)
     stats = (torch.empty((B, hkv, n, hq // hkv + 2, s1), dtype=torch.float32, device=q.device)
              if save_stats else None)
-    gm_ser_sea_forward(idx1, w1, idx2, w2, q, k, v, io, wo, o, scale, stream, stats)
-    return (io, wo, o, stats) if save_stats else (io, wo, o)
+    paths = (torch.empty((B, n, hkv), dtype=torch.int64, device=q.device)
+             if save_paths else None)
+    gm_ser_sea_forward(idx1, w1, idx2, w2, q, k, v, io, wo, o, scale, stream, stats, paths)
+    return (io, wo, o) + ((stats,) if save_stats else ()) + ((paths,) if save_paths else ())
 
 
 def sea_workspace(q, idx, device=None) -> torch.Tensor:
@@ -381,13 +396,13 @@ def ser_workspace(idx1, idx2, aliased, device=None) -> torch.Tensor:
 
 
 def ser_backward(idx1, w1, idx2, w2, idx_out, w_out, dw_out, aliased=False, workspace=None,
-                 stream=None):
+                 stream=None, paths=None):
     """(dw1, dw2); with ``aliased`` the legs are one tensor and one gradient
     (the same tensor, returned twice) receives both contributions."""
     dw1 = torch.empty(idx1.shape, dtype=torch.float32, device=idx1.device)
     dw2 = dw1 if aliased else torch.empty(idx2.shape, dtype=torch.float32, device=idx1.device)
     ws = ser_workspace(idx1, idx2, aliased) if workspace is None else workspace
-    gm_ser_backward(idx1, w1, idx2, w2, idx_out, w_out, dw_out, dw1, dw2, ws, stream)
+    gm_ser_backward(idx1, w1, idx2, w2, idx_out, w_out, dw_out, dw1, dw2, ws, stream, paths)
     return dw1, dw2
 
 

@@ -99,7 +99,7 @@ bool overlaps(const void* a, size_t an, const void* b, size_t bn) {
 
 extern "C" {
 
-int gm_abi_version(void) { return 6; }
+int gm_abi_version(void) { return 7; }
 
 const char* gm_status_string(gm_status s) {
     switch (s) {
@@ -118,11 +118,25 @@ const char* gm_status_string(gm_status s) {
     return "unknown status";
 }
 
+// The optional path map: produced for s1, s2, s3 <= 4; 8-byte aligned and
+// overlapping none of the call's other arrays.
+static gm_status check_paths(const uint64_t* paths, int s1, int s2, int s3, size_t rows,
+                      const void* const* arrays, const size_t* bytes, int narrays) {
+    if (!paths) return GM_OK;
+    if (s1 > 4 || s2 > 4 || s3 > 4) return GM_ERR_UNSUPPORTED;
+    if (!aligned(paths, 8)) return GM_ERR_ALIGN;
+    for (int a = 0; a < narrays; ++a)
+        if (arrays[a] && bytes[a] && overlaps(paths, rows * 8, arrays[a], bytes[a]))
+            return GM_ERR_ALIAS;
+    return GM_OK;
+}
+
 gm_status gm_ser_forward(int B, int n, int hkv, const int32_t* idx1, const float* w1, int s2,
                          const int32_t* idx2, const float* w2, int s3, int32_t* idx_out,
-                         float* w_out, int s1, hipStream_t stream) {
+                         float* w_out, int s1, uint64_t* paths, hipStream_t stream) {
     gm_status st = check_ser(B, n, hkv, s1, s2, s3);
     if (st != GM_OK) return st;
+    if (paths && (s1 > 4 || s2 > 4 || s3 > 4)) return GM_ERR_UNSUPPORTED;
     if (empty(B, n, hkv)) return GM_OK;
     if ((st = check_edge_ptrs(idx1, w1)) != GM_OK) return st;
     if ((st = check_edge_ptrs(idx2, w2)) != GM_OK) return st;
@@ -135,8 +149,11 @@ gm_status gm_ser_forward(int B, int n, int hkv, const int32_t* idx1, const float
         overlaps(w_out, o4, idx2, rows * s3 * 4) || overlaps(w_out, o4, w2, rows * s3 * 4) ||
         overlaps(idx_out, o4, w_out, o4))
         return GM_ERR_ALIAS;
+    const void* arr[6] = {idx1, w1, idx2, w2, idx_out, w_out};
+    const size_t arb[6] = {rows * s2 * 4, rows * s2 * 4, rows * s3 * 4, rows * s3 * 4, o4, o4};
+    if ((st = check_paths(paths, s1, s2, s3, rows, arr, arb, 6)) != GM_OK) return st;
     return hip_status(gm::launch_ser_forward(B, n, hkv, idx1, w1, s2, idx2, w2, s3, idx_out,
-                                             w_out, s1, stream));
+                                             w_out, s1, paths, stream));
 }
 
 gm_status gm_sea_forward(int B, int n, int hq, int hkv, int d, gm_dtype dt, float scale,
@@ -169,10 +186,11 @@ gm_status gm_ser_sea_forward(int B, int n, int hq, int hkv, int d, gm_dtype dt, 
                              const int32_t* idx1, const float* w1, int s2, const int32_t* idx2,
                              const float* w2, int s3, int s1, const void* q, const void* k,
                              const void* v, int32_t* idx_out, float* w_out, void* o,
-                             float* stats, hipStream_t stream) {
+                             float* stats, uint64_t* paths, hipStream_t stream) {
     gm_status st = check_ser(B, n, hkv, s1, s2, s3);
     if (st != GM_OK) return st;
     if ((st = check_sea(B, n, hq, hkv, d, dt, s1)) != GM_OK) return st;
+    if (paths && (s1 > 4 || s2 > 4 || s3 > 4)) return GM_ERR_UNSUPPORTED;
     if (empty(B, n, hkv)) return GM_OK;
     if ((st = check_edge_ptrs(idx1, w1)) != GM_OK) return st;
     if ((st = check_edge_ptrs(idx2, w2)) != GM_OK) return st;
@@ -196,9 +214,13 @@ gm_status gm_ser_sea_forward(int B, int n, int hq, int hkv, int d, gm_dtype dt, 
         for (int b = a + 1; b < 4; ++b)
             if (outb[b] && overlaps(outs[a], outb[a], outs[b], outb[b])) return GM_ERR_ALIAS;
     }
+    const void* arr[11] = {idx1, w1, idx2, w2, q, k, v, idx_out, w_out, o, stats};
+    const size_t arb[11] = {inb[0], inb[1], inb[2], inb[3], inb[4], inb[5], inb[6],
+                            outb[0], outb[1], outb[2], outb[3]};
+    if ((st = check_paths(paths, s1, s2, s3, rows, arr, arb, 11)) != GM_OK) return st;
     return hip_status(gm::launch_ser_sea_forward(B, n, hq, hkv, d, dt == GM_BF16, scale, idx1, w1,
                                                  s2, idx2, w2, s3, s1, q, k, v, idx_out, w_out,
-                                                 o, stats, stream));
+                                                 o, stats, paths, stream));
 }
 
 gm_status gm_leg_mix_forward(int B, int n, int hkv, const int32_t* idx, const float* w, int K,
@@ -444,10 +466,11 @@ size_t gm_ser_backward_workspace_bytes(int B, int n, int hkv, int s2, int s3, in
 gm_status gm_ser_backward(int B, int n, int hkv, const int32_t* idx1, const float* w1, int s2,
                           const int32_t* idx2, const float* w2, int s3,
                           const int32_t* idx_out, const float* w_out, int s1,
-                          const float* dw_out, float* dw1, float* dw2, void* workspace,
-                          size_t workspace_bytes, hipStream_t stream) {
+                          const float* dw_out, const uint64_t* paths, float* dw1, float* dw2,
+                          void* workspace, size_t workspace_bytes, hipStream_t stream) {
     gm_status st = check_ser(B, n, hkv, s1, s2, s3);
     if (st != GM_OK) return st;
+    if (paths && (s1 > 4 || s2 > 4 || s3 > 4)) return GM_ERR_UNSUPPORTED;
     if (empty(B, n, hkv)) return GM_OK;
     if ((st = check_edge_ptrs(idx1, w1)) != GM_OK) return st;
     if ((st = check_edge_ptrs(idx2, w2)) != GM_OK) return st;
@@ -473,10 +496,15 @@ gm_status gm_ser_backward(int B, int n, int hkv, const int32_t* idx1, const floa
             if (overlaps(outs[a], outb[a], outs[b], outb[b])) return GM_ERR_ALIAS;
         }
     }
+    const void* arr[10] = {idx1, w1, idx2, w2, idx_out, w_out, dw_out, dw1, dw2, workspace};
+    const size_t arb[10] = {inb[0], inb[1], inb[2], inb[3], inb[4], inb[5], inb[6],
+                            outb[0], outb[1], outb[2]};
+    if ((st = check_paths(paths, s1, s2, s3, rows, arr, arb, 10)) != GM_OK) return st;
     double* ws1 = static_cast<double*>(workspace);
     double* ws2 = ws1 + rows * s2;
     return hip_status(gm::launch_ser_backward(B, n, hkv, idx1, w1, s2, idx2, w2, s3, idx_out,
-                                              w_out, s1, dw_out, dw1, dw2, ws1, ws2, stream));
+                                              w_out, s1, dw_out, paths, dw1, dw2, ws1, ws2,
+                                              stream));
 }
 
 gm_status gm_check_edges(int B, int n, int hkv, const int32_t* idx, const float* w, int s,

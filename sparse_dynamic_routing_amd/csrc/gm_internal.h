@@ -18,9 +18,12 @@ struct TeamShape {
 };
 TeamShape sea_team(int d, int elem_bytes, int s);
 
+// paths: optional path map per unit (s2, s3, s1 <= 4), read back by the
+// backward's source-chunk kernel; ignored for other shapes.
 hipError_t launch_ser_forward(int B, int n, int hkv, const int32_t* idx1, const float* w1,
                               int s2, const int32_t* idx2, const float* w2, int s3,
-                              int32_t* idx_out, float* w_out, int s1, hipStream_t st);
+                              int32_t* idx_out, float* w_out, int s1, uint64_t* paths,
+                              hipStream_t st);
 
 // The 16-lane-row fast kernels apply: one d-row is 256 bytes, s <= 4, and
 // activation tensors are addressable with 32-bit byte offsets.
@@ -45,7 +48,7 @@ hipError_t launch_ser_sea_forward(int B, int n, int hq, int hkv, int d, bool bf1
                                   const int32_t* idx2, const float* w2, int s3, int s1,
                                   const void* q, const void* k, const void* v,
                                   int32_t* idx_out, float* w_out, void* o, float* stats,
-                                  hipStream_t st);
+                                  uint64_t* paths, hipStream_t st);
 
 // Leg construction (stored edges mixed into a leg), forward and backward.
 size_t leg_mix_backward_workspace_bytes(int B, int n, int hkv, int K);
@@ -82,8 +85,8 @@ hipError_t launch_sea_backward(int B, int n, int hq, int hkv, int d, bool bf16, 
 hipError_t launch_ser_backward(int B, int n, int hkv, const int32_t* idx1, const float* w1,
                                int s2, const int32_t* idx2, const float* w2, int s3,
                                const int32_t* idx_out, const float* w_out, int s1,
-                               const float* dw_out, float* dw1, float* dw2, double* ws1,
-                               double* ws2, hipStream_t st);
+                               const float* dw_out, const uint64_t* paths, float* dw1,
+                               float* dw2, double* ws1, double* ws2, hipStream_t st);
 
 // Reverse (target-sorted) index of an edge tensor [B][n][hkv][s], s <= 4:
 // beg/len per pair-major row (pair * n + j), list of edge ids; list needs

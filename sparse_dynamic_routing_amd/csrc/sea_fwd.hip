@@ -518,6 +518,7 @@ struct SerSeaFwd {
     const float* w2;
     int32_t* idx_out;
     float* w_out;
+    uint64_t* paths;       // path map per unit (as gm_ser_forward writes it), or null
 };
 
 template <int G>
@@ -592,6 +593,21 @@ __global__ __launch_bounds__(kBlock) void ser_sea_fwd_row_kernel(SerSeaFwd a) {
         if (r == 1)
             *reinterpret_cast<float4*>(a.w_out + (size_t)cur.pos.unit * S) =
                 make_float4(wt[0], wt[1], wt[2], wt[3]);
+        if (a.paths) {
+            // path r's slot of A' (15: none), four bits per path, gathered
+            // from the row's lanes bit plane by bit plane
+            uint32_t sl = 15;
+#pragma unroll
+            for (int t = 0; t < S; ++t) sl = cur.cw > 0.0 && wt[t] > 0.0f && jt[t] == cur.m ? t : sl;
+            uint64_t mp = 0;
+#pragma unroll
+            for (int bit = 0; bit < 4; ++bit) {
+                const uint32_t plane = (uint32_t)(__ballot((sl >> bit) & 1u) >> rbase) & 0xFFFFu;
+#pragma unroll
+                for (int k = 0; k < 16; ++k) mp |= (uint64_t)((plane >> k) & 1u) << (4 * k + bit);
+            }
+            if (r == 2) a.paths[cur.pos.unit] = mp;
+        }
 
         // SEA on the kept slots (as sea_fwd_row_kernel, 256-byte rows)
         bool live[S];
@@ -762,12 +778,12 @@ hipError_t launch_ser_sea_forward(int B, int n, int hq, int hkv, int d, bool bf1
                                   const int32_t* idx2, const float* w2, int s3, int s1,
                                   const void* q, const void* k, const void* v,
                                   int32_t* idx_out, float* w_out, void* o, float* stats,
-                                  hipStream_t st) {
+                                  uint64_t* paths, hipStream_t st) {
     if (!ser_sea_fused_shape(B, n, hq, hkv, d, bf16, s1, s2, s3, idx1, w1, idx2, w2, idx_out,
                              w_out)) {
         // other shapes: the two stages one after the other
         const hipError_t e = launch_ser_forward(B, n, hkv, idx1, w1, s2, idx2, w2, s3, idx_out,
-                                                w_out, s1, st);
+                                                w_out, s1, paths, st);
         if (e != hipSuccess) return e;
         return launch_sea_forward(B, n, hq, hkv, d, bf16, scale, q, k, v, idx_out, w_out, s1, o,
                                   stats, st);
@@ -782,6 +798,7 @@ hipError_t launch_ser_sea_forward(int B, int n, int hq, int hkv, int d, bool bf1
     a.f.vec = 1;
     a.idx1 = idx1; a.w1 = w1; a.idx2 = idx2; a.w2 = w2;
     a.idx_out = idx_out; a.w_out = w_out;
+    a.paths = paths;
     switch (hq / hkv) {
         case 1: return run_ser_sea<1>(a, st);
         case 2: return run_ser_sea<2>(a, st);

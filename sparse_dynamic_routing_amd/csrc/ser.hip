@@ -174,10 +174,33 @@ struct SerUnitArgs {
     FastDiv fd_hkv, fd_n;
     int vec_out;           // forward: outputs 16-byte aligned, s1 == 4
     int vec_in;            // legs 16-byte aligned, s2 == s3 == 4: one load per row
+    uint64_t* paths = nullptr;   // forward: the path map of every unit, or null
 };
 
 constexpr int kSmax = 4;
 constexpr int kCand = kSmax * kSmax;
+
+// Path map of a unit (s2, s3, s1 <= 4): 4 bits per path k = 4a + c (leg-1
+// slot a, leg-2 slot c), the slot of A' whose target the path reaches, or
+// kNoSlot when the path has a zero leg weight or its target was not kept.
+// With it the backward knows every path's gradient dw'[slot] without
+// gathering the leg-2 indices or reading A' again.
+constexpr uint32_t kNoSlot = 15;
+__device__ __forceinline__ uint64_t path_map(const int (&m)[kCand], const float (&x)[kSmax],
+                                             const float (&y)[kCand], const int (&om)[kSmax],
+                                             const float (&ow)[kSmax], int s1) {
+    uint64_t mp = 0;
+#pragma unroll
+    for (int k = 0; k < kCand; ++k) {
+        uint32_t sl = kNoSlot;
+        if (m[k] >= 0 && x[k / kSmax] > 0.0f && y[k] > 0.0f) {
+#pragma unroll
+            for (int r = 0; r < kSmax; ++r) sl = r < s1 && ow[r] > 0.0f && om[r] == m[k] ? r : sl;
+        }
+        mp |= (uint64_t)sl << (4 * k);
+    }
+    return mp;
+}
 
 // Token i of unit u (u = (b*n + i)*hkv + h); the row of token j of the same
 // (b, h) is u + (j - i) * hkv.
@@ -293,6 +316,7 @@ __global__ __launch_bounds__(kBlock) void ser_fwd_unit_kernel(SerUnitArgs a) {
         }
     }
     if (a.s1 <= kSmax) {
+        if (a.paths) a.paths[u] = path_map(m, x, y, om, ow, a.s1);
         if (a.vec_out) {
             *reinterpret_cast<int4*>(a.idx_out + ob) = make_int4(om[0], om[1], om[2], om[3]);
             *reinterpret_cast<float4*>(a.w_out + ob) = make_float4(ow[0], ow[1], ow[2], ow[3]);
@@ -341,8 +365,11 @@ __device__ __forceinline__ void load_paths_vec(const SerUnitArgs& a, int u, int 
 }
 
 // S1: retained slots (4, or 2 for the narrower top-2-of-16 budget).
-template <int S1>
-__global__ __launch_bounds__(kBlock) void ser_fwd_vec_kernel(SerUnitArgs a) {
+// MAP: also write the path map (held to 128 registers, four wavefronts per
+// SIMD: the map keeps the candidates' targets live through the sorting
+// network; without it the kernel needs fewer)
+template <int S1, bool MAP>
+__global__ __launch_bounds__(kBlock, MAP ? 4 : 1) void ser_fwd_vec_kernel(SerUnitArgs a) {
     static_assert(S1 == 2 || S1 == 4, "vector stores of 2 or 4 slots");
     const int u = xcd_unit(a.U);
     if (u < 0) return;
@@ -353,10 +380,12 @@ __global__ __launch_bounds__(kBlock) void ser_fwd_vec_kernel(SerUnitArgs a) {
     // set (targets are >= 0): it then matches no later candidate, whose
     // weight goes to the earlier, first candidate of the target instead
     double cw[kCand], acc[kCand];
+    uint32_t pos = 0;   // paths of positive weight (both legs > 0), for the path map
 #pragma unroll
     for (int k = 0; k < kCand; ++k) {
         cw[k] = (double)x[k / kSmax] * (double)y[k];
         acc[k] = cw[k];
+        pos |= (cw[k] > 0.0 ? 1u : 0u) << k;
     }
 #pragma unroll
     for (int k = 1; k < kCand; ++k) {
@@ -396,6 +425,20 @@ __global__ __launch_bounds__(kBlock) void ser_fwd_vec_kernel(SerUnitArgs a) {
     } else {
         *reinterpret_cast<int2*>(a.idx_out + (size_t)u * 2) = make_int2(om[0], om[1]);
         *reinterpret_cast<float2*>(a.w_out + (size_t)u * 2) = make_float2(ow[0], ow[1]);
+    }
+    if constexpr (MAP) {
+        // targets with the duplicate mark (bit 31) cleared
+        uint64_t mp = 0;
+#pragma unroll
+        for (int k = 0; k < kCand; ++k) {
+            const int tk = (int)((uint32_t)m[k] & 0x7fffffffu);
+            uint32_t sl = kNoSlot;
+#pragma unroll
+            for (int r = 0; r < S1; ++r) sl = ow[r] > 0.0f && om[r] == tk ? r : sl;
+            sl = (pos >> k) & 1u ? sl : kNoSlot;
+            mp |= (uint64_t)sl << (4 * k);
+        }
+        a.paths[u] = mp;
     }
 }
 
@@ -600,6 +643,7 @@ struct SerPartArgs {
     const int32_t* idx_out;
     const float* w_out;
     const float* dw_out;
+    const uint64_t* paths;   // the forward's path map, or null
     float* dw1;
     float* dw2;
     double* part;
@@ -612,6 +656,41 @@ __host__ __device__ inline long long part_row_off(int n, int c) {
     long long off = 0;
     for (int k = 0; k < c; ++k) off += (k + 1) * kSerThreads < n ? (k + 1) * kSerThreads : n;
     return off;
+}
+
+// Source i's contributions, from the gradients pg of its 16 paths: its own
+// dw1 (into the accumulator when the legs alias, else stored), and
+// dw2[j_a, c] += pg(a, c) w1[i, a] into the accumulator rows j_a.
+__device__ __forceinline__ void ser_part_accumulate(const SerPartArgs& a, double* acc, int i,
+                                                    int u, const int (&j)[4],
+                                                    const float (&x)[kSmax],
+                                                    const float (&y)[kCand],
+                                                    const double (&pg)[kCand]) {
+    // own row: dw1[i, a] = sum_c g(a, c) w2[j_a, c]
+    double d1[kSmax];
+#pragma unroll
+    for (int aa = 0; aa < kSmax; ++aa) {
+        d1[aa] = 0.0;
+#pragma unroll
+        for (int cc = 0; cc < kSmax; ++cc) d1[aa] += pg[aa * kSmax + cc] * (double)y[aa * kSmax + cc];
+    }
+    if (a.aliased) {
+#pragma unroll
+        for (int aa = 0; aa < kSmax; ++aa)
+            if (d1[aa] != 0.0) atomicAdd(acc + i * 4 + aa, d1[aa]);
+    } else {
+        *reinterpret_cast<float4*>(a.dw1 + (size_t)u * 4) =
+            make_float4((float)d1[0], (float)d1[1], (float)d1[2], (float)d1[3]);
+    }
+    // leg-2 slots of the target rows: dw2[j_a, c] += g(a, c) w1[i, a]
+#pragma unroll
+    for (int aa = 0; aa < kSmax; ++aa) {
+#pragma unroll
+        for (int cc = 0; cc < kSmax; ++cc) {
+            const double g = pg[aa * kSmax + cc];
+            if (g != 0.0) atomicAdd(acc + j[aa] * 4 + cc, g * (double)x[aa]);
+        }
+    }
 }
 
 template <int S1>
@@ -630,7 +709,40 @@ __global__ __launch_bounds__(kSerThreads) void ser_bwd_part_kernel(SerPartArgs a
     __syncthreads();
 
     const int i = i0 + (int)threadIdx.x;
-    if (i < thi) {
+    if (i < thi && a.paths) {
+        // with the forward's path map: leg-1 row, leg-2 weights, dw' only
+        const int u = (b * n + i) * hkv + h;
+        const int4 j4 = *reinterpret_cast<const int4*>(a.u.idx1 + (size_t)u * 4);
+        const float4 x4 = *reinterpret_cast<const float4*>(a.u.w1 + (size_t)u * 4);
+        const uint64_t mp = a.paths[u];
+        const int j[4] = {j4.x, j4.y, j4.z, j4.w};
+        const float x[4] = {x4.x, x4.y, x4.z, x4.w};
+        float y[kCand];
+#pragma unroll
+        for (int aa = 0; aa < kSmax; ++aa) {
+            const float4 yi =
+                *reinterpret_cast<const float4*>(a.u.w2 + ((size_t)u + (j[aa] - i) * hkv) * 4);
+            y[aa * 4 + 0] = yi.x; y[aa * 4 + 1] = yi.y; y[aa * 4 + 2] = yi.z; y[aa * 4 + 3] = yi.w;
+        }
+        float gt[kSmax];
+        if constexpr (S1 == 4) {
+            const float4 g4 = *reinterpret_cast<const float4*>(a.dw_out + (size_t)u * 4);
+            gt[0] = g4.x; gt[1] = g4.y; gt[2] = g4.z; gt[3] = g4.w;
+        } else {
+            const float2 g2 = *reinterpret_cast<const float2*>(a.dw_out + (size_t)u * 2);
+            gt[0] = g2.x; gt[1] = g2.y; gt[2] = 0.0f; gt[3] = 0.0f;
+        }
+        double pg[kCand];
+#pragma unroll
+        for (int k = 0; k < kCand; ++k) {
+            const uint32_t sl = (uint32_t)(mp >> (4 * k)) & 0xFu;
+            float g = 0.0f;
+#pragma unroll
+            for (int t = 0; t < kSmax; ++t) g = sl == (uint32_t)t ? gt[t] : g;
+            pg[k] = sl != kNoSlot ? 0.0 + (double)g : 0.0;
+        }
+        ser_part_accumulate(a, acc, i, u, j, x, y, pg);
+    } else if (i < thi) {
         const int u = (b * n + i) * hkv + h;
         int m[kCand];
         float x[kSmax], y[kCand];
@@ -659,32 +771,7 @@ __global__ __launch_bounds__(kSerThreads) void ser_bwd_part_kernel(SerPartArgs a
 #pragma unroll
         for (int k = 0; k < kCand; ++k)
             pg[k] = x[k / kSmax] > 0.0f && y[k] > 0.0f ? path_grad(m[k], mt, wt, gt) : 0.0;
-        // own row: dw1[i, a] = sum_c g(a, c) w2[j_a, c]
-        double d1[kSmax];
-#pragma unroll
-        for (int aa = 0; aa < kSmax; ++aa) {
-            d1[aa] = 0.0;
-#pragma unroll
-            for (int cc = 0; cc < kSmax; ++cc)
-                d1[aa] += pg[aa * kSmax + cc] * (double)y[aa * kSmax + cc];
-        }
-        if (a.aliased) {
-#pragma unroll
-            for (int aa = 0; aa < kSmax; ++aa)
-                if (d1[aa] != 0.0) atomicAdd(acc + i * 4 + aa, d1[aa]);
-        } else {
-            *reinterpret_cast<float4*>(a.dw1 + (size_t)u * 4) =
-                make_float4((float)d1[0], (float)d1[1], (float)d1[2], (float)d1[3]);
-        }
-        // leg-2 slots of the target rows: dw2[j_a, c] += g(a, c) w1[i, a]
-#pragma unroll
-        for (int aa = 0; aa < kSmax; ++aa) {
-#pragma unroll
-            for (int cc = 0; cc < kSmax; ++cc) {
-                const double g = pg[aa * kSmax + cc];
-                if (g != 0.0) atomicAdd(acc + j[aa] * 4 + cc, g * (double)x[aa]);
-            }
-        }
+        ser_part_accumulate(a, acc, i, u, j, x, y, pg);
     }
     __syncthreads();
     double* dst = a.part + (part_row_off(n, a.nch) * pair + part_row_off(n, c)) * 4;
@@ -865,7 +952,8 @@ hipError_t launch_zero_f64(double* p, size_t count, hipStream_t st) {
 
 hipError_t launch_ser_forward(int B, int n, int hkv, const int32_t* idx1, const float* w1,
                               int s2, const int32_t* idx2, const float* w2, int s3,
-                              int32_t* idx_out, float* w_out, int s1, hipStream_t st) {
+                              int32_t* idx_out, float* w_out, int s1, uint64_t* paths,
+                              hipStream_t st) {
     if (s2 <= kSmax && s3 <= kSmax) {
         SerUnitArgs u{idx1, w1, idx2, w2, idx_out, w_out, nullptr, nullptr, nullptr,
                       n, hkv, s1, s2, s3, B * n * hkv,
@@ -874,13 +962,20 @@ hipError_t launch_ser_forward(int B, int n, int hkv, const int32_t* idx1, const 
                       s2 == 4 && s3 == 4 &&
                           (((uintptr_t)idx1 | (uintptr_t)w1 | (uintptr_t)idx2 | (uintptr_t)w2) &
                            15) == 0};
+        u.paths = s1 <= kSmax ? paths : nullptr;
         const bool out8 = (((uintptr_t)idx_out | (uintptr_t)w_out) & 7) == 0;
-        if (s1 == 4 && u.vec_out && u.vec_in)
-            hipLaunchKernelGGL(ser_fwd_vec_kernel<4>, dim3(xcd_unit_grid(u.U)), dim3(kBlock), 0,
-                               st, u);
-        else if (s1 == 2 && out8 && u.vec_in)
-            hipLaunchKernelGGL(ser_fwd_vec_kernel<2>, dim3(xcd_unit_grid(u.U)), dim3(kBlock), 0,
-                               st, u);
+        const dim3 grid(xcd_unit_grid(u.U));
+        if (s1 == 4 && u.vec_out && u.vec_in) {
+            if (u.paths)
+                hipLaunchKernelGGL((ser_fwd_vec_kernel<4, true>), grid, dim3(kBlock), 0, st, u);
+            else
+                hipLaunchKernelGGL((ser_fwd_vec_kernel<4, false>), grid, dim3(kBlock), 0, st, u);
+        } else if (s1 == 2 && out8 && u.vec_in) {
+            if (u.paths)
+                hipLaunchKernelGGL((ser_fwd_vec_kernel<2, true>), grid, dim3(kBlock), 0, st, u);
+            else
+                hipLaunchKernelGGL((ser_fwd_vec_kernel<2, false>), grid, dim3(kBlock), 0, st, u);
+        }
         else
             hipLaunchKernelGGL(ser_fwd_unit_kernel, dim3(xcd_unit_grid(u.U)), dim3(kBlock), 0, st,
                                u);
@@ -902,8 +997,8 @@ hipError_t launch_ser_forward(int B, int n, int hkv, const int32_t* idx1, const 
 hipError_t launch_ser_backward(int B, int n, int hkv, const int32_t* idx1, const float* w1,
                                int s2, const int32_t* idx2, const float* w2, int s3,
                                const int32_t* idx_out, const float* w_out, int s1,
-                               const float* dw_out, float* dw1, float* dw2, double* ws1,
-                               double* ws2, hipStream_t st) {
+                               const float* dw_out, const uint64_t* paths, float* dw1,
+                               float* dw2, double* ws1, double* ws2, hipStream_t st) {
     const size_t rows = (size_t)B * n * hkv;
     const bool aliased = dw1 == dw2;
     // the source-chunk path: legs of 4 slots, A' of 4 or 2, vector-aligned rows
@@ -918,6 +1013,7 @@ hipError_t launch_ser_backward(int B, int n, int hkv, const int32_t* idx1, const
                            n, hkv, s1, s2, s3, (int)rows,
                            make_fastdiv((uint32_t)hkv), make_fastdiv((uint32_t)n), 1, 1};
         pa.idx_out = idx_out; pa.w_out = w_out; pa.dw_out = dw_out;
+        pa.paths = paths;
         pa.dw1 = dw1; pa.dw2 = dw2;
         pa.part = ws1;
         pa.nch = (n + kSerThreads - 1) / kSerThreads;

@@ -127,14 +127,20 @@ class Inputs:
 
 def run_gpu(inp: Inputs, stats: bool = False):
     """One pass of the path on the GPU; returns device tensors by name.  With
-    ``stats`` the forward saves its p / w statistics and the backward uses
-    them."""
+    ``stats`` the forward saves its p / w statistics and the SER path map, and
+    the backward uses them."""
     p = inp.p
     out = {}
     idx, w = dev(inp.idx), dev(inp.w)
     q, k, v = dev(inp.q), dev(inp.k), dev(inp.v)
+    paths = None
     if p.ser:
-        ia, wa = gm.ser_forward(idx, w, idx, w, p.s1)
+        # with saved state (stats) the forward also writes the path map for
+        # the SER backward, as the measured pass does
+        if stats and max(p.s1, p.s2, p.s3) <= 4:
+            ia, wa, paths = gm.ser_forward(idx, w, idx, w, p.s1, save_paths=True)
+        else:
+            ia, wa = gm.ser_forward(idx, w, idx, w, p.s1)
         out["idx"], out["w"] = ia, wa
     else:
         ia, wa = idx, w
@@ -149,7 +155,7 @@ def run_gpu(inp: Inputs, stats: bool = False):
         dq, dk, dv, dw = gm.sea_backward(q, k, v, ia, wa, do, stats=st)
         out.update(dq=dq, dk=dk, dv=dv, dwp=dw)
         if p.ser:
-            dA, _ = gm.ser_backward(idx, w, idx, w, ia, wa, dw, aliased=True)
+            dA, _ = gm.ser_backward(idx, w, idx, w, ia, wa, dw, aliased=True, paths=paths)
             out["dA"] = dA
     torch.cuda.synchronize()
     return out

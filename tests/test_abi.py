@@ -35,7 +35,7 @@ def test_library_exports_every_declared_call(lib):
     assert set(names) == set(binding.EXPORTS)
     for name in names:
         assert hasattr(lib, name), name
-    assert lib.gm_abi_version() == 6
+    assert lib.gm_abi_version() == 7
 
 
 def test_status_strings(lib):
@@ -56,17 +56,22 @@ def fake(addr):
 def test_ser_forward_argument_checks(lib):
     a = fake(0x10000)
     f = lib.gm_ser_forward
-    assert f(-1, 4, 1, a, a, 2, a, a, 2, a, a, 2, None) == SHAPE
-    assert f(1, 4, 1, a, a, 2, a, a, 2, a, a, 0, None) == UNSUP       # s1 = 0
-    assert f(1, 4, 1, a, a, 9, a, a, 8, a, a, 4, None) == UNSUP       # 72 candidates
-    assert f(1, 4, 1, a, a, 2, a, a, 2, a, a, 65, None) == UNSUP
-    assert f(1, 4, 1, None, a, 2, a, a, 2, a, a, 2, None) == NULL
+    assert f(-1, 4, 1, a, a, 2, a, a, 2, a, a, 2, None, None) == SHAPE
+    assert f(1, 4, 1, a, a, 2, a, a, 2, a, a, 0, None, None) == UNSUP       # s1 = 0
+    assert f(1, 4, 1, a, a, 9, a, a, 8, a, a, 4, None, None) == UNSUP       # 72 candidates
+    assert f(1, 4, 1, a, a, 2, a, a, 2, a, a, 65, None, None) == UNSUP
+    assert f(1, 4, 1, None, a, 2, a, a, 2, a, a, 2, None, None) == NULL
     assert f(1, 4, 1, fake(0x10002), a, 2, a, a, 2, fake(0x20000), fake(0x30000), 2,
-             None) == ALIGN
+             None, None) == ALIGN
     assert f(1, 4, 1, a, fake(0x40000), 2, a, fake(0x40000), 2, a, fake(0x50000), 2,
-             None) == ALIAS                                           # idx_out on idx1
-    assert f(0, 4, 1, None, None, 2, None, None, 2, None, None, 2, None) == OK  # empty
-    assert f(70000, 70000, 1, a, a, 2, a, a, 2, a, a, 2, None) == SHAPE  # > 2^31 units
+             None, None) == ALIAS                                           # idx_out on idx1
+    assert f(0, 4, 1, None, None, 2, None, None, 2, None, None, 2, None, None) == OK  # empty
+    assert f(70000, 70000, 1, a, a, 2, a, a, 2, a, a, 2, None, None) == SHAPE  # > 2^31 units
+    far = [fake(k << 32) for k in range(1, 8)]
+    assert f(1, 4, 1, *far[:2], 4, *far[2:4], 8, *far[4:6], 4, far[6], None) == UNSUP  # paths: s3 > 4
+    assert f(1, 4, 1, *far[:2], 4, *far[2:4], 4, *far[4:6], 4, fake((8 << 32) + 4),
+             None) == ALIGN                                           # paths 8-byte aligned
+    assert f(1, 4, 1, *far[:2], 4, *far[2:4], 4, *far[4:6], 4, far[0], None) == ALIAS
 
 
 def test_sea_argument_checks(lib):
@@ -183,13 +188,16 @@ def test_ser_backward_workspace_checks(lib):
     assert lib.gm_ser_backward_workspace_bytes(8, 4096, 8, 4, 4, 0) == need
     ptrs = [fake(0x1000000 * (k + 1)) for k in range(10)]
     args = [8, 4096, 8, ptrs[0], ptrs[1], 4, ptrs[2], ptrs[3], 4, ptrs[4], ptrs[5], 4,
-            ptrs[6], ptrs[7], ptrs[7], ptrs[8], need - 8, None]
+            ptrs[6], None, ptrs[7], ptrs[7], ptrs[8], need - 8, None]
     assert lib.gm_ser_backward(*args) == WS
-    args[16] = need; args[15] = None
+    args[17] = need; args[16] = None
     assert lib.gm_ser_backward(*args) == WS
-    args[15] = fake(0x9000004)
+    args[16] = fake(0x9000004)
     assert lib.gm_ser_backward(*args) == ALIGN
-    args[15] = ptrs[8]
+    args[16] = ptrs[8]
+    args[13] = fake(0xA000004)                 # path map misaligned
+    assert lib.gm_ser_backward(*args) == ALIGN
+    args[13] = ptrs[9]
     args[5] = 2                                # aliased outputs with s2 != s3
     assert lib.gm_ser_backward(*args) == ALIAS
 

@@ -423,3 +423,64 @@ def test_sea_backward_bucketed_index_concentrated_targets():
     for name, g, g2, r in zip(("dq", "dk", "dv", "dw"), first, second, ref):
         assert torch.equal(g, g2), f"{name} differs between two runs"
         assert_close(name, host(g), r, 2e-2)
+
+
+def _host_path_map(idx1, w1, idx2, w2, io, wo):
+    """The path map written out from its definition (numpy, on the oracle's
+    A'): nibble k = 4a + c of unit (b, i, h) is the slot t of A' whose index
+    is path (a, c)'s target, when both leg weights are positive and w'_t > 0,
+    else 15 (also for k beyond the s2 x s3 paths)."""
+    B, n, hkv, s2 = idx1.shape
+    s3, s1 = idx2.shape[-1], io.shape[-1]
+    bb = np.arange(B).reshape(B, 1, 1)
+    hh = np.arange(hkv).reshape(1, 1, hkv)
+    mp = np.full((B, n, hkv), np.uint64(0xFFFFFFFFFFFFFFFF), dtype=np.uint64)   # 15: no path
+    for a in range(s2):
+        j = idx1[..., a]
+        for c in range(s3):
+            m = idx2[bb, j, hh, c]
+            ok = (w1[..., a] > 0) & (w2[bb, j, hh, c] > 0)
+            sl = np.full((B, n, hkv), 15, dtype=np.uint64)
+            for t in range(s1):
+                sl = np.where(ok & (wo[..., t] > 0) & (io[..., t] == m), np.uint64(t), sl)
+            sh = np.uint64(4 * (4 * a + c))
+            mp = (mp & ~(np.uint64(15) << sh)) | (sl << sh)
+    return mp
+
+
+@pytest.mark.parametrize("s1,s2,s3,n,ties", [(4, 4, 4, 2500, False), (2, 4, 4, 1100, True),
+                                             (3, 2, 3, 300, False), (4, 4, 4, 70, True)])
+def test_ser_path_map(s1, s2, s3, n, ties):
+    """The SER forward's path map equals its definition (computed on the
+    host from the oracle's A'), and the SER backward gives bitwise the same
+    gradients with and without it, for separate and aliased legs."""
+    say(f"case SER path map s={s1}/{s2}/{s3} n={n} ties={ties}")
+    rng = np.random.default_rng(6000 + n)
+    B, hkv = 2, 3
+    idx1, w1 = cases.edges(rng, B, n, hkv, s2, pad_frac=0.05, ties=ties, dead_frac=0.05)
+    idx2, w2 = cases.edges(rng, B, n, hkv, s3, pad_frac=0.05, ties=ties, dead_frac=0.05)
+    orc = oracle.get()
+    for legs in ("separate", "aliased"):
+        if legs == "aliased":
+            if s2 != s3:
+                continue
+            idx2, w2 = idx1, w1
+        io, wo, pm = gm.ser_forward(dev(idx1), dev(w1), dev(idx2), dev(w2), s1, save_paths=True)
+        rio, rwo = orc.ser_forward(idx1, w1, idx2, w2, s1)
+        assert_ser_match(host(io), host(wo), rio, rwo)
+        ref = _host_path_map(idx1, w1, idx2, w2, rio, rwo)
+        got = pm.cpu().numpy().view(np.uint64)
+        assert np.array_equal(got, ref), f"path map differs ({legs} legs)"
+        dwo = dev(rng.standard_normal(rio.shape).astype(np.float32))
+        al = legs == "aliased"
+        with_map = gm.ser_backward(dev(idx1), dev(w1), dev(idx2), dev(w2), io, wo, dwo,
+                                   aliased=al, paths=pm)
+        without = gm.ser_backward(dev(idx1), dev(w1), dev(idx2), dev(w2), io, wo, dwo,
+                                  aliased=al)
+        torch.cuda.synchronize()
+        for a_, b_ in zip(with_map, without):
+            assert torch.equal(a_, b_), f"SER backward with the path map differs ({legs} legs)"
+        r1, r2 = orc.ser_backward(idx1, w1, idx2, w2, rio, rwo, host(dwo), aliased=al)
+        assert_close(f"dw1 ({legs}, path map)", host(with_map[0]), r1, 1e-5)
+        if not al:
+            assert_close("dw2 (path map)", host(with_map[1]), r2, 1e-5)

@@ -88,8 +88,14 @@ def test_fused_shapes(B, n, hkv, G, d, s1, s2, s3, dtype, ties, pad):
     k = torch.from_numpy(rng.standard_normal((B, n, hkv, d), dtype=np.float32)).to(dtype)
     v = torch.from_numpy(rng.standard_normal((B, n, hkv, d), dtype=np.float32)).to(dtype)
     args = [dev(x) for x in (idx1, w1, idx2, w2)]
-    fused = gm.ser_sea_forward(*args, s1, dev(q), dev(k), dev(v), save_stats=True)
+    with_paths = max(s1, s2, s3) <= 4
+    fused = gm.ser_sea_forward(*args, s1, dev(q), dev(k), dev(v), save_stats=True,
+                               save_paths=with_paths)
     ref = _two_calls(*args, s1, dev(q), dev(k), dev(v))
+    if with_paths:
+        # the path map as gm_ser_forward writes it
+        assert torch.equal(fused[4], gm.ser_forward(*args, s1, save_paths=True)[2])
+        fused = fused[:4]
     again = gm.ser_sea_forward(*args, s1, dev(q), dev(k), dev(v), save_stats=True)
     torch.cuda.synchronize()
     _check_equal(fused, ref)

@@ -46,24 +46,26 @@ class LayerPass:
         self.dv = torch.empty(ks, **f32)
         self.dwa = torch.empty(idx.shape, **f32)
         self.dA = torch.empty(idx.shape, **f32)
+        self.paths = torch.empty(idx.shape[:3], dtype=torch.int64, device="cuda")
         self.ws_sea = gm.sea_workspace(self.q, self.ia)
         self.ws_ser = gm.ser_workspace(self.idx, self.idx, aliased=True)
 
     def outputs(self):
-        return {"ia": self.ia, "wa": self.wa, "o": self.o, "stats": self.stats, "dq": self.dq,
+        return {"ia": self.ia, "wa": self.wa, "paths": self.paths, "o": self.o,
+                "stats": self.stats, "dq": self.dq,
                 "dk": self.dk, "dv": self.dv, "dwa": self.dwa, "dA": self.dA}
 
     def run(self):
-        gm.gm_ser_forward(self.idx, self.w, self.idx, self.w, self.ia, self.wa)
+        gm.gm_ser_forward(self.idx, self.w, self.idx, self.w, self.ia, self.wa, paths=self.paths)
         gm.gm_sea_forward(self.q, self.k, self.v, self.ia, self.wa, self.o, stats=self.stats)
         gm.gm_sea_backward(self.q, self.k, self.v, self.ia, self.wa, self.dout, self.dq, self.dk,
                            self.dv, self.dwa, self.ws_sea, stats=self.stats)
         gm.gm_ser_backward(self.idx, self.w, self.idx, self.w, self.ia, self.wa, self.dwa,
-                           self.dA, self.dA, self.ws_ser)
+                           self.dA, self.dA, self.ws_ser, paths=self.paths)
 
     def poison(self):
         for t in self.outputs().values():
-            if t.dtype == torch.int32:
+            if t.dtype in (torch.int32, torch.int64):
                 t.fill_(-7)
             else:
                 t.fill_(float("nan"))
