@@ -445,6 +445,45 @@ __global__ __launch_bounds__(kBlock, MAP ? 4 : 1) void ser_fwd_vec_kernel(SerUni
 __global__ __launch_bounds__(kBlock) void ser_bwd_unit_kernel(SerUnitArgs a) {
     const int u = blockIdx.x * kBlock + threadIdx.x;
     if (u >= a.U) return;
+    if (a.paths && a.vec_in) {
+        // with the forward's path map (s2 = s3 = 4): the leg-1 row, the map,
+        // the leg-2 weights and dw' are enough; the same fp64 terms as below
+        const int i = token_of(u, a);
+        const int4 j4 = *reinterpret_cast<const int4*>(a.idx1 + (size_t)u * 4);
+        const float4 x4 = *reinterpret_cast<const float4*>(a.w1 + (size_t)u * 4);
+        const uint64_t mp = a.paths[u];
+        const int j[4] = {j4.x, j4.y, j4.z, j4.w};
+        const float x[4] = {x4.x, x4.y, x4.z, x4.w};
+        float gt[kSmax];
+#pragma unroll
+        for (int t = 0; t < kSmax; ++t) gt[t] = t < a.s1 ? a.dw_out[(size_t)u * a.s1 + t] : 0.0f;
+        float y[kCand];
+        int r2[kSmax];
+#pragma unroll
+        for (int aa = 0; aa < kSmax; ++aa) {
+            r2[aa] = u + (j[aa] - i) * a.hkv;
+            const float4 yi = *reinterpret_cast<const float4*>(a.w2 + (size_t)r2[aa] * 4);
+            y[aa * 4 + 0] = yi.x; y[aa * 4 + 1] = yi.y; y[aa * 4 + 2] = yi.z; y[aa * 4 + 3] = yi.w;
+        }
+        // the terms in the order of the path below: slot t, then path k
+        double d1[kSmax];
+#pragma unroll
+        for (int aa = 0; aa < kSmax; ++aa) d1[aa] = 0.0;
+#pragma unroll
+        for (int t = 0; t < kSmax; ++t) {
+            const double g = (double)gt[t];
+#pragma unroll
+            for (int k = 0; k < kCand; ++k) {
+                if (((uint32_t)(mp >> (4 * k)) & 0xFu) != (uint32_t)t) continue;
+                const int aa = k / kSmax;
+                d1[aa] += g * (double)y[k];
+                unsafeAtomicAdd(a.ws2 + (size_t)r2[aa] * a.s3 + (k % kSmax), g * (double)x[aa]);
+            }
+        }
+#pragma unroll
+        for (int aa = 0; aa < kSmax; ++aa) a.ws1[(size_t)u * a.s2 + aa] = d1[aa];
+        return;
+    }
     int m[kCand];
     float x[kSmax], y[kCand];
     int r2[kSmax];
@@ -1064,6 +1103,7 @@ hipError_t launch_ser_backward(int B, int n, int hkv, const int32_t* idx1, const
                       s2 == 4 && s3 == 4 &&
                           (((uintptr_t)idx1 | (uintptr_t)w1 | (uintptr_t)idx2 | (uintptr_t)w2) &
                            15) == 0};
+        u.paths = const_cast<uint64_t*>(paths);
         hipLaunchKernelGGL(ser_bwd_unit_kernel, dim3((unsigned)((rows + kBlock - 1) / kBlock)),
                            dim3(kBlock), 0, st, u);
         hipLaunchKernelGGL(ser_bwd_finish_kernel, dim3(grid_for(rows * s2, 8192)), dim3(kBlock), 0,

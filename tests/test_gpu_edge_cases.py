@@ -449,11 +449,14 @@ def _host_path_map(idx1, w1, idx2, w2, io, wo):
 
 
 @pytest.mark.parametrize("s1,s2,s3,n,ties", [(4, 4, 4, 2500, False), (2, 4, 4, 1100, True),
-                                             (3, 2, 3, 300, False), (4, 4, 4, 70, True)])
+                                             (3, 2, 3, 300, False), (4, 4, 4, 70, True),
+                                             (4, 4, 4, 5000, False)])
 def test_ser_path_map(s1, s2, s3, n, ties):
     """The SER forward's path map equals its definition (computed on the
-    host from the oracle's A'), and the SER backward gives bitwise the same
-    gradients with and without it, for separate and aliased legs."""
+    host from the oracle's A'), and the SER backward gives the same
+    gradients with and without it, for separate and aliased legs: bitwise
+    on the source-chunk path (n <= 4096), within rounding on the fp64-atomic
+    path beyond (its atomics add in an order that varies)."""
     say(f"case SER path map s={s1}/{s2}/{s3} n={n} ties={ties}")
     rng = np.random.default_rng(6000 + n)
     B, hkv = 2, 3
@@ -479,7 +482,10 @@ def test_ser_path_map(s1, s2, s3, n, ties):
                                   aliased=al)
         torch.cuda.synchronize()
         for a_, b_ in zip(with_map, without):
-            assert torch.equal(a_, b_), f"SER backward with the path map differs ({legs} legs)"
+            if n <= 4096:
+                assert torch.equal(a_, b_), f"SER backward with the path map differs ({legs} legs)"
+            else:
+                assert torch.allclose(a_, b_, rtol=1e-6, atol=1e-7), f"{legs} legs"
         r1, r2 = orc.ser_backward(idx1, w1, idx2, w2, rio, rwo, host(dwo), aliased=al)
         assert_close(f"dw1 ({legs}, path map)", host(with_map[0]), r1, 1e-5)
         if not al:
