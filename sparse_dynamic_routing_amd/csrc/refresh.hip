@@ -16,28 +16,31 @@
 // the four lanes l%16 + 16c (two swaps) instead of over sixteen.
 //
 // A workgroup of 8 wavefronts takes 128 or 256 consecutive tokens of one
-// (batch, KV head): each wavefront RT 16-token tiles (two when G * d <= 256
-// and G <= 2, else one) for all G query heads, with its query rows held as
-// B-fragments in registers.  Key tiles of 64 rows are staged in LDS (rows
-// padded by 16 bytes against bank conflicts), shared by the eight
-// wavefronts, the next tile's global loads in flight while the current one
-// is used; the more tokens a workgroup covers, the fewer times each key row
-// is fetched (the keys of a pair are re-read once per later token tile).
-// The kernels are held to 128 registers (four wavefronts per SIMD): the
-// vector work of one wavefront then overlaps the matrix work of another,
-// which measured worth more than the few spilled registers it costs.
-// Workgroups are issued heaviest first (the last token tiles see the most
-// keys), consecutive workgroups on different (batch, KV head) pairs so one
-// XCD keeps a fixed set of pairs.
+// (batch, KV head): each wavefront RT 16-token tiles for all G query heads,
+// with its query rows held as B-fragments in registers (two tiles in the lse
+// pass when G * d <= 256 and G <= 2, one in the selection pass, whose top
+// lists need the registers).  Key tiles of 64 rows are brought into LDS by
+// direct global->LDS loads (no registers in between), double-buffered so
+// the next tile's loads are in flight while the current one is used; the
+// 16-byte pieces of a row are XOR-swizzled with the row index so that the
+// sixteen rows of a fragment load fall on different banks.  The more tokens
+// a workgroup covers, the fewer times each key row is fetched (the keys of
+// a pair are re-read once per later token tile).  The kernels are held to
+// 128 registers (four wavefronts per SIMD): the vector work of one
+// wavefront then overlaps the matrix work of another.  Workgroups are
+// issued heaviest first (the last token tiles see the most keys),
+// consecutive workgroups on different (batch, KV head) pairs so one XCD
+// keeps a fixed set of pairs.
 //
 // Two passes: the first keeps an online max/sum per (token, head) in base 2
-// (rescaled only when a maximum passes the reference by a factor 2^16, a wavefront-
-// uniform branch that is rarely taken) and writes lse (skipped when the caller
-// passes the dense layer's own lse); the second recomputes the scores, forms
-// pbar and keeps the top list.  The four lanes of a token share, after
-// every 16 keys, the largest of their S-th kept values: a later key at or
-// below it already has S positions ahead of it, so it is dropped without
-// touching the list.
+// (rescaled only when a term would pass 2^16, a wavefront-uniform branch
+// that is rarely taken) and writes lse (skipped when the caller passes the
+// dense layer's own lse); the second recomputes the scores, forms pbar and
+// keeps, per lane, a sorted top list of its own keys.  After every key tile
+// the four lanes of a token find the S-th largest value they hold together
+// (two bitonic merges across lanes): a later key at or below it already
+// has S positions ahead of it and is dropped without touching a list; the
+// rest enter by a branch-free insertion.
 #include "gm_common.h"
 #include "gm_internal.h"
 #include "gm_wave.h"
@@ -51,6 +54,7 @@ typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
 constexpr int kRefKeys = 64;     // keys per LDS tile
+constexpr int kRefWaves = 8;     // wavefronts per workgroup
 constexpr int kRefSmax = 8;      // kept positions per token, at most
 constexpr float kLog2e = 1.4426950408889634f;
 
@@ -74,15 +78,41 @@ __device__ __forceinline__ float max4(float a, float b, float c, float d) {
 }
 constexpr float kSlack = 16.0f;
 
-// the largest of x over the four rows of the wavefront (lanes l%16 + 16c)
-__device__ __forceinline__ float max_over_rows(float x) {
-    float a = x, b = x;
-    swap16(a, b);
-    x = fmaxf(a, b);
-    a = x;
-    b = x;
-    swap32(a, b);
-    return fmaxf(a, b);
+// The S-th largest value over the four lanes of a token (lanes l%16 + 16c,
+// c = grp), each holding S values sorted in descending order.  For two
+// sorted lists a and b, max(a_i, b_{S-1-i}) over i is the set of the S
+// largest of both (bitonic); sorted by a bitonic merge it pairs again with
+// the other pair's set, and the smallest of those S maxima is the answer.
+template <int S>
+__device__ __forceinline__ float union_kth(const float (&v)[S], int grp) {
+    const bool odd16 = (grp & 1) != 0, odd32 = grp >= 2;
+    float c[S];
+#pragma unroll
+    for (int i = 0; i < S; ++i) {
+        // a permlane16 swap of (x, y) hands odd rows the even rows' y and
+        // even rows the odd rows' x: both hold v_{S-1-i}, the partner's
+        float x = v[S - 1 - i], y = v[S - 1 - i];
+        swap16(x, y);
+        c[i] = fmaxf(v[i], odd16 ? x : y);
+    }
+#pragma unroll
+    for (int k = S / 2; k >= 1; k /= 2)
+#pragma unroll
+        for (int i = 0; i < S; ++i)
+            if ((i & k) == 0) {
+                const float hi = fmaxf(c[i], c[i + k]), lo = fminf(c[i], c[i + k]);
+                c[i] = hi;
+                c[i + k] = lo;
+            }
+    float m = 0.0f;
+#pragma unroll
+    for (int i = 0; i < S; ++i) {
+        float x = c[S - 1 - i], y = c[S - 1 - i];
+        swap32(x, y);
+        const float d = fmaxf(c[i], odd32 ? x : y);
+        m = i == 0 ? d : fminf(m, d);
+    }
+    return m;
 }
 
 __device__ __forceinline__ bf16x8_t as_frag(const uint4& u) {
@@ -99,20 +129,25 @@ struct TopS {
 __device__ __forceinline__ bool ahead(float va, int ja, float vb, int jb) {
     return va > vb || (va == vb && ja < jb);
 }
-// insert (v, j) where j exceeds every position already held: an equal value
-// stays behind, so only a strictly larger one enters
+// insert (v, j) where j exceeds every position already held, without
+// branches: ge[e] (entry e stays ahead: larger, or equal and earlier) is
+// true below the insertion point and false from it on, so each entry either
+// stays, takes the new pair or takes its predecessor; v at or below the last
+// entry changes nothing
 template <int S>
 __device__ __forceinline__ void insert_later(TopS<S>& t, float v, int j) {
-    if (!(v > t.v[S - 1])) return;
-    t.v[S - 1] = v;
-    t.j[S - 1] = j;
+    bool ge[S];
+#pragma unroll
+    for (int e = 0; e < S; ++e) ge[e] = t.v[e] >= v;
 #pragma unroll
     for (int e = S - 1; e > 0; --e) {
-        if (t.v[e] > t.v[e - 1]) {
-            const float tv = t.v[e]; t.v[e] = t.v[e - 1]; t.v[e - 1] = tv;
-            const int tj = t.j[e]; t.j[e] = t.j[e - 1]; t.j[e - 1] = tj;
-        }
+        const float nv = ge[e - 1] ? (ge[e] ? t.v[e] : v) : t.v[e - 1];
+        const int nj = ge[e - 1] ? (ge[e] ? t.j[e] : j) : t.j[e - 1];
+        t.v[e] = nv;
+        t.j[e] = nj;
     }
+    t.v[0] = ge[0] ? t.v[0] : v;
+    t.j[0] = ge[0] ? t.j[0] : j;
 }
 // merge two sorted lists over disjoint positions, keeping the first S
 template <int S>
@@ -138,27 +173,58 @@ __device__ __forceinline__ TopS<S> merge(const TopS<S>& a, const TopS<S>& b) {
     return r;
 }
 
-// 16-token tiles per wavefront: as many as keep the query fragments within
-// 128 registers (RT * G * d / 8 of them)
-constexpr int ref_rt(int D, int G) { return G <= 2 && G * D <= 256 ? 2 : 1; }
-constexpr int kRefWaves = 8;     // wavefronts per workgroup
-constexpr int ref_tokens(int D, int G) { return kRefWaves * 16 * ref_rt(D, G); }
+// LDS slot of the 16-byte piece p of key row r in a tile: rows of D / 8
+// pieces, the piece index XORed with the row, so the sixteen rows that one
+// fragment load reads (same p) sit on sixteen different bank groups
+template <int D>
+__device__ __forceinline__ int key_slot(int r, int p) {
+    constexpr int PPR = D / 8;
+    return r * PPR + (p ^ (r & (PPR - 1)));
+}
+
+// Direct global->LDS loads of a tile of kRefKeys key rows from position j0
+// (rows past n - 1 repeat row n - 1; their scores are masked).  Each
+// wavefront instruction fills 64 consecutive 16-byte slots, lane l slot l,
+// so every lane fetches the piece that belongs at its slot.
+template <int D>
+__device__ __forceinline__ void load_key_tile(uint4* buf, const bf16_t* kbase, size_t kstride,
+                                              int j0, int n, int wv, int lane) {
+    constexpr int PPR = D / 8;
+    constexpr int SLOTS = kRefKeys * PPR;
+    constexpr int U = SLOTS / (kRefWaves * kWave);   // instructions per wavefront
+    static_assert(U >= 1 && U * kRefWaves * kWave == SLOTS, "tile slots must divide evenly");
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        const int base = (u * kRefWaves + wv) * kWave;   // first slot of the instruction
+        const int slot = base + lane;
+        const int row = slot / PPR;
+        const int piece = (slot % PPR) ^ (row & (PPR - 1));
+        const int j = j0 + row < n ? j0 + row : n - 1;
+        __builtin_amdgcn_global_load_lds(
+            kbase + (size_t)j * kstride + piece * 8,
+            (__attribute__((address_space(3))) void*)(buf + base), 16, 0, 0);
+    }
+}
+
+// 16-token tiles per wavefront: two for the lse pass when the query
+// fragments (RT * G * d / 8 registers) leave room; one for the selection
+// pass, whose top lists and insertion need the registers
+constexpr int ref_rt(int MODE, int D, int G) {
+    return MODE == 0 && G <= 2 && G * D <= 256 ? 2 : 1;
+}
+constexpr int ref_tokens(int MODE, int D, int G) { return kRefWaves * 16 * ref_rt(MODE, D, G); }
 
 // MODE 0: lse; MODE 1: the top-S refresh edges.  D head dim, G query heads
 // per KV head.
 template <int MODE, int D, int G, int S>
 __global__ __launch_bounds__(kRefWaves * kWave, 4) void refresh_kernel(RefreshArgs a) {
-    constexpr int RT = ref_rt(D, G);              // 16-token tiles per wavefront
-    constexpr int NT = kRefWaves * kWave;         // threads
+    constexpr int RT = ref_rt(MODE, D, G);        // 16-token tiles per wavefront
     constexpr int TW = 16 * RT;                   // tokens per wavefront
     constexpr int KS = D / 32;                    // MFMA k-steps over d
-    constexpr int ROWB = D * 2 + 16;              // padded LDS row bytes
-    constexpr int PPR = D / 8;                    // 16-byte pieces per key row
-    constexpr int U = kRefKeys * PPR / NT;        // pieces per thread per tile
-    static_assert(U >= 1 && U * NT == kRefKeys * PPR, "tile pieces must divide evenly");
-    __shared__ __attribute__((aligned(16))) unsigned char kt[kRefKeys * ROWB];
+    __shared__ __attribute__((aligned(16))) uint4 kt[2][kRefKeys * D / 8];
     const int lane = (int)(threadIdx.x & (kWave - 1));
-    const int wv = (int)threadIdx.x / kWave;
+    // wavefront index, scalar: every per-wavefront bound below is uniform
+    const int wv = __builtin_amdgcn_readfirstlane((int)threadIdx.x / kWave);
     const int pair = (int)blockIdx.x % a.npair;
     const int tile = a.ntile - 1 - (int)blockIdx.x / a.npair;   // heaviest first
     const int b = pair / a.hkv, h = pair - (pair / a.hkv) * a.hkv;
@@ -184,9 +250,9 @@ __global__ __launch_bounds__(kRefWaves * kWave, 4) void refresh_kernel(RefreshAr
     }
     float m2[RT][G], z[RT][G];     // MODE 0: running max / sum, base 2
     float ls2[RT][G];             // MODE 1: the token's lse + log(G), base 2
+    TopS<S> top[RT];             // MODE 1: this lane's sorted top list
+    float thr[RT];               // MODE 1: the token's S-th value at the last tile
     const float log2g = G == 1 ? 0.0f : G == 2 ? 1.0f : G == 4 ? 2.0f : 3.0f;
-    TopS<S> top[RT];
-    float thr[RT];               // MODE 1: drop candidates at or below this
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt) {
         const int tok = t0 + 16 * rt + col;
@@ -200,67 +266,56 @@ __global__ __launch_bounds__(kRefWaves * kWave, 4) void refresh_kernel(RefreshAr
                     ls2[rt][g] = fmaf(a.lse[((size_t)b * n + tok) * a.hq + h * G + g], kLog2e,
                                       log2g);
         }
+        thr[rt] = 0.0f;
 #pragma unroll
         for (int e = 0; e < S; ++e) { top[rt].v[e] = 0.0f; top[rt].j[e] = 0x7fffffff; }
-        thr[rt] = 0.0f;
     }
 
-    // this thread's pieces of a key tile: piece p = threadIdx + NT u
+    // key tiles, double-buffered: filled by direct global->LDS loads (no
+    // registers in between), the next tile's loads in flight while the
+    // current one is used
     const bf16_t* kbase = a.k + ((size_t)b * n * a.hkv + h) * D;
     const size_t kstride = (size_t)a.hkv * D;
-    uint4 pf[U];
-    auto fetch = [&](int j0) {
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-            const int p = (int)threadIdx.x + NT * u;
-            const int row = p / PPR, piece = p - (p / PPR) * PPR;
-            const int j = j0 + row < n ? j0 + row : n - 1;
-            pf[u] = *reinterpret_cast<const uint4*>(kbase + (size_t)j * kstride + piece * 8);
-        }
-    };
     const int last = T0 + kRefWaves * TW - 1 < n - 1 ? T0 + kRefWaves * TW - 1 : n - 1;
-    fetch(0);
-    for (int j0 = 0; j0 <= last; j0 += kRefKeys) {
-        __syncthreads();   // every wavefront is done with the previous tile
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-            const int p = (int)threadIdx.x + NT * u;
-            const int row = p / PPR, piece = p - (p / PPR) * PPR;
-            *reinterpret_cast<uint4*>(kt + row * ROWB + piece * 16) = pf[u];
-        }
+    load_key_tile<D>(kt[0], kbase, kstride, 0, n, wv, lane);
+    for (int j0 = 0, buf = 0; j0 <= last; j0 += kRefKeys, buf ^= 1) {
+        // this thread's loads of the tile have landed; after the barrier
+        // every thread's have, and no wavefront still reads the other buffer
+        __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
-        if (j0 + kRefKeys <= last) fetch(j0 + kRefKeys);   // in flight during this tile
+        if (j0 + kRefKeys <= last)
+            load_key_tile<D>(kt[buf ^ 1], kbase, kstride, j0 + kRefKeys, n, wv, lane);
         if (j0 > t0 + TW - 1) continue;   // every key of the tile is after this wavefront's tokens
+        const uint4* cur = kt[buf];
 #pragma unroll
         for (int sub = 0; sub < kRefKeys / 16; ++sub) {
             const int jk = j0 + 16 * sub;
             if (jk > t0 + TW - 1) break;
-            // key A-fragments: lane l holds k[jk + l%16][32 ks + 8(l/16) .. + 8]
-            bf16x8_t kf[KS];
-#pragma unroll
-            for (int ks = 0; ks < KS; ++ks)
-                kf[ks] = as_frag(*reinterpret_cast<const uint4*>(kt + (16 * sub + col) * ROWB +
-                                                                 (32 * ks + 8 * grp) * 2));
+            const int krow = 16 * sub + col;
             const int key0 = jk + 4 * grp;   // this lane's keys key0 + r
-            // every score of the sub-tile first: the matrix cores work through
-            // the later tiles while the vector units take the earlier ones
+            bool liv[RT];                    // token tile rt has a key at or before it here
+#pragma unroll
+            for (int rt = 0; rt < RT; ++rt) liv[rt] = jk <= t0 + 16 * rt + 15;
+            // every score of the sub-tile first (the matrix cores work through
+            // the later tiles while the vector units take the earlier ones),
+            // k-step outermost so one key fragment is live at a time and the
+            // RT * G accumulator chains interleave
             f32x4_t scs[RT][G];
 #pragma unroll
-            for (int rt = 0; rt < RT; ++rt) {
-                if (jk > t0 + 16 * rt + 15) continue;   // all keys after all tokens
+            for (int ks = 0; ks < KS; ++ks) {
+                // key A-fragment: lane l holds k[jk + l%16][32 ks + 8(l/16) .. + 8]
+                const bf16x8_t kf = as_frag(cur[key_slot<D>(krow, 4 * ks + grp)]);
 #pragma unroll
-                for (int g = 0; g < G; ++g) {
-                    f32x4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
+                for (int rt = 0; rt < RT; ++rt)
+                    if (liv[rt])
 #pragma unroll
-                    for (int ks = 0; ks < KS; ++ks)
-                        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[ks], qf[rt][g][ks], acc,
-                                                                      0, 0, 0);
-                    scs[rt][g] = acc;
-                }
+                        for (int g = 0; g < G; ++g)
+                            scs[rt][g] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                                kf, qf[rt][g][ks], ks == 0 ? f32x4_t{0.0f, 0.0f, 0.0f, 0.0f} : scs[rt][g], 0, 0, 0);
             }
 #pragma unroll
             for (int rt = 0; rt < RT; ++rt) {
-                if (jk > t0 + 16 * rt + 15) continue;
+                if (!liv[rt]) continue;
                 const int tok = t0 + 16 * rt + col;
                 const f32x4_t* sc = scs[rt];
                 // keys past the token only in the diagonal tiles: masks there alone
@@ -270,24 +325,33 @@ __global__ __launch_bounds__(kRefWaves * kWave, 4) void refresh_kernel(RefreshAr
 #pragma unroll
                     for (int r = 0; r < 4; ++r) live[r] = !M || key0 + r <= tok;
                     if constexpr (MODE == 0) {
+                        float x[G][4], y[G][4];
+                        float my = -INFINITY;
 #pragma unroll
-                        for (int g = 0; g < G; ++g) {
-                            float x[4];
+                        for (int g = 0; g < G; ++g)
 #pragma unroll
-                            for (int r = 0; r < 4; ++r) x[r] = live[r] ? sc[g][r] : -INFINITY;
-                            const float mx = max4(x[0], x[1], x[2], x[3]) * a.c;
-                            // rescale only when some lane's maximum passes its
-                            // reference by kSlack (terms stay below 2^kSlack):
-                            // rare once a few hundred keys are in
-                            if (__builtin_amdgcn_ballot_w64(mx > m2[rt][g] + kSlack)) {
-                                const float mn = fmaxf(m2[rt][g], mx);
+                            for (int r = 0; r < 4; ++r) {
+                                x[g][r] = live[r] ? sc[g][r] : -INFINITY;
+                                y[g][r] = fmaf(x[g][r], a.c, -m2[rt][g]);
+                                my = fmaxf(my, y[g][r]);
+                            }
+                        // rescale only when some lane's term would pass
+                        // 2^kSlack: rare once a few hundred keys are in
+                        if (__builtin_amdgcn_ballot_w64(my > kSlack)) {
+#pragma unroll
+                            for (int g = 0; g < G; ++g) {
+                                const float mn = fmaxf(
+                                    m2[rt][g], max4(x[g][0], x[g][1], x[g][2], x[g][3]) * a.c);
                                 z[rt][g] *= fexp2(m2[rt][g] - mn);
                                 m2[rt][g] = mn;
+#pragma unroll
+                                for (int r = 0; r < 4; ++r) y[g][r] = fmaf(x[g][r], a.c, -mn);
                             }
-                            const float nm = -m2[rt][g];
-                            z[rt][g] += (fexp2(fmaf(x[0], a.c, nm)) + fexp2(fmaf(x[1], a.c, nm))) +
-                                        (fexp2(fmaf(x[2], a.c, nm)) + fexp2(fmaf(x[3], a.c, nm)));
                         }
+#pragma unroll
+                        for (int g = 0; g < G; ++g)
+                            z[rt][g] += (fexp2(y[g][0]) + fexp2(y[g][1])) +
+                                        (fexp2(y[g][2]) + fexp2(y[g][3]));
                     } else {
                         float pb[4];
 #pragma unroll
@@ -297,11 +361,18 @@ __global__ __launch_bounds__(kRefWaves * kWave, 4) void refresh_kernel(RefreshAr
                             for (int g = 1; g < G; ++g) x += fexp2(fmaf(sc[g][r], a.c, -ls2[rt][g]));
                             pb[r] = live[r] ? x : 0.0f;
                         }
-                        const float mx = max4(pb[0], pb[1], pb[2], pb[3]);
-                        if (mx > thr[rt]) {
+                        // a key enters only past the token's bound and this
+                        // lane's last entry; keys in position order, the
+                        // insertion run by the lanes that need it
+                        float lim = fmaxf(thr[rt], top[rt].v[S - 1]);
+                        if (__builtin_amdgcn_ballot_w64(max4(pb[0], pb[1], pb[2], pb[3]) > lim)) {
 #pragma unroll
-                            for (int r = 0; r < 4; ++r)
-                                insert_later(top[rt], pb[r] > thr[rt] ? pb[r] : 0.0f, key0 + r);
+                            for (int r = 0; r < 4; ++r) {
+                                if (pb[r] > lim) {
+                                    insert_later(top[rt], pb[r], key0 + r);
+                                    lim = fmaxf(thr[rt], top[rt].v[S - 1]);
+                                }
+                            }
                         }
                     }
                 };
@@ -310,13 +381,14 @@ __global__ __launch_bounds__(kRefWaves * kWave, 4) void refresh_kernel(RefreshAr
                 else
                     body(std::false_type{});
             }
-            if constexpr (MODE == 1) {
-                // the token's four lanes each hold S positions, all before this
-                // sub-tile's keys: a later key no larger than the largest of
-                // their S-th values has S positions ahead of it and is dropped
+        }
+        if constexpr (MODE == 1) {
+            // the token's four lanes each hold S positions, all before the
+            // next tile's keys: a later key no larger than the S-th largest
+            // value they hold together has S positions ahead of it and is
+            // dropped
 #pragma unroll
-                for (int rt = 0; rt < RT; ++rt) thr[rt] = max_over_rows(top[rt].v[S - 1]);
-            }
+            for (int rt = 0; rt < RT; ++rt) thr[rt] = union_kth<S>(top[rt].v, grp);
         }
     }
 
@@ -369,17 +441,24 @@ __global__ __launch_bounds__(kRefWaves * kWave, 4) void refresh_kernel(RefreshAr
 
 template <int D, int G>
 hipError_t run_dg(RefreshArgs a, int B, bool lse_given, hipStream_t st) {
-    constexpr int TOK = ref_tokens(D, G);
-    a.ntile = (a.n + TOK - 1) / TOK;
     a.npair = B * a.hkv;
-    const dim3 grid((unsigned)(a.npair * a.ntile)), block(kRefWaves * kWave);
-    if (!lse_given) hipLaunchKernelGGL((refresh_kernel<0, D, G, 1>), grid, block, 0, st, a);
+    const dim3 block(kRefWaves * kWave);
+    auto grid = [&](int mode) {
+        const int tok = mode == 0 ? ref_tokens(0, D, G) : ref_tokens(1, D, G);
+        a.ntile = (a.n + tok - 1) / tok;
+        return dim3((unsigned)(a.npair * a.ntile));
+    };
+    if (!lse_given) {
+        const dim3 g0 = grid(0);
+        hipLaunchKernelGGL((refresh_kernel<0, D, G, 1>), g0, block, 0, st, a);
+    }
+    const dim3 g1 = grid(1);
     if (a.s <= 2)
-        hipLaunchKernelGGL((refresh_kernel<1, D, G, 2>), grid, block, 0, st, a);
+        hipLaunchKernelGGL((refresh_kernel<1, D, G, 2>), g1, block, 0, st, a);
     else if (a.s <= 4)
-        hipLaunchKernelGGL((refresh_kernel<1, D, G, 4>), grid, block, 0, st, a);
+        hipLaunchKernelGGL((refresh_kernel<1, D, G, 4>), g1, block, 0, st, a);
     else
-        hipLaunchKernelGGL((refresh_kernel<1, D, G, kRefSmax>), grid, block, 0, st, a);
+        hipLaunchKernelGGL((refresh_kernel<1, D, G, kRefSmax>), g1, block, 0, st, a);
     return hipGetLastError();
 }
 
