@@ -125,20 +125,18 @@ def stage_bytes(stage: str, p: synth.Preset) -> int:
 def profiled_traffic(call: str):
     """Calibrated HBM bytes per launch of `call` from the committed counter
     summary, or None when it is missing or the kernels changed since."""
-    from sparse_dynamic_routing_amd.profile_summary import source_hash
+    from sparse_dynamic_routing_amd.profile_summary import summary_hash_ok
     if not os.path.exists(PROFILE):
         return None
-    kernels, hsh = {}, None
+    kernels = {}
     for line in open(PROFILE):
         line = line.strip()
-        if line.startswith("source_hash:"):
-            hsh = line.split(":", 1)[1].strip()
-        elif line.startswith("kernel:"):
+        if line.startswith("kernel:"):
             parts = [x.strip() for x in line.split("|")]
             name = parts[0].split(":", 1)[1].strip()
             kv = dict(x.split("=") for x in parts[1:])
             kernels[name] = float(kv["fetch_bytes"]) + float(kv["write_bytes"])
-    if hsh != source_hash():
+    if not summary_hash_ok(PROFILE):
         return None
     total = 0.0
     for name in CALL_KERNELS[call]:
@@ -539,18 +537,16 @@ def run_refresh(a):
 def profiled_step_bytes(config: str):
     """Counter bytes per step from profiles/<config>_kernels.md, or None when
     it is missing or the kernel sources changed since."""
-    from sparse_dynamic_routing_amd.profile_summary import source_hash
+    from sparse_dynamic_routing_amd.profile_summary import summary_hash_ok
     path = os.path.join(ROOT, "profiles", f"{config}_kernels.md")
     if not os.path.exists(path):
         return None
-    hsh, per_step = None, None
+    per_step = None
     for line in open(path):
         line = line.strip()
-        if line.startswith("source_hash:"):
-            hsh = line.split(":", 1)[1].strip()
-        elif line.startswith("bytes_per_step:"):
+        if line.startswith("bytes_per_step:"):
             per_step = float(line.split(":", 1)[1])
-    return per_step if hsh == source_hash() else None
+    return per_step if summary_hash_ok(path) else None
 
 
 def _cpu_model() -> str:

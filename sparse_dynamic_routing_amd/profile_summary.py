@@ -54,17 +54,41 @@ def code_text(src: str) -> str:
     return " ".join("".join(out).split())
 
 
-def source_hash() -> str:
-    """sha256 over the code (comments left out) of the HIP sources and the C
-    header: what the counters measured."""
+# The sources the layer pass's kernels are built from (the C ABI, the
+# shared headers, SER, SEA and the reverse edge index); a summary names the
+# files its hash covers, so work on an unrelated kernel leaves it valid.
+PASS_SOURCES = ["edge_index.hip", "gm_api.hip", "gm_common.h", "gm_internal.h", "gm_select.h",
+                "gm_wave.h", "sea_bwd.hip", "sea_fwd.hip", "ser.hip"]
+
+
+def source_hash(files=None) -> str:
+    """sha256 over the code (comments left out) of the given csrc files (by
+    default every HIP source and header) and the C header: what the counters
+    measured."""
     h = hashlib.sha256()
-    files = sorted(glob.glob(os.path.join(PKG, "csrc", "*"))) + [
-        os.path.join(ROOT, "include", "gm.h")]
-    for f in files:
+    if files is None:
+        paths = sorted(glob.glob(os.path.join(PKG, "csrc", "*")))
+    else:
+        paths = [os.path.join(PKG, "csrc", f) for f in sorted(files)]
+    for f in paths + [os.path.join(ROOT, "include", "gm.h")]:
         h.update(os.path.basename(f).encode())
         with open(f, encoding="utf-8") as fh:
             h.update(code_text(fh.read()).encode())
     return h.hexdigest()[:16]
+
+
+def summary_hash_ok(path: str) -> bool:
+    """True when the summary at `path` carries the hash of the sources it
+    names (or of all sources, for a summary that names none) as they are
+    now."""
+    hsh, files = None, None
+    for line in open(path):
+        line = line.strip()
+        if line.startswith("source_hash:"):
+            hsh = line.split(":", 1)[1].strip()
+        elif line.startswith("source_files:"):
+            files = [f.strip() for f in line.split(":", 1)[1].split(",") if f.strip()]
+    return hsh is not None and hsh == source_hash(files)
 
 
 def short(name: str) -> str:
@@ -82,9 +106,12 @@ def _csv(d: str, suffix: str):
 
 
 def kernel_stats(d: str):
+    """Calls and average microseconds of this library's kernels (those in
+    namespace gm; torch's input draws are left out)."""
     out = {}
     for r in _csv(d, "kernel_stats.csv"):
-        out[short(r["Name"])] = (int(r["Calls"]), float(r["AverageNs"]) / 1000.0)
+        if "gm::" in r["Name"]:
+            out[short(r["Name"])] = (int(r["Calls"]), float(r["AverageNs"]) / 1000.0)
     return out
 
 
@@ -109,12 +136,16 @@ def main():
     ap.add_argument("--workload", default="B=8, n=4096, 16 q / 8 KV heads, d=128, "
                     "s1=s2=s3=4, bf16 activations\n(one SER fwd + SEA fwd + SEA bwd + "
                     "SER bwd per step)")
-    ap.add_argument("--steps-run", type=int, default=7,
-                    help="steps the profiled program ran, warm-up included "
-                         "(to turn launches into launches per step)")
+    ap.add_argument("--sources", default=",".join(PASS_SOURCES),
+                    help="csrc files the measured kernels are built from (comma list)")
+    ap.add_argument("--steps-run", type=int, default=0,
+                    help="passes the profiled program ran (to turn launches into launches "
+                         "per pass); default: the fewest launches of any kernel, every kernel "
+                         "running at least once per pass")
     a = ap.parse_args()
 
     ks = kernel_stats(a.trace)
+    passes = a.steps_run or min(calls for calls, _ in ks.values())
     fetch, write = counter(a.fetch, "FETCH_SIZE"), counter(a.write, "WRITE_SIZE")
     cf, cw = counter(a.copy_fetch, "FETCH_SIZE"), counter(a.copy_write, "WRITE_SIZE")
     copy_bytes = a.copy_mib * (1 << 20)
@@ -140,13 +171,15 @@ def main():
         rows.append((k, calls, us, fb, wb))
         print(f"| {k} | {calls} | {us:.1f} | {fb / 1e6:.1f} | {wb / 1e6:.1f} | {gbs:.0f} |")
     print("\n```")
-    print(f"source_hash: {source_hash()}")
+    files = [f for f in a.sources.split(",") if f]
+    print(f"source_files: {','.join(files)}")
+    print(f"source_hash: {source_hash(files)}")
     print(f"fetch_scale: {f_scale:.6f}")
     print(f"write_scale: {w_scale:.6f}")
     per_step = 0.0
     for k, calls, us, fb, wb in rows:
         print(f"kernel: {k} | us={us:.3f} | fetch_bytes={fb:.0f} | write_bytes={wb:.0f}")
-        per_step += (fb + wb) * calls / a.steps_run
+        per_step += (fb + wb) * calls / passes
     print(f"bytes_per_step: {per_step:.0f}")
     print("```")
 

@@ -48,6 +48,26 @@ def test_committed_profiles_name_their_command_and_sources():
             assert "source_hash:" in text, f
     h = profile_summary.source_hash()
     assert len(h) == 16 and all(c in "0123456789abcdef" for c in h)
+    assert profile_summary.source_hash(profile_summary.PASS_SOURCES) != h
+
+
+def test_summary_hash_names_its_sources(tmp_path):
+    """A summary is valid while the sources it names hash as recorded; a
+    wrong hash, or none, makes it stale."""
+    files = profile_summary.PASS_SOURCES
+    good = tmp_path / "good.md"
+    good.write_text(f"source_files: {','.join(files)}\n"
+                    f"source_hash: {profile_summary.source_hash(files)}\n")
+    assert profile_summary.summary_hash_ok(str(good))
+    bad = tmp_path / "bad.md"
+    bad.write_text(f"source_files: {','.join(files)}\nsource_hash: 0123456789abcdef\n")
+    assert not profile_summary.summary_hash_ok(str(bad))
+    whole = tmp_path / "whole.md"
+    whole.write_text(f"source_hash: {profile_summary.source_hash()}\n")
+    assert profile_summary.summary_hash_ok(str(whole))
+    none = tmp_path / "none.md"
+    none.write_text("nothing here\n")
+    assert not profile_summary.summary_hash_ok(str(none))
 
 
 def test_source_hash_ignores_comments_only():
