@@ -519,6 +519,22 @@ def run_refresh(a):
         torch.cuda.synchronize()
         tf += e[0].elapsed_time(e[1]); ts += e[1].elapsed_time(e[2])
     tf, ts = tf / a.steps, ts / a.steps
+    # the same query width with one query head per KV head (hq = hkv = 16):
+    # G = 1 takes the one-pass kernel (lse and the edges together)
+    k1 = synth.normal(seed, "k", (p.B, p.n, p.hq, p.d), torch.bfloat16, 0, "cuda")
+    io1 = torch.empty((p.B, p.n, p.hq, s), dtype=torch.int32, device="cuda")
+    wo1 = torch.empty((p.B, p.n, p.hq, s), dtype=torch.float32, device="cuda")
+    full1 = lambda: gm.gm_dense_refresh(q, k1, lse, io1, wo1)  # noqa: E731
+    sel1 = lambda: gm.gm_dense_refresh(q, k1, lse, io1, wo1, lse_given=True)  # noqa: E731
+    for _ in range(a.warmup):
+        full1(); sel1()
+    torch.cuda.synchronize()
+    tf1 = ts1 = 0.0
+    for _ in range(a.steps):
+        e[0].record(); full1(); e[1].record(); sel1(); e[2].record()
+        torch.cuda.synchronize()
+        tf1 += e[0].elapsed_time(e[1]); ts1 += e[1].elapsed_time(e[2])
+    tf1, ts1 = tf1 / a.steps, ts1 / a.steps
     pairs = p.B * p.hq * p.n * (p.n + 1) // 2          # causal (token, key, query head)
     flops = 2 * p.d * pairs                            # one score contraction
     print(json.dumps({
@@ -528,6 +544,10 @@ def run_refresh(a):
         "score_flops_per_pass": flops,
         "select_tflops": flops / (ts * 1e-3) / 1e12, "mfma_peak_tflops": PEAK_BF16_TFLOPS,
         "scores_per_s": pairs / (ts * 1e-3),
+        "mha_g1": {"hq": p.hq, "hkv": p.hq, "one_pass_us": tf1 * 1e3,
+                   "select_alone_us": ts1 * 1e3,
+                   "one_pass_tflops": flops / (tf1 * 1e-3) / 1e12,
+                   "how": "G = 1: one launch forms lse and keeps the top scores"},
         "roofline": {"kernel": "refresh_kernel (selection pass)", "bound": "mfma",
                      "achieved": flops / (ts * 1e-3) / 1e12, "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": flops / (ts * 1e-3) / 1e12 / PEAK_BF16_TFLOPS},

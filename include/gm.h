@@ -336,9 +336,11 @@ gm_status gm_decode_step(int B, int T, int hq, int hkv, int d, gm_dtype dt, floa
  * Limits: dt GM_BF16 only; (d, G) in {64: 1,2,4,8; 128: 1,2,4; 256: 1,2};
  * 1 <= s <= 8; scale positive and finite.  q, k 16-byte aligned; lse, idx_out, w_out 4-byte aligned;
  * no output may overlap an input or another output.  Two launches (one with
- * lse_given); no workspace.  Scores are fp32 sums of bf16 products on the
- * matrix cores, so positions whose pbar differ by less than that rounding
- * may come out in either order.
+ * lse_given), except for G = 1 without lse_given: one launch forms lse and
+ * keeps the positions of largest score (the same order as pbar when G = 1),
+ * and weighs them with the final lse.  No workspace.  Scores are fp32 sums
+ * of bf16 products on the matrix cores, so positions whose pbar differ by
+ * less than that rounding may come out in either order.
  */
 gm_status gm_dense_refresh(int B, int n, int hq, int hkv, int d, gm_dtype dt, float scale,
                            const void* q, const void* k, int s, int lse_given, float* lse,

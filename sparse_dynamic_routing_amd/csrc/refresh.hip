@@ -210,12 +210,15 @@ __device__ __forceinline__ void load_key_tile(uint4* buf, const bf16_t* kbase, s
 // fragments (RT * G * d / 8 registers) leave room; one for the selection
 // pass, whose top lists and insertion need the registers
 constexpr int ref_rt(int MODE, int D, int G) {
-    return MODE == 0 && G <= 2 && G * D <= 256 ? 2 : 1;
+    return (MODE == 0 && G <= 2 && G * D <= 256) || (MODE == 2 && G * D <= 128) ? 2 : 1;
 }
 constexpr int ref_tokens(int MODE, int D, int G) { return kRefWaves * 16 * ref_rt(MODE, D, G); }
 
-// MODE 0: lse; MODE 1: the top-S refresh edges.  D head dim, G query heads
-// per KV head.
+// MODE 0: lse; MODE 1: the top-S refresh edges given lse; MODE 2 (G = 1):
+// both in one pass.  With one query head per KV head pbar_j = exp(score_j -
+// lse) ranks the keys as their raw scores do, so the lanes keep their top
+// lists by score while they form lse, and the kept weights are taken from
+// the final lse at the end.  D head dim, G query heads per KV head.
 template <int MODE, int D, int G, int S>
 __global__ __launch_bounds__(kRefWaves * kWave, 4) void refresh_kernel(RefreshArgs a) {
     constexpr int RT = ref_rt(MODE, D, G);        // 16-token tiles per wavefront
@@ -248,10 +251,14 @@ __global__ __launch_bounds__(kRefWaves * kWave, 4) void refresh_kernel(RefreshAr
                 qf[rt][g][ks] = as_frag(*reinterpret_cast<const uint4*>(qr + 32 * ks + 8 * grp));
         }
     }
-    float m2[RT][G], z[RT][G];     // MODE 0: running max / sum, base 2
+    static_assert(MODE != 2 || G == 1, "one pass only for one query head per KV head");
+    constexpr bool LSE = MODE != 1, SEL = MODE != 0;
+    // (values of the lists: pbar in MODE 1, the raw score in MODE 2)
+    constexpr float kEmpty = MODE == 2 ? -INFINITY : 0.0f;
+    float m2[RT][G], z[RT][G];     // MODE 0, 2: running max / sum, base 2
     float ls2[RT][G];             // MODE 1: the token's lse + log(G), base 2
-    TopS<S> top[RT];             // MODE 1: this lane's sorted top list
-    float thr[RT];               // MODE 1: the token's S-th value at the last tile
+    TopS<S> top[RT];             // MODE 1, 2: this lane's sorted top list
+    float thr[RT];               // MODE 1, 2: the token's S-th value at the last tile
     const float log2g = G == 1 ? 0.0f : G == 2 ? 1.0f : G == 4 ? 2.0f : 3.0f;
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt) {
@@ -266,9 +273,9 @@ __global__ __launch_bounds__(kRefWaves * kWave, 4) void refresh_kernel(RefreshAr
                     ls2[rt][g] = fmaf(a.lse[((size_t)b * n + tok) * a.hq + h * G + g], kLog2e,
                                       log2g);
         }
-        thr[rt] = 0.0f;
+        thr[rt] = kEmpty;
 #pragma unroll
-        for (int e = 0; e < S; ++e) { top[rt].v[e] = 0.0f; top[rt].j[e] = 0x7fffffff; }
+        for (int e = 0; e < S; ++e) { top[rt].v[e] = kEmpty; top[rt].j[e] = 0x7fffffff; }
     }
 
     // key tiles, double-buffered: filled by direct global->LDS loads (no
@@ -324,14 +331,18 @@ __global__ __launch_bounds__(kRefWaves * kWave, 4) void refresh_kernel(RefreshAr
                     bool live[4];
 #pragma unroll
                     for (int r = 0; r < 4; ++r) live[r] = !M || key0 + r <= tok;
-                    if constexpr (MODE == 0) {
-                        float x[G][4], y[G][4];
+                    float x[G][4];
+#pragma unroll
+                    for (int g = 0; g < G; ++g)
+#pragma unroll
+                        for (int r = 0; r < 4; ++r) x[g][r] = live[r] ? sc[g][r] : -INFINITY;
+                    if constexpr (LSE) {
+                        float y[G][4];
                         float my = -INFINITY;
 #pragma unroll
                         for (int g = 0; g < G; ++g)
 #pragma unroll
                             for (int r = 0; r < 4; ++r) {
-                                x[g][r] = live[r] ? sc[g][r] : -INFINITY;
                                 y[g][r] = fmaf(x[g][r], a.c, -m2[rt][g]);
                                 my = fmaxf(my, y[g][r]);
                             }
@@ -352,14 +363,20 @@ __global__ __launch_bounds__(kRefWaves * kWave, 4) void refresh_kernel(RefreshAr
                         for (int g = 0; g < G; ++g)
                             z[rt][g] += (fexp2(y[g][0]) + fexp2(y[g][1])) +
                                         (fexp2(y[g][2]) + fexp2(y[g][3]));
-                    } else {
+                    }
+                    if constexpr (SEL) {
                         float pb[4];
 #pragma unroll
                         for (int r = 0; r < 4; ++r) {
-                            float x = fexp2(fmaf(sc[0][r], a.c, -ls2[rt][0]));
+                            if constexpr (MODE == 2) {
+                                pb[r] = x[0][r];
+                            } else {
+                                float e = fexp2(fmaf(sc[0][r], a.c, -ls2[rt][0]));
 #pragma unroll
-                            for (int g = 1; g < G; ++g) x += fexp2(fmaf(sc[g][r], a.c, -ls2[rt][g]));
-                            pb[r] = live[r] ? x : 0.0f;
+                                for (int g = 1; g < G; ++g)
+                                    e += fexp2(fmaf(sc[g][r], a.c, -ls2[rt][g]));
+                                pb[r] = live[r] ? e : 0.0f;
+                            }
                         }
                         // a key enters only past the token's bound and this
                         // lane's last entry; keys in position order, the
@@ -382,7 +399,7 @@ __global__ __launch_bounds__(kRefWaves * kWave, 4) void refresh_kernel(RefreshAr
                     body(std::false_type{});
             }
         }
-        if constexpr (MODE == 1) {
+        if constexpr (SEL) {
             // the token's four lanes each hold S positions, all before the
             // next tile's keys: a later key no larger than the S-th largest
             // value they hold together has S positions ahead of it and is
@@ -396,7 +413,8 @@ __global__ __launch_bounds__(kRefWaves * kWave, 4) void refresh_kernel(RefreshAr
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt) {
         const int tok = t0 + 16 * rt + col;
-        if constexpr (MODE == 0) {
+        float lse2 = 0.0f;   // MODE 2: the token's lse, base 2
+        if constexpr (LSE) {
 #pragma unroll
             for (int g = 0; g < G; ++g) {
                 float m = m2[rt][g], zz = z[rt][g];
@@ -408,11 +426,12 @@ __global__ __launch_bounds__(kRefWaves * kWave, 4) void refresh_kernel(RefreshAr
                     zz = zz * fexp2(m - mn) + zo * fexp2(mo - mn);
                     m = mn;
                 }
+                lse2 = m + log2f(zz);
                 if (grp == 0 && tok < n)
-                    a.lse[((size_t)b * n + tok) * a.hq + h * G + g] =
-                        (m + log2f(zz)) * 0.69314718055994531f;
+                    a.lse[((size_t)b * n + tok) * a.hq + h * G + g] = lse2 * 0.69314718055994531f;
             }
-        } else {
+        }
+        if constexpr (SEL) {
             TopS<S> t = top[rt];
 #pragma unroll
             for (int o = 16; o < kWave; o <<= 1) {
@@ -429,9 +448,14 @@ __global__ __launch_bounds__(kRefWaves * kWave, 4) void refresh_kernel(RefreshAr
 #pragma unroll
                 for (int e = 0; e < S; ++e) {
                     if (e < a.s) {
-                        const bool ok = t.v[e] > 0.0f;
+                        // MODE 2: the weight of a kept score from the final lse
+                        const float w = MODE == 2 ? (t.j[e] != 0x7fffffff
+                                                         ? fexp2(fmaf(t.v[e], a.c, -lse2))
+                                                         : 0.0f)
+                                                  : t.v[e];
+                        const bool ok = w > 0.0f;
                         a.idx_out[ob + e] = ok ? t.j[e] : 0;
-                        a.w_out[ob + e] = ok ? t.v[e] : 0.0f;
+                        a.w_out[ob + e] = ok ? w : 0.0f;
                     }
                 }
             }
@@ -439,27 +463,39 @@ __global__ __launch_bounds__(kRefWaves * kWave, 4) void refresh_kernel(RefreshAr
     }
 }
 
+template <int MODE, int D, int G>
+hipError_t launch_sel(RefreshArgs a, dim3 grid, hipStream_t st) {
+    const dim3 block(kRefWaves * kWave);
+    if (a.s <= 2)
+        hipLaunchKernelGGL((refresh_kernel<MODE, D, G, 2>), grid, block, 0, st, a);
+    else if (a.s <= 4)
+        hipLaunchKernelGGL((refresh_kernel<MODE, D, G, 4>), grid, block, 0, st, a);
+    else
+        hipLaunchKernelGGL((refresh_kernel<MODE, D, G, kRefSmax>), grid, block, 0, st, a);
+    return hipGetLastError();
+}
+
 template <int D, int G>
 hipError_t run_dg(RefreshArgs a, int B, bool lse_given, hipStream_t st) {
     a.npair = B * a.hkv;
-    const dim3 block(kRefWaves * kWave);
     auto grid = [&](int mode) {
-        const int tok = mode == 0 ? ref_tokens(0, D, G) : ref_tokens(1, D, G);
+        const int tok = mode == 0   ? ref_tokens(0, D, G)
+                        : mode == 1 ? ref_tokens(1, D, G)
+                                    : ref_tokens(2, D, G);
         a.ntile = (a.n + tok - 1) / tok;
         return dim3((unsigned)(a.npair * a.ntile));
     };
-    if (!lse_given) {
+    if constexpr (G == 1) {
+        if (!lse_given) {   // one pass: lse and the edges together
+            const dim3 g2 = grid(2);
+            return launch_sel<2, D, G>(a, g2, st);
+        }
+    } else if (!lse_given) {
         const dim3 g0 = grid(0);
-        hipLaunchKernelGGL((refresh_kernel<0, D, G, 1>), g0, block, 0, st, a);
+        hipLaunchKernelGGL((refresh_kernel<0, D, G, 1>), g0, dim3(kRefWaves * kWave), 0, st, a);
     }
     const dim3 g1 = grid(1);
-    if (a.s <= 2)
-        hipLaunchKernelGGL((refresh_kernel<1, D, G, 2>), g1, block, 0, st, a);
-    else if (a.s <= 4)
-        hipLaunchKernelGGL((refresh_kernel<1, D, G, 4>), g1, block, 0, st, a);
-    else
-        hipLaunchKernelGGL((refresh_kernel<1, D, G, kRefSmax>), g1, block, 0, st, a);
-    return hipGetLastError();
+    return launch_sel<1, D, G>(a, g1, st);
 }
 
 }  // namespace

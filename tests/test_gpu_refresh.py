@@ -81,6 +81,8 @@ REFRESH_CASES = [
     (2, 130, 2, 4, 128, 3, 1.0, 7),      # s not a power of two
     (1, 300, 1, 2, 256, 8, 2.0, 13),     # d = 256 with the longest list (registers spill)
     (2, 1000, 3, 1, 64, 5, 3.0, 14),     # three KV heads (pairs not a power of two), 4 tiles
+    (1, 300, 2, 1, 256, 8, 2.0, 15),     # one pass (G = 1) at d = 256, the longest list
+    (2, 700, 2, 1, 128, 4, 0.3, 16),     # one pass, flat attention (many near-equal scores)
 ]
 
 
@@ -134,10 +136,12 @@ def test_refresh_tiny_sequences_pad():
         np.testing.assert_allclose(host(wo)[:, 0, :, 0], 1.0, rtol=1e-6)
 
 
-def test_refresh_repeated_keys_tie_to_the_lower_position():
+@pytest.mark.parametrize("G", [2, 1])
+def test_refresh_repeated_keys_tie_to_the_lower_position(G):
     """Equal key rows give equal probabilities: the lower position is kept
-    first (both sides compute the two scores the same way)."""
-    B, n, hkv, G, d, s = 1, 200, 2, 2, 128, 4
+    first (both sides compute the two scores the same way; G = 1 takes the
+    one-pass kernel, which ranks by the raw score)."""
+    B, n, hkv, d, s = 1, 200, 2, 128, 4
     q, k = _inputs(B, n, hkv, G, d, 3.0, 12)
     k[:, 1::2] = k[:, 0::2][:, : k[:, 1::2].shape[1]]   # position 2t+1 repeats 2t
     io, wo, lse = gm.dense_refresh(dev(q), dev(k), s)
