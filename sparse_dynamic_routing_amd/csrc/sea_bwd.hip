@@ -68,7 +68,9 @@ WsLayout ws_layout(long long U, int s, int G, int n) {
     l.off = l.cnt + align256((size_t)U * sizeof(int));
     l.bsum = l.off + align256((size_t)(U + 1) * sizeof(int));
     l.list = l.bsum + align256((size_t)((U + kScanPerBlock - 1) / kScanPerBlock) * sizeof(int));
-    l.beg = l.list + align256((size_t)U * s * sizeof(int));
+    // eight spare entries: the target pass reads the next four ids of a row
+    // at once, up to seven past the row's end
+    l.beg = l.list + align256(((size_t)U * s + 8) * sizeof(int));
     l.len = l.beg + align256((size_t)U * sizeof(int));
     l.head = l.len + align256((size_t)U * sizeof(int));
     l.tgt = l.head + align256((size_t)U * 4 * sizeof(int));
@@ -1156,6 +1158,167 @@ __global__ __launch_bounds__(kDstBlock) void sea_bwd_dst_row_kernel(SeaBwdFast a
     }
 }
 
+// Target pass with four incoming edges per pass (s = 4): the same work as
+// sea_bwd_dst_row_kernel<T, G, 4, R>, with everything that is the same for
+// the whole wavefront read through the scalar data cache: the row's head
+// record, offset and length, each pass's four coefficient records and the
+// next pass's four edge ids.  Only the q/dout rows go through the vector
+// memory path, whose outstanding requests per CU bound this pass.
+template <typename T, int G, int R>
+__global__ __launch_bounds__(kDstBlock) void sea_bwd_dst_row_s_kernel(SeaBwdFast a) {
+    using A = typename io<T>::acc;
+    constexpr int V = io<T>::V;
+    constexpr int P = 4;
+    constexpr int ROW = R == 0 ? 128 : 256 * R;
+    constexpr int NP = R == 0 ? 1 : R;
+    constexpr int FROW = ROW * 4 / (int)sizeof(T);
+    constexpr int FPART = FROW / NP;
+    static_assert(R > 0 || V / 2 >= P, "a 128-byte row needs V/2 >= P");
+    static_assert(G >= 1 && G <= 4, "the coefficient records of four edges fit the scalar registers");
+    constexpr int L = V / P;
+    constexpr int CW = 2 * G;   // coefficient words per edge
+    const int lane = threadIdx.x & (kWave - 1);
+    const int r = lane & 15;
+    const int row = lane >> 4;   // the edge slot of this 16-lane row
+    const int x = blockIdx.x % kXcds;
+    const int q = (int)(blockIdx.x / kXcds);   // one target row per wavefront
+    const int nseg_x = x < a.sp.nseg ? (a.sp.nseg - x + kXcds - 1) / kXcds : 0;
+    if (q >= nseg_x * a.sp.L) return;
+    const Pos pos = pos_of(a.sp, x, q);
+    const int h = pos.unit - pos.bi * a.hkv;
+    const int* hp = a.ws.head + (size_t)pos.prow * 4;
+    int e0 = hp[0], e1 = hp[1], e2 = hp[2], e3 = hp[3];   // -1 padded
+    asm("" : "+s"(e0), "+s"(e1), "+s"(e2), "+s"(e3));
+    const int beg = a.ws.beg[pos.prow];
+    const int len = a.ws.len[pos.prow];
+    const uint32_t qbase = (uint32_t)h * G;
+    const float* coef = reinterpret_cast<const float*>(a.ws.coef);
+
+    A ak[NP][V], av[NP][V];
+#pragma unroll
+    for (int k = 0; k < NP; ++k)
+#pragma unroll
+        for (int e = 0; e < V; ++e) { ak[k][e] = 0; av[k][e] = 0; }
+    for (int p0 = 0;;) {
+        int eid = e0;
+        eid = row == 1 ? e1 : eid;
+        eid = row == 2 ? e2 : eid;
+        eid = row == 3 ? e3 : eid;
+        uint4 qr[G][NP], dr[G][NP];
+        if (eid >= 0) {
+            const int src = (int)fdiv((uint32_t)eid, a.fd_s);      // source unit
+            const int sbi = (int)fdiv((uint32_t)src, a.fd_hkv);    // its b*n + i
+            const uint32_t qrow = (uint32_t)sbi * a.hq + qbase;
+#pragma unroll
+            for (int g = 0; g < G; ++g)
+#pragma unroll
+                for (int k = 0; k < NP; ++k) {
+                    if constexpr (R == 0) {
+                        const uint2 q2 = *reinterpret_cast<const uint2*>(a.q + (qrow + g) * ROW + r * 8);
+                        const uint2 d2 =
+                            *reinterpret_cast<const uint2*>(a.dout + (qrow + g) * ROW + r * 8);
+                        qr[g][k] = make_uint4(q2.x, q2.y, 0u, 0u);
+                        dr[g][k] = make_uint4(d2.x, d2.y, 0u, 0u);
+                    } else {
+                        qr[g][k] = *reinterpret_cast<const uint4*>(a.q + (qrow + g) * ROW +
+                                                                   256 * k + r * 16);
+                        dr[g][k] = *reinterpret_cast<const uint4*>(a.dout + (qrow + g) * ROW +
+                                                                   256 * k + r * 16);
+                    }
+                }
+        }
+        // the four edges' coefficient records (a dead slot reads record 0)
+        // and the next pass's ids (the list ends in eight spare entries, so
+        // these reads stay inside it), all in one scalar round trip
+        float c0[CW], c1[CW], c2[CW], c3[CW];
+        const int pn = p0 + P;
+        int n0, n1, n2, n3;
+        {
+            const float* p0c = coef + (size_t)(e0 < 0 ? 0 : e0) * CW;
+            const float* p1c = coef + (size_t)(e1 < 0 ? 0 : e1) * CW;
+            const float* p2c = coef + (size_t)(e2 < 0 ? 0 : e2) * CW;
+            const float* p3c = coef + (size_t)(e3 < 0 ? 0 : e3) * CW;
+#pragma unroll
+            for (int j = 0; j < CW; ++j) {
+                c0[j] = p0c[j]; c1[j] = p1c[j]; c2[j] = p2c[j]; c3[j] = p3c[j];
+                // opaque to the optimiser: a select between loaded values
+                // would otherwise become branches around the loads
+                asm("" : "+s"(c0[j]), "+s"(c1[j]), "+s"(c2[j]), "+s"(c3[j]));
+            }
+            const int* lp = a.ws.list + beg + pn;
+            n0 = lp[0]; n1 = lp[1]; n2 = lp[2]; n3 = lp[3];
+            asm("" : "+s"(n0), "+s"(n1), "+s"(n2), "+s"(n3));
+            n0 = pn < len ? n0 : -1;
+            n1 = pn + 1 < len ? n1 : -1;
+            n2 = pn + 2 < len ? n2 : -1;
+            n3 = pn + 3 < len ? n3 : -1;
+        }
+        if (eid >= 0) {
+#pragma unroll
+            for (int g = 0; g < G; ++g) {
+                float cx = c0[2 * g], cy = c0[2 * g + 1];
+                cx = row == 1 ? c1[2 * g] : cx;
+                cy = row == 1 ? c1[2 * g + 1] : cy;
+                cx = row == 2 ? c2[2 * g] : cx;
+                cy = row == 2 ? c2[2 * g + 1] : cy;
+                cx = row == 3 ? c3[2 * g] : cx;
+                cy = row == 3 ? c3[2 * g + 1] : cy;
+#pragma unroll
+                for (int k = 0; k < NP; ++k) {
+                    A qf[V], df[V];
+                    unpack16<A, V>(qr[g][k], qf);
+                    unpack16<A, V>(dr[g][k], df);
+#pragma unroll
+                    for (int e = 0; e < V; ++e) {
+                        ak[k][e] += (A)cx * qf[e];
+                        av[k][e] += (A)cy * df[e];
+                    }
+                }
+            }
+        }
+        if (pn >= len) break;
+        p0 = pn;
+        e0 = n0; e1 = n1; e2 = n2; e3 = n3;
+    }
+    if constexpr (R == 0) {
+        A hk[V / 2], hv[V / 2];
+#pragma unroll
+        for (int e = 0; e < V / 2; ++e) { hk[e] = ak[0][e]; hv[e] = av[0][e]; }
+        rows_reduce_scatter<P, V / 2>(hk);
+        rows_reduce_scatter<P, V / 2>(hv);
+        const uint32_t o = (uint32_t)pos.unit * FROW + r * (V / 2) * 4 + rs_offset<V / 2, P>(row) * 4;
+        store_f32_nt<V / 2 / P>(a.dk + o, hk);
+        store_f32_nt<V / 2 / P>(a.dv + o, hv);
+        return;
+    }
+#pragma unroll
+    for (int k = 0; k < NP; ++k) {
+        rows_reduce_scatter<P, V>(ak[k]);
+        rows_reduce_scatter<P, V>(av[k]);
+    }
+    const uint32_t o = (uint32_t)pos.unit * FROW + r * 16 * 4 / (int)sizeof(T) +
+                       rs_offset<V, P>(row) * 4;
+#pragma unroll
+    for (int k = 0; k < NP; ++k) {
+        store_f32_nt<L>(a.dk + o + FPART * k, ak[k]);
+        store_f32_nt<L>(a.dv + o + FPART * k, av[k]);
+    }
+}
+
+template <typename T, int G, int PD, int R>
+void launch_dst_row(const SeaBwdFast& a, hipStream_t st) {
+    const long long per_x = (long long)((a.sp.nseg + kXcds - 1) / kXcds) * a.sp.L;
+    const long long rows_per_block = kDstBlock / kWave * (4 / PD);
+    const long long blocks = kXcds * ((per_x + rows_per_block - 1) / rows_per_block);
+    if constexpr (PD == 4 && G >= 1 && G <= 4) {
+        hipLaunchKernelGGL((sea_bwd_dst_row_s_kernel<T, G, R>), dim3((unsigned)blocks),
+                           dim3(kDstBlock), 0, st, a);
+    } else {
+        hipLaunchKernelGGL((sea_bwd_dst_row_kernel<T, G, PD, R>), dim3((unsigned)blocks),
+                           dim3(kDstBlock), 0, st, a);
+    }
+}
+
 void launch_index(const SeaBwdArgs& a, long long E, hipStream_t st) {
     const unsigned sblocks = (unsigned)((a.U + kScanPerBlock - 1) / kScanPerBlock);
     hipLaunchKernelGGL(scan_local_kernel, dim3(sblocks), dim3(1024), 0, st,
@@ -1241,11 +1404,7 @@ hipError_t run_fast2(const SeaBwdArgs& g, const SeaBwdFast& a, long long E, hipS
                                      a.ws.tgt, a.ws.beg, a.ws.len, a.ws.list, a.ws.head,
                                      a.ws.cnt, a.ws.off, a.ws.bsum, a.ws.stage, st);
     if (e != hipSuccess) return e;
-    const long long per_x = (long long)((a.sp.nseg + kXcds - 1) / kXcds) * a.sp.L;
-    const long long rows_per_block = kDstBlock / kWave * (4 / PD);
-    const long long blocks = kXcds * ((per_x + rows_per_block - 1) / rows_per_block);
-    hipLaunchKernelGGL((sea_bwd_dst_row_kernel<T, G, PD, R>), dim3((unsigned)blocks),
-                       dim3(kDstBlock), 0, st, a);
+    launch_dst_row<T, G, PD, R>(a, st);
     return hipGetLastError();
 }
 
@@ -1273,11 +1432,7 @@ hipError_t run_fast(const SeaBwdArgs& g, const SeaBwdFast& a, long long E, hipSt
         if (e != hipSuccess) return e;
     }
     if (!a.global_index) {
-        const long long per_x = (long long)((a.sp.nseg + kXcds - 1) / kXcds) * a.sp.L;
-        const long long rows_per_block = kDstBlock / kWave * (4 / PD);
-        const long long blocks = kXcds * ((per_x + rows_per_block - 1) / rows_per_block);
-        hipLaunchKernelGGL((sea_bwd_dst_row_kernel<T, G, PD, 1>), dim3((unsigned)blocks),
-                           dim3(kDstBlock), 0, st, a);
+        launch_dst_row<T, G, PD, 1>(a, st);
         return hipGetLastError();
     }
     const int ndst = persistent_grid(reinterpret_cast<const void*>(
