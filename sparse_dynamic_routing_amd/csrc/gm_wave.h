@@ -34,6 +34,12 @@ __device__ __forceinline__ double dpp(double x) {
     return __builtin_bit_cast(double, ((uint64_t)(uint32_t)hi << 32) | (uint32_t)lo);
 }
 
+// Lane L of each 16-lane row, to every lane of that row.
+template <int L>
+__device__ __forceinline__ float row_bcast(float x) {
+    return dpp<0x150 + L>(x);
+}
+
 // Sum / max over the 16 lanes of each row; every lane gets the result.
 template <typename A>
 __device__ __forceinline__ A row_sum16(A x) {

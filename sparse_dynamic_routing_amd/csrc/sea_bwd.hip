@@ -515,13 +515,19 @@ __device__ __forceinline__ A row_dot(const uint4 (&x)[R], const uint4 (&y)[R]) {
 // GLOBAL: also count the in-degree of every K/V row (global index path).
 // SAVED: the softmax comes from the forward's p / w statistics (p = stat * w),
 // so q is not read here and no scores are formed.
-template <typename T, int G, int S, bool VEC, bool GLOBAL, bool SAVED>
+// BLK (G = 2, s = 4, segments of a multiple of 4 tokens): the four units of
+// a wavefront are consecutive tokens of one pair, so their saved records
+// (p / w of both heads, then the edge copy: 16 words each) are one 256-byte
+// block, read with one word per lane and spread over each 16-lane row by
+// row broadcasts (two L2 requests per wavefront instead of eight).
+template <typename T, int G, int S, bool VEC, bool GLOBAL, bool SAVED, bool BLK>
 __global__ __launch_bounds__(kBlock) void sea_bwd_src_row_kernel(SeaBwdFast a) {
     using A = typename io<T>::acc;
     constexpr int V = io<T>::V;
     constexpr int ROW = 256;                          // bytes of an input d-row
     constexpr int FROW = ROW * 4 / (int)sizeof(T);    // bytes of an fp32 gradient row
     constexpr int GC = G < 2 ? G : 2;                 // query heads held at once
+    static_assert(!BLK || (SAVED && VEC && G == 2 && S == 4), "16-word records");
     const int r = threadIdx.x & 15;
     const A c = (A)a.scale * (A)1.4426950408889634;
     const A sc = (A)a.scale;
@@ -533,11 +539,20 @@ __global__ __launch_bounds__(kBlock) void sea_bwd_src_row_kernel(SeaBwdFast a) {
         Pos pos;
         int j[S];
         float wt[S];
+        float rec;   // BLK: word (lane) of the wavefront's record block
     };
     auto fetch = [&](int u) {
         Item it;
         it.pos = pos_of(a.sp, sch.x, u < sch.end ? u : sch.end - 1);
-        if constexpr (SAVED) {
+        if constexpr (BLK) {
+            // row 0 holds the wavefront's first item; past the end, the
+            // last block is read again (never used)
+            int ub = __builtin_amdgcn_readfirstlane(u);
+            ub = ub < sch.end ? ub : sch.end - 4;
+            const Pos p0 = pos_of(a.sp, sch.x, ub);
+            it.rec = a.stats[(size_t)p0.prow * 16 + (threadIdx.x & (kWave - 1))];
+            return it;
+        } else if constexpr (SAVED) {
             // the forward's pair-major copy of the edge row: contiguous for
             // the consecutive tokens of a wavefront, where the interleaved
             // rows of the eight KV heads would bring whole lines to every XCD
@@ -577,6 +592,19 @@ __global__ __launch_bounds__(kBlock) void sea_bwd_src_row_kernel(SeaBwdFast a) {
     Item cur = fetch(sch.q);
     for (int u = sch.q; u < sch.end; u += sch.step) {
         const Item nxt = fetch(u + sch.step);
+        float bst[BLK ? G : 1][S];   // BLK: this unit's p / w per head and slot
+        if constexpr (BLK) {
+            bst[0][0] = row_bcast<0>(cur.rec); bst[0][1] = row_bcast<1>(cur.rec);
+            bst[0][2] = row_bcast<2>(cur.rec); bst[0][3] = row_bcast<3>(cur.rec);
+            bst[1][0] = row_bcast<4>(cur.rec); bst[1][1] = row_bcast<5>(cur.rec);
+            bst[1][2] = row_bcast<6>(cur.rec); bst[1][3] = row_bcast<7>(cur.rec);
+            cur.j[0] = __float_as_int(row_bcast<8>(cur.rec));
+            cur.j[1] = __float_as_int(row_bcast<9>(cur.rec));
+            cur.j[2] = __float_as_int(row_bcast<10>(cur.rec));
+            cur.j[3] = __float_as_int(row_bcast<11>(cur.rec));
+            cur.wt[0] = row_bcast<12>(cur.rec); cur.wt[1] = row_bcast<13>(cur.rec);
+            cur.wt[2] = row_bcast<14>(cur.rec); cur.wt[3] = row_bcast<15>(cur.rec);
+        }
         bool live[S];
         int kvrow[S];
         uint4 kr[S], vr[S];
@@ -609,7 +637,10 @@ __global__ __launch_bounds__(kBlock) void sea_bwd_src_row_kernel(SeaBwdFast a) {
             float st[GC][S];
 #pragma unroll
             for (int g = 0; g < GC; ++g) {
-                if constexpr (SAVED) {
+                if constexpr (BLK) {
+#pragma unroll
+                    for (int t = 0; t < S; ++t) st[g][t] = bst[g0 + g][t];
+                } else if constexpr (SAVED) {
                     const float* sp = a.stats + ((size_t)cur.pos.prow * (G + 2) + g0 + g) * a.s;
                     if constexpr (VEC) {
                         const float4 s4 = *reinterpret_cast<const float4*>(sp);
@@ -1367,9 +1398,19 @@ hipError_t dispatch_g(const SeaBwdArgs& a, int G, long long E, hipStream_t st) {
 template <typename T, int G, int S, bool VEC, bool GLOBAL, bool SAVED, int R>
 void launch_src_k(const SeaBwdFast& a, hipStream_t st) {
     if constexpr (R == 1) {
-        const void* fn =
-            reinterpret_cast<const void*>(&sea_bwd_src_row_kernel<T, G, S, VEC, GLOBAL, SAVED>);
-        hipLaunchKernelGGL((sea_bwd_src_row_kernel<T, G, S, VEC, GLOBAL, SAVED>),
+        if constexpr (SAVED && VEC && G == 2 && S == 4) {
+            if ((a.sp.L & 3) == 0) {
+                const void* fn = reinterpret_cast<const void*>(
+                    &sea_bwd_src_row_kernel<T, G, S, VEC, GLOBAL, SAVED, true>);
+                hipLaunchKernelGGL((sea_bwd_src_row_kernel<T, G, S, VEC, GLOBAL, SAVED, true>),
+                                   dim3(persistent_grid(fn, a.U, kBlock / 16)), dim3(kBlock), 0,
+                                   st, a);
+                return;
+            }
+        }
+        const void* fn = reinterpret_cast<const void*>(
+            &sea_bwd_src_row_kernel<T, G, S, VEC, GLOBAL, SAVED, false>);
+        hipLaunchKernelGGL((sea_bwd_src_row_kernel<T, G, S, VEC, GLOBAL, SAVED, false>),
                            dim3(persistent_grid(fn, a.U, kBlock / 16)), dim3(kBlock), 0, st, a);
     } else {
         const void* fn = reinterpret_cast<const void*>(
