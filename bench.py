@@ -83,7 +83,7 @@ CALL_KERNELS = {
     "gm_ser_forward": ["ser_fwd_vec_kernel"],
     "gm_sea_forward": ["sea_fwd_row_kernel"],
     "gm_sea_backward": ["sea_bwd_src_row_kernel", "edge_index_one_kernel",
-                        "sea_bwd_dst_row_kernel"],
+                        "sea_bwd_dst_row_s_kernel"],
     "gm_ser_backward": ["ser_bwd_part_kernel", "ser_bwd_part_sum_kernel"],
 }
 PROFILE = os.path.join(ROOT, "profiles", "metric_pass_kernels.md")

@@ -22,6 +22,7 @@ pytestmark = pytest.mark.gpu
 SEA_SHAPES = [
     # dtype, d, G, s, n
     (torch.bfloat16, 128, 2, 4, 67),    # the measured layer's geometry
+    (torch.bfloat16, 128, 2, 4, 64),    # segments of 32 tokens: saved records read as blocks
     (torch.bfloat16, 128, 2, 2, 67),    # retrieving 2 per KV head
     (torch.bfloat16, 128, 1, 3, 45),    # slot count not a power of two
     (torch.bfloat16, 128, 4, 8, 33),    # two slot chunks per unit
