@@ -31,6 +31,7 @@ from __future__ import annotations
 
 import argparse
 import json
+import statistics
 import os
 import sys
 import time
@@ -167,7 +168,63 @@ def parse():
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="instead of the pass, run a plain device copy of MIB MiB "
                          "(the known-size reference for hardware byte counters)")
+    ap.add_argument("--gather-probe", action="store_true",
+                    help="instead of the pass, measure the 256-byte-row gather ceilings "
+                         "(libgm_probe.so) by set size per XCD and loads in flight")
     return ap.parse_args()
+
+
+# Gather-ceiling probe: sets per XCD (MB) from L2-resident to far beyond the
+# caches, 2^20 rows gathered per XCD per launch (2 GB in all).
+PROBE_SETS_MB = [1, 2, 3, 4, 6, 8, 16, 64, 256]
+PROBE_ROWS_PER_XCD = 1 << 20
+
+
+def run_gather_probe(a):
+    """Median TB/s of 256-byte rows gathered by 16-lane teams (the SEA
+    kernels' pattern), per set size per XCD and loads in flight per team."""
+    import ctypes
+    path = os.path.join(ROOT, "sparse_dynamic_routing_amd", "libgm_probe.so")
+    lib = ctypes.CDLL(path)
+    f = lib.gm_probe_gather
+    f.argtypes = [ctypes.c_void_p, ctypes.c_longlong, ctypes.c_void_p, ctypes.c_longlong,
+                  ctypes.c_int, ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p]
+    f.restype = ctypes.c_int
+    grid = 8 * 256
+    sink = torch.empty(grid * 256, dtype=torch.int32, device="cuda")
+    big = max(PROBE_SETS_MB) << 20
+    table = torch.ones(8 * big // 4, dtype=torch.int32, device="cuda")
+    gen = torch.Generator(device="cuda")
+    st = torch.cuda.current_stream()
+    out = []
+    for mb in PROBE_SETS_MB:
+        rows = (mb << 20) // 256
+        gen.manual_seed(20260902 + mb)
+        idx = torch.randint(0, rows, (8, PROBE_ROWS_PER_XCD), generator=gen, device="cuda",
+                            dtype=torch.int32)
+        for inf in (1, 2, 4):
+            def launch():
+                rc = f(table.data_ptr(), rows, idx.data_ptr(), PROBE_ROWS_PER_XCD, inf,
+                       sink.data_ptr(), grid, st.cuda_stream)
+                if rc:
+                    raise RuntimeError(f"gm_probe_gather returned {rc}")
+            for _ in range(max(a.warmup, 1)):
+                launch()
+            ts = []
+            for _ in range(max(a.steps, 3)):
+                e0 = torch.cuda.Event(enable_timing=True)
+                e1 = torch.cuda.Event(enable_timing=True)
+                e0.record(st)
+                launch()
+                e1.record(st)
+                e1.synchronize()
+                ts.append(e0.elapsed_time(e1) * 1e-3)
+            t = statistics.median(ts)
+            out.append({"set_MB_per_xcd": mb, "in_flight": inf, "us": round(t * 1e6, 1),
+                        "TBps": round(8 * PROBE_ROWS_PER_XCD * 256 / t / 1e12, 2)})
+            print(json.dumps(out[-1]), file=sys.stderr, flush=True)
+    print(json.dumps({"gather_probe": out, "rows_per_xcd_per_launch": PROBE_ROWS_PER_XCD,
+                      "row_bytes": 256, "workgroups": grid}))
 
 
 class Pass:
@@ -665,6 +722,9 @@ def main():
         torch.cuda.synchronize()
         print(json.dumps({"copy_calibration_bytes_read": n * 4, "bytes_written": n * 4,
                           "launches": a.warmup + a.steps}))
+        return
+    if a.gather_probe:
+        run_gather_probe(a)
         return
     gm.load()
     if a.config == "decode":

@@ -225,3 +225,18 @@ def test_sea_backward_noalloc_checks(lib):
     assert f(*args(dq=b)) == ALIAS               # dq on k
     assert f(*args(B=0)) == OK                   # empty: nothing to do
     assert b"GM_NOALLOC_SCRATCH_BYTES" in lib.gm_status_string(TOO_LARGE)
+
+
+def test_gather_probe_library_checks_arguments():
+    """The measurement probe (libgm_probe.so) loads and refuses bad arguments
+    on the host, before any launch."""
+    path = os.path.join(ROOT, "sparse_dynamic_routing_amd", "libgm_probe.so")
+    probe = ctypes.CDLL(path)
+    f = probe.gm_probe_gather
+    f.argtypes = [P, ctypes.c_longlong, P, ctypes.c_longlong, ctypes.c_int, P, ctypes.c_int, P]
+    f.restype = ctypes.c_int
+    a = fake(0x10000)
+    assert f(None, 16, a, 16, 1, a, 8, None) == 1          # no table
+    assert f(a, 16, a, 16, 3, a, 8, None) == 1             # 3 loads in flight: not built
+    assert f(a, 16, a, 16, 1, a, 12, None) == 1            # grid not a multiple of 8
+    assert f(a, 0, a, 16, 1, a, 8, None) == 1              # empty set
