@@ -518,8 +518,11 @@ __device__ __forceinline__ A row_dot(const uint4 (&x)[R], const uint4 (&y)[R]) {
 // BLK (G = 2, s = 4, segments of a multiple of 4 tokens): the four units of
 // a wavefront are consecutive tokens of one pair, so their saved records
 // (p / w of both heads, then the edge copy: 16 words each) are one 256-byte
-// block, read with one word per lane and spread over each 16-lane row by
-// row broadcasts (two L2 requests per wavefront instead of eight).
+// block.  The edge copies (index and weight words) come one unit ahead
+// through the scalar data cache, so the wait for them at the top of a unit
+// does not also drain the previous unit's vector stores; the p / w words
+// are read with one word per lane and spread over each 16-lane row by row
+// broadcasts (two L2 requests per wavefront instead of eight).
 template <typename T, int G, int S, bool VEC, bool GLOBAL, bool SAVED, bool BLK>
 __global__ __launch_bounds__(kBlock) void sea_bwd_src_row_kernel(SeaBwdFast a) {
     using A = typename io<T>::acc;
@@ -539,7 +542,8 @@ __global__ __launch_bounds__(kBlock) void sea_bwd_src_row_kernel(SeaBwdFast a) {
         Pos pos;
         int j[S];
         float wt[S];
-        float rec;   // BLK: word (lane) of the wavefront's record block
+        size_t rec;      // BLK: word offset of the wavefront's record block
+        float sr[32];    // BLK: the four units' index and weight words (scalar)
     };
     auto fetch = [&](int u) {
         Item it;
@@ -550,7 +554,13 @@ __global__ __launch_bounds__(kBlock) void sea_bwd_src_row_kernel(SeaBwdFast a) {
             int ub = __builtin_amdgcn_readfirstlane(u);
             ub = ub < sch.end ? ub : sch.end - 4;
             const Pos p0 = pos_of(a.sp, sch.x, ub);
-            it.rec = a.stats[(size_t)p0.prow * 16 + (threadIdx.x & (kWave - 1))];
+            it.rec = (size_t)p0.prow * 16;
+            typedef const __attribute__((address_space(4))) float cf4;
+            cf4* rp = (cf4*)(a.stats + it.rec);
+#pragma unroll
+            for (int k = 0; k < 4; ++k)
+#pragma unroll
+                for (int w = 0; w < 8; ++w) it.sr[k * 8 + w] = rp[k * 16 + 8 + w];
             return it;
         } else if constexpr (SAVED) {
             // the forward's pair-major copy of the edge row: contiguous for
@@ -592,18 +602,25 @@ __global__ __launch_bounds__(kBlock) void sea_bwd_src_row_kernel(SeaBwdFast a) {
     Item cur = fetch(sch.q);
     for (int u = sch.q; u < sch.end; u += sch.step) {
         const Item nxt = fetch(u + sch.step);
-        float bst[BLK ? G : 1][S];   // BLK: this unit's p / w per head and slot
+        float brec = 0.0f;   // BLK: word (lane) of the wavefront's record block
         if constexpr (BLK) {
-            bst[0][0] = row_bcast<0>(cur.rec); bst[0][1] = row_bcast<1>(cur.rec);
-            bst[0][2] = row_bcast<2>(cur.rec); bst[0][3] = row_bcast<3>(cur.rec);
-            bst[1][0] = row_bcast<4>(cur.rec); bst[1][1] = row_bcast<5>(cur.rec);
-            bst[1][2] = row_bcast<6>(cur.rec); bst[1][3] = row_bcast<7>(cur.rec);
-            cur.j[0] = __float_as_int(row_bcast<8>(cur.rec));
-            cur.j[1] = __float_as_int(row_bcast<9>(cur.rec));
-            cur.j[2] = __float_as_int(row_bcast<10>(cur.rec));
-            cur.j[3] = __float_as_int(row_bcast<11>(cur.rec));
-            cur.wt[0] = row_bcast<12>(cur.rec); cur.wt[1] = row_bcast<13>(cur.rec);
-            cur.wt[2] = row_bcast<14>(cur.rec); cur.wt[3] = row_bcast<15>(cur.rec);
+            const int rw = (threadIdx.x >> 4) & 3;
+            // row masks, opaque so that the blend below is not turned into
+            // an indexed (scratch) access
+            uint32_t m0 = rw == 0 ? ~0u : 0u, m1 = rw == 1 ? ~0u : 0u;
+            uint32_t m2 = rw == 2 ? ~0u : 0u, m3 = rw == 3 ? ~0u : 0u;
+            asm("" : "+v"(m0), "+v"(m1), "+v"(m2), "+v"(m3));
+#pragma unroll
+            for (int w = 0; w < 32; ++w) asm("" : "+s"(cur.sr[w]));
+#pragma unroll
+            for (int t = 0; t < 8; ++t) {
+                const uint32_t v = (__float_as_uint(cur.sr[t]) & m0) |
+                                   (__float_as_uint(cur.sr[8 + t]) & m1) |
+                                   (__float_as_uint(cur.sr[16 + t]) & m2) |
+                                   (__float_as_uint(cur.sr[24 + t]) & m3);
+                if (t < 4) cur.j[t] = (int)v; else cur.wt[t - 4] = __uint_as_float(v);
+            }
+            brec = a.stats[cur.rec + (threadIdx.x & (kWave - 1))];
         }
         bool live[S];
         int kvrow[S];
@@ -638,8 +655,13 @@ __global__ __launch_bounds__(kBlock) void sea_bwd_src_row_kernel(SeaBwdFast a) {
 #pragma unroll
             for (int g = 0; g < GC; ++g) {
                 if constexpr (BLK) {
-#pragma unroll
-                    for (int t = 0; t < S; ++t) st[g][t] = bst[g0 + g][t];
+                    if (g0 + g == 0) {
+                        st[g][0] = row_bcast<0>(brec); st[g][1] = row_bcast<1>(brec);
+                        st[g][2] = row_bcast<2>(brec); st[g][3] = row_bcast<3>(brec);
+                    } else {
+                        st[g][0] = row_bcast<4>(brec); st[g][1] = row_bcast<5>(brec);
+                        st[g][2] = row_bcast<6>(brec); st[g][3] = row_bcast<7>(brec);
+                    }
                 } else if constexpr (SAVED) {
                     const float* sp = a.stats + ((size_t)cur.pos.prow * (G + 2) + g0 + g) * a.s;
                     if constexpr (VEC) {

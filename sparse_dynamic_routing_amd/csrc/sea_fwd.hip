@@ -285,7 +285,12 @@ hipError_t dispatch_g(const SeaFwdArgs& a, int G, hipStream_t st) {
 // only cross-lane step is the 16-lane DPP sum of each score; the softmax
 // over the slots and the weighted sum of the V rows are lane-local.  Slots
 // t >= s (when s < S) are dead.  Rows never exchange data, so rows of one
-// wavefront may leave the item loop at different times.
+// wavefront may leave the item loop at different times.  With s = 4,
+// aligned edge rows and 256- or 512-byte d-rows, the edge rows of a
+// wavefront's next four units come through the scalar data cache, so the
+// wait for them at the top of a unit does not also drain the previous
+// unit's vector stores (at 128-byte rows the scalar rows' registers cost
+// more than the drain: measured slower).
 template <typename T, int G, int S, bool VEC, int R>
 __global__ __launch_bounds__(kBlock) void sea_fwd_row_kernel(SeaFwdFast a) {
     using A = typename io<T>::acc;
@@ -300,17 +305,36 @@ __global__ __launch_bounds__(kBlock) void sea_fwd_row_kernel(SeaFwdFast a) {
     const Sched sc = xcd_sched(a.sp, 16);
     if (sc.q >= sc.end) return;
 
+    constexpr bool SCAL = VEC && S == 4 && R != 0;
     struct Item {
         UnitPos pos;
         int j[S];
         float wt[S];
+        float sr[SCAL ? 32 : 1];   // SCAL: the four units' index and weight rows
     };
     // the item's edge slots; past the end the last item is read again (a
     // valid address, so the load needs no branch) and never used
     auto fetch = [&](int u) {
         Item it;
         it.pos = unit_pos(a.sp, sc.x, u < sc.end ? u : sc.end - 1);
-        if constexpr (VEC) {
+        if constexpr (SCAL) {
+            // row k of the wavefront holds item ub + k (row 0's item is
+            // ub), clamped at the end like the vector path
+            typedef const __attribute__((address_space(4))) float cf4;
+            const int ub = __builtin_amdgcn_readfirstlane(u);
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                const UnitPos pk = unit_pos(a.sp, sc.x, ub + k < sc.end ? ub + k : sc.end - 1);
+                cf4* ip = (cf4*)(reinterpret_cast<const float*>(a.idx) + (size_t)pk.unit * 4);
+                cf4* wp = (cf4*)(a.w + (size_t)pk.unit * 4);
+#pragma unroll
+                for (int t = 0; t < 4; ++t) {
+                    it.sr[k * 8 + t] = ip[t];
+                    it.sr[k * 8 + 4 + t] = wp[t];
+                }
+            }
+            return it;
+        } else if constexpr (VEC) {
             const int4 j4 = *reinterpret_cast<const int4*>(a.idx + (size_t)it.pos.unit * 4);
             const float4 w4 = *reinterpret_cast<const float4*>(a.w + (size_t)it.pos.unit * 4);
             it.j[0] = j4.x; it.j[1] = j4.y; it.j[2] = j4.z; it.j[3] = j4.w;
@@ -331,6 +355,25 @@ __global__ __launch_bounds__(kBlock) void sea_fwd_row_kernel(SeaFwdFast a) {
     Item cur = fetch(sc.q);
     for (int u = sc.q; u < sc.end; u += sc.step) {
         const Item nxt = fetch(u + sc.step);
+        if constexpr (SCAL) {
+            // this row's unit: a blend of the four scalar rows under row
+            // masks (opaque, so that the blend is not turned into an
+            // indexed access through scratch memory)
+            const int rw = (threadIdx.x >> 4) & 3;
+            uint32_t m0 = rw == 0 ? ~0u : 0u, m1 = rw == 1 ? ~0u : 0u;
+            uint32_t m2 = rw == 2 ? ~0u : 0u, m3 = rw == 3 ? ~0u : 0u;
+            asm("" : "+v"(m0), "+v"(m1), "+v"(m2), "+v"(m3));
+#pragma unroll
+            for (int w = 0; w < 32; ++w) asm("" : "+s"(cur.sr[w]));
+#pragma unroll
+            for (int t = 0; t < 8; ++t) {
+                const uint32_t v = (__float_as_uint(cur.sr[t]) & m0) |
+                                   (__float_as_uint(cur.sr[8 + t]) & m1) |
+                                   (__float_as_uint(cur.sr[16 + t]) & m2) |
+                                   (__float_as_uint(cur.sr[24 + t]) & m3);
+                if (t < 4) cur.j[t] = (int)v; else cur.wt[t - 4] = __uint_as_float(v);
+            }
+        }
         bool live[S];
         uint4 kr[S][NP], vr[S][NP];
 #pragma unroll
