@@ -286,11 +286,12 @@ hipError_t dispatch_g(const SeaFwdArgs& a, int G, hipStream_t st) {
 // over the slots and the weighted sum of the V rows are lane-local.  Slots
 // t >= s (when s < S) are dead.  Rows never exchange data, so rows of one
 // wavefront may leave the item loop at different times.  With s = 4,
-// aligned edge rows and 256- or 512-byte d-rows, the edge rows of a
+// aligned edge rows and bf16 256- or 512-byte d-rows, the edge rows of a
 // wavefront's next four units come through the scalar data cache, so the
 // wait for them at the top of a unit does not also drain the previous
-// unit's vector stores (at 128-byte rows the scalar rows' registers cost
-// more than the drain: measured slower).
+// unit's vector stores (at 128-byte rows, and with the fp64 accumulators of
+// fp32 inputs, the scalar rows' registers cost more than the drain:
+// measured slower).
 template <typename T, int G, int S, bool VEC, int R>
 __global__ __launch_bounds__(kBlock) void sea_fwd_row_kernel(SeaFwdFast a) {
     using A = typename io<T>::acc;
@@ -305,7 +306,7 @@ __global__ __launch_bounds__(kBlock) void sea_fwd_row_kernel(SeaFwdFast a) {
     const Sched sc = xcd_sched(a.sp, 16);
     if (sc.q >= sc.end) return;
 
-    constexpr bool SCAL = VEC && S == 4 && R != 0;
+    constexpr bool SCAL = VEC && S == 4 && R != 0 && std::is_same<T, bf16_t>::value;
     struct Item {
         UnitPos pos;
         int j[S];
