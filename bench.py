@@ -107,14 +107,15 @@ CONFIG_STAGES = {
 
 def stage_bytes(stage: str, p: synth.Preset) -> int:
     """Compulsory bytes per unit of one stage (edges: 8 bytes per slot; the
-    forward saves p / w, 4 bytes per query head and slot, and a copy of the
-    edge row, only when a backward follows; the backward reads that copy in
-    place of the edge row)."""
+    forward saves p / w, 4 bytes per query head and slot (8 for fp32 inputs,
+    whose statistics are fp64), and a copy of the edge row, only when a
+    backward follows; the backward reads that copy in place of the edge
+    row)."""
     s1 = p.s1
     G = p.hq // p.hkv
     es = 2 if p.dtype == torch.bfloat16 else 4
     qrow, kv = G * p.d * es, 2 * p.d * es          # a unit's q (or o, dout); its K and V rows
-    st = 4 * G * s1 if p.backward else 0
+    st = (4 if es == 2 else 8) * G * s1 if p.backward else 0
     pm = 8 if p.backward and max(p.s1, p.s2, p.s3) <= 4 else 0   # the SER path map
     return {"ser_fwd": 8 * p.s2 + 8 * s1 + pm,
             "sea_fwd": qrow + 8 * s1 + kv + qrow + st + (8 * s1 if p.backward else 0),
@@ -247,7 +248,7 @@ class Pass:
         self.wa = torch.empty(es, **f32)
         self.o = torch.empty_like(self.q)
         # p / w per query head and slot, saved by the forward for the backward
-        self.stats = (torch.empty((p.B, p.hkv, p.n, p.hq // p.hkv + 2, p.s1), **f32)
+        self.stats = (torch.empty(gm.stats_shape(self.q, p.hkv, p.s1), **f32)
                       if p.backward else None)
         self.dq = torch.empty(qs, **f32)
         self.dk = torch.empty(ks, **f32)

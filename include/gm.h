@@ -107,13 +107,16 @@ gm_status gm_ser_forward(int B, int n, int hkv,
  *        idx, w [B][n][hkv][s1]
  *        scale: multiplies q.k (normally 1/sqrt(d))
  *   out  o [B][n][hq][d] dtype dt
- *        stats [B][hkv][n][hq/hkv + 2][s1] fp32 (KV-head-major, so that
- *        each pass writes and reads it in contiguous rows), optional (NULL:
- *        not written; else 16-byte aligned, overlapping nothing): rows
- *        g < G = hq/hkv hold, for query head hkv_index*G + g, p_t / w_t of
- *        every live slot, i.e. exp(scale*q.k[idx_t]) / sum_u w_u
- *        exp(scale*q.k[idx_u]), and 0 for a dead slot; row G holds idx (the
- *        int32 bits) and row G + 1 w, a copy of the unit's edge row.
+ *        stats [B][hkv][n][E*G + 2][s1] 4-byte words, G = hq/hkv, E = 1 for
+ *        bf16 inputs and 2 for fp32 inputs (KV-head-major, so that each
+ *        pass writes and reads it in contiguous rows), optional (NULL: not
+ *        written; else 16-byte aligned, overlapping nothing): the first
+ *        E*G rows of a unit hold, for query head hkv_index*G + g and slot
+ *        t (in (g, t) order), p_t / w_t of every live slot, i.e.
+ *        exp(scale*q.k[idx_t]) / sum_u w_u exp(scale*q.k[idx_u]), and 0 for
+ *        a dead slot, as fp32 (E = 1) or fp64 (E = 2: G*s1 doubles, the
+ *        precision the fp32-input backward computes in); row E*G holds idx
+ *        (the int32 bits) and row E*G + 1 w, a copy of the unit's edge row.
  *        gm_sea_backward takes it to skip the softmax recomputation (and
  *        the q reads it needs) and reads its edges from the copy.
  * o[hq] = sum_t p_t v[idx_t], p = softmax over live slots (w_t > 0) of
@@ -156,9 +159,9 @@ size_t gm_sea_backward_workspace_bytes(int B, int n, int hq, int hkv, int s1);
  * through the soft edge weights).
  *   in   q, k, v, idx, w, s1, scale as for the forward; dout [B][n][hq][d] dt;
  *        stats: NULL, or what gm_sea_forward wrote for these q, k, idx, w
- *        and scale (16-byte aligned).  With bf16 inputs the backward then
- *        takes p_t = stats_t * w_t and dl_t / w_t from it instead of
- *        recomputing the scores; fp32 inputs always recompute.
+ *        and scale (16-byte aligned).  The backward then takes
+ *        p_t = stats_t * w_t and dl_t / w_t from it instead of recomputing
+ *        the scores (in fp64 for fp32 inputs, whose statistics are fp64).
  *        Precision: bf16 inputs are computed in fp32.  For fp32 inputs the
  *        scores, softmax, g - gbar, dq, dw and the dk/dv row sums are fp64;
  *        the per-edge coefficients (scale * dl, p) that the source-token

@@ -11,7 +11,7 @@ from .binding import (  # noqa: F401
     gm_sea_backward, gm_sea_backward_noalloc, gm_sea_forward, gm_ser_sea_forward, ser_sea_forward,
     gm_sea_backward_workspace_bytes, gm_ser_backward, gm_ser_backward_workspace_bytes, gm_ser_forward,
     load, sea_backward, sea_forward, sea_workspace, ser_backward, ser_forward, ser_workspace,
-    stats_as_query_heads, stats_edge_copy, gm_leg_mix_forward, gm_leg_mix_backward,
+    stats_as_query_heads, stats_edge_copy, stats_shape, gm_leg_mix_forward, gm_leg_mix_backward,
     gm_leg_mix_backward_workspace_bytes, leg_mix, leg_mix_backward, gm_dense_refresh,
     dense_refresh,
 )

@@ -138,8 +138,17 @@ def gm_ser_forward(idx1, w1, idx2, w2, idx_out, w_out, stream=None, paths=None) 
           _ptr(idx_out), _ptr(w_out), s1, _ptr(paths), _stream(stream))
 
 
+def stats_shape(q: torch.Tensor, hkv: int, s1: int) -> tuple:
+    """Shape of the saved statistics for query tensor q [B, n, hq, d]:
+    [B, hkv, n, E G + 2, s1] 4-byte words, E = 1 for bf16 inputs (fp32 p / w)
+    and 2 for fp32 inputs (fp64 p / w)."""
+    B, n, hq, _ = q.shape
+    E = 1 if q.dtype == torch.bfloat16 else 2
+    return (B, hkv, n, E * (hq // hkv) + 2, s1)
+
+
 def gm_sea_forward(q, k, v, idx, w, o, scale=None, stream=None, stats=None) -> None:
-    """``stats`` (optional, [B, hkv, n, hq // hkv + 2, s1] fp32) receives p / w
+    """``stats`` (optional, ``stats_shape(q, hkv, s1)`` fp32 words) receives p / w
     per query head and slot, then a copy of the edge indices (int32 bits) and
     weights, for gm_sea_backward."""
     B, n, hq, d = q.shape
@@ -149,7 +158,7 @@ def gm_sea_forward(q, k, v, idx, w, o, scale=None, stream=None, stats=None) -> N
     _need(idx, "idx", (torch.int32,), (B, n, hkv, s1)); _need(w, "w", (torch.float32,), idx.shape)
     _need(o, "o", (q.dtype,), q.shape)
     if stats is not None:
-        _need(stats, "stats", (torch.float32,), (B, hkv, n, hq // hkv + 2, s1))
+        _need(stats, "stats", (torch.float32,), stats_shape(q, hkv, s1))
     scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
     _call("gm_sea_forward", B, n, hq, hkv, d, _act_dtype(q), scale, _ptr(q), _ptr(k), _ptr(v),
           _ptr(idx), _ptr(w), s1, _ptr(o), _ptr(stats), _stream(stream))
@@ -170,7 +179,7 @@ def gm_ser_sea_forward(idx1, w1, idx2, w2, q, k, v, idx_out, w_out, o, scale=Non
     _need(k, "k", (q.dtype,), (B, n, hkv, d)); _need(v, "v", (q.dtype,), (B, n, hkv, d))
     _need(o, "o", (q.dtype,), q.shape)
     if stats is not None:
-        _need(stats, "stats", (torch.float32,), (B, hkv, n, hq // hkv + 2, s1))
+        _need(stats, "stats", (torch.float32,), stats_shape(q, hkv, s1))
     if paths is not None:
         _need(paths, "paths", (torch.int64,), (B, n, hkv))
     scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
@@ -197,7 +206,7 @@ def gm_sea_backward(q, k, v, idx, w, dout, dq, dk, dv, dw, workspace, scale=None
     _need(dw, "dw", (torch.float32,), idx.shape)
     _need(workspace, "workspace", (torch.uint8, torch.float64))
     if stats is not None:
-        _need(stats, "stats", (torch.float32,), (B, hkv, n, hq // hkv + 2, s1))
+        _need(stats, "stats", (torch.float32,), stats_shape(q, hkv, s1))
     scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
     _call("gm_sea_backward", B, n, hq, hkv, d, _act_dtype(q), scale, _ptr(q), _ptr(k), _ptr(v),
           _ptr(idx), _ptr(w), s1, _ptr(dout), _ptr(stats), _ptr(dq), _ptr(dk), _ptr(dv),
@@ -219,7 +228,7 @@ def gm_sea_backward_noalloc(q, k, v, idx, w, dout, dq, dk, dv, dw, scale=None, s
     _need(dk, "dk", (torch.float32,), k.shape); _need(dv, "dv", (torch.float32,), v.shape)
     _need(dw, "dw", (torch.float32,), idx.shape)
     if stats is not None:
-        _need(stats, "stats", (torch.float32,), (B, hkv, n, hq // hkv + 2, s1))
+        _need(stats, "stats", (torch.float32,), stats_shape(q, hkv, s1))
     scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
     _call("gm_sea_backward_noalloc", B, n, hq, hkv, d, _act_dtype(q), scale, _ptr(q), _ptr(k),
           _ptr(v), _ptr(idx), _ptr(w), s1, _ptr(dout), _ptr(stats), _ptr(dq), _ptr(dk),
@@ -344,12 +353,12 @@ def ser_forward(idx1, w1, idx2, w2, s1, stream=None, save_paths=False):
 
 
 def sea_forward(q, k, v, idx, w, scale=None, stream=None, save_stats=False):
-    """o, or (o, stats) with ``save_stats`` (stats [B, hkv, n, G + 2, s1]:
+    """o, or (o, stats) with ``save_stats`` (stats ``stats_shape(q, hkv, s1)``:
     p / w per query head and slot, then the edge row, for sea_backward)."""
     o = torch.empty_like(q)
     B, n, hq, _ = q.shape
     hkv, s1 = idx.shape[2], idx.shape[3]
-    stats = (torch.empty((B, hkv, n, hq // hkv + 2, s1), dtype=torch.float32, device=q.device)
+    stats = (torch.empty(stats_shape(q, hkv, s1), dtype=torch.float32, device=q.device)
              if save_stats else None)
     gm_sea_forward(q, k, v, idx, w, o, scale, stream, stats)
     return (o, stats) if save_stats else o
@@ -363,7 +372,7 @@ def ser_sea_forward(idx1, w1, idx2, w2, s1, q, k, v, scale=None, stream=None, sa
     io = torch.empty((B, n, hkv, s1), dtype=torch.int32, device=idx1.device)
     wo = torch.empty((B, n, hkv, s1), dtype=torch.float32, device=idx1.device)
     o = torch.empty_like(q)
-    stats = (torch.empty((B, hkv, n, hq // hkv + 2, s1), dtype=torch.float32, device=q.device)
+    stats = (torch.empty(stats_shape(q, hkv, s1), dtype=torch.float32, device=q.device)
              if save_stats else None)
     paths = (torch.empty((B, n, hkv), dtype=torch.int64, device=q.device)
              if save_paths else None)
@@ -414,11 +423,18 @@ def check_edges(idx, w, stream=None):
     return int(c[0]), int(c[1])
 
 
-def stats_as_query_heads(stats: torch.Tensor) -> torch.Tensor:
-    """The p / w rows of the saved statistics [B, hkv, n, G + 2, s1] as
-    [B, n, hq, s1]."""
-    B, hkv, n, G2, s1 = stats.shape
-    return stats[:, :, :, :G2 - 2].permute(0, 2, 1, 3, 4).reshape(B, n, hkv * (G2 - 2), s1)
+def stats_as_query_heads(stats: torch.Tensor, G: int) -> torch.Tensor:
+    """The p / w rows of the saved statistics [B, hkv, n, E G + 2, s1] of G
+    query heads per KV head as [B, n, hq, s1] (fp32 for E = 1, fp64 for
+    E = 2)."""
+    B, hkv, n, R, s1 = stats.shape
+    E = (R - 2) // G
+    if E not in (1, 2) or E * G + 2 != R:
+        raise ValueError(f"statistics of {R} rows do not fit G = {G}")
+    pw = stats[:, :, :, :E * G].reshape(B, hkv, n, E * G * s1)
+    if E == 2:
+        pw = pw.contiguous().view(torch.float64)          # G s1 doubles per unit
+    return pw.reshape(B, hkv, n, G, s1).permute(0, 2, 1, 3, 4).reshape(B, n, hkv * G, s1)
 
 
 def stats_edge_copy(stats: torch.Tensor):

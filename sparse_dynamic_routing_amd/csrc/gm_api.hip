@@ -170,7 +170,8 @@ gm_status gm_sea_forward(int B, int n, int hq, int hkv, int d, gm_dtype dt, floa
     const size_t es = dt == GM_BF16 ? 2 : 4;
     const size_t qb = (size_t)B * n * hq * d * es, kb = (size_t)B * n * hkv * d * es;
     const size_t eb = (size_t)B * n * hkv * s1 * 4;
-    const size_t sb = (size_t)B * n * (hq + 2 * hkv) * s1 * 4;   // (G + 2) rows per unit
+    // statistics: E G + 2 rows of s1 words per unit (E = 2 for fp32 inputs)
+    const size_t sb = (size_t)B * n * ((dt == GM_BF16 ? 1 : 2) * hq + 2 * hkv) * s1 * 4;
     if (overlaps(o, qb, q, qb) || overlaps(o, qb, k, kb) || overlaps(o, qb, v, kb) ||
         overlaps(o, qb, idx, eb) || overlaps(o, qb, w, eb))
         return GM_ERR_ALIAS;
@@ -202,7 +203,7 @@ gm_status gm_ser_sea_forward(int B, int n, int hq, int hkv, int d, gm_dtype dt, 
     const size_t es = dt == GM_BF16 ? 2 : 4;
     const size_t rows = (size_t)B * n * hkv;
     const size_t qb = (size_t)B * n * hq * d * es, kb = (size_t)B * n * hkv * d * es;
-    const size_t sb = (size_t)B * n * (hq + 2 * hkv) * s1 * 4;
+    const size_t sb = (size_t)B * n * ((dt == GM_BF16 ? 1 : 2) * hq + 2 * hkv) * s1 * 4;
     const void* ins[7] = {idx1, w1, idx2, w2, q, k, v};
     const size_t inb[7] = {rows * s2 * 4, rows * s2 * 4, rows * s3 * 4, rows * s3 * 4, qb, kb, kb};
     const void* outs[4] = {idx_out, w_out, o, stats};
@@ -384,7 +385,8 @@ gm_status sea_backward_checks(int B, int n, int hq, int hkv, int d, gm_dtype dt,
     const size_t es = dt == GM_BF16 ? 2 : 4;
     const size_t nq = (size_t)B * n * hq * d, nk = (size_t)B * n * hkv * d;
     const size_t ne = (size_t)B * n * hkv * s1;
-    const size_t ns = (size_t)B * n * (hq + 2 * hkv) * s1;   // statistics: (G + 2) rows per unit
+    // statistics: E G + 2 rows of s1 words per unit (E = 2 for fp32 inputs)
+    const size_t ns = (size_t)B * n * ((dt == GM_BF16 ? 1 : 2) * hq + 2 * hkv) * s1;
     const void* ins[7] = {q, k, v, dout, idx, w, stats};
     const size_t inb[7] = {nq * es, nk * es, nk * es, nq * es, ne * 4, ne * 4,
                            stats ? ns * 4 : 0};

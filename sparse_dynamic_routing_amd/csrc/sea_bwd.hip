@@ -462,6 +462,41 @@ struct Pos {
     int unit, bi, kvrow0, prow;   // prow = pair * n + i (pair-major row)
 };
 
+// The forward's saved statistics of a unit (pair-major row prow): E G + 2
+// rows of s 4-byte words, p / w per head and slot in the accumulation type A
+// (E = sizeof(A) / 4: fp32 for bf16 inputs, fp64 for fp32 inputs), then the
+// unit's edge indices and weights.
+template <typename A>
+__device__ __forceinline__ const float* saved_edge_copy(const float* stats, size_t prow, int G,
+                                                        int s) {
+    constexpr int E = sizeof(A) / 4;
+    return stats + (prow * (E * G + 2) + E * G) * s;
+}
+template <typename A, int S, bool VEC>
+__device__ __forceinline__ void load_saved_pw(const float* stats, size_t prow, int G, int s, int g,
+                                              A (&st)[S]) {
+    if constexpr (sizeof(A) == 4) {
+        const float* sp = stats + (prow * (G + 2) + g) * s;
+        if constexpr (VEC) {
+            const float4 s4 = *reinterpret_cast<const float4*>(sp);
+            st[0] = s4.x; st[1] = s4.y; st[2] = s4.z; st[3] = s4.w;
+        } else {
+#pragma unroll
+            for (int t = 0; t < S; ++t) st[t] = sp[t < s ? t : s - 1];
+        }
+    } else {
+        const double* sp = reinterpret_cast<const double*>(stats) + (prow * (G + 1) + g) * s;
+        if constexpr (VEC) {
+            const double2 lo = *reinterpret_cast<const double2*>(sp);
+            const double2 hi = *reinterpret_cast<const double2*>(sp + 2);
+            st[0] = lo.x; st[1] = lo.y; st[2] = hi.x; st[3] = hi.y;
+        } else {
+#pragma unroll
+            for (int t = 0; t < S; ++t) st[t] = sp[t < s ? t : s - 1];
+        }
+    }
+}
+
 __device__ __forceinline__ Pos pos_of(const SegPlan& sp, int x, int q) {
     int pair, i;
     sched_item(sp, x, q, pair, i);
@@ -566,7 +601,7 @@ __global__ __launch_bounds__(kBlock) void sea_bwd_src_row_kernel(SeaBwdFast a) {
             // the forward's pair-major copy of the edge row: contiguous for
             // the consecutive tokens of a wavefront, where the interleaved
             // rows of the eight KV heads would bring whole lines to every XCD
-            const float* e = a.stats + ((size_t)it.pos.prow * (G + 2) + G) * a.s;
+            const float* e = saved_edge_copy<A>(a.stats, (size_t)it.pos.prow, G, a.s);
             if constexpr (VEC) {
                 const int4 j4 = *reinterpret_cast<const int4*>(e);
                 const float4 w4 = *reinterpret_cast<const float4*>(e + 4);
@@ -651,7 +686,7 @@ __global__ __launch_bounds__(kBlock) void sea_bwd_src_row_kernel(SeaBwdFast a) {
 #pragma unroll
         for (int g0 = 0; g0 < G; g0 += GC) {
             uint4 qr[GC], dr[GC];
-            float st[GC][S];
+            A st[GC][S];
 #pragma unroll
             for (int g = 0; g < GC; ++g) {
                 if constexpr (BLK) {
@@ -663,14 +698,7 @@ __global__ __launch_bounds__(kBlock) void sea_bwd_src_row_kernel(SeaBwdFast a) {
                         st[g][2] = row_bcast<6>(brec); st[g][3] = row_bcast<7>(brec);
                     }
                 } else if constexpr (SAVED) {
-                    const float* sp = a.stats + ((size_t)cur.pos.prow * (G + 2) + g0 + g) * a.s;
-                    if constexpr (VEC) {
-                        const float4 s4 = *reinterpret_cast<const float4*>(sp);
-                        st[g][0] = s4.x; st[g][1] = s4.y; st[g][2] = s4.z; st[g][3] = s4.w;
-                    } else {
-#pragma unroll
-                        for (int t = 0; t < S; ++t) st[g][t] = sp[t < a.s ? t : a.s - 1];
-                    }
+                    load_saved_pw<A, S, VEC>(a.stats, (size_t)cur.pos.prow, G, a.s, g0 + g, st[g]);
                 } else {
                     qr[g] = load_split_nt<V>(a.q + (qrow + g0 + g) * ROW, r);
                 }
@@ -805,7 +833,7 @@ __global__ __launch_bounds__(kBlock) void sea_bwd_src_wide_kernel(SeaBwdFast a) 
             // the forward's pair-major copy of the edge row: contiguous for
             // the consecutive tokens of a wavefront, where the interleaved
             // rows of the eight KV heads would bring whole lines to every XCD
-            const float* e = a.stats + ((size_t)it.pos.prow * (G + 2) + G) * a.s;
+            const float* e = saved_edge_copy<A>(a.stats, (size_t)it.pos.prow, G, a.s);
             if constexpr (VEC) {
                 const int4 j4 = *reinterpret_cast<const int4*>(e);
                 const float4 w4 = *reinterpret_cast<const float4*>(e + 4);
@@ -880,18 +908,11 @@ __global__ __launch_bounds__(kBlock) void sea_bwd_src_wide_kernel(SeaBwdFast a) 
 #pragma unroll
         for (int g0 = 0; g0 < G; g0 += GC) {
             uint4 qr[GC][NP], dr[GC][NP];
-            float st[GC][S];
+            A st[GC][S];
 #pragma unroll
             for (int g = 0; g < GC; ++g) {
                 if constexpr (SAVED) {
-                    const float* sp = a.stats + ((size_t)cur.pos.prow * (G + 2) + g0 + g) * a.s;
-                    if constexpr (VEC) {
-                        const float4 s4 = *reinterpret_cast<const float4*>(sp);
-                        st[g][0] = s4.x; st[g][1] = s4.y; st[g][2] = s4.z; st[g][3] = s4.w;
-                    } else {
-#pragma unroll
-                        for (int t = 0; t < S; ++t) st[g][t] = sp[t < a.s ? t : a.s - 1];
-                    }
+                    load_saved_pw<A, S, VEC>(a.stats, (size_t)cur.pos.prow, G, a.s, g0 + g, st[g]);
                 } else {
 #pragma unroll
                     for (int k = 0; k < NP; ++k)
@@ -1420,7 +1441,7 @@ hipError_t dispatch_g(const SeaBwdArgs& a, int G, long long E, hipStream_t st) {
 template <typename T, int G, int S, bool VEC, bool GLOBAL, bool SAVED, int R>
 void launch_src_k(const SeaBwdFast& a, hipStream_t st) {
     if constexpr (R == 1) {
-        if constexpr (SAVED && VEC && G == 2 && S == 4) {
+        if constexpr (SAVED && VEC && G == 2 && S == 4 && std::is_same<T, bf16_t>::value) {
             if ((a.sp.L & 3) == 0) {
                 const void* fn = reinterpret_cast<const void*>(
                     &sea_bwd_src_row_kernel<T, G, S, VEC, GLOBAL, SAVED, true>);
@@ -1444,9 +1465,9 @@ void launch_src_k(const SeaBwdFast& a, hipStream_t st) {
 
 template <typename T, int G, int S, bool VEC, bool GLOBAL, int R>
 void launch_src(const SeaBwdFast& a, hipStream_t st) {
-    // the saved statistics replace the recomputed softmax for bf16 inputs;
-    // fp32 inputs keep their fp64 recomputation
-    if (std::is_same<T, bf16_t>::value && a.stats) {
+    // the saved statistics (fp32 p / w for bf16 inputs, fp64 for fp32
+    // inputs) replace the recomputed softmax
+    if (a.stats) {
         launch_src_k<T, G, S, VEC, GLOBAL, true, R>(a, st);
     } else {
         launch_src_k<T, G, S, VEC, GLOBAL, false, R>(a, st);

@@ -38,14 +38,28 @@ TeamShape sea_team(int d, int elem_bytes, int s) {
 
 namespace {
 
-// The saved statistics of a unit (pair-major row `prow`) are (G + 2) rows
-// of s floats: p / w per query head, then the unit's edge indices (int32
-// bits) and weights, a pair-major copy of its edge row for the backward.
+// The saved statistics of a unit (pair-major row `prow`) are E G + 2 rows
+// of s 4-byte words: p / w per query head and slot, in the precision the
+// backward computes in (E = 1: fp32 for bf16 inputs; E = 2: fp64 for fp32
+// inputs, G s doubles), then the unit's edge indices (int32 bits) and
+// weights, a pair-major copy of its edge row for the backward.  A is the
+// accumulation type (float for bf16 inputs, double for fp32), so E =
+// sizeof(A) / 4.
+template <typename A>
 __device__ __forceinline__ void store_edge_copy(float* stats, size_t prow, int G, int s, int t,
                                                 int j, float wt) {
-    float* e = stats + (prow * (G + 2) + G) * s;
+    constexpr int E = sizeof(A) / 4;
+    float* e = stats + (prow * (E * G + 2) + E * G) * s;
     e[t] = __int_as_float(j);
     e[s + t] = wt;
+}
+template <typename A>
+__device__ __forceinline__ void store_pw(float* stats, size_t prow, int G, int s, int g, int t,
+                                         A v) {
+    if constexpr (sizeof(A) == 4)
+        stats[(prow * (G + 2) + g) * s + t] = v;
+    else
+        reinterpret_cast<double*>(stats)[(prow * (G + 1) + g) * s + t] = v;
 }
 
 struct SeaFwdArgs {
@@ -55,7 +69,7 @@ struct SeaFwdArgs {
     const int32_t* idx;
     const float* w;
     void* o;
-    float* stats;   // [B][hkv][n][G + 2][s]: p / w per live slot (0 dead), idx, w; or null
+    float* stats;   // [B][hkv][n][E G + 2][s]: p / w per live slot (0 dead), idx, w; or null
     int n, hq, hkv, d, s, U;
     float scale;
     TeamShape ts;
@@ -129,13 +143,13 @@ __global__ __launch_bounds__(kBlock) void sea_fwd_kernel(SeaFwdArgs a) {
             const int off = reduce_scatter(ov, tl, R, team, len);
             const A inv = Z > 0 ? (A)1 / Z : (A)0;
             if (a.stats && r == 0 && t < a.s)
-                a.stats[(srow * (G + 2) + g) * a.s + t] =
-                    live ? (float)(aexp2(dot * c - M) * inv) : 0.0f;
+                store_pw<A>(a.stats, srow, G, a.s, g, t, live ? aexp2(dot * c - M) * inv : (A)0);
 #pragma unroll
             for (int e = 0; e < V; ++e) ov[e] *= inv;
             if (storer) store_len(op + g * d + off, ov, len);
         }
-        if (a.stats && r == 0 && t < a.s) store_edge_copy(a.stats, srow, G, a.s, t, ip[t], wp[t]);
+        if (a.stats && r == 0 && t < a.s)
+            store_edge_copy<A>(a.stats, srow, G, a.s, t, ip[t], wp[t]);
         return;
     }
 
@@ -205,9 +219,9 @@ __global__ __launch_bounds__(kBlock) void sea_fwd_kernel(SeaFwdArgs a) {
                 for (int e = 0; e < V; ++e) dot += qg[e] * kr[e];
                 dot = sum_bits(dot, 1, R);
                 if (r == 0 && t < a.s) {
-                    a.stats[(srow * (G + 2) + g) * a.s + t] =
-                        live ? (float)(aexp2(dot * c - M) * inv) : 0.0f;
-                    if (g == 0) store_edge_copy(a.stats, srow, G, a.s, t, ip[t], wp[t]);
+                    store_pw<A>(a.stats, srow, G, a.s, g, t,
+                                live ? aexp2(dot * c - M) * inv : (A)0);
+                    if (g == 0) store_edge_copy<A>(a.stats, srow, G, a.s, t, ip[t], wp[t]);
                 }
             }
         }
@@ -402,7 +416,9 @@ __global__ __launch_bounds__(kBlock) void sea_fwd_row_kernel(SeaFwdFast a) {
         for (int t = 0; t < S; ++t) lw[t] = live[t] ? fast_log2((A)cur.wt[t]) : NEG;
         // the unit's statistics, p / w per head and slot, then its edge
         // indices and weights, in one store per lane when they fit 16 lanes
-        const bool st_one = (G + 2) * a.s <= 16;
+        // (fp32 words only: fp64 p / w, E = 2, store per head)
+        constexpr int E = sizeof(A) / 4;
+        const bool st_one = E == 1 && (G + 2) * a.s <= 16;
         float st_val = 0.0f;
         if (a.stats) {
             // lanes G s .. (G + 2) s - 1: the edge copy (index bits, then weight)
@@ -418,7 +434,7 @@ __global__ __launch_bounds__(kBlock) void sea_fwd_row_kernel(SeaFwdFast a) {
             if (st_one) {
                 st_val = ev;
             } else if (r < a.s) {
-                float* e = a.stats + ((size_t)cur.pos.prow * (G + 2) + G) * a.s;
+                float* e = a.stats + ((size_t)cur.pos.prow * (E * G + 2) + E * G) * a.s;
                 float jv = 0.0f, wv = 0.0f;
 #pragma unroll
                 for (int t = 0; t < S; ++t) {
@@ -470,11 +486,18 @@ __global__ __launch_bounds__(kBlock) void sea_fwd_row_kernel(SeaFwdFast a) {
                         mine = t0 == t ? sd[t] : mine;
                         ml = t0 == t ? live[t] : ml;
                     }
-                    if (t0 >= 0 && t0 < a.s) st_val = ml ? (float)(fast_exp2(mine - M) * inv) : 0.0f;
-                    if (!st_one && t0 >= 0 && t0 < a.s)
-                        __builtin_nontemporal_store(
-                            st_val,
-                            a.stats + ((size_t)cur.pos.prow * (G + 2) + g0 + g) * a.s + t0);
+                    const A pv = ml ? fast_exp2(mine - M) * inv : (A)0;
+                    if (t0 >= 0 && t0 < a.s) st_val = (float)pv;
+                    if (!st_one && t0 >= 0 && t0 < a.s) {
+                        if constexpr (E == 1)
+                            __builtin_nontemporal_store(
+                                st_val,
+                                a.stats + ((size_t)cur.pos.prow * (G + 2) + g0 + g) * a.s + t0);
+                        else
+                            __builtin_nontemporal_store(
+                                (double)pv, reinterpret_cast<double*>(a.stats) +
+                                                ((size_t)cur.pos.prow * (G + 1) + g0 + g) * a.s + t0);
+                    }
                 }
 #pragma unroll
                 for (int k = 0; k < NP; ++k) {

@@ -192,7 +192,9 @@ def download(got: dict) -> dict:
     """Every output of run_gpu as host numpy (statistics per query head)."""
     out = {}
     for name, t in got.items():
-        out[name] = host(gm.stats_as_query_heads(t) if name == "stats" else t)
+        if name == "stats":
+            t = gm.stats_as_query_heads(t, got["o"].shape[2] // t.shape[1])
+        out[name] = host(t)
     return out
 
 
@@ -205,7 +207,7 @@ def compare_pair(p: synth.Preset, got: dict, ref: dict, b: int, h: int, worst=No
     G = p.hq // p.hkv
     X = TOL[p.dtype]
     hst = lambda name: got[name] if isinstance(got[name], np.ndarray) else (  # noqa: E731
-        host(gm.stats_as_query_heads(got[name])) if name == "stats" else host(got[name]))
+        host(gm.stats_as_query_heads(got[name], G)) if name == "stats" else host(got[name]))
 
     def check(name, g, r, bar):
         e = assert_close(name, g, r, bar, quiet=quiet)

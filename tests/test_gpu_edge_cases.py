@@ -92,7 +92,7 @@ def test_sea_forward_backward_shapes(dtype, d, G, s, n):
         assert_close("o", host(o), ro, X)
         if with_stats:
             live = np.repeat(w > 0, G, axis=2)
-            hs = host(gm.stats_as_query_heads(st))
+            hs = host(gm.stats_as_query_heads(st, G))
             assert (hs[~live] == 0).all()
             assert_close("p (statistics * w)", hs * np.repeat(w, G, axis=2), rp, 1e-4)
             ei, ew = gm.stats_edge_copy(st)      # the backward's copy of the edge rows

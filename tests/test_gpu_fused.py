@@ -27,7 +27,11 @@ def _two_calls(idx1, w1, idx2, w2, s1, q, k, v):
 
 
 def _check_equal(fused, ref):
+    # bit patterns: the statistics of fp32 inputs hold fp64 values, whose
+    # halves read as fp32 words can be NaN patterns
     for name, a, b in zip(("idx'", "w'", "o", "stats"), fused, ref):
+        if a.dtype == torch.float32:
+            a, b = a.view(torch.int32), b.view(torch.int32)
         assert torch.equal(a, b), f"{name}: fused call differs from the two calls"
 
 

@@ -39,7 +39,7 @@ class LayerPass:
         self.ia = torch.empty(idx.shape, dtype=torch.int32, device="cuda")
         self.wa = torch.empty(idx.shape, **f32)
         self.o = torch.empty_like(self.q)
-        self.stats = torch.empty((B, hkv, n, hq // hkv + 2, s), dtype=torch.float32,
+        self.stats = torch.empty(gm.stats_shape(self.q, hkv, s), dtype=torch.float32,
                                  device="cuda")
         self.dq = torch.empty(qs, **f32)
         self.dk = torch.empty(ks, **f32)

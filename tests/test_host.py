@@ -81,3 +81,36 @@ def test_source_hash_ignores_comments_only():
     s = 'const char* m = "a // b"; // tail'
     assert '"a // b"' in ct(s) and "tail" not in ct(s)
     assert ct('x = 1; /* multi\nline */ y = 2;') == "x = 1; y = 2;"
+
+
+def test_stats_helpers_read_both_layouts():
+    """The saved statistics hold fp32 p / w (bf16 inputs) or fp64 p / w (fp32
+    inputs, two words each); the helpers give them per query head, and the
+    edge copy, from either layout."""
+    B, hkv, n, G, s1 = 2, 2, 5, 3, 3
+    q16 = torch.zeros(B, n, hkv * G, 8, dtype=torch.bfloat16)
+    q32 = torch.zeros(B, n, hkv * G, 8, dtype=torch.float32)
+    assert gm.stats_shape(q16, hkv, s1) == (B, hkv, n, G + 2, s1)
+    assert gm.stats_shape(q32, hkv, s1) == (B, hkv, n, 2 * G + 2, s1)
+    g = torch.Generator().manual_seed(5)
+    pw = torch.rand(B, hkv, n, G, s1, dtype=torch.float64, generator=g)
+    idx = torch.randint(0, 5, (B, hkv, n, s1), dtype=torch.int32, generator=g)
+    w = torch.rand(B, hkv, n, s1, generator=g)
+    want = pw.permute(0, 2, 1, 3, 4).reshape(B, n, hkv * G, s1)
+    for E in (1, 2):
+        st = torch.zeros(B, hkv, n, E * G + 2, s1)
+        flat = st.view(B, hkv, n, (E * G + 2) * s1)
+        if E == 1:
+            flat[..., :G * s1] = pw.float().reshape(B, hkv, n, G * s1)
+        else:
+            flat[..., :2 * G * s1] = pw.reshape(B, hkv, n, G * s1).contiguous().view(
+                torch.float32).reshape(B, hkv, n, 2 * G * s1)
+        st[:, :, :, E * G] = idx.view(torch.float32)
+        st[:, :, :, E * G + 1] = w
+        got = gm.stats_as_query_heads(st, G)
+        assert got.dtype == (torch.float32 if E == 1 else torch.float64)
+        assert torch.equal(got.double(), want.float().double() if E == 1 else want)
+        ei, ew = gm.stats_edge_copy(st)
+        assert torch.equal(ei, idx.permute(0, 2, 1, 3)) and torch.equal(ew, w.permute(0, 2, 1, 3))
+    with pytest.raises(ValueError):
+        gm.stats_as_query_heads(torch.zeros(B, hkv, n, 7, s1), 3)
