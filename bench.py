@@ -118,6 +118,7 @@ def stage_bytes(stage: str, p: synth.Preset) -> int:
     st = (4 if es == 2 else 8) * G * s1 if p.backward else 0
     pm = 8 if p.backward and max(p.s1, p.s2, p.s3) <= 4 else 0   # the SER path map
     return {"ser_fwd": 8 * p.s2 + 8 * s1 + pm,
+            "ser_chain2": 8 * p.s2 + 8 * s1,      # A0 in, A2 out; A1 never leaves the chip
             "sea_fwd": qrow + 8 * s1 + kv + qrow + st + (8 * s1 if p.backward else 0),
             "sea_bwd": 2 * qrow + 8 * s1 + kv + st + 4 * G * p.d + 4 * s1 + 8 * p.d,
             "ser_bwd": (8 * p.s2 + pm + 4 * s1 + 4 * p.s2 if pm
@@ -166,6 +167,9 @@ def parse():
     ap.add_argument("--fused", action="store_true",
                     help="run SER and SEA forward as the one fused call gm_ser_sea_forward "
                          "(measured slower than the two calls on this workload)")
+    ap.add_argument("--chain2", action="store_true",
+                    help="with --config stack21: the two chained SER steps as the one call "
+                         "gm_ser_forward_chain2")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="instead of the pass, run a plain device copy of MIB MiB "
                          "(the known-size reference for hardware byte counters)")
@@ -279,6 +283,11 @@ class Pass:
                             lambda s_=src, d_=dst, pm_=pm: gm.gm_ser_forward(*s_, *s_, *d_,
                                                                             paths=pm_)))
                 edges = dst
+            elif st == "ser_chain2":   # two chained SER steps in one launch
+                out.append(("gm_ser_forward_chain2",
+                            lambda: gm.gm_ser_forward_chain2(self.idx, self.w, self.ia, self.wa)))
+                n_ser = 1
+                edges = (self.ia, self.wa)
             elif st == "sea_fwd":
                 e = (self.ia, self.wa) if n_ser else (self.idx, self.w)
                 out.append(("gm_sea_forward",
@@ -386,6 +395,13 @@ def run_config(a):
     events around each stage) and print one JSON line for it."""
     p = synth.PRESETS[a.config]
     stages = CONFIG_STAGES[a.config]
+    label = a.config
+    if a.chain2:
+        if stages[:2] != ["ser_fwd", "ser_fwd"]:
+            raise SystemExit(f"--chain2 needs a configuration with two chained SER steps, "
+                             f"not {a.config}")
+        stages = ["ser_chain2"] + stages[2:]
+        label = f"{a.config}_chain2"
     ps = Pass(p)
     calls = ps.stage_calls(stages)
     for _ in range(a.warmup):
@@ -406,9 +422,9 @@ def run_config(a):
     ms = float(np.mean([ev[s_][0].elapsed_time(ev[s_][-1]) for s_ in range(a.steps)]))
     U = p.units
     step_bytes = sum(stage_bytes(st, p) for st in stages) * U
-    counter = profiled_step_bytes(a.config)
+    counter = profiled_step_bytes(label)
     print(json.dumps({
-        "config": a.config, "stages": stages, "units_per_step": U,
+        "config": label, "stages": stages, "units_per_step": U,
         "shape": {"B": p.B, "n": p.n, "hq": p.hq, "hkv": p.hkv, "d": p.d,
                   "s1": p.s1, "s2": p.s2, "dtype": str(p.dtype).replace("torch.", "")},
         "ms_per_step": ms, "value": U / (ms * 1e-3), "unit": "tokens·KV-heads/s",
@@ -420,7 +436,7 @@ def run_config(a):
             "bytes": counter, "GBps": counter / (ms * 1e-3) / 1e9,
             "frac_of_peak": counter / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS,
             "over_compulsory": counter / step_bytes,
-            "source": f"profiles/{a.config}_kernels.md"},
+            "source": f"profiles/{label}_kernels.md"},
         "steps": a.steps, "warmup": a.warmup, "data": "synthetic"}), flush=True)
 
 

@@ -99,6 +99,27 @@ gm_status gm_ser_forward(int B, int n, int hkv,
                          hipStream_t stream);
 
 /*
+ * Two chained referral steps in one call (ai.info Key Contributions 2: the
+ * edge matrix raised to a power, one referral step per factor; Methodology:
+ * each step mixes the edges the previous step left):
+ *   A1 = Sparsify_s(A0 A0), A2 = Sparsify_s(A1 A1)
+ *   in   idx, w            [B][n][hkv][s]  A0, s = 2 or 4 (else
+ *                          GM_ERR_UNSUPPORTED)
+ *   out  idx_mid, w_mid    [B][n][hkv][s]  A1, optional (both NULL: not
+ *                          written; one NULL: GM_ERR_NULL)
+ *        idx_out, w_out    [B][n][hkv][s]  A2
+ * Every pointer must be aligned to s*4 bytes (GM_ERR_ALIGN) and no output
+ * may overlap another array (GM_ERR_ALIAS).  A1 and A2 are bitwise what two
+ * gm_ser_forward calls with s1 = s2 = s3 = s and both legs equal give.
+ * One launch: each unit recomputes the rows of A1 it needs (its own and
+ * those at its s targets) instead of waiting for other workgroups to write
+ * them, so no A1 round trip through memory is needed.
+ */
+gm_status gm_ser_forward_chain2(int B, int n, int hkv, const int32_t* idx, const float* w,
+                                int s, int32_t* idx_mid, float* w_mid,
+                                int32_t* idx_out, float* w_out, hipStream_t stream);
+
+/*
  * Sparse edge attention, forward (ai.info Key Contributions 3: edge indices
  * pick the positions that supply keys and values, node factor = scaled
  * query-key score, edge factor = log edge weight, product of experts;

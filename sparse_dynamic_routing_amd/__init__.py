@@ -13,5 +13,5 @@ from .binding import (  # noqa: F401
     load, sea_backward, sea_forward, sea_workspace, ser_backward, ser_forward, ser_workspace,
     stats_as_query_heads, stats_edge_copy, stats_shape, gm_leg_mix_forward, gm_leg_mix_backward,
     gm_leg_mix_backward_workspace_bytes, leg_mix, leg_mix_backward, gm_dense_refresh,
-    dense_refresh,
+    dense_refresh, gm_ser_forward_chain2, ser_forward_chain2,
 )

@@ -24,7 +24,7 @@ GM_F32, GM_BF16 = 0, 1
 STATUS = {0: "GM_OK", 1: "GM_ERR_NULL", 2: "GM_ERR_SHAPE", 3: "GM_ERR_UNSUPPORTED",
           4: "GM_ERR_WORKSPACE", 5: "GM_ERR_HIP", 6: "GM_ERR_ALIGN", 7: "GM_ERR_ALIAS",
           8: "GM_ERR_TOO_LARGE"}
-EXPORTS = ("gm_ser_forward", "gm_sea_forward", "gm_sea_backward_workspace_bytes",
+EXPORTS = ("gm_ser_forward", "gm_ser_forward_chain2", "gm_sea_forward", "gm_sea_backward_workspace_bytes",
            "gm_sea_backward", "gm_sea_backward_noalloc", "gm_ser_sea_forward", "gm_decode_step", "gm_dense_refresh", "gm_leg_mix_forward",
            "gm_leg_mix_backward_workspace_bytes", "gm_leg_mix_backward",
            "gm_ser_backward_workspace_bytes", "gm_ser_backward", "gm_check_edges",
@@ -51,6 +51,7 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib = ctypes.CDLL(path)
     sig = {
         "gm_ser_forward": [_I, _I, _I, _P, _P, _I, _P, _P, _I, _P, _P, _I, _P, _P],
+        "gm_ser_forward_chain2": [_I, _I, _I, _P, _P, _I, _P, _P, _P, _P, _P],
         "gm_sea_forward": [_I, _I, _I, _I, _I, _I, _F, _P, _P, _P, _P, _P, _I, _P, _P, _P],
         "gm_sea_backward_workspace_bytes": [_I, _I, _I, _I, _I],
         "gm_sea_backward": [_I, _I, _I, _I, _I, _I, _F, _P, _P, _P, _P, _P, _I, _P, _P,
@@ -333,6 +334,22 @@ def gm_ser_backward(idx1, w1, idx2, w2, idx_out, w_out, dw_out, dw1, dw2, worksp
           _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream))
 
 
+def gm_ser_forward_chain2(idx, w, idx_out, w_out, idx_mid=None, w_mid=None,
+                          stream=None) -> None:
+    """Two chained referral steps: A2 -> (idx_out, w_out), A1 -> (idx_mid,
+    w_mid) when given."""
+    B, n, hkv, s = idx.shape
+    _need(idx, "idx", (torch.int32,)); _need(w, "w", (torch.float32,), idx.shape)
+    _need(idx_out, "idx_out", (torch.int32,), idx.shape)
+    _need(w_out, "w_out", (torch.float32,), idx.shape)
+    if idx_mid is not None:
+        _need(idx_mid, "idx_mid", (torch.int32,), idx.shape)
+    if w_mid is not None:
+        _need(w_mid, "w_mid", (torch.float32,), idx.shape)
+    _call("gm_ser_forward_chain2", B, n, hkv, _ptr(idx), _ptr(w), s, _ptr(idx_mid),
+          _ptr(w_mid), _ptr(idx_out), _ptr(w_out), _stream(stream))
+
+
 def gm_check_edges(idx, w, counts, stream=None) -> None:
     B, n, hkv, s = idx.shape
     _need(idx, "idx", (torch.int32,)); _need(w, "w", (torch.float32,), idx.shape)
@@ -350,6 +367,17 @@ def ser_forward(idx1, w1, idx2, w2, s1, stream=None, save_paths=False):
              if save_paths else None)
     gm_ser_forward(idx1, w1, idx2, w2, idx_out, w_out, stream, paths)
     return (idx_out, w_out, paths) if save_paths else (idx_out, w_out)
+
+
+def ser_forward_chain2(idx, w, stream=None, save_mid=False):
+    """(idx_out, w_out) of Sp(A1 A1) with A1 = Sp(A0 A0), A0 = (idx, w), in
+    one call; with ``save_mid`` also (idx_mid, w_mid) = A1."""
+    idx_out = torch.empty_like(idx)
+    w_out = torch.empty_like(w)
+    idx_mid = torch.empty_like(idx) if save_mid else None
+    w_mid = torch.empty_like(w) if save_mid else None
+    gm_ser_forward_chain2(idx, w, idx_out, w_out, idx_mid, w_mid, stream)
+    return (idx_out, w_out, idx_mid, w_mid) if save_mid else (idx_out, w_out)
 
 
 def sea_forward(q, k, v, idx, w, scale=None, stream=None, save_stats=False):

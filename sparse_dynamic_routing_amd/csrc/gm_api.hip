@@ -99,7 +99,7 @@ bool overlaps(const void* a, size_t an, const void* b, size_t bn) {
 
 extern "C" {
 
-int gm_abi_version(void) { return 7; }
+int gm_abi_version(void) { return 8; }
 
 const char* gm_status_string(gm_status s) {
     switch (s) {
@@ -154,6 +154,33 @@ gm_status gm_ser_forward(int B, int n, int hkv, const int32_t* idx1, const float
     if ((st = check_paths(paths, s1, s2, s3, rows, arr, arb, 6)) != GM_OK) return st;
     return hip_status(gm::launch_ser_forward(B, n, hkv, idx1, w1, s2, idx2, w2, s3, idx_out,
                                              w_out, s1, paths, stream));
+}
+
+gm_status gm_ser_forward_chain2(int B, int n, int hkv, const int32_t* idx, const float* w,
+                                int s, int32_t* idx_mid, float* w_mid, int32_t* idx_out,
+                                float* w_out, hipStream_t stream) {
+    gm_status st = check_ser(B, n, hkv, s, s, s);
+    if (st != GM_OK) return st;
+    if (s != 2 && s != 4) return GM_ERR_UNSUPPORTED;
+    if (empty(B, n, hkv)) return GM_OK;
+    if ((st = check_edge_ptrs(idx, w)) != GM_OK) return st;
+    if ((st = check_edge_ptrs(idx_out, w_out)) != GM_OK) return st;
+    if (!idx_mid != !w_mid) return GM_ERR_NULL;
+    const uintptr_t row = (uintptr_t)s * 4;
+    if (!aligned(idx, row) || !aligned(w, row) || !aligned(idx_out, row) ||
+        !aligned(w_out, row) || (idx_mid && (!aligned(idx_mid, row) || !aligned(w_mid, row))))
+        return GM_ERR_ALIGN;
+    const size_t bytes = (size_t)B * n * hkv * s * 4;
+    const void* ins[2] = {idx, w};
+    const void* outs[4] = {idx_out, w_out, idx_mid, w_mid};
+    for (int o = 0; o < 4; ++o) {
+        for (int i = 0; i < 2; ++i)
+            if (overlaps(outs[o], bytes, ins[i], bytes)) return GM_ERR_ALIAS;
+        for (int o2 = o + 1; o2 < 4; ++o2)
+            if (overlaps(outs[o], bytes, outs[o2], bytes)) return GM_ERR_ALIAS;
+    }
+    return hip_status(gm::launch_ser_chain2(B, n, hkv, idx, w, s, idx_mid, w_mid, idx_out, w_out,
+                                            stream));
 }
 
 gm_status gm_sea_forward(int B, int n, int hq, int hkv, int d, gm_dtype dt, float scale,

@@ -25,6 +25,13 @@ hipError_t launch_ser_forward(int B, int n, int hkv, const int32_t* idx1, const 
                               int32_t* idx_out, float* w_out, int s1, uint64_t* paths,
                               hipStream_t st);
 
+// Two chained referral steps in one launch (s1 = s2 = s3 = s, s = 2 or 4,
+// rows s-word aligned): A2 = Sp(A1 A1), A1 = Sp(A0 A0); idx_mid / w_mid
+// receive A1 when not null.
+hipError_t launch_ser_chain2(int B, int n, int hkv, const int32_t* idx, const float* w, int s,
+                             int32_t* idx_mid, float* w_mid, int32_t* idx_out, float* w_out,
+                             hipStream_t st);
+
 // The 16-lane-row fast kernels apply: one d-row is 256 bytes, s <= 4, and
 // activation tensors are addressable with 32-bit byte offsets.
 bool sea_fast_shape(int B, int n, int hq, int hkv, int d, bool bf16, int s);

@@ -442,6 +442,149 @@ __global__ __launch_bounds__(kBlock, MAP ? 4 : 1) void ser_fwd_vec_kernel(SerUni
     }
 }
 
+// ------------------------------------------- two chained referral steps
+// A2 = Sp(A1 A1) with A1 = Sp(A0 A0): the edge matrix raised to the power
+// 4 by two referral steps, each mixing the edges the previous step left
+// (ai.info Key Contributions 2, the l-th power of the edge matrix, here
+// l = 2; Methodology: referral works on the current stored edges).
+// Step 2 reads rows of A1 at any earlier token of the pair, rows that other
+// workgroups would write, so one launch cannot wait for them without a
+// grid-wide barrier.  Instead a lane owns unit i and ranks A1's row i from
+// A0, then A1's rows at the S targets of that row (again from A0), and then
+// A2's row i from those: S + 1 referrals of A0 and one of A1 per unit, with
+// no intermediate tensor in memory (it may still be written, for a later
+// backward).  Every row goes through the arithmetic of one referral step
+// (path products in double, merged in path order, rounded once, ranked by
+// weight then lower index), so A1 and A2 are bitwise those of two separate
+// steps.  s1 = s2 = s3 = S, S = 2 or 4, rows S-word aligned.
+struct SerChainArgs {
+    const int32_t* idx;   // A0
+    const float* w;
+    int32_t* idx_mid;     // A1, or null
+    float* w_mid;
+    int32_t* idx_out;     // A2
+    float* w_out;
+    int hkv, U;
+    FastDiv fd_hkv, fd_n;
+    int n;
+};
+
+template <int S>
+__device__ __forceinline__ void load_row(const int32_t* idx, const float* w, int row,
+                                         int* m, float* y) {
+    if constexpr (S == 4) {
+        const int4 mi = *reinterpret_cast<const int4*>(idx + (size_t)row * 4);
+        const float4 yi = *reinterpret_cast<const float4*>(w + (size_t)row * 4);
+        m[0] = mi.x; m[1] = mi.y; m[2] = mi.z; m[3] = mi.w;
+        y[0] = yi.x; y[1] = yi.y; y[2] = yi.z; y[3] = yi.w;
+    } else {
+        const int2 mi = *reinterpret_cast<const int2*>(idx + (size_t)row * 2);
+        const float2 yi = *reinterpret_cast<const float2*>(w + (size_t)row * 2);
+        m[0] = mi.x; m[1] = mi.y;
+        y[0] = yi.x; y[1] = yi.y;
+    }
+}
+
+template <int S>
+__device__ __forceinline__ void store_row(int32_t* idx, float* w, int row, const int (&m)[S],
+                                          const float (&y)[S]) {
+    if constexpr (S == 4) {
+        *reinterpret_cast<int4*>(idx + (size_t)row * 4) = make_int4(m[0], m[1], m[2], m[3]);
+        *reinterpret_cast<float4*>(w + (size_t)row * 4) = make_float4(y[0], y[1], y[2], y[3]);
+    } else {
+        *reinterpret_cast<int2*>(idx + (size_t)row * 2) = make_int2(m[0], m[1]);
+        *reinterpret_cast<float2*>(w + (size_t)row * 2) = make_float2(y[0], y[1]);
+    }
+}
+
+template <int S, bool MID>
+__global__ __launch_bounds__(kBlock) void ser_chain2_kernel(SerChainArgs a) {
+    constexpr int C = S * S;
+    const int u = xcd_unit(a.U);
+    if (u < 0) return;
+    const int bi = (int)fdiv((uint32_t)u, a.fd_hkv);
+    const int i = bi - (int)fdiv((uint32_t)bi, a.fd_n) * a.n;
+    // Rows r = 0 .. S + 1, one at a time: r = 0 is A1's row i, r = 1 .. S
+    // A1's rows at the S targets of row i (the second step's leg 2), each
+    // referred from A0; r = S + 1 is A2's row i, referred from those.  Rows
+    // are parked in this lane's LDS slots.  The merge is written once, in
+    // the loop body: ranked side by side (or behind a helper function) the
+    // rows' merges hold far more registers than one (a single wavefront
+    // per SIMD).
+    __shared__ int2 park[(S + 1) * S][kBlock];
+#pragma unroll 1
+    for (int r = 0; r <= S + 1; ++r) {
+        int m[C];
+        float x[S], y[C];
+        if (r <= S) {
+            const int tgt = r == 0 ? i : park[r - 1][threadIdx.x].x;
+            const int row = u + (tgt - i) * a.hkv;
+            int j[S];
+            load_row<S>(a.idx, a.w, row, j, x);
+#pragma unroll
+            for (int aa = 0; aa < S; ++aa)
+                load_row<S>(a.idx, a.w, row + (j[aa] - tgt) * a.hkv, m + aa * S, y + aa * S);
+        } else {
+#pragma unroll
+            for (int c = 0; c < S; ++c) x[c] = __int_as_float(park[c][threadIdx.x].y);
+#pragma unroll
+            for (int k = 0; k < C; ++k) {
+                const int2 e = park[S + k][threadIdx.x];
+                m[k] = e.x;
+                y[k] = __int_as_float(e.y);
+            }
+        }
+        // merge in path order (ser_fwd_vec_kernel's arithmetic), then rank
+        double cw[C], acc[C];
+#pragma unroll
+        for (int k = 0; k < C; ++k) {
+            cw[k] = (double)x[k / S] * (double)y[k];
+            acc[k] = cw[k];
+        }
+#pragma unroll
+        for (int k = 1; k < C; ++k) {
+            uint32_t dup = 0;
+#pragma unroll
+            for (int k2 = 0; k2 < k; ++k2) {
+                const bool same = m[k2] == m[k];
+                acc[k2] += same ? cw[k] : 0.0;
+                dup |= same ? 0x80000000u : 0u;
+            }
+            m[k] = (int)((uint32_t)m[k] | dup);
+        }
+        uint64_t key[C];
+#pragma unroll
+        for (int k = 0; k < C; ++k) {
+            const float wk = (float)acc[k];
+            key[k] = m[k] >= 0 && wk > 0.0f
+                         ? ((uint64_t)__float_as_uint(wk) << 32) | (uint32_t)~(uint32_t)m[k]
+                         : 0ull;
+        }
+        if constexpr (S == 4) {
+            sort4_desc(key + 0); sort4_desc(key + 4); sort4_desc(key + 8); sort4_desc(key + 12);
+            merge_top4(key + 0, key + 4);
+            merge_top4(key + 8, key + 12);
+            merge_top4(key + 0, key + 8);
+        } else {
+            sort4_desc(key);
+        }
+        int om[S];
+        float ow[S];
+#pragma unroll
+        for (int c = 0; c < S; ++c) {
+            om[c] = key[c] ? (int)~(uint32_t)key[c] : 0;
+            ow[c] = key[c] ? __uint_as_float((uint32_t)(key[c] >> 32)) : 0.0f;
+        }
+        if (r <= S) {
+#pragma unroll
+            for (int c = 0; c < S; ++c)
+                park[r * S + c][threadIdx.x] = make_int2(om[c], __float_as_int(ow[c]));
+        }
+        if (MID && r == 0) store_row<S>(a.idx_mid, a.w_mid, u, om, ow);
+        if (r == S + 1) store_row<S>(a.idx_out, a.w_out, u, om, ow);
+    }
+}
+
 __global__ __launch_bounds__(kBlock) void ser_bwd_unit_kernel(SerUnitArgs a) {
     const int u = blockIdx.x * kBlock + threadIdx.x;
     if (u >= a.U) return;
@@ -1031,6 +1174,26 @@ hipError_t launch_ser_forward(int B, int n, int hkv, const int32_t* idx1, const 
         case 64: return run_fwd<64>(a, st);
         default: return hipErrorInvalidValue;
     }
+}
+
+hipError_t launch_ser_chain2(int B, int n, int hkv, const int32_t* idx, const float* w, int s,
+                             int32_t* idx_mid, float* w_mid, int32_t* idx_out, float* w_out,
+                             hipStream_t st) {
+    SerChainArgs a{idx, w, idx_mid, w_mid, idx_out, w_out, hkv, B * n * hkv,
+                   make_fastdiv((uint32_t)hkv), make_fastdiv((uint32_t)n), n};
+    const dim3 grid(xcd_unit_grid(a.U));
+    const bool mid = idx_mid != nullptr;
+    if (s == 4 && mid)
+        hipLaunchKernelGGL((ser_chain2_kernel<4, true>), grid, dim3(kBlock), 0, st, a);
+    else if (s == 4)
+        hipLaunchKernelGGL((ser_chain2_kernel<4, false>), grid, dim3(kBlock), 0, st, a);
+    else if (s == 2 && mid)
+        hipLaunchKernelGGL((ser_chain2_kernel<2, true>), grid, dim3(kBlock), 0, st, a);
+    else if (s == 2)
+        hipLaunchKernelGGL((ser_chain2_kernel<2, false>), grid, dim3(kBlock), 0, st, a);
+    else
+        return hipErrorInvalidValue;
+    return hipGetLastError();
 }
 
 hipError_t launch_ser_backward(int B, int n, int hkv, const int32_t* idx1, const float* w1,

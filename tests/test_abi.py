@@ -35,7 +35,7 @@ def test_library_exports_every_declared_call(lib):
     assert set(names) == set(binding.EXPORTS)
     for name in names:
         assert hasattr(lib, name), name
-    assert lib.gm_abi_version() == 7
+    assert lib.gm_abi_version() == 8
 
 
 def test_status_strings(lib):
@@ -72,6 +72,22 @@ def test_ser_forward_argument_checks(lib):
     assert f(1, 4, 1, *far[:2], 4, *far[2:4], 4, *far[4:6], 4, fake((8 << 32) + 4),
              None) == ALIGN                                           # paths 8-byte aligned
     assert f(1, 4, 1, *far[:2], 4, *far[2:4], 4, *far[4:6], 4, far[0], None) == ALIAS
+
+
+def test_ser_forward_chain2_argument_checks(lib):
+    f = lib.gm_ser_forward_chain2
+    i, w, io, wo = (fake(k << 32) for k in range(1, 5))
+    im, wm = fake(5 << 32), fake(6 << 32)
+    assert f(-1, 4, 1, i, w, 4, None, None, io, wo, None) == SHAPE
+    assert f(1, 4, 1, i, w, 3, None, None, io, wo, None) == UNSUP        # s = 3
+    assert f(1, 4, 1, i, w, 8, None, None, io, wo, None) == UNSUP        # s = 8
+    assert f(0, 4, 1, None, None, 4, None, None, None, None, None) == OK  # empty
+    assert f(1, 4, 1, None, w, 4, None, None, io, wo, None) == NULL
+    assert f(1, 4, 1, i, w, 4, im, None, io, wo, None) == NULL           # half of A1
+    assert f(1, 4, 1, fake((1 << 32) + 8), w, 4, None, None, io, wo, None) == ALIGN
+    assert f(1, 4, 1, i, w, 4, im, fake((6 << 32) + 4), io, wo, None) == ALIGN
+    assert f(1, 4, 1, i, w, 4, None, None, i, wo, None) == ALIAS         # A2 on A0
+    assert f(1, 4, 1, i, w, 4, io, wm, io, wo, None) == ALIAS            # A1 on A2
 
 
 def test_sea_argument_checks(lib):
