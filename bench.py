@@ -173,6 +173,10 @@ def parse():
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="instead of the pass, run a plain device copy of MIB MiB "
                          "(the known-size reference for hardware byte counters)")
+    ap.add_argument("--dispatch-probe", action="store_true",
+                    help="time the start of 262,144 wavefronts that each store one word per "
+                         "lane, as one-wavefront and as four-wavefront workgroups "
+                         "(libgm_probe.so; measurement only)")
     ap.add_argument("--gather-probe", action="store_true",
                     help="instead of the pass, measure the 256-byte-row gather ceilings "
                          "(libgm_probe.so) by set size per XCD and loads in flight")
@@ -230,6 +234,38 @@ def run_gather_probe(a):
             print(json.dumps(out[-1]), file=sys.stderr, flush=True)
     print(json.dumps({"gather_probe": out, "rows_per_xcd_per_launch": PROBE_ROWS_PER_XCD,
                       "row_bytes": 256, "workgroups": grid}))
+
+
+def run_dispatch_probe(a):
+    """Median microseconds to start 262,144 wavefronts (the target pass's
+    one per target row at the measured shape) as one- or four-wavefront
+    workgroups, each lane storing one word."""
+    import ctypes
+    path = os.path.join(ROOT, "sparse_dynamic_routing_amd", "libgm_probe.so")
+    lib = ctypes.CDLL(path)
+    f = lib.gm_probe_dispatch
+    f.argtypes = [ctypes.c_void_p, ctypes.c_longlong, ctypes.c_int, ctypes.c_void_p]
+    f.restype = ctypes.c_int
+    waves = 262144
+    out = torch.empty(waves * 64, dtype=torch.int32, device="cuda")
+    st = torch.cuda.current_stream()
+    res = {}
+    for wpg in (1, 4):
+        ts = []
+        for it in range(max(a.warmup, 1) + max(a.steps, 5)):
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record(st)
+            rc = f(out.data_ptr(), waves, wpg, st.cuda_stream)
+            e1.record(st)
+            e1.synchronize()
+            if rc:
+                raise RuntimeError(f"gm_probe_dispatch returned {rc}")
+            if it >= max(a.warmup, 1):
+                ts.append(e0.elapsed_time(e1) * 1e3)
+        res[f"{wpg}_wave_workgroups_us"] = round(statistics.median(ts), 1)
+    print(json.dumps({"dispatch_probe": res, "waves": waves,
+                      "how": "one word stored per lane; HIP events around the launch"}))
 
 
 class Pass:
@@ -742,6 +778,9 @@ def main():
         return
     if a.gather_probe:
         run_gather_probe(a)
+        return
+    if a.dispatch_probe:
+        run_dispatch_probe(a)
         return
     gm.load()
     if a.config == "decode":

@@ -21,6 +21,18 @@
 //          rows are waited on (as the layer kernels do with their edge ids)
 //   grid   workgroups of 256 threads, a multiple of 8
 // Returns 0, 1 for bad arguments, 2 when the launch fails.
+//
+// Dispatch-rate probe (same library): how long does the GPU take just to
+// start `waves` wavefronts that each store one word per lane, dealt as
+// one-wavefront workgroups or as four-wavefront workgroups?  The SEA
+// backward's target pass starts one one-wavefront workgroup per target row.
+//
+//   int gm_probe_dispatch(unsigned* out, long long waves, int waves_per_wg,
+//                         hipStream_t stream);
+//
+//   out    [waves * 64] words, device (every word written once)
+//   waves_per_wg in {1, 4}; waves a multiple of waves_per_wg
+// Returns 0, 1 for bad arguments, 2 when the launch fails.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -89,5 +101,27 @@ extern "C" int gm_probe_gather(const void* table, long long rows_per_xcd, const 
         default:
             return 1;
     }
+    return hipGetLastError() == hipSuccess ? 0 : 2;
+}
+
+namespace {
+
+template <int W>
+__global__ __launch_bounds__(64 * W) void dispatch_probe_kernel(unsigned* __restrict__ out) {
+    out[(size_t)blockIdx.x * (64 * W) + threadIdx.x] = blockIdx.x;
+}
+
+}  // namespace
+
+extern "C" int gm_probe_dispatch(unsigned* out, long long waves, int waves_per_wg,
+                                 hipStream_t stream) {
+    if (!out || waves < 1 || (waves_per_wg != 1 && waves_per_wg != 4) ||
+        waves % waves_per_wg != 0 || waves / waves_per_wg > 0x7fffffffLL)
+        return 1;
+    const unsigned grid = (unsigned)(waves / waves_per_wg);
+    if (waves_per_wg == 1)
+        hipLaunchKernelGGL(dispatch_probe_kernel<1>, dim3(grid), dim3(64), 0, stream, out);
+    else
+        hipLaunchKernelGGL(dispatch_probe_kernel<4>, dim3(grid), dim3(256), 0, stream, out);
     return hipGetLastError() == hipSuccess ? 0 : 2;
 }
