@@ -65,11 +65,16 @@ typedef enum {
     GM_ERR_HIP = 5,          /* a HIP launch or runtime call failed          */
     GM_ERR_ALIGN = 6,        /* a pointer is not aligned as required         */
     GM_ERR_ALIAS = 7,        /* an output overlaps an input it must not      */
-    GM_ERR_TOO_LARGE = 8     /* the sizes need more than the fixed scratch of
+    GM_ERR_TOO_LARGE = 8,    /* the sizes need more than the fixed scratch of
                                 gm_sea_backward_noalloc                       */
+    GM_STATUS_RANGE = 0x7fffffff   /* not a status: gives the type the range of
+                                      int, so that any value a caller passes
+                                      (e.g. to gm_status_string) is valid */
 } gm_status;
 
-typedef enum { GM_F32 = 0, GM_BF16 = 1 } gm_dtype;
+/* GM_DTYPE_RANGE is not a dtype: it gives the type the range of int, so that
+   the library can reject any value a caller passes (GM_ERR_UNSUPPORTED). */
+typedef enum { GM_F32 = 0, GM_BF16 = 1, GM_DTYPE_RANGE = 0x7fffffff } gm_dtype;
 
 /*
  * Sparse edge referral, forward: A' = Sparsify_s1(A1 A2)

@@ -114,6 +114,7 @@ const char* gm_status_string(gm_status s) {
         case GM_ERR_TOO_LARGE:
             return "sizes need more scratch than the fixed GM_NOALLOC_SCRATCH_BYTES of the "
                    "allocation-free call (use the call with a workspace)";
+        case GM_STATUS_RANGE: break;
     }
     return "unknown status";
 }
