@@ -53,6 +53,9 @@ SEA_SHAPES = [
     (torch.float32, 64, 3, 4, 33),
     (torch.float32, 128, 6, 3, 29),
     (torch.bfloat16, 256, 5, 3, 19),
+    # groups wider than the row kernels' sixteen heads (multi-query widths)
+    (torch.bfloat16, 64, 32, 4, 29),
+    (torch.float32, 32, 24, 2, 21),
 ]
 
 
