@@ -249,6 +249,30 @@ def test_sea_backward_partitioned_index(n, s, dtype, d):
         assert_close("dw", host(dw), rdw, X)
 
 
+def test_sea_backward_beyond_partitioned_index():
+    """n = 2^20 + 37 tokens (one pair, fp32, d = 64: 256-byte rows): beyond
+    the partitioned index's 2^20 rows the row kernels count in-degrees in
+    the source pass, scan them over the whole tensor, and reduce every K/V
+    row with the persistent target kernel; every output compared with the
+    oracle, with and without the forward's statistics."""
+    n, s, d = (1 << 20) + 37, 4, 64
+    say(f"case sea backward beyond the partitioned index n={n} s={s} fp32 d={d}")
+    rng = np.random.default_rng(1 << 20)
+    q, k, v, do, idx, w = _sea_inputs(rng, torch.float32, d, 1, s, n, B=1, hkv=1)
+    rdq, rdk, rdv, rdw = oracle.get().sea_backward(q, k, v, idx, w, do)
+    X = TOL[torch.float32]
+    dq_, dk_, dv_, do_ = dev(q), dev(k), dev(v), dev(do)
+    di, dw_ = dev(idx), dev(w)
+    _, st = gm.sea_forward(dq_, dk_, dv_, di, dw_, save_stats=True)
+    for stats in (None, st):
+        say(f"  stats={stats is not None}")
+        dq, dk, dv, dw = gm.sea_backward(dq_, dk_, dv_, di, dw_, do_, stats=stats)
+        assert_close("dq", host(dq), rdq, X)
+        assert_close("dk", host(dk), rdk, X)
+        assert_close("dv", host(dv), rdv, X)
+        assert_close("dw", host(dw), rdw, X)
+
+
 def _unaligned(x: np.ndarray) -> torch.Tensor:
     """x on the GPU, starting 4 bytes past a 16-byte boundary (contiguous)."""
     flat = torch.empty(x.size + 1, dtype=torch.from_numpy(x[:0].copy()).dtype, device="cuda")

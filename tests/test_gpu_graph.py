@@ -75,7 +75,7 @@ ORDER_VARIES = {"dA"}
 
 
 @pytest.mark.parametrize("B,n", [(2, 2048), (1, 8192)],
-                         ids=["n2048-one-pass-index", "n8192-global-index"])
+                         ids=["n2048-one-pass-index", "n8192-partitioned-index"])
 def test_layer_pass_graph_replays_match_eager(B, n):
     say(f"case graph replay B={B} n={n}")
     lp = LayerPass(B, n)
