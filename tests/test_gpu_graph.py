@@ -128,10 +128,11 @@ def _capture(fn):
 
 
 def test_other_calls_graph_replays_match_eager():
-    """Leg construction (forward and backward), the decode step and the
-    refresh edges captured together and replayed three times against the
-    eager results (all bitwise: their sums run in a fixed order)."""
-    say("case graph replay: leg construction, decode step, refresh edges")
+    """Leg construction (forward and backward), the decode step, the refresh
+    edges and two chained referral steps in one call captured together and
+    replayed three times against the eager results (all bitwise: their sums
+    run in a fixed order)."""
+    say("case graph replay: leg construction, decode step, refresh edges, chained referral")
     B, n, hkv, hq, d, K, s = 2, 1024, 4, 8, 128, 16, 4
     seed = synth.BASE_SEED + 42
     cu = lambda x: torch.from_numpy(x).cuda()  # noqa: E731
@@ -155,6 +156,10 @@ def test_other_calls_graph_replays_match_eager():
         "ri": torch.empty((B, n, hkv, s), dtype=torch.int32, device="cuda"),
         "rw": torch.empty((B, n, hkv, s), **f32),
         "lse": torch.empty((B, n, hq), **f32),
+        "c1i": torch.empty((B, n, hkv, s), dtype=torch.int32, device="cuda"),
+        "c1w": torch.empty((B, n, hkv, s), **f32),
+        "c2i": torch.empty((B, n, hkv, s), dtype=torch.int32, device="cuda"),
+        "c2w": torch.empty((B, n, hkv, s), **f32),
     }
     dleg = synth.normal(seed + 7, "dout", (B, n, hkv, s), torch.float32, device="cuda")
     ws = torch.empty(max(gm.gm_leg_mix_backward_workspace_bytes(B, n, hkv, K), 8) // 8,
@@ -168,6 +173,7 @@ def test_other_calls_graph_replays_match_eager():
                                out["da"], ws)
         gm.gm_decode_step(i1, w1, eidx, ew, q1, k, v, out["di"], out["dwt"], out["do"])
         gm.gm_dense_refresh(q, k, out["lse"], out["ri"], out["rw"])
+        gm.gm_ser_forward_chain2(eidx, ew, out["c2i"], out["c2w"], out["c1i"], out["c1w"])
 
     run()
     torch.cuda.synchronize()
