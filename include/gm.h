@@ -118,7 +118,10 @@ gm_status gm_ser_forward(int B, int n, int hkv,
  * gm_ser_forward calls with s1 = s2 = s3 = s and both legs equal give.
  * One launch: each unit recomputes the rows of A1 it needs (its own and
  * those at its s targets) instead of waiting for other workgroups to write
- * them, so no A1 round trip through memory is needed.
+ * them, so no A1 round trip through memory is needed.  That is s + 2
+ * merges per unit instead of 2: on MI355X it takes about twice as long as
+ * the two gm_ser_forward calls (the merges, not memory, bound it), so it is
+ * for callers that want A2 without holding A1.
  */
 gm_status gm_ser_forward_chain2(int B, int n, int hkv, const int32_t* idx, const float* w,
                                 int s, int32_t* idx_mid, float* w_mid,
